@@ -1,0 +1,120 @@
+"""Seeded synthetic inputs for joint image+text attention.
+
+This module only draws random tensors with the shapes of the workloads below; it holds none of the
+attention arithmetic, so both the fp64 oracle (test-side) and the HIP path can be fed from it.
+
+Workload shapes (the pages give no dataset we can use; these tensors stand in for the activations
+the models on the pages produce):
+
+* ``tiny``      - B1 H2 D32, 4x4 patch grid (16 image tokens) + 8 text tokens = L 24.
+* ``mmdit512``  - B16 H12 D64, 512 px image -> 4x64x64 latent, patch 2 -> 1024 image tokens,
+                  plus 77 CLIP text tokens = L 1101 (re-diffusion README: the architecture
+                  flowchart and the profiling table quote batch 16 and a B x 12 x 1101 x 1101
+                  score matrix; width 768 / 12 heads gives D 64).
+* ``dit256``    - B64 H16 D72, class-conditional DiT-XL/2 at 256 px: 32x32x4 latent, patch 2 ->
+                  256 image tokens, no text stream (DiT-MoE README, training and sampling
+                  commands name DiT-XL/2 at 256 px).
+* ``mmdit768``  - B4 H24 D128, 768 px: 96x96 latent, patch 2 -> 2304 image tokens + 77 text
+                  tokens = L 2381; the q, k, v rows at text positions are multiplied by 3 before
+                  the bf16 cast (LavenderFlow model card: 768x768 MM-DiT).
+* ``ragged``    - B2 H24 D128, 4096 image tokens + up to 256 text tokens, L 4352; per-sample
+                  valid text length drawn uniformly from [1, 256]; keys past
+                  valid_len[b] = 4096 + txt_len[b] are padding (diffusion-pipe summary: the
+                  attention wrapper's varlen path).
+
+Recipe (all on CPU, one ``torch.Generator`` seeded with ``seed``, in this order):
+1. ragged only: ``txt_len = randint(1, 257, (B,))``.
+2. q, k, v = ``randn(B, L, H, D)`` fp32 each; ``mmdit768`` scales the text rows by 3; cast to bf16.
+3. gains = ``1 + 0.1 * randn(2, D)`` fp32 (row 0 for Q, row 1 for K).
+4. dout = ``randn(B, L, H, D).bfloat16()``.
+Text tokens sit at positions N_img .. L-1 (image first, text last).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    D: int
+    n_img: int
+    n_txt: int
+    txt_row_scale: float = 1.0
+    ragged_text: bool = False
+
+    @property
+    def L(self) -> int:
+        return self.n_img + self.n_txt
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", B=1, H=2, D=32, n_img=16, n_txt=8),
+    "mmdit512": Workload("mmdit512", B=16, H=12, D=64, n_img=1024, n_txt=77),
+    "dit256": Workload("dit256", B=64, H=16, D=72, n_img=256, n_txt=0),
+    "mmdit768": Workload("mmdit768", B=4, H=24, D=128, n_img=2304, n_txt=77, txt_row_scale=3.0),
+    "ragged": Workload("ragged", B=2, H=24, D=128, n_img=4096, n_txt=256, ragged_text=True),
+}
+
+EPS = 1e-6
+
+
+def default_scale(D: int) -> float:
+    """Softmax scale 1/sqrt(D) with the true head dim."""
+    return 1.0 / math.sqrt(D)
+
+
+def make_inputs(workload: str | Workload, seed: int = 0) -> dict:
+    """Draw the inputs of a named workload. Returns CPU tensors:
+    q, k, v, dout: bf16 [B, L, H, D]; gains: fp32 [2, D]; valid_len: int32 [B] or None;
+    plus the python scalars scale, eps and the workload itself."""
+    w = WORKLOADS[workload] if isinstance(workload, str) else workload
+    g = torch.Generator().manual_seed(seed)
+    B, L, H, D = w.B, w.L, w.H, w.D
+    valid_len = None
+    if w.ragged_text:
+        txt_len = torch.randint(1, w.n_txt + 1, (B,), generator=g)
+        valid_len = (w.n_img + txt_len).to(torch.int32)
+    qkv = []
+    for _ in range(3):
+        x = torch.randn(B, L, H, D, generator=g)
+        if w.txt_row_scale != 1.0 and w.n_txt > 0:
+            x[:, w.n_img:] *= w.txt_row_scale
+        qkv.append(x.bfloat16())
+    gains = 1.0 + 0.1 * torch.randn(2, D, generator=g)
+    dout = torch.randn(B, L, H, D, generator=g).bfloat16()
+    return dict(q=qkv[0], k=qkv[1], v=qkv[2], gains=gains.float(), dout=dout,
+                valid_len=valid_len, scale=default_scale(D), eps=EPS, workload=w)
+
+
+def make_shape_inputs(B: int, L: int, H: int, D: int, seed: int = 0,
+                      valid_len: Optional[list] = None, scale: Optional[float] = None,
+                      eps: float = EPS, gain_std: float = 0.1, qk_std: float = 1.0) -> dict:
+    """Same recipe for an arbitrary shape (edge-case tests). ``valid_len`` is taken as given."""
+    g = torch.Generator().manual_seed(seed)
+    q = (qk_std * torch.randn(B, L, H, D, generator=g)).bfloat16()
+    k = (qk_std * torch.randn(B, L, H, D, generator=g)).bfloat16()
+    v = torch.randn(B, L, H, D, generator=g).bfloat16()
+    gains = (1.0 + gain_std * torch.randn(2, D, generator=g)).float()
+    dout = torch.randn(B, L, H, D, generator=g).bfloat16()
+    vl = None if valid_len is None else torch.tensor(valid_len, dtype=torch.int32)
+    return dict(q=q, k=k, v=v, gains=gains, dout=dout, valid_len=vl,
+                scale=default_scale(D) if scale is None else float(scale), eps=eps,
+                workload=Workload(f"B{B}L{L}H{H}D{D}", B=B, H=H, D=D, n_img=L, n_txt=0))
+
+
+def flops(B: int, L: int, H: int, D: int, valid_len=None) -> dict:
+    """Algorithmic FLOPs: forward 4*D per (query, valid key) pair, backward 2.5x that."""
+    if valid_len is None:
+        pairs = B * L * L
+    else:
+        pairs = sum(L * max(0, min(L, int(n))) for n in valid_len)
+    fwd = 4.0 * H * D * pairs
+    return dict(fwd=fwd, bwd=2.5 * fwd, total=3.5 * fwd,
+                fwd_padded=4.0 * B * H * L * L * D)
