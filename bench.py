@@ -1,0 +1,205 @@
+"""Benchmark: joint-attention forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mmdit512] [--no-cpu-baseline]
+
+A step is one forward (jattn_fwd) plus one backward (jattn_bwd) over the whole batch of the workload,
+inputs resident in HBM. Prints one JSON line. The throughput is algorithmic TFLOP/s:
+4*B*H*L*L*D for the forward (valid keys only for ragged workloads) and 2.5x that for the backward.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "joint-attn fwd+bwd TFLOP/s @ B16 L1101 H12 D64 bf16; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mmdit512")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the op shards with no "
+              "communication: each GPU runs its own micro-batch).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from diffusion_transformer_joint_amd import _lib
+    from diffusion_transformer_joint_amd.inputs import WORKLOADS, flops, make_inputs
+
+    w = WORKLOADS[args.workload]
+    B, L, H, D = w.B, w.L, w.H, w.D
+    inp = make_inputs(args.workload, seed=0)
+    dev = torch.device("cuda:0")
+    q, k, v, dout = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+    gains = inp["gains"].to(dev)
+    vl = None if inp["valid_len"] is None else inp["valid_len"].to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, L, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty(2, D, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    ws_bytes = int(lib.jattn_bwd_workspace_bytes(B, L, H, D))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    scale, eps = ctypes.c_float(inp["scale"]), ctypes.c_float(inp["eps"])
+    vlp = None if vl is None else vl.data_ptr()
+    fwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), vlp, B, L, H, D, scale, eps,
+                out.data_ptr(), lse.data_ptr(), sp)
+    bwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), vlp, out.data_ptr(), lse.data_ptr(),
+                dout.data_ptr(), B, L, H, D, scale, eps, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                dg.data_ptr(), ws.data_ptr(), ws_bytes, sp)
+
+    def fwd():
+        _lib.check("jattn_fwd", lib.jattn_fwd(*fwd_args))
+
+    def bwd(events=None):
+        if events is None:
+            _lib.check("jattn_bwd", lib.jattn_bwd(*bwd_args))
+        else:
+            _lib.check("jattn_bwd_ex", lib.jattn_bwd_ex(*bwd_args[:-1], events, len(_lib.BWD_STAGES), sp))
+
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)  # creates the underlying hipEvent_t
+        return e
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps of forward + backward. Per step, events bracket the forward kernel and
+    # the backward's three kernels (recorded by the library on the same stream via jattn_bwd_ex).
+    K = args.steps
+    ev_fwd0 = [new_event() for _ in range(K)]
+    ev_fwd1 = [new_event() for _ in range(K)]
+    ev_bwd = [[new_event() for _ in _lib.BWD_STAGES] for _ in range(K)]
+    arrays = [(ctypes.c_void_p * len(_lib.BWD_STAGES))(*[e.cuda_event for e in evs]) for evs in ev_bwd]
+    handles = [ctypes.cast(a, ctypes.c_void_p) for a in arrays]
+    start, end = new_event(), new_event()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        ev_fwd0[i].record(stream)
+        fwd()
+        ev_fwd1[i].record(stream)
+        bwd(handles[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    kern_ms = {
+        f"fwd_kernel<{D}>": sum(ev_fwd0[i].elapsed_time(ev_fwd1[i]) for i in range(K)) / K,
+        f"bwd_dq_kernel<{D}>": sum(ev_fwd1[i].elapsed_time(ev_bwd[i][0]) for i in range(K)) / K,
+        f"bwd_dkdv_kernel<{D}>": sum(ev_bwd[i][0].elapsed_time(ev_bwd[i][1]) for i in range(K)) / K,
+        "dg_reduce_kernel": sum(ev_bwd[i][1].elapsed_time(ev_bwd[i][2]) for i in range(K)) / K,
+    }
+    ms_fwd = kern_ms[f"fwd_kernel<{D}>"]
+    ms_bwd = ms_step - ms_fwd
+
+    vlist = None if inp["valid_len"] is None else inp["valid_len"].tolist()
+    fl = flops(B, L, H, D, vlist)
+    tflops = fl["total"] / (ms_step * 1e-3) / 1e12
+    fwd_tflops = fl["fwd"] / (ms_fwd * 1e-3) / 1e12
+    bwd_tflops = fl["bwd"] / (ms_bwd * 1e-3) / 1e12
+    # Roofline of the dominant kernel: MFMA FLOPs one launch executes per (query, valid key) pair --
+    # forward 4D (S, PV); dq kernel 6D (S, dP recomputed, dQ); dk/dv kernel 8D (S, dP, dV, dK).
+    pairs = fl["fwd"] / (4.0 * H * D)
+    per_pair = {f"fwd_kernel<{D}>": 4 * D, f"bwd_dq_kernel<{D}>": 6 * D, f"bwd_dkdv_kernel<{D}>": 8 * D}
+    dom = max(per_pair, key=lambda k: kern_ms[k])
+    achieved = per_pair[dom] * H * pairs / (kern_ms[dom] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flop_per_launch": per_pair[dom] * H * pairs, "avg_launch_ms": round(kern_ms[dom], 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "L": L, "H": H, "D": D, "n_img": w.n_img,
+                   "n_txt": w.n_txt, "valid_len": vlist, "global_batch": B, "seq_len": L,
+                   "parallelism": "single-gpu"},
+        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(ms_fwd, 5),
+        "bwd_ms": round(ms_bwd, 5),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "bwd_tflops": round(bwd_tflops, 2),
+        "gflop_per_step": round(fl["total"] / 1e9, 3),
+        "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(inp, seconds):
+    """The fp64 oracle (as is) on the first (batch, head) pairs of the same inputs, time-bounded."""
+    import numpy as np
+    import torch
+
+    from oracle import attention_fwd_bwd
+
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = 1
+    w = inp["workload"]
+    B, L, H, D = w.B, w.L, w.H, w.D
+    f = lambda t: t.to(torch.float64).numpy()
+    q, k, v, do = (f(inp[n]) for n in ("q", "k", "v", "dout"))
+    g = inp["gains"].double().numpy()
+    vl = None if inp["valid_len"] is None else inp["valid_len"].tolist()
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    done, flop = 0, 0.0
+    t0 = time.perf_counter()
+    chunk = 4
+    while done < len(pairs) and time.perf_counter() - t0 < seconds:
+        sel = pairs[done:done + chunk]
+        attention_fwd_bwd(q, k, v, g, do, vl, inp["scale"], inp["eps"], pairs=sel)
+        for b, _ in sel:
+            n = L if vl is None else max(0, min(L, vl[b]))
+            flop += 3.5 * 4.0 * L * n * D
+        done += len(sel)
+    dt = time.perf_counter() - t0
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle fwd+bwd on the first {done} of {len(pairs)} (batch, head) pairs of "
+                      f"the same seed-0 inputs, {dt:.1f} s wall; BLAS threads = cores, elementwise steps "
+                      f"single-threaded",
+            "seconds": round(dt, 2), "pairs": done}
+
+
+if __name__ == "__main__":
+    main()

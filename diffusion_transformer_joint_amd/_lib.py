@@ -1,0 +1,66 @@
+"""ctypes loader for libjattn.so (the C ABI declared in include/jattn.h).
+
+The library is built in-tree by ``diffusion_transformer_joint_amd.build``. Loading fails loudly if it
+is missing: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjattn.so")
+
+STATUS = {0: "JATTN_SUCCESS", 1: "JATTN_ERROR_INVALID_VALUE", 2: "JATTN_ERROR_NOT_SUPPORTED",
+          3: "JATTN_ERROR_WORKSPACE", 4: "JATTN_ERROR_HIP"}
+SUCCESS, INVALID_VALUE, NOT_SUPPORTED, WORKSPACE, HIP = range(5)
+
+EXPORTED = ("jattn_fwd", "jattn_bwd", "jattn_bwd_ex", "jattn_bwd_workspace_bytes",
+            "jattn_status_string", "jattn_abi_version")
+BWD_STAGES = ("bwd_dq_kernel", "bwd_dkdv_kernel", "dg_reduce_kernel")
+
+_lock = threading.Lock()
+_lib = None
+
+P = ctypes.c_void_p
+I = ctypes.c_int
+F = ctypes.c_float
+
+
+class JattnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libjattn.so once and declare the argument types of every entry point."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -m diffusion_transformer_joint_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.jattn_fwd.restype = I
+        lib.jattn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, F, P, P, P]
+        lib.jattn_bwd.restype = I
+        lib.jattn_bwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, F, P, P, P, P, P,
+                                  ctypes.c_size_t, P]
+        lib.jattn_bwd_ex.restype = I
+        lib.jattn_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, F, P, P, P, P, P,
+                                     ctypes.c_size_t, P, I, P]
+        lib.jattn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.jattn_bwd_workspace_bytes.argtypes = [I, I, I, I]
+        lib.jattn_status_string.restype = ctypes.c_char_p
+        lib.jattn_status_string.argtypes = [I]
+        lib.jattn_abi_version.restype = I
+        lib.jattn_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != SUCCESS:
+        raise JattnError(fn, status)

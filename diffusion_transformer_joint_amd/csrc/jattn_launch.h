@@ -1,0 +1,56 @@
+// Internal interface between the C ABI (jattn_api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace jattn {
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* gains;      // [2, D]
+  const int32_t* valid_len;  // [B] or nullptr
+  uint16_t* out;
+  float* lse;              // [B, H, L] natural log
+  int B, L, H;
+  float c;                 // softmax_scale * log2(e)
+  float eps;
+  int nblk;                // query blocks per (batch, head)
+  int items;               // B * H * nblk
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* gains;
+  const int32_t* valid_len;
+  const uint16_t* out;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dgains;           // [2, D]
+  float* delta;            // workspace [B, H, L]: rowsum(dout * out)
+  float* part_q;           // workspace [items, D]: gain-gradient partials of the query blocks
+  float* part_k;           // workspace [items, D]: gain-gradient partials of the key blocks
+  int B, L, H;
+  float scale;
+  float c;                 // scale * log2(e)
+  float eps;
+  int nblk;                // row blocks (queries or keys) per (batch, head)
+  int items;               // B * H * nblk
+};
+
+// Rows per workgroup of every kernel; shared by the host-side grid and workspace sizing.
+constexpr int kRowsPerBlock = 128;
+
+hipError_t launch_fwd(int D, const FwdArgs& a, hipStream_t stream);
+// Enqueues the backward kernels; if n_events > 0, records events[i] after stage i (i < n_events).
+hipError_t launch_bwd(int D, const BwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream);
+
+}  // namespace jattn

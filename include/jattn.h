@@ -1,0 +1,110 @@
+/*
+ * jattn.h -- C ABI of libjattn.so: QK-RMSNorm joint image+text attention, forward and backward,
+ * on MI355X (gfx950) HIP kernels.
+ *
+ * What is computed (re-diffusion README: the DiT-layer box of the architecture flowchart
+ * concatenates the per-stream Q/K/V and runs one joint multi-head attention over the concatenated
+ * sequence; the design-notes table, "QK norm" row, applies RMSNorm to Q and K; the profiling
+ * section describes the same attention as an explicit score matrix with an fp32 softmax. The
+ * diffusion-pipe summary's attention wrapper has a varlen path, the source of the key-padding
+ * length below). For every batch b and head h, with rows x of q and k over the head dim D:
+ *
+ *   r(x)   = 1 / sqrt(mean_d x_d^2 + eps)
+ *   Qn_i   = q_i * r(q_i) * gains[0, :]          Kn_j = k_j * r(k_j) * gains[1, :]
+ *   S_ij   = softmax_scale * <Qn_i, Kn_j>        for keys j < n_b, where n_b = clamp(valid_len[b], 0, L)
+ *   P_ij   = exp(S_ij - lse_i),  lse_i = log sum_{j < n_b} exp(S_ij)     (natural log)
+ *   out_i  = sum_j P_ij v_j                      (non-causal: every query sees every valid key)
+ *
+ * Padded keys (j >= n_b) are excluded; padded query rows are still computed over the valid keys.
+ * A row with no valid key gets out = 0 and lse = -inf. The backward pass returns the gradients of
+ * sum(out * dout) with respect to q, k, v and both gain rows; no gradient flows into lse.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major memory owned by the caller.
+ *    bf16 tensors ([B, L, H, D], 2 bytes per element, element (b, l, h, d) at ((b*L + l)*H + h)*D + d)
+ *    must be 16-byte aligned; fp32 / int32 arrays 4-byte aligned; the workspace 256-byte aligned.
+ *  - Inputs are read only. Outputs are fully overwritten (including zeros for dk and dv at padded
+ *    keys); dgains is overwritten, not accumulated.
+ *  - Work is enqueued asynchronously on `stream` (NULL = the null stream). The library never
+ *    allocates, frees, synchronises or prints, and keeps no mutable global state.
+ *  - Arguments are validated on the host before any HIP call. Device-side data (valid_len values,
+ *    tensor contents) is not validated: valid_len values are clamped to [0, L]; NaN inputs propagate.
+ *  - Supported head dims: D in {32, 64, 72, 128}. Sizes must satisfy L*H*D < 2^31 and B*H*L < 2^31.
+ */
+#ifndef JATTN_H
+#define JATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    JATTN_SUCCESS = 0,
+    JATTN_ERROR_INVALID_VALUE = 1, /* null pointer, size < 1, misalignment, non-finite scale,
+                                      eps < 0 or non-finite, output aliasing another buffer  */
+    JATTN_ERROR_NOT_SUPPORTED = 2, /* head dim outside the compiled set, or sizes too large    */
+    JATTN_ERROR_WORKSPACE = 3,     /* workspace NULL or smaller than jattn_bwd_workspace_bytes */
+    JATTN_ERROR_HIP = 4            /* a kernel launch failed (hipGetLastError)                 */
+} jattn_status;
+
+/* Forward pass.
+ *   q, k, v    bf16 [B, L, H, D] inputs.
+ *   gains      fp32 [2, D]: row 0 multiplies the normalised Q rows, row 1 the normalised K rows.
+ *   valid_len  int32 [B] number of valid (unpadded) keys per sequence, or NULL for all L.
+ *   softmax_scale  any finite value (the usual choice is 1/sqrt(D)); eps >= 0 (e.g. 1e-6).
+ *   out        bf16 [B, L, H, D] output.
+ *   lse        fp32 [B, H, L] row log-sum-exp of the scaled scores (natural log), used by jattn_bwd.
+ * out and lse must not overlap any input or each other. */
+jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float* gains,
+                       const int32_t* valid_len, int B, int L, int H, int D,
+                       float softmax_scale, float eps, void* out, float* lse, hipStream_t stream);
+
+/* Bytes of device workspace jattn_bwd needs for these sizes (row statistics and per-workgroup
+ * partial sums of the gain gradients). Returns 0 for invalid or unsupported sizes. */
+size_t jattn_bwd_workspace_bytes(int B, int L, int H, int D);
+
+/* Backward pass. Takes the forward inputs, the forward outputs out and lse (from jattn_fwd with the
+ * same arguments) and dout (bf16 [B, L, H, D], the gradient of the loss with respect to out).
+ *   dq, dk, dv  bf16 [B, L, H, D] gradients with respect to q, k, v (overwritten).
+ *   dgains      fp32 [2, D] gradient with respect to gains (overwritten; deterministic).
+ *   workspace   device scratch of at least jattn_bwd_workspace_bytes(B, L, H, D) bytes; its contents
+ *               on entry do not matter and are clobbered.
+ * Outputs and workspace must not overlap any input or each other. */
+jattn_status jattn_bwd(const void* q, const void* k, const void* v, const float* gains,
+                       const int32_t* valid_len, const void* out, const float* lse, const void* dout,
+                       int B, int L, int H, int D, float softmax_scale, float eps,
+                       void* dq, void* dk, void* dv, float* dgains,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Number of kernels jattn_bwd enqueues, in order: 0 = dq (query-parallel; also writes the row
+ * statistics Delta), 1 = dk/dv (key-parallel), 2 = gain-gradient reduction. */
+#define JATTN_BWD_STAGES 3
+
+/* jattn_bwd with per-stage timing hooks, for callers that attribute time to the individual kernels
+ * (profilers, benchmarks). Identical results to jattn_bwd. If n_stage_events > 0, stage_events points
+ * to n_stage_events (<= JATTN_BWD_STAGES) events created by the caller; event i is recorded on `stream`
+ * right after stage i is enqueued, so hipEventElapsedTime between an event recorded before the call
+ * and event 0, or between events i-1 and i, gives the duration of stage i. n_stage_events < 0, or
+ * > 0 with a NULL array, or > JATTN_BWD_STAGES -> INVALID_VALUE. A failed hipEventRecord -> HIP. */
+jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const float* gains,
+                          const int32_t* valid_len, const void* out, const float* lse, const void* dout,
+                          int B, int L, int H, int D, float softmax_scale, float eps,
+                          void* dq, void* dk, void* dv, float* dgains,
+                          void* workspace, size_t workspace_bytes,
+                          const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* jattn_status_string(jattn_status s);
+
+/* Version of this ABI; bumped on any incompatible change. */
+int jattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JATTN_H */

@@ -1,0 +1,50 @@
+"""Write the oracle's gain gradients for the full-size workloads to tests/golden/dgains_<name>.json.
+
+The gain gradient sums over every (batch, head) pair, so at full size it is the one output the
+parity tests cannot recompute from a few sampled pairs in seconds. This script computes it with the
+fp64 oracle only (inputs from the seeded workload generator, seed 0) and stores it; the GPU tests
+compare against the stored values.
+
+    python tests/golden/make_golden.py [workload ...]
+"""
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+from diffusion_transformer_joint_amd.inputs import make_inputs  # noqa: E402
+from oracle import attention_fwd_bwd  # noqa: E402
+
+FULL = ["mmdit512", "dit256", "mmdit768", "ragged"]
+
+
+def f64(t):
+    import torch
+    return t.to(torch.float64).numpy()
+
+
+def main(names):
+    for name in names:
+        t0 = time.time()
+        inp = make_inputs(name, seed=0)
+        vl = None if inp["valid_len"] is None else inp["valid_len"].tolist()
+        r = attention_fwd_bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), inp["gains"].double().numpy(),
+                              f64(inp["dout"]), vl, inp["scale"], inp["eps"])
+        w = inp["workload"]
+        rec = dict(workload=name, seed=0, B=w.B, L=w.L, H=w.H, D=w.D, valid_len=vl, scale=inp["scale"],
+                   eps=inp["eps"], source="oracle/jattn_oracle.py attention_fwd_bwd, fp64, all pairs",
+                   dgains=np.asarray(r["dgains"]).tolist(),
+                   out_sq_sum=float(np.sum(r["out"] ** 2)))
+        with open(os.path.join(HERE, f"dgains_{name}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(f"{name}: {time.time() - t0:.1f} s", flush=True)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:] or FULL)

@@ -1,0 +1,140 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point declared in
+include/jattn.h, and rejects invalid arguments on the host before any HIP call.
+
+Every call here is constructed to fail validation: the fake device addresses are never
+dereferenced, because a call that passed validation would enqueue kernels."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from diffusion_transformer_joint_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libjattn.so not built (run __graft_entry__.build())")
+
+A = 0x10000  # 256-byte aligned fake addresses, distinct ranges
+TB = 1 << 24
+
+
+def fake(i):
+    return A + i * TB
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    header = open(os.path.join(ROOT, "include", "jattn.h")).read()
+    declared = set(re.findall(r"\b(jattn_[a-z_]+)\s*\(", header))
+    assert declared == set(_lib.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS.items():
+        assert lib.jattn_status_string(code).decode() == name
+    assert lib.jattn_status_string(99).decode() == "JATTN_UNKNOWN_STATUS"
+    assert lib.jattn_abi_version() == 1
+
+
+def fwd(lib, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gains=fake(3), valid_len=None, B=2, L=100, H=3, D=64,
+             scale=0.125, eps=1e-6, out=fake(4), lse=fake(5), stream=None)
+    a.update(kw)
+    return lib.jattn_fwd(a["q"], a["k"], a["v"], a["gains"], a["valid_len"], a["B"], a["L"], a["H"], a["D"],
+                         ctypes.c_float(a["scale"]), ctypes.c_float(a["eps"]), a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), _lib.INVALID_VALUE),
+    (dict(k=None), _lib.INVALID_VALUE),
+    (dict(v=None), _lib.INVALID_VALUE),
+    (dict(gains=None), _lib.INVALID_VALUE),
+    (dict(out=None), _lib.INVALID_VALUE),
+    (dict(lse=None), _lib.INVALID_VALUE),
+    (dict(B=0), _lib.INVALID_VALUE),
+    (dict(L=0), _lib.INVALID_VALUE),
+    (dict(H=-1), _lib.INVALID_VALUE),
+    (dict(D=48), _lib.NOT_SUPPORTED),
+    (dict(D=256), _lib.NOT_SUPPORTED),
+    (dict(B=1, L=1 << 20, H=64, D=128), _lib.NOT_SUPPORTED),
+    (dict(scale=math.inf), _lib.INVALID_VALUE),
+    (dict(scale=math.nan), _lib.INVALID_VALUE),
+    (dict(eps=-1e-6), _lib.INVALID_VALUE),
+    (dict(eps=math.nan), _lib.INVALID_VALUE),
+    (dict(q=fake(0) + 8), _lib.INVALID_VALUE),          # misaligned bf16 tensor
+    (dict(lse=fake(5) + 2), _lib.INVALID_VALUE),        # misaligned fp32 array
+    (dict(out=fake(0)), _lib.INVALID_VALUE),            # out aliases q
+    (dict(lse=fake(4) + 4096), _lib.INVALID_VALUE),     # lse overlaps out
+    (dict(out=fake(3) - 16), _lib.INVALID_VALUE),       # out overlaps gains
+])
+def test_fwd_rejects(lib, kw, expect):
+    assert fwd(lib, **kw) == expect
+
+
+def bwd(lib, ws_bytes=None, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gains=fake(3), valid_len=None, out=fake(4), lse=fake(5),
+             dout=fake(6), B=2, L=100, H=3, D=64, scale=0.125, eps=1e-6, dq=fake(7), dk=fake(8), dv=fake(9),
+             dgains=fake(10), ws=fake(11), stream=None)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.jattn_bwd_workspace_bytes(a["B"], a["L"], a["H"], a["D"])
+    return lib.jattn_bwd(a["q"], a["k"], a["v"], a["gains"], a["valid_len"], a["out"], a["lse"], a["dout"],
+                         a["B"], a["L"], a["H"], a["D"], ctypes.c_float(a["scale"]), ctypes.c_float(a["eps"]),
+                         a["dq"], a["dk"], a["dv"], a["dgains"], a["ws"], ws_bytes, a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dout=None), _lib.INVALID_VALUE),
+    (dict(dq=None), _lib.INVALID_VALUE),
+    (dict(dgains=None), _lib.INVALID_VALUE),
+    (dict(lse=None), _lib.INVALID_VALUE),
+    (dict(B=0), _lib.INVALID_VALUE),
+    (dict(D=16), _lib.NOT_SUPPORTED),
+    (dict(scale=-math.inf), _lib.INVALID_VALUE),
+    (dict(eps=-0.5), _lib.INVALID_VALUE),
+    (dict(ws=None), _lib.WORKSPACE),
+    (dict(dk=fake(8) + 4), _lib.INVALID_VALUE),
+    (dict(ws=fake(11) + 64), _lib.INVALID_VALUE),       # workspace must be 256-byte aligned
+    (dict(dq=fake(6)), _lib.INVALID_VALUE),             # dq aliases dout
+    (dict(dv=fake(7) + 4096), _lib.INVALID_VALUE),      # dv overlaps dq
+    (dict(ws=fake(0)), _lib.INVALID_VALUE),             # workspace aliases q
+])
+def test_bwd_rejects(lib, kw, expect):
+    assert bwd(lib, **kw) == expect
+
+
+def test_bwd_ex_rejects_bad_event_arguments(lib):
+    need = lib.jattn_bwd_workspace_bytes(2, 100, 3, 64)
+    base = [fake(0), fake(1), fake(2), fake(3), None, fake(4), fake(5), fake(6), 2, 100, 3, 64,
+            ctypes.c_float(0.125), ctypes.c_float(1e-6), fake(7), fake(8), fake(9), fake(10), fake(11), need]
+    assert lib.jattn_bwd_ex(*base, None, 1, None) == _lib.INVALID_VALUE
+    assert lib.jattn_bwd_ex(*base, fake(12), -1, None) == _lib.INVALID_VALUE
+    assert lib.jattn_bwd_ex(*base, fake(12), 4, None) == _lib.INVALID_VALUE
+    # valid event arguments still fail on the invalid tensor arguments, before any HIP call
+    bad = list(base)
+    bad[0] = None
+    assert lib.jattn_bwd_ex(*bad, fake(12), 3, None) == _lib.INVALID_VALUE
+
+
+def test_bwd_rejects_small_workspace(lib):
+    need = lib.jattn_bwd_workspace_bytes(2, 100, 3, 64)
+    assert need > 0
+    assert bwd(lib, ws_bytes=need - 1) == _lib.WORKSPACE
+
+
+def test_workspace_bytes(lib):
+    assert lib.jattn_bwd_workspace_bytes(0, 10, 1, 64) == 0
+    assert lib.jattn_bwd_workspace_bytes(1, 10, 1, 40) == 0
+    w = lib.jattn_bwd_workspace_bytes(16, 1101, 12, 64)
+    # delta rows + two sets of per-workgroup gain partials (9 blocks of 128 rows per pair)
+    assert w >= 16 * 12 * 1101 * 4 + 2 * 16 * 12 * 9 * 64 * 4
+    assert w % 256 == 0

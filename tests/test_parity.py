@@ -1,0 +1,239 @@
+"""GPU parity: the HIP library (through its C ABI and the ctypes binding) against the fp64 oracle on
+the same seeded inputs.
+
+Tolerances (fixed for this op): forward out relative L2 <= 5e-3 and max abs <= 2e-2; backward
+relative L2 <= 1e-2 for each of dq, dk, dv, dgains. LSE (natural log) max abs <= 1e-2, with -inf
+exactly where a row has no valid key. Relative L2 = ||x - ref||_2 / ||ref||_2 over the compared
+elements. At full workload sizes the per-token outputs are compared on sampled (batch, head) pairs
+(pairs are independent, so the oracle computes them exactly); dgains, which sums over all pairs,
+is compared against oracle values stored by tests/golden/make_golden.py.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from diffusion_transformer_joint_amd import ops
+from diffusion_transformer_joint_amd.inputs import WORKLOADS, make_inputs, make_shape_inputs
+from oracle import attention_fwd_bwd
+
+pytestmark = pytest.mark.gpu
+
+FWD_REL, FWD_ABS, BWD_REL, LSE_ABS = 5e-3, 2e-2, 1e-2, 1e-2
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def to_dev(inp):
+    dev = torch.device("cuda:0")
+    d = {k: inp[k].to(dev).contiguous() for k in ("q", "k", "v", "gains", "dout")}
+    d["valid_len"] = None if inp["valid_len"] is None else inp["valid_len"].to(dev)
+    return d
+
+
+def run_gpu(inp):
+    d = to_dev(inp)
+    out, lse = ops.forward(d["q"], d["k"], d["v"], d["gains"], d["valid_len"], inp["scale"], inp["eps"])
+    dq, dk, dv, dg = ops.backward(d["q"], d["k"], d["v"], d["gains"], out, lse, d["dout"], d["valid_len"],
+                                  inp["scale"], inp["eps"])
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    return dict(out=f(out), lse=f(lse), dq=f(dq), dk=f(dk), dv=f(dv), dgains=f(dg))
+
+
+def run_oracle(inp, pairs=None):
+    f = lambda t: t.to(torch.float64).numpy()
+    vl = None if inp["valid_len"] is None else inp["valid_len"].tolist()
+    return attention_fwd_bwd(f(inp["q"]), f(inp["k"]), f(inp["v"]), inp["gains"].double().numpy(),
+                             f(inp["dout"]), vl, inp["scale"], inp["eps"], pairs=pairs)
+
+
+def rel_l2(x, ref):
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(x - ref)
+    return num / den if den > 0 else num
+
+
+def select(t, pairs, key):
+    if pairs is None:
+        return t.ravel()
+    if key == "lse":
+        return np.concatenate([t[b, h].ravel() for b, h in pairs])
+    return np.concatenate([t[b, :, h].ravel() for b, h in pairs])
+
+
+def check(got, ref, pairs=None, dgains_ref=None, tag=""):
+    errs = {}
+    o, ro = select(got["out"], pairs, "out"), select(ref["out"], pairs, "out")
+    errs["out_rel"], errs["out_abs"] = rel_l2(o, ro), float(np.max(np.abs(o - ro)))
+    l, rl = select(got["lse"], pairs, "lse"), select(ref["lse"], pairs, "lse")
+    assert np.array_equal(np.isneginf(l), np.isneginf(rl)), f"{tag}: -inf rows differ"
+    fin = np.isfinite(rl)
+    errs["lse_abs"] = float(np.max(np.abs(l[fin] - rl[fin]))) if fin.any() else 0.0
+    for key in ("dq", "dk", "dv"):
+        errs[key] = rel_l2(select(got[key], pairs, key), select(ref[key], pairs, key))
+    dg_ref = ref["dgains"] if dgains_ref is None else dgains_ref
+    if dg_ref is not None:
+        errs["dgains"] = rel_l2(got["dgains"], dg_ref)
+    say(f"{tag}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert errs["out_rel"] <= FWD_REL and errs["out_abs"] <= FWD_ABS, (tag, errs)
+    assert errs["lse_abs"] <= LSE_ABS, (tag, errs)
+    for key in ("dq", "dk", "dv", "dgains"):
+        if key in errs:
+            assert errs[key] <= BWD_REL, (tag, key, errs)
+    return errs
+
+
+# ------------------------------------------------------------------------------ small, full oracle
+def test_tiny_workload():
+    say("case: tiny workload B1 L24 H2 D32, seed 0")
+    inp = make_inputs("tiny", seed=0)
+    check(run_gpu(inp), run_oracle(inp), tag="tiny")
+
+
+SHAPES = [
+    # B, L, H, D, valid_len
+    (2, 1, 2, 64, None),
+    (1, 37, 2, 32, None),
+    (2, 200, 2, 64, [200, 71]),
+    (2, 300, 2, 72, [300, 129]),
+    (1, 257, 3, 128, None),
+    (2, 130, 2, 128, [1, 130]),
+    (3, 64, 1, 64, [64, 63, 65]),
+    (1, 513, 2, 64, None),
+]
+
+
+@pytest.mark.parametrize("B,L,H,D,vl", SHAPES)
+def test_shapes(B, L, H, D, vl):
+    say(f"case: shape B{B} L{L} H{H} D{D} valid_len={vl}, seed 1")
+    inp = make_shape_inputs(B, L, H, D, seed=1, valid_len=vl)
+    check(run_gpu(inp), run_oracle(inp), tag=f"B{B}L{L}H{H}D{D}")
+
+
+def test_valid_len_edges():
+    """valid_len 0 (row with no key), past L (clamped), negative (clamped to 0), 1."""
+    say("case: valid_len edges B4 L70 H2 D64 [0, 75, -3, 1]")
+    inp = make_shape_inputs(4, 70, 2, 64, seed=2, valid_len=[0, 75, -3, 1])
+    got = run_gpu(inp)
+    check(got, run_oracle(inp), tag="vl-edges")
+    for b in (0, 2):
+        assert np.all(got["out"][b] == 0) and np.all(np.isneginf(got["lse"][b]))
+        for key in ("dq", "dk", "dv"):
+            assert np.all(got[key][b] == 0), key
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_online_softmax_path(D):
+    """A huge K gain on one head-dim channel that every query leaves at zero inflates the score bound
+    past the fixed-shift limit without changing any score, so the kernels take the running-maximum
+    softmax on a well-conditioned problem."""
+    say(f"case: running-max softmax B2 L150 H2 D{D}, g_k[0] = 40, q[..., 0] = 0")
+    inp = make_shape_inputs(2, 150, 2, D, seed=3, valid_len=[150, 90])
+    inp["gains"][1, 0] = 40.0
+    inp["q"][..., 0] = 0
+    check(run_gpu(inp), run_oracle(inp), tag=f"online-D{D}")
+
+
+def test_identical_value_rows():
+    """Identical V rows u: out = u for every row and dq = dk = dgains = 0 in exact arithmetic."""
+    say("case: identical value rows B1 L200 H2 D64")
+    inp = make_shape_inputs(1, 200, 2, 64, seed=8)
+    u = torch.randn(64, generator=torch.Generator().manual_seed(3)).bfloat16()
+    inp["v"][:] = u
+    got = run_gpu(inp)
+    np.testing.assert_array_equal(got["out"], np.broadcast_to(u.double().numpy(), got["out"].shape))
+    typical = make_shape_inputs(1, 200, 2, 64, seed=8)
+    ref = run_gpu(typical)
+    for key in ("dq", "dk"):
+        assert np.linalg.norm(got[key]) <= 1e-3 * np.linalg.norm(ref[key]), key
+    assert np.linalg.norm(got["dgains"]) <= 1e-3 * np.linalg.norm(ref["dgains"])
+
+
+def test_zero_and_negative_scale():
+    for scale in (0.0, -0.3):
+        say(f"case: scale {scale} B1 L90 H2 D64")
+        inp = make_shape_inputs(1, 90, 2, 64, seed=4, scale=scale)
+        got = run_gpu(inp)
+        check(got, run_oracle(inp), tag=f"scale{scale}")
+
+
+# ------------------------------------------------------------------------------ full workloads
+def sample_pairs(B, H):
+    return sorted({(0, 0), (B // 2, H // 2), (B - 1, H - 1)})
+
+
+@pytest.mark.parametrize("name", ["mmdit512", "dit256", "mmdit768", "ragged"])
+def test_full_workload(name):
+    w = WORKLOADS[name]
+    say(f"case: full workload {name} B{w.B} L{w.L} H{w.H} D{w.D}, seed 0")
+    inp = make_inputs(name, seed=0)
+    got = run_gpu(inp)
+    pairs = sample_pairs(w.B, w.H)
+    ref = run_oracle(inp, pairs=pairs)
+    with open(os.path.join(GOLDEN, f"dgains_{name}.json")) as f:
+        gold = json.load(f)
+    assert gold["B"] == w.B and gold["L"] == w.L and gold["valid_len"] == (
+        None if inp["valid_len"] is None else inp["valid_len"].tolist())
+    check(got, ref, pairs=pairs, dgains_ref=np.array(gold["dgains"]), tag=name)
+    # a property that holds at any size: the gain identity <g_q, dg_q> = <g_k, dg_k>. An error e in
+    # dg with ||e|| <= BWD_REL ||dg|| moves <g, dg> by at most ||g|| ||e|| (Cauchy-Schwarz).
+    g, dg = inp["gains"].double().numpy(), got["dgains"]
+    a, b = float(g[0] @ dg[0]), float(g[1] @ dg[1])
+    bound = BWD_REL * (np.linalg.norm(g[0]) * np.linalg.norm(dg[0]) + np.linalg.norm(g[1]) * np.linalg.norm(dg[1]))
+    assert abs(a - b) <= bound, (a, b, bound)
+    if inp["valid_len"] is not None:
+        for bi, n in enumerate(inp["valid_len"].tolist()):
+            assert np.all(got["dk"][bi, n:] == 0) and np.all(got["dv"][bi, n:] == 0)
+
+
+# ------------------------------------------------------------------------------ properties
+def test_backward_is_deterministic():
+    say("case: determinism B2 L300 H3 D64")
+    inp = make_shape_inputs(2, 300, 3, 64, seed=5, valid_len=[300, 222])
+    d = to_dev(inp)
+    out, lse = ops.forward(d["q"], d["k"], d["v"], d["gains"], d["valid_len"], inp["scale"], inp["eps"])
+    r1 = ops.backward(d["q"], d["k"], d["v"], d["gains"], out, lse, d["dout"], d["valid_len"], inp["scale"])
+    r1 = [t.clone() for t in r1]
+    out2, lse2 = ops.forward(d["q"], d["k"], d["v"], d["gains"], d["valid_len"], inp["scale"], inp["eps"])
+    r2 = ops.backward(d["q"], d["k"], d["v"], d["gains"], out2, lse2, d["dout"], d["valid_len"], inp["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_padded_values_do_not_matter():
+    say("case: padding perturbation B2 L200 H2 D128 valid [120, 200]")
+    inp = make_shape_inputs(2, 200, 2, 128, seed=6, valid_len=[120, 200])
+    base = run_gpu(inp)
+    pert = dict(inp)
+    k, v = inp["k"].clone(), inp["v"].clone()
+    k[0, 120:] = (50 * torch.randn(k[0, 120:].shape, generator=torch.Generator().manual_seed(9))).bfloat16()
+    v[0, 120:] = float("nan")
+    pert["k"], pert["v"] = k, v
+    got = run_gpu(pert)
+    for key in ("out", "lse", "dq", "dgains"):
+        assert np.array_equal(got[key], base[key]), key
+    assert np.all(got["dk"][0, 120:] == 0) and np.all(got["dv"][0, 120:] == 0)
+    assert np.array_equal(got["dk"][:, :120], base["dk"][:, :120])
+
+
+def test_autograd_function_matches_backward():
+    say("case: autograd B1 L80 H2 D64")
+    inp = make_shape_inputs(1, 80, 2, 64, seed=7)
+    d = to_dev(inp)
+    q, k, v, g = (d[n].clone().requires_grad_(True) for n in ("q", "k", "v", "gains"))
+    out = ops.joint_attention(q, k, v, g, None, inp["scale"], inp["eps"])
+    out.backward(d["dout"])
+    o2, lse = ops.forward(d["q"], d["k"], d["v"], d["gains"], None, inp["scale"], inp["eps"])
+    dq, dk, dv, dg = ops.backward(d["q"], d["k"], d["v"], d["gains"], o2, lse, d["dout"], None, inp["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), o2)
+    assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
+    assert torch.equal(g.grad, dg)
