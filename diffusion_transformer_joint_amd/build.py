@@ -22,7 +22,10 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the code objects (the backend would otherwise form
 # them from plain float code); the host pass does not know the feature and warns, harmlessly.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # MFMA accumulators in VGPRs: the score tiles feed VALU work right away, and the
+                # AGPR form costs two copies per element plus a hazard wait
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
                 f"-I{INCLUDE}", f"-I{CSRC}"]
 

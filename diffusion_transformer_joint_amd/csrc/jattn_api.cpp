@@ -10,7 +10,7 @@
 
 namespace {
 
-using jattn::kRowsPerBlock;
+using jattn::kBwdRowsPerBlock;
 
 constexpr int kAbiVersion = 1;
 
@@ -45,8 +45,8 @@ jattn_status check_sizes(int B, int L, int H, int D) {
   if (B < 1 || L < 1 || H < 1 || D < 1) return JATTN_ERROR_INVALID_VALUE;
   if (!supported_head_dim(D)) return JATTN_ERROR_NOT_SUPPORTED;
   const int64_t lhd = (int64_t)L * H * D, bhl = (int64_t)B * H * L;
-  const int64_t items = (int64_t)B * H * ((L + kRowsPerBlock - 1) / kRowsPerBlock);
-  if (lhd >= (int64_t(1) << 31) || bhl >= (int64_t(1) << 31) || items * D >= (int64_t(1) << 31) ||
+  const int64_t items = (int64_t)B * H * ((L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock);
+  if ((int64_t)(L + 256) * H * D >= (int64_t(1) << 31) || bhl >= (int64_t(1) << 31) || items * D >= (int64_t(1) << 31) ||
       (int64_t)B * lhd >= (int64_t(1) << 40))
     return JATTN_ERROR_NOT_SUPPORTED;
   return JATTN_SUCCESS;
@@ -59,7 +59,7 @@ struct WorkspaceLayout {
 };
 
 WorkspaceLayout workspace_layout(int B, int L, int H, int D) {
-  const size_t items = (size_t)B * H * ((L + kRowsPerBlock - 1) / kRowsPerBlock);
+  const size_t items = (size_t)B * H * ((L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock);
   WorkspaceLayout w;
   w.delta = 0;
   w.part_q = round_up((size_t)B * H * L * sizeof(float), 256);
@@ -118,7 +118,7 @@ jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float*
   a.H = H;
   a.c = softmax_scale * 1.4426950408889634f;
   a.eps = eps;
-  a.nblk = (L + kRowsPerBlock - 1) / kRowsPerBlock;
+  a.nblk = (L + jattn::fwd_rows_per_block(D) - 1) / jattn::fwd_rows_per_block(D);
   a.items = B * H * a.nblk;
   return jattn::launch_fwd(D, a, stream) == hipSuccess ? JATTN_SUCCESS : JATTN_ERROR_HIP;
 }
@@ -181,7 +181,7 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
   a.scale = softmax_scale;
   a.c = softmax_scale * 1.4426950408889634f;
   a.eps = eps;
-  a.nblk = (L + kRowsPerBlock - 1) / kRowsPerBlock;
+  a.nblk = (L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock;
   a.items = B * H * a.nblk;
   return jattn::launch_bwd(D, a, stage_events, n_stage_events, stream) == hipSuccess ? JATTN_SUCCESS
                                                                                     : JATTN_ERROR_HIP;

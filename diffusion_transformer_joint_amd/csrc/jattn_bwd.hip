@@ -12,8 +12,8 @@
 //    per 32-key step S^T, dP^T (both: lane = query), dS^T in registers, dQn^T += Kn^T dS^T with Kn^T
 //    read by ds_read_b64_tr_b16. It also computes Delta for its rows (stored for the other kernel),
 //    runs the Q-side RMSNorm backward in its epilogue and writes per-workgroup dg_q partials.
-//  * dkdv kernel (key-parallel): each wave owns 32 keys (Kn and V rows in registers) and streams Q'
-//    and dO; per 32-query step S, dP (lane = key), then dV^T += dO^T P and dKn^T += Q'^T dS with the
+//  * dkdv kernel (key-parallel): each wave owns 32 keys (K rows normalised with both gains, and V
+//    rows, in registers) and streams the normalised, pre-scaled Q rows and dO; per 32-query step S, dP (lane = key), then dV^T += dO^T P and dKn^T += Q'^T dS with the
 //    transposed operands read by ds_read_b64_tr_b16. Epilogue: K-side RMSNorm backward, dk, dv and
 //    dg_k partials. Padded keys get exact zeros.
 //  * a small kernel sums the gain partials in a fixed order (deterministic dgains).
@@ -24,22 +24,45 @@
 
 namespace jattn {
 
+static_assert(kBlockRows == kBwdRowsPerBlock, "host and device block sizes differ");
+
+// LDS plan of the two kernels. Tiles read both as row fragments and transposed use the swizzled
+// layout; the dq kernel's value rows are only read as row fragments.
+// Waves per SIMD the register allocation targets: two up to D = 72, one at D = 128 (whose
+// accumulators and operand fragments need the whole register file).
 template <int D>
-struct BwdSmem {
-  static constexpr int STAGE = 2 * 2 * Dims<D>::TILE_ELEMS * 2;  // two operands, double buffered
-  static constexpr int STATS = 2 * 2 * kTile * 4;                 // -lse2 and -delta per staged row
+constexpr int bwd_waves_per_eu() { return D <= 72 ? 2 : 1; }
+
+template <int D>
+struct DqCfg {
+  using LK = Lay<D, kSwizzled>;  // normalised key rows: S (row fragments) and dQ (transposed)
+  using LV = Lay<D, kRowRead>;   // value rows: dP (row fragments)
+  static constexpr int STAGE = 2 * (LK::ELEMS + LV::ELEMS) * 2;
   static constexpr int SCRATCH = (kBlockRows + 8) * Dims<D>::DM * 4;
-  static constexpr int BYTES = (STAGE + STATS > SCRATCH ? STAGE + STATS : SCRATCH);
+  static constexpr int BYTES = STAGE > SCRATCH ? STAGE : SCRATCH;
+};
+
+template <int D>
+struct DkdvCfg {
+  using LQ = Lay<D, kSwizzled>;  // normalised, pre-scaled query rows: S and dK
+  using LO = Lay<D, kSwizzled>;  // dout rows: dP and dV
+  static constexpr int STAGE = 2 * (LQ::ELEMS + LO::ELEMS) * 2;
+  static constexpr int STATS = 2 * 2 * kTile * 4;  // -lse2 and -delta per staged row, double buffered
+  static constexpr int SCRATCH = (kBlockRows + 8) * Dims<D>::DM * 4;
+  static constexpr int BYTES = STAGE + STATS > SCRATCH ? STAGE + STATS : SCRATCH;
 };
 
 // RMSNorm backward for one wave row held in the C/D layout (lane = row; register i of tile mt
-// holds d = 32*mt + 8*(i/4) + 4*g + i%4; the other half of the row is in lane l^32). If `exists`,
-// writes the bf16 gradient row (zeros when not `valid`, i.e. a padded key). On return dxn holds the
-// dg contributions dxn * x * r (zeros for rows that are not valid).
+// holds d = 32*mt + 8*(i/4) + 4*g + i%4; the other half of the row is in lane l^32). On entry dxn
+// holds the gradient with respect to the normalised row divided by gpre[d] (the factor the MFMA
+// operands left out); `gain` is the row's own RMSNorm gain. If `exists`, writes the bf16 gradient row
+// (zeros when not `valid`, i.e. a padded key). On return dxn holds the dg contributions dxn * x * r
+// (zeros for rows that are not valid).
 template <int D>
 __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT], const uint16_t* __restrict__ xrow,
-                                                     const float* __restrict__ gain, float r, bool valid,
-                                                     bool exists, uint16_t* __restrict__ dxrow, int g) {
+                                                     const float* __restrict__ gain, const float* __restrict__ gpre,
+                                                     float r, bool valid, bool exists,
+                                                     uint16_t* __restrict__ dxrow, int g) {
   using Dm = Dims<D>;
   float x[Dm::MT][16];
   float gv[Dm::MT][16];
@@ -53,9 +76,11 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
       if (valid && d0 < D) unpack4(*reinterpret_cast<const u32x2*>(xrow + d0), xv);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[mt][j4 * 4 + e] = xv[e];
-        gv[mt][j4 * 4 + e] = d0 < D ? gain[d0 + e] : 0.f;
-        t += gv[mt][j4 * 4 + e] * dxn[mt][j4 * 4 + e] * xv[e];
+        const int i = j4 * 4 + e;
+        x[mt][i] = xv[e];
+        gv[mt][i] = d0 < D ? gain[d0 + e] : 0.f;
+        dxn[mt][i] *= d0 < D ? gpre[d0 + e] : 0.f;
+        t += gv[mt][i] * dxn[mt][i] * xv[e];
       }
     }
   t += __shfl_xor(t, 32);
@@ -83,12 +108,63 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
 
 // ------------------------------------------------------------------------------------------------
 // dq kernel: query-parallel
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
+
+// One 64-key tile: for both 32-key halves S'^T = Kr Q'^T and dP^T - Delta = V dO^T (lane = query),
+// dS^T = P * (dP - Delta) with P = exp2(S' - lse2), then dQn^T += Kr^T dS^T. The next tile is
+// staged and the one after it fetched inside the same body. MASKED: keys at or past n are seeded
+// with -inf (P = 0).
+template <int D, bool MASKED>
+__device__ __forceinline__ void dq_tile(const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn,
+                                        TileRegs<D>& tk, TileRegs<D>& tv, __amdgpu_buffer_rsrc_t rk,
+                                        __amdgpu_buffer_rsrc_t rv, int rs, const bf16x8 (&qf)[Dims<D>::KS],
+                                        const bf16x8 (&dof)[Dims<D>::KS], const f32x16& cs, const f32x16& cp,
+                                        f32x16 (&acc)[Dims<D>::MT], int key0, int n, float eps, int tid) {
   using Dm = Dims<D>;
-  __shared__ __attribute__((aligned(16))) char smem[BwdSmem<D>::BYTES];
+  using LK = typename DqCfg<D>::LK;
+  using LV = typename DqCfg<D>::LV;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f32x16 s = cs, dp = cp;
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + h * 32 + (i >> 2) * 8 + g * 4 + (i & 3) >= n) s[i] = -INFINITY;
+    }
+#pragma unroll
+    for (int ks = 0; ks < Dm::KS; ++ks) {
+      s = mfma(lds_row_frag<LK>(kt, h * 32 + l32, ks * 16 + g * 8), qf[ks], s);
+      dp = mfma(lds_row_frag<LV>(vt, h * 32 + l32, ks * 16 + g * 8), dof[ks], dp);
+    }
+    if (h == 0) {
+      tile_store_rmsnorm<D, LK>(tk, kn, 1.f, eps, key0 + kTile, n, tid);
+      tile_store_raw<D, LV>(tv, vn, tid);
+    }
+    float ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * dp[i];
+    const bf16x8 f0 = to_bf16x8(ds), f1 = to_bf16x8(ds + 8);
+#pragma unroll
+    for (int mt = 0; mt < Dm::MT; ++mt) {
+      acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32, mt * 32, lane), f0, acc[mt]);
+      acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32 + 16, mt * 32, lane), f1, acc[mt]);
+    }
+  }
+  tile_load_buf<D>(tk, rk, rs, key0 + 2 * kTile, tid);
+  tile_load_buf<D>(tv, rv, rs, key0 + 2 * kTile, tid);
+  __builtin_amdgcn_iglp_opt(2);
+  __syncthreads();
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
+void bwd_dq_kernel(BwdArgs a) {
+  using Dm = Dims<D>;
+  using LK = typename DqCfg<D>::LK;
+  using LV = typename DqCfg<D>::LV;
+  __shared__ __attribute__((aligned(16))) char smem[DqCfg<D>::BYTES];
   __bf16* sk = reinterpret_cast<__bf16*>(smem);
-  __bf16* sv = sk + 2 * Dm::TILE_ELEMS;
+  __bf16* sv = sk + 2 * LK::ELEMS;
 
   int bh, blk, item;
   if (!map_item(a.items, a.nblk, bh, blk, item)) return;
@@ -99,9 +175,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   const int rs = H * D;
   const size_t base = ((size_t)b * L * H + (bh - b * H)) * D;
 
-  zero_pad_columns<D>(sk, 4, tid);
-  float gk[Dm::CPT][8];
-  stage_gains<D>(gk, a.gains + D, 1.f, tid);
+  zero_pad_columns<D, LK>(sk, 2, tid);
+  zero_pad_columns<D, LV>(sv, 2, tid);
 
   const int qrow = blk * kBlockRows + wave * kWaveRows + l32;
   const bool qvalid = qrow < L;
@@ -111,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   {
     float x[Dm::KS][8];
     load_row_chunks<D>(x, a.q + roff, qvalid, g);
-    rq = rmsnorm_row_frags<D>(qf, x, a.gains, a.c, a.eps, qvalid, g);
+    rq = rmsnorm_row_frags<D>(qf, x, a.gains, a.gains + D, a.c, a.eps, qvalid, g);
   }
   load_row_frags_raw<D>(dof, a.dout + roff, qvalid, g);
   float delta = 0.f;
@@ -138,69 +213,167 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
 
-  const uint16_t* kb = a.k + base;
-  const uint16_t* vb = a.v + base;
-  const int ntiles = (n + kTile - 1) / kTile;
-  TileRegs<D> tk, tv;
+  const int ntiles = (n + kTile - 1) / kTile, nfull = n / kTile;
   if (ntiles > 0) {
-    tile_load<D>(tk, kb, rs, 0, n, tid);
-    tile_load<D>(tv, vb, rs, 0, n, tid);
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    __bf16* kt = sk + (t & 1) * Dm::TILE_ELEMS;
-    __bf16* vt = sv + (t & 1) * Dm::TILE_ELEMS;
-    tile_store_rmsnorm<D>(tk, kt, gk, a.eps, t * kTile, n, tid);
-    tile_store_raw<D>(tv, vt, tid);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + base, rows_bytes<D>(n, rs));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + base, rows_bytes<D>(n, rs));
+    TileRegs<D> tk, tv;
+    tile_load_buf<D>(tk, rk, rs, 0, tid);
+    tile_load_buf<D>(tv, rv, rs, 0, tid);
+    tile_store_rmsnorm<D, LK>(tk, sk, 1.f, a.eps, 0, n, tid);
+    tile_store_raw<D, LV>(tv, sv, tid);
+    tile_load_buf<D>(tk, rk, rs, kTile, tid);
+    tile_load_buf<D>(tv, rv, rs, kTile, tid);
     __syncthreads();
-    if (t + 1 < ntiles) {
-      tile_load<D>(tk, kb, rs, (t + 1) * kTile, n, tid);
-      tile_load<D>(tv, vb, rs, (t + 1) * kTile, n, tid);
+    for (int t = 0; t < nfull; ++t) {
+      const int ck = (t & 1) * LK::ELEMS, nk = LK::ELEMS - ck, cv = (t & 1) * LV::ELEMS, nv = LV::ELEMS - cv;
+      dq_tile<D, false>(sk + ck, sv + cv, sk + nk, sv + nv, tk, tv, rk, rv, rs, qf, dof, cs, cp, acc, t * kTile, n,
+                        a.eps, tid);
     }
-#pragma unroll
-    for (int sb = 0; sb < kTile / 32; ++sb) {
-      const int key0 = t * kTile + sb * 32;
-      if (key0 >= n) break;
-      f32x16 s = cs, dp = cp;
-      const __bf16* kr = kt + (sb * 32 + l32) * Dm::PITCH + g * 8;
-      const __bf16* vr = vt + (sb * 32 + l32) * Dm::PITCH + g * 8;
-#pragma unroll
-      for (int ks = 0; ks < Dm::KS; ++ks) s = mfma(lds_row_frag(kr + ks * 16), qf[ks], s);
-#pragma unroll
-      for (int ks = 0; ks < Dm::KS; ++ks) dp = mfma(lds_row_frag(vr + ks * 16), dof[ks], dp);
-      float ds[16];
-      const bool tail = key0 + 32 > n;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(s[i]);
-        if (tail && key0 + (i >> 2) * 8 + g * 4 + (i & 3) >= n) p = 0.f;
-        ds[i] = p * dp[i];
-      }
-      const bf16x8 f0 = to_bf16x8(ds), f1 = to_bf16x8(ds + 8);
-#pragma unroll
-      for (int mt = 0; mt < Dm::MT; ++mt) {
-        acc[mt] = mfma(lds_tr_frag(kt, Dm::PITCH, sb * 32, mt * 32, lane), f0, acc[mt]);
-        acc[mt] = mfma(lds_tr_frag(kt, Dm::PITCH, sb * 32 + 16, mt * 32, lane), f1, acc[mt]);
-      }
+    if (ntiles > nfull) {
+      const int ck = (nfull & 1) * LK::ELEMS, nk = LK::ELEMS - ck, cv = (nfull & 1) * LV::ELEMS,
+                nv = LV::ELEMS - cv;
+      dq_tile<D, true>(sk + ck, sv + cv, sk + nk, sv + nv, tk, tv, rk, rv, rs, qf, dof, cs, cp, acc, nfull * kTile,
+                       n, a.eps, tid);
     }
   }
 
+  // dQn = scale * g_k * (dS Kr): the staged key rows carry no gain
 #pragma unroll
-  for (int mt = 0; mt < Dm::MT; ++mt) acc[mt] *= a.scale;  // dQn
-  rmsnorm_backward_row<D>(acc, a.q + roff, a.gains, rq, qvalid, qvalid, a.dq + roff, g);
+  for (int mt = 0; mt < Dm::MT; ++mt) acc[mt] *= a.scale;
+  rmsnorm_backward_row<D>(acc, a.q + roff, a.gains, a.gains + D, rq, qvalid, qvalid, a.dq + roff, g);
   __syncthreads();  // all waves are done with the staged tiles before the scratch reuse
   block_column_sums<D>(acc, reinterpret_cast<float*>(smem), a.part_q + (size_t)item * D, tid);
 }
 
 // ------------------------------------------------------------------------------------------------
 // dkdv kernel: key-parallel
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
+
+// Stage the row statistics of query tile t: -lse2 (-inf past L) and -Delta, one row per thread of
+// the first wave.
+__device__ __forceinline__ void stats_load(float& sl, float& sd, __amdgpu_buffer_rsrc_t rl,
+                                           __amdgpu_buffer_rsrc_t rd, int q0, int L, int tid) {
+  if (tid < kTile) {
+    const int qi = q0 + tid;
+    // (the b32 buffer load returns the raw word as an integer)
+    const float l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)qi * 4u, 0, 0));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)qi * 4u, 0, 0));
+    sl = qi < L ? -l * kLog2e : -INFINITY;
+    sd = -d;
+  }
+}
+
+// One 64-query tile: for both 32-query halves S' = Q'' Kf^T and dP - Delta = dO V^T (lane = key),
+// P = exp2(S' - lse2), dS = P * (dP - Delta), then dV^T += dO^T P and dKn^T += Q''^T dS.
+// KMASK: this wave holds keys at or past n, whose P is forced to zero.
+template <int D, bool KMASK>
+__device__ __forceinline__ void dkdv_tile(const __bf16* qt, const __bf16* ot, const float* sl, const float* sd,
+                                          __bf16* qn, __bf16* on, float* sln, float* sdn, TileRegs<D>& tq,
+                                          TileRegs<D>& to, float& stl, float& std_, __amdgpu_buffer_rsrc_t rq,
+                                          __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
+                                          __amdgpu_buffer_rsrc_t rd, int rs, const bf16x8 (&kf)[Dims<D>::KS],
+                                          const bf16x8 (&vf)[Dims<D>::KS], f32x16 (&dva)[Dims<D>::MT],
+                                          f32x16 (&dka)[Dims<D>::MT], bool kvalid, int q0, int L, float c,
+                                          float eps, int tid) {
   using Dm = Dims<D>;
-  __shared__ __attribute__((aligned(16))) char smem[BwdSmem<D>::BYTES];
+  using LQ = typename DkdvCfg<D>::LQ;
+  using LO = typename DkdvCfg<D>::LO;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f32x16 s, dp;
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + h * 32 + j4 * 8 + g * 4);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sd + h * 32 + j4 * 8 + g * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[j4 * 4 + e] = l4[e];
+        dp[j4 * 4 + e] = d4[e];
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < Dm::KS; ++ks) {
+      s = mfma(lds_row_frag<LQ>(qt, h * 32 + l32, ks * 16 + g * 8), kf[ks], s);
+      dp = mfma(lds_row_frag<LO>(ot, h * 32 + l32, ks * 16 + g * 8), vf[ks], dp);
+    }
+    if (h == 0) {
+      tile_store_rmsnorm<D, LQ>(tq, qn, c, eps, q0 + kTile, L, tid);
+      tile_store_raw<D, LO>(to, on, tid);
+      if (tid < kTile) {
+        sln[tid] = stl;
+        sdn[tid] = std_;
+      }
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = fast_exp2(s[i]);
+      if constexpr (KMASK) p[i] = kvalid ? p[i] : 0.f;
+      ds[i] = p[i] * dp[i];
+    }
+    const bf16x8 pf0 = to_bf16x8(p), pf1 = to_bf16x8(p + 8);
+    const bf16x8 df0 = to_bf16x8(ds), df1 = to_bf16x8(ds + 8);
+#pragma unroll
+    for (int mt = 0; mt < Dm::MT; ++mt) {
+      dva[mt] = mfma(lds_tr_frag<LO>(ot, h * 32, mt * 32, lane), pf0, dva[mt]);
+      dva[mt] = mfma(lds_tr_frag<LO>(ot, h * 32 + 16, mt * 32, lane), pf1, dva[mt]);
+      dka[mt] = mfma(lds_tr_frag<LQ>(qt, h * 32, mt * 32, lane), df0, dka[mt]);
+      dka[mt] = mfma(lds_tr_frag<LQ>(qt, h * 32 + 16, mt * 32, lane), df1, dka[mt]);
+    }
+  }
+  tile_load_buf<D>(tq, rq, rs, q0 + 2 * kTile, tid);
+  tile_load_buf<D>(to, ro, rs, q0 + 2 * kTile, tid);
+  stats_load(stl, std_, rl, rd, q0 + 2 * kTile, L, tid);
+  __builtin_amdgcn_iglp_opt(2);
+  __syncthreads();
+}
+
+template <int D, bool KMASK>
+__device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t base, int bh, int rs,
+                                          const bf16x8 (&kf)[Dims<D>::KS], const bf16x8 (&vf)[Dims<D>::KS],
+                                          f32x16 (&dva)[Dims<D>::MT], f32x16 (&dka)[Dims<D>::MT], bool kvalid,
+                                          int tid) {
+  using LQ = typename DkdvCfg<D>::LQ;
+  using LO = typename DkdvCfg<D>::LO;
   __bf16* sq = reinterpret_cast<__bf16*>(smem);
-  __bf16* sdo = sq + 2 * Dm::TILE_ELEMS;
-  float* slse = reinterpret_cast<float*>(smem + BwdSmem<D>::STAGE);  // [2][kTile]: -lse2
-  float* sdel = slse + 2 * kTile;                                      // [2][kTile]: -delta
+  __bf16* so = sq + 2 * LQ::ELEMS;
+  float* sl = reinterpret_cast<float*>(smem + DkdvCfg<D>::STAGE);  // [2][kTile]
+  float* sd = sl + 2 * kTile;                                        // [2][kTile]
+  const int L = a.L;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + base, rows_bytes<D>(L, rs));
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.dout + base, rows_bytes<D>(L, rs));
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + (size_t)bh * L, (uint32_t)L * 4u);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + (size_t)bh * L, (uint32_t)L * 4u);
+  TileRegs<D> tq, to;
+  float stl = 0.f, std_ = 0.f;
+  tile_load_buf<D>(tq, rq, rs, 0, tid);
+  tile_load_buf<D>(to, ro, rs, 0, tid);
+  stats_load(stl, std_, rl, rd, 0, L, tid);
+  tile_store_rmsnorm<D, LQ>(tq, sq, a.c, a.eps, 0, L, tid);
+  tile_store_raw<D, LO>(to, so, tid);
+  if (tid < kTile) {
+    sl[tid] = stl;
+    sd[tid] = std_;
+  }
+  tile_load_buf<D>(tq, rq, rs, kTile, tid);
+  tile_load_buf<D>(to, ro, rs, kTile, tid);
+  stats_load(stl, std_, rl, rd, kTile, L, tid);
+  __syncthreads();
+  const int ntiles = (L + kTile - 1) / kTile;
+  for (int t = 0; t < ntiles; ++t) {
+    const int cq = (t & 1) * LQ::ELEMS, nq = LQ::ELEMS - cq, co = (t & 1) * LO::ELEMS, no = LO::ELEMS - co;
+    const int cs = (t & 1) * kTile, ns = kTile - cs;
+    dkdv_tile<D, KMASK>(sq + cq, so + co, sl + cs, sd + cs, sq + nq, so + no, sl + ns, sd + ns, tq, to, stl, std_,
+                        rq, ro, rl, rd, rs, kf, vf, dva, dka, kvalid, t * kTile, L, a.c, a.eps, tid);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
+void bwd_dkdv_kernel(BwdArgs a) {
+  using Dm = Dims<D>;
+  __shared__ __attribute__((aligned(16))) char smem[DkdvCfg<D>::BYTES];
 
   int bh, blk, item;
   if (!map_item(a.items, a.nblk, bh, blk, item)) return;
@@ -229,19 +402,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
     return;
   }
 
-  zero_pad_columns<D>(sq, 4, tid);
-  float gq[Dm::CPT][8];
-  stage_gains<D>(gq, a.gains, a.c, tid);
+  zero_pad_columns<D, typename DkdvCfg<D>::LQ>(reinterpret_cast<__bf16*>(smem), 4, tid);
 
   bf16x8 kf[Dm::KS], vf[Dm::KS];
   float rk;
   {
     float x[Dm::KS][8];
     load_row_chunks<D>(x, a.k + roff, kvalid, g);
-    rk = rmsnorm_row_frags<D>(kf, x, a.gains + D, 1.f, a.eps, kvalid, g);
+    rk = rmsnorm_row_frags<D>(kf, x, a.gains, a.gains + D, 1.f, a.eps, kvalid, g);  // k r_k g_q g_k
   }
   load_row_frags_raw<D>(vf, a.v + roff, kvalid, g);
-  const bool wave_live = blk * kBlockRows + wave * kWaveRows < n;
 
   f32x16 dva[Dm::MT], dka[Dm::MT];
 #pragma unroll
@@ -251,79 +421,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
       dva[mt][i] = 0.f;
       dka[mt][i] = 0.f;
     }
-
-  const uint16_t* qb = a.q + base;
-  const uint16_t* ob = a.dout + base;
-  const float* lse_bh = a.lse + (size_t)bh * L;
-  const float* del_bh = a.delta + (size_t)bh * L;
-  const int ntiles = (L + kTile - 1) / kTile;
-  TileRegs<D> tq, to;
-  float st_lse = 0.f, st_del = 0.f;
-  auto load_stats = [&](int t) {
-    if (tid < kTile) {
-      const int qi = t * kTile + tid;
-      st_lse = qi < L ? -lse_bh[qi] * kLog2e : -INFINITY;
-      st_del = qi < L ? -del_bh[qi] : 0.f;
-    }
-  };
-  tile_load<D>(tq, qb, rs, 0, L, tid);
-  tile_load<D>(to, ob, rs, 0, L, tid);
-  load_stats(0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    __bf16* qt = sq + buf * Dm::TILE_ELEMS;
-    __bf16* ot = sdo + buf * Dm::TILE_ELEMS;
-    tile_store_rmsnorm<D>(tq, qt, gq, a.eps, t * kTile, L, tid);
-    tile_store_raw<D>(to, ot, tid);
-    if (tid < kTile) {
-      slse[buf * kTile + tid] = st_lse;
-      sdel[buf * kTile + tid] = st_del;
-    }
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      tile_load<D>(tq, qb, rs, (t + 1) * kTile, L, tid);
-      tile_load<D>(to, ob, rs, (t + 1) * kTile, L, tid);
-      load_stats(t + 1);
-    }
-    if (!wave_live) continue;
-#pragma unroll
-    for (int sb = 0; sb < kTile / 32; ++sb) {
-      const int q0 = t * kTile + sb * 32;
-      if (q0 >= L) break;
-      f32x16 s, dp;
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(slse + buf * kTile + sb * 32 + j4 * 8 + g * 4);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sdel + buf * kTile + sb * 32 + j4 * 8 + g * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s[j4 * 4 + e] = l4[e];
-          dp[j4 * 4 + e] = d4[e];
-        }
-      }
-      const __bf16* qr = qt + (sb * 32 + l32) * Dm::PITCH + g * 8;
-      const __bf16* orr = ot + (sb * 32 + l32) * Dm::PITCH + g * 8;
-#pragma unroll
-      for (int ks = 0; ks < Dm::KS; ++ks) s = mfma(lds_row_frag(qr + ks * 16), kf[ks], s);
-#pragma unroll
-      for (int ks = 0; ks < Dm::KS; ++ks) dp = mfma(lds_row_frag(orr + ks * 16), vf[ks], dp);
-      float p[16], ds[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = kvalid ? fast_exp2(s[i]) : 0.f;
-        ds[i] = p[i] * dp[i];
-      }
-      const bf16x8 pf0 = to_bf16x8(p), pf1 = to_bf16x8(p + 8);
-      const bf16x8 df0 = to_bf16x8(ds), df1 = to_bf16x8(ds + 8);
-#pragma unroll
-      for (int mt = 0; mt < Dm::MT; ++mt) {
-        dva[mt] = mfma(lds_tr_frag(ot, Dm::PITCH, sb * 32, mt * 32, lane), pf0, dva[mt]);
-        dva[mt] = mfma(lds_tr_frag(ot, Dm::PITCH, sb * 32 + 16, mt * 32, lane), pf1, dva[mt]);
-        dka[mt] = mfma(lds_tr_frag(qt, Dm::PITCH, sb * 32, mt * 32, lane), df0, dka[mt]);
-        dka[mt] = mfma(lds_tr_frag(qt, Dm::PITCH, sb * 32 + 16, mt * 32, lane), df1, dka[mt]);
-      }
-    }
-  }
+  // waves whose 32 keys are all valid skip the key mask
+  if (blk * kBlockRows + (wave + 1) * kWaveRows <= n)
+    dkdv_loop<D, false>(a, smem, base, bh, rs, kf, vf, dva, dka, kvalid, tid);
+  else
+    dkdv_loop<D, true>(a, smem, base, bh, rs, kf, vf, dva, dka, kvalid, tid);
 
   // dv (zeros at padded keys)
   if (kin) {
@@ -340,11 +442,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
   }
-  // dKn = scale * dS^T Qn = ln(2) * dS^T Q'   (Q' carries scale * log2(e))
+  // dKn = scale * dS^T Qn = ln(2) * g_q * dS^T Q''  (the staged query rows carry scale * log2(e), no gain)
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) dka[mt] *= kLn2;
   if (kin) {
-    rmsnorm_backward_row<D>(dka, a.k + roff, a.gains + D, rk, kvalid, true, a.dk + roff, g);
+    rmsnorm_backward_row<D>(dka, a.k + roff, a.gains + D, a.gains, rk, kvalid, true, a.dk + roff, g);
   } else {
 #pragma unroll
     for (int mt = 0; mt < Dm::MT; ++mt)

@@ -47,13 +47,49 @@ struct Dims {
   static constexpr int KS = DK / 16;                  // MFMA k-steps over d
   static constexpr int DM = (D + 31) / 32 * 32;       // output width (32-row MFMA tiles over d)
   static constexpr int MT = DM / 32;                  // MFMA tiles over d
-  static constexpr int PITCH = DM + 8;                // LDS row pitch in bf16 (16-byte skew)
   static constexpr int TPR = NCH >= 8 ? 8 : NCH;      // staging threads per row
   static constexpr int CPT = (NCH + TPR - 1) / TPR;   // staging chunks per thread
   static constexpr int RPP = kThreads / TPR;          // rows staged per pass
   static constexpr int PASSES = kTile / RPP;          // passes per tile
-  static constexpr int TILE_ELEMS = kTile * PITCH;
   static_assert((TPR & (TPR - 1)) == 0 && kTile % RPP == 0, "staging layout");
+};
+
+
+// ---------------------------------------------------------------------------------------------
+// LDS tile layouts (kTile rows of up to DM bf16 columns). Each knows where logical (row, column)
+// lives; columns [D, DM) of the padded layouts are zero. Bank model: 64 four-byte banks; a b128
+// read is served 16 lanes at a time and a b64 transpose read 32 lanes at a time.
+//
+// kRowRead  - rows read as 16-byte fragments (lane = row, ds_read_b128). Pitch DM + 8: 16 rows at
+//             one column hit 16 different 4-bank groups.
+// kTrRead   - rows read by ds_read_b64_tr_b16 (32 lanes = 4 rows x 64 bytes). Pitch chosen so that
+//             4 consecutive rows start 16 banks apart: 64 mod 256 bytes or 192 mod 256 bytes.
+// kSwizzled - read both ways (D = 64 and 128 only; other head dims fall back to kRowRead). Pitch DM,
+//             16-byte chunk c of row r stored at chunk c ^ f(r): f gives 16 consecutive rows distinct
+//             (row parity, chunk) bank groups for b128 reads, and 4 consecutive rows disjoint 4-chunk
+//             blocks for transpose reads.
+enum LayoutKind { kRowRead = 0, kTrRead = 1, kSwizzled = 2 };
+
+template <int D, int KIND>
+struct Lay {
+  using Dm = Dims<D>;
+  static constexpr bool SWZ = KIND == kSwizzled && (D == 64 || D == 128);
+  static constexpr int tr_pitch() {
+    int p = Dm::DM * 2;  // bytes
+    while (p % 256 != 64 && p % 256 != 192) p += 64;
+    return p / 2;
+  }
+  static constexpr int PITCH = SWZ ? Dm::DM : (KIND == kTrRead ? tr_pitch() : Dm::DM + 8);
+  static constexpr int ELEMS = kTile * PITCH;
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (!SWZ) return 0;
+    else if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return ((r & 3) << 2) | ((r >> 2) & 3);
+  }
+  // element offset of logical (row r, column col); col % 4 == 0
+  __device__ static __forceinline__ int off(int r, int col) {
+    return r * PITCH + (((col >> 3) ^ swz(r)) << 3) + (col & 7);
+  }
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -124,24 +160,25 @@ __device__ __forceinline__ float wave_max(float x) {
 // ---------------------------------------------------------------------------------------------
 // LDS fragment reads
 
-// B/A operand fragment of 8 contiguous bf16 from a row-major LDS tile.
-__device__ __forceinline__ bf16x8 lds_row_frag(const __bf16* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+// Operand fragment of 8 contiguous bf16 (columns col .. col+7, col % 8 == 0) of one LDS tile row.
+template <class LY>
+__device__ __forceinline__ bf16x8 lds_row_frag(const __bf16* tile, int r, int col) {
+  return *reinterpret_cast<const bf16x8*>(tile + LY::off(r, col));
 }
 
-// Transposed operand fragment from a row-major LDS tile T[row][col] (pitch in elements).
+// Transposed operand fragment from an LDS tile T[row][col].
 // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element i%4 of the 8-byte chunk
 // addressed by lane 4*t + i/4, for t = 0..3. If lane j of the group addresses T[r0 + j/4][c0 + 4*(j%4)],
 // lane i receives T[r0 + t][c0 + i] for t = 0..3: four consecutive rows of one column.
 // Lane l of the wave gets column c = col0 + l%32 and rows
 //   row0 + 4*(l/32) + [0..3]  (elements 0..3)  and  row0 + 8 + 4*(l/32) + [0..3]  (elements 4..7),
 // the contraction-slot order of a C/D tile reused as a B operand (see the file header).
-__device__ __forceinline__ bf16x8 lds_tr_frag(const __bf16* tile, int pitch, int row0, int col0,
-                                              int lane) {
-  const __bf16* p = tile + (row0 + 4 * (lane >> 5) + ((lane & 15) >> 2)) * pitch + col0 +
-                    ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JATTN_LDS i16x4*)(p));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JATTN_LDS i16x4*)(p + 8 * pitch));
+template <class LY>
+__device__ __forceinline__ bf16x8 lds_tr_frag(const __bf16* tile, int row0, int col0, int lane) {
+  const int r = row0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = col0 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JATTN_LDS i16x4*)(tile + LY::off(r, col)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JATTN_LDS i16x4*)(tile + LY::off(r + 8, col)));
   const bf16x4 a = __builtin_bit_cast(bf16x4, lo);
   const bf16x4 b = __builtin_bit_cast(bf16x4, hi);
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -177,8 +214,41 @@ __device__ __forceinline__ void tile_load(TileRegs<D>& t, const uint16_t* __rest
   }
 }
 
-// Store the tile unchanged.
+// Buffer resource over `nbytes` bytes from `base` (raw buffer, no stride). Loads at byte offsets at or
+// past nbytes return zeros, so tile loads need no bounds branches.
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer descriptor word 3: 32-bit data, no swizzle
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, kBufferWord3);
+}
+
+// Bytes covering rows [0, nrows) of a [rows][D] bf16 view with row stride rs elements.
 template <int D>
+__device__ __forceinline__ uint32_t rows_bytes(int nrows, int rs) {
+  return nrows > 0 ? (uint32_t)((nrows - 1) * rs + D) * 2u : 0u;
+}
+
+// Load rows [row0, row0 + kTile) through a buffer resource that covers the valid rows only; rows
+// outside it read as zeros.
+template <int D>
+__device__ __forceinline__ void tile_load_buf(TileRegs<D>& t, __amdgpu_buffer_rsrc_t rsrc, int rs, int row0,
+                                              int tid) {
+  using Dm = Dims<D>;
+  const int rr = tid / Dm::TPR, cc = tid % Dm::TPR;
+#pragma unroll
+  for (int p = 0; p < Dm::PASSES; ++p) {
+    const uint32_t row = (uint32_t)(row0 + p * Dm::RPP + rr);
+#pragma unroll
+    for (int j = 0; j < Dm::CPT; ++j) {
+      const uint32_t c = (uint32_t)(cc + j * Dm::TPR);
+      // chunks past the row (head dims that are not a multiple of 64) read as zeros
+      const uint32_t off = c < (uint32_t)Dm::NCH ? (row * (uint32_t)rs + c * 8u) * 2u : 0xFFFFFFF0u;
+      t.r[p][j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+    }
+  }
+}
+
+// Store the tile unchanged.
+template <int D, class LY>
 __device__ __forceinline__ void tile_store_raw(const TileRegs<D>& t, __bf16* lds, int tid) {
   using Dm = Dims<D>;
   const int rr = tid / Dm::TPR, cc = tid % Dm::TPR;
@@ -188,69 +258,74 @@ __device__ __forceinline__ void tile_store_raw(const TileRegs<D>& t, __bf16* lds
     for (int j = 0; j < Dm::CPT; ++j) {
       const int c = cc + j * Dm::TPR;
       if (c < Dm::NCH)
-        *reinterpret_cast<u32x4*>(lds + (p * Dm::RPP + rr) * Dm::PITCH + c * 8) = t.r[p][j];
+        *reinterpret_cast<u32x4*>(lds + LY::off(p * Dm::RPP + rr, c * 8)) = t.r[p][j];
     }
 }
 
-// Per-thread gain multipliers for the staged chunks: gm[j][e] = mul * gain[(cc + j*TPR)*8 + e].
-template <int D>
-__device__ __forceinline__ void stage_gains(float (&gm)[Dims<D>::CPT][8], const float* __restrict__ gain,
-                                            float mul, int tid) {
-  using Dm = Dims<D>;
-  const int cc = tid % Dm::TPR;
-#pragma unroll
-  for (int j = 0; j < Dm::CPT; ++j) {
-    const int c = cc + j * Dm::TPR;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) gm[j][e] = c < Dm::NCH ? mul * gain[c * 8 + e] : 0.f;
-  }
+// Sum over each aligned group of N lanes (N = 4 or 8) with DPP lane moves: no LDS traffic.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 4 || N == 8, "group size");
+  // quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2), row_half_mirror (lane i <-> 7-i)
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  if constexpr (N == 8)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  return x;
 }
 
-// Store the tile RMS-normalised over D: x * rsqrt(mean(x^2) + eps) * gm. Rows at or past `nrows`
+// Sum of squares of the 8 bf16 values in a 16-byte chunk, accumulated in fp32 with v_dot2c_f32_bf16.
+__device__ __forceinline__ float sumsq8(const u32x4& u, float acc) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = u[j];
+    const bf16x2 v = __builtin_bit_cast(bf16x2, w);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+  }
+  return acc;
+}
+
+// Store the tile with every row RMS-normalised over D and multiplied by `mul`:
+// x * rsqrt(mean(x^2) + eps) * mul (gains are applied elsewhere). Rows at or past `nrows`
 // (relative row index >= nrows - row0) are written as zeros.
-template <int D>
-__device__ __forceinline__ void tile_store_rmsnorm(const TileRegs<D>& t, __bf16* lds,
-                                                   const float (&gm)[Dims<D>::CPT][8], float eps,
+template <int D, class LY>
+__device__ __forceinline__ void tile_store_rmsnorm(const TileRegs<D>& t, __bf16* lds, float mul, float eps,
                                                    int row0, int nrows, int tid) {
   using Dm = Dims<D>;
   const int rr = tid / Dm::TPR, cc = tid % Dm::TPR;
 #pragma unroll
   for (int p = 0; p < Dm::PASSES; ++p) {
-    float x[Dm::CPT][8];
     float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < Dm::CPT; ++j) {
-      unpack8(t.r[p][j], x[j]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x[j][e] * x[j][e];
-    }
-#pragma unroll
-    for (int m = 1; m < Dm::TPR; m <<= 1) ss += __shfl_xor(ss, m);
+    for (int j = 0; j < Dm::CPT; ++j) ss = sumsq8(t.r[p][j], ss);
+    ss = group_sum<Dm::TPR>(ss);
     const bool valid = row0 + p * Dm::RPP + rr < nrows;
-    const float r = valid ? rsqrtf(ss * (1.0f / D) + eps) : 0.f;
+    const float r = valid ? rsqrtf(ss * (1.0f / D) + eps) * mul : 0.f;
 #pragma unroll
     for (int j = 0; j < Dm::CPT; ++j) {
       const int c = cc + j * Dm::TPR;
       if (c < Dm::NCH) {
-        float y[8];
+        float x[8];
+        unpack8(t.r[p][j], x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = x[j][e] * r * gm[j][e];
-        *reinterpret_cast<bf16x8*>(lds + (p * Dm::RPP + rr) * Dm::PITCH + c * 8) = to_bf16x8(y);
+        for (int e = 0; e < 8; ++e) x[e] *= r;
+        *reinterpret_cast<bf16x8*>(lds + LY::off(p * Dm::RPP + rr, c * 8)) = to_bf16x8(x);
       }
     }
   }
 }
 
-// Zero the columns [D, DM) of `ntiles` LDS tiles (only head dims that are not a multiple of 32
-// have them). Staging never writes those columns, so this is done once per kernel.
-template <int D>
+// Zero the columns [D, DM) of `ntiles` consecutive LDS tiles of layout LY (only head dims that are
+// not a multiple of 32 have them). Staging never writes those columns, so this is done once.
+template <int D, class LY>
 __device__ __forceinline__ void zero_pad_columns(__bf16* lds, int ntiles, int tid) {
   using Dm = Dims<D>;
   if constexpr (Dm::DM > D) {
     constexpr int W = Dm::DM - D;  // multiple of 8
     for (int idx = tid; idx < ntiles * kTile * (W / 8); idx += kThreads) {
       const int row = idx / (W / 8), c = idx % (W / 8);
-      *reinterpret_cast<u32x4*>(lds + row * Dm::PITCH + D + c * 8) = (u32x4){0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(lds + (row / kTile) * LY::ELEMS + LY::off(row % kTile, D + c * 8)) =
+          (u32x4){0u, 0u, 0u, 0u};
     }
   }
 }
@@ -288,11 +363,12 @@ __device__ __forceinline__ void load_row_frags_raw(bf16x8 (&f)[Dims<D>::KS],
 }
 
 // RMS-normalise a wave row held as in load_row_chunks (the other half of the row sits in lane l^32)
-// and round x * r * gain * mul to bf16 fragments. Returns r (0 for invalid rows).
+// and round x * r * mul * ga[d] * gb[d] to bf16 fragments (gb may be null). Returns r (0 for
+// invalid rows).
 template <int D>
 __device__ __forceinline__ float rmsnorm_row_frags(bf16x8 (&f)[Dims<D>::KS], const float (&x)[Dims<D>::KS][8],
-                                                   const float* __restrict__ gain, float mul, float eps,
-                                                   bool valid, int g) {
+                                                   const float* __restrict__ ga, const float* __restrict__ gb,
+                                                   float mul, float eps, bool valid, int g) {
   using Dm = Dims<D>;
   float ss = 0.f;
 #pragma unroll
@@ -306,7 +382,10 @@ __device__ __forceinline__ float rmsnorm_row_frags(bf16x8 (&f)[Dims<D>::KS], con
     const int c = 2 * ks + g;
     float y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = c < Dm::NCH ? x[ks][e] * r * (mul * gain[c * 8 + e]) : 0.f;
+    for (int e = 0; e < 8; ++e) {
+      const int d = c * 8 + e;
+      y[e] = c < Dm::NCH ? x[ks][e] * r * mul * ga[d] * (gb ? gb[d] : 1.f) : 0.f;
+    }
     f[ks] = to_bf16x8(y);
   }
   return r;

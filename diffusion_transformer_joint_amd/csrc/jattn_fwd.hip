@@ -6,120 +6,188 @@
 // this kernel never materialises):
 //   out_i = sum_j softmax_j(scale * <Qn_i, Kn_j>) v_j over valid keys j < n_b,  lse_i = log sum_j exp(.)
 //
-// One workgroup = 4 waves = 128 consecutive queries of one (batch, head) pair; each wave owns 32
-// queries and streams all valid keys in tiles of 64 through LDS (double buffered, one barrier per
-// tile). Per 32-key step a wave computes S^T = Kn Q'^T (4..8 MFMA over d, result: lane = query),
-// turns it into P in registers, and accumulates O^T += V^T P^T with V^T read by ds_read_b64_tr_b16
-// straight from the row-major V tile. Q' = bf16(q * r_q * g_q * scale * log2(e)) lives in registers
-// for the whole loop, so scores come out in log2 units.
+// One workgroup = 4 waves; each wave owns QT independent tiles of 32 queries (QT = 2 for D <= 64)
+// and streams all valid keys of the (batch, head) pair in tiles of 64 through LDS (double
+// buffered, one barrier per tile). Per 32-key half and query tile a wave computes S'^T = Kr Q'^T
+// (the result has the query on the lane), turns it into P in registers, and accumulates
+// O^T += V^T P^T with V^T read by ds_read_b64_tr_b16 straight from the row-major V tile. Each K and V
+// fragment read from LDS feeds QT MFMAs, and the QT query tiles give every wave independent MFMA
+// work to overlap with the softmax of the other tile.
 //
-// Softmax shift. QK-RMSNorm bounds every score: ||Kn_j|| <= sqrt(D) * max|g_k| for any key, so
-// |S'_ij| <= B_i = ||Q'_i|| * sqrt(D) * max|g_k| (plus a margin for bf16 rounding). When every row of
-// the workgroup has B_i <= 48 (log2 units), the kernel uses the fixed shift B_i instead of a running
+// Both gains go to the query side: Q' = bf16(q * r_q * g_q * g_k * scale * log2(e)) lives in
+// registers for the whole loop, and the staged key rows are only normalised, Kr = bf16(k * r_k), so
+// S' = Q' Kr^T = scale * log2(e) * Qn Kn^T comes out in log2 units.
+//
+// Softmax shift. QK-RMSNorm bounds every score: ||k_j * r_k|| <= sqrt(D) for any key, so
+// |S'_ij| <= B_i = ||Q'_i|| * sqrt(D) (plus a margin for bf16 rounding). When every row of the
+// workgroup has B_i <= 48 (log2 units), the kernel uses the fixed shift B_i instead of a running
 // maximum: the MFMA accumulator starts at -B_i, exp2 of the result lies in [2^-96, 1], and no row
 // maximum, rescale or cross-lane exchange is needed inside the loop. Otherwise (large scale or gains)
 // it runs the usual online softmax with a running maximum. Both give the same softmax up to rounding.
+//
+// Staging: the K/V rows of tile t+1 are normalised (K) and written to the other LDS buffer inside
+// the body of tile t, and the rows of tile t+2 are fetched with buffer loads whose range ends at
+// the last valid key (reads past it return zeros), so the tile body is straight-line code.
 #include "jattn_device.h"
 #include "jattn_launch.h"
 
 namespace jattn {
 
 constexpr float kBoundLimit = 48.f;
-static_assert(kBlockRows == kRowsPerBlock, "host and device block sizes differ");
 
 template <int D>
-struct FwdSmem {
-  static constexpr int STAGE = 2 * 2 * Dims<D>::TILE_ELEMS * 2;  // K and V, double buffered, bytes
+struct Fwd {
+  static constexpr int QT = fwd_rows_per_block(D) / kBlockRows;  // 32-query tiles per wave
+  static constexpr int ROWS = fwd_rows_per_block(D);
+  using LK = Lay<D, kRowRead>;  // key rows: read as row fragments only
+  using LV = Lay<D, kTrRead>;   // value rows: read transposed only
+  static constexpr int STAGE = 2 * (LK::ELEMS + LV::ELEMS) * 2;  // double buffered, bytes
   static constexpr int BYTES = STAGE + 16;
+  static_assert(QT == 1 || QT == 2, "query tiles per wave");
 };
+
+// Per-wave softmax state of QT query tiles.
+template <int D>
+struct FwdState {
+  f32x16 o[Fwd<D>::QT][Dims<D>::MT];  // O^T accumulators (d x queries)
+  float lsum[Fwd<D>::QT];             // partial row sums (this lane's half of the keys)
+  float mrow[Fwd<D>::QT];             // shift (bounded) or running maximum, log2 units
+};
+
+// Softmax of one 32-key half for one query tile (S'^T in registers, lane = query) -> bf16 P
+// fragments, with the running-maximum bookkeeping when the fixed shift is not usable.
+template <int D, bool BOUNDED>
+__device__ __forceinline__ void softmax_half(const f32x16& s, f32x16 (&o)[Dims<D>::MT], float& lsum, float& mrow,
+                                             bf16x8& pf0, bf16x8& pf1) {
+  using Dm = Dims<D>;
+  float p[16];
+  if constexpr (BOUNDED) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(s[i]);
+  } else {
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(mrow, mx);
+    const float mu = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = fast_exp2(mrow - mu);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(s[i] - mu);
+    lsum *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < Dm::MT; ++mt) o[mt] *= alpha;
+    mrow = mnew;
+  }
+  pack_probs(p, pf0, pf1, lsum);
+}
+
+// One 64-key tile from LDS (kt, vt), with the staging of the next tile (registers tk, tv -> kn, vn)
+// and the loads of the tile after it in the same straight-line body. MASKED: keys at or past n get
+// a -inf accumulator seed (p = 0).
+template <int D, bool BOUNDED, bool MASKED>
+__device__ __forceinline__ void fwd_tile(const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn,
+                                         TileRegs<D>& tk, TileRegs<D>& tv, __amdgpu_buffer_rsrc_t rk,
+                                         __amdgpu_buffer_rsrc_t rv, int rs,
+                                         const bf16x8 (&qf)[Fwd<D>::QT][Dims<D>::KS],
+                                         const f32x16 (&cinit)[Fwd<D>::QT], FwdState<D>& st, int key0, int n,
+                                         float eps, int tid) {
+  using Dm = Dims<D>;
+  using LK = typename Fwd<D>::LK;
+  using LV = typename Fwd<D>::LV;
+  constexpr int QT = Fwd<D>::QT;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    // S'^T (keys x queries) = Kr Q'^T for this 32-key half and every query tile
+    f32x16 s[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      s[qt] = cinit[qt];
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key0 + h * 32 + (i >> 2) * 8 + g * 4 + (i & 3) >= n) s[qt][i] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < Dm::KS; ++ks) {
+      const bf16x8 kf = lds_row_frag<LK>(kt, h * 32 + l32, ks * 16 + g * 8);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) s[qt] = mfma(kf, qf[qt][ks], s[qt]);
+    }
+    if (h == 0) {
+      // stage the next tile into the other buffer while the MFMAs run
+      tile_store_rmsnorm<D, LK>(tk, kn, 1.f, eps, key0 + kTile, n, tid);
+      tile_store_raw<D, LV>(tv, vn, tid);
+    }
+    bf16x8 pf[QT][2];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+      softmax_half<D, BOUNDED>(s[qt], st.o[qt], st.lsum[qt], st.mrow[qt], pf[qt][0], pf[qt][1]);
+    // O^T (d x queries) += V^T P^T; each V fragment serves every query tile
+#pragma unroll
+    for (int mt = 0; mt < Dm::MT; ++mt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 vf = lds_tr_frag<LV>(vt, h * 32 + kk * 16, mt * 32, lane);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) st.o[qt][mt] = mfma(vf, pf[qt][kk], st.o[qt][mt]);
+      }
+  }
+  // fetch the tile after next (rows past the valid keys read as zeros)
+  tile_load_buf<D>(tk, rk, rs, key0 + 2 * kTile, tid);
+  tile_load_buf<D>(tv, rv, rs, key0 + 2 * kTile, tid);
+  __builtin_amdgcn_iglp_opt(2);
+  __syncthreads();
+}
 
 template <int D, bool BOUNDED>
 __device__ __forceinline__ void fwd_loop(const FwdArgs& a, __bf16* sk, __bf16* sv,
                                          const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
-                                         int rs, int n, const bf16x8 (&qf)[Dims<D>::KS], float shift,
-                                         const float (&gk)[Dims<D>::CPT][8], f32x16 (&oacc)[Dims<D>::MT],
-                                         float& lsum, float& mrow, int tid) {
-  using Dm = Dims<D>;
-  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  const int ntiles = (n + kTile - 1) / kTile;
+                                         int rs, int n, const bf16x8 (&qf)[Fwd<D>::QT][Dims<D>::KS],
+                                         const float (&shift)[Fwd<D>::QT], FwdState<D>& st, int tid) {
+  using LK = typename Fwd<D>::LK;
+  using LV = typename Fwd<D>::LV;
+  constexpr int QT = Fwd<D>::QT;
+  const int ntiles = (n + kTile - 1) / kTile, nfull = n / kTile;
+  if (ntiles == 0) return;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, rows_bytes<D>(n, rs));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, rows_bytes<D>(n, rs));
+  f32x16 cinit[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cinit[qt][i] = BOUNDED ? -shift[qt] : 0.f;
   TileRegs<D> tk, tv;
-  if (ntiles > 0) {
-    tile_load<D>(tk, kb, rs, 0, n, tid);
-    tile_load<D>(tv, vb, rs, 0, n, tid);
+  tile_load_buf<D>(tk, rk, rs, 0, tid);
+  tile_load_buf<D>(tv, rv, rs, 0, tid);
+  tile_store_rmsnorm<D, LK>(tk, sk, 1.f, a.eps, 0, n, tid);
+  tile_store_raw<D, LV>(tv, sv, tid);
+  tile_load_buf<D>(tk, rk, rs, kTile, tid);
+  tile_load_buf<D>(tv, rv, rs, kTile, tid);
+  __syncthreads();
+  for (int t = 0; t < nfull; ++t) {
+    const int ck = (t & 1) * LK::ELEMS, nk = LK::ELEMS - ck, cv = (t & 1) * LV::ELEMS, nv = LV::ELEMS - cv;
+    fwd_tile<D, BOUNDED, false>(sk + ck, sv + cv, sk + nk, sv + nv, tk, tv, rk, rv, rs, qf, cinit, st,
+                                t * kTile, n, a.eps, tid);
   }
-  f32x16 cinit;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) cinit[i] = BOUNDED ? -shift : 0.f;
-
-  for (int t = 0; t < ntiles; ++t) {
-    __bf16* kt = sk + (t & 1) * Dm::TILE_ELEMS;
-    __bf16* vt = sv + (t & 1) * Dm::TILE_ELEMS;
-    tile_store_rmsnorm<D>(tk, kt, gk, a.eps, t * kTile, n, tid);
-    tile_store_raw<D>(tv, vt, tid);
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      tile_load<D>(tk, kb, rs, (t + 1) * kTile, n, tid);
-      tile_load<D>(tv, vb, rs, (t + 1) * kTile, n, tid);
-    }
-#pragma unroll
-    for (int sb = 0; sb < kTile / 32; ++sb) {
-      const int key0 = t * kTile + sb * 32;
-      if (key0 >= n) break;
-      // S'^T (keys x queries) = Kn Q'^T, accumulator seeded with the shift
-      f32x16 s = cinit;
-      const __bf16* kr = kt + (sb * 32 + l32) * Dm::PITCH + g * 8;
-#pragma unroll
-      for (int ks = 0; ks < Dm::KS; ++ks) s = mfma(lds_row_frag(kr + ks * 16), qf[ks], s);
-
-      float p[16];
-      const bool tail = key0 + 32 > n;
-      if constexpr (BOUNDED) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = fast_exp2(s[i]);
-        if (tail) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (key0 + (i >> 2) * 8 + g * 4 + (i & 3) >= n) p[i] = 0.f;
-        }
-      } else {
-        if (tail) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (key0 + (i >> 2) * 8 + g * 4 + (i & 3) >= n) s[i] = -INFINITY;
-        }
-        float mx = s[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrow, mx);
-        const float mu = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = fast_exp2(mrow - mu);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = fast_exp2(s[i] - mu);
-        lsum *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < Dm::MT; ++mt) oacc[mt] *= alpha;
-        mrow = mnew;
-      }
-      bf16x8 pf0, pf1;
-      pack_probs(p, pf0, pf1, lsum);
-      // O^T (d x queries) += V^T P^T
-#pragma unroll
-      for (int mt = 0; mt < Dm::MT; ++mt) {
-        oacc[mt] = mfma(lds_tr_frag(vt, Dm::PITCH, sb * 32, mt * 32, lane), pf0, oacc[mt]);
-        oacc[mt] = mfma(lds_tr_frag(vt, Dm::PITCH, sb * 32 + 16, mt * 32, lane), pf1, oacc[mt]);
-      }
-    }
+  if (ntiles > nfull) {
+    const int ck = (nfull & 1) * LK::ELEMS, nk = LK::ELEMS - ck, cv = (nfull & 1) * LV::ELEMS,
+              nv = LV::ELEMS - cv;
+    fwd_tile<D, BOUNDED, true>(sk + ck, sv + cv, sk + nk, sv + nv, tk, tv, rk, rv, rs, qf, cinit, st,
+                               nfull * kTile, n, a.eps, tid);
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(FwdArgs a) {
   using Dm = Dims<D>;
-  __shared__ __attribute__((aligned(16))) char smem[FwdSmem<D>::BYTES];
+  constexpr int QT = Fwd<D>::QT;
+  __shared__ __attribute__((aligned(16))) char smem[Fwd<D>::BYTES];
   __bf16* sk = reinterpret_cast<__bf16*>(smem);
-  __bf16* sv = sk + 2 * Dm::TILE_ELEMS;
-  float* sbound = reinterpret_cast<float*>(smem + FwdSmem<D>::STAGE);
+  __bf16* sv = sk + 2 * Fwd<D>::LK::ELEMS;
+  float* sbound = reinterpret_cast<float*>(smem + Fwd<D>::STAGE);
 
   int bh, blk, item;
   if (!map_item(a.items, a.nblk, bh, blk, item)) return;
@@ -129,73 +197,81 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
   const int rs = H * D;
   const size_t base = ((size_t)b * L * H + (bh - b * H)) * D;
-  const uint16_t* qb = a.q + base;
-  const uint16_t* kb = a.k + base;
-  const uint16_t* vb = a.v + base;
 
-  zero_pad_columns<D>(sk, 4, tid);
+  zero_pad_columns<D, typename Fwd<D>::LK>(sk, 2, tid);
+  zero_pad_columns<D, typename Fwd<D>::LV>(sv, 2, tid);
 
-  float gk[Dm::CPT][8];
-  stage_gains<D>(gk, a.gains + D, 1.f, tid);
-
-  // This wave's 32 query rows, normalised and pre-scaled, as B-operand fragments.
-  const int qrow = blk * kBlockRows + wave * kWaveRows + l32;
-  const bool qvalid = qrow < L;
-  bf16x8 qf[Dm::KS];
-  float qq = 0.f;
-  {
+  // This wave's query rows, normalised with both gains and pre-scaled, as B-operand fragments,
+  // and their score bounds in log2 units (margin covers the bf16 rounding of Kr and Q').
+  int qrow[QT];
+  bf16x8 qf[QT][Dm::KS];
+  float shift[QT];
+  float wmax = 0.f;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    qrow[qt] = blk * Fwd<D>::ROWS + wave * 32 * QT + qt * 32 + l32;
+    const bool qvalid = qrow[qt] < L;
     float x[Dm::KS][8];
-    load_row_chunks<D>(x, qb + (size_t)qrow * rs, qvalid, g);
-    rmsnorm_row_frags<D>(qf, x, a.gains, a.c, a.eps, qvalid, g);
+    load_row_chunks<D>(x, a.q + base + (size_t)qrow[qt] * rs, qvalid, g);
+    rmsnorm_row_frags<D>(qf[qt], x, a.gains, a.gains + D, a.c, a.eps, qvalid, g);
+    float qq = 0.f;
 #pragma unroll
     for (int ks = 0; ks < Dm::KS; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float y = (float)qf[ks][e];
+        const float y = (float)qf[qt][ks][e];
         qq += y * y;
       }
     qq += __shfl_xor(qq, 32);
+    shift[qt] = sqrtf(qq) * sqrtf((float)D) * (1.f + 1.f / 64.f);
+    wmax = fmaxf(wmax, wave_max(shift[qt]));
   }
-  // max |g_k| over d, then the per-row score bound in log2 units
-  float gkmax = 0.f;
-  for (int d = lane; d < D; d += 64) gkmax = fmaxf(gkmax, fabsf(a.gains[D + d]));
-  gkmax = wave_max(gkmax);
-  const float shift = sqrtf(qq) * sqrtf((float)D) * gkmax * (1.f + 1.f / 64.f);
-  const float wmax = wave_max(shift);
   if (lane == 0) sbound[wave] = wmax;
   __syncthreads();
   const float bmax = fmaxf(fmaxf(sbound[0], sbound[1]), fmaxf(sbound[2], sbound[3]));
 
-  f32x16 oacc[Dm::MT];
+  FwdState<D> st;
 #pragma unroll
-  for (int mt = 0; mt < Dm::MT; ++mt)
+  for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[mt][i] = 0.f;
-  float lsum = 0.f, mrow;
+    for (int mt = 0; mt < Dm::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[qt][mt][i] = 0.f;
+    st.lsum[qt] = 0.f;
+  }
+  const uint16_t* kb = a.k + base;
+  const uint16_t* vb = a.v + base;
   if (bmax <= kBoundLimit) {  // uniform over the workgroup
-    mrow = shift;
-    fwd_loop<D, true>(a, sk, sv, kb, vb, rs, n, qf, shift, gk, oacc, lsum, mrow, tid);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = shift[qt];
+    fwd_loop<D, true>(a, sk, sv, kb, vb, rs, n, qf, shift, st, tid);
   } else {
-    mrow = -INFINITY;
-    fwd_loop<D, false>(a, sk, sv, kb, vb, rs, n, qf, shift, gk, oacc, lsum, mrow, tid);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = -INFINITY;
+    fwd_loop<D, false>(a, sk, sv, kb, vb, rs, n, qf, shift, st, tid);
   }
 
-  lsum += __shfl_xor(lsum, 32);
-  if (!qvalid) return;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  if (g == 0) a.lse[(size_t)bh * L + qrow] = lsum > 0.f ? (mrow + __log2f(lsum)) * kLn2 : -INFINITY;
-  uint16_t* orow = a.out + base + (size_t)qrow * rs;
 #pragma unroll
-  for (int mt = 0; mt < Dm::MT; ++mt)
+  for (int qt = 0; qt < QT; ++qt) {
+    const float lsum = st.lsum[qt] + __shfl_xor(st.lsum[qt], 32);
+    if (qrow[qt] >= L) continue;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    if (g == 0)
+      a.lse[(size_t)bh * L + qrow[qt]] = lsum > 0.f ? (st.mrow[qt] + __log2f(lsum)) * kLn2 : -INFINITY;
+    uint16_t* orow = a.out + base + (size_t)qrow[qt] * rs;
 #pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      const int d0 = mt * 32 + j4 * 8 + g * 4;
-      if (d0 < D) {
-        const u32x2 u = {pack2(oacc[mt][j4 * 4 + 0] * inv, oacc[mt][j4 * 4 + 1] * inv),
-                         pack2(oacc[mt][j4 * 4 + 2] * inv, oacc[mt][j4 * 4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d0) = u;
+    for (int mt = 0; mt < Dm::MT; ++mt)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int d0 = mt * 32 + j4 * 8 + g * 4;
+        if (d0 < D) {
+          const f32x16& o = st.o[qt][mt];
+          const u32x2 u = {pack2(o[j4 * 4 + 0] * inv, o[j4 * 4 + 1] * inv),
+                           pack2(o[j4 * 4 + 2] * inv, o[j4 * 4 + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d0) = u;
+        }
       }
-    }
+  }
 }
 
 template <int D>

@@ -46,8 +46,12 @@ struct BwdArgs {
   int items;               // B * H * nblk
 };
 
-// Rows per workgroup of every kernel; shared by the host-side grid and workspace sizing.
-constexpr int kRowsPerBlock = 128;
+// Rows per workgroup, shared by the host-side grid and workspace sizing and the kernels.
+// Forward: 4 waves of 64 queries (two independent 32-query tiles per wave) for D <= 64, where the
+// register budget allows it; 4 waves of 32 queries otherwise.
+constexpr int fwd_rows_per_block(int D) { return D <= 64 ? 256 : 128; }
+// Backward: both kernels use 4 waves of 32 rows.
+constexpr int kBwdRowsPerBlock = 128;
 
 hipError_t launch_fwd(int D, const FwdArgs& a, hipStream_t stream);
 // Enqueues the backward kernels; if n_events > 0, records events[i] after stage i (i < n_events).
