@@ -89,7 +89,7 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: K steps of forward + backward. Per step, events bracket the forward kernel and
-    # the backward's three kernels (recorded by the library on the same stream via jattn_bwd_ex).
+    # the backward's kernels (recorded by the library on the same stream via jattn_bwd_ex).
     K = args.steps
     ev_fwd0 = [new_event() for _ in range(K)]
     ev_fwd1 = [new_event() for _ in range(K)]
@@ -107,12 +107,11 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
-    kern_ms = {
-        f"fwd_kernel<{D}>": sum(ev_fwd0[i].elapsed_time(ev_fwd1[i]) for i in range(K)) / K,
-        f"bwd_dq_kernel<{D}>": sum(ev_fwd1[i].elapsed_time(ev_bwd[i][0]) for i in range(K)) / K,
-        f"bwd_dkdv_kernel<{D}>": sum(ev_bwd[i][0].elapsed_time(ev_bwd[i][1]) for i in range(K)) / K,
-        "dg_reduce_kernel": sum(ev_bwd[i][1].elapsed_time(ev_bwd[i][2]) for i in range(K)) / K,
-    }
+    kern_ms = {f"fwd_kernel<{D}>": sum(ev_fwd0[i].elapsed_time(ev_fwd1[i]) for i in range(K)) / K}
+    for j, name in enumerate(_lib.BWD_STAGES):
+        prev = [ev_fwd1[i] if j == 0 else ev_bwd[i][j - 1] for i in range(K)]
+        key = name if name == "dg_reduce_kernel" else f"{name}<{D}>"
+        kern_ms[key] = sum(prev[i].elapsed_time(ev_bwd[i][j]) for i in range(K)) / K
     ms_fwd = kern_ms[f"fwd_kernel<{D}>"]
     ms_bwd = ms_step - ms_fwd
 

@@ -17,7 +17,7 @@ SUCCESS, INVALID_VALUE, NOT_SUPPORTED, WORKSPACE, HIP = range(5)
 
 EXPORTED = ("jattn_fwd", "jattn_bwd", "jattn_bwd_ex", "jattn_bwd_workspace_bytes",
             "jattn_status_string", "jattn_abi_version")
-BWD_STAGES = ("bwd_dq_kernel", "bwd_dkdv_kernel", "dg_reduce_kernel")
+BWD_STAGES = ("bwd_prenorm_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "dg_reduce_kernel")
 
 _lock = threading.Lock()
 _lib = None

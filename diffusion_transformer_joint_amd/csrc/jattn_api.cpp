@@ -55,16 +55,25 @@ jattn_status check_sizes(int B, int L, int H, int D) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-  size_t delta, part_q, part_k, total;
+  size_t kr, qs, nlse2, ndelta, part_q, part_k, total;
 };
 
+// Normalised key rows and pre-scaled normalised query rows (bf16, [B, H, L, D]), the two row
+// statistics (fp32, [B, H, lp] with lp = L rounded up to whole row blocks) and the per-workgroup
+// gain-gradient partials (fp32, [items, D] for each side), each 256-byte aligned.
 WorkspaceLayout workspace_layout(int B, int L, int H, int D) {
-  const size_t items = (size_t)B * H * ((L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock);
+  const size_t nblk = (L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock;
+  const size_t items = (size_t)B * H * nblk, lp = nblk * kBwdRowsPerBlock;
+  const size_t rows = round_up((size_t)B * H * L * D * 2, 256), stats = round_up((size_t)B * H * lp * 4, 256),
+               parts = round_up(items * D * sizeof(float), 256);
   WorkspaceLayout w;
-  w.delta = 0;
-  w.part_q = round_up((size_t)B * H * L * sizeof(float), 256);
-  w.part_k = w.part_q + round_up(items * D * sizeof(float), 256);
-  w.total = w.part_k + round_up(items * D * sizeof(float), 256);
+  w.kr = 0;
+  w.qs = w.kr + rows;
+  w.nlse2 = w.qs + rows;
+  w.ndelta = w.nlse2 + stats;
+  w.part_q = w.ndelta + stats;
+  w.part_k = w.part_q + parts;
+  w.total = w.part_k + parts;
   return w;
 }
 
@@ -172,7 +181,10 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
   a.dgains = dgains;
-  a.delta = reinterpret_cast<float*>(ws + wl.delta);
+  a.kr = reinterpret_cast<uint16_t*>(ws + wl.kr);
+  a.qs = reinterpret_cast<uint16_t*>(ws + wl.qs);
+  a.nlse2 = reinterpret_cast<float*>(ws + wl.nlse2);
+  a.ndelta = reinterpret_cast<float*>(ws + wl.ndelta);
   a.part_q = reinterpret_cast<float*>(ws + wl.part_q);
   a.part_k = reinterpret_cast<float*>(ws + wl.part_k);
   a.B = B;
@@ -183,6 +195,7 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
   a.eps = eps;
   a.nblk = (L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock;
   a.items = B * H * a.nblk;
+  a.lp = a.nblk * kBwdRowsPerBlock;
   return jattn::launch_bwd(D, a, stage_events, n_stage_events, stream) == hipSuccess ? JATTN_SUCCESS
                                                                                     : JATTN_ERROR_HIP;
 }

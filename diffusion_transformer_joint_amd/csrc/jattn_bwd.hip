@@ -7,16 +7,21 @@
 //   dV = P^T dO,  dQn = scale dS Kn,  dKn = scale dS^T Qn,
 //   RMSNorm backward: dx = r (g * dxn) - x (r^3 / D) <g * dxn, x>,   dg = sum_rows dxn * x * r.
 //
-// Two kernels, no atomics:
-//  * dq kernel  (query-parallel, like the forward): each wave owns 32 queries and streams Kn and V;
-//    per 32-key step S^T, dP^T (both: lane = query), dS^T in registers, dQn^T += Kn^T dS^T with Kn^T
-//    read by ds_read_b64_tr_b16. It also computes Delta for its rows (stored for the other kernel),
-//    runs the Q-side RMSNorm backward in its epilogue and writes per-workgroup dg_q partials.
+// Four kernels, no atomics:
+//  * prenorm: Kr = bf16(k * r_k) (normalised keys without gain) into the workspace, [B, H, L, D].
+//  * dq kernel (query-parallel, like the forward): each wave owns 32 queries and streams Kr and V;
+//    per 32-key step S^T, dP^T (both: lane = query), dS^T in registers, dQn^T += Kr^T dS^T with Kr^T
+//    read by ds_read_b64_tr_b16. Epilogue: Q-side RMSNorm backward, dq, dg_q partials, and for the
+//    key-parallel kernel the pre-scaled normalised queries Qs = bf16(scale log2(e) q r_q) and the
+//    row statistics -lse log2(e) and -Delta.
 //  * dkdv kernel (key-parallel): each wave owns 32 keys (K rows normalised with both gains, and V
-//    rows, in registers) and streams the normalised, pre-scaled Q rows and dO; per 32-query step S, dP (lane = key), then dV^T += dO^T P and dKn^T += Q'^T dS with the
-//    transposed operands read by ds_read_b64_tr_b16. Epilogue: K-side RMSNorm backward, dk, dv and
-//    dg_k partials. Padded keys get exact zeros.
+//    rows, in registers) and streams Qs, dO and the row statistics; per 32-query step S, dP
+//    (lane = key), then dV^T += dO^T P and dKn^T += Qs^T dS with the transposed operands read by
+//    ds_read_b64_tr_b16. Epilogue: K-side RMSNorm backward, dk, dv and dg_k partials. Padded keys
+//    get exact zeros.
 //  * a small kernel sums the gain partials in a fixed order (deterministic dgains).
+// The streamed tiles go straight from memory into LDS (buffer loads with the LDS bit), issued two
+// tiles ahead into a ring of LDS buffers: no registers or VALU work are spent on staging.
 // dQ is recomputed rather than accumulated across key blocks: fp32 atomics on this chip sustain a
 // few hundred G/s, far below what a key-parallel dQ accumulation would need.
 #include "jattn_device.h"
@@ -26,43 +31,100 @@ namespace jattn {
 
 static_assert(kBlockRows == kBwdRowsPerBlock, "host and device block sizes differ");
 
-// LDS plan of the two kernels. Tiles read both as row fragments and transposed use the swizzled
-// layout; the dq kernel's value rows are only read as row fragments.
 // Waves per SIMD the register allocation targets: two up to D = 72, one at D = 128 (whose
 // accumulators and operand fragments need the whole register file).
 template <int D>
 constexpr int bwd_waves_per_eu() { return D <= 72 ? 2 : 1; }
+// LDS ring depth: three tile buffers (loads issued two tiles ahead), two at D = 72 whose padded
+// tiles would otherwise not leave room for two workgroups per CU.
+template <int D>
+constexpr int bwd_nbuf() { return D == 72 ? 2 : 3; }
 
+// LDS plan of the two main kernels. The swizzled layout (D = 64, 128) serves both row-fragment and
+// transposed reads without bank conflicts; other head dims use padded rows.
 template <int D>
 struct DqCfg {
   using LK = Lay<D, kSwizzled>;  // normalised key rows: S (row fragments) and dQ (transposed)
-  using LV = Lay<D, kRowRead>;   // value rows: dP (row fragments)
-  static constexpr int STAGE = 2 * (LK::ELEMS + LV::ELEMS) * 2;
+  using LV = Lay<D, kSwizzled>;  // value rows: dP (row fragments)
+  static constexpr int NB = bwd_nbuf<D>();
+  static constexpr int STAGE = NB * (LK::ELEMS + LV::ELEMS) * 2;
   static constexpr int SCRATCH = (kBlockRows + 8) * Dims<D>::DM * 4;
   static constexpr int BYTES = STAGE > SCRATCH ? STAGE : SCRATCH;
 };
 
 template <int D>
 struct DkdvCfg {
-  using LQ = Lay<D, kSwizzled>;  // normalised, pre-scaled query rows: S and dK
+  using LQ = Lay<D, kSwizzled>;  // pre-scaled normalised query rows: S and dK
   using LO = Lay<D, kSwizzled>;  // dout rows: dP and dV
-  static constexpr int STAGE = 2 * (LQ::ELEMS + LO::ELEMS) * 2;
-  static constexpr int STATS = 2 * 2 * kTile * 4;  // -lse2 and -delta per staged row, double buffered
+  static constexpr int NB = bwd_nbuf<D>();
+  static constexpr int STAGE = NB * (LQ::ELEMS + LO::ELEMS) * 2;
+  static constexpr int STATS = NB * 2 * kTile * 4;  // -lse2 and -delta per streamed row
   static constexpr int SCRATCH = (kBlockRows + 8) * Dims<D>::DM * 4;
   static constexpr int BYTES = STAGE + STATS > SCRATCH ? STAGE + STATS : SCRATCH;
 };
+
+// ------------------------------------------------------------------------------------------------
+// prenorm kernel: Kr[b, h, l, :] = bf16(k[b, l, h, :] * r_k) for the valid keys (l < valid length;
+// later rows are never read). Thread t covers chunks t%TPR + j*TPR of row t/TPR of each pass.
+constexpr int kPrenormPasses = 4;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_prenorm_kernel(BwdArgs a) {
+  using Dm = Dims<D>;
+  const int tid = threadIdx.x, rr = tid / Dm::TPR, cc = tid % Dm::TPR;
+  const int L = a.L, H = a.H;
+  const int total = a.B * L * H;
+  u32x4 x[kPrenormPasses][Dm::CPT];
+  int row[kPrenormPasses];
+#pragma unroll
+  for (int p = 0; p < kPrenormPasses; ++p) {
+    row[p] = (blockIdx.x * kPrenormPasses + p) * Dm::RPP + rr;  // input row (b * L + l) * H + h
+#pragma unroll
+    for (int j = 0; j < Dm::CPT; ++j) {
+      const int c = cc + j * Dm::TPR;
+      x[p][j] = row[p] < total && c < Dm::NCH ? *reinterpret_cast<const u32x4*>(a.k + (size_t)row[p] * D + c * 8)
+                                              : (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kPrenormPasses; ++p) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < Dm::CPT; ++j) ss = sumsq8(x[p][j], ss);
+    ss = group_sum<Dm::TPR>(ss);
+    const float r = rsqrtf(ss * (1.0f / D) + a.eps);
+    const int R = row[p];
+    if (R >= total) continue;
+    const int bl = R / H, h = R - bl * H, b = bl / L, l = bl - b * L;
+    const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
+    if (l >= n) continue;
+    uint16_t* dst = a.kr + (((size_t)b * H + h) * L + l) * D;
+#pragma unroll
+    for (int j = 0; j < Dm::CPT; ++j) {
+      const int c = cc + j * Dm::TPR;
+      if (c < Dm::NCH) {
+        float f[8];
+        unpack8(x[p][j], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] *= r;
+        *reinterpret_cast<bf16x8*>(dst + c * 8) = to_bf16x8(f);
+      }
+    }
+  }
+}
 
 // RMSNorm backward for one wave row held in the C/D layout (lane = row; register i of tile mt
 // holds d = 32*mt + 8*(i/4) + 4*g + i%4; the other half of the row is in lane l^32). On entry dxn
 // holds the gradient with respect to the normalised row divided by gpre[d] (the factor the MFMA
 // operands left out); `gain` is the row's own RMSNorm gain. If `exists`, writes the bf16 gradient row
-// (zeros when not `valid`, i.e. a padded key). On return dxn holds the dg contributions dxn * x * r
-// (zeros for rows that are not valid).
+// (zeros when not `valid`, i.e. a padded key) and, if xsrow is set, bf16(x * r * xs_mul). On return
+// dxn holds the dg contributions dxn * x * r (zeros for rows that are not valid).
 template <int D>
 __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT], const uint16_t* __restrict__ xrow,
                                                      const float* __restrict__ gain, const float* __restrict__ gpre,
                                                      float r, bool valid, bool exists,
-                                                     uint16_t* __restrict__ dxrow, int g) {
+                                                     uint16_t* __restrict__ dxrow, uint16_t* __restrict__ xsrow,
+                                                     float xs_mul, int g) {
   using Dm = Dims<D>;
   float x[Dm::MT][16];
   float gv[Dm::MT][16];
@@ -85,6 +147,7 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
     }
   t += __shfl_xor(t, 32);
   const float c3 = r * r * r * (1.0f / D) * t;
+  const float xs = r * xs_mul;
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt)
 #pragma unroll
@@ -96,8 +159,13 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
         const int i = j4 * 4 + e;
         y[e] = valid ? r * gv[mt][i] * dxn[mt][i] - x[mt][i] * c3 : 0.f;
       }
-      if (exists && d0 < D)
+      if (exists && d0 < D) {
         *reinterpret_cast<u32x2*>(dxrow + d0) = (u32x2){pack2(y[0], y[1]), pack2(y[2], y[3])};
+        const int i = j4 * 4;
+        if (xsrow)
+          *reinterpret_cast<u32x2*>(xsrow + d0) = (u32x2){pack2(x[mt][i] * xs, x[mt][i + 1] * xs),
+                                                          pack2(x[mt][i + 2] * xs, x[mt][i + 3] * xs)};
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = j4 * 4 + e;
@@ -110,19 +178,16 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
 // dq kernel: query-parallel
 
 // One 64-key tile: for both 32-key halves S'^T = Kr Q'^T and dP^T - Delta = V dO^T (lane = query),
-// dS^T = P * (dP - Delta) with P = exp2(S' - lse2), then dQn^T += Kr^T dS^T. The next tile is
-// staged and the one after it fetched inside the same body. MASKED: keys at or past n are seeded
-// with -inf (P = 0).
+// dS^T = P * (dP - Delta) with P = exp2(S' - lse2), then dQn^T += Kr^T dS^T. MASKED: keys at or
+// past n are seeded with -inf (P = 0).
 template <int D, bool MASKED>
-__device__ __forceinline__ void dq_tile(const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn,
-                                        TileRegs<D>& tk, TileRegs<D>& tv, __amdgpu_buffer_rsrc_t rk,
-                                        __amdgpu_buffer_rsrc_t rv, int rs, const bf16x8 (&qf)[Dims<D>::KS],
+__device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __bf16* __restrict__ vt, const bf16x8 (&qf)[Dims<D>::KS],
                                         const bf16x8 (&dof)[Dims<D>::KS], const f32x16& cs, const f32x16& cp,
-                                        f32x16 (&acc)[Dims<D>::MT], int key0, int n, float eps, int tid) {
+                                        f32x16 (&acc)[Dims<D>::MT], int key0, int n, int lane) {
   using Dm = Dims<D>;
   using LK = typename DqCfg<D>::LK;
   using LV = typename DqCfg<D>::LV;
-  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     f32x16 s = cs, dp = cp;
@@ -136,10 +201,6 @@ __device__ __forceinline__ void dq_tile(const __bf16* kt, const __bf16* vt, __bf
       s = mfma(lds_row_frag<LK>(kt, h * 32 + l32, ks * 16 + g * 8), qf[ks], s);
       dp = mfma(lds_row_frag<LV>(vt, h * 32 + l32, ks * 16 + g * 8), dof[ks], dp);
     }
-    if (h == 0) {
-      tile_store_rmsnorm<D, LK>(tk, kn, 1.f, eps, key0 + kTile, n, tid);
-      tile_store_raw<D, LV>(tv, vn, tid);
-    }
     float ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * dp[i];
@@ -150,33 +211,42 @@ __device__ __forceinline__ void dq_tile(const __bf16* kt, const __bf16* vt, __bf
       acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32 + 16, mt * 32, lane), f1, acc[mt]);
     }
   }
-  tile_load_buf<D>(tk, rk, rs, key0 + 2 * kTile, tid);
-  tile_load_buf<D>(tv, rv, rs, key0 + 2 * kTile, tid);
-  __builtin_amdgcn_iglp_opt(2);
-  __syncthreads();
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
 void bwd_dq_kernel(BwdArgs a) {
   using Dm = Dims<D>;
-  using LK = typename DqCfg<D>::LK;
-  using LV = typename DqCfg<D>::LV;
-  __shared__ __attribute__((aligned(16))) char smem[DqCfg<D>::BYTES];
+  using Cfg = DqCfg<D>;
+  using LK = typename Cfg::LK;
+  using LV = typename Cfg::LV;
+  constexpr int NB = Cfg::NB;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
   __bf16* sk = reinterpret_cast<__bf16*>(smem);
-  __bf16* sv = sk + 2 * LK::ELEMS;
+  __bf16* sv = sk + NB * LK::ELEMS;
 
   int bh, blk, item;
   if (!map_item(a.items, a.nblk, bh, blk, item)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int L = a.L, H = a.H;
   const int b = bh / H;
   const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
   const int rs = H * D;
   const size_t base = ((size_t)b * L * H + (bh - b * H)) * D;
 
-  zero_pad_columns<D, LK>(sk, 2, tid);
-  zero_pad_columns<D, LV>(sv, 2, tid);
+  // start streaming the first key tiles before the per-row set-up
+  const int ntiles = (n + kTile - 1) / kTile, nfull = n / kTile;
+  DirectTile<D, LK> dk;
+  DirectTile<D, LV> dv;
+  dk.init(D, wave, lane);
+  dv.init(rs, wave, lane);
+  const uint16_t* kb = a.kr + (size_t)bh * L * D;
+  const uint16_t* vb = a.v + base;
+  auto issue = [&](int t, int buf) {
+    dk.issue(tile_rsrc<D>(kb, D, t * kTile, n), sk + buf * LK::ELEMS, wave);
+    dv.issue(tile_rsrc<D>(vb, rs, t * kTile, n), sv + buf * LV::ELEMS, wave);
+  };
+  for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
 
   const int qrow = blk * kBlockRows + wave * kWaveRows + l32;
   const bool qvalid = qrow < L;
@@ -200,7 +270,6 @@ void bwd_dq_kernel(BwdArgs a) {
     delta += __shfl_xor(delta, 32);
   }
   const float lse2 = qvalid ? a.lse[(size_t)bh * L + qrow] * kLog2e : 0.f;
-  if (qvalid && g == 0) a.delta[(size_t)bh * L + qrow] = delta;
   f32x16 cs, cp;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -213,72 +282,56 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
 
-  const int ntiles = (n + kTile - 1) / kTile, nfull = n / kTile;
-  if (ntiles > 0) {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + base, rows_bytes<D>(n, rs));
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + base, rows_bytes<D>(n, rs));
-    TileRegs<D> tk, tv;
-    tile_load_buf<D>(tk, rk, rs, 0, tid);
-    tile_load_buf<D>(tv, rv, rs, 0, tid);
-    tile_store_rmsnorm<D, LK>(tk, sk, 1.f, a.eps, 0, n, tid);
-    tile_store_raw<D, LV>(tv, sv, tid);
-    tile_load_buf<D>(tk, rk, rs, kTile, tid);
-    tile_load_buf<D>(tv, rv, rs, kTile, tid);
-    __syncthreads();
-    for (int t = 0; t < nfull; ++t) {
-      const int ck = (t & 1) * LK::ELEMS, nk = LK::ELEMS - ck, cv = (t & 1) * LV::ELEMS, nv = LV::ELEMS - cv;
-      dq_tile<D, false>(sk + ck, sv + cv, sk + nk, sv + nv, tk, tv, rk, rv, rs, qf, dof, cs, cp, acc, t * kTile, n,
-                        a.eps, tid);
-    }
-    if (ntiles > nfull) {
-      const int ck = (nfull & 1) * LK::ELEMS, nk = LK::ELEMS - ck, cv = (nfull & 1) * LV::ELEMS,
-                nv = LV::ELEMS - cv;
-      dq_tile<D, true>(sk + ck, sv + cv, sk + nk, sv + nv, tk, tv, rk, rv, rs, qf, dof, cs, cp, acc, nfull * kTile,
-                       n, a.eps, tid);
-    }
+  wait_vmem();
+  __syncthreads();
+  int cur = 0;
+  for (int t = 0; t < ntiles; ++t) {
+    const bool ahead = t + NB - 1 < ntiles;
+    if (ahead) issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
+    if (t < nfull)
+      dq_tile<D, false>(sk + cur * LK::ELEMS, sv + cur * LV::ELEMS, qf, dof, cs, cp, acc, t * kTile, n, lane);
+    else
+      dq_tile<D, true>(sk + cur * LK::ELEMS, sv + cur * LV::ELEMS, qf, dof, cs, cp, acc, t * kTile, n, lane);
+    // the tile after this one has landed (only the newest tile's loads may still be in flight)
+    if (ahead)
+      stream_barrier<DirectTile<D, LK>::MIN_PER_WAVE + DirectTile<D, LV>::MIN_PER_WAVE>();
+    else
+      stream_barrier<0>();
+    cur = cur + 1 == NB ? 0 : cur + 1;
   }
 
-  // dQn = scale * g_k * (dS Kr): the staged key rows carry no gain
+  // row statistics for the key-parallel kernel, for every row of the block (-inf / 0 past L)
+  if (g == 0) {
+    const size_t si = (size_t)bh * a.lp + qrow;
+    a.nlse2[si] = qvalid ? -lse2 : -INFINITY;
+    a.ndelta[si] = qvalid ? -delta : 0.f;
+  }
+  // dQn = scale * g_k * (dS Kr): the streamed key rows carry no gain
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) acc[mt] *= a.scale;
-  rmsnorm_backward_row<D>(acc, a.q + roff, a.gains, a.gains + D, rq, qvalid, qvalid, a.dq + roff, g);
-  __syncthreads();  // all waves are done with the staged tiles before the scratch reuse
+  rmsnorm_backward_row<D>(acc, a.q + roff, a.gains, a.gains + D, rq, qvalid, qvalid, a.dq + roff,
+                          a.qs + ((size_t)bh * L + qrow) * D, a.c, g);
+  // (the loop ended with every load retired and a barrier: the LDS ring is free for the scratch)
   block_column_sums<D>(acc, reinterpret_cast<float*>(smem), a.part_q + (size_t)item * D, tid);
 }
 
 // ------------------------------------------------------------------------------------------------
 // dkdv kernel: key-parallel
 
-// Stage the row statistics of query tile t: -lse2 (-inf past L) and -Delta, one row per thread of
-// the first wave.
-__device__ __forceinline__ void stats_load(float& sl, float& sd, __amdgpu_buffer_rsrc_t rl,
-                                           __amdgpu_buffer_rsrc_t rd, int q0, int L, int tid) {
-  if (tid < kTile) {
-    const int qi = q0 + tid;
-    // (the b32 buffer load returns the raw word as an integer)
-    const float l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)qi * 4u, 0, 0));
-    const float d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)qi * 4u, 0, 0));
-    sl = qi < L ? -l * kLog2e : -INFINITY;
-    sd = -d;
-  }
-}
-
-// One 64-query tile: for both 32-query halves S' = Q'' Kf^T and dP - Delta = dO V^T (lane = key),
-// P = exp2(S' - lse2), dS = P * (dP - Delta), then dV^T += dO^T P and dKn^T += Q''^T dS.
-// KMASK: this wave holds keys at or past n, whose P is forced to zero.
+// One 64-query tile: for both 32-query halves S' = Qs Kf^T and dP - Delta = dO V^T (lane = key),
+// P = exp2(S' - lse2), dS = P * (dP - Delta), then dV^T += dO^T P and dKn^T += Qs^T dS.
+// sl / sd hold -lse2 and -Delta of the tile's rows. KMASK: this wave holds keys at or past n, whose
+// P is forced to zero.
 template <int D, bool KMASK>
-__device__ __forceinline__ void dkdv_tile(const __bf16* qt, const __bf16* ot, const float* sl, const float* sd,
-                                          __bf16* qn, __bf16* on, float* sln, float* sdn, TileRegs<D>& tq,
-                                          TileRegs<D>& to, float& stl, float& std_, __amdgpu_buffer_rsrc_t rq,
-                                          __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
-                                          __amdgpu_buffer_rsrc_t rd, int rs, const bf16x8 (&kf)[Dims<D>::KS],
-                                          const bf16x8 (&vf)[Dims<D>::KS], f32x16 (&dva)[Dims<D>::MT],
-                                          f32x16 (&dka)[Dims<D>::MT], bool kvalid, int q0, int L, float c,
-                                          float eps, int tid) {
+__device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const __bf16* __restrict__ ot,
+                                          const float* __restrict__ sl, const float* __restrict__ sd,
+                                          const bf16x8 (&kf)[Dims<D>::KS], const bf16x8 (&vf)[Dims<D>::KS],
+                                          f32x16 (&dva)[Dims<D>::MT], f32x16 (&dka)[Dims<D>::MT], bool kvalid,
+                                          int lane) {
   using Dm = Dims<D>;
   using LQ = typename DkdvCfg<D>::LQ;
   using LO = typename DkdvCfg<D>::LO;
-  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     f32x16 s, dp;
@@ -297,14 +350,6 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* qt, const __bf16* ot, co
       s = mfma(lds_row_frag<LQ>(qt, h * 32 + l32, ks * 16 + g * 8), kf[ks], s);
       dp = mfma(lds_row_frag<LO>(ot, h * 32 + l32, ks * 16 + g * 8), vf[ks], dp);
     }
-    if (h == 0) {
-      tile_store_rmsnorm<D, LQ>(tq, qn, c, eps, q0 + kTile, L, tid);
-      tile_store_raw<D, LO>(to, on, tid);
-      if (tid < kTile) {
-        sln[tid] = stl;
-        sdn[tid] = std_;
-      }
-    }
     float p[16], ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -322,11 +367,6 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* qt, const __bf16* ot, co
       dka[mt] = mfma(lds_tr_frag<LQ>(qt, h * 32 + 16, mt * 32, lane), df1, dka[mt]);
     }
   }
-  tile_load_buf<D>(tq, rq, rs, q0 + 2 * kTile, tid);
-  tile_load_buf<D>(to, ro, rs, q0 + 2 * kTile, tid);
-  stats_load(stl, std_, rl, rd, q0 + 2 * kTile, L, tid);
-  __builtin_amdgcn_iglp_opt(2);
-  __syncthreads();
 }
 
 template <int D, bool KMASK>
@@ -334,38 +374,52 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t b
                                           const bf16x8 (&kf)[Dims<D>::KS], const bf16x8 (&vf)[Dims<D>::KS],
                                           f32x16 (&dva)[Dims<D>::MT], f32x16 (&dka)[Dims<D>::MT], bool kvalid,
                                           int tid) {
-  using LQ = typename DkdvCfg<D>::LQ;
-  using LO = typename DkdvCfg<D>::LO;
+  using Cfg = DkdvCfg<D>;
+  using LQ = typename Cfg::LQ;
+  using LO = typename Cfg::LO;
+  constexpr int NB = Cfg::NB;
   __bf16* sq = reinterpret_cast<__bf16*>(smem);
-  __bf16* so = sq + 2 * LQ::ELEMS;
-  float* sl = reinterpret_cast<float*>(smem + DkdvCfg<D>::STAGE);  // [2][kTile]
-  float* sd = sl + 2 * kTile;                                        // [2][kTile]
+  __bf16* so = sq + NB * LQ::ELEMS;
+  float* sl = reinterpret_cast<float*>(smem + Cfg::STAGE);  // [NB][kTile]
+  float* sd = sl + NB * kTile;                                // [NB][kTile]
+  const int lane = tid & 63, wave = wave_id();
   const int L = a.L;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + base, rows_bytes<D>(L, rs));
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.dout + base, rows_bytes<D>(L, rs));
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + (size_t)bh * L, (uint32_t)L * 4u);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + (size_t)bh * L, (uint32_t)L * 4u);
-  TileRegs<D> tq, to;
-  float stl = 0.f, std_ = 0.f;
-  tile_load_buf<D>(tq, rq, rs, 0, tid);
-  tile_load_buf<D>(to, ro, rs, 0, tid);
-  stats_load(stl, std_, rl, rd, 0, L, tid);
-  tile_store_rmsnorm<D, LQ>(tq, sq, a.c, a.eps, 0, L, tid);
-  tile_store_raw<D, LO>(to, so, tid);
-  if (tid < kTile) {
-    sl[tid] = stl;
-    sd[tid] = std_;
-  }
-  tile_load_buf<D>(tq, rq, rs, kTile, tid);
-  tile_load_buf<D>(to, ro, rs, kTile, tid);
-  stats_load(stl, std_, rl, rd, kTile, L, tid);
-  __syncthreads();
+  DirectTile<D, LQ> dq;
+  DirectTile<D, LO> dout;
+  dq.init(D, wave, lane);
+  dout.init(rs, wave, lane);
+  const uint16_t* qb = a.qs + (size_t)bh * L * D;
+  const uint16_t* ob = a.dout + base;
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.nlse2 + (size_t)bh * a.lp, (uint32_t)a.lp * 4u);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.ndelta + (size_t)bh * a.lp, (uint32_t)a.lp * 4u);
+  // Tile t: rows [64 t, 64 t + 64) of Qs and dO (zeros past L) and of the statistics (written by the
+  // dq kernel for every row of its blocks, so 64 t + 63 < lp). Waves 0 and 1 carry the statistics.
+  auto issue = [&](int t, int buf) {
+    if (wave == 0)
+      lds_load_dwords(rl, sl + buf * kTile, (uint32_t)(t * kTile + lane) * 4u);
+    else if (wave == 1)
+      lds_load_dwords(rd, sd + buf * kTile, (uint32_t)(t * kTile + lane) * 4u);
+    dq.issue(tile_rsrc<D>(qb, D, t * kTile, L), sq + buf * LQ::ELEMS, wave);
+    dout.issue(tile_rsrc<D>(ob, rs, t * kTile, L), so + buf * LO::ELEMS, wave);
+  };
   const int ntiles = (L + kTile - 1) / kTile;
+  for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
+  wait_vmem();
+  __syncthreads();
+  constexpr int NEWEST = DirectTile<D, LQ>::MIN_PER_WAVE + DirectTile<D, LO>::MIN_PER_WAVE;
+  int cur = 0;
   for (int t = 0; t < ntiles; ++t) {
-    const int cq = (t & 1) * LQ::ELEMS, nq = LQ::ELEMS - cq, co = (t & 1) * LO::ELEMS, no = LO::ELEMS - co;
-    const int cs = (t & 1) * kTile, ns = kTile - cs;
-    dkdv_tile<D, KMASK>(sq + cq, so + co, sl + cs, sd + cs, sq + nq, so + no, sl + ns, sd + ns, tq, to, stl, std_,
-                        rq, ro, rl, rd, rs, kf, vf, dva, dka, kvalid, t * kTile, L, a.c, a.eps, tid);
+    const bool ahead = t + NB - 1 < ntiles;
+    if (ahead) issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
+    dkdv_tile<D, KMASK>(sq + cur * LQ::ELEMS, so + cur * LO::ELEMS, sl + cur * kTile, sd + cur * kTile, kf, vf,
+                        dva, dka, kvalid, lane);
+    if (!ahead)
+      stream_barrier<0>();
+    else if (wave < 2)
+      stream_barrier<NEWEST + 1>();  // (these waves also load a statistics row per tile)
+    else
+      stream_barrier<NEWEST>();
+    cur = cur + 1 == NB ? 0 : cur + 1;
   }
 }
 
@@ -377,7 +431,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
   int bh, blk, item;
   if (!map_item(a.items, a.nblk, bh, blk, item)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int L = a.L, H = a.H;
   const int b = bh / H;
   const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
@@ -401,8 +455,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
     for (int d = tid; d < D; d += kThreads) a.part_k[(size_t)item * D + d] = 0.f;
     return;
   }
-
-  zero_pad_columns<D, typename DkdvCfg<D>::LQ>(reinterpret_cast<__bf16*>(smem), 4, tid);
 
   bf16x8 kf[Dm::KS], vf[Dm::KS];
   float rk;
@@ -442,11 +494,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
   }
-  // dKn = scale * dS^T Qn = ln(2) * g_q * dS^T Q''  (the staged query rows carry scale * log2(e), no gain)
+  // dKn = scale * dS^T Qn = ln(2) * g_q * dS^T Qs  (the streamed query rows carry scale * log2(e), no gain)
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) dka[mt] *= kLn2;
   if (kin) {
-    rmsnorm_backward_row<D>(dka, a.k + roff, a.gains + D, a.gains, rk, kvalid, true, a.dk + roff, g);
+    rmsnorm_backward_row<D>(dka, a.k + roff, a.gains + D, a.gains, rk, kvalid, true, a.dk + roff, nullptr, 0.f,
+                            g);
   } else {
 #pragma unroll
     for (int mt = 0; mt < Dm::MT; ++mt)
@@ -483,20 +536,26 @@ __global__ __launch_bounds__(64) void dg_reduce_kernel(const float* __restrict__
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a, const hipEvent_t* events, int n_events,
                                hipStream_t stream) {
+  const int prenorm_rows = Dims<D>::RPP * kPrenormPasses;
+  const int prenorm_blocks = (int)(((int64_t)a.B * a.L * a.H + prenorm_rows - 1) / prenorm_rows);
   const dim3 grid(grid_for_items(a.items));
+  int stage = 0;
+  auto recorded = [&]() {
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && n_events > stage) e = hipEventRecord(events[stage], stream);
+    ++stage;
+    return e;
+  };
+  hipLaunchKernelGGL(bwd_prenorm_kernel<D>, dim3(prenorm_blocks), dim3(kThreads), 0, stream, a);
+  hipError_t e = recorded();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dq_kernel<D>, grid, dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && n_events > 0) e = hipEventRecord(events[0], stream);
-  if (e != hipSuccess) return e;
+  if ((e = recorded()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, grid, dim3(kThreads), 0, stream, a);
-  e = hipGetLastError();
-  if (e == hipSuccess && n_events > 1) e = hipEventRecord(events[1], stream);
-  if (e != hipSuccess) return e;
+  if ((e = recorded()) != hipSuccess) return e;
   hipLaunchKernelGGL(dg_reduce_kernel, dim3(2 * D), dim3(64), 0, stream, a.part_q, a.part_k, a.items, D,
                      a.dgains);
-  e = hipGetLastError();
-  if (e == hipSuccess && n_events > 2) e = hipEventRecord(events[2], stream);
-  return e;
+  return recorded();
 }
 
 hipError_t launch_bwd(int D, const BwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream) {

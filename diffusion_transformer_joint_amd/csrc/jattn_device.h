@@ -151,6 +151,9 @@ __device__ __forceinline__ void pack_probs(const float (&p)[16], bf16x8& f0, bf1
   f1 = __builtin_bit_cast(bf16x8, b);
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
@@ -162,7 +165,7 @@ __device__ __forceinline__ float wave_max(float x) {
 
 // Operand fragment of 8 contiguous bf16 (columns col .. col+7, col % 8 == 0) of one LDS tile row.
 template <class LY>
-__device__ __forceinline__ bf16x8 lds_row_frag(const __bf16* tile, int r, int col) {
+__device__ __forceinline__ bf16x8 lds_row_frag(const __bf16* __restrict__ tile, int r, int col) {
   return *reinterpret_cast<const bf16x8*>(tile + LY::off(r, col));
 }
 
@@ -174,7 +177,7 @@ __device__ __forceinline__ bf16x8 lds_row_frag(const __bf16* tile, int r, int co
 //   row0 + 4*(l/32) + [0..3]  (elements 0..3)  and  row0 + 8 + 4*(l/32) + [0..3]  (elements 4..7),
 // the contraction-slot order of a C/D tile reused as a B operand (see the file header).
 template <class LY>
-__device__ __forceinline__ bf16x8 lds_tr_frag(const __bf16* tile, int row0, int col0, int lane) {
+__device__ __forceinline__ bf16x8 lds_tr_frag(const __bf16* __restrict__ tile, int row0, int col0, int lane) {
   const int r = row0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int col = col0 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JATTN_LDS i16x4*)(tile + LY::off(r, col)));
@@ -245,6 +248,74 @@ __device__ __forceinline__ void tile_load_buf(TileRegs<D>& t, __amdgpu_buffer_rs
       t.r[p][j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
     }
   }
+}
+
+// Direct-to-LDS tile loads (buffer_load_dwordx4 ... lds): one wave instruction writes the 16 bytes
+// of lane l to LDS at base + 16*l, so the tile's physical 16-byte chunks, taken in LDS order, are
+// covered by NWL consecutive wave loads. Each lane precomputes (once) the global offset of the
+// logical chunk that belongs at its physical position -- undoing the layout's swizzle -- or an
+// out-of-range offset (zeros) for padding positions. Per tile only the buffer resource changes.
+// The data bypasses VGPRs; completion is covered by the s_waitcnt vmcnt before the next barrier.
+template <int D, class LY>
+struct DirectTile {
+  using Dm = Dims<D>;
+  static constexpr int CPR = LY::PITCH / 8;                 // physical chunks per row (incl. padding)
+  static constexpr int NWL = (kTile * CPR + 63) / 64;       // wave loads per tile
+  static constexpr int PER_WAVE = (NWL + 3) / 4;            // most loads one wave issues (4 waves)
+  static constexpr int MIN_PER_WAVE = NWL / 4;              // fewest loads one wave issues
+  static constexpr int ALLOC = NWL * 512;                   // elements one tile buffer occupies
+  uint32_t voff[PER_WAVE];
+
+  __device__ __forceinline__ void init(int rs, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int p = (wave + 4 * j) * 64 + lane;  // physical chunk index in the tile
+      const int row = p / CPR, pc = p - row * CPR;
+      const int lc = pc ^ LY::swz(row & (kTile - 1));
+      const bool real = wave + 4 * j < NWL && row < kTile && pc * 8 < Dm::DM && lc < Dm::NCH;
+      voff[j] = real ? (uint32_t)(row * rs + lc * 8) * 2u : 0xFFFFFFF0u;
+    }
+  }
+  // Issue this wave's share of the tile whose first row is addressed by `rsrc`.
+  // (The restrict qualifiers here and on the tile readers let the compiler see that reads of the
+  // current tile do not depend on the loads in flight into another buffer; without them it waits
+  // for every outstanding load before each transposed LDS read.)
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, __bf16* __restrict__ lds, int wave) const {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int i = wave + 4 * j;
+      if (NWL % 4 == 0 || i < NWL)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (JATTN_LDS void*)(lds + i * 512), 16, voff[j], 0, 0, 0);
+    }
+  }
+};
+
+// Direct-to-LDS load of one dword per lane: lane l's word (byte offset voff in rsrc) lands at dst[l].
+__device__ __forceinline__ void lds_load_dwords(__amdgpu_buffer_rsrc_t rsrc, float* __restrict__ dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (JATTN_LDS void*)dst, 4, voff, 0, 0, 0);
+}
+
+// Buffer resource for the tile starting at row `row0` of a [rows][D] view (row stride rs elements)
+// whose rows [0, nrows) are valid: later rows read as zeros.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int rs, int row0, int nrows) {
+  const uint32_t total = rows_bytes<D>(nrows, rs), start = (uint32_t)row0 * (uint32_t)rs * 2u;
+  // (the range is wave-uniform; saying so keeps the descriptor in scalar registers, where the
+  // buffer instructions need it, instead of a loop over its distinct per-lane values)
+  const uint32_t range = __builtin_amdgcn_readfirstlane(total > start ? total - start : 0u);
+  return make_rsrc(base + (size_t)row0 * rs, range);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier for the tile-streaming loops: each wave first waits until at most N of its
+// vector memory operations are outstanding (they retire in issue order, so every load older than the
+// N most recent has landed in LDS) and until its LDS reads have returned, then meets the others.
+// __syncthreads() would add a memory-model fence that waits for all outstanding loads, including
+// those of tiles further ahead. The asm statement is also a compiler barrier for memory accesses.
+template <int N>
+__device__ __forceinline__ void stream_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // Store the tile unchanged.

@@ -35,7 +35,10 @@ struct BwdArgs {
   uint16_t* dk;
   uint16_t* dv;
   float* dgains;           // [2, D]
-  float* delta;            // workspace [B, H, L]: rowsum(dout * out)
+  uint16_t* kr;            // workspace [B, H, L, D]: bf16(k * r_k), valid keys only
+  uint16_t* qs;            // workspace [B, H, L, D]: bf16(scale * log2(e) * q * r_q)
+  float* nlse2;            // workspace [B, H, lp]: -lse * log2(e) (-inf past L)
+  float* ndelta;           // workspace [B, H, lp]: -rowsum(dout * out) (0 past L)
   float* part_q;           // workspace [items, D]: gain-gradient partials of the query blocks
   float* part_k;           // workspace [items, D]: gain-gradient partials of the key blocks
   int B, L, H;
@@ -44,6 +47,7 @@ struct BwdArgs {
   float eps;
   int nblk;                // row blocks (queries or keys) per (batch, head)
   int items;               // B * H * nblk
+  int lp;                  // nblk * kBwdRowsPerBlock: statistics rows per (batch, head)
 };
 
 // Rows per workgroup, shared by the host-side grid and workspace sizing and the kernels.

@@ -63,8 +63,9 @@ jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float*
                        const int32_t* valid_len, int B, int L, int H, int D,
                        float softmax_scale, float eps, void* out, float* lse, hipStream_t stream);
 
-/* Bytes of device workspace jattn_bwd needs for these sizes (row statistics and per-workgroup
- * partial sums of the gain gradients). Returns 0 for invalid or unsupported sizes. */
+/* Bytes of device workspace jattn_bwd needs for these sizes: normalised K rows and pre-scaled
+ * normalised Q rows (2 * B*L*H*D bf16), two fp32 row statistics per query row, and per-workgroup
+ * partial sums of the gain gradients. Returns 0 for invalid or unsupported sizes. */
 size_t jattn_bwd_workspace_bytes(int B, int L, int H, int D);
 
 /* Backward pass. Takes the forward inputs, the forward outputs out and lse (from jattn_fwd with the
@@ -80,9 +81,10 @@ jattn_status jattn_bwd(const void* q, const void* k, const void* v, const float*
                        void* dq, void* dk, void* dv, float* dgains,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Number of kernels jattn_bwd enqueues, in order: 0 = dq (query-parallel; also writes the row
- * statistics Delta), 1 = dk/dv (key-parallel), 2 = gain-gradient reduction. */
-#define JATTN_BWD_STAGES 3
+/* Number of kernels jattn_bwd enqueues, in order: 0 = K-row RMS normalisation, 1 = dq
+ * (query-parallel; also writes the normalised Q rows and the row statistics), 2 = dk/dv
+ * (key-parallel), 3 = gain-gradient reduction. */
+#define JATTN_BWD_STAGES 4
 
 /* jattn_bwd with per-stage timing hooks, for callers that attribute time to the individual kernels
  * (profilers, benchmarks). Identical results to jattn_bwd. If n_stage_events > 0, stage_events points

@@ -118,11 +118,11 @@ def test_bwd_ex_rejects_bad_event_arguments(lib):
             ctypes.c_float(0.125), ctypes.c_float(1e-6), fake(7), fake(8), fake(9), fake(10), fake(11), need]
     assert lib.jattn_bwd_ex(*base, None, 1, None) == _lib.INVALID_VALUE
     assert lib.jattn_bwd_ex(*base, fake(12), -1, None) == _lib.INVALID_VALUE
-    assert lib.jattn_bwd_ex(*base, fake(12), 4, None) == _lib.INVALID_VALUE
+    assert lib.jattn_bwd_ex(*base, fake(12), len(_lib.BWD_STAGES) + 1, None) == _lib.INVALID_VALUE
     # valid event arguments still fail on the invalid tensor arguments, before any HIP call
     bad = list(base)
     bad[0] = None
-    assert lib.jattn_bwd_ex(*bad, fake(12), 3, None) == _lib.INVALID_VALUE
+    assert lib.jattn_bwd_ex(*bad, fake(12), len(_lib.BWD_STAGES), None) == _lib.INVALID_VALUE
 
 
 def test_bwd_rejects_small_workspace(lib):
@@ -135,6 +135,12 @@ def test_workspace_bytes(lib):
     assert lib.jattn_bwd_workspace_bytes(0, 10, 1, 64) == 0
     assert lib.jattn_bwd_workspace_bytes(1, 10, 1, 40) == 0
     w = lib.jattn_bwd_workspace_bytes(16, 1101, 12, 64)
-    # delta rows + two sets of per-workgroup gain partials (9 blocks of 128 rows per pair)
-    assert w >= 16 * 12 * 1101 * 4 + 2 * 16 * 12 * 9 * 64 * 4
+    # normalised K and Q rows (bf16), two statistics per padded query row (9 blocks of 128 rows per
+    # pair) and two sets of per-workgroup gain partials
+    assert w >= 2 * 16 * 12 * 1101 * 64 * 2 + 2 * 16 * 12 * 9 * 128 * 4 + 2 * 16 * 12 * 9 * 64 * 4
     assert w % 256 == 0
+
+
+def test_stage_names_match_header():
+    hdr = open(os.path.join(ROOT, "include", "jattn.h")).read()
+    assert int(re.search(r"#define JATTN_BWD_STAGES (\d+)", hdr).group(1)) == len(_lib.BWD_STAGES)
