@@ -24,6 +24,8 @@
 // tiles ahead into a ring of LDS buffers: no registers or VALU work are spent on staging.
 // dQ is recomputed rather than accumulated across key blocks: fp32 atomics on this chip sustain a
 // few hundred G/s, far below what a key-parallel dQ accumulation would need.
+#include <type_traits>
+
 #include "jattn_device.h"
 #include "jattn_launch.h"
 
@@ -39,6 +41,24 @@ constexpr int bwd_waves_per_eu() { return D <= 72 ? 2 : 1; }
 // tiles would otherwise not leave room for two workgroups per CU.
 template <int D>
 constexpr int bwd_nbuf() { return D == 72 ? 2 : 3; }
+
+// End-of-step barrier of the tile rings. At the end of step t the tile t + 1 must have landed in LDS;
+// the k tiles after it whose loads are already issued (k <= NB - 2) may stay in flight, and each
+// wave issued at least PER loads for each of them. k is wave-uniform.
+template <int PER, int MAXK>
+__device__ __forceinline__ void ring_barrier(int k) {
+  static_assert(MAXK >= 0 && MAXK <= 3, "ring depth");
+  if constexpr (MAXK >= 3) {
+    if (k >= 3) return stream_barrier<3 * PER>();
+  }
+  if constexpr (MAXK >= 2) {
+    if (k >= 2) return stream_barrier<2 * PER>();
+  }
+  if constexpr (MAXK >= 1) {
+    if (k >= 1) return stream_barrier<PER>();
+  }
+  stream_barrier<0>();
+}
 
 // LDS plan of the two main kernels. The swizzled layout (D = 64, 128) serves both row-fragment and
 // transposed reads without bank conflicts; other head dims use padded rows.
@@ -180,37 +200,64 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
 // One 64-key tile: for both 32-key halves S'^T = Kr Q'^T and dP^T - Delta = V dO^T (lane = query),
 // dS^T = P * (dP - Delta) with P = exp2(S' - lse2), then dQn^T += Kr^T dS^T. MASKED: keys at or
 // past n are seeded with -inf (P = 0).
+// The body is written as a two-stage software pipeline over the halves -- row fragments of half 1
+// are read under the products of half 0, and the softmax of half 0 sits between the products of
+// half 1 -- which gives the scheduler independent matrix work to cover LDS and VALU latency.
 template <int D, bool MASKED>
-__device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __bf16* __restrict__ vt, const bf16x8 (&qf)[Dims<D>::KS],
-                                        const bf16x8 (&dof)[Dims<D>::KS], const f32x16& cs, const f32x16& cp,
-                                        f32x16 (&acc)[Dims<D>::MT], int key0, int n, int lane) {
+__device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __bf16* __restrict__ vt,
+                                        const bf16x8 (&qf)[Dims<D>::KS], const bf16x8 (&dof)[Dims<D>::KS],
+                                        const f32x16& cs, const f32x16& cp, f32x16 (&acc)[Dims<D>::MT], int key0,
+                                        int n, int lane) {
   using Dm = Dims<D>;
   using LK = typename DqCfg<D>::LK;
   using LV = typename DqCfg<D>::LV;
+  constexpr int KS = Dm::KS, MT = Dm::MT;
   const int g = lane >> 5, l32 = lane & 31;
+  bf16x8 kr[2][KS], vr[2][KS], f[2][2];
+  f32x16 s[2], dp[2];
+  auto rows = [&](int h) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    f32x16 s = cs, dp = cp;
+    for (int ks = 0; ks < KS; ++ks) {
+      kr[h][ks] = lds_row_frag<LK>(kt, h * 32 + l32, ks * 16 + g * 8);
+      vr[h][ks] = lds_row_frag<LV>(vt, h * 32 + l32, ks * 16 + g * 8);
+    }
+  };
+  auto scores = [&](int h) {
+    s[h] = cs;
+    dp[h] = cp;
     if constexpr (MASKED) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (key0 + h * 32 + (i >> 2) * 8 + g * 4 + (i & 3) >= n) s[i] = -INFINITY;
+        if (key0 + h * 32 + (i >> 2) * 8 + g * 4 + (i & 3) >= n) s[h][i] = -INFINITY;
     }
 #pragma unroll
-    for (int ks = 0; ks < Dm::KS; ++ks) {
-      s = mfma(lds_row_frag<LK>(kt, h * 32 + l32, ks * 16 + g * 8), qf[ks], s);
-      dp = mfma(lds_row_frag<LV>(vt, h * 32 + l32, ks * 16 + g * 8), dof[ks], dp);
+    for (int ks = 0; ks < KS; ++ks) {
+      s[h] = mfma(kr[h][ks], qf[ks], s[h]);
+      dp[h] = mfma(vr[h][ks], dof[ks], dp[h]);
     }
+  };
+  auto softmax = [&](int h) {
     float ds[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[i]) * dp[i];
-    const bf16x8 f0 = to_bf16x8(ds), f1 = to_bf16x8(ds + 8);
+    for (int i = 0; i < 16; ++i) ds[i] = fast_exp2(s[h][i]) * dp[h][i];
+    f[h][0] = to_bf16x8(ds);
+    f[h][1] = to_bf16x8(ds + 8);
+  };
+  auto accumulate = [&](int h) {
 #pragma unroll
-    for (int mt = 0; mt < Dm::MT; ++mt) {
-      acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32, mt * 32, lane), f0, acc[mt]);
-      acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32 + 16, mt * 32, lane), f1, acc[mt]);
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32, mt * 32, lane), f[h][0], acc[mt]);
+      acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32 + 16, mt * 32, lane), f[h][1], acc[mt]);
     }
-  }
+  };
+  rows(0);
+  scores(0);
+  rows(1);
+  scores(1);
+  softmax(0);
+  accumulate(0);
+  softmax(1);
+  accumulate(1);
 }
 
 template <int D>
@@ -284,21 +331,20 @@ void bwd_dq_kernel(BwdArgs a) {
 
   wait_vmem();
   __syncthreads();
+  // One loop over the full tiles and a separate step for the partial one: a masked / unmasked
+  // branch inside the loop makes the two bodies keep the accumulators in different registers, with
+  // copies at the join.
   int cur = 0;
-  for (int t = 0; t < ntiles; ++t) {
+  auto step = [&](auto masked, int t) {
     const bool ahead = t + NB - 1 < ntiles;
     if (ahead) issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
-    if (t < nfull)
-      dq_tile<D, false>(sk + cur * LK::ELEMS, sv + cur * LV::ELEMS, qf, dof, cs, cp, acc, t * kTile, n, lane);
-    else
-      dq_tile<D, true>(sk + cur * LK::ELEMS, sv + cur * LV::ELEMS, qf, dof, cs, cp, acc, t * kTile, n, lane);
-    // the tile after this one has landed (only the newest tile's loads may still be in flight)
-    if (ahead)
-      stream_barrier<DirectTile<D, LK>::MIN_PER_WAVE + DirectTile<D, LV>::MIN_PER_WAVE>();
-    else
-      stream_barrier<0>();
+    dq_tile<D, decltype(masked)::value>(sk + cur * LK::ELEMS, sv + cur * LV::ELEMS, qf, dof, cs, cp, acc, t * kTile,
+                                        n, lane);
+    ring_barrier<DirectTile<D, LK>::MIN_PER_WAVE + DirectTile<D, LV>::MIN_PER_WAVE, NB - 2>(ntiles - 2 - t);
     cur = cur + 1 == NB ? 0 : cur + 1;
-  }
+  };
+  for (int t = 0; t < nfull; ++t) step(std::false_type{}, t);
+  if (nfull < ntiles) step(std::true_type{}, nfull);
 
   // row statistics for the key-parallel kernel, for every row of the block (-inf / 0 past L)
   if (g == 0) {
@@ -321,7 +367,7 @@ void bwd_dq_kernel(BwdArgs a) {
 // One 64-query tile: for both 32-query halves S' = Qs Kf^T and dP - Delta = dO V^T (lane = key),
 // P = exp2(S' - lse2), dS = P * (dP - Delta), then dV^T += dO^T P and dKn^T += Qs^T dS.
 // sl / sd hold -lse2 and -Delta of the tile's rows. KMASK: this wave holds keys at or past n, whose
-// P is forced to zero.
+// P is forced to zero. Written as the same two-stage pipeline over the halves as dq_tile.
 template <int D, bool KMASK>
 __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const __bf16* __restrict__ ot,
                                           const float* __restrict__ sl, const float* __restrict__ sd,
@@ -331,42 +377,64 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const _
   using Dm = Dims<D>;
   using LQ = typename DkdvCfg<D>::LQ;
   using LO = typename DkdvCfg<D>::LO;
+  constexpr int KS = Dm::KS, MT = Dm::MT;
   const int g = lane >> 5, l32 = lane & 31;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    f32x16 s, dp;
+  bf16x8 qr[2][KS], orr[2][KS], pf[2][2], df[2][2];
+  f32x16 s[2], dp[2];
+  auto rows = [&](int h) {  // statistics (the MFMA seeds) and row fragments
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + h * 32 + j4 * 8 + g * 4);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(sd + h * 32 + j4 * 8 + g * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        s[j4 * 4 + e] = l4[e];
-        dp[j4 * 4 + e] = d4[e];
+        s[h][j4 * 4 + e] = l4[e];
+        dp[h][j4 * 4 + e] = d4[e];
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < Dm::KS; ++ks) {
-      s = mfma(lds_row_frag<LQ>(qt, h * 32 + l32, ks * 16 + g * 8), kf[ks], s);
-      dp = mfma(lds_row_frag<LO>(ot, h * 32 + l32, ks * 16 + g * 8), vf[ks], dp);
+    for (int ks = 0; ks < KS; ++ks) {
+      qr[h][ks] = lds_row_frag<LQ>(qt, h * 32 + l32, ks * 16 + g * 8);
+      orr[h][ks] = lds_row_frag<LO>(ot, h * 32 + l32, ks * 16 + g * 8);
     }
+  };
+  auto scores = [&](int h) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s[h] = mfma(qr[h][ks], kf[ks], s[h]);
+      dp[h] = mfma(orr[h][ks], vf[ks], dp[h]);
+    }
+  };
+  auto probs = [&](int h) {
     float p[16], ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      p[i] = fast_exp2(s[i]);
+      p[i] = fast_exp2(s[h][i]);
       if constexpr (KMASK) p[i] = kvalid ? p[i] : 0.f;
-      ds[i] = p[i] * dp[i];
+      ds[i] = p[i] * dp[h][i];
     }
-    const bf16x8 pf0 = to_bf16x8(p), pf1 = to_bf16x8(p + 8);
-    const bf16x8 df0 = to_bf16x8(ds), df1 = to_bf16x8(ds + 8);
+    pf[h][0] = to_bf16x8(p);
+    pf[h][1] = to_bf16x8(p + 8);
+    df[h][0] = to_bf16x8(ds);
+    df[h][1] = to_bf16x8(ds + 8);
+  };
+  auto accumulate = [&](int h) {
 #pragma unroll
-    for (int mt = 0; mt < Dm::MT; ++mt) {
-      dva[mt] = mfma(lds_tr_frag<LO>(ot, h * 32, mt * 32, lane), pf0, dva[mt]);
-      dva[mt] = mfma(lds_tr_frag<LO>(ot, h * 32 + 16, mt * 32, lane), pf1, dva[mt]);
-      dka[mt] = mfma(lds_tr_frag<LQ>(qt, h * 32, mt * 32, lane), df0, dka[mt]);
-      dka[mt] = mfma(lds_tr_frag<LQ>(qt, h * 32 + 16, mt * 32, lane), df1, dka[mt]);
+    for (int mt = 0; mt < MT; ++mt) {
+      dva[mt] = mfma(lds_tr_frag<LO>(ot, h * 32, mt * 32, lane), pf[h][0], dva[mt]);
+      dva[mt] = mfma(lds_tr_frag<LO>(ot, h * 32 + 16, mt * 32, lane), pf[h][1], dva[mt]);
+      dka[mt] = mfma(lds_tr_frag<LQ>(qt, h * 32, mt * 32, lane), df[h][0], dka[mt]);
+      dka[mt] = mfma(lds_tr_frag<LQ>(qt, h * 32 + 16, mt * 32, lane), df[h][1], dka[mt]);
     }
-  }
+  };
+  rows(0);
+  scores(0);
+  rows(1);
+  scores(1);
+  probs(0);
+  accumulate(0);
+  probs(1);
+  accumulate(1);
 }
 
 template <int D, bool KMASK>
@@ -406,19 +474,17 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t b
   for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
   wait_vmem();
   __syncthreads();
-  constexpr int NEWEST = DirectTile<D, LQ>::MIN_PER_WAVE + DirectTile<D, LO>::MIN_PER_WAVE;
+  constexpr int PER = DirectTile<D, LQ>::MIN_PER_WAVE + DirectTile<D, LO>::MIN_PER_WAVE;
   int cur = 0;
   for (int t = 0; t < ntiles; ++t) {
     const bool ahead = t + NB - 1 < ntiles;
     if (ahead) issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
     dkdv_tile<D, KMASK>(sq + cur * LQ::ELEMS, so + cur * LO::ELEMS, sl + cur * kTile, sd + cur * kTile, kf, vf,
                         dva, dka, kvalid, lane);
-    if (!ahead)
-      stream_barrier<0>();
-    else if (wave < 2)
-      stream_barrier<NEWEST + 1>();  // (these waves also load a statistics row per tile)
+    if (wave < 2)
+      ring_barrier<PER + 1, NB - 2>(ntiles - 2 - t);  // (these waves also load a statistics row per tile)
     else
-      stream_barrier<NEWEST>();
+      ring_barrier<PER, NB - 2>(ntiles - 2 - t);
     cur = cur + 1 == NB ? 0 : cur + 1;
   }
 }
