@@ -55,12 +55,12 @@ jattn_status check_sizes(int B, int L, int H, int D) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-  size_t kr, qs, nlse2, ndelta, part_q, part_k, total;
+  size_t kr, qs, nlse2, ndelta, part, total;
 };
 
 // Normalised key rows and pre-scaled normalised query rows (bf16, [B, H, L, D]), the two row
 // statistics (fp32, [B, H, lp] with lp = L rounded up to whole row blocks) and the per-workgroup
-// gain-gradient partials (fp32, [items, D] for each side), each 256-byte aligned.
+// partial sums of the gain-gradient factor (fp32, [items, D]), each 256-byte aligned.
 WorkspaceLayout workspace_layout(int B, int L, int H, int D) {
   const size_t nblk = (L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock;
   const size_t items = (size_t)B * H * nblk, lp = nblk * kBwdRowsPerBlock;
@@ -71,9 +71,8 @@ WorkspaceLayout workspace_layout(int B, int L, int H, int D) {
   w.qs = w.kr + rows;
   w.nlse2 = w.qs + rows;
   w.ndelta = w.nlse2 + stats;
-  w.part_q = w.ndelta + stats;
-  w.part_k = w.part_q + parts;
-  w.total = w.part_k + parts;
+  w.part = w.ndelta + stats;
+  w.total = w.part + parts;
   return w;
 }
 
@@ -185,8 +184,7 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
   a.qs = reinterpret_cast<uint16_t*>(ws + wl.qs);
   a.nlse2 = reinterpret_cast<float*>(ws + wl.nlse2);
   a.ndelta = reinterpret_cast<float*>(ws + wl.ndelta);
-  a.part_q = reinterpret_cast<float*>(ws + wl.part_q);
-  a.part_k = reinterpret_cast<float*>(ws + wl.part_k);
+  a.part = reinterpret_cast<float*>(ws + wl.part);
   a.B = B;
   a.L = L;
   a.H = H;

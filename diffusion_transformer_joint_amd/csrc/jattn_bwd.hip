@@ -7,19 +7,25 @@
 //   dV = P^T dO,  dQn = scale dS Kn,  dKn = scale dS^T Qn,
 //   RMSNorm backward: dx = r (g * dxn) - x (r^3 / D) <g * dxn, x>,   dg = sum_rows dxn * x * r.
 //
+// Gain gradients. The gains enter the scores only through their product w = g_q * g_k:
+// S_ij = scale * sum_d Xq_i[d] w[d] Xk_j[d] with Xq = q r_q, Xk = k r_k. So dg_q = g_k * T and
+// dg_k = g_q * T with T[d] = scale * sum_ij dS_ij Xq_i[d] Xk_j[d] = sum_j dKn_j[d] Xk_j[d] / g_q[d]: one
+// column sum, taken in the key-parallel kernel.
+//
 // Four kernels, no atomics:
 //  * prenorm: Kr = bf16(k * r_k) (normalised keys without gain) into the workspace, [B, H, L, D].
 //  * dq kernel (query-parallel, like the forward): each wave owns 32 queries and streams Kr and V;
 //    per 32-key step S^T, dP^T (both: lane = query), dS^T in registers, dQn^T += Kr^T dS^T with Kr^T
-//    read by ds_read_b64_tr_b16. Epilogue: Q-side RMSNorm backward, dq, dg_q partials, and for the
-//    key-parallel kernel the pre-scaled normalised queries Qs = bf16(scale log2(e) q r_q) and the
-//    row statistics -lse log2(e) and -Delta.
+//    read by ds_read_b64_tr_b16. Epilogue: Q-side RMSNorm backward and dq, and for the key-parallel
+//    kernel the pre-scaled normalised queries Qs = bf16(scale log2(e) q r_q) and the row statistics
+//    -lse log2(e) and -Delta.
 //  * dkdv kernel (key-parallel): each wave owns 32 keys (K rows normalised with both gains, and V
 //    rows, in registers) and streams Qs, dO and the row statistics; per 32-query step S, dP
 //    (lane = key), then dV^T += dO^T P and dKn^T += Qs^T dS with the transposed operands read by
-//    ds_read_b64_tr_b16. Epilogue: K-side RMSNorm backward, dk, dv and dg_k partials. Padded keys
-//    get exact zeros.
-//  * a small kernel sums the gain partials in a fixed order (deterministic dgains).
+//    ds_read_b64_tr_b16. Epilogue: K-side RMSNorm backward, dk, dv and per-workgroup partial sums of
+//    T. Padded keys get exact zeros.
+//  * a small kernel sums the partials in a fixed order and scales them by the other gain
+//    (deterministic dgains).
 // The streamed tiles go straight from memory into LDS (buffer loads with the LDS bit), issued two
 // tiles ahead into a ring of LDS buffers: no registers or VALU work are spent on staging.
 // dQ is recomputed rather than accumulated across key blocks: fp32 atomics on this chip sustain a
@@ -67,9 +73,7 @@ struct DqCfg {
   using LK = Lay<D, kSwizzled>;  // normalised key rows: S (row fragments) and dQ (transposed)
   using LV = Lay<D, kSwizzled>;  // value rows: dP (row fragments)
   static constexpr int NB = bwd_nbuf<D>();
-  static constexpr int STAGE = NB * (LK::ELEMS + LV::ELEMS) * 2;
-  static constexpr int SCRATCH = (kBlockRows + 8) * Dims<D>::DM * 4;
-  static constexpr int BYTES = STAGE > SCRATCH ? STAGE : SCRATCH;
+  static constexpr int BYTES = NB * (LK::ELEMS + LV::ELEMS) * 2;
 };
 
 template <int D>
@@ -137,9 +141,9 @@ __global__ __launch_bounds__(kThreads) void bwd_prenorm_kernel(BwdArgs a) {
 // holds d = 32*mt + 8*(i/4) + 4*g + i%4; the other half of the row is in lane l^32). On entry dxn
 // holds the gradient with respect to the normalised row divided by gpre[d] (the factor the MFMA
 // operands left out); `gain` is the row's own RMSNorm gain. If `exists`, writes the bf16 gradient row
-// (zeros when not `valid`, i.e. a padded key) and, if xsrow is set, bf16(x * r * xs_mul). On return
-// dxn holds the dg contributions dxn * x * r (zeros for rows that are not valid).
-template <int D>
+// (zeros when not `valid`, i.e. a padded key) and, if xsrow is set, bf16(x * r * xs_mul). With TSUM,
+// dxn holds dxn * x * r on return (this row's term of T; zeros for rows that are not valid).
+template <int D, bool TSUM>
 __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT], const uint16_t* __restrict__ xrow,
                                                      const float* __restrict__ gain, const float* __restrict__ gpre,
                                                      float r, bool valid, bool exists,
@@ -147,7 +151,7 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
                                                      float xs_mul, int g) {
   using Dm = Dims<D>;
   float x[Dm::MT][16];
-  float gv[Dm::MT][16];
+  float gd[Dm::MT][16];  // gain * (gradient with respect to the normalised row)
   float t = 0.f;
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt)
@@ -160,9 +164,8 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
       for (int e = 0; e < 4; ++e) {
         const int i = j4 * 4 + e;
         x[mt][i] = xv[e];
-        gv[mt][i] = d0 < D ? gain[d0 + e] : 0.f;
-        dxn[mt][i] *= d0 < D ? gpre[d0 + e] : 0.f;
-        t += gv[mt][i] * dxn[mt][i] * xv[e];
+        gd[mt][i] = d0 < D ? gain[d0 + e] * gpre[d0 + e] * dxn[mt][i] : 0.f;
+        t += gd[mt][i] * xv[e];
       }
     }
   t += __shfl_xor(t, 32);
@@ -177,7 +180,7 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = j4 * 4 + e;
-        y[e] = valid ? r * gv[mt][i] * dxn[mt][i] - x[mt][i] * c3 : 0.f;
+        y[e] = valid ? r * gd[mt][i] - x[mt][i] * c3 : 0.f;
       }
       if (exists && d0 < D) {
         *reinterpret_cast<u32x2*>(dxrow + d0) = (u32x2){pack2(y[0], y[1]), pack2(y[2], y[3])};
@@ -186,10 +189,12 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
           *reinterpret_cast<u32x2*>(xsrow + d0) = (u32x2){pack2(x[mt][i] * xs, x[mt][i + 1] * xs),
                                                           pack2(x[mt][i + 2] * xs, x[mt][i + 3] * xs)};
       }
+      if constexpr (TSUM) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = j4 * 4 + e;
-        dxn[mt][i] = valid ? dxn[mt][i] * x[mt][i] * r : 0.f;  // reuse as the dg contribution
+        for (int e = 0; e < 4; ++e) {
+          const int i = j4 * 4 + e;
+          dxn[mt][i] = valid ? dxn[mt][i] * x[mt][i] * r : 0.f;
+        }
       }
     }
 }
@@ -200,9 +205,8 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
 // One 64-key tile: for both 32-key halves S'^T = Kr Q'^T and dP^T - Delta = V dO^T (lane = query),
 // dS^T = P * (dP - Delta) with P = exp2(S' - lse2), then dQn^T += Kr^T dS^T. MASKED: keys at or
 // past n are seeded with -inf (P = 0).
-// The body is written as a two-stage software pipeline over the halves -- row fragments of half 1
-// are read under the products of half 0, and the softmax of half 0 sits between the products of
-// half 1 -- which gives the scheduler independent matrix work to cover LDS and VALU latency.
+// The halves run one after the other (issuing the second half's row reads under the first half's
+// products measured no faster).
 template <int D, bool MASKED>
 __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __bf16* __restrict__ vt,
                                         const bf16x8 (&qf)[Dims<D>::KS], const bf16x8 (&dof)[Dims<D>::KS],
@@ -252,10 +256,10 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
   };
   rows(0);
   scores(0);
-  rows(1);
-  scores(1);
   softmax(0);
   accumulate(0);
+  rows(1);
+  scores(1);
   softmax(1);
   accumulate(1);
 }
@@ -355,10 +359,8 @@ void bwd_dq_kernel(BwdArgs a) {
   // dQn = scale * g_k * (dS Kr): the streamed key rows carry no gain
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) acc[mt] *= a.scale;
-  rmsnorm_backward_row<D>(acc, a.q + roff, a.gains, a.gains + D, rq, qvalid, qvalid, a.dq + roff,
-                          a.qs + ((size_t)bh * L + qrow) * D, a.c, g);
-  // (the loop ended with every load retired and a barrier: the LDS ring is free for the scratch)
-  block_column_sums<D>(acc, reinterpret_cast<float*>(smem), a.part_q + (size_t)item * D, tid);
+  rmsnorm_backward_row<D, false>(acc, a.q + roff, a.gains, a.gains + D, rq, qvalid, qvalid, a.dq + roff,
+                                 a.qs + ((size_t)bh * L + qrow) * D, a.c, g);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -367,7 +369,7 @@ void bwd_dq_kernel(BwdArgs a) {
 // One 64-query tile: for both 32-query halves S' = Qs Kf^T and dP - Delta = dO V^T (lane = key),
 // P = exp2(S' - lse2), dS = P * (dP - Delta), then dV^T += dO^T P and dKn^T += Qs^T dS.
 // sl / sd hold -lse2 and -Delta of the tile's rows. KMASK: this wave holds keys at or past n, whose
-// P is forced to zero. Written as the same two-stage pipeline over the halves as dq_tile.
+// P is forced to zero.
 template <int D, bool KMASK>
 __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const __bf16* __restrict__ ot,
                                           const float* __restrict__ sl, const float* __restrict__ sd,
@@ -429,10 +431,10 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const _
   };
   rows(0);
   scores(0);
-  rows(1);
-  scores(1);
   probs(0);
   accumulate(0);
+  rows(1);
+  scores(1);
   probs(1);
   accumulate(1);
 }
@@ -518,7 +520,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         *reinterpret_cast<u32x4*>(a.dv + roff + c * 8) = (u32x4){0u, 0u, 0u, 0u};
       }
     }
-    for (int d = tid; d < D; d += kThreads) a.part_k[(size_t)item * D + d] = 0.f;
+    for (int d = tid; d < D; d += kThreads) a.part[(size_t)item * D + d] = 0.f;
     return;
   }
 
@@ -564,8 +566,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) dka[mt] *= kLn2;
   if (kin) {
-    rmsnorm_backward_row<D>(dka, a.k + roff, a.gains + D, a.gains, rk, kvalid, true, a.dk + roff, nullptr, 0.f,
-                            g);
+    rmsnorm_backward_row<D, true>(dka, a.k + roff, a.gains + D, a.gains, rk, kvalid, true, a.dk + roff, nullptr,
+                                  0.f, g);
   } else {
 #pragma unroll
     for (int mt = 0; mt < Dm::MT; ++mt)
@@ -573,17 +575,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
       for (int i = 0; i < 16; ++i) dka[mt][i] = 0.f;
   }
   __syncthreads();
-  block_column_sums<D>(dka, reinterpret_cast<float*>(smem), a.part_k + (size_t)item * D, tid);
+  block_column_sums<D>(dka, reinterpret_cast<float*>(smem), a.part + (size_t)item * D, tid);
 }
 
 // ------------------------------------------------------------------------------------------------
-// dgains[side][d] = sum over workgroups of the partials, in a fixed order. Block (side, d); lane j
-// sums items j, j + 64, ... with the loads issued in batches of 8, then a fixed butterfly.
-__global__ __launch_bounds__(64) void dg_reduce_kernel(const float* __restrict__ part_q,
-                                                       const float* __restrict__ part_k, int items,
-                                                       int D, float* __restrict__ dgains) {
-  const int side = blockIdx.x / D, d = blockIdx.x - side * D;
-  const float* p = (side ? part_k : part_q) + d;
+// dgains[0][d] = g_k[d] * T[d] and dgains[1][d] = g_q[d] * T[d], with T[d] the sum over workgroups of
+// the partials in a fixed order. Block d; lane j sums items j, j + 64, ... with the loads issued in
+// batches of 8, then a fixed butterfly.
+__global__ __launch_bounds__(64) void dg_reduce_kernel(const float* __restrict__ part, const float* __restrict__ gains,
+                                                       int items, int D, float* __restrict__ dgains) {
+  const int d = blockIdx.x;
+  const float* p = part + d;
   float s = 0.f;
   int i = threadIdx.x;
   for (; i + 7 * 64 < items; i += 8 * 64) {
@@ -596,7 +598,10 @@ __global__ __launch_bounds__(64) void dg_reduce_kernel(const float* __restrict__
   for (; i < items; i += 64) s += p[(size_t)i * D];
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-  if (threadIdx.x == 0) dgains[side * D + d] = s;
+  if (threadIdx.x == 0) {
+    dgains[d] = gains[D + d] * s;
+    dgains[D + d] = gains[d] * s;
+  }
 }
 
 template <int D>
@@ -619,8 +624,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, const hipEvent_t* events, int n
   if ((e = recorded()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, grid, dim3(kThreads), 0, stream, a);
   if ((e = recorded()) != hipSuccess) return e;
-  hipLaunchKernelGGL(dg_reduce_kernel, dim3(2 * D), dim3(64), 0, stream, a.part_q, a.part_k, a.items, D,
-                     a.dgains);
+  hipLaunchKernelGGL(dg_reduce_kernel, dim3(D), dim3(64), 0, stream, a.part, a.gains, a.items, D, a.dgains);
   return recorded();
 }
 

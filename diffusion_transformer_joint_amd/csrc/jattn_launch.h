@@ -39,8 +39,7 @@ struct BwdArgs {
   uint16_t* qs;            // workspace [B, H, L, D]: bf16(scale * log2(e) * q * r_q)
   float* nlse2;            // workspace [B, H, lp]: -lse * log2(e) (-inf past L)
   float* ndelta;           // workspace [B, H, lp]: -rowsum(dout * out) (0 past L)
-  float* part_q;           // workspace [items, D]: gain-gradient partials of the query blocks
-  float* part_k;           // workspace [items, D]: gain-gradient partials of the key blocks
+  float* part;             // workspace [items, D]: per key block partial sums of T (see jattn_bwd.hip)
   int B, L, H;
   float scale;
   float c;                 // scale * log2(e)
