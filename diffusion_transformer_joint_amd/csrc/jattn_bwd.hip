@@ -137,14 +137,37 @@ __global__ __launch_bounds__(kThreads) void bwd_prenorm_kernel(BwdArgs a) {
   }
 }
 
+// A wave row in the C/D layout (pair j4 of tile mt holds d = 32 mt + 8 j4 + 4 g + [0..3]) as raw bf16
+// pairs, for the RMSNorm backward of the epilogue. Where registers allow it the row is loaded in the
+// prologue and kept through the tile loop: loading it after the loop leaves its latency, for every
+// workgroup at once, between the last tile and the epilogue.
+template <int D>
+struct RowC {
+  u32x2 w[Dims<D>::MT][4];
+};
+template <int D>
+constexpr bool keep_row_c() { return D != 72; }  // D = 72 has no registers to spare at two waves/SIMD
+
+template <int D>
+__device__ __forceinline__ void load_row_c(RowC<D>& x, const uint16_t* __restrict__ row, bool valid, int g) {
+#pragma unroll
+  for (int mt = 0; mt < Dims<D>::MT; ++mt)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int d0 = mt * 32 + j4 * 8 + g * 4;
+      x.w[mt][j4] = valid && d0 < D ? *reinterpret_cast<const u32x2*>(row + d0) : (u32x2){0u, 0u};
+    }
+}
+
 // RMSNorm backward for one wave row held in the C/D layout (lane = row; register i of tile mt
 // holds d = 32*mt + 8*(i/4) + 4*g + i%4; the other half of the row is in lane l^32). On entry dxn
 // holds the gradient with respect to the normalised row divided by gpre[d] (the factor the MFMA
-// operands left out); `gain` is the row's own RMSNorm gain. If `exists`, writes the bf16 gradient row
+// operands left out); xc is the raw row (zeros when not `valid`); `gain` is the row's own RMSNorm
+// gain. If `exists`, writes the bf16 gradient row
 // (zeros when not `valid`, i.e. a padded key) and, if xsrow is set, bf16(x * r * xs_mul). With TSUM,
 // dxn holds dxn * x * r on return (this row's term of T; zeros for rows that are not valid).
 template <int D, bool TSUM>
-__device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT], const uint16_t* __restrict__ xrow,
+__device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT], const RowC<D>& xc,
                                                      const float* __restrict__ gain, const float* __restrict__ gpre,
                                                      float r, bool valid, bool exists,
                                                      uint16_t* __restrict__ dxrow, uint16_t* __restrict__ xsrow,
@@ -158,8 +181,8 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = mt * 32 + j4 * 8 + g * 4;
-      float xv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (valid && d0 < D) unpack4(*reinterpret_cast<const u32x2*>(xrow + d0), xv);
+      float xv[4];
+      unpack4(xc.w[mt][j4], xv);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = j4 * 4 + e;
@@ -310,6 +333,8 @@ void bwd_dq_kernel(BwdArgs a) {
     rq = rmsnorm_row_frags<D>(qf, x, a.gains, a.gains + D, a.c, a.eps, qvalid, g);
   }
   load_row_frags_raw<D>(dof, a.dout + roff, qvalid, g);
+  RowC<D> xq;
+  if constexpr (keep_row_c<D>()) load_row_c<D>(xq, a.q + roff, qvalid, g);
   float delta = 0.f;
   {
     float o[Dm::KS][8];
@@ -359,7 +384,8 @@ void bwd_dq_kernel(BwdArgs a) {
   // dQn = scale * g_k * (dS Kr): the streamed key rows carry no gain
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) acc[mt] *= a.scale;
-  rmsnorm_backward_row<D, false>(acc, a.q + roff, a.gains, a.gains + D, rq, qvalid, qvalid, a.dq + roff,
+  if constexpr (!keep_row_c<D>()) load_row_c<D>(xq, a.q + roff, qvalid, g);
+  rmsnorm_backward_row<D, false>(acc, xq, a.gains, a.gains + D, rq, qvalid, qvalid, a.dq + roff,
                                  a.qs + ((size_t)bh * L + qrow) * D, a.c, g);
 }
 
@@ -532,6 +558,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
     rk = rmsnorm_row_frags<D>(kf, x, a.gains, a.gains + D, 1.f, a.eps, kvalid, g);  // k r_k g_q g_k
   }
   load_row_frags_raw<D>(vf, a.v + roff, kvalid, g);
+  RowC<D> xk;
+  if constexpr (keep_row_c<D>()) load_row_c<D>(xk, a.k + roff, kvalid, g);
 
   f32x16 dva[Dm::MT], dka[Dm::MT];
 #pragma unroll
@@ -566,7 +594,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) dka[mt] *= kLn2;
   if (kin) {
-    rmsnorm_backward_row<D, true>(dka, a.k + roff, a.gains + D, a.gains, rk, kvalid, true, a.dk + roff, nullptr,
+    if constexpr (!keep_row_c<D>()) load_row_c<D>(xk, a.k + roff, kvalid, g);
+    rmsnorm_backward_row<D, true>(dka, xk, a.gains + D, a.gains, rk, kvalid, true, a.dk + roff, nullptr,
                                   0.f, g);
   } else {
 #pragma unroll
