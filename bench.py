@@ -96,18 +96,23 @@ def main():
     lib = _lib.load()
     ws_bytes = int(lib.jattn_bwd_workspace_bytes(B, L, H, D))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    fws_bytes = int(lib.jattn_fwd_workspace_bytes(B, L, H, D))
+    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     scale, eps = ctypes.c_float(inp["scale"]), ctypes.c_float(inp["eps"])
     vlp = None if vl is None else vl.data_ptr()
     fwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), vlp, B, L, H, D, scale, eps,
-                out.data_ptr(), lse.data_ptr(), sp)
+                out.data_ptr(), lse.data_ptr(), fws.data_ptr(), fws_bytes, sp)
     bwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), vlp, out.data_ptr(), lse.data_ptr(),
                 dout.data_ptr(), B, L, H, D, scale, eps, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                dg.data_ptr(), ws.data_ptr(), ws_bytes, sp)
+                dg.data_ptr(), ws.data_ptr(), ws_bytes, fws.data_ptr(), sp)
 
-    def fwd():
-        _lib.check("jattn_fwd", lib.jattn_fwd(*fwd_args))
+    def fwd(events=None):
+        if events is None:
+            _lib.check("jattn_fwd", lib.jattn_fwd(*fwd_args))
+        else:
+            _lib.check("jattn_fwd_ex", lib.jattn_fwd_ex(*fwd_args[:-1], events, len(_lib.FWD_STAGES), sp))
 
     def bwd(events=None):
         if events is None:
@@ -133,31 +138,37 @@ def main():
         bwd()
     torch.cuda.synchronize()
 
-    # Timed region: K steps of forward + backward. Per step, events bracket the forward kernel and
-    # the backward's kernels (recorded by the library on the same stream via jattn_bwd_ex).
+    # Timed region: K steps of forward + backward. Per step, an event before the forward and the
+    # events the library records after each of its kernels (jattn_fwd_ex / jattn_bwd_ex, same stream)
+    # give every kernel's duration.
     K = args.steps
-    ev_fwd0 = [new_event() for _ in range(K)]
-    ev_fwd1 = [new_event() for _ in range(K)]
-    ev_bwd = [[new_event() for _ in _lib.BWD_STAGES] for _ in range(K)]
-    arrays = [(ctypes.c_void_p * len(_lib.BWD_STAGES))(*[e.cuda_event for e in evs]) for evs in ev_bwd]
-    handles = [ctypes.cast(a, ctypes.c_void_p) for a in arrays]
+    stages = [f"{n}<{D}> (fwd)" if n == "prenorm_kernel" else f"{n}<{D}>" for n in _lib.FWD_STAGES]
+    stages += [f"{n}<{D}> (bwd)" if n == "prenorm_kernel" else (n if n == "dg_reduce_kernel" else f"{n}<{D}>")
+               for n in _lib.BWD_STAGES]
+    nf = len(_lib.FWD_STAGES)
+    ev0 = [new_event() for _ in range(K)]
+    ev = [[new_event() for _ in stages] for _ in range(K)]
+
+    def handle(evs):
+        arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+        return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+    fh = [handle(ev[i][:nf]) for i in range(K)]
+    bh = [handle(ev[i][nf:]) for i in range(K)]
     start, end = new_event(), new_event()
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):
-        ev_fwd0[i].record(stream)
-        fwd()
-        ev_fwd1[i].record(stream)
-        bwd(handles[i])
+        ev0[i].record(stream)
+        fwd(fh[i][1])
+        bwd(bh[i][1])
     end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
-    kern_ms = {f"fwd_kernel<{D}>": sum(ev_fwd0[i].elapsed_time(ev_fwd1[i]) for i in range(K)) / K}
-    for j, name in enumerate(_lib.BWD_STAGES):
-        prev = [ev_fwd1[i] if j == 0 else ev_bwd[i][j - 1] for i in range(K)]
-        key = name if name == "dg_reduce_kernel" else f"{name}<{D}>"
-        kern_ms[key] = sum(prev[i].elapsed_time(ev_bwd[i][j]) for i in range(K)) / K
-    ms_fwd = kern_ms[f"fwd_kernel<{D}>"]
+    kern_ms = {}
+    for j, name in enumerate(stages):
+        kern_ms[name] = sum((ev0[i] if j == 0 else ev[i][j - 1]).elapsed_time(ev[i][j]) for i in range(K)) / K
+    ms_fwd = sum(ev0[i].elapsed_time(ev[i][nf - 1]) for i in range(K)) / K
     ms_bwd = ms_step - ms_fwd
 
     vlist = None if inp["valid_len"] is None else inp["valid_len"].tolist()

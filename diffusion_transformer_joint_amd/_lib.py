@@ -15,9 +15,11 @@ STATUS = {0: "JATTN_SUCCESS", 1: "JATTN_ERROR_INVALID_VALUE", 2: "JATTN_ERROR_NO
           3: "JATTN_ERROR_WORKSPACE", 4: "JATTN_ERROR_HIP"}
 SUCCESS, INVALID_VALUE, NOT_SUPPORTED, WORKSPACE, HIP = range(5)
 
-EXPORTED = ("jattn_fwd", "jattn_bwd", "jattn_bwd_ex", "jattn_bwd_workspace_bytes",
+EXPORTED = ("jattn_fwd", "jattn_fwd_ex", "jattn_fwd_workspace_bytes", "jattn_bwd", "jattn_bwd_ex", "jattn_bwd_workspace_bytes",
             "jattn_status_string", "jattn_abi_version")
-BWD_STAGES = ("bwd_prenorm_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "dg_reduce_kernel")
+ABI_VERSION = 3
+FWD_STAGES = ("prenorm_kernel", "fwd_kernel")
+BWD_STAGES = ("prenorm_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "dg_reduce_kernel")
 
 _lock = threading.Lock()
 _lib = None
@@ -44,19 +46,26 @@ def load() -> ctypes.CDLL:
                               "`python -m diffusion_transformer_joint_amd.build`")
         lib = ctypes.CDLL(LIB_PATH)
         lib.jattn_fwd.restype = I
-        lib.jattn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, F, P, P, P]
+        lib.jattn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, F, P, P, P, ctypes.c_size_t, P]
+        lib.jattn_fwd_ex.restype = I
+        lib.jattn_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, F, P, P, P, ctypes.c_size_t, P, I, P]
+        lib.jattn_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.jattn_fwd_workspace_bytes.argtypes = [I, I, I, I]
         lib.jattn_bwd.restype = I
         lib.jattn_bwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, F, P, P, P, P, P,
-                                  ctypes.c_size_t, P]
+                                  ctypes.c_size_t, P, P]
         lib.jattn_bwd_ex.restype = I
         lib.jattn_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, F, P, P, P, P, P,
-                                     ctypes.c_size_t, P, I, P]
+                                     ctypes.c_size_t, P, P, I, P]
         lib.jattn_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.jattn_bwd_workspace_bytes.argtypes = [I, I, I, I]
         lib.jattn_status_string.restype = ctypes.c_char_p
         lib.jattn_status_string.argtypes = [I]
         lib.jattn_abi_version.restype = I
         lib.jattn_abi_version.argtypes = []
+        if lib.jattn_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI version {lib.jattn_abi_version()}, expected {ABI_VERSION}; "
+                              "rebuild it")
         _lib = lib
         return lib
 

@@ -12,7 +12,7 @@ namespace {
 
 using jattn::kBwdRowsPerBlock;
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 3;
 
 bool supported_head_dim(int D) { return D == 32 || D == 64 || D == 72 || D == 128; }
 
@@ -93,14 +93,22 @@ const char* jattn_status_string(jattn_status s) {
   return "JATTN_UNKNOWN_STATUS";
 }
 
+size_t jattn_fwd_workspace_bytes(int B, int L, int H, int D) {
+  if (check_sizes(B, L, H, D) != JATTN_SUCCESS) return 0;
+  return round_up((size_t)B * H * L * D * 2, 256);  // the normalised key rows
+}
+
 size_t jattn_bwd_workspace_bytes(int B, int L, int H, int D) {
   if (check_sizes(B, L, H, D) != JATTN_SUCCESS) return 0;
   return workspace_layout(B, L, H, D).total;
 }
 
-jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float* gains,
-                       const int32_t* valid_len, int B, int L, int H, int D, float softmax_scale,
-                       float eps, void* out, float* lse, hipStream_t stream) {
+jattn_status jattn_fwd_ex(const void* q, const void* k, const void* v, const float* gains,
+                          const int32_t* valid_len, int B, int L, int H, int D, float softmax_scale,
+                          float eps, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream) {
+  if (n_stage_events < 0 || n_stage_events > JATTN_FWD_STAGES || (n_stage_events > 0 && !stage_events))
+    return JATTN_ERROR_INVALID_VALUE;
   if (!q || !k || !v || !gains || !out || !lse) return JATTN_ERROR_INVALID_VALUE;
   const jattn_status st = check_sizes(B, L, H, D);
   if (st != JATTN_SUCCESS) return st;
@@ -108,15 +116,19 @@ jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float*
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(gains, 4) ||
       !aligned(lse, 4) || !aligned(valid_len, 4))
     return JATTN_ERROR_INVALID_VALUE;
+  const size_t wsb = jattn_fwd_workspace_bytes(B, L, H, D);
+  if (!workspace || workspace_bytes < wsb) return JATTN_ERROR_WORKSPACE;
+  if (!aligned(workspace, 256)) return JATTN_ERROR_INVALID_VALUE;
   const size_t tb = (size_t)B * L * H * D * 2, lb = (size_t)B * H * L * 4;
   const Range ins[] = {{q, tb}, {k, tb}, {v, tb}, {gains, (size_t)2 * D * 4}, {valid_len, (size_t)B * 4}};
-  const Range outs[] = {{out, tb}, {lse, lb}};
-  if (!outputs_disjoint(outs, 2, ins, 5)) return JATTN_ERROR_INVALID_VALUE;
+  const Range outs[] = {{out, tb}, {lse, lb}, {workspace, wsb}};
+  if (!outputs_disjoint(outs, 3, ins, 5)) return JATTN_ERROR_INVALID_VALUE;
 
   jattn::FwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
+  a.kr = static_cast<const uint16_t*>(workspace);
   a.gains = gains;
   a.valid_len = valid_len;
   a.out = static_cast<uint16_t*>(out);
@@ -128,23 +140,33 @@ jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float*
   a.eps = eps;
   a.nblk = (L + jattn::fwd_rows_per_block(D) - 1) / jattn::fwd_rows_per_block(D);
   a.items = B * H * a.nblk;
-  return jattn::launch_fwd(D, a, stream) == hipSuccess ? JATTN_SUCCESS : JATTN_ERROR_HIP;
+  return jattn::launch_fwd(D, a, stage_events, n_stage_events, stream) == hipSuccess ? JATTN_SUCCESS
+                                                                                  : JATTN_ERROR_HIP;
+}
+
+jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float* gains,
+                       const int32_t* valid_len, int B, int L, int H, int D, float softmax_scale,
+                       float eps, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return jattn_fwd_ex(q, k, v, gains, valid_len, B, L, H, D, softmax_scale, eps, out, lse, workspace,
+                      workspace_bytes, nullptr, 0, stream);
 }
 
 jattn_status jattn_bwd(const void* q, const void* k, const void* v, const float* gains,
                        const int32_t* valid_len, const void* out, const float* lse, const void* dout,
                        int B, int L, int H, int D, float softmax_scale, float eps, void* dq, void* dk,
                        void* dv, float* dgains, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+                       const void* fwd_workspace, hipStream_t stream) {
   return jattn_bwd_ex(q, k, v, gains, valid_len, out, lse, dout, B, L, H, D, softmax_scale, eps, dq, dk, dv,
-                      dgains, workspace, workspace_bytes, nullptr, 0, stream);
+                      dgains, workspace, workspace_bytes, fwd_workspace, nullptr, 0, stream);
 }
 
 jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const float* gains,
                           const int32_t* valid_len, const void* out, const float* lse, const void* dout,
                           int B, int L, int H, int D, float softmax_scale, float eps, void* dq, void* dk,
                           void* dv, float* dgains, void* workspace, size_t workspace_bytes,
-                          const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream) {
+                          const void* fwd_workspace, const hipEvent_t* stage_events, int n_stage_events,
+                          hipStream_t stream) {
   if (n_stage_events < 0 || n_stage_events > JATTN_BWD_STAGES || (n_stage_events > 0 && !stage_events))
     return JATTN_ERROR_INVALID_VALUE;
   if (!q || !k || !v || !gains || !out || !lse || !dout || !dq || !dk || !dv || !dgains)
@@ -158,13 +180,14 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
     return JATTN_ERROR_INVALID_VALUE;
   const WorkspaceLayout wl = workspace_layout(B, L, H, D);
   if (!workspace || workspace_bytes < wl.total) return JATTN_ERROR_WORKSPACE;
-  if (!aligned(workspace, 256)) return JATTN_ERROR_INVALID_VALUE;
+  if (!aligned(workspace, 256) || !aligned(fwd_workspace, 256)) return JATTN_ERROR_INVALID_VALUE;
   const size_t tb = (size_t)B * L * H * D * 2, lb = (size_t)B * H * L * 4;
+  const size_t fwb = fwd_workspace ? jattn_fwd_workspace_bytes(B, L, H, D) : 0;
   const Range ins[] = {{q, tb},   {k, tb},    {v, tb},
                        {gains, (size_t)2 * D * 4}, {valid_len, (size_t)B * 4}, {out, tb},
-                       {lse, lb}, {dout, tb}};
+                       {lse, lb}, {dout, tb}, {fwd_workspace, fwb}};
   const Range outs[] = {{dq, tb}, {dk, tb}, {dv, tb}, {dgains, (size_t)2 * D * 4}, {workspace, wl.total}};
-  if (!outputs_disjoint(outs, 5, ins, 8)) return JATTN_ERROR_INVALID_VALUE;
+  if (!outputs_disjoint(outs, 5, ins, 9)) return JATTN_ERROR_INVALID_VALUE;
 
   char* ws = static_cast<char*>(workspace);
   jattn::BwdArgs a;
@@ -180,7 +203,9 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
   a.dgains = dgains;
-  a.kr = reinterpret_cast<uint16_t*>(ws + wl.kr);
+  // normalised keys: the forward's own copy when the caller passes its workspace, else computed here
+  a.kr = fwd_workspace ? static_cast<uint16_t*>(const_cast<void*>(fwd_workspace))
+                       : reinterpret_cast<uint16_t*>(ws + wl.kr);
   a.qs = reinterpret_cast<uint16_t*>(ws + wl.qs);
   a.nlse2 = reinterpret_cast<float*>(ws + wl.nlse2);
   a.ndelta = reinterpret_cast<float*>(ws + wl.ndelta);
@@ -194,7 +219,8 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
   a.nblk = (L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock;
   a.items = B * H * a.nblk;
   a.lp = a.nblk * kBwdRowsPerBlock;
-  return jattn::launch_bwd(D, a, stage_events, n_stage_events, stream) == hipSuccess ? JATTN_SUCCESS
+  return jattn::launch_bwd(D, a, fwd_workspace == nullptr, stage_events, n_stage_events, stream) == hipSuccess
+             ? JATTN_SUCCESS
                                                                                     : JATTN_ERROR_HIP;
 }
 

@@ -13,7 +13,8 @@
 // column sum, taken in the key-parallel kernel.
 //
 // Four kernels, no atomics:
-//  * prenorm: Kr = bf16(k * r_k) (normalised keys without gain) into the workspace, [B, H, L, D].
+//  * prenorm (jattn_prenorm.hip): Kr = bf16(k * r_k), normalised keys without gain, into the
+//    workspace as [B, H, L, D].
 //  * dq kernel (query-parallel, like the forward): each wave owns 32 queries and streams Kr and V;
 //    per 32-key step S^T, dP^T (both: lane = query), dS^T in registers, dQn^T += Kr^T dS^T with Kr^T
 //    read by ds_read_b64_tr_b16. Epilogue: Q-side RMSNorm backward and dq, and for the key-parallel
@@ -48,23 +49,6 @@ constexpr int bwd_waves_per_eu() { return D <= 72 ? 2 : 1; }
 template <int D>
 constexpr int bwd_nbuf() { return D == 72 ? 2 : 3; }
 
-// End-of-step barrier of the tile rings. At the end of step t the tile t + 1 must have landed in LDS;
-// the k tiles after it whose loads are already issued (k <= NB - 2) may stay in flight, and each
-// wave issued at least PER loads for each of them. k is wave-uniform.
-template <int PER, int MAXK>
-__device__ __forceinline__ void ring_barrier(int k) {
-  static_assert(MAXK >= 0 && MAXK <= 3, "ring depth");
-  if constexpr (MAXK >= 3) {
-    if (k >= 3) return stream_barrier<3 * PER>();
-  }
-  if constexpr (MAXK >= 2) {
-    if (k >= 2) return stream_barrier<2 * PER>();
-  }
-  if constexpr (MAXK >= 1) {
-    if (k >= 1) return stream_barrier<PER>();
-  }
-  stream_barrier<0>();
-}
 
 // LDS plan of the two main kernels. The swizzled layout (D = 64, 128) serves both row-fragment and
 // transposed reads without bank conflicts; other head dims use padded rows.
@@ -86,56 +70,6 @@ struct DkdvCfg {
   static constexpr int SCRATCH = (kBlockRows + 8) * Dims<D>::DM * 4;
   static constexpr int BYTES = STAGE + STATS > SCRATCH ? STAGE + STATS : SCRATCH;
 };
-
-// ------------------------------------------------------------------------------------------------
-// prenorm kernel: Kr[b, h, l, :] = bf16(k[b, l, h, :] * r_k) for the valid keys (l < valid length;
-// later rows are never read). Thread t covers chunks t%TPR + j*TPR of row t/TPR of each pass.
-constexpr int kPrenormPasses = 4;
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_prenorm_kernel(BwdArgs a) {
-  using Dm = Dims<D>;
-  const int tid = threadIdx.x, rr = tid / Dm::TPR, cc = tid % Dm::TPR;
-  const int L = a.L, H = a.H;
-  const int total = a.B * L * H;
-  u32x4 x[kPrenormPasses][Dm::CPT];
-  int row[kPrenormPasses];
-#pragma unroll
-  for (int p = 0; p < kPrenormPasses; ++p) {
-    row[p] = (blockIdx.x * kPrenormPasses + p) * Dm::RPP + rr;  // input row (b * L + l) * H + h
-#pragma unroll
-    for (int j = 0; j < Dm::CPT; ++j) {
-      const int c = cc + j * Dm::TPR;
-      x[p][j] = row[p] < total && c < Dm::NCH ? *reinterpret_cast<const u32x4*>(a.k + (size_t)row[p] * D + c * 8)
-                                              : (u32x4){0u, 0u, 0u, 0u};
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < kPrenormPasses; ++p) {
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < Dm::CPT; ++j) ss = sumsq8(x[p][j], ss);
-    ss = group_sum<Dm::TPR>(ss);
-    const float r = rsqrtf(ss * (1.0f / D) + a.eps);
-    const int R = row[p];
-    if (R >= total) continue;
-    const int bl = R / H, h = R - bl * H, b = bl / L, l = bl - b * L;
-    const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
-    if (l >= n) continue;
-    uint16_t* dst = a.kr + (((size_t)b * H + h) * L + l) * D;
-#pragma unroll
-    for (int j = 0; j < Dm::CPT; ++j) {
-      const int c = cc + j * Dm::TPR;
-      if (c < Dm::NCH) {
-        float f[8];
-        unpack8(x[p][j], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] *= r;
-        *reinterpret_cast<bf16x8*>(dst + c * 8) = to_bf16x8(f);
-      }
-    }
-  }
-}
 
 // A wave row in the C/D layout (pair j4 of tile mt holds d = 32 mt + 8 j4 + 4 g + [0..3]) as raw bf16
 // pairs, for the RMSNorm backward of the epilogue. Where registers allow it the row is loaded in the
@@ -287,20 +221,16 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
   accumulate(1);
 }
 
+// One work item of the dq kernel: query rows [128 blk, 128 blk + 128) of (batch, head) pair bh.
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
-void bwd_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, int blk) {
   using Dm = Dims<D>;
   using Cfg = DqCfg<D>;
   using LK = typename Cfg::LK;
   using LV = typename Cfg::LV;
   constexpr int NB = Cfg::NB;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
   __bf16* sk = reinterpret_cast<__bf16*>(smem);
   __bf16* sv = sk + NB * LK::ELEMS;
-
-  int bh, blk, item;
-  if (!map_item(a.items, a.nblk, bh, blk, item)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int L = a.L, H = a.H;
   const int b = bh / H;
@@ -387,6 +317,18 @@ void bwd_dq_kernel(BwdArgs a) {
   if constexpr (!keep_row_c<D>()) load_row_c<D>(xq, a.q + roff, qvalid, g);
   rmsnorm_backward_row<D, false>(acc, xq, a.gains, a.gains + D, rq, qvalid, qvalid, a.dq + roff,
                                  a.qs + ((size_t)bh * L + qrow) * D, a.c, g);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
+void bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[DqCfg<D>::BYTES];
+  // (an item ends with its tile loop's barrier and its epilogue does not touch LDS, so the next
+  // item may refill the ring right away)
+  for (ItemIter it(a.items); it.valid(); it.next()) {
+    const int bh = it.item() / a.nblk;
+    dq_item<D>(a, smem, bh, it.item() - bh * a.nblk);
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -517,14 +459,10 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t b
   }
 }
 
+// One work item of the dk/dv kernel: key rows [128 blk, 128 blk + 128) of (batch, head) pair bh.
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
-void bwd_dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, int blk, int item) {
   using Dm = Dims<D>;
-  __shared__ __attribute__((aligned(16))) char smem[DkdvCfg<D>::BYTES];
-
-  int bh, blk, item;
-  if (!map_item(a.items, a.nblk, bh, blk, item)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int L = a.L, H = a.H;
   const int b = bh / H;
@@ -607,6 +545,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
   block_column_sums<D>(dka, reinterpret_cast<float*>(smem), a.part + (size_t)item * D, tid);
 }
 
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
+void bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[DkdvCfg<D>::BYTES];
+  for (ItemIter it(a.items); it.valid(); it.next()) {
+    const int bh = it.item() / a.nblk;
+    dkdv_item<D>(a, smem, bh, it.item() - bh * a.nblk, it.item());
+    __syncthreads();  // the column-sum scratch overlaps the ring the next item refills
+  }
+}
+
 // ------------------------------------------------------------------------------------------------
 // dgains[0][d] = g_k[d] * T[d] and dgains[1][d] = g_q[d] * T[d], with T[d] the sum over workgroups of
 // the partials in a fixed order. Block d; lane j sums items j, j + 64, ... with the loads issued in
@@ -634,35 +583,44 @@ __global__ __launch_bounds__(64) void dg_reduce_kernel(const float* __restrict__
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, const hipEvent_t* events, int n_events,
+static hipError_t launch_bwd_d(const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
                                hipStream_t stream) {
-  const int prenorm_rows = Dims<D>::RPP * kPrenormPasses;
-  const int prenorm_blocks = (int)(((int64_t)a.B * a.L * a.H + prenorm_rows - 1) / prenorm_rows);
-  const dim3 grid(grid_for_items(a.items));
   int stage = 0;
-  auto recorded = [&]() {
-    hipError_t e = hipGetLastError();
+  auto recorded = [&](hipError_t e) {
+    if (e == hipSuccess) e = hipGetLastError();
     if (e == hipSuccess && n_events > stage) e = hipEventRecord(events[stage], stream);
     ++stage;
     return e;
   };
-  hipLaunchKernelGGL(bwd_prenorm_kernel<D>, dim3(prenorm_blocks), dim3(kThreads), 0, stream, a);
-  hipError_t e = recorded();
+  PrenormArgs p;
+  p.k = a.k;
+  p.valid_len = a.valid_len;
+  p.kr = a.kr;
+  p.B = a.B;
+  p.L = a.L;
+  p.H = a.H;
+  p.eps = a.eps;
+  hipError_t e = recorded(prenorm ? launch_prenorm(D, p, stream) : hipSuccess);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, grid, dim3(kThreads), 0, stream, a);
-  if ((e = recorded()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, grid, dim3(kThreads), 0, stream, a);
-  if ((e = recorded()) != hipSuccess) return e;
+  int grid = 0;
+  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dq_kernel<D>), a.items, &grid)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid), dim3(kThreads), 0, stream, a);
+  if ((e = recorded(hipSuccess)) != hipSuccess) return e;
+  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dkdv_kernel<D>), a.items, &grid)) != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid), dim3(kThreads), 0, stream, a);
+  if ((e = recorded(hipSuccess)) != hipSuccess) return e;
   hipLaunchKernelGGL(dg_reduce_kernel, dim3(D), dim3(64), 0, stream, a.part, a.gains, a.items, D, a.dgains);
-  return recorded();
+  return recorded(hipSuccess);
 }
 
-hipError_t launch_bwd(int D, const BwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream) {
+hipError_t launch_bwd(int D, const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
+                      hipStream_t stream) {
   switch (D) {
-    case 32: return launch_bwd_d<32>(a, events, n_events, stream);
-    case 64: return launch_bwd_d<64>(a, events, n_events, stream);
-    case 72: return launch_bwd_d<72>(a, events, n_events, stream);
-    case 128: return launch_bwd_d<128>(a, events, n_events, stream);
+    case 32: return launch_bwd_d<32>(a, prenorm, events, n_events, stream);
+    case 64: return launch_bwd_d<64>(a, prenorm, events, n_events, stream);
+    case 72: return launch_bwd_d<72>(a, prenorm, events, n_events, stream);
+    case 128: return launch_bwd_d<128>(a, prenorm, events, n_events, stream);
     default: return hipErrorInvalidValue;
   }
 }

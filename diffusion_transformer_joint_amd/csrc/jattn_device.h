@@ -318,6 +318,24 @@ __device__ __forceinline__ void stream_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// End-of-step barrier of the tile rings. At the end of step t the tile t + 1 must have landed in LDS;
+// the k tiles after it whose loads are already issued (k <= NB - 2) may stay in flight, and each
+// wave issued at least PER loads for each of them. k is wave-uniform.
+template <int PER, int MAXK>
+__device__ __forceinline__ void ring_barrier(int k) {
+  static_assert(MAXK >= 0 && MAXK <= 3, "ring depth");
+  if constexpr (MAXK >= 3) {
+    if (k >= 3) return stream_barrier<3 * PER>();
+  }
+  if constexpr (MAXK >= 2) {
+    if (k >= 2) return stream_barrier<2 * PER>();
+  }
+  if constexpr (MAXK >= 1) {
+    if (k >= 1) return stream_barrier<PER>();
+  }
+  stream_barrier<0>();
+}
+
 // Store the tile unchanged.
 template <int D, class LY>
 __device__ __forceinline__ void tile_store_raw(const TileRegs<D>& t, __bf16* lds, int tid) {
@@ -476,6 +494,25 @@ __device__ __forceinline__ bool map_item(int items, int nblk, int& bh, int& blk,
 }
 
 __host__ __device__ inline int grid_for_items(int items) { return ((items + 7) >> 3) << 3; }
+
+// Persistent grids: gridDim.x (a multiple of 8) workgroups stay resident and loop over the items.
+// Workgroup w serves XCD w % 8, whose items are the contiguous range [x * per, (x + 1) * per) with
+// per = ceil(items / 8) -- so the row blocks of one (batch, head) pair share an L2 -- taking every
+// (gridDim.x / 8)-th of them. Looping instead of launching one workgroup per item lets the stores of
+// one item drain under the next item's work and keeps the workgroups of a CU from running their
+// memory-bound prologues and epilogues in lockstep.
+struct ItemIter {
+  int per, base, j, step, items;
+  __device__ explicit ItemIter(int n_items) : items(n_items) {
+    per = (n_items + 7) >> 3;
+    base = (int)(blockIdx.x & 7) * per;
+    j = (int)(blockIdx.x >> 3);
+    step = (int)(gridDim.x >> 3);
+  }
+  __device__ bool valid() const { return j < per && base + j < items; }
+  __device__ int item() const { return base + j; }
+  __device__ void next() { j += step; }
+};
 
 // ---------------------------------------------------------------------------------------------
 // Deterministic per-workgroup column sums of a [4 waves x 32 rows x D] set of values held in the

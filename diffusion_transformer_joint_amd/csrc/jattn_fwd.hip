@@ -25,9 +25,13 @@
 // maximum, rescale or cross-lane exchange is needed inside the loop. Otherwise (large scale or gains)
 // it runs the usual online softmax with a running maximum. Both give the same softmax up to rounding.
 //
-// Staging: the K/V rows of tile t+1 are normalised (K) and written to the other LDS buffer inside
-// the body of tile t, and the rows of tile t+2 are fetched with buffer loads whose range ends at
-// the last valid key (reads past it return zeros), so the tile body is straight-line code.
+// Streaming: a prenorm kernel first writes Kr = bf16(k * r_k) (per (batch, head), contiguous rows)
+// to the workspace. The forward kernel then streams Kr and V tiles straight from memory into a ring
+// of LDS buffers with buffer loads that carry the LDS bit, issued two tiles ahead. Their range ends
+// at the last valid key, so later rows and padding columns land as zeros. No registers or VALU work
+// are spent on staging, and the tile body is straight-line code.
+#include <type_traits>
+
 #include "jattn_device.h"
 #include "jattn_launch.h"
 
@@ -39,9 +43,12 @@ template <int D>
 struct Fwd {
   static constexpr int QT = fwd_rows_per_block(D) / kBlockRows;  // 32-query tiles per wave
   static constexpr int ROWS = fwd_rows_per_block(D);
-  using LK = Lay<D, kRowRead>;  // key rows: read as row fragments only
-  using LV = Lay<D, kTrRead>;   // value rows: read transposed only
-  static constexpr int STAGE = 2 * (LK::ELEMS + LV::ELEMS) * 2;  // double buffered, bytes
+  using LK = Lay<D, kSwizzled>;  // key rows: row fragments (padded rows where D has no swizzle)
+  // value rows: read transposed only (swizzled for D = 64, 128, else a pitch for transposed reads)
+  using LV = Lay<D, (D == 64 || D == 128) ? kSwizzled : kTrRead>;
+  // ring depth: three buffers (loads two tiles ahead) where two workgroups per CU still fit in LDS
+  static constexpr int NB = (D == 72 || D == 128) ? 2 : 3;
+  static constexpr int STAGE = NB * (LK::ELEMS + LV::ELEMS) * 2;  // bytes
   static constexpr int BYTES = STAGE + 16;
   static_assert(QT == 1 || QT == 2, "query tiles per wave");
 };
@@ -82,21 +89,17 @@ __device__ __forceinline__ void softmax_half(const f32x16& s, f32x16 (&o)[Dims<D
   pack_probs(p, pf0, pf1, lsum);
 }
 
-// One 64-key tile from LDS (kt, vt), with the staging of the next tile (registers tk, tv -> kn, vn)
-// and the loads of the tile after it in the same straight-line body. MASKED: keys at or past n get
-// a -inf accumulator seed (p = 0).
+// One 64-key tile from LDS (kt, vt). MASKED: keys at or past n get a -inf accumulator seed (p = 0).
 template <int D, bool BOUNDED, bool MASKED>
-__device__ __forceinline__ void fwd_tile(const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn,
-                                         TileRegs<D>& tk, TileRegs<D>& tv, __amdgpu_buffer_rsrc_t rk,
-                                         __amdgpu_buffer_rsrc_t rv, int rs,
+__device__ __forceinline__ void fwd_tile(const __bf16* __restrict__ kt, const __bf16* __restrict__ vt,
                                          const bf16x8 (&qf)[Fwd<D>::QT][Dims<D>::KS],
                                          const f32x16 (&cinit)[Fwd<D>::QT], FwdState<D>& st, int key0, int n,
-                                         float eps, int tid) {
+                                         int lane) {
   using Dm = Dims<D>;
   using LK = typename Fwd<D>::LK;
   using LV = typename Fwd<D>::LV;
   constexpr int QT = Fwd<D>::QT;
-  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     // S'^T (keys x queries) = Kr Q'^T for this 32-key half and every query tile
@@ -116,11 +119,6 @@ __device__ __forceinline__ void fwd_tile(const __bf16* kt, const __bf16* vt, __b
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) s[qt] = mfma(kf, qf[qt][ks], s[qt]);
     }
-    if (h == 0) {
-      // stage the next tile into the other buffer while the MFMAs run
-      tile_store_rmsnorm<D, LK>(tk, kn, 1.f, eps, key0 + kTile, n, tid);
-      tile_store_raw<D, LV>(tv, vn, tid);
-    }
     bf16x8 pf[QT][2];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
@@ -135,49 +133,51 @@ __device__ __forceinline__ void fwd_tile(const __bf16* kt, const __bf16* vt, __b
         for (int qt = 0; qt < QT; ++qt) st.o[qt][mt] = mfma(vf, pf[qt][kk], st.o[qt][mt]);
       }
   }
-  // fetch the tile after next (rows past the valid keys read as zeros)
-  tile_load_buf<D>(tk, rk, rs, key0 + 2 * kTile, tid);
-  tile_load_buf<D>(tv, rv, rs, key0 + 2 * kTile, tid);
-  __builtin_amdgcn_iglp_opt(2);
-  __syncthreads();
 }
 
-template <int D, bool BOUNDED>
-__device__ __forceinline__ void fwd_loop(const FwdArgs& a, __bf16* sk, __bf16* sv,
-                                         const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
-                                         int rs, int n, const bf16x8 (&qf)[Fwd<D>::QT][Dims<D>::KS],
-                                         const float (&shift)[Fwd<D>::QT], FwdState<D>& st, int tid) {
+// The LDS ring of key and value tiles: tile t lives in buffer t % NB. The first NB - 1 tiles are
+// issued by the kernel before its prologue; each step issues the tile NB - 1 ahead.
+template <int D>
+struct FwdRing {
   using LK = typename Fwd<D>::LK;
   using LV = typename Fwd<D>::LV;
-  constexpr int QT = Fwd<D>::QT;
-  const int ntiles = (n + kTile - 1) / kTile, nfull = n / kTile;
-  if (ntiles == 0) return;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, rows_bytes<D>(n, rs));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, rows_bytes<D>(n, rs));
+  static constexpr int NB = Fwd<D>::NB;
+  static constexpr int PER = DirectTile<D, LK>::MIN_PER_WAVE + DirectTile<D, LV>::MIN_PER_WAVE;
+  __bf16* sk;
+  __bf16* sv;
+  const uint16_t* kb;  // Kr rows of this (batch, head), row stride D
+  const uint16_t* vb;  // V rows, row stride rs
+  int rs, n, ntiles, wave;
+  DirectTile<D, LK> dk;
+  DirectTile<D, LV> dv;
+  __device__ __forceinline__ void issue(int t, int buf) {
+    dk.issue(tile_rsrc<D>(kb, D, t * kTile, n), sk + buf * LK::ELEMS, wave);
+    dv.issue(tile_rsrc<D>(vb, rs, t * kTile, n), sv + buf * LV::ELEMS, wave);
+  }
+};
+
+template <int D, bool BOUNDED>
+__device__ __forceinline__ void fwd_loop(FwdRing<D>& ring, const bf16x8 (&qf)[Fwd<D>::QT][Dims<D>::KS],
+                                         const float (&shift)[Fwd<D>::QT], FwdState<D>& st, int lane) {
+  using LK = typename Fwd<D>::LK;
+  using LV = typename Fwd<D>::LV;
+  constexpr int QT = Fwd<D>::QT, NB = Fwd<D>::NB;
+  const int n = ring.n, ntiles = ring.ntiles, nfull = n / kTile;
   f32x16 cinit[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) cinit[qt][i] = BOUNDED ? -shift[qt] : 0.f;
-  TileRegs<D> tk, tv;
-  tile_load_buf<D>(tk, rk, rs, 0, tid);
-  tile_load_buf<D>(tv, rv, rs, 0, tid);
-  tile_store_rmsnorm<D, LK>(tk, sk, 1.f, a.eps, 0, n, tid);
-  tile_store_raw<D, LV>(tv, sv, tid);
-  tile_load_buf<D>(tk, rk, rs, kTile, tid);
-  tile_load_buf<D>(tv, rv, rs, kTile, tid);
-  __syncthreads();
-  for (int t = 0; t < nfull; ++t) {
-    const int ck = (t & 1) * LK::ELEMS, nk = LK::ELEMS - ck, cv = (t & 1) * LV::ELEMS, nv = LV::ELEMS - cv;
-    fwd_tile<D, BOUNDED, false>(sk + ck, sv + cv, sk + nk, sv + nv, tk, tv, rk, rv, rs, qf, cinit, st,
-                                t * kTile, n, a.eps, tid);
-  }
-  if (ntiles > nfull) {
-    const int ck = (nfull & 1) * LK::ELEMS, nk = LK::ELEMS - ck, cv = (nfull & 1) * LV::ELEMS,
-              nv = LV::ELEMS - cv;
-    fwd_tile<D, BOUNDED, true>(sk + ck, sv + cv, sk + nk, sv + nv, tk, tv, rk, rv, rs, qf, cinit, st,
-                               nfull * kTile, n, a.eps, tid);
-  }
+  int cur = 0;
+  auto step = [&](auto masked, int t) {
+    if (t + NB - 1 < ntiles) ring.issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
+    fwd_tile<D, BOUNDED, decltype(masked)::value>(ring.sk + cur * LK::ELEMS, ring.sv + cur * LV::ELEMS, qf, cinit,
+                                                  st, t * kTile, n, lane);
+    ring_barrier<FwdRing<D>::PER, NB - 2>(ntiles - 2 - t);
+    cur = cur + 1 == NB ? 0 : cur + 1;
+  };
+  for (int t = 0; t < nfull; ++t) step(std::false_type{}, t);
+  if (nfull < ntiles) step(std::true_type{}, nfull);
 }
 
 template <int D>
@@ -185,21 +185,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   using Dm = Dims<D>;
   constexpr int QT = Fwd<D>::QT;
   __shared__ __attribute__((aligned(16))) char smem[Fwd<D>::BYTES];
-  __bf16* sk = reinterpret_cast<__bf16*>(smem);
-  __bf16* sv = sk + 2 * Fwd<D>::LK::ELEMS;
   float* sbound = reinterpret_cast<float*>(smem + Fwd<D>::STAGE);
 
   int bh, blk, item;
   if (!map_item(a.items, a.nblk, bh, blk, item)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int L = a.L, H = a.H;
   const int b = bh / H;
   const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
   const int rs = H * D;
   const size_t base = ((size_t)b * L * H + (bh - b * H)) * D;
 
-  zero_pad_columns<D, typename Fwd<D>::LK>(sk, 2, tid);
-  zero_pad_columns<D, typename Fwd<D>::LV>(sv, 2, tid);
+  // start streaming the first key/value tiles before the per-row set-up
+  FwdRing<D> ring;
+  ring.sk = reinterpret_cast<__bf16*>(smem);
+  ring.sv = ring.sk + Fwd<D>::NB * Fwd<D>::LK::ELEMS;
+  ring.kb = a.kr + (size_t)bh * L * D;
+  ring.vb = a.v + base;
+  ring.rs = rs;
+  ring.n = n;
+  ring.ntiles = (n + kTile - 1) / kTile;
+  ring.wave = wave;
+  ring.dk.init(D, wave, lane);
+  ring.dv.init(rs, wave, lane);
+  for (int t = 0; t < Fwd<D>::NB - 1 && t < ring.ntiles; ++t) ring.issue(t, t);
 
   // This wave's query rows, normalised with both gains and pre-scaled, as B-operand fragments,
   // and their score bounds in log2 units (margin covers the bf16 rounding of Kr and Q').
@@ -227,6 +236,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     wmax = fmaxf(wmax, wave_max(shift[qt]));
   }
   if (lane == 0) sbound[wave] = wmax;
+  wait_vmem();  // (the first tiles have landed in LDS as well)
   __syncthreads();
   const float bmax = fmaxf(fmaxf(sbound[0], sbound[1]), fmaxf(sbound[2], sbound[3]));
 
@@ -239,16 +249,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int i = 0; i < 16; ++i) st.o[qt][mt][i] = 0.f;
     st.lsum[qt] = 0.f;
   }
-  const uint16_t* kb = a.k + base;
-  const uint16_t* vb = a.v + base;
   if (bmax <= kBoundLimit) {  // uniform over the workgroup
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = shift[qt];
-    fwd_loop<D, true>(a, sk, sv, kb, vb, rs, n, qf, shift, st, tid);
+    fwd_loop<D, true>(ring, qf, shift, st, lane);
   } else {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = -INFINITY;
-    fwd_loop<D, false>(a, sk, sv, kb, vb, rs, n, qf, shift, st, tid);
+    fwd_loop<D, false>(ring, qf, shift, st, lane);
   }
 
 #pragma unroll
@@ -275,17 +283,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 template <int D>
-static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
+static hipError_t launch_fwd_d(const FwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream) {
+  PrenormArgs p;
+  p.k = a.k;
+  p.valid_len = a.valid_len;
+  p.kr = const_cast<uint16_t*>(a.kr);
+  p.B = a.B;
+  p.L = a.L;
+  p.H = a.H;
+  p.eps = a.eps;
+  hipError_t e = launch_prenorm(D, p, stream);
+  if (e == hipSuccess && n_events > 0) e = hipEventRecord(events[0], stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fwd_kernel<D>, dim3(grid_for_items(a.items)), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess && n_events > 1) e = hipEventRecord(events[1], stream);
+  return e;
 }
 
-hipError_t launch_fwd(int D, const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_fwd(int D, const FwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream) {
   switch (D) {
-    case 32: return launch_fwd_d<32>(a, stream);
-    case 64: return launch_fwd_d<64>(a, stream);
-    case 72: return launch_fwd_d<72>(a, stream);
-    case 128: return launch_fwd_d<128>(a, stream);
+    case 32: return launch_fwd_d<32>(a, events, n_events, stream);
+    case 64: return launch_fwd_d<64>(a, events, n_events, stream);
+    case 72: return launch_fwd_d<72>(a, events, n_events, stream);
+    case 128: return launch_fwd_d<128>(a, events, n_events, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -7,10 +7,19 @@
 
 namespace jattn {
 
+struct PrenormArgs {
+  const uint16_t* k;
+  const int32_t* valid_len;  // [B] or nullptr
+  uint16_t* kr;              // [B, H, L, D]: bf16(k * r_k), valid keys only
+  int B, L, H;
+  float eps;
+};
+
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
+  const uint16_t* kr;      // workspace [B, H, L, D]: bf16(k * r_k), written by the prenorm kernel
   const float* gains;      // [2, D]
   const int32_t* valid_len;  // [B] or nullptr
   uint16_t* out;
@@ -56,8 +65,18 @@ constexpr int fwd_rows_per_block(int D) { return D <= 64 ? 256 : 128; }
 // Backward: both kernels use 4 waves of 32 rows.
 constexpr int kBwdRowsPerBlock = 128;
 
-hipError_t launch_fwd(int D, const FwdArgs& a, hipStream_t stream);
-// Enqueues the backward kernels; if n_events > 0, records events[i] after stage i (i < n_events).
-hipError_t launch_bwd(int D, const BwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream);
+// Grid size of a persistent kernel (256 threads per workgroup, no dynamic LDS) over `items` work items:
+// as many workgroups as the current device keeps resident at once, a multiple of 8 and no more than
+// the items need (rounded up to 8).
+hipError_t persistent_grid(const void* kernel, int items, int* grid);
+
+hipError_t launch_prenorm(int D, const PrenormArgs& a, hipStream_t stream);
+// Enqueues the key normalisation (into a.kr) and the forward kernel; if n_events > 0, records
+// events[i] after stage i (i < n_events).
+hipError_t launch_fwd(int D, const FwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream);
+// Enqueues the backward kernels (the key normalisation only if `prenorm`; a.kr then already holds
+// it); if n_events > 0, records events[i] after stage i (i < n_events).
+hipError_t launch_bwd(int D, const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
+                      hipStream_t stream);
 
 }  // namespace jattn

@@ -1,0 +1,91 @@
+// RMS normalisation of the key rows, shared by the forward and the backward pass.
+//
+// The normalised keys Kr = k * r_k with r_k = (mean_d k^2 + eps)^(-1/2) (the RMSNorm of the QK-norm
+// row in the re-diffusion README's design-notes table, without its gain) are written once per call
+// as bf16 in a [B, H, L, D] layout. Both gains are folded into the query side by the attention
+// kernels, which then stream Kr tiles straight into LDS with no arithmetic on the way.
+#include "jattn_device.h"
+#include "jattn_launch.h"
+
+namespace jattn {
+
+// Kr[b, h, l, :] = bf16(k[b, l, h, :] * r_k) for the valid keys (l < valid length; later rows are
+// never read). Thread t covers chunks t%TPR + j*TPR of row t/TPR of each pass.
+constexpr int kPrenormPasses = 4;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void prenorm_kernel(PrenormArgs a) {
+  using Dm = Dims<D>;
+  const int tid = threadIdx.x, rr = tid / Dm::TPR, cc = tid % Dm::TPR;
+  const int L = a.L, H = a.H;
+  const int total = a.B * L * H;
+  u32x4 x[kPrenormPasses][Dm::CPT];
+  int row[kPrenormPasses];
+#pragma unroll
+  for (int p = 0; p < kPrenormPasses; ++p) {
+    row[p] = (blockIdx.x * kPrenormPasses + p) * Dm::RPP + rr;  // input row (b * L + l) * H + h
+#pragma unroll
+    for (int j = 0; j < Dm::CPT; ++j) {
+      const int c = cc + j * Dm::TPR;
+      x[p][j] = row[p] < total && c < Dm::NCH ? *reinterpret_cast<const u32x4*>(a.k + (size_t)row[p] * D + c * 8)
+                                              : (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kPrenormPasses; ++p) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < Dm::CPT; ++j) ss = sumsq8(x[p][j], ss);
+    ss = group_sum<Dm::TPR>(ss);
+    const float r = rsqrtf(ss * (1.0f / D) + a.eps);
+    const int R = row[p];
+    if (R >= total) continue;
+    const int bl = R / H, h = R - bl * H, b = bl / L, l = bl - b * L;
+    const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
+    if (l >= n) continue;
+    uint16_t* dst = a.kr + (((size_t)b * H + h) * L + l) * D;
+#pragma unroll
+    for (int j = 0; j < Dm::CPT; ++j) {
+      const int c = cc + j * Dm::TPR;
+      if (c < Dm::NCH) {
+        float f[8];
+        unpack8(x[p][j], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] *= r;
+        *reinterpret_cast<bf16x8*>(dst + c * 8) = to_bf16x8(f);
+      }
+    }
+  }
+}
+
+hipError_t persistent_grid(const void* kernel, int items, int* grid) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
+  if (e != hipSuccess) return e;
+  const int resident = ((cus * (per_cu > 0 ? per_cu : 1)) >> 3) << 3;
+  const int need = grid_for_items(items);
+  *grid = resident >= 8 && resident < need ? resident : need;
+  return hipSuccess;
+}
+
+template <int D>
+static hipError_t launch_prenorm_d(const PrenormArgs& a, hipStream_t stream) {
+  const int rows = Dims<D>::RPP * kPrenormPasses;
+  const int blocks = (int)(((int64_t)a.B * a.L * a.H + rows - 1) / rows);
+  hipLaunchKernelGGL(prenorm_kernel<D>, dim3(blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prenorm(int D, const PrenormArgs& a, hipStream_t stream) {
+  switch (D) {
+    case 32: return launch_prenorm_d<32>(a, stream);
+    case 64: return launch_prenorm_d<64>(a, stream);
+    case 72: return launch_prenorm_d<72>(a, stream);
+    case 128: return launch_prenorm_d<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace jattn

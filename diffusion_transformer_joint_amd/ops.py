@@ -15,7 +15,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["forward", "backward", "workspace_bytes", "JointAttention", "joint_attention"]
+__all__ = ["forward", "backward", "workspace_bytes", "fwd_workspace_bytes", "JointAttention", "joint_attention"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -50,8 +50,10 @@ def _check_common(q, k, v, gains, valid_len):
 
 
 def forward(q, k, v, gains, valid_len=None, scale: Optional[float] = None, eps: float = 1e-6,
-            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
-    """Joint attention forward. Returns (out bf16 [B, L, H, D], lse fp32 [B, H, L])."""
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, return_workspace: bool = False):
+    """Joint attention forward. Returns (out bf16 [B, L, H, D], lse fp32 [B, H, L]), plus the forward
+    workspace (the normalised key rows, reusable by `backward`) if return_workspace."""
     B, L, H, D = _check_common(q, k, v, gains, valid_len)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
@@ -61,19 +63,31 @@ def forward(q, k, v, gains, valid_len=None, scale: Optional[float] = None, eps: 
     _check_tensor("out", out, torch.bfloat16, (B, L, H, D), q.device)
     _check_tensor("lse", lse, torch.float32, (B, H, L), q.device)
     lib = _lib.load()
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.jattn_fwd_workspace_bytes(B, L, H, D)), 1), dtype=torch.uint8,
+                                device=q.device)
     st = lib.jattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gains), _ptr(valid_len), B, L, H, D,
-                       ctypes.c_float(scale), ctypes.c_float(eps), _ptr(out), _ptr(lse), _stream(q))
+                       ctypes.c_float(scale), ctypes.c_float(eps), _ptr(out), _ptr(lse), _ptr(workspace),
+                       workspace.numel(), _stream(q))
     _lib.check("jattn_fwd", st)
-    return out, lse
+    return (out, lse, workspace) if return_workspace else (out, lse)
 
 
 def workspace_bytes(B: int, L: int, H: int, D: int) -> int:
+    """Device workspace bytes of the backward pass."""
     return int(_lib.load().jattn_bwd_workspace_bytes(B, L, H, D))
 
 
+def fwd_workspace_bytes(B: int, L: int, H: int, D: int) -> int:
+    """Device workspace bytes of the forward pass."""
+    return int(_lib.load().jattn_fwd_workspace_bytes(B, L, H, D))
+
+
 def backward(q, k, v, gains, out, lse, dout, valid_len=None, scale: Optional[float] = None,
-             eps: float = 1e-6, dq=None, dk=None, dv=None, dgains=None, workspace=None):
-    """Joint attention backward. Returns (dq, dk, dv bf16 [B, L, H, D], dgains fp32 [2, D])."""
+             eps: float = 1e-6, dq=None, dk=None, dv=None, dgains=None, workspace=None, fwd_workspace=None):
+    """Joint attention backward. Returns (dq, dk, dv bf16 [B, L, H, D], dgains fp32 [2, D]).
+    fwd_workspace: the workspace returned by the forward call that produced out and lse (optional;
+    the backward then reuses its normalised key rows)."""
     B, L, H, D = _check_common(q, k, v, gains, valid_len)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dev = q.device
@@ -93,26 +107,27 @@ def backward(q, k, v, gains, out, lse, dout, valid_len=None, scale: Optional[flo
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = lib.jattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gains), _ptr(valid_len), _ptr(out), _ptr(lse),
                        _ptr(dout), B, L, H, D, ctypes.c_float(scale), ctypes.c_float(eps), _ptr(dq),
-                       _ptr(dk), _ptr(dv), _ptr(dgains), _ptr(workspace), workspace.numel(), _stream(q))
+                       _ptr(dk), _ptr(dv), _ptr(dgains), _ptr(workspace), workspace.numel(), _ptr(fwd_workspace),
+                       _stream(q))
     _lib.check("jattn_bwd", st)
     return dq, dk, dv, dgains
 
 
 class JointAttention(torch.autograd.Function):
-    """Autograd wrapper: saves the forward outputs (out, lse) and calls jattn_bwd."""
+    """Autograd wrapper: saves the forward outputs (out, lse, the normalised keys) and calls jattn_bwd."""
 
     @staticmethod
     def forward(ctx, q, k, v, gains, valid_len=None, scale=None, eps=1e-6):
-        out, lse = forward(q, k, v, gains, valid_len, scale, eps)
-        ctx.save_for_backward(q, k, v, gains, out, lse, valid_len)
+        out, lse, ws = forward(q, k, v, gains, valid_len, scale, eps, return_workspace=True)
+        ctx.save_for_backward(q, k, v, gains, out, lse, valid_len, ws)
         ctx.scale, ctx.eps = scale, eps
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v, gains, out, lse, valid_len = ctx.saved_tensors
+        q, k, v, gains, out, lse, valid_len, ws = ctx.saved_tensors
         dq, dk, dv, dg = backward(q, k, v, gains, out, lse, dout.to(torch.bfloat16).contiguous(),
-                                  valid_len, ctx.scale, ctx.eps)
+                                  valid_len, ctx.scale, ctx.eps, fwd_workspace=ws)
         return dq, dk, dv, dg, None, None, None
 
 

@@ -47,9 +47,13 @@ typedef enum {
     JATTN_ERROR_INVALID_VALUE = 1, /* null pointer, size < 1, misalignment, non-finite scale,
                                       eps < 0 or non-finite, output aliasing another buffer  */
     JATTN_ERROR_NOT_SUPPORTED = 2, /* head dim outside the compiled set, or sizes too large    */
-    JATTN_ERROR_WORKSPACE = 3,     /* workspace NULL or smaller than jattn_bwd_workspace_bytes */
+    JATTN_ERROR_WORKSPACE = 3,     /* workspace NULL or smaller than the *_workspace_bytes size */
     JATTN_ERROR_HIP = 4            /* a kernel launch failed (hipGetLastError)                 */
 } jattn_status;
+
+/* Bytes of device workspace jattn_fwd needs for these sizes: the RMS-normalised K rows
+ * (B*L*H*D bf16, rounded up to 256 bytes). Returns 0 for invalid or unsupported sizes. */
+size_t jattn_fwd_workspace_bytes(int B, int L, int H, int D);
 
 /* Forward pass.
  *   q, k, v    bf16 [B, L, H, D] inputs.
@@ -58,10 +62,25 @@ typedef enum {
  *   softmax_scale  any finite value (the usual choice is 1/sqrt(D)); eps >= 0 (e.g. 1e-6).
  *   out        bf16 [B, L, H, D] output.
  *   lse        fp32 [B, H, L] row log-sum-exp of the scaled scores (natural log), used by jattn_bwd.
- * out and lse must not overlap any input or each other. */
+ *   workspace  device scratch of at least jattn_fwd_workspace_bytes(B, L, H, D) bytes, 256-byte
+ *              aligned; its contents on entry do not matter and are clobbered.
+ * out, lse and the workspace must not overlap any input or each other. */
 jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float* gains,
                        const int32_t* valid_len, int B, int L, int H, int D,
-                       float softmax_scale, float eps, void* out, float* lse, hipStream_t stream);
+                       float softmax_scale, float eps, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Number of kernels jattn_fwd enqueues, in order: 0 = K-row RMS normalisation (into the
+ * workspace), 1 = the attention forward. */
+#define JATTN_FWD_STAGES 2
+
+/* jattn_fwd with per-stage timing hooks; identical results. stage_events / n_stage_events as for
+ * jattn_bwd_ex below, with JATTN_FWD_STAGES stages. */
+jattn_status jattn_fwd_ex(const void* q, const void* k, const void* v, const float* gains,
+                          const int32_t* valid_len, int B, int L, int H, int D,
+                          float softmax_scale, float eps, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
 
 /* Bytes of device workspace jattn_bwd needs for these sizes: normalised K rows and pre-scaled
  * normalised Q rows (2 * B*L*H*D bf16), two fp32 row statistics per query row, and per-workgroup
@@ -72,16 +91,21 @@ size_t jattn_bwd_workspace_bytes(int B, int L, int H, int D);
  * same arguments) and dout (bf16 [B, L, H, D], the gradient of the loss with respect to out).
  *   dq, dk, dv  bf16 [B, L, H, D] gradients with respect to q, k, v (overwritten).
  *   dgains      fp32 [2, D] gradient with respect to gains (overwritten; deterministic).
- *   workspace   device scratch of at least jattn_bwd_workspace_bytes(B, L, H, D) bytes; its contents
- *               on entry do not matter and are clobbered.
- * Outputs and workspace must not overlap any input or each other. */
+ *   workspace   device scratch of at least jattn_bwd_workspace_bytes(B, L, H, D) bytes, 256-byte
+ *               aligned; its contents on entry do not matter and are clobbered.
+ *   fwd_workspace  NULL, or the workspace of the jattn_fwd call that produced out and lse, unchanged
+ *               since (it holds the normalised K rows; the backward then reuses them instead of
+ *               normalising K again). Read only; 256-byte aligned.
+ * Outputs and workspace must not overlap any input (fwd_workspace included) or each other. */
 jattn_status jattn_bwd(const void* q, const void* k, const void* v, const float* gains,
                        const int32_t* valid_len, const void* out, const float* lse, const void* dout,
                        int B, int L, int H, int D, float softmax_scale, float eps,
                        void* dq, void* dk, void* dv, float* dgains,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+                       void* workspace, size_t workspace_bytes, const void* fwd_workspace,
+                       hipStream_t stream);
 
-/* Number of kernels jattn_bwd enqueues, in order: 0 = K-row RMS normalisation, 1 = dq
+/* Number of kernels jattn_bwd enqueues, in order: 0 = K-row RMS normalisation (skipped, with its
+ * event still recorded, when fwd_workspace is given), 1 = dq
  * (query-parallel; also writes the normalised Q rows and the row statistics), 2 = dk/dv
  * (key-parallel), 3 = gain-gradient reduction. */
 #define JATTN_BWD_STAGES 4
@@ -96,7 +120,7 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
                           const int32_t* valid_len, const void* out, const float* lse, const void* dout,
                           int B, int L, int H, int D, float softmax_scale, float eps,
                           void* dq, void* dk, void* dv, float* dgains,
-                          void* workspace, size_t workspace_bytes,
+                          void* workspace, size_t workspace_bytes, const void* fwd_workspace,
                           const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */

@@ -42,15 +42,18 @@ def test_status_strings(lib):
     for code, name in _lib.STATUS.items():
         assert lib.jattn_status_string(code).decode() == name
     assert lib.jattn_status_string(99).decode() == "JATTN_UNKNOWN_STATUS"
-    assert lib.jattn_abi_version() == 1
+    assert lib.jattn_abi_version() == _lib.ABI_VERSION
 
 
 def fwd(lib, **kw):
     a = dict(q=fake(0), k=fake(1), v=fake(2), gains=fake(3), valid_len=None, B=2, L=100, H=3, D=64,
-             scale=0.125, eps=1e-6, out=fake(4), lse=fake(5), stream=None)
+             scale=0.125, eps=1e-6, out=fake(4), lse=fake(5), ws=fake(6), ws_bytes=None, stream=None)
     a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = lib.jattn_fwd_workspace_bytes(a["B"], a["L"], a["H"], a["D"])
     return lib.jattn_fwd(a["q"], a["k"], a["v"], a["gains"], a["valid_len"], a["B"], a["L"], a["H"], a["D"],
-                         ctypes.c_float(a["scale"]), ctypes.c_float(a["eps"]), a["out"], a["lse"], a["stream"])
+                         ctypes.c_float(a["scale"]), ctypes.c_float(a["eps"]), a["out"], a["lse"], a["ws"],
+                         a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -75,6 +78,11 @@ def fwd(lib, **kw):
     (dict(out=fake(0)), _lib.INVALID_VALUE),            # out aliases q
     (dict(lse=fake(4) + 4096), _lib.INVALID_VALUE),     # lse overlaps out
     (dict(out=fake(3) - 16), _lib.INVALID_VALUE),       # out overlaps gains
+    (dict(ws=None), _lib.WORKSPACE),                    # no workspace
+    (dict(ws_bytes=1024), _lib.WORKSPACE),              # workspace too small
+    (dict(ws=fake(6) + 64), _lib.INVALID_VALUE),        # workspace must be 256-byte aligned
+    (dict(ws=fake(1)), _lib.INVALID_VALUE),             # workspace aliases k
+    (dict(ws=fake(4)), _lib.INVALID_VALUE),             # workspace aliases out
 ])
 def test_fwd_rejects(lib, kw, expect):
     assert fwd(lib, **kw) == expect
@@ -83,13 +91,13 @@ def test_fwd_rejects(lib, kw, expect):
 def bwd(lib, ws_bytes=None, **kw):
     a = dict(q=fake(0), k=fake(1), v=fake(2), gains=fake(3), valid_len=None, out=fake(4), lse=fake(5),
              dout=fake(6), B=2, L=100, H=3, D=64, scale=0.125, eps=1e-6, dq=fake(7), dk=fake(8), dv=fake(9),
-             dgains=fake(10), ws=fake(11), stream=None)
+             dgains=fake(10), ws=fake(11), fws=None, stream=None)
     a.update(kw)
     if ws_bytes is None:
         ws_bytes = lib.jattn_bwd_workspace_bytes(a["B"], a["L"], a["H"], a["D"])
     return lib.jattn_bwd(a["q"], a["k"], a["v"], a["gains"], a["valid_len"], a["out"], a["lse"], a["dout"],
                          a["B"], a["L"], a["H"], a["D"], ctypes.c_float(a["scale"]), ctypes.c_float(a["eps"]),
-                         a["dq"], a["dk"], a["dv"], a["dgains"], a["ws"], ws_bytes, a["stream"])
+                         a["dq"], a["dk"], a["dv"], a["dgains"], a["ws"], ws_bytes, a["fws"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -107,6 +115,9 @@ def bwd(lib, ws_bytes=None, **kw):
     (dict(dq=fake(6)), _lib.INVALID_VALUE),             # dq aliases dout
     (dict(dv=fake(7) + 4096), _lib.INVALID_VALUE),      # dv overlaps dq
     (dict(ws=fake(0)), _lib.INVALID_VALUE),             # workspace aliases q
+    (dict(fws=fake(12) + 64), _lib.INVALID_VALUE),      # forward workspace must be 256-byte aligned
+    (dict(fws=fake(11)), _lib.INVALID_VALUE),           # workspace aliases the forward workspace
+    (dict(fws=fake(8)), _lib.INVALID_VALUE),            # dk aliases the forward workspace
 ])
 def test_bwd_rejects(lib, kw, expect):
     assert bwd(lib, **kw) == expect
@@ -115,7 +126,7 @@ def test_bwd_rejects(lib, kw, expect):
 def test_bwd_ex_rejects_bad_event_arguments(lib):
     need = lib.jattn_bwd_workspace_bytes(2, 100, 3, 64)
     base = [fake(0), fake(1), fake(2), fake(3), None, fake(4), fake(5), fake(6), 2, 100, 3, 64,
-            ctypes.c_float(0.125), ctypes.c_float(1e-6), fake(7), fake(8), fake(9), fake(10), fake(11), need]
+            ctypes.c_float(0.125), ctypes.c_float(1e-6), fake(7), fake(8), fake(9), fake(10), fake(11), need, None]
     assert lib.jattn_bwd_ex(*base, None, 1, None) == _lib.INVALID_VALUE
     assert lib.jattn_bwd_ex(*base, fake(12), -1, None) == _lib.INVALID_VALUE
     assert lib.jattn_bwd_ex(*base, fake(12), len(_lib.BWD_STAGES) + 1, None) == _lib.INVALID_VALUE
@@ -131,6 +142,13 @@ def test_bwd_rejects_small_workspace(lib):
     assert bwd(lib, ws_bytes=need - 1) == _lib.WORKSPACE
 
 
+def test_fwd_workspace_bytes(lib):
+    assert lib.jattn_fwd_workspace_bytes(0, 10, 1, 64) == 0
+    assert lib.jattn_fwd_workspace_bytes(1, 10, 1, 40) == 0
+    w = lib.jattn_fwd_workspace_bytes(16, 1101, 12, 64)
+    assert w >= 16 * 1101 * 12 * 64 * 2 and w % 256 == 0
+
+
 def test_workspace_bytes(lib):
     assert lib.jattn_bwd_workspace_bytes(0, 10, 1, 64) == 0
     assert lib.jattn_bwd_workspace_bytes(1, 10, 1, 40) == 0
@@ -141,6 +159,18 @@ def test_workspace_bytes(lib):
     assert w % 256 == 0
 
 
+def test_fwd_ex_rejects_bad_event_arguments(lib):
+    base = [fake(0), fake(1), fake(2), fake(3), None, 2, 100, 3, 64, ctypes.c_float(0.125), ctypes.c_float(1e-6),
+            fake(4), fake(5), fake(6), lib.jattn_fwd_workspace_bytes(2, 100, 3, 64)]
+    assert lib.jattn_fwd_ex(*base, None, 1, None) == _lib.INVALID_VALUE
+    assert lib.jattn_fwd_ex(*base, fake(12), -1, None) == _lib.INVALID_VALUE
+    assert lib.jattn_fwd_ex(*base, fake(12), len(_lib.FWD_STAGES) + 1, None) == _lib.INVALID_VALUE
+    bad = list(base)
+    bad[0] = None
+    assert lib.jattn_fwd_ex(*bad, fake(12), len(_lib.FWD_STAGES), None) == _lib.INVALID_VALUE
+
+
 def test_stage_names_match_header():
     hdr = open(os.path.join(ROOT, "include", "jattn.h")).read()
     assert int(re.search(r"#define JATTN_BWD_STAGES (\d+)", hdr).group(1)) == len(_lib.BWD_STAGES)
+    assert int(re.search(r"#define JATTN_FWD_STAGES (\d+)", hdr).group(1)) == len(_lib.FWD_STAGES)

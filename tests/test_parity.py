@@ -240,3 +240,21 @@ def test_autograd_function_matches_backward():
     assert torch.equal(out.detach(), o2)
     assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
     assert torch.equal(g.grad, dg)
+
+
+@pytest.mark.parametrize("B,L,H,D,vl", [(2, 300, 2, 72, [300, 129]), (2, 200, 2, 128, [57, 200])])
+def test_backward_reuses_forward_keys(B, L, H, D, vl):
+    """Passing the forward's workspace (its normalised key rows) gives the same gradients, bit for
+    bit, as letting the backward normalise the keys itself."""
+    say(f"case: forward-workspace reuse B{B} L{L} H{H} D{D} valid {vl}")
+    inp = make_shape_inputs(B, L, H, D, seed=8, valid_len=vl)
+    d = to_dev(inp)
+    out, lse, fws = ops.forward(d["q"], d["k"], d["v"], d["gains"], d["valid_len"], inp["scale"], inp["eps"],
+                                return_workspace=True)
+    own = [t.clone() for t in ops.backward(d["q"], d["k"], d["v"], d["gains"], out, lse, d["dout"], d["valid_len"],
+                                           inp["scale"], inp["eps"])]
+    reused = ops.backward(d["q"], d["k"], d["v"], d["gains"], out, lse, d["dout"], d["valid_len"], inp["scale"],
+                          inp["eps"], fwd_workspace=fws)
+    torch.cuda.synchronize()
+    for a, b in zip(own, reused):
+        assert torch.equal(a, b)
