@@ -38,7 +38,7 @@
 
 namespace jattn {
 
-static_assert(kBlockRows == kBwdRowsPerBlock, "host and device block sizes differ");
+static_assert(kBwdRowsPerBlock == kBwdWaves * kWaveRows && kBwdWaves >= 2, "backward workgroup shape");
 
 // Waves per SIMD the register allocation targets: two up to D = 72, one at D = 128 (whose
 // accumulators and operand fragments need the whole register file).
@@ -47,7 +47,7 @@ constexpr int bwd_waves_per_eu() { return D <= 72 ? 2 : 1; }
 // LDS ring depth: three tile buffers (loads issued two tiles ahead), two at D = 72 whose padded
 // tiles would otherwise not leave room for two workgroups per CU.
 template <int D>
-constexpr int bwd_nbuf() { return D == 72 ? 2 : 3; }
+constexpr int bwd_nbuf() { return D == 72 || kBwdWaves < 4 ? 2 : 3; }
 
 
 // LDS plan of the two main kernels. The swizzled layout (D = 64, 128) serves both row-fragment and
@@ -67,7 +67,7 @@ struct DkdvCfg {
   static constexpr int NB = bwd_nbuf<D>();
   static constexpr int STAGE = NB * (LQ::ELEMS + LO::ELEMS) * 2;
   static constexpr int STATS = NB * 2 * kTile * 4;  // -lse2 and -delta per streamed row
-  static constexpr int SCRATCH = (kBlockRows + 8) * Dims<D>::DM * 4;
+  static constexpr int SCRATCH = colsum_scratch_floats<D, kBwdWaves>() * 4;
   static constexpr int BYTES = STAGE + STATS > SCRATCH ? STAGE + STATS : SCRATCH;
 };
 
@@ -240,8 +240,8 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
 
   // start streaming the first key tiles before the per-row set-up
   const int ntiles = (n + kTile - 1) / kTile, nfull = n / kTile;
-  DirectTile<D, LK> dk;
-  DirectTile<D, LV> dv;
+  DirectTile<D, LK, kBwdWaves> dk;
+  DirectTile<D, LV, kBwdWaves> dv;
   dk.init(D, wave, lane);
   dv.init(rs, wave, lane);
   const uint16_t* kb = a.kr + (size_t)bh * L * D;
@@ -252,7 +252,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
   };
   for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
 
-  const int qrow = blk * kBlockRows + wave * kWaveRows + l32;
+  const int qrow = blk * kBwdRowsPerBlock + wave * kWaveRows + l32;
   const bool qvalid = qrow < L;
   const size_t roff = base + (size_t)qrow * rs;
   bf16x8 qf[Dm::KS], dof[Dm::KS];
@@ -299,7 +299,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
     if (ahead) issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
     dq_tile<D, decltype(masked)::value>(sk + cur * LK::ELEMS, sv + cur * LV::ELEMS, qf, dof, cs, cp, acc, t * kTile,
                                         n, lane);
-    ring_barrier<DirectTile<D, LK>::MIN_PER_WAVE + DirectTile<D, LV>::MIN_PER_WAVE, NB - 2>(ntiles - 2 - t);
+    ring_barrier<DirectTile<D, LK, kBwdWaves>::MIN_PER_WAVE + DirectTile<D, LV, kBwdWaves>::MIN_PER_WAVE, NB - 2>(ntiles - 2 - t);
     cur = cur + 1 == NB ? 0 : cur + 1;
   };
   for (int t = 0; t < nfull; ++t) step(std::false_type{}, t);
@@ -320,7 +320,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
 void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DqCfg<D>::BYTES];
   // (an item ends with its tile loop's barrier and its epilogue does not touch LDS, so the next
@@ -422,8 +422,8 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t b
   float* sd = sl + NB * kTile;                                // [NB][kTile]
   const int lane = tid & 63, wave = wave_id();
   const int L = a.L;
-  DirectTile<D, LQ> dq;
-  DirectTile<D, LO> dout;
+  DirectTile<D, LQ, kBwdWaves> dq;
+  DirectTile<D, LO, kBwdWaves> dout;
   dq.init(D, wave, lane);
   dout.init(rs, wave, lane);
   const uint16_t* qb = a.qs + (size_t)bh * L * D;
@@ -444,7 +444,7 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t b
   for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
   wait_vmem();
   __syncthreads();
-  constexpr int PER = DirectTile<D, LQ>::MIN_PER_WAVE + DirectTile<D, LO>::MIN_PER_WAVE;
+  constexpr int PER = DirectTile<D, LQ, kBwdWaves>::MIN_PER_WAVE + DirectTile<D, LO, kBwdWaves>::MIN_PER_WAVE;
   int cur = 0;
   for (int t = 0; t < ntiles; ++t) {
     const bool ahead = t + NB - 1 < ntiles;
@@ -470,12 +470,12 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
   const int rs = H * D;
   const size_t base = ((size_t)b * L * H + (bh - b * H)) * D;
 
-  const int key = blk * kBlockRows + wave * kWaveRows + l32;
+  const int key = blk * kBwdRowsPerBlock + wave * kWaveRows + l32;
   const bool kin = key < L;      // row exists
   const bool kvalid = key < n;   // row is an unpadded key
   const size_t roff = base + (size_t)key * rs;
 
-  if (blk * kBlockRows >= n) {
+  if (blk * kBwdRowsPerBlock >= n) {
     // every key of this workgroup is padding: exact zeros, no dg contribution
     if (kin) {
 #pragma unroll
@@ -484,7 +484,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
         *reinterpret_cast<u32x4*>(a.dv + roff + c * 8) = (u32x4){0u, 0u, 0u, 0u};
       }
     }
-    for (int d = tid; d < D; d += kThreads) a.part[(size_t)item * D + d] = 0.f;
+    for (int d = tid; d < D; d += kBwdThreads) a.part[(size_t)item * D + d] = 0.f;
     return;
   }
 
@@ -508,7 +508,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
       dka[mt][i] = 0.f;
     }
   // waves whose 32 keys are all valid skip the key mask
-  if (blk * kBlockRows + (wave + 1) * kWaveRows <= n)
+  if (blk * kBwdRowsPerBlock + (wave + 1) * kWaveRows <= n)
     dkdv_loop<D, false>(a, smem, base, bh, rs, kf, vf, dva, dka, kvalid, tid);
   else
     dkdv_loop<D, true>(a, smem, base, bh, rs, kf, vf, dva, dka, kvalid, tid);
@@ -542,11 +542,11 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
       for (int i = 0; i < 16; ++i) dka[mt][i] = 0.f;
   }
   __syncthreads();
-  block_column_sums<D>(dka, reinterpret_cast<float*>(smem), a.part + (size_t)item * D, tid);
+  block_column_sums<D, kBwdWaves>(dka, reinterpret_cast<float*>(smem), a.part + (size_t)item * D, tid);
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
 void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DkdvCfg<D>::BYTES];
   for (ItemIter it(a.items); it.valid(); it.next()) {
@@ -603,12 +603,12 @@ static hipError_t launch_bwd_d(const BwdArgs& a, bool prenorm, const hipEvent_t*
   hipError_t e = recorded(prenorm ? launch_prenorm(D, p, stream) : hipSuccess);
   if (e != hipSuccess) return e;
   int grid = 0;
-  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dq_kernel<D>), a.items, &grid)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid), dim3(kThreads), 0, stream, a);
+  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dq_kernel<D>), a.items, kBwdThreads, &grid)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid), dim3(kBwdThreads), 0, stream, a);
   if ((e = recorded(hipSuccess)) != hipSuccess) return e;
-  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dkdv_kernel<D>), a.items, &grid)) != hipSuccess)
+  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dkdv_kernel<D>), a.items, kBwdThreads, &grid)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid), dim3(kBwdThreads), 0, stream, a);
   if ((e = recorded(hipSuccess)) != hipSuccess) return e;
   hipLaunchKernelGGL(dg_reduce_kernel, dim3(D), dim3(64), 0, stream, a.part, a.gains, a.items, D, a.dgains);
   return recorded(hipSuccess);

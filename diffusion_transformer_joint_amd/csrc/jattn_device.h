@@ -33,9 +33,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr int kThreads = 256;  // 4 waves per workgroup
+constexpr int kThreads = 256;  // 4 waves per workgroup (forward and prenorm kernels)
 constexpr int kWaveRows = 32;  // rows (queries or keys) owned by one wave
-constexpr int kBlockRows = 128;  // rows owned by one workgroup
+constexpr int kBlockRows = 128;  // rows owned by one workgroup of 4 waves
 constexpr int kTile = 64;      // rows of the streamed operand staged per LDS tile
 
 // Head-dim dependent sizes. D is a multiple of 8 (16-byte rows chunks in HBM).
@@ -256,23 +256,23 @@ __device__ __forceinline__ void tile_load_buf(TileRegs<D>& t, __amdgpu_buffer_rs
 // logical chunk that belongs at its physical position -- undoing the layout's swizzle -- or an
 // out-of-range offset (zeros) for padding positions. Per tile only the buffer resource changes.
 // The data bypasses VGPRs; completion is covered by the s_waitcnt vmcnt before the next barrier.
-template <int D, class LY>
-struct DirectTile {
+template <int D, class LY, int W = 4>
+struct DirectTile {  // W waves share the loads of a tile
   using Dm = Dims<D>;
   static constexpr int CPR = LY::PITCH / 8;                 // physical chunks per row (incl. padding)
   static constexpr int NWL = (kTile * CPR + 63) / 64;       // wave loads per tile
-  static constexpr int PER_WAVE = (NWL + 3) / 4;            // most loads one wave issues (4 waves)
-  static constexpr int MIN_PER_WAVE = NWL / 4;              // fewest loads one wave issues
+  static constexpr int PER_WAVE = (NWL + W - 1) / W;        // most loads one wave issues
+  static constexpr int MIN_PER_WAVE = NWL / W;              // fewest loads one wave issues
   static constexpr int ALLOC = NWL * 512;                   // elements one tile buffer occupies
   uint32_t voff[PER_WAVE];
 
   __device__ __forceinline__ void init(int rs, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int p = (wave + 4 * j) * 64 + lane;  // physical chunk index in the tile
+      const int p = (wave + W * j) * 64 + lane;  // physical chunk index in the tile
       const int row = p / CPR, pc = p - row * CPR;
       const int lc = pc ^ LY::swz(row & (kTile - 1));
-      const bool real = wave + 4 * j < NWL && row < kTile && pc * 8 < Dm::DM && lc < Dm::NCH;
+      const bool real = wave + W * j < NWL && row < kTile && pc * 8 < Dm::DM && lc < Dm::NCH;
       voff[j] = real ? (uint32_t)(row * rs + lc * 8) * 2u : 0xFFFFFFF0u;
     }
   }
@@ -283,8 +283,8 @@ struct DirectTile {
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, __bf16* __restrict__ lds, int wave) const {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int i = wave + 4 * j;
-      if (NWL % 4 == 0 || i < NWL)
+      const int i = wave + W * j;
+      if (NWL % W == 0 || i < NWL)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (JATTN_LDS void*)(lds + i * 512), 16, voff[j], 0, 0, 0);
     }
   }
@@ -515,38 +515,47 @@ struct ItemIter {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Deterministic per-workgroup column sums of a [4 waves x 32 rows x D] set of values held in the
-// C/D layout of MT tiles (lane = row, register = d). `scr` must hold 128*DM + 8*DM floats and is
-// only touched after the caller's barrier. Writes the D sums to out[0..D).
-template <int D>
+// Deterministic per-workgroup column sums of a [W waves x 32 rows x D] set of values held in the
+// C/D layout of MT tiles (lane = row, register = d). `scr` must hold colsum_scratch_floats<D, W>()
+// floats and is only touched after the caller's barrier. Writes the D sums to out[0..D).
+// Rows are staged with an odd pitch (DM + 1 floats): the 32 lanes of a wave write 32 different rows
+// of one column, which then fall in 32 different banks.
+template <int D, int W>
+__host__ __device__ constexpr int colsum_scratch_floats() {
+  return 32 * W * (Dims<D>::DM + 1) + 8 * Dims<D>::DM;
+}
+
+template <int D, int W>
 __device__ __forceinline__ void block_column_sums(const f32x16 (&v)[Dims<D>::MT], float* scr,
                                                   float* __restrict__ out, int tid) {
   using Dm = Dims<D>;
+  constexpr int P = Dm::DM + 1, ROWS = 32 * W, THREADS = 64 * W;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
-  float* rows = scr;                        // [128][DM]
-  float* segs = scr + kBlockRows * Dm::DM;  // [SEGS][DM]
+  float* rows = scr;             // [ROWS][P]
+  float* segs = scr + ROWS * P;  // [SEGS][DM]
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int d = mt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-      rows[(wave * 32 + l32) * Dm::DM + d] = v[mt][i];
+      rows[(wave * 32 + l32) * P + d] = v[mt][i];
     }
   __syncthreads();
   constexpr int COLS = Dm::DM <= 32 ? 32 : (Dm::DM <= 64 ? 64 : 128);  // power of two >= DM
-  constexpr int SEGS = kThreads / COLS;
-  constexpr int RPS = kBlockRows / SEGS;
+  constexpr int SEGS = THREADS / COLS;
+  constexpr int RPS = ROWS / SEGS;
+  static_assert(SEGS >= 1 && SEGS <= 8 && ROWS % SEGS == 0, "column-sum split");
   {
     const int col = tid % COLS, seg = tid / COLS;
     if (col < Dm::DM) {
       float s = 0.f;
 #pragma unroll 8
-      for (int r = 0; r < RPS; ++r) s += rows[(seg * RPS + r) * Dm::DM + col];
+      for (int r = 0; r < RPS; ++r) s += rows[(seg * RPS + r) * P + col];
       segs[seg * Dm::DM + col] = s;
     }
   }
   __syncthreads();
-  for (int d = tid; d < D; d += kThreads) {
+  for (int d = tid; d < D; d += THREADS) {
     float s = 0.f;
 #pragma unroll
     for (int seg = 0; seg < SEGS; ++seg) s += segs[seg * Dm::DM + d];

@@ -62,13 +62,15 @@ struct BwdArgs {
 // Forward: 4 waves of 64 queries (two independent 32-query tiles per wave) for D <= 64, where the
 // register budget allows it; 4 waves of 32 queries otherwise.
 constexpr int fwd_rows_per_block(int D) { return D <= 64 ? 256 : 128; }
-// Backward: both kernels use 4 waves of 32 rows.
-constexpr int kBwdRowsPerBlock = 128;
+// Backward: both kernels use workgroups of kBwdWaves waves of 32 rows.
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdRowsPerBlock = 32 * kBwdWaves;
 
-// Grid size of a persistent kernel (256 threads per workgroup, no dynamic LDS) over `items` work items:
+// Grid size of a persistent kernel (`threads` per workgroup, no dynamic LDS) over `items` work items:
 // as many workgroups as the current device keeps resident at once, a multiple of 8 and no more than
 // the items need (rounded up to 8).
-hipError_t persistent_grid(const void* kernel, int items, int* grid);
+hipError_t persistent_grid(const void* kernel, int items, int threads, int* grid);
 
 hipError_t launch_prenorm(int D, const PrenormArgs& a, hipStream_t stream);
 // Enqueues the key normalisation (into a.kr) and the forward kernel; if n_events > 0, records

@@ -58,11 +58,11 @@ __global__ __launch_bounds__(kThreads) void prenorm_kernel(PrenormArgs a) {
   }
 }
 
-hipError_t persistent_grid(const void* kernel, int items, int* grid) {
+hipError_t persistent_grid(const void* kernel, int items, int threads, int* grid) {
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
   if (e != hipSuccess) return e;
   const int resident = ((cus * (per_cu > 0 ? per_cu : 1)) >> 3) << 3;
   const int need = grid_for_items(items);
