@@ -293,12 +293,15 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
   // One loop over the full tiles and a separate step for the partial one: a masked / unmasked
   // branch inside the loop makes the two bodies keep the accumulators in different registers, with
   // copies at the join.
+  // a wave whose 32 query rows all lie past L keeps the ring going but skips the math
+  const bool active = blk * kBwdRowsPerBlock + wave * kWaveRows < L;
   int cur = 0;
   auto step = [&](auto masked, int t) {
     const bool ahead = t + NB - 1 < ntiles;
     if (ahead) issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
-    dq_tile<D, decltype(masked)::value>(sk + cur * LK::ELEMS, sv + cur * LV::ELEMS, qf, dof, cs, cp, acc, t * kTile,
-                                        n, lane);
+    if (active)
+      dq_tile<D, decltype(masked)::value>(sk + cur * LK::ELEMS, sv + cur * LV::ELEMS, qf, dof, cs, cp, acc,
+                                          t * kTile, n, lane);
     ring_barrier<DirectTile<D, LK, kBwdWaves>::MIN_PER_WAVE + DirectTile<D, LV, kBwdWaves>::MIN_PER_WAVE, NB - 2>(ntiles - 2 - t);
     cur = cur + 1 == NB ? 0 : cur + 1;
   };
@@ -407,11 +410,12 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const _
   accumulate(1);
 }
 
+// `active`: this wave holds at least one valid key (a wave of padded keys only keeps the ring going).
 template <int D, bool KMASK>
 __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t base, int bh, int rs,
                                           const bf16x8 (&kf)[Dims<D>::KS], const bf16x8 (&vf)[Dims<D>::KS],
                                           f32x16 (&dva)[Dims<D>::MT], f32x16 (&dka)[Dims<D>::MT], bool kvalid,
-                                          int tid) {
+                                          bool active, int tid) {
   using Cfg = DkdvCfg<D>;
   using LQ = typename Cfg::LQ;
   using LO = typename Cfg::LO;
@@ -449,8 +453,9 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t b
   for (int t = 0; t < ntiles; ++t) {
     const bool ahead = t + NB - 1 < ntiles;
     if (ahead) issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
-    dkdv_tile<D, KMASK>(sq + cur * LQ::ELEMS, so + cur * LO::ELEMS, sl + cur * kTile, sd + cur * kTile, kf, vf,
-                        dva, dka, kvalid, lane);
+    if (active)
+      dkdv_tile<D, KMASK>(sq + cur * LQ::ELEMS, so + cur * LO::ELEMS, sl + cur * kTile, sd + cur * kTile, kf, vf,
+                          dva, dka, kvalid, lane);
     if (wave < 2)
       ring_barrier<PER + 1, NB - 2>(ntiles - 2 - t);  // (these waves also load a statistics row per tile)
     else
@@ -484,7 +489,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
         *reinterpret_cast<u32x4*>(a.dv + roff + c * 8) = (u32x4){0u, 0u, 0u, 0u};
       }
     }
-    for (int d = tid; d < D; d += kBwdThreads) a.part[(size_t)item * D + d] = 0.f;
+    for (int d = tid; d < D; d += kBwdThreads) a.part[(size_t)d * a.items + item] = 0.f;
     return;
   }
 
@@ -508,10 +513,11 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
       dka[mt][i] = 0.f;
     }
   // waves whose 32 keys are all valid skip the key mask
+  const bool active = blk * kBwdRowsPerBlock + wave * kWaveRows < n;
   if (blk * kBwdRowsPerBlock + (wave + 1) * kWaveRows <= n)
-    dkdv_loop<D, false>(a, smem, base, bh, rs, kf, vf, dva, dka, kvalid, tid);
+    dkdv_loop<D, false>(a, smem, base, bh, rs, kf, vf, dva, dka, kvalid, active, tid);
   else
-    dkdv_loop<D, true>(a, smem, base, bh, rs, kf, vf, dva, dka, kvalid, tid);
+    dkdv_loop<D, true>(a, smem, base, bh, rs, kf, vf, dva, dka, kvalid, active, tid);
 
   // dv (zeros at padded keys)
   if (kin) {
@@ -542,7 +548,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
       for (int i = 0; i < 16; ++i) dka[mt][i] = 0.f;
   }
   __syncthreads();
-  block_column_sums<D, kBwdWaves>(dka, reinterpret_cast<float*>(smem), a.part + (size_t)item * D, tid);
+  block_column_sums<D, kBwdWaves>(dka, reinterpret_cast<float*>(smem), a.part + item, (size_t)a.items, tid);
 }
 
 template <int D>
@@ -558,27 +564,37 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------------------------------------
 // dgains[0][d] = g_k[d] * T[d] and dgains[1][d] = g_q[d] * T[d], with T[d] the sum over workgroups of
-// the partials in a fixed order. Block d; lane j sums items j, j + 64, ... with the loads issued in
-// batches of 8, then a fixed butterfly.
-__global__ __launch_bounds__(64) void dg_reduce_kernel(const float* __restrict__ part, const float* __restrict__ gains,
-                                                       int items, int D, float* __restrict__ dgains) {
-  const int d = blockIdx.x;
-  const float* p = part + d;
+// the partials (stored column-major, part[d][item]) in a fixed order. Block d: thread t sums items
+// t, t + 256, ... (coalesced), then the wave sums are combined by a fixed butterfly and in wave order.
+constexpr int kReduceThreads = 256;
+
+__global__ __launch_bounds__(kReduceThreads) void dg_reduce_kernel(const float* __restrict__ part,
+                                                                   const float* __restrict__ gains, int items,
+                                                                   int D, float* __restrict__ dgains) {
+  __shared__ float wsum[kReduceThreads / 64];
+  const int d = blockIdx.x, t = threadIdx.x;
+  const float* p = part + (size_t)d * items;
   float s = 0.f;
-  int i = threadIdx.x;
-  for (; i + 7 * 64 < items; i += 8 * 64) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[(size_t)(i + u * 64) * D];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
+  int i = t;
+  for (; i + 3 * kReduceThreads < items; i += 4 * kReduceThreads) {
+    const float v0 = p[i], v1 = p[i + kReduceThreads], v2 = p[i + 2 * kReduceThreads],
+                v3 = p[i + 3 * kReduceThreads];
+    s += v0;
+    s += v1;
+    s += v2;
+    s += v3;
   }
-  for (; i < items; i += 64) s += p[(size_t)i * D];
+  for (; i < items; i += kReduceThreads) s += p[i];
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-  if (threadIdx.x == 0) {
-    dgains[d] = gains[D + d] * s;
-    dgains[D + d] = gains[d] * s;
+  if ((t & 63) == 0) wsum[t >> 6] = s;
+  __syncthreads();
+  if (t == 0) {
+    float total = 0.f;
+#pragma unroll
+    for (int w = 0; w < kReduceThreads / 64; ++w) total += wsum[w];
+    dgains[d] = gains[D + d] * total;
+    dgains[D + d] = gains[d] * total;
   }
 }
 
@@ -610,7 +626,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a, bool prenorm, const hipEvent_t*
     return e;
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid), dim3(kBwdThreads), 0, stream, a);
   if ((e = recorded(hipSuccess)) != hipSuccess) return e;
-  hipLaunchKernelGGL(dg_reduce_kernel, dim3(D), dim3(64), 0, stream, a.part, a.gains, a.items, D, a.dgains);
+  hipLaunchKernelGGL(dg_reduce_kernel, dim3(D), dim3(kReduceThreads), 0, stream, a.part, a.gains, a.items, D,
+                     a.dgains);
   return recorded(hipSuccess);
 }
 

@@ -482,17 +482,6 @@ __device__ __forceinline__ float rmsnorm_row_frags(bf16x8 (&f)[Dims<D>::KS], con
 
 // ---------------------------------------------------------------------------------------------
 // Grid mapping. Workgroups are dispatched round-robin over the 8 XCDs (workgroup i -> XCD i % 8).
-// Work items are numbered so that consecutive items (the row blocks of one (batch, head) pair) land
-// on the same XCD, which keeps that pair's streamed operands in one L2.
-__device__ __forceinline__ bool map_item(int items, int nblk, int& bh, int& blk, int& item) {
-  const int per = (items + 7) >> 3;
-  item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if (item >= items) return false;
-  bh = item / nblk;
-  blk = item - bh * nblk;
-  return true;
-}
-
 __host__ __device__ inline int grid_for_items(int items) { return ((items + 7) >> 3) << 3; }
 
 // Persistent grids: gridDim.x (a multiple of 8) workgroups stay resident and loop over the items.
@@ -517,7 +506,7 @@ struct ItemIter {
 // ---------------------------------------------------------------------------------------------
 // Deterministic per-workgroup column sums of a [W waves x 32 rows x D] set of values held in the
 // C/D layout of MT tiles (lane = row, register = d). `scr` must hold colsum_scratch_floats<D, W>()
-// floats and is only touched after the caller's barrier. Writes the D sums to out[0..D).
+// floats and is only touched after the caller's barrier. Writes the sum of column d to out[d * stride].
 // Rows are staged with an odd pitch (DM + 1 floats): the 32 lanes of a wave write 32 different rows
 // of one column, which then fall in 32 different banks.
 template <int D, int W>
@@ -527,7 +516,7 @@ __host__ __device__ constexpr int colsum_scratch_floats() {
 
 template <int D, int W>
 __device__ __forceinline__ void block_column_sums(const f32x16 (&v)[Dims<D>::MT], float* scr,
-                                                  float* __restrict__ out, int tid) {
+                                                  float* __restrict__ out, size_t stride, int tid) {
   using Dm = Dims<D>;
   constexpr int P = Dm::DM + 1, ROWS = 32 * W, THREADS = 64 * W;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -559,7 +548,7 @@ __device__ __forceinline__ void block_column_sums(const f32x16 (&v)[Dims<D>::MT]
     float s = 0.f;
 #pragma unroll
     for (int seg = 0; seg < SEGS; ++seg) s += segs[seg * Dm::DM + d];
-    out[d] = s;
+    out[d * stride] = s;
   }
 }
 

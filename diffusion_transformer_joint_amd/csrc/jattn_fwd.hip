@@ -156,9 +156,12 @@ struct FwdRing {
   }
 };
 
+// `active`: this wave has at least one query row inside the sequence (a wave past L only keeps the
+// ring going: it issues its share of the loads and meets the barriers, but skips the math).
 template <int D, bool BOUNDED>
 __device__ __forceinline__ void fwd_loop(FwdRing<D>& ring, const bf16x8 (&qf)[Fwd<D>::QT][Dims<D>::KS],
-                                         const float (&shift)[Fwd<D>::QT], FwdState<D>& st, int lane) {
+                                         const float (&shift)[Fwd<D>::QT], FwdState<D>& st, bool active,
+                                         int lane) {
   using LK = typename Fwd<D>::LK;
   using LV = typename Fwd<D>::LV;
   constexpr int QT = Fwd<D>::QT, NB = Fwd<D>::NB;
@@ -171,8 +174,9 @@ __device__ __forceinline__ void fwd_loop(FwdRing<D>& ring, const bf16x8 (&qf)[Fw
   int cur = 0;
   auto step = [&](auto masked, int t) {
     if (t + NB - 1 < ntiles) ring.issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
-    fwd_tile<D, BOUNDED, decltype(masked)::value>(ring.sk + cur * LK::ELEMS, ring.sv + cur * LV::ELEMS, qf, cinit,
-                                                  st, t * kTile, n, lane);
+    if (active)
+      fwd_tile<D, BOUNDED, decltype(masked)::value>(ring.sk + cur * LK::ELEMS, ring.sv + cur * LV::ELEMS, qf,
+                                                    cinit, st, t * kTile, n, lane);
     ring_barrier<FwdRing<D>::PER, NB - 2>(ntiles - 2 - t);
     cur = cur + 1 == NB ? 0 : cur + 1;
   };
@@ -180,15 +184,12 @@ __device__ __forceinline__ void fwd_loop(FwdRing<D>& ring, const bf16x8 (&qf)[Fw
   if (nfull < ntiles) step(std::true_type{}, nfull);
 }
 
+// One work item: query rows [ROWS blk, ROWS blk + ROWS) of (batch, head) pair bh.
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, int blk) {
   using Dm = Dims<D>;
   constexpr int QT = Fwd<D>::QT;
-  __shared__ __attribute__((aligned(16))) char smem[Fwd<D>::BYTES];
   float* sbound = reinterpret_cast<float*>(smem + Fwd<D>::STAGE);
-
-  int bh, blk, item;
-  if (!map_item(a.items, a.nblk, bh, blk, item)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int L = a.L, H = a.H;
   const int b = bh / H;
@@ -249,14 +250,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int i = 0; i < 16; ++i) st.o[qt][mt][i] = 0.f;
     st.lsum[qt] = 0.f;
   }
+  const bool active = blk * Fwd<D>::ROWS + wave * 32 * QT < L;  // wave-uniform
   if (bmax <= kBoundLimit) {  // uniform over the workgroup
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = shift[qt];
-    fwd_loop<D, true>(ring, qf, shift, st, lane);
+    fwd_loop<D, true>(ring, qf, shift, st, active, lane);
   } else {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = -INFINITY;
-    fwd_loop<D, false>(ring, qf, shift, st, lane);
+    fwd_loop<D, false>(ring, qf, shift, st, active, lane);
   }
 
 #pragma unroll
@@ -280,6 +282,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
       }
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[Fwd<D>::BYTES];
+  // one item per workgroup (a persistent grid measured slower here: the items are few and large),
+  // numbered so that the row blocks of one (batch, head) pair share an XCD and its L2
+  const ItemIter it(a.items);
+  if (!it.valid()) return;
+  const int bh = it.item() / a.nblk;
+  fwd_item<D>(a, smem, bh, it.item() - bh * a.nblk);
 }
 
 template <int D>
