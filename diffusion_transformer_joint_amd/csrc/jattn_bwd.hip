@@ -44,10 +44,10 @@ static_assert(kBwdRowsPerBlock == kBwdWaves * kWaveRows && kBwdWaves >= 2, "back
 // accumulators and operand fragments need the whole register file).
 template <int D>
 constexpr int bwd_waves_per_eu() { return D <= 72 ? 2 : 1; }
-// LDS ring depth: three tile buffers (loads issued two tiles ahead), two at D = 72 whose padded
-// tiles would otherwise not leave room for two workgroups per CU.
+// LDS ring depth: four tile buffers (loads issued three tiles ahead; measured slightly faster than
+// three), two at D = 72 whose padded tiles would otherwise not leave room for two workgroups per CU.
 template <int D>
-constexpr int bwd_nbuf() { return D == 72 || kBwdWaves < 4 ? 2 : 3; }
+constexpr int bwd_nbuf() { return D == 72 || kBwdWaves < 4 ? 2 : 4; }
 
 
 // LDS plan of the two main kernels. The swizzled layout (D = 64, 128) serves both row-fragment and
