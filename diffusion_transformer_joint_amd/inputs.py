@@ -27,7 +27,10 @@ Recipe (all on CPU, one ``torch.Generator`` seeded with ``seed``, in this order)
 2. q, k, v = ``randn(B, L, H, D)`` fp32 each; ``mmdit768`` scales the text rows by 3; cast to bf16.
 3. gains = ``1 + 0.1 * randn(2, D)`` fp32 (row 0 for Q, row 1 for K).
 4. dout = ``randn(B, L, H, D).bfloat16()``.
-Text tokens sit at positions N_img .. L-1 (image first, text last).
+5. two-stream inputs only: per-stream gains = ``1 + 0.1 * randn(2, 2, D)`` fp32 ([stream][Q, K]).
+Text tokens sit at positions N_img .. L-1 (image first, text last). The two-stream inputs are the
+same q, k, v and dout split along the token axis into an image part [B, N_img, H, D] and a text
+part [B, N_txt, H, D] (each its own contiguous tensor).
 """
 from __future__ import annotations
 
@@ -75,7 +78,45 @@ def make_inputs(workload: str | Workload, seed: int = 0) -> dict:
     q, k, v, dout: bf16 [B, L, H, D]; gains: fp32 [2, D]; valid_len: int32 [B] or None;
     plus the python scalars scale, eps and the workload itself."""
     w = WORKLOADS[workload] if isinstance(workload, str) else workload
+    return _draw(w, torch.Generator().manual_seed(seed))
+
+
+def _split(t: torch.Tensor, n_img: int):
+    return t[:, :n_img].contiguous(), t[:, n_img:].contiguous()
+
+
+def make_stream_inputs(workload: str | Workload, seed: int = 0) -> dict:
+    """Two-stream inputs of a named workload: q, k, v, dout as (image, text) pairs of bf16 tensors
+    [B, N_img, H, D] and [B, N_txt, H, D]; gains fp32 [2, 2, D] (gains[s, 0] for the Q rows and
+    gains[s, 1] for the K rows of stream s; image = 0, text = 1); valid_len as in make_inputs (a
+    prefix length of the joint sequence, image first)."""
+    w = WORKLOADS[workload] if isinstance(workload, str) else workload
     g = torch.Generator().manual_seed(seed)
+    d = _draw(w, g)
+    gains = (1.0 + 0.1 * torch.randn(2, 2, w.D, generator=g)).float()
+    out = {k: _split(d[k], w.n_img) for k in ("q", "k", "v", "dout")}
+    out.update(gains=gains, valid_len=d["valid_len"], scale=d["scale"], eps=d["eps"], workload=w)
+    return out
+
+
+def make_shape_stream_inputs(B: int, n_img: int, n_txt: int, H: int, D: int, seed: int = 0,
+                             valid_len: Optional[list] = None, scale: Optional[float] = None,
+                             eps: float = EPS, gain_std: float = 0.1) -> dict:
+    """Two-stream inputs of an arbitrary shape (edge-case tests): the make_shape_inputs recipe for the
+    joint sequence, split at n_img, then per-stream gains 1 + gain_std * randn(2, 2, D)."""
+    L = n_img + n_txt
+    g = torch.Generator().manual_seed(seed)
+    joint = [torch.randn(B, L, H, D, generator=g).bfloat16() for _ in range(3)]
+    dout = torch.randn(B, L, H, D, generator=g).bfloat16()
+    gains = (1.0 + gain_std * torch.randn(2, 2, D, generator=g)).float()
+    vl = None if valid_len is None else torch.tensor(valid_len, dtype=torch.int32)
+    w = Workload(f"B{B}I{n_img}T{n_txt}H{H}D{D}", B=B, H=H, D=D, n_img=n_img, n_txt=n_txt)
+    return dict(q=_split(joint[0], n_img), k=_split(joint[1], n_img), v=_split(joint[2], n_img),
+                dout=_split(dout, n_img), gains=gains, valid_len=vl,
+                scale=default_scale(D) if scale is None else float(scale), eps=eps, workload=w)
+
+
+def _draw(w: Workload, g: torch.Generator) -> dict:
     B, L, H, D = w.B, w.L, w.H, w.D
     valid_len = None
     if w.ragged_text:

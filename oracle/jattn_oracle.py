@@ -40,7 +40,7 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["rmsnorm", "head_forward", "head_backward", "attention_forward", "attention_backward",
-           "attention_fwd_bwd"]
+           "attention_fwd_bwd", "streams_fwd_bwd"]
 
 
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> Tuple[np.ndarray, np.ndarray]:
@@ -162,3 +162,56 @@ def _fwd_bwd(q, k, v, gains, dout, valid_len, scale, eps, pairs):
         dg[0] += dgq
         dg[1] += dgk
     return out, lse, dq, dk, dv, dg
+
+
+# ------------------------------------------------------------------------------------------------
+# Two-stream form. [RD]'s DiT-layer box projects Q, K and V separately for the image stream x and
+# the text stream c ("QKV each"), concatenates the two streams, runs the joint attention and splits
+# the result back per stream. Here each stream keeps its own tensors and its own QK-norm gains (a
+# norm attached to each stream's projection; [RD]'s design-notes table names RMSNorm on Q and K
+# without saying whether the streams share it). Rows are concatenated image first, so valid_len is
+# still a prefix length of the joint sequence.
+
+def _stream_of_rows(n_img: int, L: int) -> np.ndarray:
+    """Stream index (0 = image, 1 = text) of each joint row."""
+    return (np.arange(L) >= n_img).astype(np.int64)
+
+
+def streams_fwd_bwd(q, k, v, gains, dout, valid_len=None, scale: float = None, eps: float = 1e-6,
+                    pairs: Optional[Sequence[Tuple[int, int]]] = None) -> dict:
+    """q, k, v, dout: (image [B, N_img, H, D], text [B, N_txt, H, D]) pairs; gains [2, 2, D] with
+    gains[s, 0] the Q gain and gains[s, 1] the K gain of stream s. Concatenates each pair along the
+    token axis (image first), runs the joint attention with every row normalised by its own stream's
+    gains, and splits the per-token results back.
+    Returns dict(out, dq, dk, dv) as (image, text) pairs, lse [B, H, N_img + N_txt] (joint row order)
+    and dgains [2, 2, D] (fp64). ``pairs`` as in attention_forward."""
+    cat = lambda t: np.concatenate([np.asarray(t[0], dtype=np.float64), np.asarray(t[1], dtype=np.float64)],
+                                   axis=1)
+    qj, kj, vj, doj = cat(q), cat(k), cat(v), cat(dout)
+    gains = np.asarray(gains, dtype=np.float64)
+    B, L, H, D = qj.shape
+    n_img = np.asarray(q[0]).shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    stream = _stream_of_rows(n_img, L)
+    gq_rows, gk_rows = gains[stream, 0], gains[stream, 1]  # [L, D] each
+    out = np.full((B, L, H, D), np.nan)
+    lse = np.full((B, H, L), np.nan)
+    dq, dk, dv = (np.full((B, L, H, D), np.nan) for _ in range(3))
+    dg = np.zeros((2, 2, D))
+    for b, h in _pairs(B, H, pairs):
+        n = _valid_keys(valid_len, b, L)
+        Q, K, V, dO = qj[b, :, h], kj[b, :, h], vj[b, :, h], doj[b, :, h]
+        f = head_forward(Q, K, V, gq_rows, gk_rows, n, scale, eps)
+        dQ, dK, dV, _, _, ex = head_backward(Q, K, V, gq_rows, gk_rows, dO, n, scale, eps, fwd=f)
+        out[b, :, h], lse[b, h] = f["O"], f["lse"]
+        dq[b, :, h], dk[b, :, h], dv[b, :, h] = dQ, dK, dV
+        # gain gradients: each row's term dxn * x * r goes to its own stream's gain
+        tq = ex["dQn"] * Q * f["rq"]
+        tk = ex["dKn"] * K * f["rk"]
+        for s in (0, 1):
+            rows = stream == s
+            dg[s, 0] += tq[rows].sum(axis=0)
+            dg[s, 1] += tk[rows].sum(axis=0)
+    split = lambda t: (t[:, :n_img], t[:, n_img:])
+    return dict(out=split(out), lse=lse, dq=split(dq), dk=split(dk), dv=split(dv), dgains=dg)

@@ -47,3 +47,15 @@ def test_flop_count():
     assert abs(f["total"] - 208.537e9) / 208.537e9 < 1e-4
     r = flops(2, 4352, 24, 128, valid_len=[4269, 4144])
     assert r["fwd"] < r["fwd_padded"]
+
+
+def test_stream_inputs_split_the_joint_draw():
+    from diffusion_transformer_joint_amd.inputs import make_stream_inputs
+    a, b = make_inputs("tiny", seed=0), make_stream_inputs("tiny", seed=0)
+    for key in ("q", "k", "v", "dout"):
+        img, txt = b[key]
+        assert img.shape == (1, 16, 2, 32) and txt.shape == (1, 8, 2, 32)
+        assert img.is_contiguous() and txt.is_contiguous()
+        assert torch.equal(torch.cat([img, txt], dim=1), a[key])
+    assert b["gains"].shape == (2, 2, 32) and b["gains"].dtype == torch.float32
+    assert not torch.equal(b["gains"][0], b["gains"][1])
