@@ -16,8 +16,8 @@ STATUS = {0: "JATTN_SUCCESS", 1: "JATTN_ERROR_INVALID_VALUE", 2: "JATTN_ERROR_NO
 SUCCESS, INVALID_VALUE, NOT_SUPPORTED, WORKSPACE, HIP = range(5)
 
 EXPORTED = ("jattn_fwd", "jattn_fwd_ex", "jattn_fwd_workspace_bytes", "jattn_bwd", "jattn_bwd_ex", "jattn_bwd_workspace_bytes",
-            "jattn_status_string", "jattn_abi_version")
-ABI_VERSION = 3
+            "jattn_fwd_streams", "jattn_bwd_streams", "jattn_status_string", "jattn_abi_version")
+ABI_VERSION = 4
 FWD_STAGES = ("prenorm_kernel", "fwd_kernel")
 BWD_STAGES = ("prenorm_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "dg_reduce_kernel")
 
@@ -57,6 +57,11 @@ def load() -> ctypes.CDLL:
         lib.jattn_bwd_ex.restype = I
         lib.jattn_bwd_ex.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, F, P, P, P, P, P,
                                      ctypes.c_size_t, P, P, I, P]
+        lib.jattn_fwd_streams.restype = I
+        lib.jattn_fwd_streams.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, P, P, P, ctypes.c_size_t, P, I, P]
+        lib.jattn_bwd_streams.restype = I
+        lib.jattn_bwd_streams.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, F, P, P, P, P, P,
+                                          ctypes.c_size_t, P, P, I, P]
         lib.jattn_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.jattn_bwd_workspace_bytes.argtypes = [I, I, I, I]
         lib.jattn_status_string.restype = ctypes.c_char_p
@@ -68,6 +73,15 @@ def load() -> ctypes.CDLL:
                               "rebuild it")
         _lib = lib
         return lib
+
+
+class PtrPair:
+    """Host array of two device pointers ({image part, text part}) for the two-stream entry points.
+    Keep the object alive for the duration of the call; `.arg` is what the call takes."""
+
+    def __init__(self, a, b):
+        self.arr = (ctypes.c_void_p * 2)(a, b)
+        self.arg = ctypes.cast(self.arr, ctypes.c_void_p)
 
 
 def check(fn: str, status: int) -> None:

@@ -3,6 +3,7 @@
 // touch the device.
 #include "jattn.h"
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
@@ -12,7 +13,7 @@ namespace {
 
 using jattn::kBwdRowsPerBlock;
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool supported_head_dim(int D) { return D == 32 || D == 64 || D == 72 || D == 128; }
 
@@ -60,12 +61,12 @@ struct WorkspaceLayout {
 
 // Normalised key rows and pre-scaled normalised query rows (bf16, [B, H, L, D]), the two row
 // statistics (fp32, [B, H, lp] with lp = L rounded up to whole row blocks) and the per-workgroup
-// partial sums of the gain-gradient factor (fp32, [items, D]), each 256-byte aligned.
+// partial sums of the gain gradients (fp32, [kPartSets, D, items]), each 256-byte aligned.
 WorkspaceLayout workspace_layout(int B, int L, int H, int D) {
   const size_t nblk = (L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock;
   const size_t items = (size_t)B * H * nblk, lp = nblk * kBwdRowsPerBlock;
   const size_t rows = round_up((size_t)B * H * L * D * 2, 256), stats = round_up((size_t)B * H * lp * 4, 256),
-               parts = round_up(items * D * sizeof(float), 256);
+               parts = round_up(jattn::kPartSets * items * D * sizeof(float), 256);
   WorkspaceLayout w;
   w.kr = 0;
   w.qs = w.kr + rows;
@@ -74,6 +75,110 @@ WorkspaceLayout workspace_layout(int B, int L, int H, int D) {
   w.part = w.ndelta + stats;
   w.total = w.part + parts;
   return w;
+}
+
+// Kernel arguments of a validated call. Tensors come as (block 0, block 1) pointer pairs: rows
+// [0, n0) of each sequence in block 0, the rest in block 1 (the joint entry points pass n0 = L).
+jattn_status run_fwd(bool streams, const void* const q[2], const void* const k[2], const void* const v[2],
+                     const float* gains, const int32_t* valid_len, int B, int L, int n0, int H, int D,
+                     float softmax_scale, float eps, void* const out[2], float* lse, void* workspace,
+                     const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream) {
+  auto in = [](const void* p) { return static_cast<const uint16_t*>(p); };
+  jattn::FwdArgs a;
+  a.q = in(q[0]);
+  a.k = in(k[0]);
+  a.v = in(v[0]);
+  a.q1 = in(q[1]);
+  a.k1 = in(k[1]);
+  a.v1 = in(v[1]);
+  a.kr = static_cast<const uint16_t*>(workspace);
+  a.gains = gains;
+  a.valid_len = valid_len;
+  a.out = static_cast<uint16_t*>(out[0]);
+  a.out1 = static_cast<uint16_t*>(out[1]);
+  a.lse = lse;
+  a.B = B;
+  a.L = L;
+  a.H = H;
+  a.n0 = n0;
+  a.c = softmax_scale * 1.4426950408889634f;
+  a.eps = eps;
+  a.nblk = (L + jattn::fwd_rows_per_block(D) - 1) / jattn::fwd_rows_per_block(D);
+  a.items = B * H * a.nblk;
+  return jattn::launch_fwd(D, streams, a, stage_events, n_stage_events, stream) == hipSuccess ? JATTN_SUCCESS
+                                                                                           : JATTN_ERROR_HIP;
+}
+
+jattn_status run_bwd(bool streams, const void* const q[2], const void* const k[2], const void* const v[2],
+                     const float* gains, const int32_t* valid_len, const void* const out[2], const float* lse,
+                     const void* const dout[2], int B, int L, int n0, int H, int D, float softmax_scale, float eps,
+                     void* const dq[2], void* const dk[2], void* const dv[2], float* dgains, void* workspace,
+                     const void* fwd_workspace, const hipEvent_t* stage_events, int n_stage_events,
+                     hipStream_t stream) {
+  auto in = [](const void* p) { return static_cast<const uint16_t*>(p); };
+  auto outp = [](void* p) { return static_cast<uint16_t*>(p); };
+  const WorkspaceLayout wl = workspace_layout(B, L, H, D);
+  char* ws = static_cast<char*>(workspace);
+  jattn::BwdArgs a;
+  a.q = in(q[0]);
+  a.k = in(k[0]);
+  a.v = in(v[0]);
+  a.q1 = in(q[1]);
+  a.k1 = in(k[1]);
+  a.v1 = in(v[1]);
+  a.gains = gains;
+  a.valid_len = valid_len;
+  a.out = in(out[0]);
+  a.out1 = in(out[1]);
+  a.lse = lse;
+  a.dout = in(dout[0]);
+  a.dout1 = in(dout[1]);
+  a.dq = outp(dq[0]);
+  a.dk = outp(dk[0]);
+  a.dv = outp(dv[0]);
+  a.dq1 = outp(dq[1]);
+  a.dk1 = outp(dk[1]);
+  a.dv1 = outp(dv[1]);
+  a.dgains = dgains;
+  // normalised keys: the forward's own copy when the caller passes its workspace, else computed here
+  a.kr = fwd_workspace ? static_cast<uint16_t*>(const_cast<void*>(fwd_workspace))
+                       : reinterpret_cast<uint16_t*>(ws + wl.kr);
+  a.qs = reinterpret_cast<uint16_t*>(ws + wl.qs);
+  a.nlse2 = reinterpret_cast<float*>(ws + wl.nlse2);
+  a.ndelta = reinterpret_cast<float*>(ws + wl.ndelta);
+  a.part = reinterpret_cast<float*>(ws + wl.part);
+  a.B = B;
+  a.L = L;
+  a.H = H;
+  a.n0 = n0;
+  a.scale = softmax_scale;
+  a.c = softmax_scale * 1.4426950408889634f;
+  a.eps = eps;
+  a.nblk = (L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock;
+  a.items = B * H * a.nblk;
+  a.lp = a.nblk * kBwdRowsPerBlock;
+  return jattn::launch_bwd(D, streams, a, fwd_workspace == nullptr, stage_events, n_stage_events, stream) ==
+                 hipSuccess
+             ? JATTN_SUCCESS
+             : JATTN_ERROR_HIP;
+}
+
+// Sizes of a two-stream call: N_img, N_txt >= 0 with at least one token.
+jattn_status check_stream_sizes(int B, int n_img, int n_txt, int H, int D, int* L) {
+  if (n_img < 0 || n_txt < 0) return JATTN_ERROR_INVALID_VALUE;
+  const int64_t l = (int64_t)n_img + n_txt;
+  if (l > INT_MAX) return JATTN_ERROR_NOT_SUPPORTED;
+  *L = (int)l;
+  return check_sizes(B, *L, H, D);
+}
+
+// A (image, text) pointer pair: the host array exists, and each pointer of a non-empty stream is
+// non-null and 16-byte aligned (a pointer of an empty stream is ignored).
+bool pair_ok(const void* const p[2], int n_img, int n_txt) {
+  if (!p) return false;
+  if (n_img > 0 && (!p[0] || !aligned(p[0], 16))) return false;
+  if (n_txt > 0 && (!p[1] || !aligned(p[1], 16))) return false;
+  return true;
 }
 
 }  // namespace
@@ -124,24 +229,12 @@ jattn_status jattn_fwd_ex(const void* q, const void* k, const void* v, const flo
   const Range outs[] = {{out, tb}, {lse, lb}, {workspace, wsb}};
   if (!outputs_disjoint(outs, 3, ins, 5)) return JATTN_ERROR_INVALID_VALUE;
 
-  jattn::FwdArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.kr = static_cast<const uint16_t*>(workspace);
-  a.gains = gains;
-  a.valid_len = valid_len;
-  a.out = static_cast<uint16_t*>(out);
-  a.lse = lse;
-  a.B = B;
-  a.L = L;
-  a.H = H;
-  a.c = softmax_scale * 1.4426950408889634f;
-  a.eps = eps;
-  a.nblk = (L + jattn::fwd_rows_per_block(D) - 1) / jattn::fwd_rows_per_block(D);
-  a.items = B * H * a.nblk;
-  return jattn::launch_fwd(D, a, stage_events, n_stage_events, stream) == hipSuccess ? JATTN_SUCCESS
-                                                                                  : JATTN_ERROR_HIP;
+  const void* const qp[2] = {q, nullptr};
+  const void* const kp[2] = {k, nullptr};
+  const void* const vp[2] = {v, nullptr};
+  void* const op[2] = {out, nullptr};
+  return run_fwd(false, qp, kp, vp, gains, valid_len, B, L, L, H, D, softmax_scale, eps, op, lse, workspace,
+                 stage_events, n_stage_events, stream);
 }
 
 jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float* gains,
@@ -189,39 +282,96 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
   const Range outs[] = {{dq, tb}, {dk, tb}, {dv, tb}, {dgains, (size_t)2 * D * 4}, {workspace, wl.total}};
   if (!outputs_disjoint(outs, 5, ins, 9)) return JATTN_ERROR_INVALID_VALUE;
 
-  char* ws = static_cast<char*>(workspace);
-  jattn::BwdArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.gains = gains;
-  a.valid_len = valid_len;
-  a.out = static_cast<const uint16_t*>(out);
-  a.lse = lse;
-  a.dout = static_cast<const uint16_t*>(dout);
-  a.dq = static_cast<uint16_t*>(dq);
-  a.dk = static_cast<uint16_t*>(dk);
-  a.dv = static_cast<uint16_t*>(dv);
-  a.dgains = dgains;
-  // normalised keys: the forward's own copy when the caller passes its workspace, else computed here
-  a.kr = fwd_workspace ? static_cast<uint16_t*>(const_cast<void*>(fwd_workspace))
-                       : reinterpret_cast<uint16_t*>(ws + wl.kr);
-  a.qs = reinterpret_cast<uint16_t*>(ws + wl.qs);
-  a.nlse2 = reinterpret_cast<float*>(ws + wl.nlse2);
-  a.ndelta = reinterpret_cast<float*>(ws + wl.ndelta);
-  a.part = reinterpret_cast<float*>(ws + wl.part);
-  a.B = B;
-  a.L = L;
-  a.H = H;
-  a.scale = softmax_scale;
-  a.c = softmax_scale * 1.4426950408889634f;
-  a.eps = eps;
-  a.nblk = (L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock;
-  a.items = B * H * a.nblk;
-  a.lp = a.nblk * kBwdRowsPerBlock;
-  return jattn::launch_bwd(D, a, fwd_workspace == nullptr, stage_events, n_stage_events, stream) == hipSuccess
-             ? JATTN_SUCCESS
-                                                                                    : JATTN_ERROR_HIP;
+  const void* const qp[2] = {q, nullptr};
+  const void* const kp[2] = {k, nullptr};
+  const void* const vp[2] = {v, nullptr};
+  const void* const op[2] = {out, nullptr};
+  const void* const dop[2] = {dout, nullptr};
+  void* const dqp[2] = {dq, nullptr};
+  void* const dkp[2] = {dk, nullptr};
+  void* const dvp[2] = {dv, nullptr};
+  return run_bwd(false, qp, kp, vp, gains, valid_len, op, lse, dop, B, L, L, H, D, softmax_scale, eps, dqp, dkp, dvp,
+                 dgains, workspace, fwd_workspace, stage_events, n_stage_events, stream);
+}
+
+jattn_status jattn_fwd_streams(const void* const q[2], const void* const k[2], const void* const v[2],
+                               const float* gains, const int32_t* valid_len, int B, int n_img, int n_txt, int H,
+                               int D, float softmax_scale, float eps, void* const out[2], float* lse,
+                               void* workspace, size_t workspace_bytes, const hipEvent_t* stage_events,
+                               int n_stage_events, hipStream_t stream) {
+  if (n_stage_events < 0 || n_stage_events > JATTN_FWD_STAGES || (n_stage_events > 0 && !stage_events))
+    return JATTN_ERROR_INVALID_VALUE;
+  if (!q || !k || !v || !out || !gains || !lse) return JATTN_ERROR_INVALID_VALUE;
+  int L = 0;
+  const jattn_status st = check_stream_sizes(B, n_img, n_txt, H, D, &L);
+  if (st != JATTN_SUCCESS) return st;
+  if (!pair_ok(q, n_img, n_txt) || !pair_ok(k, n_img, n_txt) || !pair_ok(v, n_img, n_txt) ||
+      !pair_ok(out, n_img, n_txt))
+    return JATTN_ERROR_INVALID_VALUE;
+  if (!std::isfinite(softmax_scale) || !std::isfinite(eps) || eps < 0.f) return JATTN_ERROR_INVALID_VALUE;
+  if (!aligned(gains, 4) || !aligned(lse, 4) || !aligned(valid_len, 4)) return JATTN_ERROR_INVALID_VALUE;
+  const size_t wsb = jattn_fwd_workspace_bytes(B, L, H, D);
+  if (!workspace || workspace_bytes < wsb) return JATTN_ERROR_WORKSPACE;
+  if (!aligned(workspace, 256)) return JATTN_ERROR_INVALID_VALUE;
+  const size_t ti = (size_t)B * n_img * H * D * 2, tt = (size_t)B * n_txt * H * D * 2, lb = (size_t)B * H * L * 4;
+  const Range ins[] = {{q[0], ti}, {q[1], tt}, {k[0], ti}, {k[1], tt}, {v[0], ti}, {v[1], tt},
+                       {gains, (size_t)4 * D * 4}, {valid_len, (size_t)B * 4}};
+  const Range outs[] = {{out[0], ti}, {out[1], tt}, {lse, lb}, {workspace, wsb}};
+  if (!outputs_disjoint(outs, 4, ins, 8)) return JATTN_ERROR_INVALID_VALUE;
+  // (pointers of an empty stream are never dereferenced; pass them on as null)
+  auto pick = [&](const void* const p[2], int s) -> const void* { return (s == 0 ? n_img : n_txt) > 0 ? p[s] : nullptr; };
+  const void* const qp[2] = {pick(q, 0), pick(q, 1)};
+  const void* const kp[2] = {pick(k, 0), pick(k, 1)};
+  const void* const vp[2] = {pick(v, 0), pick(v, 1)};
+  void* const op[2] = {n_img > 0 ? out[0] : nullptr, n_txt > 0 ? out[1] : nullptr};
+  return run_fwd(true, qp, kp, vp, gains, valid_len, B, L, n_img, H, D, softmax_scale, eps, op, lse, workspace,
+                 stage_events, n_stage_events, stream);
+}
+
+jattn_status jattn_bwd_streams(const void* const q[2], const void* const k[2], const void* const v[2],
+                               const float* gains, const int32_t* valid_len, const void* const out[2],
+                               const float* lse, const void* const dout[2], int B, int n_img, int n_txt, int H,
+                               int D, float softmax_scale, float eps, void* const dq[2], void* const dk[2],
+                               void* const dv[2], float* dgains, void* workspace, size_t workspace_bytes,
+                               const void* fwd_workspace, const hipEvent_t* stage_events, int n_stage_events,
+                               hipStream_t stream) {
+  if (n_stage_events < 0 || n_stage_events > JATTN_BWD_STAGES || (n_stage_events > 0 && !stage_events))
+    return JATTN_ERROR_INVALID_VALUE;
+  if (!q || !k || !v || !out || !dout || !dq || !dk || !dv || !gains || !lse || !dgains)
+    return JATTN_ERROR_INVALID_VALUE;
+  int L = 0;
+  const jattn_status st = check_stream_sizes(B, n_img, n_txt, H, D, &L);
+  if (st != JATTN_SUCCESS) return st;
+  if (!pair_ok(q, n_img, n_txt) || !pair_ok(k, n_img, n_txt) || !pair_ok(v, n_img, n_txt) ||
+      !pair_ok(out, n_img, n_txt) || !pair_ok(dout, n_img, n_txt) || !pair_ok(dq, n_img, n_txt) ||
+      !pair_ok(dk, n_img, n_txt) || !pair_ok(dv, n_img, n_txt))
+    return JATTN_ERROR_INVALID_VALUE;
+  if (!std::isfinite(softmax_scale) || !std::isfinite(eps) || eps < 0.f) return JATTN_ERROR_INVALID_VALUE;
+  if (!aligned(gains, 4) || !aligned(lse, 4) || !aligned(dgains, 4) || !aligned(valid_len, 4))
+    return JATTN_ERROR_INVALID_VALUE;
+  const WorkspaceLayout wl = workspace_layout(B, L, H, D);
+  if (!workspace || workspace_bytes < wl.total) return JATTN_ERROR_WORKSPACE;
+  if (!aligned(workspace, 256) || !aligned(fwd_workspace, 256)) return JATTN_ERROR_INVALID_VALUE;
+  const size_t ti = (size_t)B * n_img * H * D * 2, tt = (size_t)B * n_txt * H * D * 2, lb = (size_t)B * H * L * 4;
+  const size_t fwb = fwd_workspace ? jattn_fwd_workspace_bytes(B, L, H, D) : 0, gb = (size_t)4 * D * 4;
+  const Range ins[] = {{q[0], ti},   {q[1], tt},   {k[0], ti},    {k[1], tt},        {v[0], ti},
+                       {v[1], tt},   {out[0], ti}, {out[1], tt},  {dout[0], ti},     {dout[1], tt},
+                       {gains, gb},  {lse, lb},    {valid_len, (size_t)B * 4},      {fwd_workspace, fwb}};
+  const Range outs[] = {{dq[0], ti}, {dq[1], tt}, {dk[0], ti}, {dk[1], tt}, {dv[0], ti}, {dv[1], tt},
+                        {dgains, gb}, {workspace, wl.total}};
+  if (!outputs_disjoint(outs, 8, ins, 14)) return JATTN_ERROR_INVALID_VALUE;
+  auto pick = [&](const void* const p[2], int s) -> const void* { return (s == 0 ? n_img : n_txt) > 0 ? p[s] : nullptr; };
+  auto pickw = [&](void* const p[2], int s) -> void* { return (s == 0 ? n_img : n_txt) > 0 ? p[s] : nullptr; };
+  const void* const qp[2] = {pick(q, 0), pick(q, 1)};
+  const void* const kp[2] = {pick(k, 0), pick(k, 1)};
+  const void* const vp[2] = {pick(v, 0), pick(v, 1)};
+  const void* const op[2] = {pick(out, 0), pick(out, 1)};
+  const void* const dop[2] = {pick(dout, 0), pick(dout, 1)};
+  void* const dqp[2] = {pickw(dq, 0), pickw(dq, 1)};
+  void* const dkp[2] = {pickw(dk, 0), pickw(dk, 1)};
+  void* const dvp[2] = {pickw(dv, 0), pickw(dv, 1)};
+  return run_bwd(true, qp, kp, vp, gains, valid_len, op, lse, dop, B, L, n_img, H, D, softmax_scale, eps, dqp, dkp,
+                 dvp, dgains, workspace, fwd_workspace, stage_events, n_stage_events, stream);
 }
 
 }  // extern "C"

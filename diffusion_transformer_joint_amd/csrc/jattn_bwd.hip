@@ -27,6 +27,13 @@
 //    T. Padded keys get exact zeros.
 //  * a small kernel sums the partials in a fixed order and scales them by the other gain
 //    (deterministic dgains).
+//
+// Two-stream variant (S): image and text tokens in their own tensors, addressed through a two-block
+// row map, and a gain pair per stream. The gain product then depends on the (query, key) stream
+// pair and no longer factors out, so every normalised row carries its own stream's gain (Kr and the
+// register key rows the K gain, the query fragments and Qs the Q gain) and the gain gradients are
+// summed directly, dg_q,s = sum over queries of stream s of dQn * q * r_q (dq kernel) and
+// dg_k,s = sum over keys of stream s of dKn * k * r_k (dk/dv kernel), one partial-sum set each.
 // The streamed tiles go straight from memory into LDS (buffer loads with the LDS bit), issued two
 // tiles ahead into a ring of LDS buffers: no registers or VALU work are spent on staging.
 // dQ is recomputed rather than accumulated across key blocks: fp32 atomics on this chip sustain a
@@ -57,7 +64,13 @@ struct DqCfg {
   using LK = Lay<D, kSwizzled>;  // normalised key rows: S (row fragments) and dQ (transposed)
   using LV = Lay<D, kSwizzled>;  // value rows: dP (row fragments)
   static constexpr int NB = bwd_nbuf<D>();
-  static constexpr int BYTES = NB * (LK::ELEMS + LV::ELEMS) * 2;
+  static constexpr int STAGE = NB * (LK::ELEMS + LV::ELEMS) * 2;
+  // LDS bytes of the kernel (two-stream: the epilogue's per-stream column sums reuse the ring)
+  template <bool S>
+  static constexpr int bytes() {
+    return S && colsum2_scratch_floats<D, kBwdWaves>() * 4 > STAGE ? colsum2_scratch_floats<D, kBwdWaves>() * 4
+                                                                   : STAGE;
+  }
 };
 
 template <int D>
@@ -67,8 +80,11 @@ struct DkdvCfg {
   static constexpr int NB = bwd_nbuf<D>();
   static constexpr int STAGE = NB * (LQ::ELEMS + LO::ELEMS) * 2;
   static constexpr int STATS = NB * 2 * kTile * 4;  // -lse2 and -delta per streamed row
-  static constexpr int SCRATCH = colsum_scratch_floats<D, kBwdWaves>() * 4;
-  static constexpr int BYTES = STAGE + STATS > SCRATCH ? STAGE + STATS : SCRATCH;
+  template <bool S>
+  static constexpr int bytes() {
+    constexpr int scratch = (S ? colsum2_scratch_floats<D, kBwdWaves>() : colsum_scratch_floats<D, kBwdWaves>()) * 4;
+    return STAGE + STATS > scratch ? STAGE + STATS : scratch;
+  }
 };
 
 // A wave row in the C/D layout (pair j4 of tile mt holds d = 32 mt + 8 j4 + 4 g + [0..3]) as raw bf16
@@ -96,16 +112,17 @@ __device__ __forceinline__ void load_row_c(RowC<D>& x, const uint16_t* __restric
 // RMSNorm backward for one wave row held in the C/D layout (lane = row; register i of tile mt
 // holds d = 32*mt + 8*(i/4) + 4*g + i%4; the other half of the row is in lane l^32). On entry dxn
 // holds the gradient with respect to the normalised row divided by gpre[d] (the factor the MFMA
-// operands left out); xc is the raw row (zeros when not `valid`); `gain` is the row's own RMSNorm
-// gain. If `exists`, writes the bf16 gradient row
-// (zeros when not `valid`, i.e. a padded key) and, if xsrow is set, bf16(x * r * xs_mul). With TSUM,
-// dxn holds dxn * x * r on return (this row's term of T; zeros for rows that are not valid).
+// operands left out; null = 1); xc is the raw row (zeros when not `valid`); `gain` is the row's own
+// RMSNorm gain. If `exists`, writes the bf16 gradient row
+// (zeros when not `valid`, i.e. a padded key) and, if xsrow is set, bf16(x * r * xs_mul * xs_gain[d])
+// (xs_gain null = 1). With TSUM, dxn holds dxn * x * r on return (this row's term of the gain
+// gradient; zeros for rows that are not valid).
 template <int D, bool TSUM>
 __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT], const RowC<D>& xc,
                                                      const float* __restrict__ gain, const float* __restrict__ gpre,
                                                      float r, bool valid, bool exists,
                                                      uint16_t* __restrict__ dxrow, uint16_t* __restrict__ xsrow,
-                                                     float xs_mul, int g) {
+                                                     float xs_mul, const float* __restrict__ xs_gain, int g) {
   using Dm = Dims<D>;
   float x[Dm::MT][16];
   float gd[Dm::MT][16];  // gain * (gradient with respect to the normalised row)
@@ -121,7 +138,7 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
       for (int e = 0; e < 4; ++e) {
         const int i = j4 * 4 + e;
         x[mt][i] = xv[e];
-        gd[mt][i] = d0 < D ? gain[d0 + e] * gpre[d0 + e] * dxn[mt][i] : 0.f;
+        gd[mt][i] = d0 < D ? gain[d0 + e] * (gpre ? gpre[d0 + e] : 1.f) * dxn[mt][i] : 0.f;
         t += gd[mt][i] * xv[e];
       }
     }
@@ -142,9 +159,12 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
       if (exists && d0 < D) {
         *reinterpret_cast<u32x2*>(dxrow + d0) = (u32x2){pack2(y[0], y[1]), pack2(y[2], y[3])};
         const int i = j4 * 4;
-        if (xsrow)
-          *reinterpret_cast<u32x2*>(xsrow + d0) = (u32x2){pack2(x[mt][i] * xs, x[mt][i + 1] * xs),
-                                                          pack2(x[mt][i + 2] * xs, x[mt][i + 3] * xs)};
+        if (xsrow) {
+          float z[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] = x[mt][i + e] * xs * (xs_gain ? xs_gain[d0 + e] : 1.f);
+          *reinterpret_cast<u32x2*>(xsrow + d0) = (u32x2){pack2(z[0], z[1]), pack2(z[2], z[3])};
+        }
       }
       if constexpr (TSUM) {
 #pragma unroll
@@ -222,7 +242,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
 }
 
 // One work item of the dq kernel: query rows [128 blk, 128 blk + 128) of (batch, head) pair bh.
-template <int D>
+template <int D, bool S>
 __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, int blk) {
   using Dm = Dims<D>;
   using Cfg = DqCfg<D>;
@@ -235,40 +255,41 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
   const int L = a.L, H = a.H;
   const int b = bh / H;
   const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
-  const int rs = H * D;
-  const size_t base = ((size_t)b * L * H + (bh - b * H)) * D;
+  const RowMap<S> map(b, bh - b * H, L, H, D, a.n0);
 
   // start streaming the first key tiles before the per-row set-up
   const int ntiles = (n + kTile - 1) / kTile, nfull = n / kTile;
   DirectTile<D, LK, kBwdWaves> dk;
   DirectTile<D, LV, kBwdWaves> dv;
   dk.init(D, wave, lane);
-  dv.init(rs, wave, lane);
+  dv.init(map.rs, wave, lane);
   const uint16_t* kb = a.kr + (size_t)bh * L * D;
-  const uint16_t* vb = a.v + base;
   auto issue = [&](int t, int buf) {
     dk.issue(tile_rsrc<D>(kb, D, t * kTile, n), sk + buf * LK::ELEMS, wave);
-    dv.issue(tile_rsrc<D>(vb, rs, t * kTile, n), sv + buf * LV::ELEMS, wave);
+    dv.issue_blocks(S, a.v, a.v1, map.o0, map.o1, map.n0, map.rs, t * kTile, n, sv + buf * LV::ELEMS, wave,
+                                 lane);
   };
   for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
 
   const int qrow = blk * kBwdRowsPerBlock + wave * kWaveRows + l32;
   const bool qvalid = qrow < L;
-  const size_t roff = base + (size_t)qrow * rs;
+  // the row's Q gain (two-stream: its own stream's; the joint form folds both gains in)
+  const float* gq = a.gains + (S ? map.block(qrow) * 2 * D : 0);
+  const uint16_t* qptr = map.row(a.q, a.q1, qrow);
   bf16x8 qf[Dm::KS], dof[Dm::KS];
   float rq;
   {
     float x[Dm::KS][8];
-    load_row_chunks<D>(x, a.q + roff, qvalid, g);
-    rq = rmsnorm_row_frags<D>(qf, x, a.gains, a.gains + D, a.c, a.eps, qvalid, g);
+    load_row_chunks<D>(x, qptr, qvalid, g);
+    rq = rmsnorm_row_frags<D>(qf, x, gq, S ? nullptr : a.gains + D, a.c, a.eps, qvalid, g);
   }
-  load_row_frags_raw<D>(dof, a.dout + roff, qvalid, g);
+  load_row_frags_raw<D>(dof, map.row(a.dout, a.dout1, qrow), qvalid, g);
   RowC<D> xq;
-  if constexpr (keep_row_c<D>()) load_row_c<D>(xq, a.q + roff, qvalid, g);
+  if constexpr (keep_row_c<D>()) load_row_c<D>(xq, qptr, qvalid, g);
   float delta = 0.f;
   {
     float o[Dm::KS][8];
-    load_row_chunks<D>(o, a.out + roff, qvalid, g);
+    load_row_chunks<D>(o, map.row(a.out, a.out1, qrow), qvalid, g);
 #pragma unroll
     for (int ks = 0; ks < Dm::KS; ++ks)
 #pragma unroll
@@ -314,23 +335,36 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
     a.nlse2[si] = qvalid ? -lse2 : -INFINITY;
     a.ndelta[si] = qvalid ? -delta : 0.f;
   }
-  // dQn = scale * g_k * (dS Kr): the streamed key rows carry no gain
+  // dQn = scale * (dS Kr) times g_k in the joint form (its streamed key rows carry no gain)
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) acc[mt] *= a.scale;
-  if constexpr (!keep_row_c<D>()) load_row_c<D>(xq, a.q + roff, qvalid, g);
-  rmsnorm_backward_row<D, false>(acc, xq, a.gains, a.gains + D, rq, qvalid, qvalid, a.dq + roff,
-                                 a.qs + ((size_t)bh * L + qrow) * D, a.c, g);
+  if constexpr (!keep_row_c<D>()) load_row_c<D>(xq, qptr, qvalid, g);
+  uint16_t* qsrow = a.qs + ((size_t)bh * L + qrow) * D;
+  if constexpr (!S) {
+    rmsnorm_backward_row<D, false>(acc, xq, a.gains, a.gains + D, rq, qvalid, qvalid, map.row(a.dq, a.dq1, qrow),
+                                   qsrow, a.c, nullptr, g);
+  } else {
+    // Qs carries the row's own Q gain; the gain-gradient terms of the block go to the partial sets of
+    // the two streams (rows below n0 - 128 blk are image rows)
+    rmsnorm_backward_row<D, true>(acc, xq, gq, nullptr, rq, qvalid, qvalid, map.row(a.dq, a.dq1, qrow), qsrow, a.c,
+                                  gq, g);
+    const size_t set = (size_t)D * a.items, item = (size_t)bh * a.nblk + blk;
+    const int split = min(max(map.n0 - blk * kBwdRowsPerBlock, 0), kBwdRowsPerBlock);
+    block_column_sums2<D, kBwdWaves, true>(acc, reinterpret_cast<float*>(smem), a.part + item, a.part + 2 * set + item,
+                                           (size_t)a.items, split, tid);
+  }
 }
 
-template <int D>
+template <int D, bool S>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
 void bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[DqCfg<D>::BYTES];
-  // (an item ends with its tile loop's barrier and its epilogue does not touch LDS, so the next
-  // item may refill the ring right away)
+  __shared__ __attribute__((aligned(16))) char smem[DqCfg<D>::template bytes<S>()];
+  // (an item ends with its tile loop's barrier and, in the joint form, its epilogue does not touch
+  // LDS, so the next item may refill the ring right away; the two-stream epilogue's column sums do)
   for (ItemIter it(a.items); it.valid(); it.next()) {
     const int bh = it.item() / a.nblk;
-    dq_item<D>(a, smem, bh, it.item() - bh * a.nblk);
+    dq_item<D, S>(a, smem, bh, it.item() - bh * a.nblk);
+    if constexpr (S) __syncthreads();
   }
 }
 
@@ -411,8 +445,8 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const _
 }
 
 // `active`: this wave holds at least one valid key (a wave of padded keys only keeps the ring going).
-template <int D, bool KMASK>
-__device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t base, int bh, int rs,
+template <int D, bool S, bool KMASK>
+__device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, const RowMap<S>& map, int bh,
                                           const bf16x8 (&kf)[Dims<D>::KS], const bf16x8 (&vf)[Dims<D>::KS],
                                           f32x16 (&dva)[Dims<D>::MT], f32x16 (&dka)[Dims<D>::MT], bool kvalid,
                                           bool active, int tid) {
@@ -429,9 +463,10 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t b
   DirectTile<D, LQ, kBwdWaves> dq;
   DirectTile<D, LO, kBwdWaves> dout;
   dq.init(D, wave, lane);
+  const int rs = map.rs;
   dout.init(rs, wave, lane);
   const uint16_t* qb = a.qs + (size_t)bh * L * D;
-  const uint16_t* ob = a.dout + base;
+  const uint16_t* ob = a.dout + map.o0;  // (joint form)
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.nlse2 + (size_t)bh * a.lp, (uint32_t)a.lp * 4u);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.ndelta + (size_t)bh * a.lp, (uint32_t)a.lp * 4u);
   // Tile t: rows [64 t, 64 t + 64) of Qs and dO (zeros past L) and of the statistics (written by the
@@ -442,7 +477,11 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t b
     else if (wave == 1)
       lds_load_dwords(rd, sd + buf * kTile, (uint32_t)(t * kTile + lane) * 4u);
     dq.issue(tile_rsrc<D>(qb, D, t * kTile, L), sq + buf * LQ::ELEMS, wave);
-    dout.issue(tile_rsrc<D>(ob, rs, t * kTile, L), so + buf * LO::ELEMS, wave);
+    if constexpr (S)
+      dout.issue_blocks(true, a.dout, a.dout1, map.o0, map.o1, map.n0, rs, t * kTile, L, so + buf * LO::ELEMS, wave,
+                        lane);
+    else
+      dout.issue(tile_rsrc<D>(ob, rs, t * kTile, L), so + buf * LO::ELEMS, wave);
   };
   const int ntiles = (L + kTile - 1) / kTile;
   for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
@@ -465,44 +504,57 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, size_t b
 }
 
 // One work item of the dk/dv kernel: key rows [128 blk, 128 blk + 128) of (batch, head) pair bh.
-template <int D>
+template <int D, bool S>
 __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, int blk, int item) {
   using Dm = Dims<D>;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int L = a.L, H = a.H;
   const int b = bh / H;
   const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
-  const int rs = H * D;
-  const size_t base = ((size_t)b * L * H + (bh - b * H)) * D;
+  const RowMap<S> map(b, bh - b * H, L, H, D, a.n0);
+  const size_t set = (size_t)D * a.items;
 
   const int key = blk * kBwdRowsPerBlock + wave * kWaveRows + l32;
   const bool kin = key < L;      // row exists
   const bool kvalid = key < n;   // row is an unpadded key
-  const size_t roff = base + (size_t)key * rs;
+  const size_t roff = map.o0 + (size_t)key * map.rs;  // (joint form)
+  // (the joint form addresses its rows by one offset computed here: with pointers formed after the
+  // tile loop instead, the compiler schedules the loop's LDS reads one at a time)
 
   if (blk * kBwdRowsPerBlock >= n) {
     // every key of this workgroup is padding: exact zeros, no dg contribution
     if (kin) {
+      uint16_t* dkrow = map.row(a.dk, a.dk1, key);
+      uint16_t* dvrow = S ? map.row(a.dv, a.dv1, key) : a.dv + roff;
 #pragma unroll
       for (int c = g; c < Dm::NCH; c += 2) {
-        *reinterpret_cast<u32x4*>(a.dk + roff + c * 8) = (u32x4){0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(a.dv + roff + c * 8) = (u32x4){0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(dkrow + c * 8) = (u32x4){0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(dvrow + c * 8) = (u32x4){0u, 0u, 0u, 0u};
       }
     }
-    for (int d = tid; d < D; d += kBwdThreads) a.part[(size_t)d * a.items + item] = 0.f;
+    for (int d = tid; d < D; d += kBwdThreads) {
+      if constexpr (S) {
+        a.part[set + (size_t)d * a.items + item] = 0.f;
+        a.part[3 * set + (size_t)d * a.items + item] = 0.f;
+      } else {
+        a.part[(size_t)d * a.items + item] = 0.f;
+      }
+    }
     return;
   }
 
+  // the key's own K gain (two-stream) or both gains (joint form: the streamed Qs rows carry none)
+  const float* gk = a.gains + (S ? map.block(key) * 2 * D : 0) + D;
   bf16x8 kf[Dm::KS], vf[Dm::KS];
   float rk;
   {
     float x[Dm::KS][8];
-    load_row_chunks<D>(x, a.k + roff, kvalid, g);
-    rk = rmsnorm_row_frags<D>(kf, x, a.gains, a.gains + D, 1.f, a.eps, kvalid, g);  // k r_k g_q g_k
+    load_row_chunks<D>(x, S ? map.row(a.k, a.k1, key) : a.k + roff, kvalid, g);
+    rk = rmsnorm_row_frags<D>(kf, x, S ? gk : a.gains, S ? nullptr : a.gains + D, 1.f, a.eps, kvalid, g);
   }
-  load_row_frags_raw<D>(vf, a.v + roff, kvalid, g);
+  load_row_frags_raw<D>(vf, S ? map.row(a.v, a.v1, key) : a.v + roff, kvalid, g);
   RowC<D> xk;
-  if constexpr (keep_row_c<D>()) load_row_c<D>(xk, a.k + roff, kvalid, g);
+  if constexpr (keep_row_c<D>()) load_row_c<D>(xk, S ? map.row(a.k, a.k1, key) : a.k + roff, kvalid, g);
 
   f32x16 dva[Dm::MT], dka[Dm::MT];
 #pragma unroll
@@ -515,12 +567,13 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
   // waves whose 32 keys are all valid skip the key mask
   const bool active = blk * kBwdRowsPerBlock + wave * kWaveRows < n;
   if (blk * kBwdRowsPerBlock + (wave + 1) * kWaveRows <= n)
-    dkdv_loop<D, false>(a, smem, base, bh, rs, kf, vf, dva, dka, kvalid, active, tid);
+    dkdv_loop<D, S, false>(a, smem, map, bh, kf, vf, dva, dka, kvalid, active, tid);
   else
-    dkdv_loop<D, true>(a, smem, base, bh, rs, kf, vf, dva, dka, kvalid, active, tid);
+    dkdv_loop<D, S, true>(a, smem, map, bh, kf, vf, dva, dka, kvalid, active, tid);
 
   // dv (zeros at padded keys)
   if (kin) {
+    uint16_t* dvrow = S ? map.row(a.dv, a.dv1, key) : a.dv + roff;
 #pragma unroll
     for (int mt = 0; mt < Dm::MT; ++mt)
 #pragma unroll
@@ -530,17 +583,18 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
           float y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[e] = kvalid ? dva[mt][j4 * 4 + e] : 0.f;
-          *reinterpret_cast<u32x2*>(a.dv + roff + d0) = (u32x2){pack2(y[0], y[1]), pack2(y[2], y[3])};
+          *reinterpret_cast<u32x2*>(dvrow + d0) = (u32x2){pack2(y[0], y[1]), pack2(y[2], y[3])};
         }
       }
   }
-  // dKn = scale * dS^T Qn = ln(2) * g_q * dS^T Qs  (the streamed query rows carry scale * log2(e), no gain)
+  // dKn = scale * dS^T Qn = ln(2) * dS^T Qs, times g_q in the joint form (the streamed query rows carry
+  // scale * log2(e), and in the two-stream form also their own Q gain)
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) dka[mt] *= kLn2;
   if (kin) {
-    if constexpr (!keep_row_c<D>()) load_row_c<D>(xk, a.k + roff, kvalid, g);
-    rmsnorm_backward_row<D, true>(dka, xk, a.gains + D, a.gains, rk, kvalid, true, a.dk + roff, nullptr,
-                                  0.f, g);
+    if constexpr (!keep_row_c<D>()) load_row_c<D>(xk, map.row(a.k, a.k1, key), kvalid, g);
+    rmsnorm_backward_row<D, true>(dka, xk, gk, S ? nullptr : a.gains, rk, kvalid, true, S ? map.row(a.dk, a.dk1, key) : a.dk + roff,
+                                  nullptr, 0.f, nullptr, g);
   } else {
 #pragma unroll
     for (int mt = 0; mt < Dm::MT; ++mt)
@@ -548,32 +602,42 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
       for (int i = 0; i < 16; ++i) dka[mt][i] = 0.f;
   }
   __syncthreads();
-  block_column_sums<D, kBwdWaves>(dka, reinterpret_cast<float*>(smem), a.part + item, (size_t)a.items, tid);
+  if constexpr (S) {
+    const int split = min(max(map.n0 - blk * kBwdRowsPerBlock, 0), kBwdRowsPerBlock);
+    block_column_sums2<D, kBwdWaves, true>(dka, reinterpret_cast<float*>(smem), a.part + set + item,
+                                           a.part + 3 * set + item, (size_t)a.items, split, tid);
+  } else {
+    block_column_sums<D, kBwdWaves>(dka, reinterpret_cast<float*>(smem), a.part + item, (size_t)a.items, tid);
+  }
 }
 
-template <int D>
+template <int D, bool S>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
 void bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[DkdvCfg<D>::BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[DkdvCfg<D>::template bytes<S>()];
   for (ItemIter it(a.items); it.valid(); it.next()) {
     const int bh = it.item() / a.nblk;
-    dkdv_item<D>(a, smem, bh, it.item() - bh * a.nblk, it.item());
+    dkdv_item<D, S>(a, smem, bh, it.item() - bh * a.nblk, it.item());
     __syncthreads();  // the column-sum scratch overlaps the ring the next item refills
   }
 }
 
 // ------------------------------------------------------------------------------------------------
-// dgains[0][d] = g_k[d] * T[d] and dgains[1][d] = g_q[d] * T[d], with T[d] the sum over workgroups of
-// the partials (stored column-major, part[d][item]) in a fixed order. Block d: thread t sums items
-// t, t + 256, ... (coalesced), then the wave sums are combined by a fixed butterfly and in wave order.
+// Gain gradients from the per-workgroup partial sums (stored column-major, part[set][d][item]), each
+// summed in a fixed order: block x sums row x of the partials; thread t sums items t, t + 256, ...
+// (coalesced), then the wave sums are combined by a fixed butterfly and in wave order.
+// Joint form (x = d < D): dgains[0][d] = g_k[d] * T[d] and dgains[1][d] = g_q[d] * T[d] with T the
+// total of set 0. Two-stream form (x = set * D + d < 4 D): dgains[x] = the total of row x, i.e.
+// dgains[s][0] (Q gain of stream s) from set 2 s and dgains[s][1] from set 2 s + 1.
 constexpr int kReduceThreads = 256;
 
+template <bool S>
 __global__ __launch_bounds__(kReduceThreads) void dg_reduce_kernel(const float* __restrict__ part,
                                                                    const float* __restrict__ gains, int items,
                                                                    int D, float* __restrict__ dgains) {
   __shared__ float wsum[kReduceThreads / 64];
-  const int d = blockIdx.x, t = threadIdx.x;
-  const float* p = part + (size_t)d * items;
+  const int x = blockIdx.x, t = threadIdx.x;
+  const float* p = part + (size_t)x * items;
   float s = 0.f;
   int i = t;
   for (; i + 3 * kReduceThreads < items; i += 4 * kReduceThreads) {
@@ -593,12 +657,16 @@ __global__ __launch_bounds__(kReduceThreads) void dg_reduce_kernel(const float* 
     float total = 0.f;
 #pragma unroll
     for (int w = 0; w < kReduceThreads / 64; ++w) total += wsum[w];
-    dgains[d] = gains[D + d] * total;
-    dgains[D + d] = gains[d] * total;
+    if constexpr (S) {
+      dgains[x] = total;
+    } else {
+      dgains[x] = gains[D + x] * total;
+      dgains[D + x] = gains[x] * total;
+    }
   }
 }
 
-template <int D>
+template <int D, bool S>
 static hipError_t launch_bwd_d(const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
                                hipStream_t stream) {
   int stage = 0;
@@ -610,36 +678,48 @@ static hipError_t launch_bwd_d(const BwdArgs& a, bool prenorm, const hipEvent_t*
   };
   PrenormArgs p;
   p.k = a.k;
+  p.k1 = a.k1;
+  p.gains = a.gains;
   p.valid_len = a.valid_len;
   p.kr = a.kr;
   p.B = a.B;
   p.L = a.L;
   p.H = a.H;
+  p.n0 = a.n0;
   p.eps = a.eps;
-  hipError_t e = recorded(prenorm ? launch_prenorm(D, p, stream) : hipSuccess);
+  hipError_t e = recorded(prenorm ? launch_prenorm(D, S, p, stream) : hipSuccess);
   if (e != hipSuccess) return e;
   int grid = 0;
-  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dq_kernel<D>), a.items, kBwdThreads, &grid)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid), dim3(kBwdThreads), 0, stream, a);
-  if ((e = recorded(hipSuccess)) != hipSuccess) return e;
-  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dkdv_kernel<D>), a.items, kBwdThreads, &grid)) != hipSuccess)
+  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dq_kernel<D, S>), a.items, kBwdThreads, &grid)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid), dim3(kBwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, S>), dim3(grid), dim3(kBwdThreads), 0, stream, a);
   if ((e = recorded(hipSuccess)) != hipSuccess) return e;
-  hipLaunchKernelGGL(dg_reduce_kernel, dim3(D), dim3(kReduceThreads), 0, stream, a.part, a.gains, a.items, D,
-                     a.dgains);
+  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dkdv_kernel<D, S>), a.items, kBwdThreads, &grid)) !=
+      hipSuccess)
+    return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, S>), dim3(grid), dim3(kBwdThreads), 0, stream, a);
+  if ((e = recorded(hipSuccess)) != hipSuccess) return e;
+  hipLaunchKernelGGL(dg_reduce_kernel<S>, dim3(S ? kPartSets * D : D), dim3(kReduceThreads), 0, stream, a.part,
+                     a.gains, a.items, D, a.dgains);
   return recorded(hipSuccess);
 }
 
-hipError_t launch_bwd(int D, const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
-                      hipStream_t stream) {
+template <bool S>
+static hipError_t launch_bwd_s(int D, const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
+                               hipStream_t stream) {
   switch (D) {
-    case 32: return launch_bwd_d<32>(a, prenorm, events, n_events, stream);
-    case 64: return launch_bwd_d<64>(a, prenorm, events, n_events, stream);
-    case 72: return launch_bwd_d<72>(a, prenorm, events, n_events, stream);
-    case 128: return launch_bwd_d<128>(a, prenorm, events, n_events, stream);
+    case 32: return launch_bwd_d<32, S>(a, prenorm, events, n_events, stream);
+    case 64: return launch_bwd_d<64, S>(a, prenorm, events, n_events, stream);
+    case 72: return launch_bwd_d<72, S>(a, prenorm, events, n_events, stream);
+    case 128: return launch_bwd_d<128, S>(a, prenorm, events, n_events, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_bwd(int D, bool streams, const BwdArgs& a, bool prenorm, const hipEvent_t* events,
+                      int n_events, hipStream_t stream) {
+  return streams ? launch_bwd_s<true>(D, a, prenorm, events, n_events, stream)
+                 : launch_bwd_s<false>(D, a, prenorm, events, n_events, stream);
 }
 
 }  // namespace jattn

@@ -230,6 +230,17 @@ __device__ __forceinline__ uint32_t rows_bytes(int nrows, int rs) {
   return nrows > 0 ? (uint32_t)((nrows - 1) * rs + D) * 2u : 0u;
 }
 
+// Buffer resource for the tile starting at row `row0` of a [rows][D] view (row stride rs elements)
+// whose rows [0, nrows) are valid: later rows read as zeros.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int rs, int row0, int nrows) {
+  const uint32_t total = rows_bytes<D>(nrows, rs), start = (uint32_t)row0 * (uint32_t)rs * 2u;
+  // (the range is wave-uniform; saying so keeps the descriptor in scalar registers, where the
+  // buffer instructions need it, instead of a loop over its distinct per-lane values)
+  const uint32_t range = __builtin_amdgcn_readfirstlane(total > start ? total - start : 0u);
+  return make_rsrc(base + (size_t)row0 * rs, range);
+}
+
 // Load rows [row0, row0 + kTile) through a buffer resource that covers the valid rows only; rows
 // outside it read as zeros.
 template <int D>
@@ -259,6 +270,7 @@ __device__ __forceinline__ void tile_load_buf(TileRegs<D>& t, __amdgpu_buffer_rs
 template <int D, class LY, int W = 4>
 struct DirectTile {  // W waves share the loads of a tile
   using Dm = Dims<D>;
+  static constexpr int HEAD_DIM = D;
   static constexpr int CPR = LY::PITCH / 8;                 // physical chunks per row (incl. padding)
   static constexpr int NWL = (kTile * CPR + 63) / 64;       // wave loads per tile
   static constexpr int PER_WAVE = (NWL + W - 1) / W;        // most loads one wave issues
@@ -288,6 +300,45 @@ struct DirectTile {  // W waves share the loads of a tile
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (JATTN_LDS void*)(lds + i * 512), 16, voff[j], 0, 0, 0);
     }
   }
+  // Issue a tile whose rows [0, split) come from `r0` (addressed from the tile's first row) and rows
+  // [split, kTile) from `r1` (addressed from tile row `split`); 0 < split < kTile. Each lane loads
+  // through the resource of its own row, with the other lanes switched off, so a wave may issue up
+  // to two loads where `issue` issues one. Lanes of padding positions keep an out-of-range offset
+  // under either resource and still write zeros.
+  __device__ __forceinline__ void issue_split(__amdgpu_buffer_rsrc_t r0, __amdgpu_buffer_rsrc_t r1, int split,
+                                              int rs, __bf16* __restrict__ lds, int wave, int lane) const {
+    const uint32_t shift = (uint32_t)split * (uint32_t)rs * 2u;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int i = wave + W * j;
+      if (NWL % W == 0 || i < NWL) {
+        const int row = (i * 64 + lane) / CPR;
+        if (row < split)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r0, (JATTN_LDS void*)(lds + i * 512), 16, voff[j], 0, 0, 0);
+        if (row >= split)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, (JATTN_LDS void*)(lds + i * 512), 16, voff[j] - shift, 0, 0,
+                                                   0);
+      }
+    }
+  }
+  // Issue the tile of rows [row0, row0 + kTile) of a tensor stored in two row blocks (see RowMap:
+  // rows [0, n0) at p0 + o0, rows [n0, ...) at p1 + o1, row stride rs) whose rows [0, n) are valid
+  // (later rows read as zeros). A tile inside one block takes one resource; the (at most one per
+  // sequence) tile across the block boundary is split per lane. two = false: block 0 only (callers
+  // pass a compile-time constant). n and n0 are wave-uniform.
+  // (An ordinary member rather than a member template: the host-side pass of the compiler rejected
+  // calls of such a member template from the dk/dv loop.)
+  __device__ __forceinline__ void issue_blocks(bool two, const uint16_t* p0, const uint16_t* p1, size_t o0, size_t o1,
+                                               int n0, int rs, int row0, int n, __bf16* __restrict__ lds, int wave,
+                                               int lane) const {
+    if (!two || row0 + kTile <= n0 || n <= n0)  // (no valid row in block 1: it is never addressed)
+      issue(tile_rsrc<D>(p0 + o0, rs, row0, two ? min(n, n0) : n), lds, wave);
+    else if (row0 >= n0)
+      issue(tile_rsrc<D>(p1 + o1, rs, row0 - n0, n - n0), lds, wave);
+    else
+      issue_split(tile_rsrc<D>(p0 + o0, rs, row0, min(n, n0)), tile_rsrc<D>(p1 + o1, rs, 0, n - n0), n0 - row0, rs,
+                  lds, wave, lane);
+  }
 };
 
 // Direct-to-LDS load of one dword per lane: lane l's word (byte offset voff in rsrc) lands at dst[l].
@@ -295,16 +346,28 @@ __device__ __forceinline__ void lds_load_dwords(__amdgpu_buffer_rsrc_t rsrc, flo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (JATTN_LDS void*)dst, 4, voff, 0, 0, 0);
 }
 
-// Buffer resource for the tile starting at row `row0` of a [rows][D] view (row stride rs elements)
-// whose rows [0, nrows) are valid: later rows read as zeros.
-template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int rs, int row0, int nrows) {
-  const uint32_t total = rows_bytes<D>(nrows, rs), start = (uint32_t)row0 * (uint32_t)rs * 2u;
-  // (the range is wave-uniform; saying so keeps the descriptor in scalar registers, where the
-  // buffer instructions need it, instead of a loop over its distinct per-lane values)
-  const uint32_t range = __builtin_amdgcn_readfirstlane(total > start ? total - start : 0u);
-  return make_rsrc(base + (size_t)row0 * rs, range);
-}
+
+// Addresses of the rows of one (batch, head) pair of a per-token tensor stored in two row blocks
+// (rows [0, n0) of each sequence in block 0, [B, n0, H, D]; rows [n0, L) in block 1,
+// [B, L - n0, H, D]; the joint layout is n0 = L). o0 / o1: element offsets of row 0 in block 0 and
+// of row n0 in block 1. With S = false only block 0 exists and no per-row selection is made.
+template <bool S>
+struct RowMap {
+  size_t o0, o1;
+  int n0, rs;
+  __device__ RowMap(int b, int h, int L, int H, int D, int n_0) {
+    n0 = S ? n_0 : L;
+    rs = H * D;
+    o0 = ((size_t)b * n0 * H + h) * D;
+    o1 = ((size_t)b * (L - n0) * H + h) * D;
+  }
+  template <class T>
+  __device__ __forceinline__ T* row(T* p0, T* p1, int r) const {
+    if constexpr (!S) return p0 + o0 + (size_t)r * rs;
+    else return r < n0 ? p0 + o0 + (size_t)r * rs : p1 + o1 + (size_t)(r - n0) * rs;
+  }
+  __device__ __forceinline__ int block(int r) const { return S && r >= n0 ? 1 : 0; }
+};
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Workgroup barrier for the tile-streaming loops: each wave first waits until at most N of its
@@ -515,13 +578,22 @@ __host__ __device__ constexpr int colsum_scratch_floats() {
 }
 
 template <int D, int W>
-__device__ __forceinline__ void block_column_sums(const f32x16 (&v)[Dims<D>::MT], float* scr,
-                                                  float* __restrict__ out, size_t stride, int tid) {
+__host__ __device__ constexpr int colsum2_scratch_floats() {
+  return 32 * W * (Dims<D>::DM + 1) + 16 * Dims<D>::DM;
+}
+
+// As block_column_sums, with the rows split in two groups: rows [0, split) of the block (row index
+// 32 * wave + lane % 32) are summed into out0, rows [split, 32 W) into out1 (TWO only; without TWO
+// every row goes to out0 and out1 is not touched). Scratch: colsum2_scratch_floats<D, W>() floats.
+template <int D, int W, bool TWO>
+__device__ __forceinline__ void block_column_sums2(const f32x16 (&v)[Dims<D>::MT], float* scr,
+                                                   float* __restrict__ out0, float* __restrict__ out1, size_t stride,
+                                                   int split, int tid) {
   using Dm = Dims<D>;
   constexpr int P = Dm::DM + 1, ROWS = 32 * W, THREADS = 64 * W;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   float* rows = scr;             // [ROWS][P]
-  float* segs = scr + ROWS * P;  // [SEGS][DM]
+  float* segs = scr + ROWS * P;  // [TWO + 1][SEGS][DM]
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt)
 #pragma unroll
@@ -537,10 +609,22 @@ __device__ __forceinline__ void block_column_sums(const f32x16 (&v)[Dims<D>::MT]
   {
     const int col = tid % COLS, seg = tid / COLS;
     if (col < Dm::DM) {
-      float s = 0.f;
+      if constexpr (!TWO) {
+        float s = 0.f;
 #pragma unroll 8
-      for (int r = 0; r < RPS; ++r) s += rows[(seg * RPS + r) * P + col];
-      segs[seg * Dm::DM + col] = s;
+        for (int r = 0; r < RPS; ++r) s += rows[(seg * RPS + r) * P + col];
+        segs[seg * Dm::DM + col] = s;
+      } else {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < RPS; ++r) {
+          const float x = rows[(seg * RPS + r) * P + col];
+          if (seg * RPS + r < split) s0 += x;
+          else s1 += x;
+        }
+        segs[seg * Dm::DM + col] = s0;
+        segs[(SEGS + seg) * Dm::DM + col] = s1;
+      }
     }
   }
   __syncthreads();
@@ -548,8 +632,20 @@ __device__ __forceinline__ void block_column_sums(const f32x16 (&v)[Dims<D>::MT]
     float s = 0.f;
 #pragma unroll
     for (int seg = 0; seg < SEGS; ++seg) s += segs[seg * Dm::DM + d];
-    out[d * stride] = s;
+    out0[d * stride] = s;
+    if constexpr (TWO) {
+      float t = 0.f;
+#pragma unroll
+      for (int seg = 0; seg < SEGS; ++seg) t += segs[(SEGS + seg) * Dm::DM + d];
+      out1[d * stride] = t;
+    }
   }
+}
+
+template <int D, int W>
+__device__ __forceinline__ void block_column_sums(const f32x16 (&v)[Dims<D>::MT], float* scr,
+                                                  float* __restrict__ out, size_t stride, int tid) {
+  block_column_sums2<D, W, false>(v, scr, out, nullptr, stride, 32 * W, tid);
 }
 
 }  // namespace jattn

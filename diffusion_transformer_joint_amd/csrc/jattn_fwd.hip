@@ -18,8 +18,15 @@
 // registers for the whole loop, and the staged key rows are only normalised, Kr = bf16(k * r_k), so
 // S' = Q' Kr^T = scale * log2(e) * Qn Kn^T comes out in log2 units.
 //
+// Two-stream variant (S): image and text tokens stay in their own tensors (the per-stream QKV of
+// the README's DiT-layer box, without the concatenation and split copies) and each stream has its
+// own gain pair. Query rows, value tiles and output rows are addressed through a two-block row map;
+// the K gain of each key's stream is applied by the prenorm kernel (Kr = bf16(k * r_k * g_k)) and
+// the query side carries only its own Q gain.
+//
 // Softmax shift. QK-RMSNorm bounds every score: ||k_j * r_k|| <= sqrt(D) for any key, so
-// |S'_ij| <= B_i = ||Q'_i|| * sqrt(D) (plus a margin for bf16 rounding). When every row of the
+// |S'_ij| <= B_i = ||Q'_i|| * sqrt(D) (plus a margin for bf16 rounding; two-stream:
+// B_i = max_s ||Q'_i * g_k,s|| * sqrt(D) over the two streams' K gains). When every row of the
 // workgroup has B_i <= 48 (log2 units), the kernel uses the fixed shift B_i instead of a running
 // maximum: the MFMA accumulator starts at -B_i, exp2 of the result lies in [2^-96, 1], and no row
 // maximum, rescale or cross-lane exchange is needed inside the loop. Otherwise (large scale or gains)
@@ -137,7 +144,7 @@ __device__ __forceinline__ void fwd_tile(const __bf16* __restrict__ kt, const __
 
 // The LDS ring of key and value tiles: tile t lives in buffer t % NB. The first NB - 1 tiles are
 // issued by the kernel before its prologue; each step issues the tile NB - 1 ahead.
-template <int D>
+template <int D, bool S>
 struct FwdRing {
   using LK = typename Fwd<D>::LK;
   using LV = typename Fwd<D>::LV;
@@ -146,20 +153,23 @@ struct FwdRing {
   __bf16* sk;
   __bf16* sv;
   const uint16_t* kb;  // Kr rows of this (batch, head), row stride D
-  const uint16_t* vb;  // V rows, row stride rs
-  int rs, n, ntiles, wave;
+  const uint16_t* v0;  // value rows, two blocks (see RowMap)
+  const uint16_t* v1;
+  RowMap<S> map;
+  int n, ntiles, wave, lane;
   DirectTile<D, LK> dk;
   DirectTile<D, LV> dv;
+  __device__ FwdRing(const RowMap<S>& m) : map(m) {}
   __device__ __forceinline__ void issue(int t, int buf) {
     dk.issue(tile_rsrc<D>(kb, D, t * kTile, n), sk + buf * LK::ELEMS, wave);
-    dv.issue(tile_rsrc<D>(vb, rs, t * kTile, n), sv + buf * LV::ELEMS, wave);
+    dv.issue_blocks(S, v0, v1, map.o0, map.o1, map.n0, map.rs, t * kTile, n, sv + buf * LV::ELEMS, wave, lane);
   }
 };
 
 // `active`: this wave has at least one query row inside the sequence (a wave past L only keeps the
 // ring going: it issues its share of the loads and meets the barriers, but skips the math).
-template <int D, bool BOUNDED>
-__device__ __forceinline__ void fwd_loop(FwdRing<D>& ring, const bf16x8 (&qf)[Fwd<D>::QT][Dims<D>::KS],
+template <int D, bool S, bool BOUNDED>
+__device__ __forceinline__ void fwd_loop(FwdRing<D, S>& ring, const bf16x8 (&qf)[Fwd<D>::QT][Dims<D>::KS],
                                          const float (&shift)[Fwd<D>::QT], FwdState<D>& st, bool active,
                                          int lane) {
   using LK = typename Fwd<D>::LK;
@@ -177,7 +187,7 @@ __device__ __forceinline__ void fwd_loop(FwdRing<D>& ring, const bf16x8 (&qf)[Fw
     if (active)
       fwd_tile<D, BOUNDED, decltype(masked)::value>(ring.sk + cur * LK::ELEMS, ring.sv + cur * LV::ELEMS, qf,
                                                     cinit, st, t * kTile, n, lane);
-    ring_barrier<FwdRing<D>::PER, NB - 2>(ntiles - 2 - t);
+    ring_barrier<FwdRing<D, S>::PER, NB - 2>(ntiles - 2 - t);
     cur = cur + 1 == NB ? 0 : cur + 1;
   };
   for (int t = 0; t < nfull; ++t) step(std::false_type{}, t);
@@ -185,7 +195,7 @@ __device__ __forceinline__ void fwd_loop(FwdRing<D>& ring, const bf16x8 (&qf)[Fw
 }
 
 // One work item: query rows [ROWS blk, ROWS blk + ROWS) of (batch, head) pair bh.
-template <int D>
+template <int D, bool S>
 __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, int blk) {
   using Dm = Dims<D>;
   constexpr int QT = Fwd<D>::QT;
@@ -194,25 +204,26 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
   const int L = a.L, H = a.H;
   const int b = bh / H;
   const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
-  const int rs = H * D;
-  const size_t base = ((size_t)b * L * H + (bh - b * H)) * D;
+  const RowMap<S> map(b, bh - b * H, L, H, D, a.n0);
 
   // start streaming the first key/value tiles before the per-row set-up
-  FwdRing<D> ring;
+  FwdRing<D, S> ring(map);
   ring.sk = reinterpret_cast<__bf16*>(smem);
   ring.sv = ring.sk + Fwd<D>::NB * Fwd<D>::LK::ELEMS;
   ring.kb = a.kr + (size_t)bh * L * D;
-  ring.vb = a.v + base;
-  ring.rs = rs;
+  ring.v0 = a.v;
+  ring.v1 = a.v1;
   ring.n = n;
   ring.ntiles = (n + kTile - 1) / kTile;
   ring.wave = wave;
+  ring.lane = lane;
   ring.dk.init(D, wave, lane);
-  ring.dv.init(rs, wave, lane);
+  ring.dv.init(map.rs, wave, lane);
   for (int t = 0; t < Fwd<D>::NB - 1 && t < ring.ntiles; ++t) ring.issue(t, t);
 
-  // This wave's query rows, normalised with both gains and pre-scaled, as B-operand fragments,
-  // and their score bounds in log2 units (margin covers the bf16 rounding of Kr and Q').
+  // This wave's query rows, normalised with both gains (two-stream: its own stream's Q gain) and
+  // pre-scaled, as B-operand fragments, and their score bounds in log2 units (margin covers the
+  // bf16 rounding of Kr and Q').
   int qrow[QT];
   bf16x8 qf[QT][Dm::KS];
   float shift[QT];
@@ -222,17 +233,38 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
     qrow[qt] = blk * Fwd<D>::ROWS + wave * 32 * QT + qt * 32 + l32;
     const bool qvalid = qrow[qt] < L;
     float x[Dm::KS][8];
-    load_row_chunks<D>(x, a.q + base + (size_t)qrow[qt] * rs, qvalid, g);
-    rmsnorm_row_frags<D>(qf[qt], x, a.gains, a.gains + D, a.c, a.eps, qvalid, g);
+    load_row_chunks<D>(x, map.row(a.q, a.q1, qrow[qt]), qvalid, g);
     float qq = 0.f;
+    if constexpr (!S) {
+      rmsnorm_row_frags<D>(qf[qt], x, a.gains, a.gains + D, a.c, a.eps, qvalid, g);
 #pragma unroll
-    for (int ks = 0; ks < Dm::KS; ++ks)
+      for (int ks = 0; ks < Dm::KS; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float y = (float)qf[qt][ks][e];
-        qq += y * y;
-      }
-    qq += __shfl_xor(qq, 32);
+        for (int e = 0; e < 8; ++e) {
+          const float y = (float)qf[qt][ks][e];
+          qq += y * y;
+        }
+      qq += __shfl_xor(qq, 32);
+    } else {
+      const float* gs = a.gains + map.block(qrow[qt]) * 2 * D;
+      rmsnorm_row_frags<D>(qf[qt], x, gs, nullptr, a.c, a.eps, qvalid, g);
+      float q0 = 0.f, q1 = 0.f;  // |Q' * g_k|^2 for the K gains of both streams
+#pragma unroll
+      for (int ks = 0; ks < Dm::KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = (2 * ks + g) * 8 + e;
+          if (d < D) {
+            const float y = (float)qf[qt][ks][e];
+            const float y0 = y * a.gains[D + d], y1 = y * a.gains[3 * D + d];
+            q0 += y0 * y0;
+            q1 += y1 * y1;
+          }
+        }
+      q0 += __shfl_xor(q0, 32);
+      q1 += __shfl_xor(q1, 32);
+      qq = fmaxf(q0, q1);
+    }
     shift[qt] = sqrtf(qq) * sqrtf((float)D) * (1.f + 1.f / 64.f);
     wmax = fmaxf(wmax, wave_max(shift[qt]));
   }
@@ -254,11 +286,11 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
   if (bmax <= kBoundLimit) {  // uniform over the workgroup
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = shift[qt];
-    fwd_loop<D, true>(ring, qf, shift, st, active, lane);
+    fwd_loop<D, S, true>(ring, qf, shift, st, active, lane);
   } else {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = -INFINITY;
-    fwd_loop<D, false>(ring, qf, shift, st, active, lane);
+    fwd_loop<D, S, false>(ring, qf, shift, st, active, lane);
   }
 
 #pragma unroll
@@ -268,7 +300,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     if (g == 0)
       a.lse[(size_t)bh * L + qrow[qt]] = lsum > 0.f ? (st.mrow[qt] + __log2f(lsum)) * kLn2 : -INFINITY;
-    uint16_t* orow = a.out + base + (size_t)qrow[qt] * rs;
+    uint16_t* orow = map.row(a.out, a.out1, qrow[qt]);
 #pragma unroll
     for (int mt = 0; mt < Dm::MT; ++mt)
 #pragma unroll
@@ -284,7 +316,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
   }
 }
 
-template <int D>
+template <int D, bool S>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Fwd<D>::BYTES];
   // one item per workgroup (a persistent grid measured slower here: the items are few and large),
@@ -292,36 +324,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const ItemIter it(a.items);
   if (!it.valid()) return;
   const int bh = it.item() / a.nblk;
-  fwd_item<D>(a, smem, bh, it.item() - bh * a.nblk);
+  fwd_item<D, S>(a, smem, bh, it.item() - bh * a.nblk);
 }
 
-template <int D>
+template <int D, bool S>
 static hipError_t launch_fwd_d(const FwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream) {
   PrenormArgs p;
   p.k = a.k;
+  p.k1 = a.k1;
+  p.gains = a.gains;
   p.valid_len = a.valid_len;
   p.kr = const_cast<uint16_t*>(a.kr);
   p.B = a.B;
   p.L = a.L;
   p.H = a.H;
+  p.n0 = a.n0;
   p.eps = a.eps;
-  hipError_t e = launch_prenorm(D, p, stream);
+  hipError_t e = launch_prenorm(D, S, p, stream);
   if (e == hipSuccess && n_events > 0) e = hipEventRecord(events[0], stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fwd_kernel<D>, dim3(grid_for_items(a.items)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, S>), dim3(grid_for_items(a.items)), dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e == hipSuccess && n_events > 1) e = hipEventRecord(events[1], stream);
   return e;
 }
 
-hipError_t launch_fwd(int D, const FwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream) {
+template <bool S>
+static hipError_t launch_fwd_s(int D, const FwdArgs& a, const hipEvent_t* events, int n_events,
+                               hipStream_t stream) {
   switch (D) {
-    case 32: return launch_fwd_d<32>(a, events, n_events, stream);
-    case 64: return launch_fwd_d<64>(a, events, n_events, stream);
-    case 72: return launch_fwd_d<72>(a, events, n_events, stream);
-    case 128: return launch_fwd_d<128>(a, events, n_events, stream);
+    case 32: return launch_fwd_d<32, S>(a, events, n_events, stream);
+    case 64: return launch_fwd_d<64, S>(a, events, n_events, stream);
+    case 72: return launch_fwd_d<72, S>(a, events, n_events, stream);
+    case 128: return launch_fwd_d<128, S>(a, events, n_events, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_fwd(int D, bool streams, const FwdArgs& a, const hipEvent_t* events, int n_events,
+                      hipStream_t stream) {
+  return streams ? launch_fwd_s<true>(D, a, events, n_events, stream)
+                 : launch_fwd_s<false>(D, a, events, n_events, stream);
 }
 
 }  // namespace jattn

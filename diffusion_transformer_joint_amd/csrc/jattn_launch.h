@@ -7,11 +7,22 @@
 
 namespace jattn {
 
+// Token rows. Every per-token tensor is [B, L, H, D] bf16 with the rows of each sequence stored in
+// two blocks: rows [0, n0) in the tensor's first pointer ([B, n0, H, D]) and rows [n0, L) in its
+// second pointer (the `*1` fields, [B, L - n0, H, D]). The joint layout is the case n0 = L (second
+// pointers unused). The two-stream entry points pass the image stream as block 0 (n0 = N_img) and
+// the text stream as block 1; their kernels also select the QK-norm gains per row by block.
+//
+// Gains: joint entry points [2, D] (Q row, K row); two-stream entry points [2, 2, D]
+// (gains[s][0] = Q gain and gains[s][1] = K gain of block s).
+
 struct PrenormArgs {
   const uint16_t* k;
+  const uint16_t* k1;
+  const float* gains;        // two-stream only: K rows are multiplied by their block's K gain
   const int32_t* valid_len;  // [B] or nullptr
-  uint16_t* kr;              // [B, H, L, D]: bf16(k * r_k), valid keys only
-  int B, L, H;
+  uint16_t* kr;              // [B, H, L, D]: bf16(k * r_k) (times the K gain, two-stream), valid keys only
+  int B, L, H, n0;
   float eps;
 };
 
@@ -19,12 +30,16 @@ struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const uint16_t* kr;      // workspace [B, H, L, D]: bf16(k * r_k), written by the prenorm kernel
-  const float* gains;      // [2, D]
+  const uint16_t* q1;
+  const uint16_t* k1;
+  const uint16_t* v1;
+  const uint16_t* kr;      // workspace [B, H, L, D]: normalised keys, written by the prenorm kernel
+  const float* gains;
   const int32_t* valid_len;  // [B] or nullptr
   uint16_t* out;
+  uint16_t* out1;
   float* lse;              // [B, H, L] natural log
-  int B, L, H;
+  int B, L, H, n0;
   float c;                 // softmax_scale * log2(e)
   float eps;
   int nblk;                // query blocks per (batch, head)
@@ -35,21 +50,29 @@ struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
+  const uint16_t* q1;
+  const uint16_t* k1;
+  const uint16_t* v1;
   const float* gains;
   const int32_t* valid_len;
   const uint16_t* out;
+  const uint16_t* out1;
   const float* lse;
   const uint16_t* dout;
+  const uint16_t* dout1;
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dgains;           // [2, D]
-  uint16_t* kr;            // workspace [B, H, L, D]: bf16(k * r_k), valid keys only
-  uint16_t* qs;            // workspace [B, H, L, D]: bf16(scale * log2(e) * q * r_q)
+  uint16_t* dq1;
+  uint16_t* dk1;
+  uint16_t* dv1;
+  float* dgains;           // [2, D] (joint) or [2, 2, D] (two-stream)
+  uint16_t* kr;            // workspace [B, H, L, D]: normalised keys, valid keys only
+  uint16_t* qs;            // workspace [B, H, L, D]: bf16(scale * log2(e) * q * r_q) (times the Q gain, two-stream)
   float* nlse2;            // workspace [B, H, lp]: -lse * log2(e) (-inf past L)
   float* ndelta;           // workspace [B, H, lp]: -rowsum(dout * out) (0 past L)
-  float* part;             // workspace [items, D]: per key block partial sums of T (see jattn_bwd.hip)
-  int B, L, H;
+  float* part;             // workspace [kPartSets, D, items]: per row block partial sums of the gain gradients
+  int B, L, H, n0;
   float scale;
   float c;                 // scale * log2(e)
   float eps;
@@ -66,19 +89,25 @@ constexpr int fwd_rows_per_block(int D) { return D <= 64 ? 256 : 128; }
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRowsPerBlock = 32 * kBwdWaves;
+// Partial-sum sets of the gain gradients in the backward workspace: the joint pass uses set 0 (the
+// shared factor T); the two-stream pass uses set 2 s (Q gain of block s, from the dq kernel) and
+// set 2 s + 1 (K gain of block s, from the dk/dv kernel).
+constexpr int kPartSets = 4;
 
 // Grid size of a persistent kernel (`threads` per workgroup, no dynamic LDS) over `items` work items:
 // as many workgroups as the current device keeps resident at once, a multiple of 8 and no more than
 // the items need (rounded up to 8).
 hipError_t persistent_grid(const void* kernel, int items, int threads, int* grid);
 
-hipError_t launch_prenorm(int D, const PrenormArgs& a, hipStream_t stream);
+// `streams` selects the two-stream kernels (two row blocks, gains per block) over the joint ones.
+hipError_t launch_prenorm(int D, bool streams, const PrenormArgs& a, hipStream_t stream);
 // Enqueues the key normalisation (into a.kr) and the forward kernel; if n_events > 0, records
 // events[i] after stage i (i < n_events).
-hipError_t launch_fwd(int D, const FwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream);
+hipError_t launch_fwd(int D, bool streams, const FwdArgs& a, const hipEvent_t* events, int n_events,
+                      hipStream_t stream);
 // Enqueues the backward kernels (the key normalisation only if `prenorm`; a.kr then already holds
 // it); if n_events > 0, records events[i] after stage i (i < n_events).
-hipError_t launch_bwd(int D, const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
-                      hipStream_t stream);
+hipError_t launch_bwd(int D, bool streams, const BwdArgs& a, bool prenorm, const hipEvent_t* events,
+                      int n_events, hipStream_t stream);
 
 }  // namespace jattn

@@ -2,18 +2,23 @@
 //
 // The normalised keys Kr = k * r_k with r_k = (mean_d k^2 + eps)^(-1/2) (the RMSNorm of the QK-norm
 // row in the re-diffusion README's design-notes table, without its gain) are written once per call
-// as bf16 in a [B, H, L, D] layout. Both gains are folded into the query side by the attention
-// kernels, which then stream Kr tiles straight into LDS with no arithmetic on the way.
+// as bf16 in a [B, H, L, D] layout. With one gain pair for all tokens both gains are folded into the
+// query side by the attention kernels; with a gain pair per stream (the two-stream entry points) the
+// K gain of each key's stream is applied here. The attention kernels then stream Kr tiles straight
+// into LDS with no arithmetic on the way.
 #include "jattn_device.h"
 #include "jattn_launch.h"
 
 namespace jattn {
 
 // Kr[b, h, l, :] = bf16(k[b, l, h, :] * r_k) for the valid keys (l < valid length; later rows are
-// never read). Thread t covers chunks t%TPR + j*TPR of row t/TPR of each pass.
+// never read). Thread t covers chunks t%TPR + j*TPR of row t/TPR of each pass; rows are taken in
+// the joint (b, l, h) order. Two-stream variant (S): the key rows come from two blocks (rows
+// l < n0 from a.k, the rest from a.k1) and each is also multiplied by its block's K gain, since the
+// query side can no longer carry one K gain for every key.
 constexpr int kPrenormPasses = 4;
 
-template <int D>
+template <int D, bool S>
 __global__ __launch_bounds__(kThreads) void prenorm_kernel(PrenormArgs a) {
   using Dm = Dims<D>;
   const int tid = threadIdx.x, rr = tid / Dm::TPR, cc = tid % Dm::TPR;
@@ -23,11 +28,17 @@ __global__ __launch_bounds__(kThreads) void prenorm_kernel(PrenormArgs a) {
   int row[kPrenormPasses];
 #pragma unroll
   for (int p = 0; p < kPrenormPasses; ++p) {
-    row[p] = (blockIdx.x * kPrenormPasses + p) * Dm::RPP + rr;  // input row (b * L + l) * H + h
+    row[p] = (blockIdx.x * kPrenormPasses + p) * Dm::RPP + rr;  // joint row (b * L + l) * H + h
+    const uint16_t* src = a.k + (size_t)row[p] * D;
+    if constexpr (S) {
+      const int R = row[p] < total ? row[p] : 0;
+      const int bl = R / H, h = R - bl * H, b = bl / L, l = bl - b * L;
+      src = RowMap<true>(b, h, L, H, D, a.n0).row(a.k, a.k1, l);
+    }
 #pragma unroll
     for (int j = 0; j < Dm::CPT; ++j) {
       const int c = cc + j * Dm::TPR;
-      x[p][j] = row[p] < total && c < Dm::NCH ? *reinterpret_cast<const u32x4*>(a.k + (size_t)row[p] * D + c * 8)
+      x[p][j] = row[p] < total && c < Dm::NCH ? *reinterpret_cast<const u32x4*>(src + c * 8)
                                               : (u32x4){0u, 0u, 0u, 0u};
     }
   }
@@ -44,6 +55,7 @@ __global__ __launch_bounds__(kThreads) void prenorm_kernel(PrenormArgs a) {
     const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
     if (l >= n) continue;
     uint16_t* dst = a.kr + (((size_t)b * H + h) * L + l) * D;
+    const float* gk = a.gains + (l < a.n0 ? 0 : 2 * D) + D;  // (two-stream only)
 #pragma unroll
     for (int j = 0; j < Dm::CPT; ++j) {
       const int c = cc + j * Dm::TPR;
@@ -51,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void prenorm_kernel(PrenormArgs a) {
         float f[8];
         unpack8(x[p][j], f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] *= r;
+        for (int e = 0; e < 8; ++e) f[e] *= S ? r * gk[c * 8 + e] : r;
         *reinterpret_cast<bf16x8*>(dst + c * 8) = to_bf16x8(f);
       }
     }
@@ -70,22 +82,27 @@ hipError_t persistent_grid(const void* kernel, int items, int threads, int* grid
   return hipSuccess;
 }
 
-template <int D>
+template <int D, bool S>
 static hipError_t launch_prenorm_d(const PrenormArgs& a, hipStream_t stream) {
   const int rows = Dims<D>::RPP * kPrenormPasses;
   const int blocks = (int)(((int64_t)a.B * a.L * a.H + rows - 1) / rows);
-  hipLaunchKernelGGL(prenorm_kernel<D>, dim3(blocks), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((prenorm_kernel<D, S>), dim3(blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_prenorm(int D, const PrenormArgs& a, hipStream_t stream) {
+template <bool S>
+static hipError_t launch_prenorm_s(int D, const PrenormArgs& a, hipStream_t stream) {
   switch (D) {
-    case 32: return launch_prenorm_d<32>(a, stream);
-    case 64: return launch_prenorm_d<64>(a, stream);
-    case 72: return launch_prenorm_d<72>(a, stream);
-    case 128: return launch_prenorm_d<128>(a, stream);
+    case 32: return launch_prenorm_d<32, S>(a, stream);
+    case 64: return launch_prenorm_d<64, S>(a, stream);
+    case 72: return launch_prenorm_d<72, S>(a, stream);
+    case 128: return launch_prenorm_d<128, S>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_prenorm(int D, bool streams, const PrenormArgs& a, hipStream_t stream) {
+  return streams ? launch_prenorm_s<true>(D, a, stream) : launch_prenorm_s<false>(D, a, stream);
 }
 
 }  // namespace jattn

@@ -4,6 +4,11 @@ torch supplies device memory and the current HIP stream; every step of the compu
 library's kernels. Layouts: q, k, v, out, dout, dq, dk, dv are bf16 [B, L, H, D] contiguous;
 gains fp32 [2, D] (row 0 for Q, row 1 for K); valid_len int32 [B] (keys per sequence) or None;
 lse fp32 [B, H, L] (natural-log row log-sum-exp).
+
+Two-stream functions (``*_streams``): each per-token tensor is an (image, text) pair of bf16 tensors
+[B, N_img, H, D] and [B, N_txt, H, D] (the joint sequence is image rows then text rows, L = N_img +
+N_txt); gains fp32 [2, 2, D] (gains[s, 0] = Q gain, gains[s, 1] = K gain of stream s, image = 0);
+valid_len and lse as above, over the joint sequence.
 """
 from __future__ import annotations
 
@@ -15,7 +20,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["forward", "backward", "workspace_bytes", "fwd_workspace_bytes", "JointAttention", "joint_attention"]
+__all__ = ["forward", "backward", "workspace_bytes", "fwd_workspace_bytes", "JointAttention", "joint_attention",
+           "forward_streams", "backward_streams", "JointAttentionStreams", "joint_attention_streams"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -133,3 +139,114 @@ class JointAttention(torch.autograd.Function):
 
 def joint_attention(q, k, v, gains, valid_len=None, scale=None, eps=1e-6):
     return JointAttention.apply(q, k, v, gains, valid_len, scale, eps)
+
+
+# ------------------------------------------------------------------------------------------------
+# Two-stream entry points
+
+def _check_pair(name, t, dtype, B, n_img, n_txt, H, D, device):
+    if not isinstance(t, (tuple, list)) or len(t) != 2:
+        raise TypeError(f"{name} must be an (image, text) pair of tensors")
+    _check_tensor(f"{name}[0]", t[0], dtype, (B, n_img, H, D), device)
+    _check_tensor(f"{name}[1]", t[1], dtype, (B, n_txt, H, D), device)
+
+
+def _pair_ptrs(t):
+    return _lib.PtrPair(_ptr(t[0]) if t[0].numel() else None, _ptr(t[1]) if t[1].numel() else None)
+
+
+def _check_streams(q, k, v, gains, valid_len):
+    if not isinstance(q, (tuple, list)) or len(q) != 2 or q[0].dim() != 4 or q[1].dim() != 4:
+        raise ValueError("q must be an (image [B, N_img, H, D], text [B, N_txt, H, D]) pair")
+    B, n_img, H, D = q[0].shape
+    n_txt = q[1].shape[1]
+    dev = q[0].device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_pair(name, t, torch.bfloat16, B, n_img, n_txt, H, D, dev)
+    _check_tensor("gains", gains, torch.float32, (2, 2, D), dev)
+    if valid_len is not None:
+        _check_tensor("valid_len", valid_len, torch.int32, (B,), dev)
+    return B, n_img, n_txt, H, D
+
+
+def forward_streams(q, k, v, gains, valid_len=None, scale: Optional[float] = None, eps: float = 1e-6,
+                    out=None, lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    return_workspace: bool = False):
+    """Two-stream joint attention forward. Returns ((out_img, out_txt), lse fp32 [B, H, L]), plus the
+    forward workspace if return_workspace."""
+    B, n_img, n_txt, H, D = _check_streams(q, k, v, gains, valid_len)
+    L = n_img + n_txt
+    dev = q[0].device
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = (torch.empty_like(q[0]), torch.empty_like(q[1]))
+    if lse is None:
+        lse = torch.empty(B, H, L, dtype=torch.float32, device=dev)
+    _check_pair("out", out, torch.bfloat16, B, n_img, n_txt, H, D, dev)
+    _check_tensor("lse", lse, torch.float32, (B, H, L), dev)
+    lib = _lib.load()
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.jattn_fwd_workspace_bytes(B, L, H, D)), 1), dtype=torch.uint8, device=dev)
+    qp, kp, vp, op = _pair_ptrs(q), _pair_ptrs(k), _pair_ptrs(v), _pair_ptrs(out)
+    st = lib.jattn_fwd_streams(qp.arg, kp.arg, vp.arg, _ptr(gains), _ptr(valid_len), B, n_img, n_txt, H, D,
+                               ctypes.c_float(scale), ctypes.c_float(eps), op.arg, _ptr(lse), _ptr(workspace),
+                               workspace.numel(), None, 0, _stream(q[0]))
+    _lib.check("jattn_fwd_streams", st)
+    out = tuple(out)
+    return (out, lse, workspace) if return_workspace else (out, lse)
+
+
+def backward_streams(q, k, v, gains, out, lse, dout, valid_len=None, scale: Optional[float] = None,
+                     eps: float = 1e-6, workspace=None, fwd_workspace=None):
+    """Two-stream joint attention backward. Returns ((dq_img, dq_txt), (dk_img, dk_txt), (dv_img, dv_txt),
+    dgains fp32 [2, 2, D])."""
+    B, n_img, n_txt, H, D = _check_streams(q, k, v, gains, valid_len)
+    L = n_img + n_txt
+    dev = q[0].device
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check_pair("out", out, torch.bfloat16, B, n_img, n_txt, H, D, dev)
+    _check_pair("dout", dout, torch.bfloat16, B, n_img, n_txt, H, D, dev)
+    _check_tensor("lse", lse, torch.float32, (B, H, L), dev)
+    dq = (torch.empty_like(q[0]), torch.empty_like(q[1]))
+    dk = (torch.empty_like(k[0]), torch.empty_like(k[1]))
+    dv = (torch.empty_like(v[0]), torch.empty_like(v[1]))
+    dgains = torch.empty(2, 2, D, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.jattn_bwd_workspace_bytes(B, L, H, D)), 1), dtype=torch.uint8, device=dev)
+    ptrs = [_pair_ptrs(t) for t in (q, k, v, out, dout, dq, dk, dv)]
+    qp, kp, vp, op, dop, dqp, dkp, dvp = ptrs
+    st = lib.jattn_bwd_streams(qp.arg, kp.arg, vp.arg, _ptr(gains), _ptr(valid_len), op.arg, _ptr(lse), dop.arg,
+                               B, n_img, n_txt, H, D, ctypes.c_float(scale), ctypes.c_float(eps), dqp.arg, dkp.arg,
+                               dvp.arg, _ptr(dgains), _ptr(workspace), workspace.numel(), _ptr(fwd_workspace), None,
+                               0, _stream(q[0]))
+    _lib.check("jattn_bwd_streams", st)
+    return dq, dk, dv, dgains
+
+
+class JointAttentionStreams(torch.autograd.Function):
+    """Autograd wrapper of the two-stream entry points; inputs and outputs are the stream parts."""
+
+    @staticmethod
+    def forward(ctx, q_img, q_txt, k_img, k_txt, v_img, v_txt, gains, valid_len=None, scale=None, eps=1e-6):
+        q, k, v = (q_img, q_txt), (k_img, k_txt), (v_img, v_txt)
+        out, lse, ws = forward_streams(q, k, v, gains, valid_len, scale, eps, return_workspace=True)
+        ctx.save_for_backward(q_img, q_txt, k_img, k_txt, v_img, v_txt, gains, out[0], out[1], lse, valid_len, ws)
+        ctx.scale, ctx.eps = scale, eps
+        return out
+
+    @staticmethod
+    def backward(ctx, d_img, d_txt):
+        q_img, q_txt, k_img, k_txt, v_img, v_txt, gains, o_img, o_txt, lse, valid_len, ws = ctx.saved_tensors
+        prep = lambda t, like: (torch.zeros_like(like) if t is None else t.to(torch.bfloat16).contiguous())
+        dout = (prep(d_img, o_img), prep(d_txt, o_txt))
+        dq, dk, dv, dg = backward_streams((q_img, q_txt), (k_img, k_txt), (v_img, v_txt), gains, (o_img, o_txt),
+                                          lse, dout, valid_len, ctx.scale, ctx.eps, fwd_workspace=ws)
+        return dq[0], dq[1], dk[0], dk[1], dv[0], dv[1], dg, None, None, None
+
+
+def joint_attention_streams(q, k, v, gains, valid_len=None, scale=None, eps=1e-6):
+    """Two-stream joint attention with autograd: q, k, v as (image, text) pairs; returns (out_img, out_txt)."""
+    return JointAttentionStreams.apply(q[0], q[1], k[0], k[1], v[0], v[1], gains, valid_len, scale, eps)

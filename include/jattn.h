@@ -123,6 +123,53 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
                           void* workspace, size_t workspace_bytes, const void* fwd_workspace,
                           const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------------------
+ * Two-stream entry points (zero-copy image + text streams with a QK-norm gain pair per stream).
+ *
+ * The re-diffusion README's DiT-layer box computes Q, K and V separately for each stream ("QKV
+ * each"), concatenates them, runs the joint attention and splits the result back per stream. These
+ * entry points take each per-token tensor as its two stream parts and write the outputs back to
+ * them, so no concatenation or split copy is needed around the attention, and let each stream keep
+ * its own QK-RMSNorm gains. The result is the joint attention above on the concatenated sequence
+ * [image rows; text rows] (L = n_img + n_txt, image first), with every row of stream s normalised
+ * by that stream's gains:
+ *   Qn_i = q_i * r(q_i) * gains[s(i)][0, :]        Kn_j = k_j * r(k_j) * gains[s(j)][1, :]
+ *
+ * Tensor arguments are HOST arrays of two DEVICE pointers, {image part, text part}:
+ *   part 0  bf16 [B, n_img, H, D] (rows 0 .. n_img-1 of each joint sequence),
+ *   part 1  bf16 [B, n_txt, H, D] (rows n_img .. L-1),
+ * each contiguous and 16-byte aligned; the pointer of an empty stream (n = 0) is ignored and may be
+ * NULL. The host arrays are read during the call only.
+ *   gains   fp32 [2, 2, D]: gains[s][0] = Q gain, gains[s][1] = K gain of stream s (0 = image).
+ *   valid_len, lse, softmax_scale, eps and the workspaces: as for the joint entry points, with L =
+ *           n_img + n_txt (valid_len[b] counts keys of the joint sequence, image rows first; lse is
+ *           [B, H, L] in joint row order). Workspace sizes: jattn_fwd_workspace_bytes(B, L, H, D)
+ *           and jattn_bwd_workspace_bytes(B, L, H, D).
+ * Errors as for the joint entry points; n_img < 0, n_txt < 0 or n_img + n_txt < 1, a NULL host
+ * array, or a NULL / misaligned pointer of a non-empty stream -> INVALID_VALUE. Every output part
+ * must be disjoint from every input part and from the other outputs. */
+
+/* Forward pass over the two streams. Stages and events as jattn_fwd_ex (JATTN_FWD_STAGES; pass
+ * NULL, 0 for none). out = {image output, text output}. */
+jattn_status jattn_fwd_streams(const void* const q[2], const void* const k[2], const void* const v[2],
+                               const float* gains, const int32_t* valid_len, int B, int n_img, int n_txt,
+                               int H, int D, float softmax_scale, float eps, void* const out[2], float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
+
+/* Backward pass over the two streams: out and lse from jattn_fwd_streams with the same arguments,
+ * dout the gradient with respect to out (two parts). Writes dq, dk, dv (two parts each) and
+ * dgains fp32 [2, 2, D] (the gradient with respect to gains; overwritten, deterministic).
+ * fwd_workspace: NULL or the workspace of that jattn_fwd_streams call, unchanged since. Stages and
+ * events as jattn_bwd_ex (JATTN_BWD_STAGES; pass NULL, 0 for none). */
+jattn_status jattn_bwd_streams(const void* const q[2], const void* const k[2], const void* const v[2],
+                               const float* gains, const int32_t* valid_len, const void* const out[2],
+                               const float* lse, const void* const dout[2], int B, int n_img, int n_txt,
+                               int H, int D, float softmax_scale, float eps, void* const dq[2],
+                               void* const dk[2], void* const dv[2], float* dgains,
+                               void* workspace, size_t workspace_bytes, const void* fwd_workspace,
+                               const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* jattn_status_string(jattn_status s);
 

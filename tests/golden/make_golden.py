@@ -6,6 +6,9 @@ fp64 oracle only (inputs from the seeded workload generator, seed 0) and stores 
 compare against the stored values.
 
     python tests/golden/make_golden.py [workload ...]
+
+A name "streams:<workload>" stores the two-stream form instead (dgains_streams_<workload>.json): the
+same seed-0 workload split into image and text tensors with a QK-norm gain pair per stream.
 """
 import json
 import os
@@ -18,10 +21,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
-from diffusion_transformer_joint_amd.inputs import make_inputs  # noqa: E402
-from oracle import attention_fwd_bwd  # noqa: E402
+from diffusion_transformer_joint_amd.inputs import make_inputs, make_stream_inputs  # noqa: E402
+from oracle import attention_fwd_bwd, streams_fwd_bwd  # noqa: E402
 
-FULL = ["mmdit512", "dit256", "mmdit768", "ragged"]
+FULL = ["mmdit512", "dit256", "mmdit768", "ragged", "streams:mmdit512"]
 
 
 def f64(t):
@@ -29,8 +32,28 @@ def f64(t):
     return t.to(torch.float64).numpy()
 
 
+def streams(name):
+    t0 = time.time()
+    inp = make_stream_inputs(name, seed=0)
+    vl = None if inp["valid_len"] is None else inp["valid_len"].tolist()
+    pair = lambda key: (f64(inp[key][0]), f64(inp[key][1]))
+    r = streams_fwd_bwd(pair("q"), pair("k"), pair("v"), inp["gains"].double().numpy(), pair("dout"), vl,
+                        inp["scale"], inp["eps"])
+    w = inp["workload"]
+    rec = dict(workload=name, form="two-stream", seed=0, B=w.B, n_img=w.n_img, n_txt=w.n_txt, H=w.H, D=w.D,
+               valid_len=vl, scale=inp["scale"], eps=inp["eps"],
+               source="oracle/jattn_oracle.py streams_fwd_bwd, fp64, all pairs",
+               dgains=np.asarray(r["dgains"]).tolist())
+    with open(os.path.join(HERE, f"dgains_streams_{name}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"streams:{name}: {time.time() - t0:.1f} s", flush=True)
+
+
 def main(names):
     for name in names:
+        if name.startswith("streams:"):
+            streams(name.split(":", 1)[1])
+            continue
         t0 = time.time()
         inp = make_inputs(name, seed=0)
         vl = None if inp["valid_len"] is None else inp["valid_len"].tolist()

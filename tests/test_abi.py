@@ -174,3 +174,96 @@ def test_stage_names_match_header():
     hdr = open(os.path.join(ROOT, "include", "jattn.h")).read()
     assert int(re.search(r"#define JATTN_BWD_STAGES (\d+)", hdr).group(1)) == len(_lib.BWD_STAGES)
     assert int(re.search(r"#define JATTN_FWD_STAGES (\d+)", hdr).group(1)) == len(_lib.FWD_STAGES)
+
+
+# ------------------------------------------------------------------------------------------------
+# Two-stream entry points: tensors are host arrays {image part, text part} of device pointers.
+def pair(i, j):
+    return _lib.PtrPair(fake(i), fake(j))
+
+
+def fwd_streams(lib, **kw):
+    a = dict(q=(0, 1), k=(2, 3), v=(4, 5), gains=fake(6), valid_len=None, B=2, n_img=100, n_txt=37, H=3, D=64,
+             scale=0.125, eps=1e-6, out=(7, 8), lse=fake(9), ws=fake(10), ws_bytes=None, events=None, n_events=0)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = lib.jattn_fwd_workspace_bytes(a["B"], max(a["n_img"] + a["n_txt"], 0), a["H"], a["D"])
+    keep = {}
+    def arg(name):
+        t = a[name]
+        if t is None or isinstance(t, _lib.PtrPair):
+            keep[name] = t
+        else:
+            keep[name] = _lib.PtrPair(*[None if x is None else (fake(x) if isinstance(x, int) and x < 64 else x)
+                                        for x in t])
+        return None if keep[name] is None else keep[name].arg
+    return lib.jattn_fwd_streams(arg("q"), arg("k"), arg("v"), a["gains"], a["valid_len"], a["B"], a["n_img"],
+                                 a["n_txt"], a["H"], a["D"], ctypes.c_float(a["scale"]), ctypes.c_float(a["eps"]),
+                                 arg("out"), a["lse"], a["ws"], a["ws_bytes"], a["events"], a["n_events"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), _lib.INVALID_VALUE),                       # no host array
+    (dict(q=(None, 1)), _lib.INVALID_VALUE),                  # image part missing
+    (dict(v=(4, None)), _lib.INVALID_VALUE),                  # text part missing
+    (dict(out=(7, None)), _lib.INVALID_VALUE),
+    (dict(k=(fake(2) + 8, 3)), _lib.INVALID_VALUE),           # misaligned image part
+    (dict(n_img=-1), _lib.INVALID_VALUE),
+    (dict(n_img=0, n_txt=0), _lib.INVALID_VALUE),
+    (dict(D=48), _lib.NOT_SUPPORTED),
+    (dict(gains=None), _lib.INVALID_VALUE),
+    (dict(eps=math.nan), _lib.INVALID_VALUE),
+    (dict(out=(1, 8)), _lib.INVALID_VALUE),                   # image output aliases the text query part
+    (dict(out=(7, fake(6) - 16)), _lib.INVALID_VALUE),        # text output overlaps the gains
+    (dict(lse=fake(7) + 4096), _lib.INVALID_VALUE),           # lse overlaps the image output
+    (dict(ws=None), _lib.WORKSPACE),
+    (dict(ws_bytes=1024), _lib.WORKSPACE),
+    (dict(ws=fake(0)), _lib.INVALID_VALUE),                   # workspace aliases the image queries
+    (dict(n_events=1), _lib.INVALID_VALUE),                   # events count without an array
+    # the pointers of an empty stream are ignored: these reach the workspace check
+    (dict(n_txt=0, q=(0, None), k=(2, None), v=(4, None), out=(7, None), ws_bytes=1024), _lib.WORKSPACE),
+    (dict(n_img=0, q=(None, 1), k=(None, 3), v=(None, 5), out=(None, 8), ws_bytes=1024), _lib.WORKSPACE),
+])
+def test_fwd_streams_rejects(lib, kw, expect):
+    assert fwd_streams(lib, **kw) == expect
+
+
+def bwd_streams(lib, **kw):
+    a = dict(q=(0, 1), k=(2, 3), v=(4, 5), gains=fake(6), valid_len=None, out=(7, 8), lse=fake(9), dout=(10, 11),
+             B=2, n_img=100, n_txt=37, H=3, D=64, scale=0.125, eps=1e-6, dq=(12, 13), dk=(14, 15), dv=(16, 17),
+             dgains=fake(18), ws=fake(19), ws_bytes=None, fws=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = lib.jattn_bwd_workspace_bytes(a["B"], a["n_img"] + a["n_txt"], a["H"], a["D"])
+    keep = []
+    def arg(name):
+        t = a[name]
+        if t is None:
+            return None
+        p = _lib.PtrPair(*[None if x is None else (fake(x) if x < 64 else x) for x in t])
+        keep.append(p)
+        return p.arg
+    return lib.jattn_bwd_streams(arg("q"), arg("k"), arg("v"), a["gains"], a["valid_len"], arg("out"), a["lse"],
+                                 arg("dout"), a["B"], a["n_img"], a["n_txt"], a["H"], a["D"],
+                                 ctypes.c_float(a["scale"]), ctypes.c_float(a["eps"]), arg("dq"), arg("dk"),
+                                 arg("dv"), a["dgains"], a["ws"], a["ws_bytes"], a["fws"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dout=None), _lib.INVALID_VALUE),
+    (dict(dq=(12, None)), _lib.INVALID_VALUE),
+    (dict(dgains=None), _lib.INVALID_VALUE),
+    (dict(n_txt=-5), _lib.INVALID_VALUE),
+    (dict(dk=(14, fake(15) + 4)), _lib.INVALID_VALUE),       # misaligned text part
+    (dict(dq=(12, 10)), _lib.INVALID_VALUE),                  # text dq aliases the image dout
+    (dict(dv=(fake(13) + 4096, 17)), _lib.INVALID_VALUE),     # image dv overlaps the text dq
+    (dict(dgains=fake(6)), _lib.INVALID_VALUE),               # dgains aliases the gains
+    (dict(ws=None), _lib.WORKSPACE),
+    (dict(ws=fake(19) + 64), _lib.INVALID_VALUE),
+    (dict(fws=fake(19)), _lib.INVALID_VALUE),                 # workspace aliases the forward workspace
+    (dict(fws=fake(20) + 64), _lib.INVALID_VALUE),
+    (dict(n_txt=0, q=(0, None), k=(2, None), v=(4, None), out=(7, None), dout=(10, None), dq=(12, None),
+          dk=(14, None), dv=(16, None), ws_bytes=1024), _lib.WORKSPACE),
+])
+def test_bwd_streams_rejects(lib, kw, expect):
+    assert bwd_streams(lib, **kw) == expect
