@@ -1,11 +1,16 @@
 """Benchmark: joint-attention forward + backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mmdit512] [--no-cpu-baseline]
-                    [--calibrate-copy]
+                    [--calibrate-copy] [--variant joint|streams]
 
 A step is one forward (jattn_fwd) plus one backward (jattn_bwd) over the whole batch of the workload,
 inputs resident in HBM. Prints one JSON line. The throughput is algorithmic TFLOP/s:
 4*B*H*L*L*D for the forward (valid keys only for ragged workloads) and 2.5x that for the backward.
+
+--variant streams times the two-stream entry points instead (image and text tensors of the same
+workload, a QK-norm gain pair per stream: jattn_fwd_streams + jattn_bwd_streams), and beside them the
+step they replace: concatenating the stream tensors, the joint forward and backward, and splitting
+the outputs and gradients back (`concat_split`).
 """
 import argparse
 import ctypes
@@ -31,6 +36,7 @@ def parse():
     ap.add_argument("--workload", default="mmdit512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--variant", choices=("joint", "streams"), default="joint")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 512 MiB device-to-device three times: under rocprofv3 --pmc its "
                          "FETCH_SIZE / WRITE_SIZE give the counters' scale for a known byte count")
@@ -53,10 +59,12 @@ def kernel_sources_digest():
     return h.hexdigest()
 
 
-def stored_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary of this workload, or None
-    when there is none or the library sources changed since the counters were read."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+def stored_traffic(workload, kernel, variant="joint"):
+    """HBM bytes per launch of `kernel` from the committed counter summary of this workload (and entry
+    point variant), or None when there is none or the library sources changed since the counters were
+    read."""
+    suffix = "" if variant == "joint" else f"_{variant}"
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}{suffix}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -80,19 +88,16 @@ def main():
     import torch
 
     from diffusion_transformer_joint_amd import _lib
-    from diffusion_transformer_joint_amd.inputs import WORKLOADS, flops, make_inputs
+    from diffusion_transformer_joint_amd.inputs import WORKLOADS, flops, make_inputs, make_stream_inputs
 
     w = WORKLOADS[args.workload]
     B, L, H, D = w.B, w.L, w.H, w.D
-    inp = make_inputs(args.workload, seed=0)
+    streams = args.variant == "streams"
+    inp = make_stream_inputs(args.workload, seed=0) if streams else make_inputs(args.workload, seed=0)
     dev = torch.device("cuda:0")
-    q, k, v, dout = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
     gains = inp["gains"].to(dev)
     vl = None if inp["valid_len"] is None else inp["valid_len"].to(dev)
-    out = torch.empty_like(q)
     lse = torch.empty(B, H, L, dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dg = torch.empty(2, D, dtype=torch.float32, device=dev)
     lib = _lib.load()
     ws_bytes = int(lib.jattn_bwd_workspace_bytes(B, L, H, D))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -102,23 +107,49 @@ def main():
     sp = stream.cuda_stream
     scale, eps = ctypes.c_float(inp["scale"]), ctypes.c_float(inp["eps"])
     vlp = None if vl is None else vl.data_ptr()
-    fwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), vlp, B, L, H, D, scale, eps,
-                out.data_ptr(), lse.data_ptr(), fws.data_ptr(), fws_bytes, sp)
-    bwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), vlp, out.data_ptr(), lse.data_ptr(),
-                dout.data_ptr(), B, L, H, D, scale, eps, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                dg.data_ptr(), ws.data_ptr(), ws_bytes, fws.data_ptr(), sp)
+    if not streams:
+        q, k, v, dout = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+        out = torch.empty_like(q)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dg = torch.empty(2, D, dtype=torch.float32, device=dev)
+        fwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), vlp, B, L, H, D, scale, eps,
+                    out.data_ptr(), lse.data_ptr(), fws.data_ptr(), fws_bytes, sp)
+        bwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), vlp, out.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), B, L, H, D, scale, eps, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    dg.data_ptr(), ws.data_ptr(), ws_bytes, fws.data_ptr(), sp)
 
-    def fwd(events=None):
-        if events is None:
-            _lib.check("jattn_fwd", lib.jattn_fwd(*fwd_args))
-        else:
-            _lib.check("jattn_fwd_ex", lib.jattn_fwd_ex(*fwd_args[:-1], events, len(_lib.FWD_STAGES), sp))
+        def fwd(events=None):
+            if events is None:
+                _lib.check("jattn_fwd", lib.jattn_fwd(*fwd_args))
+            else:
+                _lib.check("jattn_fwd_ex", lib.jattn_fwd_ex(*fwd_args[:-1], events, len(_lib.FWD_STAGES), sp))
 
-    def bwd(events=None, n=len(_lib.BWD_STAGES)):
-        if events is None:
-            _lib.check("jattn_bwd", lib.jattn_bwd(*bwd_args))
-        else:
-            _lib.check("jattn_bwd_ex", lib.jattn_bwd_ex(*bwd_args[:-1], events, n, sp))
+        def bwd(events=None, n=len(_lib.BWD_STAGES)):
+            if events is None:
+                _lib.check("jattn_bwd", lib.jattn_bwd(*bwd_args))
+            else:
+                _lib.check("jattn_bwd_ex", lib.jattn_bwd_ex(*bwd_args[:-1], events, n, sp))
+    else:
+        part = lambda t: tuple(x.to(dev) for x in t)
+        q, k, v, dout = (part(inp[n]) for n in ("q", "k", "v", "dout"))
+        like = lambda t: (torch.empty_like(t[0]), torch.empty_like(t[1]))
+        out, dq, dk, dv = like(q), like(q), like(k), like(v)
+        dg = torch.empty(2, 2, D, dtype=torch.float32, device=dev)
+        pp = {name: _lib.PtrPair(t[0].data_ptr(), t[1].data_ptr())
+              for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk),
+                              ("dv", dv))}
+        fwd_args = (pp["q"].arg, pp["k"].arg, pp["v"].arg, gains.data_ptr(), vlp, B, w.n_img, w.n_txt, H, D, scale,
+                    eps, pp["out"].arg, lse.data_ptr(), fws.data_ptr(), fws_bytes)
+        bwd_args = (pp["q"].arg, pp["k"].arg, pp["v"].arg, gains.data_ptr(), vlp, pp["out"].arg, lse.data_ptr(),
+                    pp["dout"].arg, B, w.n_img, w.n_txt, H, D, scale, eps, pp["dq"].arg, pp["dk"].arg, pp["dv"].arg,
+                    dg.data_ptr(), ws.data_ptr(), ws_bytes, fws.data_ptr())
+
+        def fwd(events=None):
+            _lib.check("jattn_fwd_streams", lib.jattn_fwd_streams(*fwd_args, events, 0 if events is None else
+                                                                  len(_lib.FWD_STAGES), sp))
+
+        def bwd(events=None, n=len(_lib.BWD_STAGES)):
+            _lib.check("jattn_bwd_streams", lib.jattn_bwd_streams(*bwd_args, events, 0 if events is None else n, sp))
 
     def new_event():
         e = torch.cuda.Event(enable_timing=True)
@@ -143,11 +174,14 @@ def main():
         return arr, ctypes.cast(arr, ctypes.c_void_p)
 
     K = args.steps
-    stages = [f"{n}<{D}> (fwd)" if n == "prenorm_kernel" else f"{n}<{D}>" for n in _lib.FWD_STAGES]
-    stages += [f"{n}<{D}> (bwd)" if n == "prenorm_kernel" else (n if n == "dg_reduce_kernel" else f"{n}<{D}>")
-               for n in _lib.BWD_STAGES]
+    # stage labels: the kernels' template instantiations, as a profiler names them
+    sflag = "true" if streams else "false"
+    targs = f"{D}, {sflag}"
+    stages = [f"{n}<{targs}> (fwd)" if n == "prenorm_kernel" else f"{n}<{targs}>" for n in _lib.FWD_STAGES]
+    stages += [f"{n}<{targs}> (bwd)" if n == "prenorm_kernel" else
+               (f"{n}<{sflag}>" if n == "dg_reduce_kernel" else f"{n}<{targs}>") for n in _lib.BWD_STAGES]
     nf = len(_lib.FWD_STAGES)
-    dq_key, dkdv_key = f"bwd_dq_kernel<{D}>", f"bwd_dkdv_kernel<{D}>"
+    dq_key, dkdv_key = f"bwd_dq_kernel<{targs}>", f"bwd_dkdv_kernel<{targs}>"
 
     # Timed region: K steps of forward + backward. Recording an event costs a few microseconds of GPU
     # time, so only the events after the backward's first three kernels (key normalisation, dq, dk/dv;
@@ -185,6 +219,11 @@ def main():
     ms_fwd = sum(ev0[i].elapsed_time(evb[i][nf - 1]) for i in range(KB)) / KB
     ms_bwd = ms_step - ms_fwd
 
+    concat_split = None
+    if streams:
+        concat_split = time_concat_split(lib, _lib, torch, q, k, v, dout, gains, vl, B, L, H, D, inp, stream, K,
+                                         args.warmup)
+
     vlist = None if inp["valid_len"] is None else inp["valid_len"].tolist()
     fl = flops(B, L, H, D, vlist)
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
@@ -193,13 +232,13 @@ def main():
     # Roofline of the dominant kernel: MFMA FLOPs one launch executes per (query, valid key) pair --
     # forward 4D (S, PV); dq kernel 6D (S, dP recomputed, dQ); dk/dv kernel 8D (S, dP, dV, dK).
     pairs = fl["fwd"] / (4.0 * H * D)
-    per_pair = {f"fwd_kernel<{D}>": 4 * D, f"bwd_dq_kernel<{D}>": 6 * D, f"bwd_dkdv_kernel<{D}>": 8 * D}
+    per_pair = {f"fwd_kernel<{targs}>": 4 * D, dq_key: 6 * D, dkdv_key: 8 * D}
     dom = max(per_pair, key=lambda k: kern_ms[k])
     dom_ms = live_ms.get(dom, kern_ms[dom])  # the live timed-region duration where it was recorded
     achieved = per_pair[dom] * H * pairs / (dom_ms * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": stored_traffic(args.workload, dom),
+                "traffic": stored_traffic(args.workload, dom, args.variant),
                 "flop_per_launch": per_pair[dom] * H * pairs, "avg_launch_ms": round(dom_ms, 5),
                 "avg_launch_ms_source": "timed region" if dom in live_ms else "breakdown pass"}
 
@@ -220,8 +259,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "L": L, "H": H, "D": D, "n_img": w.n_img,
-                   "n_txt": w.n_txt, "valid_len": vlist, "global_batch": B, "seq_len": L,
+        "config": {"workload": args.workload, "variant": args.variant, "B": B, "L": L, "H": H, "D": D,
+                   "n_img": w.n_img, "n_txt": w.n_txt, "valid_len": vlist, "global_batch": B, "seq_len": L,
                    "parallelism": "single-gpu"},
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(ms_fwd, 5),
@@ -234,7 +273,57 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if concat_split is not None:
+        res["concat_split"] = concat_split
+        res["concat_split"]["speedup"] = round(concat_split["ms_per_step"] / ms_step, 4)
     print(json.dumps(res), flush=True)
+
+
+def time_concat_split(lib, _lib, torch, q, k, v, dout, gains, vl, B, L, H, D, inp, stream, K, warmup):
+    """The step the two-stream entry points replace, timed the same way: concatenate the image and text
+    parts of q, k, v (and dout), run the joint forward and backward, split out, dq, dk and dv back
+    into per-stream tensors. The joint kernels take one gain pair, so the image stream's gains stand
+    in for both (the kernel work is the same)."""
+    n_img = q[0].shape[1]
+    g0 = gains[0].contiguous()
+    vlp = None if vl is None else vl.data_ptr()
+    lse = torch.empty(B, H, L, dtype=torch.float32, device=q[0].device)
+    fws_bytes = int(lib.jattn_fwd_workspace_bytes(B, L, H, D))
+    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=q[0].device)
+    ws_bytes = int(lib.jattn_bwd_workspace_bytes(B, L, H, D))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q[0].device)
+    scale, eps = ctypes.c_float(inp["scale"]), ctypes.c_float(inp["eps"])
+    sp = stream.cuda_stream
+
+    def step():
+        qj, kj, vj = (torch.cat(t, dim=1) for t in (q, k, v))
+        out = torch.empty_like(qj)
+        _lib.check("jattn_fwd", lib.jattn_fwd(qj.data_ptr(), kj.data_ptr(), vj.data_ptr(), g0.data_ptr(), vlp, B, L,
+                                              H, D, scale, eps, out.data_ptr(), lse.data_ptr(), fws.data_ptr(),
+                                              fws_bytes, sp))
+        outs = (out[:, :n_img].contiguous(), out[:, n_img:].contiguous())
+        doj = torch.cat(dout, dim=1)
+        dq, dk, dv = torch.empty_like(qj), torch.empty_like(kj), torch.empty_like(vj)
+        dg = torch.empty(2, D, dtype=torch.float32, device=qj.device)
+        _lib.check("jattn_bwd", lib.jattn_bwd(qj.data_ptr(), kj.data_ptr(), vj.data_ptr(), g0.data_ptr(), vlp,
+                                              out.data_ptr(), lse.data_ptr(), doj.data_ptr(), B, L, H, D, scale, eps,
+                                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(),
+                                              ws.data_ptr(), ws_bytes, fws.data_ptr(), sp))
+        return outs, [(t[:, :n_img].contiguous(), t[:, n_img:].contiguous()) for t in (dq, dk, dv)]
+
+    for _ in range(min(warmup, 20)):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(K):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K
+    return {"ms_per_step": round(ms, 5),
+            "what": "torch.cat of the q, k, v and dout parts + jattn_fwd + jattn_bwd + .contiguous() splits of "
+                    "out, dq, dk, dv (same workload and stream)"}
 
 
 def cpu_baseline(inp, seconds):
@@ -242,7 +331,7 @@ def cpu_baseline(inp, seconds):
     import numpy as np
     import torch
 
-    from oracle import attention_fwd_bwd
+    from oracle import attention_fwd_bwd, streams_fwd_bwd
 
     try:
         import threadpoolctl
@@ -251,9 +340,10 @@ def cpu_baseline(inp, seconds):
         threads = 1
     w = inp["workload"]
     B, L, H, D = w.B, w.L, w.H, w.D
-    f = lambda t: t.to(torch.float64).numpy()
+    f = lambda t: tuple(f(x) for x in t) if isinstance(t, tuple) else t.to(torch.float64).numpy()
     q, k, v, do = (f(inp[n]) for n in ("q", "k", "v", "dout"))
     g = inp["gains"].double().numpy()
+    run = streams_fwd_bwd if isinstance(q, tuple) else attention_fwd_bwd
     vl = None if inp["valid_len"] is None else inp["valid_len"].tolist()
     pairs = [(b, h) for b in range(B) for h in range(H)]
     done, flop = 0, 0.0
@@ -261,14 +351,14 @@ def cpu_baseline(inp, seconds):
     chunk = 4
     while done < len(pairs) and time.perf_counter() - t0 < seconds:
         sel = pairs[done:done + chunk]
-        attention_fwd_bwd(q, k, v, g, do, vl, inp["scale"], inp["eps"], pairs=sel)
+        run(q, k, v, g, do, vl, inp["scale"], inp["eps"], pairs=sel)
         for b, _ in sel:
             n = L if vl is None else max(0, min(L, vl[b]))
             flop += 3.5 * 4.0 * L * n * D
         done += len(sel)
     dt = time.perf_counter() - t0
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 numpy oracle fwd+bwd on the first {done} of {len(pairs)} (batch, head) pairs of "
+            "sample": f"fp64 numpy oracle ({run.__name__}) fwd+bwd on the first {done} of {len(pairs)} (batch, head) pairs of "
                       f"the same seed-0 inputs, {dt:.1f} s wall; BLAS threads = cores, elementwise steps "
                       f"single-threaded",
             "seconds": round(dt, 2), "pairs": done}
