@@ -11,6 +11,11 @@ inputs resident in HBM. Prints one JSON line. The throughput is algorithmic TFLO
 workload, a QK-norm gain pair per stream: jattn_fwd_streams + jattn_bwd_streams), and beside them the
 step they replace: concatenating the stream tensors, the joint forward and backward, and splitting
 the outputs and gradients back (`concat_split`).
+
+--variant varlen (with --workload varlen_multires or varlen_ragged) times the packed variable-length
+entry points (jattn_fwd_varlen + jattn_bwd_varlen; FLOPs over each sequence's own query-key pairs),
+and beside them the same sequences padded to the longest one through the joint entry points with a
+key mask (`padded`).
 """
 import argparse
 import ctypes
@@ -36,7 +41,7 @@ def parse():
     ap.add_argument("--workload", default="mmdit512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--variant", choices=("joint", "streams"), default="joint")
+    ap.add_argument("--variant", choices=("joint", "streams", "varlen"), default="joint")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 512 MiB device-to-device three times: under rocprofv3 --pmc its "
                          "FETCH_SIZE / WRITE_SIZE give the counters' scale for a known byte count")
@@ -63,7 +68,7 @@ def stored_traffic(workload, kernel, variant="joint"):
     """HBM bytes per launch of `kernel` from the committed counter summary of this workload (and entry
     point variant), or None when there is none or the library sources changed since the counters were
     read."""
-    suffix = "" if variant == "joint" else f"_{variant}"
+    suffix = "" if variant in ("joint", "varlen") else f"_{variant}"  # (varlen workloads are named so)
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}{suffix}.md")
     if not os.path.exists(path):
         return None
@@ -88,26 +93,57 @@ def main():
     import torch
 
     from diffusion_transformer_joint_amd import _lib
-    from diffusion_transformer_joint_amd.inputs import WORKLOADS, flops, make_inputs, make_stream_inputs
+    from diffusion_transformer_joint_amd.inputs import (VARLEN_WORKLOADS, WORKLOADS, flops, make_inputs,
+                                                        make_stream_inputs, make_varlen_inputs, varlen_flops)
 
-    w = WORKLOADS[args.workload]
-    B, L, H, D = w.B, w.L, w.H, w.D
-    streams = args.variant == "streams"
-    inp = make_stream_inputs(args.workload, seed=0) if streams else make_inputs(args.workload, seed=0)
+    streams, varlen = args.variant == "streams", args.variant == "varlen"
+    if varlen and args.workload not in VARLEN_WORKLOADS:
+        args.workload = "varlen_multires"
+    if varlen:
+        w = VARLEN_WORKLOADS[args.workload]
+        inp = make_varlen_inputs(args.workload, seed=0)
+        B, H, D, L = w.B, w.H, w.D, inp["max_seqlen"]
+        total = sum(inp["lengths"])
+    else:
+        w = WORKLOADS[args.workload]
+        B, L, H, D = w.B, w.L, w.H, w.D
+        inp = make_stream_inputs(args.workload, seed=0) if streams else make_inputs(args.workload, seed=0)
     dev = torch.device("cuda:0")
     gains = inp["gains"].to(dev)
-    vl = None if inp["valid_len"] is None else inp["valid_len"].to(dev)
-    lse = torch.empty(B, H, L, dtype=torch.float32, device=dev)
+    vl = None if inp.get("valid_len") is None else inp["valid_len"].to(dev)
+    lse = torch.empty(total * H if varlen else B * H * L, dtype=torch.float32, device=dev)
     lib = _lib.load()
-    ws_bytes = int(lib.jattn_bwd_workspace_bytes(B, L, H, D))
+    if varlen:
+        ws_bytes = int(lib.jattn_varlen_bwd_workspace_bytes(B, L, total, H, D))
+        fws_bytes = int(lib.jattn_varlen_fwd_workspace_bytes(B, L, total, H, D))
+    else:
+        ws_bytes = int(lib.jattn_bwd_workspace_bytes(B, L, H, D))
+        fws_bytes = int(lib.jattn_fwd_workspace_bytes(B, L, H, D))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    fws_bytes = int(lib.jattn_fwd_workspace_bytes(B, L, H, D))
     fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     scale, eps = ctypes.c_float(inp["scale"]), ctypes.c_float(inp["eps"])
     vlp = None if vl is None else vl.data_ptr()
-    if not streams:
+    if varlen:
+        q, k, v, dout = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+        cu = inp["cu_seqlens"].to(dev)
+        out = torch.empty_like(q)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dg = torch.empty(2, D, dtype=torch.float32, device=dev)
+        fwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), cu.data_ptr(), B, L, total, H, D,
+                    scale, eps, out.data_ptr(), lse.data_ptr(), fws.data_ptr(), fws_bytes)
+        bwd_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), cu.data_ptr(), out.data_ptr(),
+                    lse.data_ptr(), dout.data_ptr(), B, L, total, H, D, scale, eps, dq.data_ptr(), dk.data_ptr(),
+                    dv.data_ptr(), dg.data_ptr(), ws.data_ptr(), ws_bytes, fws.data_ptr())
+
+        def fwd(events=None):
+            _lib.check("jattn_fwd_varlen", lib.jattn_fwd_varlen(*fwd_args, events, 0 if events is None else
+                                                                len(_lib.FWD_STAGES), sp))
+
+        def bwd(events=None, n=len(_lib.BWD_STAGES)):
+            _lib.check("jattn_bwd_varlen", lib.jattn_bwd_varlen(*bwd_args, events, 0 if events is None else n, sp))
+    elif not streams:
         q, k, v, dout = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
         out = torch.empty_like(q)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -176,7 +212,7 @@ def main():
     K = args.steps
     # stage labels: the kernels' template instantiations, as a profiler names them
     sflag = "true" if streams else "false"
-    targs = f"{D}, {sflag}"
+    targs = f"{D}, {sflag}, {'true' if varlen else 'false'}"
     stages = [f"{n}<{targs}> (fwd)" if n == "prenorm_kernel" else f"{n}<{targs}>" for n in _lib.FWD_STAGES]
     stages += [f"{n}<{targs}> (bwd)" if n == "prenorm_kernel" else
                (f"{n}<{sflag}>" if n == "dg_reduce_kernel" else f"{n}<{targs}>") for n in _lib.BWD_STAGES]
@@ -219,13 +255,15 @@ def main():
     ms_fwd = sum(ev0[i].elapsed_time(evb[i][nf - 1]) for i in range(KB)) / KB
     ms_bwd = ms_step - ms_fwd
 
-    concat_split = None
+    concat_split = padded = None
     if streams:
         concat_split = time_concat_split(lib, _lib, torch, q, k, v, dout, gains, vl, B, L, H, D, inp, stream, K,
                                          args.warmup)
+    if varlen:
+        padded = time_padded(lib, _lib, torch, inp, gains, B, L, H, D, stream, K, args.warmup)
 
-    vlist = None if inp["valid_len"] is None else inp["valid_len"].tolist()
-    fl = flops(B, L, H, D, vlist)
+    vlist = None if inp.get("valid_len") is None else inp["valid_len"].tolist()
+    fl = varlen_flops(inp["lengths"], H, D) if varlen else flops(B, L, H, D, vlist)
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
     fwd_tflops = fl["fwd"] / (ms_fwd * 1e-3) / 1e12
     bwd_tflops = fl["bwd"] / (ms_bwd * 1e-3) / 1e12
@@ -259,9 +297,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "variant": args.variant, "B": B, "L": L, "H": H, "D": D,
-                   "n_img": w.n_img, "n_txt": w.n_txt, "valid_len": vlist, "global_batch": B, "seq_len": L,
-                   "parallelism": "single-gpu"},
+        "config": ({"workload": args.workload, "variant": args.variant, "B": B, "H": H, "D": D,
+                    "lengths": inp["lengths"], "total": total, "max_seqlen": L, "global_batch": B,
+                    "parallelism": "single-gpu"} if varlen else
+                   {"workload": args.workload, "variant": args.variant, "B": B, "L": L, "H": H, "D": D,
+                    "n_img": w.n_img, "n_txt": w.n_txt, "valid_len": vlist, "global_batch": B, "seq_len": L,
+                    "parallelism": "single-gpu"}),
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(ms_fwd, 5),
         "bwd_ms": round(ms_bwd, 5),
@@ -276,6 +317,9 @@ def main():
     if concat_split is not None:
         res["concat_split"] = concat_split
         res["concat_split"]["speedup"] = round(concat_split["ms_per_step"] / ms_step, 4)
+    if padded is not None:
+        res["padded"] = padded
+        res["padded"]["speedup"] = round(padded["ms_per_step"] / ms_step, 4)
     print(json.dumps(res), flush=True)
 
 
@@ -326,12 +370,53 @@ def time_concat_split(lib, _lib, torch, q, k, v, dout, gains, vl, B, L, H, D, in
                     "out, dq, dk, dv (same workload and stream)"}
 
 
+def time_padded(lib, _lib, torch, inp, gains, B, L, H, D, stream, K, warmup):
+    """The same sequences padded to the longest one (L rows each, zeros after each sequence's end),
+    run through the joint entry points with valid_len = the lengths: what a packed batch replaces."""
+    dev = gains.device
+    lengths, cu = inp["lengths"], inp["cu_seqlens"].tolist()
+    pad = lambda t: torch.stack([torch.cat([t[cu[b]:cu[b + 1]], torch.zeros(L - n, H, D, dtype=t.dtype)])
+                                 for b, n in enumerate(lengths)]).to(dev)
+    q, k, v, dout = (pad(inp[n]) for n in ("q", "k", "v", "dout"))
+    vl = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    out, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty(B, H, L, dtype=torch.float32, device=dev)
+    dg = torch.empty(2, D, dtype=torch.float32, device=dev)
+    fws_bytes, ws_bytes = int(lib.jattn_fwd_workspace_bytes(B, L, H, D)), int(lib.jattn_bwd_workspace_bytes(B, L, H, D))
+    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    scale, eps = ctypes.c_float(inp["scale"]), ctypes.c_float(inp["eps"])
+    sp = stream.cuda_stream
+
+    def step():
+        _lib.check("jattn_fwd", lib.jattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), vl.data_ptr(),
+                                              B, L, H, D, scale, eps, out.data_ptr(), lse.data_ptr(), fws.data_ptr(),
+                                              fws_bytes, sp))
+        _lib.check("jattn_bwd", lib.jattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), gains.data_ptr(), vl.data_ptr(),
+                                              out.data_ptr(), lse.data_ptr(), dout.data_ptr(), B, L, H, D, scale, eps,
+                                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(), ws.data_ptr(),
+                                              ws_bytes, fws.data_ptr(), sp))
+
+    for _ in range(min(warmup, 20)):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(K):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return {"ms_per_step": round(a.elapsed_time(b) / K, 5),
+            "what": f"the same sequences padded to L = {L} (B = {B}), jattn_fwd + jattn_bwd with valid_len = the "
+                    "lengths (padded query rows are computed, padded keys masked)"}
+
+
 def cpu_baseline(inp, seconds):
     """The fp64 oracle (as is) on the first (batch, head) pairs of the same inputs, time-bounded."""
     import numpy as np
     import torch
 
-    from oracle import attention_fwd_bwd, streams_fwd_bwd
+    from oracle import attention_fwd_bwd, streams_fwd_bwd, varlen_fwd_bwd
 
     try:
         import threadpoolctl
@@ -339,6 +424,8 @@ def cpu_baseline(inp, seconds):
     except Exception:
         threads = 1
     w = inp["workload"]
+    if "cu_seqlens" in inp:
+        return cpu_baseline_varlen(inp, seconds, threads, varlen_fwd_bwd)
     B, L, H, D = w.B, w.L, w.H, w.D
     f = lambda t: tuple(f(x) for x in t) if isinstance(t, tuple) else t.to(torch.float64).numpy()
     q, k, v, do = (f(inp[n]) for n in ("q", "k", "v", "dout"))
@@ -366,3 +453,25 @@ def cpu_baseline(inp, seconds):
 
 if __name__ == "__main__":
     main()
+
+
+def cpu_baseline_varlen(inp, seconds, threads, varlen_fwd_bwd):
+    """The fp64 variable-length oracle on the first sequences of the same packed inputs, time-bounded."""
+    import torch
+    w = inp["workload"]
+    f = lambda t: t.to(torch.float64).numpy()
+    q, k, v, do = (f(inp[n]) for n in ("q", "k", "v", "dout"))
+    g = inp["gains"].double().numpy()
+    cu = inp["cu_seqlens"].tolist()
+    done, flop = 0, 0.0
+    t0 = time.perf_counter()
+    while done < w.B and time.perf_counter() - t0 < seconds:
+        varlen_fwd_bwd(q, k, v, g, do, cu, inp["scale"], inp["eps"], seqs=[done])
+        n = cu[done + 1] - cu[done]
+        flop += 3.5 * 4.0 * w.H * n * n * w.D
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle (varlen_fwd_bwd) fwd+bwd on the first {done} of {w.B} sequences of the "
+                      f"same seed-0 packed inputs, {dt:.1f} s wall; BLAS threads = cores",
+            "seconds": round(dt, 2), "sequences": done}

@@ -16,8 +16,10 @@ STATUS = {0: "JATTN_SUCCESS", 1: "JATTN_ERROR_INVALID_VALUE", 2: "JATTN_ERROR_NO
 SUCCESS, INVALID_VALUE, NOT_SUPPORTED, WORKSPACE, HIP = range(5)
 
 EXPORTED = ("jattn_fwd", "jattn_fwd_ex", "jattn_fwd_workspace_bytes", "jattn_bwd", "jattn_bwd_ex", "jattn_bwd_workspace_bytes",
-            "jattn_fwd_streams", "jattn_bwd_streams", "jattn_status_string", "jattn_abi_version")
-ABI_VERSION = 4
+            "jattn_fwd_streams", "jattn_bwd_streams", "jattn_varlen_fwd_workspace_bytes",
+            "jattn_varlen_bwd_workspace_bytes", "jattn_fwd_varlen", "jattn_bwd_varlen", "jattn_status_string",
+            "jattn_abi_version")
+ABI_VERSION = 5
 FWD_STAGES = ("prenorm_kernel", "fwd_kernel")
 BWD_STAGES = ("prenorm_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "dg_reduce_kernel")
 
@@ -62,6 +64,15 @@ def load() -> ctypes.CDLL:
         lib.jattn_bwd_streams.restype = I
         lib.jattn_bwd_streams.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, F, P, P, P, P, P,
                                           ctypes.c_size_t, P, P, I, P]
+        lib.jattn_varlen_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.jattn_varlen_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
+        lib.jattn_varlen_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.jattn_varlen_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+        lib.jattn_fwd_varlen.restype = I
+        lib.jattn_fwd_varlen.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, P, P, P, ctypes.c_size_t, P, I, P]
+        lib.jattn_bwd_varlen.restype = I
+        lib.jattn_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, F, P, P, P, P, P,
+                                         ctypes.c_size_t, P, P, I, P]
         lib.jattn_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.jattn_bwd_workspace_bytes.argtypes = [I, I, I, I]
         lib.jattn_status_string.restype = ctypes.c_char_p

@@ -13,7 +13,7 @@ namespace {
 
 using jattn::kBwdRowsPerBlock;
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 bool supported_head_dim(int D) { return D == 32 || D == 64 || D == 72 || D == 128; }
 
@@ -59,13 +59,18 @@ struct WorkspaceLayout {
   size_t kr, qs, nlse2, ndelta, part, total;
 };
 
-// Normalised key rows and pre-scaled normalised query rows (bf16, [B, H, L, D]), the two row
-// statistics (fp32, [B, H, lp] with lp = L rounded up to whole row blocks) and the per-workgroup
-// partial sums of the gain gradients (fp32, [kPartSets, D, items]), each 256-byte aligned.
-WorkspaceLayout workspace_layout(int B, int L, int H, int D) {
+// Normalised key rows and pre-scaled normalised query rows (bf16, one [L, D] block per (sequence,
+// head): [B, H, L, D] for fixed-length batches, total * H rows for packed ones), the two row
+// statistics (fp32, [B, H, lp] with lp = L rounded up to whole row blocks; packed batches
+// (total + 128 B) * H rows, see SeqGeom) and the per-workgroup partial sums of the gain gradients
+// (fp32, [kPartSets, D, items]), each 256-byte aligned. L is the longest sequence; total < 0 means
+// a fixed-length batch (total = B L).
+WorkspaceLayout workspace_layout(int B, int L, int H, int D, int64_t total = -1) {
   const size_t nblk = (L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock;
   const size_t items = (size_t)B * H * nblk, lp = nblk * kBwdRowsPerBlock;
-  const size_t rows = round_up((size_t)B * H * L * D * 2, 256), stats = round_up((size_t)B * H * lp * 4, 256),
+  const size_t nrows = total < 0 ? (size_t)B * L : (size_t)total;
+  const size_t rows = round_up(nrows * H * D * 2, 256),
+               stats = round_up((total < 0 ? (size_t)B * H * lp : (nrows + 128 * (size_t)B) * H) * 4, 256),
                parts = round_up(jattn::kPartSets * items * D * sizeof(float), 256);
   WorkspaceLayout w;
   w.kr = 0;
@@ -79,8 +84,9 @@ WorkspaceLayout workspace_layout(int B, int L, int H, int D) {
 
 // Kernel arguments of a validated call. Tensors come as (block 0, block 1) pointer pairs: rows
 // [0, n0) of each sequence in block 0, the rest in block 1 (the joint entry points pass n0 = L).
-jattn_status run_fwd(bool streams, const void* const q[2], const void* const k[2], const void* const v[2],
-                     const float* gains, const int32_t* valid_len, int B, int L, int n0, int H, int D,
+jattn_status run_fwd(jattn::Variant var, const void* const q[2], const void* const k[2], const void* const v[2],
+                     const float* gains, const int32_t* valid_len, const int32_t* cu_seqlens, int total, int B,
+                     int L, int n0, int H, int D,
                      float softmax_scale, float eps, void* const out[2], float* lse, void* workspace,
                      const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream) {
   auto in = [](const void* p) { return static_cast<const uint16_t*>(p); };
@@ -94,6 +100,7 @@ jattn_status run_fwd(bool streams, const void* const q[2], const void* const k[2
   a.kr = static_cast<const uint16_t*>(workspace);
   a.gains = gains;
   a.valid_len = valid_len;
+  a.cu_seqlens = cu_seqlens;
   a.out = static_cast<uint16_t*>(out[0]);
   a.out1 = static_cast<uint16_t*>(out[1]);
   a.lse = lse;
@@ -101,23 +108,25 @@ jattn_status run_fwd(bool streams, const void* const q[2], const void* const k[2
   a.L = L;
   a.H = H;
   a.n0 = n0;
+  a.total = total;
   a.c = softmax_scale * 1.4426950408889634f;
   a.eps = eps;
   a.nblk = (L + jattn::fwd_rows_per_block(D) - 1) / jattn::fwd_rows_per_block(D);
   a.items = B * H * a.nblk;
-  return jattn::launch_fwd(D, streams, a, stage_events, n_stage_events, stream) == hipSuccess ? JATTN_SUCCESS
-                                                                                           : JATTN_ERROR_HIP;
+  return jattn::launch_fwd(D, var, a, stage_events, n_stage_events, stream) == hipSuccess ? JATTN_SUCCESS
+                                                                                       : JATTN_ERROR_HIP;
 }
 
-jattn_status run_bwd(bool streams, const void* const q[2], const void* const k[2], const void* const v[2],
-                     const float* gains, const int32_t* valid_len, const void* const out[2], const float* lse,
-                     const void* const dout[2], int B, int L, int n0, int H, int D, float softmax_scale, float eps,
+jattn_status run_bwd(jattn::Variant var, const void* const q[2], const void* const k[2], const void* const v[2],
+                     const float* gains, const int32_t* valid_len, const int32_t* cu_seqlens, int total,
+                     const void* const out[2], const float* lse, const void* const dout[2], int B, int L, int n0,
+                     int H, int D, float softmax_scale, float eps,
                      void* const dq[2], void* const dk[2], void* const dv[2], float* dgains, void* workspace,
                      const void* fwd_workspace, const hipEvent_t* stage_events, int n_stage_events,
                      hipStream_t stream) {
   auto in = [](const void* p) { return static_cast<const uint16_t*>(p); };
   auto outp = [](void* p) { return static_cast<uint16_t*>(p); };
-  const WorkspaceLayout wl = workspace_layout(B, L, H, D);
+  const WorkspaceLayout wl = workspace_layout(B, L, H, D, var == jattn::kVarlen ? total : -1);
   char* ws = static_cast<char*>(workspace);
   jattn::BwdArgs a;
   a.q = in(q[0]);
@@ -128,6 +137,7 @@ jattn_status run_bwd(bool streams, const void* const q[2], const void* const k[2
   a.v1 = in(v[1]);
   a.gains = gains;
   a.valid_len = valid_len;
+  a.cu_seqlens = cu_seqlens;
   a.out = in(out[0]);
   a.out1 = in(out[1]);
   a.lse = lse;
@@ -151,16 +161,28 @@ jattn_status run_bwd(bool streams, const void* const q[2], const void* const k[2
   a.L = L;
   a.H = H;
   a.n0 = n0;
+  a.total = total;
   a.scale = softmax_scale;
   a.c = softmax_scale * 1.4426950408889634f;
   a.eps = eps;
   a.nblk = (L + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock;
   a.items = B * H * a.nblk;
   a.lp = a.nblk * kBwdRowsPerBlock;
-  return jattn::launch_bwd(D, streams, a, fwd_workspace == nullptr, stage_events, n_stage_events, stream) ==
+  return jattn::launch_bwd(D, var, a, fwd_workspace == nullptr, stage_events, n_stage_events, stream) ==
                  hipSuccess
              ? JATTN_SUCCESS
              : JATTN_ERROR_HIP;
+}
+
+// Sizes of a packed variable-length call: B sequences, the longest max_seqlen rows, total token rows.
+jattn_status check_varlen_sizes(int B, int max_seqlen, int total, int H, int D) {
+  if (total < 1) return JATTN_ERROR_INVALID_VALUE;
+  const jattn_status st = check_sizes(B, max_seqlen, H, D);
+  if (st != JATTN_SUCCESS) return st;
+  if (B > 65535) return JATTN_ERROR_NOT_SUPPORTED;  // (the key normalisation puts the sequence in grid y)
+  if ((int64_t)total * H * D >= (int64_t(1) << 39) || ((int64_t)total + 128 * (int64_t)B) * H >= (int64_t(1) << 31))
+    return JATTN_ERROR_NOT_SUPPORTED;
+  return JATTN_SUCCESS;
 }
 
 // Sizes of a two-stream call: N_img, N_txt >= 0 with at least one token.
@@ -233,8 +255,8 @@ jattn_status jattn_fwd_ex(const void* q, const void* k, const void* v, const flo
   const void* const kp[2] = {k, nullptr};
   const void* const vp[2] = {v, nullptr};
   void* const op[2] = {out, nullptr};
-  return run_fwd(false, qp, kp, vp, gains, valid_len, B, L, L, H, D, softmax_scale, eps, op, lse, workspace,
-                 stage_events, n_stage_events, stream);
+  return run_fwd(jattn::kJoint, qp, kp, vp, gains, valid_len, nullptr, B * L, B, L, L, H, D, softmax_scale, eps, op,
+                 lse, workspace, stage_events, n_stage_events, stream);
 }
 
 jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float* gains,
@@ -290,8 +312,9 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
   void* const dqp[2] = {dq, nullptr};
   void* const dkp[2] = {dk, nullptr};
   void* const dvp[2] = {dv, nullptr};
-  return run_bwd(false, qp, kp, vp, gains, valid_len, op, lse, dop, B, L, L, H, D, softmax_scale, eps, dqp, dkp, dvp,
-                 dgains, workspace, fwd_workspace, stage_events, n_stage_events, stream);
+  return run_bwd(jattn::kJoint, qp, kp, vp, gains, valid_len, nullptr, B * L, op, lse, dop, B, L, L, H, D,
+                 softmax_scale, eps, dqp, dkp, dvp, dgains, workspace, fwd_workspace, stage_events, n_stage_events,
+                 stream);
 }
 
 jattn_status jattn_fwd_streams(const void* const q[2], const void* const k[2], const void* const v[2],
@@ -324,8 +347,8 @@ jattn_status jattn_fwd_streams(const void* const q[2], const void* const k[2], c
   const void* const kp[2] = {pick(k, 0), pick(k, 1)};
   const void* const vp[2] = {pick(v, 0), pick(v, 1)};
   void* const op[2] = {n_img > 0 ? out[0] : nullptr, n_txt > 0 ? out[1] : nullptr};
-  return run_fwd(true, qp, kp, vp, gains, valid_len, B, L, n_img, H, D, softmax_scale, eps, op, lse, workspace,
-                 stage_events, n_stage_events, stream);
+  return run_fwd(jattn::kStreams, qp, kp, vp, gains, valid_len, nullptr, B * L, B, L, n_img, H, D, softmax_scale,
+                 eps, op, lse, workspace, stage_events, n_stage_events, stream);
 }
 
 jattn_status jattn_bwd_streams(const void* const q[2], const void* const k[2], const void* const v[2],
@@ -370,8 +393,87 @@ jattn_status jattn_bwd_streams(const void* const q[2], const void* const k[2], c
   void* const dqp[2] = {pickw(dq, 0), pickw(dq, 1)};
   void* const dkp[2] = {pickw(dk, 0), pickw(dk, 1)};
   void* const dvp[2] = {pickw(dv, 0), pickw(dv, 1)};
-  return run_bwd(true, qp, kp, vp, gains, valid_len, op, lse, dop, B, L, n_img, H, D, softmax_scale, eps, dqp, dkp,
-                 dvp, dgains, workspace, fwd_workspace, stage_events, n_stage_events, stream);
+  return run_bwd(jattn::kStreams, qp, kp, vp, gains, valid_len, nullptr, B * L, op, lse, dop, B, L, n_img, H, D,
+                 softmax_scale, eps, dqp, dkp, dvp, dgains, workspace, fwd_workspace, stage_events, n_stage_events,
+                 stream);
+}
+
+size_t jattn_varlen_fwd_workspace_bytes(int B, int max_seqlen, int total, int H, int D) {
+  if (check_varlen_sizes(B, max_seqlen, total, H, D) != JATTN_SUCCESS) return 0;
+  return round_up((size_t)total * H * D * 2, 256);  // the normalised key rows
+}
+
+size_t jattn_varlen_bwd_workspace_bytes(int B, int max_seqlen, int total, int H, int D) {
+  if (check_varlen_sizes(B, max_seqlen, total, H, D) != JATTN_SUCCESS) return 0;
+  return workspace_layout(B, max_seqlen, H, D, total).total;
+}
+
+jattn_status jattn_fwd_varlen(const void* q, const void* k, const void* v, const float* gains,
+                              const int32_t* cu_seqlens, int B, int max_seqlen, int total, int H, int D,
+                              float softmax_scale, float eps, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, const hipEvent_t* stage_events, int n_stage_events,
+                              hipStream_t stream) {
+  if (n_stage_events < 0 || n_stage_events > JATTN_FWD_STAGES || (n_stage_events > 0 && !stage_events))
+    return JATTN_ERROR_INVALID_VALUE;
+  if (!q || !k || !v || !gains || !cu_seqlens || !out || !lse) return JATTN_ERROR_INVALID_VALUE;
+  const jattn_status st = check_varlen_sizes(B, max_seqlen, total, H, D);
+  if (st != JATTN_SUCCESS) return st;
+  if (!std::isfinite(softmax_scale) || !std::isfinite(eps) || eps < 0.f) return JATTN_ERROR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(gains, 4) ||
+      !aligned(lse, 4) || !aligned(cu_seqlens, 4))
+    return JATTN_ERROR_INVALID_VALUE;
+  const size_t wsb = jattn_varlen_fwd_workspace_bytes(B, max_seqlen, total, H, D);
+  if (!workspace || workspace_bytes < wsb) return JATTN_ERROR_WORKSPACE;
+  if (!aligned(workspace, 256)) return JATTN_ERROR_INVALID_VALUE;
+  const size_t tb = (size_t)total * H * D * 2, lb = (size_t)total * H * 4;
+  const Range ins[] = {{q, tb}, {k, tb}, {v, tb}, {gains, (size_t)2 * D * 4}, {cu_seqlens, (size_t)(B + 1) * 4}};
+  const Range outs[] = {{out, tb}, {lse, lb}, {workspace, wsb}};
+  if (!outputs_disjoint(outs, 3, ins, 5)) return JATTN_ERROR_INVALID_VALUE;
+  const void* const qp[2] = {q, nullptr};
+  const void* const kp[2] = {k, nullptr};
+  const void* const vp[2] = {v, nullptr};
+  void* const op[2] = {out, nullptr};
+  return run_fwd(jattn::kVarlen, qp, kp, vp, gains, nullptr, cu_seqlens, total, B, max_seqlen, max_seqlen, H, D,
+                 softmax_scale, eps, op, lse, workspace, stage_events, n_stage_events, stream);
+}
+
+jattn_status jattn_bwd_varlen(const void* q, const void* k, const void* v, const float* gains,
+                              const int32_t* cu_seqlens, const void* out, const float* lse, const void* dout, int B,
+                              int max_seqlen, int total, int H, int D, float softmax_scale, float eps, void* dq,
+                              void* dk, void* dv, float* dgains, void* workspace, size_t workspace_bytes,
+                              const void* fwd_workspace, const hipEvent_t* stage_events, int n_stage_events,
+                              hipStream_t stream) {
+  if (n_stage_events < 0 || n_stage_events > JATTN_BWD_STAGES || (n_stage_events > 0 && !stage_events))
+    return JATTN_ERROR_INVALID_VALUE;
+  if (!q || !k || !v || !gains || !cu_seqlens || !out || !lse || !dout || !dq || !dk || !dv || !dgains)
+    return JATTN_ERROR_INVALID_VALUE;
+  const jattn_status st = check_varlen_sizes(B, max_seqlen, total, H, D);
+  if (st != JATTN_SUCCESS) return st;
+  if (!std::isfinite(softmax_scale) || !std::isfinite(eps) || eps < 0.f) return JATTN_ERROR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(gains, 4) || !aligned(lse, 4) ||
+      !aligned(dgains, 4) || !aligned(cu_seqlens, 4))
+    return JATTN_ERROR_INVALID_VALUE;
+  const size_t wsb = jattn_varlen_bwd_workspace_bytes(B, max_seqlen, total, H, D);
+  if (!workspace || workspace_bytes < wsb) return JATTN_ERROR_WORKSPACE;
+  if (!aligned(workspace, 256) || !aligned(fwd_workspace, 256)) return JATTN_ERROR_INVALID_VALUE;
+  const size_t tb = (size_t)total * H * D * 2, lb = (size_t)total * H * 4;
+  const size_t fwb = fwd_workspace ? jattn_varlen_fwd_workspace_bytes(B, max_seqlen, total, H, D) : 0;
+  const Range ins[] = {{q, tb},   {k, tb},    {v, tb},   {gains, (size_t)2 * D * 4}, {cu_seqlens, (size_t)(B + 1) * 4},
+                       {out, tb}, {lse, lb}, {dout, tb}, {fwd_workspace, fwb}};
+  const Range outs[] = {{dq, tb}, {dk, tb}, {dv, tb}, {dgains, (size_t)2 * D * 4}, {workspace, wsb}};
+  if (!outputs_disjoint(outs, 5, ins, 9)) return JATTN_ERROR_INVALID_VALUE;
+  const void* const qp[2] = {q, nullptr};
+  const void* const kp[2] = {k, nullptr};
+  const void* const vp[2] = {v, nullptr};
+  const void* const op[2] = {out, nullptr};
+  const void* const dop[2] = {dout, nullptr};
+  void* const dqp[2] = {dq, nullptr};
+  void* const dkp[2] = {dk, nullptr};
+  void* const dvp[2] = {dv, nullptr};
+  return run_bwd(jattn::kVarlen, qp, kp, vp, gains, nullptr, cu_seqlens, total, op, lse, dop, B, max_seqlen,
+                 max_seqlen, H, D, softmax_scale, eps, dqp, dkp, dvp, dgains, workspace, fwd_workspace, stage_events,
+                 n_stage_events, stream);
 }
 
 }  // extern "C"

@@ -241,8 +241,10 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
   accumulate(1);
 }
 
-// One work item of the dq kernel: query rows [128 blk, 128 blk + 128) of (batch, head) pair bh.
-template <int D, bool S>
+// One work item of the dq kernel: query rows [128 blk, 128 blk + 128) of (sequence, head) pair bh.
+// Varlen (V): a block past the end of its sequence has nothing to do (its statistics rows belong to
+// the next pair).
+template <int D, bool S, bool V>
 __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, int blk) {
   using Dm = Dims<D>;
   using Cfg = DqCfg<D>;
@@ -252,10 +254,18 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
   __bf16* sk = reinterpret_cast<__bf16*>(smem);
   __bf16* sv = sk + NB * LK::ELEMS;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
-  const int L = a.L, H = a.H;
-  const int b = bh / H;
-  const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
-  const RowMap<S> map(b, bh - b * H, L, H, D, a.n0);
+  const int H = a.H;
+  const int b = bh / H, h = bh - b * H;
+  // (fixed-length batches keep the offsets in their original form, e.g. (size_t)bh * L: written through
+  // the sequence geometry instead, the compiler allocated the tile loop's registers differently and
+  // the loop ran slower)
+  const SeqGeom<V> seq(a.cu_seqlens, b, a.L, a.total, a.L);
+  const int L = V ? seq.L : a.L;
+  if (V && blk * kBwdRowsPerBlock >= L) return;  // (uniform over the workgroup)
+  const int n = !V && a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
+  const size_t row0 = V ? seq.row0(h, H) : (size_t)bh * L;  // first workspace / LSE row of the pair
+  const RowMap<S> map(V ? (size_t)seq.start : (size_t)b * (S ? a.n0 : L), (size_t)b * (L - a.n0), h, H, D,
+                      S ? a.n0 : L);
 
   // start streaming the first key tiles before the per-row set-up
   const int ntiles = (n + kTile - 1) / kTile, nfull = n / kTile;
@@ -263,7 +273,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
   DirectTile<D, LV, kBwdWaves> dv;
   dk.init(D, wave, lane);
   dv.init(map.rs, wave, lane);
-  const uint16_t* kb = a.kr + (size_t)bh * L * D;
+  const uint16_t* kb = a.kr + row0 * D;
   auto issue = [&](int t, int buf) {
     dk.issue(tile_rsrc<D>(kb, D, t * kTile, n), sk + buf * LK::ELEMS, wave);
     dv.issue_blocks(S, a.v, a.v1, map.o0, map.o1, map.n0, map.rs, t * kTile, n, sv + buf * LV::ELEMS, wave,
@@ -296,7 +306,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
       for (int e = 0; e < 8; ++e) delta += (float)dof[ks][e] * o[ks][e];
     delta += __shfl_xor(delta, 32);
   }
-  const float lse2 = qvalid ? a.lse[(size_t)bh * L + qrow] * kLog2e : 0.f;
+  const float lse2 = qvalid ? a.lse[row0 + qrow] * kLog2e : 0.f;
   f32x16 cs, cp;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -331,7 +341,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
 
   // row statistics for the key-parallel kernel, for every row of the block (-inf / 0 past L)
   if (g == 0) {
-    const size_t si = (size_t)bh * a.lp + qrow;
+    const size_t si = (V ? seq.stat0(b, h, H) : (size_t)bh * a.lp) + qrow;
     a.nlse2[si] = qvalid ? -lse2 : -INFINITY;
     a.ndelta[si] = qvalid ? -delta : 0.f;
   }
@@ -339,7 +349,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) acc[mt] *= a.scale;
   if constexpr (!keep_row_c<D>()) load_row_c<D>(xq, qptr, qvalid, g);
-  uint16_t* qsrow = a.qs + ((size_t)bh * L + qrow) * D;
+  uint16_t* qsrow = a.qs + (row0 + qrow) * D;
   if constexpr (!S) {
     rmsnorm_backward_row<D, false>(acc, xq, a.gains, a.gains + D, rq, qvalid, qvalid, map.row(a.dq, a.dq1, qrow),
                                    qsrow, a.c, nullptr, g);
@@ -355,16 +365,20 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
   }
 }
 
-template <int D, bool S>
+template <int D, bool S, bool V>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
 void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DqCfg<D>::template bytes<S>()];
   // (an item ends with its tile loop's barrier and, in the joint form, its epilogue does not touch
   // LDS, so the next item may refill the ring right away; the two-stream epilogue's column sums do)
-  for (ItemIter it(a.items); it.valid(); it.next()) {
-    const int bh = it.item() / a.nblk;
-    dq_item<D, S>(a, smem, bh, it.item() - bh * a.nblk);
-    if constexpr (S) __syncthreads();
+  if constexpr (V) {
+    for (PairIter it(a.B * a.H, a.nblk); it.valid(); it.next()) dq_item<D, S, V>(a, smem, it.pair(), it.blk());
+  } else {
+    for (ItemIter it(a.items); it.valid(); it.next()) {
+      const int bh = it.item() / a.nblk;
+      dq_item<D, S, V>(a, smem, bh, it.item() - bh * a.nblk);
+      if constexpr (S) __syncthreads();
+    }
   }
 }
 
@@ -445,7 +459,8 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const _
 }
 
 // `active`: this wave holds at least one valid key (a wave of padded keys only keeps the ring going).
-template <int D, bool S, bool KMASK>
+// Streams the query rows of (sequence, head) pair bh: Qs, dout (through `map`) and the statistics.
+template <int D, bool S, bool V, bool KMASK>
 __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, const RowMap<S>& map, int bh,
                                           const bf16x8 (&kf)[Dims<D>::KS], const bf16x8 (&vf)[Dims<D>::KS],
                                           f32x16 (&dva)[Dims<D>::MT], f32x16 (&dka)[Dims<D>::MT], bool kvalid,
@@ -459,16 +474,21 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, const Ro
   float* sl = reinterpret_cast<float*>(smem + Cfg::STAGE);  // [NB][kTile]
   float* sd = sl + NB * kTile;                                // [NB][kTile]
   const int lane = tid & 63, wave = wave_id();
-  const int L = a.L;
+  // (fixed-length batches: the original offset expressions, see dq_item)
+  const int H = a.H, b = bh / H, h = bh - b * H;
+  const SeqGeom<V> seq(a.cu_seqlens, b, a.L, a.total, a.L);
+  const int L = V ? seq.L : a.L;
+  const uint16_t* qb = a.qs + (V ? seq.row0(h, H) : (size_t)bh * L) * D;
+  const size_t st0 = V ? seq.stat0(b, h, H) : (size_t)bh * a.lp;
+  const int lp = V ? seq.lp : a.lp;
   DirectTile<D, LQ, kBwdWaves> dq;
   DirectTile<D, LO, kBwdWaves> dout;
   dq.init(D, wave, lane);
   const int rs = map.rs;
   dout.init(rs, wave, lane);
-  const uint16_t* qb = a.qs + (size_t)bh * L * D;
   const uint16_t* ob = a.dout + map.o0;  // (joint form)
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.nlse2 + (size_t)bh * a.lp, (uint32_t)a.lp * 4u);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.ndelta + (size_t)bh * a.lp, (uint32_t)a.lp * 4u);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.nlse2 + st0, (uint32_t)lp * 4u);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.ndelta + st0, (uint32_t)lp * 4u);
   // Tile t: rows [64 t, 64 t + 64) of Qs and dO (zeros past L) and of the statistics (written by the
   // dq kernel for every row of its blocks, so 64 t + 63 < lp). Waves 0 and 1 carry the statistics.
   auto issue = [&](int t, int buf) {
@@ -503,15 +523,20 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, const Ro
   }
 }
 
-// One work item of the dk/dv kernel: key rows [128 blk, 128 blk + 128) of (batch, head) pair bh.
-template <int D, bool S>
+// One work item of the dk/dv kernel: key rows [128 blk, 128 blk + 128) of (sequence, head) pair bh.
+// (Varlen: a block past the end of its sequence takes the all-padding path below, which then writes
+// no rows, only its zero partial sums.)
+template <int D, bool S, bool V>
 __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, int blk, int item) {
   using Dm = Dims<D>;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
-  const int L = a.L, H = a.H;
-  const int b = bh / H;
-  const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
-  const RowMap<S> map(b, bh - b * H, L, H, D, a.n0);
+  const int H = a.H;
+  const int b = bh / H, h = bh - b * H;
+  const SeqGeom<V> seq(a.cu_seqlens, b, a.L, a.total, a.L);
+  const int L = V ? seq.L : a.L;
+  const int n = !V && a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
+  const RowMap<S> map(V ? (size_t)seq.start : (size_t)b * (S ? a.n0 : L), (size_t)b * (L - a.n0), h, H, D,
+                      S ? a.n0 : L);
   const size_t set = (size_t)D * a.items;
 
   const int key = blk * kBwdRowsPerBlock + wave * kWaveRows + l32;
@@ -567,9 +592,9 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
   // waves whose 32 keys are all valid skip the key mask
   const bool active = blk * kBwdRowsPerBlock + wave * kWaveRows < n;
   if (blk * kBwdRowsPerBlock + (wave + 1) * kWaveRows <= n)
-    dkdv_loop<D, S, false>(a, smem, map, bh, kf, vf, dva, dka, kvalid, active, tid);
+    dkdv_loop<D, S, V, false>(a, smem, map, bh, kf, vf, dva, dka, kvalid, active, tid);
   else
-    dkdv_loop<D, S, true>(a, smem, map, bh, kf, vf, dva, dka, kvalid, active, tid);
+    dkdv_loop<D, S, V, true>(a, smem, map, bh, kf, vf, dva, dka, kvalid, active, tid);
 
   // dv (zeros at padded keys)
   if (kin) {
@@ -611,14 +636,21 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
   }
 }
 
-template <int D, bool S>
+template <int D, bool S, bool V>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
 void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DkdvCfg<D>::template bytes<S>()];
-  for (ItemIter it(a.items); it.valid(); it.next()) {
-    const int bh = it.item() / a.nblk;
-    dkdv_item<D, S>(a, smem, bh, it.item() - bh * a.nblk, it.item());
-    __syncthreads();  // the column-sum scratch overlaps the ring the next item refills
+  if constexpr (V) {
+    for (PairIter it(a.B * a.H, a.nblk); it.valid(); it.next()) {
+      dkdv_item<D, S, V>(a, smem, it.pair(), it.blk(), it.pair() * a.nblk + it.blk());
+      __syncthreads();  // the column-sum scratch overlaps the ring the next item refills
+    }
+  } else {
+    for (ItemIter it(a.items); it.valid(); it.next()) {
+      const int bh = it.item() / a.nblk;
+      dkdv_item<D, S, V>(a, smem, bh, it.item() - bh * a.nblk, it.item());
+      __syncthreads();  // the column-sum scratch overlaps the ring the next item refills
+    }
   }
 }
 
@@ -666,7 +698,7 @@ __global__ __launch_bounds__(kReduceThreads) void dg_reduce_kernel(const float* 
   }
 }
 
-template <int D, bool S>
+template <int D, bool S, bool V>
 static hipError_t launch_bwd_d(const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
                                hipStream_t stream) {
   int stage = 0;
@@ -681,45 +713,51 @@ static hipError_t launch_bwd_d(const BwdArgs& a, bool prenorm, const hipEvent_t*
   p.k1 = a.k1;
   p.gains = a.gains;
   p.valid_len = a.valid_len;
+  p.cu_seqlens = a.cu_seqlens;
   p.kr = a.kr;
   p.B = a.B;
   p.L = a.L;
   p.H = a.H;
   p.n0 = a.n0;
+  p.total = a.total;
   p.eps = a.eps;
-  hipError_t e = recorded(prenorm ? launch_prenorm(D, S, p, stream) : hipSuccess);
+  hipError_t e = recorded(prenorm ? launch_prenorm(D, S ? kStreams : (V ? kVarlen : kJoint), p, stream) : hipSuccess);
   if (e != hipSuccess) return e;
   int grid = 0;
-  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dq_kernel<D, S>), a.items, kBwdThreads, &grid)) != hipSuccess)
-    return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, S>), dim3(grid), dim3(kBwdThreads), 0, stream, a);
-  if ((e = recorded(hipSuccess)) != hipSuccess) return e;
-  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dkdv_kernel<D, S>), a.items, kBwdThreads, &grid)) !=
+  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dq_kernel<D, S, V>), a.items, kBwdThreads, &grid)) !=
       hipSuccess)
     return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, S>), dim3(grid), dim3(kBwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, S, V>), dim3(grid), dim3(kBwdThreads), 0, stream, a);
+  if ((e = recorded(hipSuccess)) != hipSuccess) return e;
+  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dkdv_kernel<D, S, V>), a.items, kBwdThreads, &grid)) !=
+      hipSuccess)
+    return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, S, V>), dim3(grid), dim3(kBwdThreads), 0, stream, a);
   if ((e = recorded(hipSuccess)) != hipSuccess) return e;
   hipLaunchKernelGGL(dg_reduce_kernel<S>, dim3(S ? kPartSets * D : D), dim3(kReduceThreads), 0, stream, a.part,
                      a.gains, a.items, D, a.dgains);
   return recorded(hipSuccess);
 }
 
-template <bool S>
+template <bool S, bool V>
 static hipError_t launch_bwd_s(int D, const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
                                hipStream_t stream) {
   switch (D) {
-    case 32: return launch_bwd_d<32, S>(a, prenorm, events, n_events, stream);
-    case 64: return launch_bwd_d<64, S>(a, prenorm, events, n_events, stream);
-    case 72: return launch_bwd_d<72, S>(a, prenorm, events, n_events, stream);
-    case 128: return launch_bwd_d<128, S>(a, prenorm, events, n_events, stream);
+    case 32: return launch_bwd_d<32, S, V>(a, prenorm, events, n_events, stream);
+    case 64: return launch_bwd_d<64, S, V>(a, prenorm, events, n_events, stream);
+    case 72: return launch_bwd_d<72, S, V>(a, prenorm, events, n_events, stream);
+    case 128: return launch_bwd_d<128, S, V>(a, prenorm, events, n_events, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd(int D, bool streams, const BwdArgs& a, bool prenorm, const hipEvent_t* events,
+hipError_t launch_bwd(int D, Variant var, const BwdArgs& a, bool prenorm, const hipEvent_t* events,
                       int n_events, hipStream_t stream) {
-  return streams ? launch_bwd_s<true>(D, a, prenorm, events, n_events, stream)
-                 : launch_bwd_s<false>(D, a, prenorm, events, n_events, stream);
+  switch (var) {
+    case kStreams: return launch_bwd_s<true, false>(D, a, prenorm, events, n_events, stream);
+    case kVarlen: return launch_bwd_s<false, true>(D, a, prenorm, events, n_events, stream);
+    default: return launch_bwd_s<false, false>(D, a, prenorm, events, n_events, stream);
+  }
 }
 
 }  // namespace jattn

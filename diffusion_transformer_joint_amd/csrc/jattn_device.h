@@ -347,19 +347,22 @@ __device__ __forceinline__ void lds_load_dwords(__amdgpu_buffer_rsrc_t rsrc, flo
 }
 
 
-// Addresses of the rows of one (batch, head) pair of a per-token tensor stored in two row blocks
-// (rows [0, n0) of each sequence in block 0, [B, n0, H, D]; rows [n0, L) in block 1,
-// [B, L - n0, H, D]; the joint layout is n0 = L). o0 / o1: element offsets of row 0 in block 0 and
-// of row n0 in block 1. With S = false only block 0 exists and no per-row selection is made.
+// Addresses of the rows of one (sequence, head) pair of a per-token tensor (token rows of H * D
+// elements) stored in two row blocks: rows [0, n0) of the sequence start at token row base0 of
+// block 0, rows [n0, ...) at token row base1 of block 1. The joint layout is a single block
+// (base0 = b * L, n0 = L); the two-stream layout has base0 = b * N_img, base1 = b * N_txt; a packed
+// variable-length batch has base0 = the sequence's first token row. o0 / o1: element offsets of row 0
+// in block 0 and of row n0 in block 1. With S = false only block 0 exists and no per-row selection
+// is made.
 template <bool S>
 struct RowMap {
   size_t o0, o1;
   int n0, rs;
-  __device__ RowMap(int b, int h, int L, int H, int D, int n_0) {
-    n0 = S ? n_0 : L;
+  __device__ RowMap(size_t base0, size_t base1, int h, int H, int D, int n_0) {
+    n0 = n_0;
     rs = H * D;
-    o0 = ((size_t)b * n0 * H + h) * D;
-    o1 = ((size_t)b * (L - n0) * H + h) * D;
+    o0 = (base0 * H + h) * D;
+    o1 = (base1 * H + h) * D;
   }
   template <class T>
   __device__ __forceinline__ T* row(T* p0, T* p1, int r) const {
@@ -367,6 +370,35 @@ struct RowMap {
     else return r < n0 ? p0 + o0 + (size_t)r * rs : p1 + o1 + (size_t)(r - n0) * rs;
   }
   __device__ __forceinline__ int block(int r) const { return S && r >= n0 ? 1 : 0; }
+};
+
+// Geometry of sequence b and the offsets of one of its heads in the library's own arrays.
+// Fixed-length batch (V = false): rows [b L, b L + L) of the token tensors. Packed variable-length
+// batch (V = true): rows [start, start + L) with start = clamp(cu[b], 0, total) and
+// L = clamp(cu[b + 1], start, min(total, start + maxlen)) - start, so that no value of the device
+// array can address outside the tensors. In both forms the rows of one (sequence, head) are
+// contiguous in the workspaces ([rows, D], from row start * H + h * L) and in the LSE (from element
+// start * H + h * L); the fixed form is exactly [B, H, L] there. The row statistics of (sequence,
+// head) take lp = L rounded up to 128-row blocks from row (start + 128 b) * H + h * lp (fixed form:
+// (b H + h) lp), which leaves room for every sequence's rounding.
+template <bool V>
+struct SeqGeom {
+  int L, start, lp;
+  __device__ SeqGeom(const int32_t* cu, int b, int Lfix, int total, int maxlen) {
+    if constexpr (V) {
+      start = min(max(cu[b], 0), total);
+      const int end = min(max(cu[b + 1], start), min(total, start + maxlen));
+      L = end - start;
+    } else {
+      L = Lfix;
+      start = b * Lfix;
+    }
+    lp = (L + 127) / 128 * 128;
+  }
+  __device__ __forceinline__ size_t row0(int h, int H) const { return (size_t)start * H + (size_t)h * L; }
+  __device__ __forceinline__ size_t stat0(int b, int h, int H) const {
+    return V ? ((size_t)start + 128 * (size_t)b) * H + (size_t)h * lp : ((size_t)b * H + h) * lp;
+  }
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -565,6 +597,28 @@ struct ItemIter {
   __device__ int item() const { return base + j; }
   __device__ void next() { j += step; }
 };
+
+// Item order of the packed variable-length kernels. Sequences differ in length, and the work of a row
+// block grows with its sequence's length, so contiguous item ranges per XCD (ItemIter) would give
+// one XCD the long sequences and another the short ones. Here the (sequence, head) pairs are dealt
+// round-robin over the XCDs (pair p to XCD p % 8): every XCD gets about the same share of every
+// sequence, and the nblk row blocks of one pair stay on one XCD and its L2. Workgroup w serves XCD
+// w % 8 and takes its items j = w / 8, w / 8 + gridDim.x / 8, ... (one item per workgroup for a grid
+// of 8 * ceil(npairs / 8) * nblk).
+struct PairIter {
+  int x, j, step, per, nblk;
+  __device__ PairIter(int npairs, int nblk_) : nblk(nblk_) {
+    x = (int)(blockIdx.x & 7);
+    j = (int)(blockIdx.x >> 3);
+    step = (int)(gridDim.x >> 3);
+    per = npairs > x ? ((npairs - x + 7) >> 3) * nblk_ : 0;
+  }
+  __device__ bool valid() const { return j < per; }
+  __device__ int pair() const { return x + 8 * (j / nblk); }
+  __device__ int blk() const { return j % nblk; }
+  __device__ void next() { j += step; }
+};
+__host__ __device__ inline int pair_grid(int npairs, int nblk) { return 8 * ((npairs + 7) / 8) * nblk; }
 
 // ---------------------------------------------------------------------------------------------
 // Deterministic per-workgroup column sums of a [W waves x 32 rows x D] set of values held in the

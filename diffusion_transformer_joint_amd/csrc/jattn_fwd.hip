@@ -168,7 +168,9 @@ struct FwdRing {
 
 // `active`: this wave has at least one query row inside the sequence (a wave past L only keeps the
 // ring going: it issues its share of the loads and meets the barriers, but skips the math).
-template <int D, bool S, bool BOUNDED>
+// (V is not used here; as a template argument it keeps each caller's instantiation its own, which
+// the compiler's host-side pass needs for templates that reach the LDS-bound load builtins.)
+template <int D, bool S, bool V, bool BOUNDED>
 __device__ __forceinline__ void fwd_loop(FwdRing<D, S>& ring, const bf16x8 (&qf)[Fwd<D>::QT][Dims<D>::KS],
                                          const float (&shift)[Fwd<D>::QT], FwdState<D>& st, bool active,
                                          int lane) {
@@ -194,23 +196,30 @@ __device__ __forceinline__ void fwd_loop(FwdRing<D, S>& ring, const bf16x8 (&qf)
   if (nfull < ntiles) step(std::true_type{}, nfull);
 }
 
-// One work item: query rows [ROWS blk, ROWS blk + ROWS) of (batch, head) pair bh.
-template <int D, bool S>
+// One work item: query rows [ROWS blk, ROWS blk + ROWS) of (sequence, head) pair bh.
+// Varlen (V): the grid is sized for the longest sequence; a block past the end of its sequence has
+// nothing to do.
+template <int D, bool S, bool V>
 __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, int blk) {
   using Dm = Dims<D>;
   constexpr int QT = Fwd<D>::QT;
   float* sbound = reinterpret_cast<float*>(smem + Fwd<D>::STAGE);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
-  const int L = a.L, H = a.H;
-  const int b = bh / H;
-  const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
-  const RowMap<S> map(b, bh - b * H, L, H, D, a.n0);
+  const int H = a.H;
+  const int b = bh / H, h = bh - b * H;
+  const SeqGeom<V> seq(a.cu_seqlens, b, a.L, a.total, a.L);
+  const int L = V ? seq.L : a.L;
+  if (V && blk * Fwd<D>::ROWS >= L) return;  // (uniform over the workgroup)
+  const int n = !V && a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
+  const size_t row0 = V ? seq.row0(h, H) : (size_t)bh * L;  // first workspace / LSE row of the pair
+  const RowMap<S> map(V ? (size_t)seq.start : (size_t)b * (S ? a.n0 : L), (size_t)b * (L - a.n0), h, H, D,
+                      S ? a.n0 : L);
 
   // start streaming the first key/value tiles before the per-row set-up
   FwdRing<D, S> ring(map);
   ring.sk = reinterpret_cast<__bf16*>(smem);
   ring.sv = ring.sk + Fwd<D>::NB * Fwd<D>::LK::ELEMS;
-  ring.kb = a.kr + (size_t)bh * L * D;
+  ring.kb = a.kr + row0 * D;
   ring.v0 = a.v;
   ring.v1 = a.v1;
   ring.n = n;
@@ -286,11 +295,11 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
   if (bmax <= kBoundLimit) {  // uniform over the workgroup
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = shift[qt];
-    fwd_loop<D, S, true>(ring, qf, shift, st, active, lane);
+    fwd_loop<D, S, V, true>(ring, qf, shift, st, active, lane);
   } else {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = -INFINITY;
-    fwd_loop<D, S, false>(ring, qf, shift, st, active, lane);
+    fwd_loop<D, S, V, false>(ring, qf, shift, st, active, lane);
   }
 
 #pragma unroll
@@ -299,7 +308,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
     if (qrow[qt] >= L) continue;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     if (g == 0)
-      a.lse[(size_t)bh * L + qrow[qt]] = lsum > 0.f ? (st.mrow[qt] + __log2f(lsum)) * kLn2 : -INFINITY;
+      a.lse[row0 + qrow[qt]] = lsum > 0.f ? (st.mrow[qt] + __log2f(lsum)) * kLn2 : -INFINITY;
     uint16_t* orow = map.row(a.out, a.out1, qrow[qt]);
 #pragma unroll
     for (int mt = 0; mt < Dm::MT; ++mt)
@@ -316,55 +325,67 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
   }
 }
 
-template <int D, bool S>
+template <int D, bool S, bool V>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Fwd<D>::BYTES];
   // one item per workgroup (a persistent grid measured slower here: the items are few and large),
   // numbered so that the row blocks of one (batch, head) pair share an XCD and its L2
-  const ItemIter it(a.items);
-  if (!it.valid()) return;
-  const int bh = it.item() / a.nblk;
-  fwd_item<D, S>(a, smem, bh, it.item() - bh * a.nblk);
+  if constexpr (V) {
+    const PairIter it(a.B * a.H, a.nblk);
+    if (!it.valid()) return;
+    fwd_item<D, S, V>(a, smem, it.pair(), it.blk());
+  } else {
+    const ItemIter it(a.items);
+    if (!it.valid()) return;
+    const int bh = it.item() / a.nblk;
+    fwd_item<D, S, V>(a, smem, bh, it.item() - bh * a.nblk);
+  }
 }
 
-template <int D, bool S>
+template <int D, bool S, bool V>
 static hipError_t launch_fwd_d(const FwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream) {
   PrenormArgs p;
   p.k = a.k;
   p.k1 = a.k1;
   p.gains = a.gains;
   p.valid_len = a.valid_len;
+  p.cu_seqlens = a.cu_seqlens;
   p.kr = const_cast<uint16_t*>(a.kr);
   p.B = a.B;
   p.L = a.L;
   p.H = a.H;
   p.n0 = a.n0;
+  p.total = a.total;
   p.eps = a.eps;
-  hipError_t e = launch_prenorm(D, S, p, stream);
+  hipError_t e = launch_prenorm(D, S ? kStreams : (V ? kVarlen : kJoint), p, stream);
   if (e == hipSuccess && n_events > 0) e = hipEventRecord(events[0], stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fwd_kernel<D, S>), dim3(grid_for_items(a.items)), dim3(kThreads), 0, stream, a);
+  const int grid = V ? pair_grid(a.B * a.H, a.nblk) : grid_for_items(a.items);
+  hipLaunchKernelGGL((fwd_kernel<D, S, V>), dim3(grid), dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e == hipSuccess && n_events > 1) e = hipEventRecord(events[1], stream);
   return e;
 }
 
-template <bool S>
+template <bool S, bool V>
 static hipError_t launch_fwd_s(int D, const FwdArgs& a, const hipEvent_t* events, int n_events,
                                hipStream_t stream) {
   switch (D) {
-    case 32: return launch_fwd_d<32, S>(a, events, n_events, stream);
-    case 64: return launch_fwd_d<64, S>(a, events, n_events, stream);
-    case 72: return launch_fwd_d<72, S>(a, events, n_events, stream);
-    case 128: return launch_fwd_d<128, S>(a, events, n_events, stream);
+    case 32: return launch_fwd_d<32, S, V>(a, events, n_events, stream);
+    case 64: return launch_fwd_d<64, S, V>(a, events, n_events, stream);
+    case 72: return launch_fwd_d<72, S, V>(a, events, n_events, stream);
+    case 128: return launch_fwd_d<128, S, V>(a, events, n_events, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_fwd(int D, bool streams, const FwdArgs& a, const hipEvent_t* events, int n_events,
+hipError_t launch_fwd(int D, Variant var, const FwdArgs& a, const hipEvent_t* events, int n_events,
                       hipStream_t stream) {
-  return streams ? launch_fwd_s<true>(D, a, events, n_events, stream)
-                 : launch_fwd_s<false>(D, a, events, n_events, stream);
+  switch (var) {
+    case kStreams: return launch_fwd_s<true, false>(D, a, events, n_events, stream);
+    case kVarlen: return launch_fwd_s<false, true>(D, a, events, n_events, stream);
+    default: return launch_fwd_s<false, false>(D, a, events, n_events, stream);
+  }
 }
 
 }  // namespace jattn

@@ -15,14 +15,20 @@ namespace jattn {
 //
 // Gains: joint entry points [2, D] (Q row, K row); two-stream entry points [2, 2, D]
 // (gains[s][0] = Q gain and gains[s][1] = K gain of block s).
+//
+// Sequences. Fixed-length batches: B sequences of L rows, sequence b at token rows [b L, b L + L).
+// Packed variable-length batches (the `varlen` kernels): `cu_seqlens` [B + 1] on the device gives the
+// token row range of each sequence in [total, H, D] tensors (see SeqGeom), L is then the longest
+// sequence (max_seqlen) and sizes the grids, and valid_len is not used.
 
 struct PrenormArgs {
   const uint16_t* k;
   const uint16_t* k1;
   const float* gains;        // two-stream only: K rows are multiplied by their block's K gain
   const int32_t* valid_len;  // [B] or nullptr
+  const int32_t* cu_seqlens; // varlen only
   uint16_t* kr;              // [B, H, L, D]: bf16(k * r_k) (times the K gain, two-stream), valid keys only
-  int B, L, H, n0;
+  int B, L, H, n0, total;
   float eps;
 };
 
@@ -36,10 +42,11 @@ struct FwdArgs {
   const uint16_t* kr;      // workspace [B, H, L, D]: normalised keys, written by the prenorm kernel
   const float* gains;
   const int32_t* valid_len;  // [B] or nullptr
+  const int32_t* cu_seqlens; // varlen only
   uint16_t* out;
   uint16_t* out1;
-  float* lse;              // [B, H, L] natural log
-  int B, L, H, n0;
+  float* lse;              // [B, H, L] natural log (varlen: per sequence [H, L_b], see SeqGeom)
+  int B, L, H, n0, total;
   float c;                 // softmax_scale * log2(e)
   float eps;
   int nblk;                // query blocks per (batch, head)
@@ -55,6 +62,7 @@ struct BwdArgs {
   const uint16_t* v1;
   const float* gains;
   const int32_t* valid_len;
+  const int32_t* cu_seqlens;  // varlen only
   const uint16_t* out;
   const uint16_t* out1;
   const float* lse;
@@ -72,7 +80,7 @@ struct BwdArgs {
   float* nlse2;            // workspace [B, H, lp]: -lse * log2(e) (-inf past L)
   float* ndelta;           // workspace [B, H, lp]: -rowsum(dout * out) (0 past L)
   float* part;             // workspace [kPartSets, D, items]: per row block partial sums of the gain gradients
-  int B, L, H, n0;
+  int B, L, H, n0, total;
   float scale;
   float c;                 // scale * log2(e)
   float eps;
@@ -99,15 +107,17 @@ constexpr int kPartSets = 4;
 // the items need (rounded up to 8).
 hipError_t persistent_grid(const void* kernel, int items, int threads, int* grid);
 
-// `streams` selects the two-stream kernels (two row blocks, gains per block) over the joint ones.
-hipError_t launch_prenorm(int D, bool streams, const PrenormArgs& a, hipStream_t stream);
+// Kernel variants: the joint kernels, the two-stream kernels (two row blocks, gains per block) and
+// the packed variable-length kernels.
+enum Variant { kJoint = 0, kStreams = 1, kVarlen = 2 };
+hipError_t launch_prenorm(int D, Variant var, const PrenormArgs& a, hipStream_t stream);
 // Enqueues the key normalisation (into a.kr) and the forward kernel; if n_events > 0, records
 // events[i] after stage i (i < n_events).
-hipError_t launch_fwd(int D, bool streams, const FwdArgs& a, const hipEvent_t* events, int n_events,
+hipError_t launch_fwd(int D, Variant var, const FwdArgs& a, const hipEvent_t* events, int n_events,
                       hipStream_t stream);
 // Enqueues the backward kernels (the key normalisation only if `prenorm`; a.kr then already holds
 // it); if n_events > 0, records events[i] after stage i (i < n_events).
-hipError_t launch_bwd(int D, bool streams, const BwdArgs& a, bool prenorm, const hipEvent_t* events,
+hipError_t launch_bwd(int D, Variant var, const BwdArgs& a, bool prenorm, const hipEvent_t* events,
                       int n_events, hipStream_t stream);
 
 }  // namespace jattn

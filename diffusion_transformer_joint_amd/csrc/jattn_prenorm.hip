@@ -15,25 +15,29 @@ namespace jattn {
 // never read). Thread t covers chunks t%TPR + j*TPR of row t/TPR of each pass; rows are taken in
 // the joint (b, l, h) order. Two-stream variant (S): the key rows come from two blocks (rows
 // l < n0 from a.k, the rest from a.k1) and each is also multiplied by its block's K gain, since the
-// query side can no longer carry one K gain for every key.
+// query side can no longer carry one K gain for every key. Varlen variant (V): blockIdx.y is the
+// sequence and the rows are those of its (token, head) pairs, into the per-sequence workspace rows.
 constexpr int kPrenormPasses = 4;
 
-template <int D, bool S>
+template <int D, bool S, bool V>
 __global__ __launch_bounds__(kThreads) void prenorm_kernel(PrenormArgs a) {
   using Dm = Dims<D>;
   const int tid = threadIdx.x, rr = tid / Dm::TPR, cc = tid % Dm::TPR;
-  const int L = a.L, H = a.H;
-  const int total = a.B * L * H;
+  const int H = a.H;
+  const SeqGeom<V> seq(a.cu_seqlens, blockIdx.y, a.L, a.total, a.L);
+  const int L = seq.L;
+  // rows of this launch: all B * L * H rows (fixed length) or the L * H rows of sequence blockIdx.y
+  const int total = V ? L * H : a.B * L * H;
   u32x4 x[kPrenormPasses][Dm::CPT];
   int row[kPrenormPasses];
 #pragma unroll
   for (int p = 0; p < kPrenormPasses; ++p) {
-    row[p] = (blockIdx.x * kPrenormPasses + p) * Dm::RPP + rr;  // joint row (b * L + l) * H + h
-    const uint16_t* src = a.k + (size_t)row[p] * D;
+    row[p] = (blockIdx.x * kPrenormPasses + p) * Dm::RPP + rr;  // (b * L + l) * H + h, or l * H + h (V)
+    const uint16_t* src = a.k + ((size_t)seq.start * H + row[p]) * D;
     if constexpr (S) {
       const int R = row[p] < total ? row[p] : 0;
       const int bl = R / H, h = R - bl * H, b = bl / L, l = bl - b * L;
-      src = RowMap<true>(b, h, L, H, D, a.n0).row(a.k, a.k1, l);
+      src = RowMap<true>((size_t)b * a.n0, (size_t)b * (L - a.n0), h, H, D, a.n0).row(a.k, a.k1, l);
     }
 #pragma unroll
     for (int j = 0; j < Dm::CPT; ++j) {
@@ -51,10 +55,10 @@ __global__ __launch_bounds__(kThreads) void prenorm_kernel(PrenormArgs a) {
     const float r = rsqrtf(ss * (1.0f / D) + a.eps);
     const int R = row[p];
     if (R >= total) continue;
-    const int bl = R / H, h = R - bl * H, b = bl / L, l = bl - b * L;
-    const int n = a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
+    const int bl = R / H, h = R - bl * H, b = V ? (int)blockIdx.y : bl / L, l = V ? bl : bl - b * L;
+    const int n = !V && a.valid_len ? min(max(a.valid_len[b], 0), L) : L;
     if (l >= n) continue;
-    uint16_t* dst = a.kr + (((size_t)b * H + h) * L + l) * D;
+    uint16_t* dst = a.kr + (V ? seq.row0(h, H) + l : ((size_t)b * H + h) * L + l) * D;
     const float* gk = a.gains + (l < a.n0 ? 0 : 2 * D) + D;  // (two-stream only)
 #pragma unroll
     for (int j = 0; j < Dm::CPT; ++j) {
@@ -82,27 +86,33 @@ hipError_t persistent_grid(const void* kernel, int items, int threads, int* grid
   return hipSuccess;
 }
 
-template <int D, bool S>
+template <int D, bool S, bool V>
 static hipError_t launch_prenorm_d(const PrenormArgs& a, hipStream_t stream) {
   const int rows = Dims<D>::RPP * kPrenormPasses;
-  const int blocks = (int)(((int64_t)a.B * a.L * a.H + rows - 1) / rows);
-  hipLaunchKernelGGL((prenorm_kernel<D, S>), dim3(blocks), dim3(kThreads), 0, stream, a);
+  // (varlen: one row of blocks per sequence, each sized for the longest sequence a.L)
+  const int64_t per = V ? (int64_t)a.L * a.H : (int64_t)a.B * a.L * a.H;
+  const int blocks = (int)((per + rows - 1) / rows);
+  hipLaunchKernelGGL((prenorm_kernel<D, S, V>), dim3(blocks, V ? a.B : 1), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <bool S>
+template <bool S, bool V>
 static hipError_t launch_prenorm_s(int D, const PrenormArgs& a, hipStream_t stream) {
   switch (D) {
-    case 32: return launch_prenorm_d<32, S>(a, stream);
-    case 64: return launch_prenorm_d<64, S>(a, stream);
-    case 72: return launch_prenorm_d<72, S>(a, stream);
-    case 128: return launch_prenorm_d<128, S>(a, stream);
+    case 32: return launch_prenorm_d<32, S, V>(a, stream);
+    case 64: return launch_prenorm_d<64, S, V>(a, stream);
+    case 72: return launch_prenorm_d<72, S, V>(a, stream);
+    case 128: return launch_prenorm_d<128, S, V>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_prenorm(int D, bool streams, const PrenormArgs& a, hipStream_t stream) {
-  return streams ? launch_prenorm_s<true>(D, a, stream) : launch_prenorm_s<false>(D, a, stream);
+hipError_t launch_prenorm(int D, Variant var, const PrenormArgs& a, hipStream_t stream) {
+  switch (var) {
+    case kStreams: return launch_prenorm_s<true, false>(D, a, stream);
+    case kVarlen: return launch_prenorm_s<false, true>(D, a, stream);
+    default: return launch_prenorm_s<false, false>(D, a, stream);
+  }
 }
 
 }  // namespace jattn

@@ -28,6 +28,19 @@ Recipe (all on CPU, one ``torch.Generator`` seeded with ``seed``, in this order)
 3. gains = ``1 + 0.1 * randn(2, D)`` fp32 (row 0 for Q, row 1 for K).
 4. dout = ``randn(B, L, H, D).bfloat16()``.
 5. two-stream inputs only: per-stream gains = ``1 + 0.1 * randn(2, 2, D)`` fp32 ([stream][Q, K]).
+
+Packed variable-length inputs (sequences back to back, [total, H, D], ``cu_seqlens`` offsets):
+
+* ``varlen_ragged``   - the ``ragged`` workload without its padding: sequence b is rows
+                        [0, valid_len[b]) of that workload's sequence b (same seed-0 draws).
+* ``varlen_multires`` - B16 H12 D64 (the 512px model's heads), a multi-resolution batch: each
+                        sample's image is a square of 256, 384, 512, 640 or 768 px (patch-2 tokens
+                        of the 8x latent: 256, 576, 1024, 1600, 2304 tokens) followed by 1..77 text
+                        tokens (re-diffusion README: aspect buckets at 512 base resolution, with
+                        multi-resolution batching named as future work). Recipe: image size index
+                        ``randint(0, 5, (B,))``, text length ``randint(1, 78, (B,))``, then q, k, v =
+                        ``randn(total, H, D)`` bf16 each, gains ``1 + 0.1 * randn(2, D)``, dout
+                        ``randn(total, H, D)`` bf16.
 Text tokens sit at positions N_img .. L-1 (image first, text last). The two-stream inputs are the
 same q, k, v and dout split along the token axis into an image part [B, N_img, H, D] and a text
 part [B, N_txt, H, D] (each its own contiguous tensor).
@@ -159,3 +172,75 @@ def flops(B: int, L: int, H: int, D: int, valid_len=None) -> dict:
     fwd = 4.0 * H * D * pairs
     return dict(fwd=fwd, bwd=2.5 * fwd, total=3.5 * fwd,
                 fwd_padded=4.0 * B * H * L * L * D)
+
+
+# ------------------------------------------------------------------------------------------------
+# Packed variable-length inputs
+
+MULTIRES_IMG_TOKENS = (256, 576, 1024, 1600, 2304)  # 256 .. 768 px squares, 16 px per token
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    B: int
+    H: int
+    D: int
+
+
+VARLEN_WORKLOADS: Dict[str, VarlenWorkload] = {
+    "varlen_ragged": VarlenWorkload("varlen_ragged", B=2, H=24, D=128),
+    "varlen_multires": VarlenWorkload("varlen_multires", B=16, H=12, D=64),
+}
+
+
+def _pack(seqs):
+    return torch.cat(seqs, dim=0).contiguous()
+
+
+def make_varlen_inputs(workload: str, seed: int = 0) -> dict:
+    """Packed inputs of a named variable-length workload. Returns CPU tensors q, k, v, dout bf16
+    [total, H, D]; gains fp32 [2, D]; cu_seqlens int32 [B + 1]; plus lengths, max_seqlen, scale, eps
+    and the workload."""
+    w = VARLEN_WORKLOADS[workload]
+    if workload == "varlen_ragged":
+        d = make_inputs("ragged", seed=seed)
+        lengths = d["valid_len"].tolist()
+        t = {k: _pack([d[k][b, :n] for b, n in enumerate(lengths)]) for k in ("q", "k", "v", "dout")}
+        gains = d["gains"]
+    else:
+        g = torch.Generator().manual_seed(seed)
+        size = torch.randint(0, len(MULTIRES_IMG_TOKENS), (w.B,), generator=g)
+        txt = torch.randint(1, 78, (w.B,), generator=g)
+        lengths = [MULTIRES_IMG_TOKENS[int(i)] + int(n) for i, n in zip(size, txt)]
+        total = sum(lengths)
+        qkv = [torch.randn(total, w.H, w.D, generator=g).bfloat16() for _ in range(3)]
+        gains = (1.0 + 0.1 * torch.randn(2, w.D, generator=g)).float()
+        dout = torch.randn(total, w.H, w.D, generator=g).bfloat16()
+        t = dict(q=qkv[0], k=qkv[1], v=qkv[2], dout=dout)
+    cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int32)
+    return dict(q=t["q"], k=t["k"], v=t["v"], dout=t["dout"], gains=gains, cu_seqlens=cu, lengths=lengths,
+                max_seqlen=max(lengths), scale=default_scale(w.D), eps=EPS, workload=w)
+
+
+def make_shape_varlen_inputs(lengths, H: int, D: int, seed: int = 0, scale: Optional[float] = None,
+                             eps: float = EPS, gain_std: float = 0.1) -> dict:
+    """Packed inputs of given sequence lengths (edge-case tests): q, k, v = randn(total, H, D) bf16,
+    gains 1 + gain_std * randn(2, D), dout randn bf16, in that order."""
+    g = torch.Generator().manual_seed(seed)
+    total = int(sum(lengths))
+    qkv = [torch.randn(total, H, D, generator=g).bfloat16() for _ in range(3)]
+    gains = (1.0 + gain_std * torch.randn(2, D, generator=g)).float()
+    dout = torch.randn(total, H, D, generator=g).bfloat16()
+    cu = torch.tensor([0] + list(torch.tensor(list(lengths)).cumsum(0).tolist()), dtype=torch.int32)
+    w = VarlenWorkload(f"varlen{list(lengths)}H{H}D{D}", B=len(lengths), H=H, D=D)
+    return dict(q=qkv[0], k=qkv[1], v=qkv[2], dout=dout, gains=gains, cu_seqlens=cu, lengths=list(lengths),
+                max_seqlen=max(max(lengths), 1), scale=default_scale(D) if scale is None else float(scale), eps=eps,
+                workload=w)
+
+
+def varlen_flops(lengths, H: int, D: int) -> dict:
+    """Algorithmic FLOPs of a packed batch: 4*D per (query, key) pair of each sequence, backward 2.5x."""
+    pairs = sum(int(n) * int(n) for n in lengths)
+    fwd = 4.0 * H * D * pairs
+    return dict(fwd=fwd, bwd=2.5 * fwd, total=3.5 * fwd)

@@ -9,6 +9,11 @@ Two-stream functions (``*_streams``): each per-token tensor is an (image, text) 
 [B, N_img, H, D] and [B, N_txt, H, D] (the joint sequence is image rows then text rows, L = N_img +
 N_txt); gains fp32 [2, 2, D] (gains[s, 0] = Q gain, gains[s, 1] = K gain of stream s, image = 0);
 valid_len and lse as above, over the joint sequence.
+
+Packed variable-length functions (``*_varlen``): q, k, v, out, dout, dq, dk, dv are bf16 [total, H, D]
+with sequence b at rows cu_seqlens[b] .. cu_seqlens[b+1]-1 (cu_seqlens int32 [B + 1] on the device);
+each sequence attends only to itself. lse is fp32 [total * H]: sequence b, head h, row l at
+cu_seqlens[b] * H + h * L_b + l. max_seqlen (a Python int) bounds the sequence lengths.
 """
 from __future__ import annotations
 
@@ -21,7 +26,8 @@ import torch
 from . import _lib
 
 __all__ = ["forward", "backward", "workspace_bytes", "fwd_workspace_bytes", "JointAttention", "joint_attention",
-           "forward_streams", "backward_streams", "JointAttentionStreams", "joint_attention_streams"]
+           "forward_streams", "backward_streams", "JointAttentionStreams", "joint_attention_streams",
+           "forward_varlen", "backward_varlen", "JointAttentionVarlen", "joint_attention_varlen"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -250,3 +256,87 @@ class JointAttentionStreams(torch.autograd.Function):
 def joint_attention_streams(q, k, v, gains, valid_len=None, scale=None, eps=1e-6):
     """Two-stream joint attention with autograd: q, k, v as (image, text) pairs; returns (out_img, out_txt)."""
     return JointAttentionStreams.apply(q[0], q[1], k[0], k[1], v[0], v[1], gains, valid_len, scale, eps)
+
+
+# ------------------------------------------------------------------------------------------------
+# Packed variable-length entry points
+
+def _check_varlen(q, k, v, gains, cu_seqlens, max_seqlen):
+    if q.dim() != 3:
+        raise ValueError("q must be [total, H, D]")
+    total, H, D = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.bfloat16, (total, H, D), dev)
+    _check_tensor("gains", gains, torch.float32, (2, D), dev)
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be an int32 [B + 1] tensor")
+    B = cu_seqlens.numel() - 1
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32, (B + 1,), dev)
+    if int(max_seqlen) < 1:
+        raise ValueError("max_seqlen must be >= 1")
+    return B, total, H, D
+
+
+def forward_varlen(q, k, v, gains, cu_seqlens, max_seqlen: int, scale: Optional[float] = None, eps: float = 1e-6,
+                   return_workspace: bool = False):
+    """Packed variable-length joint attention forward. Returns (out bf16 [total, H, D], lse fp32 [total * H]),
+    plus the forward workspace if return_workspace."""
+    B, total, H, D = _check_varlen(q, k, v, gains, cu_seqlens, max_seqlen)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = torch.empty_like(q)
+    lse = torch.empty(total * H, dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    workspace = torch.empty(max(int(lib.jattn_varlen_fwd_workspace_bytes(B, int(max_seqlen), total, H, D)), 1),
+                            dtype=torch.uint8, device=q.device)
+    st = lib.jattn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(gains), _ptr(cu_seqlens), B, int(max_seqlen), total, H,
+                              D, ctypes.c_float(scale), ctypes.c_float(eps), _ptr(out), _ptr(lse), _ptr(workspace),
+                              workspace.numel(), None, 0, _stream(q))
+    _lib.check("jattn_fwd_varlen", st)
+    return (out, lse, workspace) if return_workspace else (out, lse)
+
+
+def backward_varlen(q, k, v, gains, cu_seqlens, max_seqlen: int, out, lse, dout, scale: Optional[float] = None,
+                    eps: float = 1e-6, fwd_workspace=None):
+    """Packed variable-length joint attention backward. Returns (dq, dk, dv bf16 [total, H, D], dgains fp32 [2, D])."""
+    B, total, H, D = _check_varlen(q, k, v, gains, cu_seqlens, max_seqlen)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q.device
+    _check_tensor("out", out, torch.bfloat16, (total, H, D), dev)
+    _check_tensor("dout", dout, torch.bfloat16, (total, H, D), dev)
+    _check_tensor("lse", lse, torch.float32, (total * H,), dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dgains = torch.empty(2, D, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    workspace = torch.empty(max(int(lib.jattn_varlen_bwd_workspace_bytes(B, int(max_seqlen), total, H, D)), 1),
+                            dtype=torch.uint8, device=dev)
+    st = lib.jattn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(gains), _ptr(cu_seqlens), _ptr(out), _ptr(lse),
+                              _ptr(dout), B, int(max_seqlen), total, H, D, ctypes.c_float(scale), ctypes.c_float(eps),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgains), _ptr(workspace), workspace.numel(),
+                              _ptr(fwd_workspace), None, 0, _stream(q))
+    _lib.check("jattn_bwd_varlen", st)
+    return dq, dk, dv, dgains
+
+
+class JointAttentionVarlen(torch.autograd.Function):
+    """Autograd wrapper of the packed variable-length entry points."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, gains, cu_seqlens, max_seqlen, scale=None, eps=1e-6):
+        out, lse, ws = forward_varlen(q, k, v, gains, cu_seqlens, max_seqlen, scale, eps, return_workspace=True)
+        ctx.save_for_backward(q, k, v, gains, cu_seqlens, out, lse, ws)
+        ctx.max_seqlen, ctx.scale, ctx.eps = max_seqlen, scale, eps
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, gains, cu, out, lse, ws = ctx.saved_tensors
+        dq, dk, dv, dg = backward_varlen(q, k, v, gains, cu, ctx.max_seqlen, out, lse,
+                                         dout.to(torch.bfloat16).contiguous(), ctx.scale, ctx.eps, fwd_workspace=ws)
+        return dq, dk, dv, dg, None, None, None, None
+
+
+def joint_attention_varlen(q, k, v, gains, cu_seqlens, max_seqlen, scale=None, eps=1e-6):
+    return JointAttentionVarlen.apply(q, k, v, gains, cu_seqlens, max_seqlen, scale, eps)

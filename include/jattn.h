@@ -170,6 +170,44 @@ jattn_status jattn_bwd_streams(const void* const q[2], const void* const k[2], c
                                void* workspace, size_t workspace_bytes, const void* fwd_workspace,
                                const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------------------
+ * Packed variable-length entry points (no padding: sequences of different lengths back to back).
+ *
+ * The diffusion-pipe summary's attention wrapper has a variable-length path besides the padded one;
+ * mixed caption lengths and multi-resolution buckets (the re-diffusion README's aspect buckets) give
+ * such batches. Here B sequences are stored back to back: q, k, v, out, dout, dq, dk, dv are bf16
+ * [total, H, D] with sequence b at token rows [cu_seqlens[b], cu_seqlens[b+1]). Each sequence attends
+ * only to itself, with all of its keys valid, and gets exactly the joint attention above (one gain
+ * pair gains fp32 [2, D], as jattn_fwd).
+ *   cu_seqlens  int32 [B + 1] on the DEVICE, non-decreasing, cu_seqlens[0] = 0, cu_seqlens[B] <= total.
+ *               Device data is not validated, but every access stays inside the tensors: sequence b
+ *               is taken as rows [start, end) with start = clamp(cu[b], 0, total) and end =
+ *               clamp(cu[b+1], start, min(total, start + max_seqlen)); rows not covered by any
+ *               sequence are left unwritten, and overlapping sequences give undefined results.
+ *   max_seqlen  the longest sequence (an upper bound on cu[b+1] - cu[b]); sizes the grids.
+ *   total       token rows of the tensors (>= 1).
+ *   lse         fp32, total * H elements: sequence b, head h, row l at cu[b] * H + h * L_b + l (one
+ *               [H, L_b] block per sequence; a fixed-length batch gives exactly [B, H, L]).
+ *   dgains      fp32 [2, D], summed over all sequences.
+ * Workspace sizes: jattn_varlen_fwd_workspace_bytes and jattn_varlen_bwd_workspace_bytes; stages and
+ * events as jattn_fwd_ex / jattn_bwd_ex (pass NULL, 0 for none). Errors as for the joint entry points;
+ * NULL cu_seqlens or total < 1 -> INVALID_VALUE; B > 65535 -> NOT_SUPPORTED. */
+size_t jattn_varlen_fwd_workspace_bytes(int B, int max_seqlen, int total, int H, int D);
+size_t jattn_varlen_bwd_workspace_bytes(int B, int max_seqlen, int total, int H, int D);
+
+jattn_status jattn_fwd_varlen(const void* q, const void* k, const void* v, const float* gains,
+                              const int32_t* cu_seqlens, int B, int max_seqlen, int total, int H, int D,
+                              float softmax_scale, float eps, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes,
+                              const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
+
+jattn_status jattn_bwd_varlen(const void* q, const void* k, const void* v, const float* gains,
+                              const int32_t* cu_seqlens, const void* out, const float* lse, const void* dout,
+                              int B, int max_seqlen, int total, int H, int D, float softmax_scale, float eps,
+                              void* dq, void* dk, void* dv, float* dgains,
+                              void* workspace, size_t workspace_bytes, const void* fwd_workspace,
+                              const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* jattn_status_string(jattn_status s);
 

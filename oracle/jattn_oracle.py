@@ -40,7 +40,7 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["rmsnorm", "head_forward", "head_backward", "attention_forward", "attention_backward",
-           "attention_fwd_bwd", "streams_fwd_bwd"]
+           "attention_fwd_bwd", "streams_fwd_bwd", "varlen_fwd_bwd"]
 
 
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> Tuple[np.ndarray, np.ndarray]:
@@ -215,3 +215,41 @@ def streams_fwd_bwd(q, k, v, gains, dout, valid_len=None, scale: float = None, e
             dg[s, 1] += tk[rows].sum(axis=0)
     split = lambda t: (t[:, :n_img], t[:, n_img:])
     return dict(out=split(out), lse=lse, dq=split(dq), dk=split(dk), dv=split(dv), dgains=dg)
+
+
+# ------------------------------------------------------------------------------------------------
+# Packed variable-length form. [DP]'s attention wrapper has a variable-length path beside the padded
+# one: sequences of different lengths stored back to back, each attending only to itself. Sequence b
+# holds rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of the [total, H, D] tensors; all of its keys are
+# valid.
+
+def varlen_fwd_bwd(q, k, v, gains, dout, cu_seqlens, scale: float = None, eps: float = 1e-6,
+                   seqs: Optional[Sequence[int]] = None) -> dict:
+    """q, k, v, dout: [total, H, D]; gains [2, D]; cu_seqlens: B + 1 non-decreasing offsets starting at
+    0. Runs the joint attention on every sequence separately. Returns out, dq, dk, dv [total, H, D]
+    (NaN on rows of sequences not computed), lse as a list of [H, L_b] arrays (None for sequences not
+    computed) and dgains [2, D] summed over the computed sequences. ``seqs`` limits the work to those
+    sequences."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    gains = np.asarray(gains, dtype=np.float64)
+    cu = [int(c) for c in cu_seqlens]
+    B = len(cu) - 1
+    total, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out, dq, dk, dv = (np.full((total, H, D), np.nan) for _ in range(4))
+    lse = [None] * B
+    dg = np.zeros((2, D))
+    for b in (range(B) if seqs is None else seqs):
+        r0, r1 = cu[b], cu[b + 1]
+        n = r1 - r0
+        lse[b] = np.zeros((H, n))
+        for h in range(H):
+            Q, K, V, dO = q[r0:r1, h], k[r0:r1, h], v[r0:r1, h], dout[r0:r1, h]
+            f = head_forward(Q, K, V, gains[0], gains[1], n, scale, eps)
+            dQ, dK, dV, dgq, dgk, _ = head_backward(Q, K, V, gains[0], gains[1], dO, n, scale, eps, fwd=f)
+            out[r0:r1, h], lse[b][h] = f["O"], f["lse"]
+            dq[r0:r1, h], dk[r0:r1, h], dv[r0:r1, h] = dQ, dK, dV
+            dg[0] += dgq
+            dg[1] += dgk
+    return dict(out=out, lse=lse, dq=dq, dk=dk, dv=dv, dgains=dg)

@@ -8,7 +8,8 @@ compare against the stored values.
     python tests/golden/make_golden.py [workload ...]
 
 A name "streams:<workload>" stores the two-stream form instead (dgains_streams_<workload>.json): the
-same seed-0 workload split into image and text tensors with a QK-norm gain pair per stream.
+same seed-0 workload split into image and text tensors with a QK-norm gain pair per stream. A
+packed variable-length workload name (varlen_*) stores that workload's gain gradients.
 """
 import json
 import os
@@ -21,10 +22,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
-from diffusion_transformer_joint_amd.inputs import make_inputs, make_stream_inputs  # noqa: E402
-from oracle import attention_fwd_bwd, streams_fwd_bwd  # noqa: E402
+from diffusion_transformer_joint_amd.inputs import make_inputs, make_stream_inputs, make_varlen_inputs  # noqa: E402
+from oracle import attention_fwd_bwd, streams_fwd_bwd, varlen_fwd_bwd  # noqa: E402
 
-FULL = ["mmdit512", "dit256", "mmdit768", "ragged", "streams:mmdit512"]
+FULL = ["mmdit512", "dit256", "mmdit768", "ragged", "streams:mmdit512", "varlen_multires", "varlen_ragged"]
 
 
 def f64(t):
@@ -49,10 +50,27 @@ def streams(name):
     print(f"streams:{name}: {time.time() - t0:.1f} s", flush=True)
 
 
+def varlen(name):
+    t0 = time.time()
+    inp = make_varlen_inputs(name, seed=0)
+    r = varlen_fwd_bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), inp["gains"].double().numpy(), f64(inp["dout"]),
+                       inp["cu_seqlens"].tolist(), inp["scale"], inp["eps"])
+    w = inp["workload"]
+    rec = dict(workload=name, form="packed variable-length", seed=0, B=w.B, H=w.H, D=w.D, lengths=inp["lengths"],
+               scale=inp["scale"], eps=inp["eps"], source="oracle/jattn_oracle.py varlen_fwd_bwd, fp64, all sequences",
+               dgains=np.asarray(r["dgains"]).tolist())
+    with open(os.path.join(HERE, f"dgains_{name}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"{name}: {time.time() - t0:.1f} s", flush=True)
+
+
 def main(names):
     for name in names:
         if name.startswith("streams:"):
             streams(name.split(":", 1)[1])
+            continue
+        if name.startswith("varlen_"):
+            varlen(name)
             continue
         t0 = time.time()
         inp = make_inputs(name, seed=0)

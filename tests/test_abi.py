@@ -267,3 +267,65 @@ def bwd_streams(lib, **kw):
 ])
 def test_bwd_streams_rejects(lib, kw, expect):
     assert bwd_streams(lib, **kw) == expect
+
+
+# ------------------------------------------------------------------------------------------------
+# Packed variable-length entry points
+def fwd_varlen(lib, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gains=fake(3), cu=fake(4), B=3, maxlen=100, total=250, H=3, D=64,
+             scale=0.125, eps=1e-6, out=fake(5), lse=fake(6), ws=fake(7), ws_bytes=None, events=None, n_events=0)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = lib.jattn_varlen_fwd_workspace_bytes(a["B"], a["maxlen"], a["total"], a["H"], a["D"])
+    return lib.jattn_fwd_varlen(a["q"], a["k"], a["v"], a["gains"], a["cu"], a["B"], a["maxlen"], a["total"], a["H"],
+                                a["D"], ctypes.c_float(a["scale"]), ctypes.c_float(a["eps"]), a["out"], a["lse"],
+                                a["ws"], a["ws_bytes"], a["events"], a["n_events"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(cu=None), _lib.INVALID_VALUE),
+    (dict(q=None), _lib.INVALID_VALUE),
+    (dict(total=0), _lib.INVALID_VALUE),
+    (dict(maxlen=0), _lib.INVALID_VALUE),
+    (dict(B=0), _lib.INVALID_VALUE),
+    (dict(D=40), _lib.NOT_SUPPORTED),
+    (dict(B=70000), _lib.NOT_SUPPORTED),
+    (dict(cu=fake(4) + 2), _lib.INVALID_VALUE),           # misaligned offsets
+    (dict(out=fake(0)), _lib.INVALID_VALUE),              # out aliases q
+    (dict(lse=fake(4)), _lib.INVALID_VALUE),              # lse aliases cu_seqlens
+    (dict(ws=None), _lib.WORKSPACE),
+    (dict(ws_bytes=100), _lib.WORKSPACE),
+    (dict(ws=fake(7) + 32), _lib.INVALID_VALUE),
+    (dict(n_events=3), _lib.INVALID_VALUE),
+])
+def test_fwd_varlen_rejects(lib, kw, expect):
+    assert fwd_varlen(lib, **kw) == expect
+
+
+def test_bwd_varlen_rejects(lib):
+    need = lib.jattn_varlen_bwd_workspace_bytes(3, 100, 250, 3, 64)
+    base = dict(q=fake(0), k=fake(1), v=fake(2), gains=fake(3), cu=fake(4), out=fake(5), lse=fake(6), dout=fake(7),
+                dq=fake(8), dk=fake(9), dv=fake(10), dgains=fake(11), ws=fake(12), ws_bytes=need, fws=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.jattn_bwd_varlen(a["q"], a["k"], a["v"], a["gains"], a["cu"], a["out"], a["lse"], a["dout"], 3, 100,
+                                    250, 3, 64, ctypes.c_float(0.125), ctypes.c_float(1e-6), a["dq"], a["dk"], a["dv"],
+                                    a["dgains"], a["ws"], a["ws_bytes"], a["fws"], None, 0, None)
+    assert call(cu=None) == _lib.INVALID_VALUE
+    assert call(dgains=None) == _lib.INVALID_VALUE
+    assert call(dq=fake(7)) == _lib.INVALID_VALUE       # dq aliases dout
+    assert call(dk=fake(4)) == _lib.INVALID_VALUE       # dk aliases cu_seqlens
+    assert call(ws_bytes=need - 1) == _lib.WORKSPACE
+    assert call(fws=fake(12)) == _lib.INVALID_VALUE     # workspace aliases the forward workspace
+
+
+def test_varlen_workspace_bytes(lib):
+    assert lib.jattn_varlen_fwd_workspace_bytes(2, 10, 0, 1, 64) == 0
+    assert lib.jattn_varlen_fwd_workspace_bytes(2, 10, 15, 1, 40) == 0
+    f = lib.jattn_varlen_fwd_workspace_bytes(16, 2370, 22682, 12, 64)
+    assert f >= 22682 * 12 * 64 * 2 and f % 256 == 0
+    w = lib.jattn_varlen_bwd_workspace_bytes(16, 2370, 22682, 12, 64)
+    # two bf16 row copies, two statistics per (row, head) with 128 rows of slack per sequence, gain partials
+    assert w >= 2 * 22682 * 12 * 64 * 2 + 2 * (22682 + 128 * 16) * 12 * 4 + 16 * 12 * 19 * 64 * 4

@@ -59,3 +59,15 @@ def test_stream_inputs_split_the_joint_draw():
         assert torch.equal(torch.cat([img, txt], dim=1), a[key])
     assert b["gains"].shape == (2, 2, 32) and b["gains"].dtype == torch.float32
     assert not torch.equal(b["gains"][0], b["gains"][1])
+
+
+def test_varlen_inputs():
+    from diffusion_transformer_joint_amd.inputs import make_varlen_inputs, MULTIRES_IMG_TOKENS
+    r = make_varlen_inputs("varlen_ragged")
+    p = make_inputs("ragged")
+    assert r["lengths"] == p["valid_len"].tolist() == [4269, 4144]
+    assert r["cu_seqlens"].tolist() == [0, 4269, 8413] and r["cu_seqlens"].dtype == torch.int32
+    assert torch.equal(r["q"][4269:], p["q"][1, :4144]) and torch.equal(r["dout"][:4269], p["dout"][0, :4269])
+    m = make_varlen_inputs("varlen_multires")
+    assert m["q"].shape == (sum(m["lengths"]), 12, 64) and m["max_seqlen"] == max(m["lengths"])
+    assert all(1 <= n - t <= 77 for n in m["lengths"] for t in [max(x for x in MULTIRES_IMG_TOKENS if x < n)])
