@@ -451,10 +451,6 @@ def cpu_baseline(inp, seconds):
             "seconds": round(dt, 2), "pairs": done}
 
 
-if __name__ == "__main__":
-    main()
-
-
 def cpu_baseline_varlen(inp, seconds, threads, varlen_fwd_bwd):
     """The fp64 variable-length oracle on the first sequences of the same packed inputs, time-bounded."""
     import torch
@@ -475,3 +471,7 @@ def cpu_baseline_varlen(inp, seconds, threads, varlen_fwd_bwd):
             "sample": f"fp64 numpy oracle (varlen_fwd_bwd) fwd+bwd on the first {done} of {w.B} sequences of the "
                       f"same seed-0 packed inputs, {dt:.1f} s wall; BLAS threads = cores",
             "seconds": round(dt, 2), "sequences": done}
+
+
+if __name__ == "__main__":
+    main()
