@@ -19,6 +19,9 @@ flow. [DP] = the diffusion-pipe repository summary (tdrussell/diffusion-pipe).
   one (batch, head) pair at a time: S = scale * Qn Kn^T, P = softmax(S), O = P V.
 * Key padding: keys at positions >= valid_len[b] are excluded from the softmax ([DP], the attention
   wrapper's varlen path). Padded query rows are still computed over the valid keys.
+* Local window (optional): query i sees only keys i - left <= j <= i + right ([DP], the wrapper's
+  windowed attention; the bounds are read as those of a sliding window, a negative bound meaning
+  none). A row with no key left gets O = 0, LSE = -inf and zero gradients, as with valid_len 0.
 
 Readings where the pages are silent (each one is listed in the design document):
   eps sits inside the square root, rms = sqrt(mean(x^2) + eps); the softmax scale multiplies the
@@ -57,14 +60,18 @@ def _valid_keys(valid_len, b: int, L: int) -> int:
 
 
 def head_forward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, gq: np.ndarray, gk: np.ndarray,
-                 n: int, scale: float, eps: float) -> dict:
+                 n: int, scale: float, eps: float, window: Optional[Tuple[int, int]] = None) -> dict:
     """One (batch, head) pair. Q, K, V: [L, D] fp64; n valid keys.
-    Returns the explicit intermediates: Qn, Kn, rq, rk, S (masked with -inf), P, O, lse."""
+    Returns the explicit intermediates: Qn, Kn, rq, rk, S (masked with -inf), P, O, lse.
+    window = (left, right): query i also sees only keys i - left <= j <= i + right (a negative bound
+    is no bound); a row left with no key gets P = 0, O = 0 and lse = -inf."""
     L = Q.shape[0]
     Qn, rq = rmsnorm(Q, gq, eps)
     Kn, rk = rmsnorm(K, gk, eps)
     S = scale * (Qn @ Kn.T)
     S[:, n:] = -np.inf
+    if window is not None:
+        return _windowed_softmax(Qn, Kn, rq, rk, S, V, n, window)
     if n == 0:
         P = np.zeros((L, L))
         O = np.zeros_like(V)
@@ -79,6 +86,29 @@ def head_forward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, gq: np.ndarray, gk
     return dict(Qn=Qn, Kn=Kn, rq=rq, rk=rk, S=S, P=P, O=O, lse=lse)
 
 
+def _windowed_softmax(Qn, Kn, rq, rk, S, V, n, window) -> dict:
+    """The softmax and PV product of head_forward under a local window: every row over its own set of
+    allowed keys, rows without one left at zero."""
+    L = S.shape[0]
+    left, right = window
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    allowed = j < n
+    if left >= 0:
+        allowed = allowed & (j >= i - left)
+    if right >= 0:
+        allowed = allowed & (j <= i + right)
+    S = np.where(allowed, S, -np.inf)
+    has = allowed.any(axis=1)
+    m = np.where(has, np.max(S, axis=1), 0.0)[:, None]
+    E = np.where(allowed, np.exp(S - m), 0.0)
+    den = E.sum(axis=1, keepdims=True)
+    P = np.where(has[:, None], E / np.where(den > 0, den, 1.0), 0.0)
+    O = P @ V
+    lse = np.where(has, m[:, 0] + np.log(np.where(has, den[:, 0], 1.0)), -np.inf)
+    return dict(Qn=Qn, Kn=Kn, rq=rq, rk=rk, S=S, P=P, O=O, lse=lse)
+
+
 def _rmsnorm_backward(x: np.ndarray, r: np.ndarray, g: np.ndarray, dxn: np.ndarray):
     """Gradient through xn = x * r * g for one set of rows: returns (dx, dg)."""
     D = x.shape[-1]
@@ -88,9 +118,10 @@ def _rmsnorm_backward(x: np.ndarray, r: np.ndarray, g: np.ndarray, dxn: np.ndarr
     return dx, dg
 
 
-def head_backward(Q, K, V, gq, gk, dO, n: int, scale: float, eps: float, fwd: Optional[dict] = None):
+def head_backward(Q, K, V, gq, gk, dO, n: int, scale: float, eps: float, fwd: Optional[dict] = None,
+                  window: Optional[Tuple[int, int]] = None):
     """Analytic backward for one (batch, head) pair. Returns (dQ, dK, dV, dgq, dgk, extras)."""
-    f = head_forward(Q, K, V, gq, gk, n, scale, eps) if fwd is None else fwd
+    f = head_forward(Q, K, V, gq, gk, n, scale, eps, window) if fwd is None else fwd
     P = f["P"]
     dV = P.T @ dO
     dP = dO @ V.T
@@ -108,10 +139,10 @@ def _pairs(B: int, H: int, pairs: Optional[Iterable[Tuple[int, int]]]):
 
 
 def attention_forward(q, k, v, gains, valid_len=None, scale: float = None, eps: float = 1e-6,
-                      pairs: Optional[Sequence[Tuple[int, int]]] = None):
+                      pairs: Optional[Sequence[Tuple[int, int]]] = None, window: Optional[Tuple[int, int]] = None):
     """q, k, v: [B, L, H, D] (any float dtype, promoted to fp64); gains [2, D].
     Returns out [B, L, H, D] and lse [B, H, L] (natural log) in fp64. With ``pairs`` only those
-    (b, h) pairs are computed and the rest of the outputs is NaN."""
+    (b, h) pairs are computed and the rest of the outputs is NaN. ``window`` as in head_forward."""
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
     gains = np.asarray(gains, dtype=np.float64)
     B, L, H, D = q.shape
@@ -121,28 +152,29 @@ def attention_forward(q, k, v, gains, valid_len=None, scale: float = None, eps: 
     lse = np.full((B, H, L), np.nan)
     for b, h in _pairs(B, H, pairs):
         f = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], gains[0], gains[1],
-                         _valid_keys(valid_len, b, L), scale, eps)
+                         _valid_keys(valid_len, b, L), scale, eps, window)
         out[b, :, h] = f["O"]
         lse[b, h] = f["lse"]
     return out, lse
 
 
 def attention_backward(q, k, v, gains, dout, valid_len=None, scale: float = None, eps: float = 1e-6,
-                       pairs: Optional[Sequence[Tuple[int, int]]] = None):
+                       pairs: Optional[Sequence[Tuple[int, int]]] = None, window: Optional[Tuple[int, int]] = None):
     """Gradients of sum(out * dout). Returns dq, dk, dv [B, L, H, D] and dgains [2, D] (fp64).
     With ``pairs`` the per-token gradients outside those pairs are NaN and dgains sums over the
     chosen pairs only."""
-    return _fwd_bwd(q, k, v, gains, dout, valid_len, scale, eps, pairs)[2:]
+    return _fwd_bwd(q, k, v, gains, dout, valid_len, scale, eps, pairs, window)[2:]
 
 
 def attention_fwd_bwd(q, k, v, gains, dout, valid_len=None, scale: float = None, eps: float = 1e-6,
-                      pairs: Optional[Sequence[Tuple[int, int]]] = None) -> dict:
-    """Forward and backward in one pass over the (b, h) pairs."""
-    out, lse, dq, dk, dv, dg = _fwd_bwd(q, k, v, gains, dout, valid_len, scale, eps, pairs)
+                      pairs: Optional[Sequence[Tuple[int, int]]] = None,
+                      window: Optional[Tuple[int, int]] = None) -> dict:
+    """Forward and backward in one pass over the (b, h) pairs. ``window`` as in head_forward."""
+    out, lse, dq, dk, dv, dg = _fwd_bwd(q, k, v, gains, dout, valid_len, scale, eps, pairs, window)
     return dict(out=out, lse=lse, dq=dq, dk=dk, dv=dv, dgains=dg)
 
 
-def _fwd_bwd(q, k, v, gains, dout, valid_len, scale, eps, pairs):
+def _fwd_bwd(q, k, v, gains, dout, valid_len, scale, eps, pairs, window=None):
     q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
     gains = np.asarray(gains, dtype=np.float64)
     B, L, H, D = q.shape
@@ -155,7 +187,7 @@ def _fwd_bwd(q, k, v, gains, dout, valid_len, scale, eps, pairs):
     for b, h in _pairs(B, H, pairs):
         n = _valid_keys(valid_len, b, L)
         Q, K, V, dO = q[b, :, h], k[b, :, h], v[b, :, h], dout[b, :, h]
-        f = head_forward(Q, K, V, gains[0], gains[1], n, scale, eps)
+        f = head_forward(Q, K, V, gains[0], gains[1], n, scale, eps, window)
         dQ, dK, dV, dgq, dgk, _ = head_backward(Q, K, V, gains[0], gains[1], dO, n, scale, eps, fwd=f)
         out[b, :, h], lse[b, h] = f["O"], f["lse"]
         dq[b, :, h], dk[b, :, h], dv[b, :, h] = dQ, dK, dV
