@@ -12,6 +12,10 @@ workload, a QK-norm gain pair per stream: jattn_fwd_streams + jattn_bwd_streams)
 step they replace: concatenating the stream tensors, the joint forward and backward, and splitting
 the outputs and gradients back (`concat_split`).
 
+--variant window times the local-window entry points (jattn_fwd_window + jattn_bwd_window, window
+--window LEFT RIGHT, default 256 256; FLOPs over the (query, key) pairs the window allows) and beside
+them full attention on the same inputs (`full`).
+
 --variant varlen (with --workload varlen_multires or varlen_ragged) times the packed variable-length
 entry points (jattn_fwd_varlen + jattn_bwd_varlen; FLOPs over each sequence's own query-key pairs),
 and beside them the same sequences padded to the longest one through the joint entry points with a
@@ -41,7 +45,8 @@ def parse():
     ap.add_argument("--workload", default="mmdit512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--variant", choices=("joint", "streams", "varlen"), default="joint")
+    ap.add_argument("--variant", choices=("joint", "streams", "varlen", "window"), default="joint")
+    ap.add_argument("--window", type=int, nargs=2, default=(256, 256), metavar=("LEFT", "RIGHT"))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 512 MiB device-to-device three times: under rocprofv3 --pmc its "
                          "FETCH_SIZE / WRITE_SIZE give the counters' scale for a known byte count")
@@ -96,7 +101,7 @@ def main():
     from diffusion_transformer_joint_amd.inputs import (VARLEN_WORKLOADS, WORKLOADS, flops, make_inputs,
                                                         make_stream_inputs, make_varlen_inputs, varlen_flops)
 
-    streams, varlen = args.variant == "streams", args.variant == "varlen"
+    streams, varlen, windowed = args.variant == "streams", args.variant == "varlen", args.variant == "window"
     if varlen and args.workload not in VARLEN_WORKLOADS:
         args.workload = "varlen_multires"
     if varlen:
@@ -154,17 +159,29 @@ def main():
                     dout.data_ptr(), B, L, H, D, scale, eps, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                     dg.data_ptr(), ws.data_ptr(), ws_bytes, fws.data_ptr(), sp)
 
-        def fwd(events=None):
-            if events is None:
-                _lib.check("jattn_fwd", lib.jattn_fwd(*fwd_args))
-            else:
-                _lib.check("jattn_fwd_ex", lib.jattn_fwd_ex(*fwd_args[:-1], events, len(_lib.FWD_STAGES), sp))
+        if windowed:
+            wl, wr = args.window
+            fwd_w = fwd_args[:11] + (wl, wr) + fwd_args[11:-1]
+            bwd_w = bwd_args[:14] + (wl, wr) + bwd_args[14:-1]
 
-        def bwd(events=None, n=len(_lib.BWD_STAGES)):
-            if events is None:
-                _lib.check("jattn_bwd", lib.jattn_bwd(*bwd_args))
-            else:
-                _lib.check("jattn_bwd_ex", lib.jattn_bwd_ex(*bwd_args[:-1], events, n, sp))
+            def fwd(events=None):
+                _lib.check("jattn_fwd_window", lib.jattn_fwd_window(*fwd_w, events, 0 if events is None else
+                                                                    len(_lib.FWD_STAGES), sp))
+
+            def bwd(events=None, n=len(_lib.BWD_STAGES)):
+                _lib.check("jattn_bwd_window", lib.jattn_bwd_window(*bwd_w, events, 0 if events is None else n, sp))
+        else:
+            def fwd(events=None):
+                if events is None:
+                    _lib.check("jattn_fwd", lib.jattn_fwd(*fwd_args))
+                else:
+                    _lib.check("jattn_fwd_ex", lib.jattn_fwd_ex(*fwd_args[:-1], events, len(_lib.FWD_STAGES), sp))
+
+            def bwd(events=None, n=len(_lib.BWD_STAGES)):
+                if events is None:
+                    _lib.check("jattn_bwd", lib.jattn_bwd(*bwd_args))
+                else:
+                    _lib.check("jattn_bwd_ex", lib.jattn_bwd_ex(*bwd_args[:-1], events, n, sp))
     else:
         part = lambda t: tuple(x.to(dev) for x in t)
         q, k, v, dout = (part(inp[n]) for n in ("q", "k", "v", "dout"))
@@ -212,7 +229,7 @@ def main():
     K = args.steps
     # stage labels: the kernels' template instantiations, as a profiler names them
     sflag = "true" if streams else "false"
-    targs = f"{D}, {sflag}, {'true' if varlen else 'false'}"
+    targs = f"{D}, {sflag}, {'true' if varlen else 'false'}, {'true' if windowed else 'false'}"
     stages = [f"{n}<{targs}> (fwd)" if n == "prenorm_kernel" else f"{n}<{targs}>" for n in _lib.FWD_STAGES]
     stages += [f"{n}<{targs}> (bwd)" if n == "prenorm_kernel" else
                (f"{n}<{sflag}>" if n == "dg_reduce_kernel" else f"{n}<{targs}>") for n in _lib.BWD_STAGES]
@@ -261,9 +278,15 @@ def main():
                                          args.warmup)
     if varlen:
         padded = time_padded(lib, _lib, torch, inp, gains, B, L, H, D, stream, K, args.warmup)
+    full = None
+    if windowed:
+        full = time_steps(torch, stream, lambda: (_lib.check("jattn_fwd", lib.jattn_fwd(*fwd_args)),
+                                                   _lib.check("jattn_bwd", lib.jattn_bwd(*bwd_args))), K, args.warmup)
 
     vlist = None if inp.get("valid_len") is None else inp["valid_len"].tolist()
     fl = varlen_flops(inp["lengths"], H, D) if varlen else flops(B, L, H, D, vlist)
+    if windowed:
+        fl = window_flops(B, L, H, D, vlist, args.window)
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
     fwd_tflops = fl["fwd"] / (ms_fwd * 1e-3) / 1e12
     bwd_tflops = fl["bwd"] / (ms_bwd * 1e-3) / 1e12
@@ -317,6 +340,10 @@ def main():
     if concat_split is not None:
         res["concat_split"] = concat_split
         res["concat_split"]["speedup"] = round(concat_split["ms_per_step"] / ms_step, 4)
+    if windowed:
+        res["config"]["window"] = list(args.window)
+        res["full"] = {"ms_per_step": round(full, 5), "speedup": round(full / ms_step, 4),
+                       "what": "full attention (jattn_fwd + jattn_bwd) on the same inputs"}
     if padded is not None:
         res["padded"] = padded
         res["padded"]["speedup"] = round(padded["ms_per_step"] / ms_step, 4)
@@ -368,6 +395,36 @@ def time_concat_split(lib, _lib, torch, q, k, v, dout, gains, vl, B, L, H, D, in
     return {"ms_per_step": round(ms, 5),
             "what": "torch.cat of the q, k, v and dout parts + jattn_fwd + jattn_bwd + .contiguous() splits of "
                     "out, dq, dk, dv (same workload and stream)"}
+
+
+def time_steps(torch, stream, step, K, warmup):
+    """Average ms of `step` over K calls after a short warm-up, by events around all of them."""
+    for _ in range(min(warmup, 20)):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(K):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / K
+
+
+def window_flops(B, L, H, D, valid_len, window):
+    """Algorithmic FLOPs under a local window: 4*D per (query, key) pair the window and the key padding
+    allow, backward 2.5x."""
+    import numpy as np
+    left, right = window
+    i = np.arange(L)
+    lo = np.zeros(L, dtype=np.int64) if left < 0 else np.maximum(0, i - left)
+    pairs = 0
+    for b in range(B):
+        n = L if valid_len is None else max(0, min(L, int(valid_len[b])))
+        hi = np.full(L, n, dtype=np.int64) if right < 0 else np.minimum(n, i + right + 1)
+        pairs += int(np.maximum(0, hi - lo).sum())
+    fwd = 4.0 * H * D * pairs
+    return dict(fwd=fwd, bwd=2.5 * fwd, total=3.5 * fwd)
 
 
 def time_padded(lib, _lib, torch, inp, gains, B, L, H, D, stream, K, warmup):

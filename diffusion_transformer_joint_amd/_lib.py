@@ -17,9 +17,9 @@ SUCCESS, INVALID_VALUE, NOT_SUPPORTED, WORKSPACE, HIP = range(5)
 
 EXPORTED = ("jattn_fwd", "jattn_fwd_ex", "jattn_fwd_workspace_bytes", "jattn_bwd", "jattn_bwd_ex", "jattn_bwd_workspace_bytes",
             "jattn_fwd_streams", "jattn_bwd_streams", "jattn_varlen_fwd_workspace_bytes",
-            "jattn_varlen_bwd_workspace_bytes", "jattn_fwd_varlen", "jattn_bwd_varlen", "jattn_status_string",
-            "jattn_abi_version")
-ABI_VERSION = 5
+            "jattn_varlen_bwd_workspace_bytes", "jattn_fwd_varlen", "jattn_bwd_varlen", "jattn_fwd_window",
+            "jattn_bwd_window", "jattn_status_string", "jattn_abi_version")
+ABI_VERSION = 6
 FWD_STAGES = ("prenorm_kernel", "fwd_kernel")
 BWD_STAGES = ("prenorm_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "dg_reduce_kernel")
 
@@ -64,6 +64,11 @@ def load() -> ctypes.CDLL:
         lib.jattn_bwd_streams.restype = I
         lib.jattn_bwd_streams.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, F, P, P, P, P, P,
                                           ctypes.c_size_t, P, P, I, P]
+        lib.jattn_fwd_window.restype = I
+        lib.jattn_fwd_window.argtypes = [P, P, P, P, P, I, I, I, I, F, F, I, I, P, P, P, ctypes.c_size_t, P, I, P]
+        lib.jattn_bwd_window.restype = I
+        lib.jattn_bwd_window.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, F, I, I, P, P, P, P, P,
+                                         ctypes.c_size_t, P, P, I, P]
         lib.jattn_varlen_fwd_workspace_bytes.restype = ctypes.c_size_t
         lib.jattn_varlen_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
         lib.jattn_varlen_bwd_workspace_bytes.restype = ctypes.c_size_t

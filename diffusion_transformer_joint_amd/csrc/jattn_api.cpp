@@ -13,7 +13,7 @@ namespace {
 
 using jattn::kBwdRowsPerBlock;
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 bool supported_head_dim(int D) { return D == 32 || D == 64 || D == 72 || D == 128; }
 
@@ -88,7 +88,7 @@ jattn_status run_fwd(jattn::Variant var, const void* const q[2], const void* con
                      const float* gains, const int32_t* valid_len, const int32_t* cu_seqlens, int total, int B,
                      int L, int n0, int H, int D,
                      float softmax_scale, float eps, void* const out[2], float* lse, void* workspace,
-                     const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream) {
+                     const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream, int wl = 0, int wr = 0) {
   auto in = [](const void* p) { return static_cast<const uint16_t*>(p); };
   jattn::FwdArgs a;
   a.q = in(q[0]);
@@ -109,6 +109,8 @@ jattn_status run_fwd(jattn::Variant var, const void* const q[2], const void* con
   a.H = H;
   a.n0 = n0;
   a.total = total;
+  a.wl = wl;
+  a.wr = wr;
   a.c = softmax_scale * 1.4426950408889634f;
   a.eps = eps;
   a.nblk = (L + jattn::fwd_rows_per_block(D) - 1) / jattn::fwd_rows_per_block(D);
@@ -123,7 +125,7 @@ jattn_status run_bwd(jattn::Variant var, const void* const q[2], const void* con
                      int H, int D, float softmax_scale, float eps,
                      void* const dq[2], void* const dk[2], void* const dv[2], float* dgains, void* workspace,
                      const void* fwd_workspace, const hipEvent_t* stage_events, int n_stage_events,
-                     hipStream_t stream) {
+                     hipStream_t stream, int win_left = 0, int win_right = 0) {
   auto in = [](const void* p) { return static_cast<const uint16_t*>(p); };
   auto outp = [](void* p) { return static_cast<uint16_t*>(p); };
   const WorkspaceLayout wl = workspace_layout(B, L, H, D, var == jattn::kVarlen ? total : -1);
@@ -162,6 +164,8 @@ jattn_status run_bwd(jattn::Variant var, const void* const q[2], const void* con
   a.H = H;
   a.n0 = n0;
   a.total = total;
+  a.wl = win_left;
+  a.wr = win_right;
   a.scale = softmax_scale;
   a.c = softmax_scale * 1.4426950408889634f;
   a.eps = eps;
@@ -173,6 +177,9 @@ jattn_status run_bwd(jattn::Variant var, const void* const q[2], const void* con
              ? JATTN_SUCCESS
              : JATTN_ERROR_HIP;
 }
+
+// A window bound as the kernels take it: negative (no bound) or past the sequence -> L.
+int window_bound(int w, int L) { return w < 0 || w > L ? L : w; }
 
 // Sizes of a packed variable-length call: B sequences, the longest max_seqlen rows, total token rows.
 jattn_status check_varlen_sizes(int B, int max_seqlen, int total, int H, int D) {
@@ -230,10 +237,12 @@ size_t jattn_bwd_workspace_bytes(int B, int L, int H, int D) {
   return workspace_layout(B, L, H, D).total;
 }
 
-jattn_status jattn_fwd_ex(const void* q, const void* k, const void* v, const float* gains,
-                          const int32_t* valid_len, int B, int L, int H, int D, float softmax_scale,
-                          float eps, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                          const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream) {
+// The joint forward, optionally with a local window (window_left / window_right < 0: unbounded).
+static jattn_status joint_fwd(bool windowed, int window_left, int window_right, const void* q, const void* k,
+                              const void* v, const float* gains, const int32_t* valid_len, int B, int L, int H, int D,
+                              float softmax_scale, float eps, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, const hipEvent_t* stage_events, int n_stage_events,
+                              hipStream_t stream) {
   if (n_stage_events < 0 || n_stage_events > JATTN_FWD_STAGES || (n_stage_events > 0 && !stage_events))
     return JATTN_ERROR_INVALID_VALUE;
   if (!q || !k || !v || !gains || !out || !lse) return JATTN_ERROR_INVALID_VALUE;
@@ -255,8 +264,26 @@ jattn_status jattn_fwd_ex(const void* q, const void* k, const void* v, const flo
   const void* const kp[2] = {k, nullptr};
   const void* const vp[2] = {v, nullptr};
   void* const op[2] = {out, nullptr};
-  return run_fwd(jattn::kJoint, qp, kp, vp, gains, valid_len, nullptr, B * L, B, L, L, H, D, softmax_scale, eps, op,
-                 lse, workspace, stage_events, n_stage_events, stream);
+  return run_fwd(windowed ? jattn::kWindow : jattn::kJoint, qp, kp, vp, gains, valid_len, nullptr, B * L, B, L, L, H, D,
+                 softmax_scale, eps, op, lse, workspace, stage_events, n_stage_events, stream,
+                 window_bound(window_left, L), window_bound(window_right, L));
+}
+
+jattn_status jattn_fwd_ex(const void* q, const void* k, const void* v, const float* gains,
+                          const int32_t* valid_len, int B, int L, int H, int D, float softmax_scale,
+                          float eps, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream) {
+  return joint_fwd(false, -1, -1, q, k, v, gains, valid_len, B, L, H, D, softmax_scale, eps, out, lse, workspace,
+                   workspace_bytes, stage_events, n_stage_events, stream);
+}
+
+jattn_status jattn_fwd_window(const void* q, const void* k, const void* v, const float* gains,
+                              const int32_t* valid_len, int B, int L, int H, int D, float softmax_scale, float eps,
+                              int window_left, int window_right, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, const hipEvent_t* stage_events, int n_stage_events,
+                              hipStream_t stream) {
+  return joint_fwd(true, window_left, window_right, q, k, v, gains, valid_len, B, L, H, D, softmax_scale, eps, out, lse,
+                   workspace, workspace_bytes, stage_events, n_stage_events, stream);
 }
 
 jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float* gains,
@@ -276,12 +303,13 @@ jattn_status jattn_bwd(const void* q, const void* k, const void* v, const float*
                       dgains, workspace, workspace_bytes, fwd_workspace, nullptr, 0, stream);
 }
 
-jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const float* gains,
-                          const int32_t* valid_len, const void* out, const float* lse, const void* dout,
-                          int B, int L, int H, int D, float softmax_scale, float eps, void* dq, void* dk,
-                          void* dv, float* dgains, void* workspace, size_t workspace_bytes,
-                          const void* fwd_workspace, const hipEvent_t* stage_events, int n_stage_events,
-                          hipStream_t stream) {
+// The joint backward, optionally with a local window.
+static jattn_status joint_bwd(bool windowed, int window_left, int window_right, const void* q, const void* k,
+                              const void* v, const float* gains, const int32_t* valid_len, const void* out,
+                              const float* lse, const void* dout, int B, int L, int H, int D, float softmax_scale,
+                              float eps, void* dq, void* dk, void* dv, float* dgains, void* workspace,
+                              size_t workspace_bytes, const void* fwd_workspace, const hipEvent_t* stage_events,
+                              int n_stage_events, hipStream_t stream) {
   if (n_stage_events < 0 || n_stage_events > JATTN_BWD_STAGES || (n_stage_events > 0 && !stage_events))
     return JATTN_ERROR_INVALID_VALUE;
   if (!q || !k || !v || !gains || !out || !lse || !dout || !dq || !dk || !dv || !dgains)
@@ -312,9 +340,30 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
   void* const dqp[2] = {dq, nullptr};
   void* const dkp[2] = {dk, nullptr};
   void* const dvp[2] = {dv, nullptr};
-  return run_bwd(jattn::kJoint, qp, kp, vp, gains, valid_len, nullptr, B * L, op, lse, dop, B, L, L, H, D,
-                 softmax_scale, eps, dqp, dkp, dvp, dgains, workspace, fwd_workspace, stage_events, n_stage_events,
-                 stream);
+  return run_bwd(windowed ? jattn::kWindow : jattn::kJoint, qp, kp, vp, gains, valid_len, nullptr, B * L, op, lse, dop,
+                 B, L, L, H, D, softmax_scale, eps, dqp, dkp, dvp, dgains, workspace, fwd_workspace, stage_events,
+                 n_stage_events, stream, window_bound(window_left, L), window_bound(window_right, L));
+}
+
+jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const float* gains,
+                          const int32_t* valid_len, const void* out, const float* lse, const void* dout,
+                          int B, int L, int H, int D, float softmax_scale, float eps, void* dq, void* dk,
+                          void* dv, float* dgains, void* workspace, size_t workspace_bytes,
+                          const void* fwd_workspace, const hipEvent_t* stage_events, int n_stage_events,
+                          hipStream_t stream) {
+  return joint_bwd(false, -1, -1, q, k, v, gains, valid_len, out, lse, dout, B, L, H, D, softmax_scale, eps, dq, dk, dv,
+                   dgains, workspace, workspace_bytes, fwd_workspace, stage_events, n_stage_events, stream);
+}
+
+jattn_status jattn_bwd_window(const void* q, const void* k, const void* v, const float* gains,
+                              const int32_t* valid_len, const void* out, const float* lse, const void* dout, int B,
+                              int L, int H, int D, float softmax_scale, float eps, int window_left, int window_right,
+                              void* dq, void* dk, void* dv, float* dgains, void* workspace, size_t workspace_bytes,
+                              const void* fwd_workspace, const hipEvent_t* stage_events, int n_stage_events,
+                              hipStream_t stream) {
+  return joint_bwd(true, window_left, window_right, q, k, v, gains, valid_len, out, lse, dout, B, L, H, D,
+                   softmax_scale, eps, dq, dk, dv, dgains, workspace, workspace_bytes, fwd_workspace, stage_events,
+                   n_stage_events, stream);
 }
 
 jattn_status jattn_fwd_streams(const void* const q[2], const void* const k[2], const void* const v[2],

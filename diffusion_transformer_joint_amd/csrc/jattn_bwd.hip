@@ -184,11 +184,12 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
 // past n are seeded with -inf (P = 0).
 // The halves run one after the other (issuing the second half's row reads under the first half's
 // products measured no faster).
-template <int D, bool MASKED>
+// W (local window): masked tiles also seed -inf outside the lane's query window qrow - wl .. qrow + wr.
+template <int D, bool MASKED, bool W = false>
 __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __bf16* __restrict__ vt,
                                         const bf16x8 (&qf)[Dims<D>::KS], const bf16x8 (&dof)[Dims<D>::KS],
                                         const f32x16& cs, const f32x16& cp, f32x16 (&acc)[Dims<D>::MT], int key0,
-                                        int n, int lane) {
+                                        int n, int lane, int qrow = 0, int wl = 0, int wr = 0) {
   using Dm = Dims<D>;
   using LK = typename DqCfg<D>::LK;
   using LV = typename DqCfg<D>::LV;
@@ -206,7 +207,15 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
   auto scores = [&](int h) {
     s[h] = cs;
     dp[h] = cp;
-    if constexpr (MASKED) {
+    if constexpr (MASKED && W) {
+      // keys key0 + c with c = h*32 + (i>>2)*8 + 4g + (i&3) are allowed for c in [clo, chi)
+      const int clo = qrow - wl - key0, chi = min(n, qrow + wr + 1) - key0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = h * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+        s[h][i] = (c >= clo) & (c < chi) ? s[h][i] : -INFINITY;
+      }
+    } else if constexpr (MASKED) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (key0 + h * 32 + (i >> 2) * 8 + g * 4 + (i & 3) >= n) s[h][i] = -INFINITY;
@@ -244,7 +253,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
 // One work item of the dq kernel: query rows [128 blk, 128 blk + 128) of (sequence, head) pair bh.
 // Varlen (V): a block past the end of its sequence has nothing to do (its statistics rows belong to
 // the next pair).
-template <int D, bool S, bool V>
+template <int D, bool S, bool V, bool W>
 __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, int blk) {
   using Dm = Dims<D>;
   using Cfg = DqCfg<D>;
@@ -279,7 +288,14 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
     dv.issue_blocks(S, a.v, a.v1, map.o0, map.o1, map.n0, map.rs, t * kTile, n, sv + buf * LV::ELEMS, wave,
                                  lane);
   };
-  for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
+  // (local window: the key tiles the block's query rows can reach)
+  const TileRange tr = W ? window_tiles(blk * kBwdRowsPerBlock, min(L, (blk + 1) * kBwdRowsPerBlock), a.wl, a.wr, n, n)
+                         : TileRange{0, 0, 0, 0};
+  if constexpr (W) {
+    for (int i = 0; i < NB - 1 && tr.lo + i < tr.hi; ++i) issue(tr.lo + i, i);
+  } else {
+    for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
+  }
 
   const int qrow = blk * kBwdRowsPerBlock + wave * kWaveRows + l32;
   const bool qvalid = qrow < L;
@@ -336,8 +352,24 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
     ring_barrier<DirectTile<D, LK, kBwdWaves>::MIN_PER_WAVE + DirectTile<D, LV, kBwdWaves>::MIN_PER_WAVE, NB - 2>(ntiles - 2 - t);
     cur = cur + 1 == NB ? 0 : cur + 1;
   };
-  for (int t = 0; t < nfull; ++t) step(std::false_type{}, t);
-  if (nfull < ntiles) step(std::true_type{}, nfull);
+  if constexpr (!W) {
+    for (int t = 0; t < nfull; ++t) step(std::false_type{}, t);
+    if (nfull < ntiles) step(std::true_type{}, nfull);
+  } else {
+    auto wstep = [&](auto masked, int t) {
+      if (t + NB - 1 < tr.hi) issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
+      if (active)
+        dq_tile<D, decltype(masked)::value, true>(sk + cur * LK::ELEMS, sv + cur * LV::ELEMS, qf, dof, cs, cp, acc,
+                                                  t * kTile, n, lane, qrow, a.wl, a.wr);
+      ring_barrier<DirectTile<D, LK, kBwdWaves>::MIN_PER_WAVE + DirectTile<D, LV, kBwdWaves>::MIN_PER_WAVE, NB - 2>(
+          tr.hi - 2 - t);
+      cur = cur + 1 == NB ? 0 : cur + 1;
+    };
+    int t = tr.lo;
+    for (; t < tr.flo; ++t) wstep(std::true_type{}, t);
+    for (; t < tr.fhi; ++t) wstep(std::false_type{}, t);
+    for (; t < tr.hi; ++t) wstep(std::true_type{}, t);
+  }
 
   // row statistics for the key-parallel kernel, for every row of the block (-inf / 0 past L)
   if (g == 0) {
@@ -365,18 +397,18 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
   }
 }
 
-template <int D, bool S, bool V>
+template <int D, bool S, bool V, bool W>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
 void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DqCfg<D>::template bytes<S>()];
   // (an item ends with its tile loop's barrier and, in the joint form, its epilogue does not touch
   // LDS, so the next item may refill the ring right away; the two-stream epilogue's column sums do)
   if constexpr (V) {
-    for (PairIter it(a.B * a.H, a.nblk); it.valid(); it.next()) dq_item<D, S, V>(a, smem, it.pair(), it.blk());
+    for (PairIter it(a.B * a.H, a.nblk); it.valid(); it.next()) dq_item<D, S, V, W>(a, smem, it.pair(), it.blk());
   } else {
     for (ItemIter it(a.items); it.valid(); it.next()) {
       const int bh = it.item() / a.nblk;
-      dq_item<D, S, V>(a, smem, bh, it.item() - bh * a.nblk);
+      dq_item<D, S, V, W>(a, smem, bh, it.item() - bh * a.nblk);
       if constexpr (S) __syncthreads();
     }
   }
@@ -388,13 +420,15 @@ void bwd_dq_kernel(BwdArgs a) {
 // One 64-query tile: for both 32-query halves S' = Qs Kf^T and dP - Delta = dO V^T (lane = key),
 // P = exp2(S' - lse2), dS = P * (dP - Delta), then dV^T += dO^T P and dKn^T += Qs^T dS.
 // sl / sd hold -lse2 and -Delta of the tile's rows. KMASK: this wave holds keys at or past n, whose
-// P is forced to zero.
-template <int D, bool KMASK>
+// P is forced to zero. WM (local window): P is also zero for the queries outside the window of this
+// lane's key (queries key - wr .. key + wl see it); q0 is the tile's first query row. (Selected after
+// the exp: a query with no key in its window has lse = -inf, so its S - lse is +inf.)
+template <int D, bool KMASK, bool WM = false>
 __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const __bf16* __restrict__ ot,
                                           const float* __restrict__ sl, const float* __restrict__ sd,
                                           const bf16x8 (&kf)[Dims<D>::KS], const bf16x8 (&vf)[Dims<D>::KS],
                                           f32x16 (&dva)[Dims<D>::MT], f32x16 (&dka)[Dims<D>::MT], bool kvalid,
-                                          int lane) {
+                                          int lane, int q0 = 0, int key = 0, int wl = 0, int wr = 0) {
   using Dm = Dims<D>;
   using LQ = typename DkdvCfg<D>::LQ;
   using LO = typename DkdvCfg<D>::LO;
@@ -432,6 +466,10 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const _
     for (int i = 0; i < 16; ++i) {
       p[i] = fast_exp2(s[h][i]);
       if constexpr (KMASK) p[i] = kvalid ? p[i] : 0.f;
+      if constexpr (WM) {  // queries q0 + c with c in [key - wr - q0, key + wl - q0] see this key
+        const int c = h * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+        p[i] = (c >= key - wr - q0) & (c <= key + wl - q0) ? p[i] : 0.f;
+      }
       ds[i] = p[i] * dp[h][i];
     }
     pf[h][0] = to_bf16x8(p);
@@ -460,8 +498,11 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const _
 
 // `active`: this wave holds at least one valid key (a wave of padded keys only keeps the ring going).
 // Streams the query rows of (sequence, head) pair bh: Qs, dout (through `map`) and the statistics.
-template <int D, bool S, bool V, bool KMASK>
+// W (local window): only the query tiles [tr.lo, tr.hi), the ends [tr.lo, tr.flo) and [tr.fhi, tr.hi)
+// with the window mask (tile t in buffer (t - tr.lo) % NB); key is this lane's key row.
+template <int D, bool S, bool V, bool W, bool KMASK>
 __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, const RowMap<S>& map, int bh,
+                                          const TileRange& tr, int key,
                                           const bf16x8 (&kf)[Dims<D>::KS], const bf16x8 (&vf)[Dims<D>::KS],
                                           f32x16 (&dva)[Dims<D>::MT], f32x16 (&dka)[Dims<D>::MT], bool kvalid,
                                           bool active, int tid) {
@@ -504,11 +545,34 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, const Ro
       dout.issue(tile_rsrc<D>(ob, rs, t * kTile, L), so + buf * LO::ELEMS, wave);
   };
   const int ntiles = (L + kTile - 1) / kTile;
-  for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
+  if constexpr (W) {
+    for (int i = 0; i < NB - 1 && tr.lo + i < tr.hi; ++i) issue(tr.lo + i, i);
+  } else {
+    for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
+  }
   wait_vmem();
   __syncthreads();
   constexpr int PER = DirectTile<D, LQ, kBwdWaves>::MIN_PER_WAVE + DirectTile<D, LO, kBwdWaves>::MIN_PER_WAVE;
   int cur = 0;
+  if constexpr (W) {
+    auto wstep = [&](auto masked, int t) {
+      if (t + NB - 1 < tr.hi) issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
+      if (active)
+        dkdv_tile<D, KMASK, decltype(masked)::value>(sq + cur * LQ::ELEMS, so + cur * LO::ELEMS, sl + cur * kTile,
+                                                     sd + cur * kTile, kf, vf, dva, dka, kvalid, lane, t * kTile, key,
+                                                     a.wl, a.wr);
+      if (wave < 2)
+        ring_barrier<PER + 1, NB - 2>(tr.hi - 2 - t);
+      else
+        ring_barrier<PER, NB - 2>(tr.hi - 2 - t);
+      cur = cur + 1 == NB ? 0 : cur + 1;
+    };
+    int t = tr.lo;
+    for (; t < tr.flo; ++t) wstep(std::true_type{}, t);
+    for (; t < tr.fhi; ++t) wstep(std::false_type{}, t);
+    for (; t < tr.hi; ++t) wstep(std::true_type{}, t);
+    return;
+  }
   for (int t = 0; t < ntiles; ++t) {
     const bool ahead = t + NB - 1 < ntiles;
     if (ahead) issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
@@ -526,7 +590,7 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, const Ro
 // One work item of the dk/dv kernel: key rows [128 blk, 128 blk + 128) of (sequence, head) pair bh.
 // (Varlen: a block past the end of its sequence takes the all-padding path below, which then writes
 // no rows, only its zero partial sums.)
-template <int D, bool S, bool V>
+template <int D, bool S, bool V, bool W>
 __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, int blk, int item) {
   using Dm = Dims<D>;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
@@ -591,10 +655,15 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
     }
   // waves whose 32 keys are all valid skip the key mask
   const bool active = blk * kBwdRowsPerBlock + wave * kWaveRows < n;
+  // (local window: the query tiles the block's keys can be seen from; queries past L need no mask,
+  // their statistics already give P = 0)
+  const TileRange tr = W ? window_tiles(blk * kBwdRowsPerBlock, min(L, (blk + 1) * kBwdRowsPerBlock), a.wr, a.wl, L,
+                                        L + 2 * kTile)
+                         : TileRange{0, 0, 0, 0};
   if (blk * kBwdRowsPerBlock + (wave + 1) * kWaveRows <= n)
-    dkdv_loop<D, S, V, false>(a, smem, map, bh, kf, vf, dva, dka, kvalid, active, tid);
+    dkdv_loop<D, S, V, W, false>(a, smem, map, bh, tr, key, kf, vf, dva, dka, kvalid, active, tid);
   else
-    dkdv_loop<D, S, V, true>(a, smem, map, bh, kf, vf, dva, dka, kvalid, active, tid);
+    dkdv_loop<D, S, V, W, true>(a, smem, map, bh, tr, key, kf, vf, dva, dka, kvalid, active, tid);
 
   // dv (zeros at padded keys)
   if (kin) {
@@ -636,19 +705,19 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
   }
 }
 
-template <int D, bool S, bool V>
+template <int D, bool S, bool V, bool W>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
 void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DkdvCfg<D>::template bytes<S>()];
   if constexpr (V) {
     for (PairIter it(a.B * a.H, a.nblk); it.valid(); it.next()) {
-      dkdv_item<D, S, V>(a, smem, it.pair(), it.blk(), it.pair() * a.nblk + it.blk());
+      dkdv_item<D, S, V, W>(a, smem, it.pair(), it.blk(), it.pair() * a.nblk + it.blk());
       __syncthreads();  // the column-sum scratch overlaps the ring the next item refills
     }
   } else {
     for (ItemIter it(a.items); it.valid(); it.next()) {
       const int bh = it.item() / a.nblk;
-      dkdv_item<D, S, V>(a, smem, bh, it.item() - bh * a.nblk, it.item());
+      dkdv_item<D, S, V, W>(a, smem, bh, it.item() - bh * a.nblk, it.item());
       __syncthreads();  // the column-sum scratch overlaps the ring the next item refills
     }
   }
@@ -698,7 +767,7 @@ __global__ __launch_bounds__(kReduceThreads) void dg_reduce_kernel(const float* 
   }
 }
 
-template <int D, bool S, bool V>
+template <int D, bool S, bool V, bool W>
 static hipError_t launch_bwd_d(const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
                                hipStream_t stream) {
   int stage = 0;
@@ -724,29 +793,29 @@ static hipError_t launch_bwd_d(const BwdArgs& a, bool prenorm, const hipEvent_t*
   hipError_t e = recorded(prenorm ? launch_prenorm(D, S ? kStreams : (V ? kVarlen : kJoint), p, stream) : hipSuccess);
   if (e != hipSuccess) return e;
   int grid = 0;
-  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dq_kernel<D, S, V>), a.items, kBwdThreads, &grid)) !=
+  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dq_kernel<D, S, V, W>), a.items, kBwdThreads, &grid)) !=
       hipSuccess)
     return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, S, V>), dim3(grid), dim3(kBwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, S, V, W>), dim3(grid), dim3(kBwdThreads), 0, stream, a);
   if ((e = recorded(hipSuccess)) != hipSuccess) return e;
-  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dkdv_kernel<D, S, V>), a.items, kBwdThreads, &grid)) !=
+  if ((e = persistent_grid(reinterpret_cast<const void*>(bwd_dkdv_kernel<D, S, V, W>), a.items, kBwdThreads, &grid)) !=
       hipSuccess)
     return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, S, V>), dim3(grid), dim3(kBwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, S, V, W>), dim3(grid), dim3(kBwdThreads), 0, stream, a);
   if ((e = recorded(hipSuccess)) != hipSuccess) return e;
   hipLaunchKernelGGL(dg_reduce_kernel<S>, dim3(S ? kPartSets * D : D), dim3(kReduceThreads), 0, stream, a.part,
                      a.gains, a.items, D, a.dgains);
   return recorded(hipSuccess);
 }
 
-template <bool S, bool V>
+template <bool S, bool V, bool W>
 static hipError_t launch_bwd_s(int D, const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
                                hipStream_t stream) {
   switch (D) {
-    case 32: return launch_bwd_d<32, S, V>(a, prenorm, events, n_events, stream);
-    case 64: return launch_bwd_d<64, S, V>(a, prenorm, events, n_events, stream);
-    case 72: return launch_bwd_d<72, S, V>(a, prenorm, events, n_events, stream);
-    case 128: return launch_bwd_d<128, S, V>(a, prenorm, events, n_events, stream);
+    case 32: return launch_bwd_d<32, S, V, W>(a, prenorm, events, n_events, stream);
+    case 64: return launch_bwd_d<64, S, V, W>(a, prenorm, events, n_events, stream);
+    case 72: return launch_bwd_d<72, S, V, W>(a, prenorm, events, n_events, stream);
+    case 128: return launch_bwd_d<128, S, V, W>(a, prenorm, events, n_events, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -754,9 +823,10 @@ static hipError_t launch_bwd_s(int D, const BwdArgs& a, bool prenorm, const hipE
 hipError_t launch_bwd(int D, Variant var, const BwdArgs& a, bool prenorm, const hipEvent_t* events,
                       int n_events, hipStream_t stream) {
   switch (var) {
-    case kStreams: return launch_bwd_s<true, false>(D, a, prenorm, events, n_events, stream);
-    case kVarlen: return launch_bwd_s<false, true>(D, a, prenorm, events, n_events, stream);
-    default: return launch_bwd_s<false, false>(D, a, prenorm, events, n_events, stream);
+    case kStreams: return launch_bwd_s<true, false, false>(D, a, prenorm, events, n_events, stream);
+    case kVarlen: return launch_bwd_s<false, true, false>(D, a, prenorm, events, n_events, stream);
+    case kWindow: return launch_bwd_s<false, false, true>(D, a, prenorm, events, n_events, stream);
+    default: return launch_bwd_s<false, false, false>(D, a, prenorm, events, n_events, stream);
   }
 }
 

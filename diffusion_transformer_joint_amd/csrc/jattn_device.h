@@ -598,6 +598,31 @@ struct ItemIter {
   __device__ void next() { j += step; }
 };
 
+// Streamed tiles a block of rows [r0, r1) reaches under a local window, where row r may see streamed
+// rows r - before .. r + after. Streamed rows at or past n_reach are never read; tiles [lo, flo) and
+// [fhi, hi) need an element mask, tiles [flo, fhi) are allowed for every (row, streamed row) pair
+// and have no streamed row at or past n_full. lo = hi when nothing is reachable. All bounds are
+// wave-uniform; the arguments stay far from integer overflow (window bounds are at most L).
+struct TileRange {
+  int lo, flo, fhi, hi;
+};
+__device__ __forceinline__ TileRange window_tiles(int r0, int r1, int before, int after, int n_reach, int n_full) {
+  TileRange t;
+  const int j0 = max(0, r0 - before), j1 = min(n_reach, r1 + after);
+  if (j1 <= j0) {
+    t.lo = t.flo = t.fhi = t.hi = 0;
+    return t;
+  }
+  t.lo = j0 / kTile;
+  t.hi = (j1 + kTile - 1) / kTile;
+  const int a = r1 - 1 - before;                        // a full tile starts at or after the last row's first
+  const int fl = a > 0 ? (a + kTile - 1) / kTile : 0;   // allowed streamed row ...
+  const int b = min(n_full, r0 + after + 1);            // ... and ends at or before the first row's last one
+  t.flo = min(max(fl, t.lo), t.hi);
+  t.fhi = min(max(b > 0 ? b / kTile : 0, t.flo), t.hi);
+  return t;
+}
+
 // Item order of the packed variable-length kernels. Sequences differ in length, and the work of a row
 // block grows with its sequence's length, so contiguous item ranges per XCD (ItemIter) would give
 // one XCD the long sequences and another the short ones. Here the (sequence, head) pairs are dealt

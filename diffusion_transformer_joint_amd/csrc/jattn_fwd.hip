@@ -96,12 +96,13 @@ __device__ __forceinline__ void softmax_half(const f32x16& s, f32x16 (&o)[Dims<D
   pack_probs(p, pf0, pf1, lsum);
 }
 
-// One 64-key tile from LDS (kt, vt). MASKED: keys at or past n get a -inf accumulator seed (p = 0).
-template <int D, bool BOUNDED, bool MASKED>
+// One 64-key tile from LDS (kt, vt). MASKED: keys at or past n get a -inf accumulator seed (p = 0),
+// and with a local window (W) so do the keys outside each query's window qrow - wl .. qrow + wr.
+template <int D, bool BOUNDED, bool MASKED, bool W = false>
 __device__ __forceinline__ void fwd_tile(const __bf16* __restrict__ kt, const __bf16* __restrict__ vt,
                                          const bf16x8 (&qf)[Fwd<D>::QT][Dims<D>::KS],
                                          const f32x16 (&cinit)[Fwd<D>::QT], FwdState<D>& st, int key0, int n,
-                                         int lane) {
+                                         int lane, const int* qrow = nullptr, int wl = 0, int wr = 0) {
   using Dm = Dims<D>;
   using LK = typename Fwd<D>::LK;
   using LV = typename Fwd<D>::LV;
@@ -114,7 +115,15 @@ __device__ __forceinline__ void fwd_tile(const __bf16* __restrict__ kt, const __
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       s[qt] = cinit[qt];
-      if constexpr (MASKED) {
+      if constexpr (MASKED && W) {
+        // keys key0 + c with c = h*32 + (i>>2)*8 + 4g + (i&3) are allowed for c in [clo, chi)
+        const int clo = qrow[qt] - wl - key0, chi = min(n, qrow[qt] + wr + 1) - key0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = h * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+          s[qt][i] = (c >= clo) & (c < chi) ? s[qt][i] : -INFINITY;
+        }
+      } else if constexpr (MASKED) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (key0 + h * 32 + (i >> 2) * 8 + g * 4 + (i & 3) >= n) s[qt][i] = -INFINITY;
@@ -170,10 +179,12 @@ struct FwdRing {
 // ring going: it issues its share of the loads and meets the barriers, but skips the math).
 // (V is not used here; as a template argument it keeps each caller's instantiation its own, which
 // the compiler's host-side pass needs for templates that reach the LDS-bound load builtins.)
-template <int D, bool S, bool V, bool BOUNDED>
+// W (local window): the ring holds the tiles [tr.lo, tr.hi) only, tile t in buffer (t - tr.lo) % NB;
+// the tiles [tr.flo, tr.fhi) run unmasked, the others with the window mask.
+template <int D, bool S, bool V, bool W, bool BOUNDED>
 __device__ __forceinline__ void fwd_loop(FwdRing<D, S>& ring, const bf16x8 (&qf)[Fwd<D>::QT][Dims<D>::KS],
                                          const float (&shift)[Fwd<D>::QT], FwdState<D>& st, bool active,
-                                         int lane) {
+                                         int lane, const TileRange& tr, const int* qrow, int wl, int wr) {
   using LK = typename Fwd<D>::LK;
   using LV = typename Fwd<D>::LV;
   constexpr int QT = Fwd<D>::QT, NB = Fwd<D>::NB;
@@ -192,14 +203,29 @@ __device__ __forceinline__ void fwd_loop(FwdRing<D, S>& ring, const bf16x8 (&qf)
     ring_barrier<FwdRing<D, S>::PER, NB - 2>(ntiles - 2 - t);
     cur = cur + 1 == NB ? 0 : cur + 1;
   };
-  for (int t = 0; t < nfull; ++t) step(std::false_type{}, t);
-  if (nfull < ntiles) step(std::true_type{}, nfull);
+  if constexpr (!W) {
+    for (int t = 0; t < nfull; ++t) step(std::false_type{}, t);
+    if (nfull < ntiles) step(std::true_type{}, nfull);
+  } else {
+    auto wstep = [&](auto masked, int t) {
+      if (t + NB - 1 < tr.hi) ring.issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
+      if (active)
+        fwd_tile<D, BOUNDED, decltype(masked)::value, true>(ring.sk + cur * LK::ELEMS, ring.sv + cur * LV::ELEMS, qf,
+                                                            cinit, st, t * kTile, n, lane, qrow, wl, wr);
+      ring_barrier<FwdRing<D, S>::PER, NB - 2>(tr.hi - 2 - t);
+      cur = cur + 1 == NB ? 0 : cur + 1;
+    };
+    int t = tr.lo;
+    for (; t < tr.flo; ++t) wstep(std::true_type{}, t);
+    for (; t < tr.fhi; ++t) wstep(std::false_type{}, t);
+    for (; t < tr.hi; ++t) wstep(std::true_type{}, t);
+  }
 }
 
 // One work item: query rows [ROWS blk, ROWS blk + ROWS) of (sequence, head) pair bh.
 // Varlen (V): the grid is sized for the longest sequence; a block past the end of its sequence has
 // nothing to do.
-template <int D, bool S, bool V>
+template <int D, bool S, bool V, bool W>
 __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, int blk) {
   using Dm = Dims<D>;
   constexpr int QT = Fwd<D>::QT;
@@ -228,7 +254,14 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
   ring.lane = lane;
   ring.dk.init(D, wave, lane);
   ring.dv.init(map.rs, wave, lane);
-  for (int t = 0; t < Fwd<D>::NB - 1 && t < ring.ntiles; ++t) ring.issue(t, t);
+  // (local window: the key tiles the block's query rows can reach)
+  const TileRange tr = W ? window_tiles(blk * Fwd<D>::ROWS, min(L, (blk + 1) * Fwd<D>::ROWS), a.wl, a.wr, n, n)
+                         : TileRange{0, 0, 0, 0};
+  if constexpr (W) {
+    for (int i = 0; i < Fwd<D>::NB - 1 && tr.lo + i < tr.hi; ++i) ring.issue(tr.lo + i, i);
+  } else {
+    for (int t = 0; t < Fwd<D>::NB - 1 && t < ring.ntiles; ++t) ring.issue(t, t);
+  }
 
   // This wave's query rows, normalised with both gains (two-stream: its own stream's Q gain) and
   // pre-scaled, as B-operand fragments, and their score bounds in log2 units (margin covers the
@@ -295,11 +328,11 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
   if (bmax <= kBoundLimit) {  // uniform over the workgroup
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = shift[qt];
-    fwd_loop<D, S, V, true>(ring, qf, shift, st, active, lane);
+    fwd_loop<D, S, V, W, true>(ring, qf, shift, st, active, lane, tr, qrow, a.wl, a.wr);
   } else {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = -INFINITY;
-    fwd_loop<D, S, V, false>(ring, qf, shift, st, active, lane);
+    fwd_loop<D, S, V, W, false>(ring, qf, shift, st, active, lane, tr, qrow, a.wl, a.wr);
   }
 
 #pragma unroll
@@ -325,7 +358,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
   }
 }
 
-template <int D, bool S, bool V>
+template <int D, bool S, bool V, bool W>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Fwd<D>::BYTES];
   // one item per workgroup (a persistent grid measured slower here: the items are few and large),
@@ -333,16 +366,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if constexpr (V) {
     const PairIter it(a.B * a.H, a.nblk);
     if (!it.valid()) return;
-    fwd_item<D, S, V>(a, smem, it.pair(), it.blk());
+    fwd_item<D, S, V, W>(a, smem, it.pair(), it.blk());
   } else {
     const ItemIter it(a.items);
     if (!it.valid()) return;
     const int bh = it.item() / a.nblk;
-    fwd_item<D, S, V>(a, smem, bh, it.item() - bh * a.nblk);
+    fwd_item<D, S, V, W>(a, smem, bh, it.item() - bh * a.nblk);
   }
 }
 
-template <int D, bool S, bool V>
+template <int D, bool S, bool V, bool W>
 static hipError_t launch_fwd_d(const FwdArgs& a, const hipEvent_t* events, int n_events, hipStream_t stream) {
   PrenormArgs p;
   p.k = a.k;
@@ -357,24 +390,24 @@ static hipError_t launch_fwd_d(const FwdArgs& a, const hipEvent_t* events, int n
   p.n0 = a.n0;
   p.total = a.total;
   p.eps = a.eps;
-  hipError_t e = launch_prenorm(D, S ? kStreams : (V ? kVarlen : kJoint), p, stream);
+  hipError_t e = launch_prenorm(D, S ? kStreams : (V ? kVarlen : kJoint), p, stream);  // (window: joint)
   if (e == hipSuccess && n_events > 0) e = hipEventRecord(events[0], stream);
   if (e != hipSuccess) return e;
   const int grid = V ? pair_grid(a.B * a.H, a.nblk) : grid_for_items(a.items);
-  hipLaunchKernelGGL((fwd_kernel<D, S, V>), dim3(grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, S, V, W>), dim3(grid), dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e == hipSuccess && n_events > 1) e = hipEventRecord(events[1], stream);
   return e;
 }
 
-template <bool S, bool V>
+template <bool S, bool V, bool W>
 static hipError_t launch_fwd_s(int D, const FwdArgs& a, const hipEvent_t* events, int n_events,
                                hipStream_t stream) {
   switch (D) {
-    case 32: return launch_fwd_d<32, S, V>(a, events, n_events, stream);
-    case 64: return launch_fwd_d<64, S, V>(a, events, n_events, stream);
-    case 72: return launch_fwd_d<72, S, V>(a, events, n_events, stream);
-    case 128: return launch_fwd_d<128, S, V>(a, events, n_events, stream);
+    case 32: return launch_fwd_d<32, S, V, W>(a, events, n_events, stream);
+    case 64: return launch_fwd_d<64, S, V, W>(a, events, n_events, stream);
+    case 72: return launch_fwd_d<72, S, V, W>(a, events, n_events, stream);
+    case 128: return launch_fwd_d<128, S, V, W>(a, events, n_events, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -382,9 +415,10 @@ static hipError_t launch_fwd_s(int D, const FwdArgs& a, const hipEvent_t* events
 hipError_t launch_fwd(int D, Variant var, const FwdArgs& a, const hipEvent_t* events, int n_events,
                       hipStream_t stream) {
   switch (var) {
-    case kStreams: return launch_fwd_s<true, false>(D, a, events, n_events, stream);
-    case kVarlen: return launch_fwd_s<false, true>(D, a, events, n_events, stream);
-    default: return launch_fwd_s<false, false>(D, a, events, n_events, stream);
+    case kStreams: return launch_fwd_s<true, false, false>(D, a, events, n_events, stream);
+    case kVarlen: return launch_fwd_s<false, true, false>(D, a, events, n_events, stream);
+    case kWindow: return launch_fwd_s<false, false, true>(D, a, events, n_events, stream);
+    default: return launch_fwd_s<false, false, false>(D, a, events, n_events, stream);
   }
 }
 

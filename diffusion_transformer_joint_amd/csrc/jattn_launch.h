@@ -20,6 +20,9 @@ namespace jattn {
 // Packed variable-length batches (the `varlen` kernels): `cu_seqlens` [B + 1] on the device gives the
 // token row range of each sequence in [total, H, D] tensors (see SeqGeom), L is then the longest
 // sequence (max_seqlen) and sizes the grids, and valid_len is not used.
+//
+// Local window (the `window` kernels): query i sees only keys i - wl <= j <= i + wr, besides j < n.
+// The host passes wl, wr in [0, L] (L for an unbounded side).
 
 struct PrenormArgs {
   const uint16_t* k;
@@ -47,6 +50,7 @@ struct FwdArgs {
   uint16_t* out1;
   float* lse;              // [B, H, L] natural log (varlen: per sequence [H, L_b], see SeqGeom)
   int B, L, H, n0, total;
+  int wl, wr;              // window bounds (window kernels only)
   float c;                 // softmax_scale * log2(e)
   float eps;
   int nblk;                // query blocks per (batch, head)
@@ -81,6 +85,7 @@ struct BwdArgs {
   float* ndelta;           // workspace [B, H, lp]: -rowsum(dout * out) (0 past L)
   float* part;             // workspace [kPartSets, D, items]: per row block partial sums of the gain gradients
   int B, L, H, n0, total;
+  int wl, wr;              // window bounds (window kernels only)
   float scale;
   float c;                 // scale * log2(e)
   float eps;
@@ -109,7 +114,7 @@ hipError_t persistent_grid(const void* kernel, int items, int threads, int* grid
 
 // Kernel variants: the joint kernels, the two-stream kernels (two row blocks, gains per block) and
 // the packed variable-length kernels.
-enum Variant { kJoint = 0, kStreams = 1, kVarlen = 2 };
+enum Variant { kJoint = 0, kStreams = 1, kVarlen = 2, kWindow = 3 };
 hipError_t launch_prenorm(int D, Variant var, const PrenormArgs& a, hipStream_t stream);
 // Enqueues the key normalisation (into a.kr) and the forward kernel; if n_events > 0, records
 // events[i] after stage i (i < n_events).

@@ -3,7 +3,8 @@
 torch supplies device memory and the current HIP stream; every step of the computation runs in the
 library's kernels. Layouts: q, k, v, out, dout, dq, dk, dv are bf16 [B, L, H, D] contiguous;
 gains fp32 [2, D] (row 0 for Q, row 1 for K); valid_len int32 [B] (keys per sequence) or None;
-lse fp32 [B, H, L] (natural-log row log-sum-exp).
+lse fp32 [B, H, L] (natural-log row log-sum-exp). window (optional) = (left, right): query i sees only
+keys i - left .. i + right (a negative bound is none), through jattn_fwd_window / jattn_bwd_window.
 
 Two-stream functions (``*_streams``): each per-token tensor is an (image, text) pair of bf16 tensors
 [B, N_img, H, D] and [B, N_txt, H, D] (the joint sequence is image rows then text rows, L = N_img +
@@ -63,7 +64,7 @@ def _check_common(q, k, v, gains, valid_len):
 
 def forward(q, k, v, gains, valid_len=None, scale: Optional[float] = None, eps: float = 1e-6,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-            workspace: Optional[torch.Tensor] = None, return_workspace: bool = False):
+            workspace: Optional[torch.Tensor] = None, return_workspace: bool = False, window=None):
     """Joint attention forward. Returns (out bf16 [B, L, H, D], lse fp32 [B, H, L]), plus the forward
     workspace (the normalised key rows, reusable by `backward`) if return_workspace."""
     B, L, H, D = _check_common(q, k, v, gains, valid_len)
@@ -78,10 +79,16 @@ def forward(q, k, v, gains, valid_len=None, scale: Optional[float] = None, eps: 
     if workspace is None:
         workspace = torch.empty(max(int(lib.jattn_fwd_workspace_bytes(B, L, H, D)), 1), dtype=torch.uint8,
                                 device=q.device)
-    st = lib.jattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gains), _ptr(valid_len), B, L, H, D,
-                       ctypes.c_float(scale), ctypes.c_float(eps), _ptr(out), _ptr(lse), _ptr(workspace),
-                       workspace.numel(), _stream(q))
-    _lib.check("jattn_fwd", st)
+    if window is None:
+        st = lib.jattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gains), _ptr(valid_len), B, L, H, D,
+                           ctypes.c_float(scale), ctypes.c_float(eps), _ptr(out), _ptr(lse), _ptr(workspace),
+                           workspace.numel(), _stream(q))
+        _lib.check("jattn_fwd", st)
+    else:
+        st = lib.jattn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(gains), _ptr(valid_len), B, L, H, D,
+                                  ctypes.c_float(scale), ctypes.c_float(eps), int(window[0]), int(window[1]), _ptr(out),
+                                  _ptr(lse), _ptr(workspace), workspace.numel(), None, 0, _stream(q))
+        _lib.check("jattn_fwd_window", st)
     return (out, lse, workspace) if return_workspace else (out, lse)
 
 
@@ -96,7 +103,8 @@ def fwd_workspace_bytes(B: int, L: int, H: int, D: int) -> int:
 
 
 def backward(q, k, v, gains, out, lse, dout, valid_len=None, scale: Optional[float] = None,
-             eps: float = 1e-6, dq=None, dk=None, dv=None, dgains=None, workspace=None, fwd_workspace=None):
+             eps: float = 1e-6, dq=None, dk=None, dv=None, dgains=None, workspace=None, fwd_workspace=None,
+             window=None):
     """Joint attention backward. Returns (dq, dk, dv bf16 [B, L, H, D], dgains fp32 [2, D]).
     fwd_workspace: the workspace returned by the forward call that produced out and lse (optional;
     the backward then reuses its normalised key rows)."""
@@ -117,11 +125,18 @@ def backward(q, k, v, gains, out, lse, dout, valid_len=None, scale: Optional[flo
     need = int(lib.jattn_bwd_workspace_bytes(B, L, H, D))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = lib.jattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gains), _ptr(valid_len), _ptr(out), _ptr(lse),
-                       _ptr(dout), B, L, H, D, ctypes.c_float(scale), ctypes.c_float(eps), _ptr(dq),
-                       _ptr(dk), _ptr(dv), _ptr(dgains), _ptr(workspace), workspace.numel(), _ptr(fwd_workspace),
-                       _stream(q))
-    _lib.check("jattn_bwd", st)
+    if window is None:
+        st = lib.jattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gains), _ptr(valid_len), _ptr(out), _ptr(lse),
+                           _ptr(dout), B, L, H, D, ctypes.c_float(scale), ctypes.c_float(eps), _ptr(dq),
+                           _ptr(dk), _ptr(dv), _ptr(dgains), _ptr(workspace), workspace.numel(), _ptr(fwd_workspace),
+                           _stream(q))
+        _lib.check("jattn_bwd", st)
+    else:
+        st = lib.jattn_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(gains), _ptr(valid_len), _ptr(out), _ptr(lse),
+                                  _ptr(dout), B, L, H, D, ctypes.c_float(scale), ctypes.c_float(eps), int(window[0]),
+                                  int(window[1]), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgains), _ptr(workspace),
+                                  workspace.numel(), _ptr(fwd_workspace), None, 0, _stream(q))
+        _lib.check("jattn_bwd_window", st)
     return dq, dk, dv, dgains
 
 
@@ -129,22 +144,22 @@ class JointAttention(torch.autograd.Function):
     """Autograd wrapper: saves the forward outputs (out, lse, the normalised keys) and calls jattn_bwd."""
 
     @staticmethod
-    def forward(ctx, q, k, v, gains, valid_len=None, scale=None, eps=1e-6):
-        out, lse, ws = forward(q, k, v, gains, valid_len, scale, eps, return_workspace=True)
+    def forward(ctx, q, k, v, gains, valid_len=None, scale=None, eps=1e-6, window=None):
+        out, lse, ws = forward(q, k, v, gains, valid_len, scale, eps, return_workspace=True, window=window)
         ctx.save_for_backward(q, k, v, gains, out, lse, valid_len, ws)
-        ctx.scale, ctx.eps = scale, eps
+        ctx.scale, ctx.eps, ctx.window = scale, eps, window
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, gains, out, lse, valid_len, ws = ctx.saved_tensors
         dq, dk, dv, dg = backward(q, k, v, gains, out, lse, dout.to(torch.bfloat16).contiguous(),
-                                  valid_len, ctx.scale, ctx.eps, fwd_workspace=ws)
-        return dq, dk, dv, dg, None, None, None
+                                  valid_len, ctx.scale, ctx.eps, fwd_workspace=ws, window=ctx.window)
+        return dq, dk, dv, dg, None, None, None, None
 
 
-def joint_attention(q, k, v, gains, valid_len=None, scale=None, eps=1e-6):
-    return JointAttention.apply(q, k, v, gains, valid_len, scale, eps)
+def joint_attention(q, k, v, gains, valid_len=None, scale=None, eps=1e-6, window=None):
+    return JointAttention.apply(q, k, v, gains, valid_len, scale, eps, window)
 
 
 # ------------------------------------------------------------------------------------------------

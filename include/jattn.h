@@ -124,6 +124,29 @@ jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const flo
                           const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------------
+ * Local-window entry points. The diffusion-pipe summary's attention wrapper has a windowed variant
+ * besides the full one; here it is a sliding window over the joint sequence: query i sees only the
+ * keys j with  i - window_left <= j <= i + window_right  (and j < n_b as before). A negative bound is
+ * no bound on that side, so (-1, 0) is causal attention and (-1, -1) the joint attention above. A
+ * query whose window holds no valid key gets out = 0, lse = -inf and zero gradients. Everything else
+ * (arguments, layouts, workspaces from jattn_fwd_workspace_bytes / jattn_bwd_workspace_bytes, stage
+ * events, errors) is as for jattn_fwd_ex and jattn_bwd_ex; lse and out from jattn_fwd_window go with
+ * jattn_bwd_window and the same window. Only the key tiles a block of queries can reach are read. */
+jattn_status jattn_fwd_window(const void* q, const void* k, const void* v, const float* gains,
+                              const int32_t* valid_len, int B, int L, int H, int D,
+                              float softmax_scale, float eps, int window_left, int window_right,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
+
+jattn_status jattn_bwd_window(const void* q, const void* k, const void* v, const float* gains,
+                              const int32_t* valid_len, const void* out, const float* lse, const void* dout,
+                              int B, int L, int H, int D, float softmax_scale, float eps,
+                              int window_left, int window_right,
+                              void* dq, void* dk, void* dv, float* dgains,
+                              void* workspace, size_t workspace_bytes, const void* fwd_workspace,
+                              const hipEvent_t* stage_events, int n_stage_events, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
  * Two-stream entry points (zero-copy image + text streams with a QK-norm gain pair per stream).
  *
  * The re-diffusion README's DiT-layer box computes Q, K and V separately for each stream ("QKV

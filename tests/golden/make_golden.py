@@ -9,7 +9,9 @@ compare against the stored values.
 
 A name "streams:<workload>" stores the two-stream form instead (dgains_streams_<workload>.json): the
 same seed-0 workload split into image and text tensors with a QK-norm gain pair per stream. A
-packed variable-length workload name (varlen_*) stores that workload's gain gradients.
+packed variable-length workload name (varlen_*) stores that workload's gain gradients. A name
+"window:<workload>" stores the workload under a local window of 256 keys each way
+(dgains_window_<workload>.json).
 """
 import json
 import os
@@ -25,7 +27,9 @@ sys.path.insert(0, ROOT)
 from diffusion_transformer_joint_amd.inputs import make_inputs, make_stream_inputs, make_varlen_inputs  # noqa: E402
 from oracle import attention_fwd_bwd, streams_fwd_bwd, varlen_fwd_bwd  # noqa: E402
 
-FULL = ["mmdit512", "dit256", "mmdit768", "ragged", "streams:mmdit512", "varlen_multires", "varlen_ragged"]
+FULL = ["mmdit512", "dit256", "mmdit768", "ragged", "streams:mmdit512", "varlen_multires", "varlen_ragged",
+        "window:mmdit512"]
+WINDOW = (256, 256)
 
 
 def f64(t):
@@ -64,8 +68,27 @@ def varlen(name):
     print(f"{name}: {time.time() - t0:.1f} s", flush=True)
 
 
+def windowed(name):
+    t0 = time.time()
+    inp = make_inputs(name, seed=0)
+    vl = None if inp["valid_len"] is None else inp["valid_len"].tolist()
+    r = attention_fwd_bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), inp["gains"].double().numpy(),
+                          f64(inp["dout"]), vl, inp["scale"], inp["eps"], window=WINDOW)
+    w = inp["workload"]
+    rec = dict(workload=name, form="local window", window=list(WINDOW), seed=0, B=w.B, L=w.L, H=w.H, D=w.D,
+               valid_len=vl, scale=inp["scale"], eps=inp["eps"],
+               source="oracle/jattn_oracle.py attention_fwd_bwd(window=...), fp64, all pairs",
+               dgains=np.asarray(r["dgains"]).tolist())
+    with open(os.path.join(HERE, f"dgains_window_{name}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"window:{name}: {time.time() - t0:.1f} s", flush=True)
+
+
 def main(names):
     for name in names:
+        if name.startswith("window:"):
+            windowed(name.split(":", 1)[1])
+            continue
         if name.startswith("streams:"):
             streams(name.split(":", 1)[1])
             continue

@@ -329,3 +329,29 @@ def test_varlen_workspace_bytes(lib):
     w = lib.jattn_varlen_bwd_workspace_bytes(16, 2370, 22682, 12, 64)
     # two bf16 row copies, two statistics per (row, head) with 128 rows of slack per sequence, gain partials
     assert w >= 2 * 22682 * 12 * 64 * 2 + 2 * (22682 + 128 * 16) * 12 * 4 + 16 * 12 * 19 * 64 * 4
+
+
+# ------------------------------------------------------------------------------------------------
+# Local-window entry points: the joint entry points' validation with two extra bounds
+def test_window_entry_points_reject(lib):
+    fwb = lib.jattn_fwd_workspace_bytes(2, 100, 3, 64)
+    def fwdw(**kw):
+        a = dict(q=fake(0), out=fake(4), ws=fake(6), ws_bytes=fwb, D=64, left=16, right=-1)
+        a.update(kw)
+        return lib.jattn_fwd_window(a["q"], fake(1), fake(2), fake(3), None, 2, 100, 3, a["D"], ctypes.c_float(0.125),
+                                    ctypes.c_float(1e-6), a["left"], a["right"], a["out"], fake(5), a["ws"],
+                                    a["ws_bytes"], None, 0, None)
+    assert fwdw(q=None) == _lib.INVALID_VALUE
+    assert fwdw(out=fake(1)) == _lib.INVALID_VALUE
+    assert fwdw(D=48) == _lib.NOT_SUPPORTED
+    assert fwdw(ws_bytes=16) == _lib.WORKSPACE
+    assert fwdw(left=-5, right=10**9, ws_bytes=16) == _lib.WORKSPACE   # any bounds are accepted
+    need = lib.jattn_bwd_workspace_bytes(2, 100, 3, 64)
+    def bwdw(**kw):
+        a = dict(dq=fake(7), ws=fake(11), ws_bytes=need)
+        a.update(kw)
+        return lib.jattn_bwd_window(fake(0), fake(1), fake(2), fake(3), None, fake(4), fake(5), fake(6), 2, 100, 3, 64,
+                                    ctypes.c_float(0.125), ctypes.c_float(1e-6), 4, 4, a["dq"], fake(8), fake(9),
+                                    fake(10), a["ws"], a["ws_bytes"], None, None, 0, None)
+    assert bwdw(dq=fake(6)) == _lib.INVALID_VALUE
+    assert bwdw(ws_bytes=need - 1) == _lib.WORKSPACE
