@@ -69,10 +69,10 @@ def kernel_sources_digest():
     return h.hexdigest()
 
 
-def stored_traffic(workload, kernel, variant="joint"):
+def stored_traffic(workload, kernel, variant="joint", window=None):
     """HBM bytes per launch of `kernel` from the committed counter summary of this workload (and entry
-    point variant), or None when there is none or the library sources changed since the counters were
-    read."""
+    point variant, and window for the local-window form), or None when there is none, it was read with
+    another window, or the library sources changed since the counters were read."""
     suffix = "" if variant in ("joint", "varlen") else f"_{variant}"  # (varlen workloads are named so)
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}{suffix}.md")
     if not os.path.exists(path):
@@ -83,6 +83,8 @@ def stored_traffic(workload, kernel, variant="joint"):
         return None
     rec = json.loads(text[start + 7:text.index("```", start + 7)])
     if rec.get("source_sha256") != kernel_sources_digest():
+        return None
+    if window is not None and rec.get("window") != list(window):
         return None
     ent = rec.get("kernels", {}).get(kernel)
     return None if ent is None else ent["hbm_bytes_per_launch"]
@@ -230,8 +232,9 @@ def main():
     # stage labels: the kernels' template instantiations, as a profiler names them
     sflag = "true" if streams else "false"
     targs = f"{D}, {sflag}, {'true' if varlen else 'false'}, {'true' if windowed else 'false'}"
-    stages = [f"{n}<{targs}> (fwd)" if n == "prenorm_kernel" else f"{n}<{targs}>" for n in _lib.FWD_STAGES]
-    stages += [f"{n}<{targs}> (bwd)" if n == "prenorm_kernel" else
+    pargs = targs.rsplit(",", 1)[0]  # the normalisation kernel has no window parameter
+    stages = [f"{n}<{pargs}> (fwd)" if n == "prenorm_kernel" else f"{n}<{targs}>" for n in _lib.FWD_STAGES]
+    stages += [f"{n}<{pargs}> (bwd)" if n == "prenorm_kernel" else
                (f"{n}<{sflag}>" if n == "dg_reduce_kernel" else f"{n}<{targs}>") for n in _lib.BWD_STAGES]
     nf = len(_lib.FWD_STAGES)
     dq_key, dkdv_key = f"bwd_dq_kernel<{targs}>", f"bwd_dkdv_kernel<{targs}>"
@@ -299,7 +302,7 @@ def main():
     achieved = per_pair[dom] * H * pairs / (dom_ms * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": stored_traffic(args.workload, dom, args.variant),
+                "traffic": stored_traffic(args.workload, dom, args.variant, args.window if windowed else None),
                 "flop_per_launch": per_pair[dom] * H * pairs, "avg_launch_ms": round(dom_ms, 5),
                 "avg_launch_ms_source": "timed region" if dom in live_ms else "breakdown pass"}
 

@@ -1,8 +1,9 @@
 """Pins for the local-window option of the fp64 oracle (the windowed attention of the diffusion-pipe
 summary's attention wrapper, read as a sliding window: query i sees keys i - left .. i + right).
 Independent of the oracle's formulas: finite differences, the closed form of a zero-width window,
-the unwindowed oracle restricted to each row's keys (brute force per row), and torch's fp64 causal
-scaled_dot_product_attention with autograd for the window (-1, 0)."""
+the unwindowed oracle restricted to each row's keys (brute force per row), the token-reversal symmetry
+that exchanges the two bounds, and torch's fp64 causal scaled_dot_product_attention with autograd for
+the windows (-1, 0) and, on reversed tokens, (0, -1)."""
 import numpy as np
 import pytest
 import torch
@@ -88,11 +89,31 @@ def test_each_row_is_attention_over_its_window(window):
         np.testing.assert_allclose(r[1][0, :, i], lse[0, :, 0], rtol=1e-12)
 
 
-def test_causal_window_matches_torch_sdpa_fp64():
+@pytest.mark.parametrize("window", [(4, 1), (0, 2), (3, 0)])
+def test_reversing_tokens_swaps_left_and_right(window):
+    """With every key valid, reading the sequence backwards turns the window (a, b) into (b, a): the
+    results on the reversed tokens are the reversed results, and the gain gradients are unchanged."""
+    q, k, v, gains, dout = rand_case(B=2, L=8, H=2, D=4, seed=6)
+    a = attention_fwd_bwd(q, k, v, gains, dout, None, 0.7, 1e-6, window=window)
+    rev = lambda t: t[:, ::-1].copy()
+    b = attention_fwd_bwd(rev(q), rev(k), rev(v), gains, rev(dout), None, 0.7, 1e-6, window=window[::-1])
+    for key in ("out", "dq", "dk", "dv"):
+        np.testing.assert_allclose(rev(b[key]), a[key], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(b["lse"][:, :, ::-1], a["lse"], rtol=1e-13)
+    np.testing.assert_allclose(b["dgains"], a["dgains"], rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("window", [(-1, 0), (0, -1)])
+def test_causal_window_matches_torch_sdpa_fp64(window):
+    """(-1, 0) is torch's causal attention; (0, -1), each query seeing itself and the keys after it, is
+    torch's causal attention on the token-reversed inputs, reversed back."""
     B, L, H, D = 2, 7, 3, 8
     q, k, v, gains, dout = rand_case(B, L, H, D, seed=5)
     scale, eps = 0.4, 1e-6
-    got = attention_fwd_bwd(q, k, v, gains, dout, None, scale, eps, window=(-1, 0))
+    got = attention_fwd_bwd(q, k, v, gains, dout, None, scale, eps, window=window)
+    if window == (0, -1):
+        q, k, v, dout = (t[:, ::-1].copy() for t in (q, k, v, dout))
+        got = {key: (val[:, ::-1] if key in ("out", "dq", "dk", "dv") else val) for key, val in got.items()}
     tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
     tg = torch.tensor(gains, dtype=torch.float64, requires_grad=True)
     nq = F.rms_norm(tq, (D,), weight=tg[0], eps=eps)
