@@ -20,6 +20,11 @@ them full attention on the same inputs (`full`).
 entry points (jattn_fwd_varlen + jattn_bwd_varlen; FLOPs over each sequence's own query-key pairs),
 and beside them the same sequences padded to the longest one through the joint entry points with a
 key mask (`padded`).
+
+--variant adaln (with --workload mmdit512 or mmdit768) times the adaLN-modulated QKV projection of
+both streams of a layer (jattn_adaln_qkv_fwd + jattn_adaln_qkv_bwd; FLOPs of its three GEMMs,
+2 T C 3C each for T tokens of width C), and beside it the same step written as torch's LayerNorm,
+modulation and Linear with autograd (`torch_unfused`).
 """
 import argparse
 import ctypes
@@ -45,7 +50,7 @@ def parse():
     ap.add_argument("--workload", default="mmdit512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--variant", choices=("joint", "streams", "varlen", "window"), default="joint")
+    ap.add_argument("--variant", choices=("joint", "streams", "varlen", "window", "adaln"), default="joint")
     ap.add_argument("--window", type=int, nargs=2, default=(256, 256), metavar=("LEFT", "RIGHT"))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 512 MiB device-to-device three times: under rocprofv3 --pmc its "
@@ -98,6 +103,9 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.variant == "adaln":
+        return bench_adaln(args, torch)
 
     from diffusion_transformer_joint_amd import _lib
     from diffusion_transformer_joint_amd.inputs import (VARLEN_WORKLOADS, WORKLOADS, flops, make_inputs,
@@ -351,6 +359,192 @@ def main():
         res["padded"] = padded
         res["padded"]["speedup"] = round(padded["ms_per_step"] / ms_step, 4)
     print(json.dumps(res), flush=True)
+
+
+ADALN_METRIC = "adaLN+QKV projection fwd+bwd TFLOP/s (both streams) bf16; % of bf16 MFMA peak"
+
+
+def bench_adaln(args, torch):
+    """The adaLN-modulated QKV projection of one layer, forward + backward over both streams."""
+    from diffusion_transformer_joint_amd import _lib
+    from diffusion_transformer_joint_amd.inputs import ADALN_WORKLOADS, adaln_flops, make_workload_adaln_inputs
+
+    if args.workload not in ADALN_WORKLOADS:
+        args.workload = "mmdit512"
+    w = ADALN_WORKLOADS[args.workload]
+    B, C = w.B, w.C
+    inp = make_workload_adaln_inputs(args.workload, seed=0)
+    dev = torch.device("cuda:0")
+    d = {k: tuple(t.to(dev).contiguous() for t in inp[k]) for k in ("x", "mod", "w", "bias", "dq", "dk", "dv")}
+    lib = _lib.load()
+    fws_bytes = int(lib.jattn_adaln_qkv_fwd_workspace_bytes(B, w.n_img, w.n_txt, C))
+    ws_bytes = int(lib.jattn_adaln_qkv_bwd_workspace_bytes(B, w.n_img, w.n_txt, C))
+    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ns = (w.n_img, w.n_txt)
+    q, k, v, dx = ([torch.empty(B, n, C, dtype=torch.bfloat16, device=dev) for n in ns] for _ in range(4))
+    dmod = [torch.empty(B, 2, C, dtype=torch.float32, device=dev) for _ in ns]
+    dw = [torch.empty(3 * C, C, dtype=torch.float32, device=dev) for _ in ns]
+    db = [torch.empty(3 * C, dtype=torch.float32, device=dev) for _ in ns]
+    pp = lambda t: _lib.PtrPair(t[0].data_ptr(), t[1].data_ptr())
+    keep = {n: pp(t) for n, t in (("x", d["x"]), ("mod", d["mod"]), ("w", d["w"]), ("bias", d["bias"]), ("q", q),
+                                  ("k", k), ("v", v), ("dq", d["dq"]), ("dk", d["dk"]), ("dv", d["dv"]), ("dx", dx),
+                                  ("dmod", dmod), ("dw", dw), ("db", db))}
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    nfs, nbs = len(_lib.ADALN_FWD_STAGES), len(_lib.ADALN_BWD_STAGES)
+
+    def fwd(events=None, n=nfs):
+        _lib.check("jattn_adaln_qkv_fwd", lib.jattn_adaln_qkv_fwd(
+            keep["x"].arg, keep["mod"].arg, keep["w"].arg, keep["bias"].arg, B, w.n_img, w.n_txt, C,
+            ctypes.c_float(inp["eps"]), keep["q"].arg, keep["k"].arg, keep["v"].arg, fws.data_ptr(), fws_bytes,
+            events, 0 if events is None else n, sp))
+
+    def bwd(events=None, n=nbs):
+        _lib.check("jattn_adaln_qkv_bwd", lib.jattn_adaln_qkv_bwd(
+            keep["x"].arg, keep["mod"].arg, keep["w"].arg, keep["dq"].arg, keep["dk"].arg, keep["dv"].arg, B,
+            w.n_img, w.n_txt, C, keep["dx"].arg, keep["dmod"].arg, keep["dw"].arg, keep["db"].arg, fws.data_ptr(),
+            fws_bytes, ws.data_ptr(), ws_bytes, events, 0 if events is None else n, sp))
+
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def handle(evs):
+        arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+        return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    targs = {"qkv_gemm_kernel": "256, 256, 2", "dh_gemm_kernel": "256, 256, 2", "dw_gemm_kernel": "128, 128, 4"}
+    label = lambda n: f"{n}<{targs[n]}>" if n in targs else n
+    stages = [label(n) + " (fwd)" if n == "modulate_kernel" else label(n) for n in _lib.ADALN_FWD_STAGES]
+    stages += [label(n) for n in _lib.ADALN_BWD_STAGES]
+    # timed region: the backward's first four stage events give the live durations of its GEMMs
+    ev = [[new_event() for _ in range(4)] for _ in range(K)]
+    bh = [handle(ev[i]) for i in range(K)]
+    start, end = new_event(), new_event()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        fwd()
+        bwd(bh[i][1], 4)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    live_ms = {label("dh_gemm_kernel"): sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K,
+               label("dw_gemm_kernel"): sum(ev[i][2].elapsed_time(ev[i][3]) for i in range(K)) / K}
+
+    KB = min(K, 50)
+    ev0 = [new_event() for _ in range(KB)]
+    evb = [[new_event() for _ in stages] for _ in range(KB)]
+    fh = [handle(evb[i][:nfs]) for i in range(KB)]
+    bhh = [handle(evb[i][nfs:]) for i in range(KB)]
+    torch.cuda.synchronize()
+    for i in range(KB):
+        ev0[i].record(stream)
+        fwd(fh[i][1])
+        bwd(bhh[i][1])
+    torch.cuda.synchronize()
+    kern_ms = {}
+    for j, name in enumerate(stages):
+        kern_ms[name] = sum((ev0[i] if j == 0 else evb[i][j - 1]).elapsed_time(evb[i][j]) for i in range(KB)) / KB
+    ms_fwd = sum(ev0[i].elapsed_time(evb[i][nfs - 1]) for i in range(KB)) / KB
+
+    fl = adaln_flops(B, w.n_img, w.n_txt, C)
+    tflops = fl["total"] / (ms_step * 1e-3) / 1e12
+    gemms = [label(n) for n in ("qkv_gemm_kernel", "dh_gemm_kernel", "dw_gemm_kernel")]
+    dom = max(gemms, key=lambda n: kern_ms[n])
+    dom_ms = live_ms.get(dom, kern_ms[dom])
+    achieved = fl["fwd"] / (dom_ms * 1e-3) / 1e12  # each GEMM is 2 T C 3C FLOPs per launch
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(args.workload, dom, "adaln"), "flop_per_launch": fl["fwd"],
+                "avg_launch_ms": round(dom_ms, 5),
+                "avg_launch_ms_source": "timed region" if dom in live_ms else "breakdown pass"}
+
+    unfused = time_adaln_unfused(torch, d, inp, stream, K, args.warmup)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_adaln(inp, args.cpu_seconds)
+    res = {
+        "metric": ADALN_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "variant": "adaln", "B": B, "n_img": w.n_img, "n_txt": w.n_txt,
+                   "C": C, "global_batch": B, "parallelism": "single-gpu"},
+        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_step - ms_fwd, 5),
+        "gflop_per_step": round(fl["total"] / 1e9, 3),
+        "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
+        "kernel_ms_timed_region": {k: round(v, 5) for k, v in live_ms.items()},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "torch_unfused": {"ms_per_step": round(unfused, 5), "speedup": round(unfused / ms_step, 4),
+                          "what": "torch: layer_norm, * (1 + scale) + shift, linear, split into q, k, v, and "
+                                  "autograd backward with the same upstream gradients, both streams, bf16"},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def time_adaln_unfused(torch, d, inp, stream, K, warmup):
+    """The same layer step in plain torch ops (LayerNorm, modulation and Linear as separate kernels,
+    hipBLASLt GEMMs), forward + autograd backward, timed the same way."""
+    import torch.nn.functional as F
+    C = inp["C"]
+    leaf = {k: tuple(t.clone().requires_grad_(True) for t in d[k]) for k in ("x", "mod", "w", "bias")}
+    wb = [t.detach().clone().to(torch.bfloat16).requires_grad_(True) for t in leaf["w"]]
+    bb = [t.detach().clone().to(torch.bfloat16).requires_grad_(True) for t in leaf["bias"]]
+
+    def step():
+        outs, grads = [], []
+        for s in range(2):
+            x = leaf["x"][s]
+            m = leaf["mod"][s].to(torch.bfloat16)
+            h = F.layer_norm(x, (C,), eps=inp["eps"]) * (1 + m[:, 1:2]) + m[:, 0:1]
+            y = F.linear(h, wb[s], bb[s])
+            outs += list(y.split(C, dim=-1))
+            grads += [d[n][s] for n in ("dq", "dk", "dv")]
+        torch.autograd.backward(outs, grads)
+
+    return time_steps(torch, stream, step, K, warmup)
+
+
+def cpu_baseline_adaln(inp, seconds):
+    """The fp64 oracle (adaln_qkv_fwd_bwd) on whole samples of the image stream, as many as fit the time
+    budget (at least one), in TFLOP/s of the GEMM FLOPs it covered."""
+    import numpy as np
+    from oracle import adaln_qkv_fwd_bwd
+    f64 = lambda t: t.double().numpy()
+    B, C, n = inp["B"], inp["C"], inp["n_img"]
+    t0 = time.perf_counter()
+    done = 0
+    while done < B and (done == 0 or time.perf_counter() - t0 < seconds):
+        sl = slice(done, done + 1)
+        g = lambda key: f64(inp[key][0][sl]).reshape(1, n, 1, C)
+        adaln_qkv_fwd_bwd(f64(inp["x"][0][sl]), f64(inp["mod"][0][sl]), f64(inp["w"][0]), f64(inp["bias"][0]), 1,
+                          inp["eps"], g("dq"), g("dk"), g("dv"))
+        done += 1
+    sec = time.perf_counter() - t0
+    flop = 3 * 2.0 * done * n * C * 3 * C
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = 1
+    return {"value": round(flop / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle (adaln_qkv_fwd_bwd) fwd+bwd on the first {done} of {B} samples of the "
+                      f"image stream ({n} tokens each) of the same seed-0 inputs, {sec:.1f} s wall; BLAS threads "
+                      "= cores", "seconds": round(sec, 2), "samples": done}
 
 
 def time_concat_split(lib, _lib, torch, q, k, v, dout, gains, vl, B, L, H, D, inp, stream, K, warmup):

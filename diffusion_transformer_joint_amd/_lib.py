@@ -1,4 +1,4 @@
-"""ctypes loader for libjattn.so (the C ABI declared in include/jattn.h).
+"""ctypes loader for libjattn.so (the C ABI declared in include/jattn.h and include/jattn_adaln.h).
 
 The library is built in-tree by ``diffusion_transformer_joint_amd.build``. Loading fails loudly if it
 is missing: there is no fallback implementation.
@@ -18,10 +18,13 @@ SUCCESS, INVALID_VALUE, NOT_SUPPORTED, WORKSPACE, HIP = range(5)
 EXPORTED = ("jattn_fwd", "jattn_fwd_ex", "jattn_fwd_workspace_bytes", "jattn_bwd", "jattn_bwd_ex", "jattn_bwd_workspace_bytes",
             "jattn_fwd_streams", "jattn_bwd_streams", "jattn_varlen_fwd_workspace_bytes",
             "jattn_varlen_bwd_workspace_bytes", "jattn_fwd_varlen", "jattn_bwd_varlen", "jattn_fwd_window",
-            "jattn_bwd_window", "jattn_status_string", "jattn_abi_version")
-ABI_VERSION = 6
+            "jattn_bwd_window", "jattn_adaln_qkv_fwd_workspace_bytes", "jattn_adaln_qkv_bwd_workspace_bytes",
+            "jattn_adaln_qkv_fwd", "jattn_adaln_qkv_bwd", "jattn_status_string", "jattn_abi_version")
+ABI_VERSION = 7
 FWD_STAGES = ("prenorm_kernel", "fwd_kernel")
 BWD_STAGES = ("prenorm_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "dg_reduce_kernel")
+ADALN_FWD_STAGES = ("modulate_kernel", "qkv_gemm_kernel")
+ADALN_BWD_STAGES = ("transpose_w_kernel", "dh_gemm_kernel", "rows_bwd_kernel", "dw_gemm_kernel", "reductions")
 
 _lock = threading.Lock()
 _lib = None
@@ -80,6 +83,15 @@ def load() -> ctypes.CDLL:
                                          ctypes.c_size_t, P, P, I, P]
         lib.jattn_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.jattn_bwd_workspace_bytes.argtypes = [I, I, I, I]
+        lib.jattn_adaln_qkv_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.jattn_adaln_qkv_fwd_workspace_bytes.argtypes = [I, I, I, I]
+        lib.jattn_adaln_qkv_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.jattn_adaln_qkv_bwd_workspace_bytes.argtypes = [I, I, I, I]
+        lib.jattn_adaln_qkv_fwd.restype = I
+        lib.jattn_adaln_qkv_fwd.argtypes = [P, P, P, P, I, I, I, I, F, P, P, P, P, ctypes.c_size_t, P, I, P]
+        lib.jattn_adaln_qkv_bwd.restype = I
+        lib.jattn_adaln_qkv_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, P, P, P, ctypes.c_size_t, P,
+                                            ctypes.c_size_t, P, I, P]
         lib.jattn_status_string.restype = ctypes.c_char_p
         lib.jattn_status_string.argtypes = [I]
         lib.jattn_abi_version.restype = I
@@ -98,6 +110,20 @@ class PtrPair:
     def __init__(self, a, b):
         self.arr = (ctypes.c_void_p * 2)(a, b)
         self.arg = ctypes.cast(self.arr, ctypes.c_void_p)
+
+
+def event_array(events):
+    """(pointer to a host array of hipEvent_t, count) for the stage-event arguments; (None, 0) for none.
+    The array is kept alive on the returned pointer object for the duration of the call."""
+    if not events:
+        return None, 0
+    for e in events:
+        if not e.cuda_event:  # torch creates the hipEvent_t on the first record
+            e.record()
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    ptr = ctypes.cast(arr, ctypes.c_void_p)
+    ptr._keep = arr
+    return ptr, len(events)
 
 
 def check(fn: str, status: int) -> None:

@@ -17,15 +17,17 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libjattn.so")
 
-SOURCES = ["jattn_prenorm.hip", "jattn_fwd.hip", "jattn_bwd.hip", "jattn_api.cpp"]
+SOURCES = ["jattn_prenorm.hip", "jattn_fwd.hip", "jattn_bwd.hip", "jattn_api.cpp", "adaln_qkv.hip", "adaln_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the code objects (the backend would otherwise form
 # them from plain float code); the host pass does not know the feature and warns, harmlessly.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                # MFMA accumulators in VGPRs: the score tiles feed VALU work right away, and the
-                # AGPR form costs two copies per element plus a hazard wait
-                "-mllvm", "-amdgpu-mfma-vgpr-form"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The attention kernels keep their MFMA accumulators in VGPRs: the score tiles feed VALU work right
+# away, and the AGPR form costs two copies per element plus a hazard wait. The projection GEMMs hold
+# 256 accumulators per lane and need the AGPRs.
+VGPR_ACC = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_ACC_SOURCES = {"adaln_qkv.hip"}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
                 f"-I{INCLUDE}", f"-I{CSRC}"]
 
@@ -40,6 +42,8 @@ def hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [hipcc(), f"--offload-arch={ARCH}", *COMMON_FLAGS, *DEVICE_FLAGS]
+    if src not in AGPR_ACC_SOURCES:
+        cmd += VGPR_ACC
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

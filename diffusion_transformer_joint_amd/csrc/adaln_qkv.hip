@@ -1,0 +1,637 @@
+// Kernels of the adaLN-modulated QKV projection (gfx950 / CDNA4): the adaLN modulation of the two
+// token streams of an MM-DiT layer followed by their per-stream QKV projections, forward and
+// backward (re-diffusion README: the DiT-layer box of the architecture flowchart applies adaLN with
+// the conditioning vector to each stream and computes Q, K and V per stream before the joint
+// attention; the design-notes table gives adaLN as scale + shift without gate).
+//
+//   h = LN(x) * (1 + scale_b) + shift_b            (LayerNorm over C channels, no affine parameters)
+//   [q | k | v] = h W^T + bias                     (W [3C, C]; q, k, v land in the attention's layout)
+//
+// Forward: one pass over x writes h (bf16, the MFMA operand, also kept for the weight gradient) and
+// the row statistics; one GEMM launch covers both streams, with the bias and the q/k/v split in its
+// epilogue. Backward: W is transposed once (3C x C, small), dh = dY W runs as the same kind of GEMM
+// as the forward, a row kernel applies the LayerNorm backward and sums the modulation gradients
+// per chunk of rows, and dW = dY^T h is a split-K GEMM over the tokens; fixed-order reductions
+// finish the modulation, weight and bias gradients, so every result is deterministic.
+//
+// GEMM structure: 256 threads, the output tile split 2 x 2 over the 4 waves; both operands stream
+// through LDS in 64-column contraction steps with direct-to-LDS buffer loads (no VGPR staging) into
+// 64 x 64 swizzled sub-tiles; v_mfma_f32_32x32x16_bf16 with fp32 accumulators. Operands stored with
+// the contraction index along memory rows (the weight gradient's) are read with ds_read_b64_tr_b16.
+#include "adaln_launch.h"
+#include "jattn_device.h"
+
+namespace jattn {
+
+using GL = Lay<64, kSwizzled>;     // one 64 x 64 bf16 sub-tile: 128-byte rows, swizzled 16-byte chunks
+using GT = DirectTile<64, GL, 4>;  // its direct-to-LDS loads, shared by the 4 waves of a workgroup
+constexpr int kSub = GT::ALLOC;    // elements per sub-tile
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Buffer resource of the 64 x 64 sub-tile of M at memory rows [row0, row0 + 64) and columns
+// [col0, col0 + 64) (col0 a multiple of 64, segments a multiple of 64 wide): rows at or past M.rows
+// read as zeros, and so does a sub-tile at or past M.width. All arguments are wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sub_rsrc(const MatRef& M, int row0, int col0) {
+  if (col0 >= M.width) return make_rsrc(M.p[0], 0u);
+  const int s = col0 / M.seg;
+  const uint16_t* base = (s == 0 ? M.p[0] : s == 1 ? M.p[1] : M.p[2]) + (col0 - s * M.seg);
+  return tile_rsrc<64>(base, M.rs, row0, M.rows);
+}
+
+// Main loop of one output tile: acc[i][j] += sum over k in [kbeg, kend) of A-block i x B-block j,
+// where the wave owns A rows wa * MA/2 + 32 i + [0, 32) and B rows wb * MB/2 + 32 j + [0, 32).
+// TR: operands stored with k along memory rows. NB: LDS stages in the ring.
+// (Member functions of a class template rather than function templates: the host-side pass of the
+// compiler rejects function templates that reach the LDS-DMA builtin from several kernels.)
+template <int MA, int MB, int NB, bool TR>
+struct GemmCore {
+  static constexpr int SA = MA / 64, SB = MB / 64;     // sub-tiles per operand and stage
+  static constexpr int STAGE = (SA + SB) * kSub;        // elements per stage
+  static constexpr int IA = MA / 64, IB = MB / 64;      // 32-row MFMA blocks per wave and operand
+  static constexpr int PER = (SA + SB) * GT::PER_WAVE;  // loads each wave issues per stage
+  static constexpr int BYTES = NB * STAGE * 2;
+  static_assert(GT::PER_WAVE == GT::MIN_PER_WAVE, "every wave issues the same number of loads");
+  static_assert(NB >= 2 && NB <= 5 && PER * (NB - 2) < 64, "ring depth");
+
+  GT ta, tb;
+  int wa, wb, wave, lane;
+
+  __device__ GemmCore(const GemmProblem& p) {
+    wave = wave_id();
+    lane = threadIdx.x & 63;
+    wa = wave & 1;
+    wb = wave >> 1;
+    ta.init(p.a.rs, wave, lane);
+    tb.init(p.b.rs, wave, lane);
+  }
+
+  __device__ void issue(const GemmProblem& p, int m0, int n0, int k0, __bf16* __restrict__ lds) const {
+#pragma unroll
+    for (int s = 0; s < SA; ++s)
+      ta.issue(TR ? sub_rsrc(p.a, k0, m0 + 64 * s) : sub_rsrc(p.a, m0 + 64 * s, k0), lds + s * kSub, wave);
+#pragma unroll
+    for (int s = 0; s < SB; ++s)
+      tb.issue(TR ? sub_rsrc(p.b, k0, n0 + 64 * s) : sub_rsrc(p.b, n0 + 64 * s, k0), lds + (SA + s) * kSub, wave);
+  }
+
+  // Operand fragment of the 32 rows starting at tile row r (a multiple of 32), k-step ks.
+  __device__ bf16x8 frag(const __bf16* __restrict__ op, int r, int ks) const {
+    const __bf16* sub = op + (r >> 6) * kSub;
+    if constexpr (TR)
+      return lds_tr_frag<GL>(sub, ks * 16, r & 63, lane);
+    else
+      return lds_row_frag<GL>(sub, (r & 63) + (lane & 31), ks * 16 + 8 * (lane >> 5));
+  }
+
+  __device__ void load(const __bf16* __restrict__ st, int ks, bf16x8 (&fa)[IA], bf16x8 (&fb)[IB]) const {
+#pragma unroll
+    for (int i = 0; i < IA; ++i) fa[i] = frag(st, wa * (MA / 2) + 32 * i, ks);
+#pragma unroll
+    for (int j = 0; j < IB; ++j) fb[j] = frag(st + SA * kSub, wb * (MB / 2) + 32 * j, ks);
+  }
+
+  // One contraction step (4 k-steps of 16). The fragments of k-step ks + 1 are read before the
+  // MFMAs of k-step ks start, into the other register set, so those MFMAs wait only for the older
+  // reads: with one wave per SIMD nothing else hides the LDS latency. The scheduling fences keep that
+  // order; left alone, the compiler keeps a few fragment registers and waits for each read right
+  // before its MFMAs.
+  __device__ void step(const __bf16* __restrict__ st, f32x16 (&acc)[IA][IB]) const {
+    constexpr int KS = kGemmK / 16;
+    bf16x8 fa[2][IA], fb[2][IB];
+    load(st, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = ks & 1;
+      if (ks + 1 < KS) load(st, ks + 1, fa[c ^ 1], fb[c ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < IA; ++i)
+#pragma unroll
+        for (int j = 0; j < IB; ++j) acc[i][j] = mfma(fa[c][i], fb[c][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+// Ring over the contraction steps [kbeg, kend) of one tile; `visit(stage, t)` runs after step t's
+// tile has landed and before its MFMAs (the weight-gradient kernel sums its B tiles there).
+template <int MA, int MB, int NB, bool TR, class Visit>
+__device__ __forceinline__ void gemm_tile(const GemmCore<MA, MB, NB, TR>& g, const GemmProblem& p, int m0, int n0,
+                                          int kbeg, int kend, __bf16* __restrict__ lds,
+                                          f32x16 (&acc)[MA / 64][MB / 64], Visit& visit) {
+  using GC = GemmCore<MA, MB, NB, TR>;
+#pragma unroll
+  for (int i = 0; i < GC::IA; ++i)
+#pragma unroll
+    for (int j = 0; j < GC::IB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int nk = max(0, (kend - kbeg + kGemmK - 1) / kGemmK);
+#pragma unroll
+  for (int t = 0; t < NB - 1; ++t)
+    if (t < nk) g.issue(p, m0, n0, kbeg + t * kGemmK, lds + t * GC::STAGE);
+  ring_barrier<GC::PER, NB - 2>(min(NB - 2, nk - 1));
+  for (int t = 0; t < nk; ++t) {
+    const int ahead = t + NB - 1;
+    if (ahead < nk) g.issue(p, m0, n0, kbeg + ahead * kGemmK, lds + (ahead % NB) * GC::STAGE);
+    const __bf16* st = lds + (t % NB) * GC::STAGE;
+    visit(st, t);
+    g.step(st, acc);
+    ring_barrier<GC::PER, NB - 2>(max(0, min(NB - 2, nk - t - 2)));
+  }
+}
+
+// The problem of stream s as a register copy, field by field with constant indices. (Selecting a
+// reference to a.pr[s] made the compiler copy the kernel arguments to scratch memory to index them.)
+__device__ __forceinline__ MatRef pick(const MatRef& x, const MatRef& y, bool s) {
+  MatRef m;
+  m.p[0] = s ? y.p[0] : x.p[0];
+  m.p[1] = s ? y.p[1] : x.p[1];
+  m.p[2] = s ? y.p[2] : x.p[2];
+  m.seg = s ? y.seg : x.seg;
+  m.rs = s ? y.rs : x.rs;
+  m.rows = s ? y.rows : x.rows;
+  m.width = s ? y.width : x.width;
+  return m;
+}
+
+__device__ __forceinline__ GemmProblem pick(const GemmArgs& a, bool s) {
+  const GemmProblem &x = a.pr[0], &y = a.pr[1];
+  GemmProblem p;
+  p.a = pick(x.a, y.a, s);
+  p.b = pick(x.b, y.b, s);
+  p.M = s ? y.M : x.M;
+  p.N = s ? y.N : x.N;
+  p.K = s ? y.K : x.K;
+  p.tiles_m = s ? y.tiles_m : x.tiles_m;
+  p.tiles_n = s ? y.tiles_n : x.tiles_n;
+  p.splits = s ? y.splits : x.splits;
+  p.kchunk = s ? y.kchunk : x.kchunk;
+  p.ntiles = s ? y.ntiles : x.ntiles;
+  p.out[0] = s ? y.out[0] : x.out[0];
+  p.out[1] = s ? y.out[1] : x.out[1];
+  p.out[2] = s ? y.out[2] : x.out[2];
+  p.out_seg = s ? y.out_seg : x.out_seg;
+  p.bias = s ? y.bias : x.bias;
+  p.colsum = s ? y.colsum : x.colsum;
+  return p;
+}
+
+// Output tile of workgroup blockIdx.x: the tiles of both problems in one list, dealt to the XCDs in
+// contiguous ranges (workgroup w runs on XCD w % 8), with the A-tile index fastest so that the tiles
+// sharing a block of B rows (token rows in the forward) run on one XCD and reuse them from its L2.
+struct TileId {
+  int s, tm, tn, sp;
+  bool ok;
+  __device__ explicit TileId(const GemmArgs& a) {
+    const int per = (a.ntiles + 7) >> 3;
+    const int j = (int)(blockIdx.x >> 3);
+    int t = (int)(blockIdx.x & 7) * per + j;
+    ok = j < per && t < a.ntiles;
+    if (!ok) {
+      s = tm = tn = sp = 0;
+      return;
+    }
+    s = t >= a.pr[0].ntiles ? 1 : 0;
+    const int tiles_m = s ? a.pr[1].tiles_m : a.pr[0].tiles_m, tiles_n = s ? a.pr[1].tiles_n : a.pr[0].tiles_n;
+    t -= s ? a.pr[0].ntiles : 0;
+    tm = t % tiles_m;
+    t /= tiles_m;
+    tn = t % tiles_n;
+    sp = t / tiles_n;
+  }
+};
+
+__host__ __device__ inline int gemm_grid(int ntiles) { return 8 * ((ntiles + 7) / 8); }
+
+struct NoVisit {
+  __device__ void operator()(const __bf16*, int) {}
+};
+
+// ---------------------------------------------------------------------------------------------
+// Forward: adaLN modulation, one wave per token row.
+
+template <int U>  // 16-byte chunks per lane (C <= 512 U)
+__global__ __launch_bounds__(256) void modulate_kernel(ModulateArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = (int)blockIdx.x * 4 + wave_id();
+  if (row >= a.T[0] + a.T[1]) return;
+  const int s = row >= a.T[0] ? 1 : 0;
+  const int r = row - (s ? a.T[0] : 0);
+  const int C = a.C, nch = C >> 3;
+  const int b = r / (s ? a.n[1] : a.n[0]);
+  const uint16_t* x = (s ? a.x[1] : a.x[0]) + (size_t)r * C;
+  u32x4 v[U];
+  float sum = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c8 = lane + 64 * u;
+    v[u] = c8 < nch ? *reinterpret_cast<const u32x4*>(x + c8 * 8) : (u32x4){0u, 0u, 0u, 0u};
+    float f[8];
+    unpack8(v[u], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += f[e];
+  }
+  const float mean = wave_sum(sum) / (float)C;
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (lane + 64 * u < nch) {
+      float f[8];
+      unpack8(v[u], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += (f[e] - mean) * (f[e] - mean);
+    }
+  }
+  const float rstd = 1.f / sqrtf(wave_sum(ss) / (float)C + a.eps);
+  const float* m = (s ? a.mod[1] : a.mod[0]) + (size_t)b * 2 * C;
+  uint16_t* h = (s ? a.h[1] : a.h[0]) + (size_t)r * C;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c8 = lane + 64 * u;
+    if (c8 < nch) {
+      const f32x4* sh = reinterpret_cast<const f32x4*>(m + c8 * 8);
+      const f32x4* sc = reinterpret_cast<const f32x4*>(m + C + c8 * 8);
+      const f32x4 sh0 = sh[0], sh1 = sh[1], sc0 = sc[0], sc1 = sc[1];
+      const float shv[8] = {sh0[0], sh0[1], sh0[2], sh0[3], sh1[0], sh1[1], sh1[2], sh1[3]};
+      const float scv[8] = {sc0[0], sc0[1], sc0[2], sc0[3], sc1[0], sc1[1], sc1[2], sc1[3]};
+      float f[8], o[8];
+      unpack8(v[u], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (f[e] - mean) * rstd * (1.f + scv[e]) + shv[e];
+      *reinterpret_cast<u32x4*>(h + c8 * 8) =
+          (u32x4){pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
+    }
+  }
+  if (lane == 0) {
+    float* st = (s ? a.stats[1] : a.stats[0]) + 2 * (size_t)r;
+    st[0] = mean;
+    st[1] = rstd;
+  }
+}
+
+// Forward GEMM: MFMA-A = W rows (output columns), MFMA-B = h rows (tokens), so each lane ends with
+// one token and runs of 4 consecutive output columns: 8-byte bf16 stores into q, k or v.
+template <int MA, int MB, int NB>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qkv_gemm_kernel(
+    GemmArgs a) {
+  using GC = GemmCore<MA, MB, NB, false>;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[GC::BYTES / 2];
+  __shared__ __attribute__((aligned(16))) float bias_lds[MA];
+  const TileId id(a);
+  if (!id.ok) return;
+  const GemmProblem p = pick(a, id.s != 0);
+  const GC g(p);
+  const int m0 = id.tm * MA, n0 = id.tn * MB;
+  // The tile's MA bias values go straight to LDS (one dword per lane, wave w the w-th 64), issued
+  // before the ring's first loads: each wave's loads complete in order, so the ring's first wait
+  // covers them too.
+  static_assert(MA <= 64 * 4, "one bias load per wave");
+  if (p.bias && g.wave < MA / 64) {
+    const int nb = min(MA, p.M - m0);
+    lds_load_dwords(make_rsrc(p.bias + m0, (uint32_t)__builtin_amdgcn_readfirstlane(nb * 4)), bias_lds + 64 * g.wave,
+                    (uint32_t)(64 * g.wave + g.lane) * 4u);
+  }
+  f32x16 acc[GC::IA][GC::IB];
+  NoVisit none;
+  gemm_tile(g, p, m0, n0, 0, p.K, smem, acc, none);
+#pragma unroll
+  for (int i = 0; i < GC::IA; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = m0 + g.wa * (MA / 2) + 32 * i + 8 * q + 4 * (g.lane >> 5);
+      if (n >= p.M) continue;
+      const int t = n >= 2 * p.out_seg ? 2 : n >= p.out_seg ? 1 : 0, c = n - t * p.out_seg;
+      uint16_t* out = static_cast<uint16_t*>(t == 0 ? p.out[0] : t == 1 ? p.out[1] : p.out[2]);
+      const int nl = g.wa * (MA / 2) + 32 * i + 8 * q + 4 * (g.lane >> 5);
+      const f32x4 b = p.bias ? *reinterpret_cast<const f32x4*>(bias_lds + nl) : (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < GC::IB; ++j) {
+        const int tok = n0 + g.wb * (MB / 2) + 32 * j + (g.lane & 31);
+        if (tok < p.N) {
+          const f32x16& v = acc[i][j];
+          *reinterpret_cast<u32x2*>(out + (size_t)tok * p.out_seg + c) =
+              (u32x2){pack2(v[4 * q] + b[0], v[4 * q + 1] + b[1]), pack2(v[4 * q + 2] + b[2], v[4 * q + 3] + b[3])};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Backward.
+
+// W [3C, C] -> W^T [C, 3C] through a padded LDS tile, 64 x 64 elements per workgroup.
+__global__ __launch_bounds__(256) void transpose_w_kernel(TransposeArgs a) {
+  __shared__ uint16_t t[64][66];
+  const int C = a.C, tiles_c = C / 64;
+  const int per = 3 * tiles_c * tiles_c;
+  const int s = (int)blockIdx.x >= per ? 1 : 0;
+  const int id = (int)blockIdx.x - s * per;
+  const int r0 = (id / tiles_c) * 64, c0 = (id % tiles_c) * 64;  // rows of W (0..3C), columns (0..C)
+  const uint16_t* w = s ? a.w[1] : a.w[0];
+  uint16_t* wt = s ? a.wt[1] : a.wt[0];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) t[r][tx] = w[(size_t)(r0 + r) * C + c0 + tx];
+  __syncthreads();
+  for (int c = ty; c < 64; c += 4) wt[(size_t)(c0 + c) * 3 * C + r0 + tx] = t[tx][c];
+}
+
+// dh = dY W as MFMA-A = W^T rows (channels), MFMA-B = dY rows (tokens; k runs over the three tensors
+// dq, dk, dv): fp32 stores of 4 consecutive channels per lane.
+template <int MA, int MB, int NB>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dh_gemm_kernel(
+    GemmArgs a) {
+  using GC = GemmCore<MA, MB, NB, false>;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[GC::BYTES / 2];
+  const TileId id(a);
+  if (!id.ok) return;
+  const GemmProblem p = pick(a, id.s != 0);
+  const GC g(p);
+  const int m0 = id.tm * MA, n0 = id.tn * MB;
+  f32x16 acc[GC::IA][GC::IB];
+  NoVisit none;
+  gemm_tile(g, p, m0, n0, 0, p.K, smem, acc, none);
+  float* dh = static_cast<float*>(p.out[0]);
+#pragma unroll
+  for (int i = 0; i < GC::IA; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = m0 + g.wa * (MA / 2) + 32 * i + 8 * q + 4 * (g.lane >> 5);
+      if (c >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < GC::IB; ++j) {
+        const int tok = n0 + g.wb * (MB / 2) + 32 * j + (g.lane & 31);
+        if (tok < p.N) {
+          const f32x16& v = acc[i][j];
+          *reinterpret_cast<f32x4*>(dh + (size_t)tok * p.out_seg + c) =
+              (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        }
+      }
+    }
+}
+
+// Column sums of the B tiles (dY over the tokens, for the bias gradient), in the workgroups of
+// A-tile 0 only: thread t sums 8 consecutive columns over rows t / (MB/8) + (256 / (MB/8)) * i.
+template <int MB>
+struct ColSumVisit {
+  static constexpr int CH = MB / 8, RG = kGemmThreads / CH;
+  float acc[8];  // this thread's 8 column sums
+  int sb_off;    // element offset of the B operand inside a stage
+  bool on;
+  __device__ void operator()(const __bf16* st, int) {
+    if (!on) return;
+    const int c8 = (int)threadIdx.x % CH, rg = (int)threadIdx.x / CH;
+    const __bf16* sub = st + sb_off + (c8 * 8 / 64) * kSub;
+#pragma unroll
+    for (int i = 0; i < 64 / RG; ++i) {
+      const bf16x8 f = lds_row_frag<GL>(sub, rg + RG * i, (c8 * 8) & 63);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += (float)f[e];
+    }
+  }
+};
+
+// dW = dY^T h as split-K over the tokens: MFMA-A = h^T (channels), MFMA-B = dY^T (output columns),
+// both read transposed from [64 tokens x 64] sub-tiles. Each split writes its fp32 partial
+// [splits, 3C, C] (lane = output column, 4 consecutive channels per store) and, in the workgroups
+// of A-tile 0, its partial column sums of dY.
+template <int MA, int MB, int NB>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dw_gemm_kernel(
+    GemmArgs a) {
+  using GC = GemmCore<MA, MB, NB, true>;
+  using CS = ColSumVisit<MB>;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[GC::BYTES / 2];
+  const TileId id(a);
+  if (!id.ok) return;
+  const GemmProblem p = pick(a, id.s != 0);
+  const GC g(p);
+  const int m0 = id.tm * MA, n0 = id.tn * MB;
+  const int kbeg = id.sp * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
+  f32x16 acc[GC::IA][GC::IB];
+  const bool sums = p.colsum != nullptr && id.tm == 0;
+  CS cs{{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, GC::SA * kSub, sums};
+  gemm_tile(g, p, m0, n0, kbeg, kend, smem, acc, cs);
+  float* part = static_cast<float*>(p.out[0]) + (size_t)id.sp * p.N * p.M;
+#pragma unroll
+  for (int i = 0; i < GC::IA; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = m0 + g.wa * (MA / 2) + 32 * i + 8 * q + 4 * (g.lane >> 5);
+      if (c >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < GC::IB; ++j) {
+        const int n = n0 + g.wb * (MB / 2) + 32 * j + (g.lane & 31);
+        if (n < p.N) {
+          const f32x16& v = acc[i][j];
+          *reinterpret_cast<f32x4*>(part + (size_t)n * p.M + c) = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        }
+      }
+    }
+  if (sums) {  // combine the row groups' column sums in LDS (the ring's last barrier has passed)
+    float* red = reinterpret_cast<float*>(smem);
+    const int c8 = (int)threadIdx.x % CS::CH, rg = (int)threadIdx.x / CS::CH;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rg * MB + c8 * 8 + e] = cs.acc[e];
+    __syncthreads();
+    if ((int)threadIdx.x < MB) {
+      float t = 0.f;
+      for (int r = 0; r < CS::RG; ++r) t += red[r * MB + threadIdx.x];
+      const int n = n0 + (int)threadIdx.x;
+      if (n < p.N) p.colsum[(size_t)id.sp * p.N + n] = t;
+    }
+  }
+}
+
+// LayerNorm backward and the modulation gradients' partial sums. Workgroup = (stream, sample,
+// chunk of kBwdRowChunk rows); wave w takes rows w, w + 4, ...; lane l holds channels 4 l + 256 u.
+// With g = dh (1 + scale):  dx = rstd (g - mean(g) - xhat mean(g xhat)),  and the chunk's partial
+// sums of dh (shift gradient) and dh xhat (scale gradient) per channel, combined over the 4 waves
+// in a fixed order.
+template <int U>  // float4 chunks per lane (C <= 256 U)
+__global__ __launch_bounds__(256) void rows_bwd_kernel(RowsBwdArgs a) {
+  __shared__ float red[2 * 4096];
+  const int s = (int)blockIdx.x >= a.blocks0 ? 1 : 0;
+  const int blk = (int)blockIdx.x - (s ? a.blocks0 : 0);
+  const int chunks = s ? a.chunks[1] : a.chunks[0], n = s ? a.n[1] : a.n[0];
+  const int b = blk / chunks, ch = blk - b * chunks;
+  const int C = a.C, lane = threadIdx.x & 63, wave = wave_id();
+  const int r_lo = ch * kBwdRowChunk, r_hi = min(n, r_lo + kBwdRowChunk);
+  const uint16_t* x = s ? a.x[1] : a.x[0];
+  const float* dh = s ? a.dh[1] : a.dh[0];
+  const float* st = s ? a.stats[1] : a.stats[0];
+  uint16_t* dx = s ? a.dx[1] : a.dx[0];
+  const float* sc = (s ? a.mod[1] : a.mod[0]) + (size_t)b * 2 * C + C;
+  float s1[U][4], acc0[U][4], acc1[U][4];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = 4 * lane + 256 * u;
+    const f32x4 v = c < C ? *reinterpret_cast<const f32x4*>(sc + c) : (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s1[u][e] = 1.f + v[e];
+      acc0[u][e] = acc1[u][e] = 0.f;
+    }
+  }
+  for (int r = r_lo + wave; r < r_hi; r += 4) {
+    const size_t row = (size_t)b * n + r;
+    const float mean = st[2 * row], rstd = st[2 * row + 1];
+    float g[U][4], xh[U][4], sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = 4 * lane + 256 * u;
+      if (c < C) {
+        const f32x4 d = *reinterpret_cast<const f32x4*>(dh + row * C + c);
+        float xf[4];
+        unpack4(*reinterpret_cast<const u32x2*>(x + row * C + c), xf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xh[u][e] = (xf[e] - mean) * rstd;
+          g[u][e] = d[e] * s1[u][e];
+          sg += g[u][e];
+          sgx += g[u][e] * xh[u][e];
+          acc0[u][e] += d[e];
+          acc1[u][e] += d[e] * xh[u][e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g[u][e] = xh[u][e] = 0.f;
+      }
+    }
+    const float mg = wave_sum(sg) / (float)C, mgx = wave_sum(sgx) / (float)C;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = 4 * lane + 256 * u;
+      if (c < C) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = rstd * (g[u][e] - mg - xh[u][e] * mgx);
+        *reinterpret_cast<u32x2*>(dx + row * C + c) = (u32x2){pack2(o[0], o[1]), pack2(o[2], o[3])};
+      }
+    }
+  }
+  // waves add their sums into LDS one after the other (fixed order)
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = 4 * lane + 256 * u;
+        if (c < C)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            red[c + e] = (w ? red[c + e] : 0.f) + acc0[u][e];
+            red[C + c + e] = (w ? red[C + c + e] : 0.f) + acc1[u][e];
+          }
+      }
+    }
+    __syncthreads();
+  }
+  float* part = (s ? a.part[1] : a.part[0]) + ((size_t)b * chunks + ch) * 2 * C;
+  for (int i = threadIdx.x; i < 2 * C; i += 256) part[i] = red[i];
+}
+
+// Modulation gradient [B, 2, C] of each stream: the sum over the chunks of [B, chunks, 2, C]
+// partials, in chunk order (inner = 2C).
+__global__ __launch_bounds__(256) void mod_reduce_kernel(ReduceArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int s = e >= a.len[0] ? 1 : 0;
+  const int64_t i = e - (s ? a.len[0] : 0);
+  if (i >= a.len[s ? 1 : 0]) return;
+  const int inner = s ? a.inner[1] : a.inner[0], count = s ? a.count[1] : a.count[0];
+  const int64_t outer = i / inner, in = i - outer * inner;
+  const float* p = (s ? a.part[1] : a.part[0]) + outer * count * inner + in;
+  float t = 0.f;
+  for (int c = 0; c < count; ++c) t += p[(int64_t)c * inner];
+  (s ? a.out[1] : a.out[0])[i] = t;
+}
+
+__global__ __launch_bounds__(256) void w_reduce_kernel(ReduceArgs a) {
+  const int64_t e4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t l0 = a.len[0], l1 = a.len[1];
+  if (e4 < l0 + l1) {
+    const int s = e4 >= l0 ? 1 : 0;
+    const int64_t i = e4 - (s ? l0 : 0), len = s ? l1 : l0;
+    const int count = s ? a.count[1] : a.count[0];
+    const float* p = (s ? a.part[1] : a.part[0]) + i;
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < count; ++c) t += *reinterpret_cast<const f32x4*>(p + (int64_t)c * len);
+    *reinterpret_cast<f32x4*>((s ? a.out[1] : a.out[0]) + i) = t;
+  }
+  // bias gradient: the first workgroups also reduce the column sums (clen = 3C per stream)
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t c0 = a.cout[0] ? a.clen[0] : 0, c1 = a.cout[1] ? a.clen[1] : 0;
+  if (j < c0 + c1) {
+    const int s = j >= c0 ? 1 : 0;
+    const int64_t i = j - (s ? c0 : 0), len = s ? c1 : c0;
+    const int count = s ? a.count[1] : a.count[0];
+    const float* p = (s ? a.cpart[1] : a.cpart[0]) + i;
+    float t = 0.f;
+    for (int c = 0; c < count; ++c) t += p[(int64_t)c * len];
+    (s ? a.cout[1] : a.cout[0])[i] = t;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Launchers
+
+constexpr int kQkvNB = 2, kDhNB = 2, kDwNB = 4;
+
+void launch_modulate(const ModulateArgs& a, hipStream_t stream) {
+  const int rows = a.T[0] + a.T[1];
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (a.C <= 1024)
+    hipLaunchKernelGGL(modulate_kernel<2>, grid, block, 0, stream, a);
+  else if (a.C <= 2048)
+    hipLaunchKernelGGL(modulate_kernel<4>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(modulate_kernel<8>, grid, block, 0, stream, a);
+}
+
+void launch_qkv_gemm(const GemmArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((qkv_gemm_kernel<kQkvMA, kQkvMB, kQkvNB>), dim3(gemm_grid(a.ntiles)), dim3(kGemmThreads), 0,
+                     stream, a);
+}
+
+void launch_dh_gemm(const GemmArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((dh_gemm_kernel<kDhMA, kDhMB, kDhNB>), dim3(gemm_grid(a.ntiles)), dim3(kGemmThreads), 0, stream,
+                     a);
+}
+
+void launch_dw_gemm(const GemmArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((dw_gemm_kernel<kDwMA, kDwMB, kDwNB>), dim3(gemm_grid(a.ntiles)), dim3(kGemmThreads), 0, stream,
+                     a);
+}
+
+void launch_transpose_w(const TransposeArgs& a, hipStream_t stream) {
+  const int per = 3 * (a.C / 64) * (a.C / 64);
+  hipLaunchKernelGGL(transpose_w_kernel, dim3(per * a.nstreams), dim3(256), 0, stream, a);
+}
+
+void launch_rows_bwd(const RowsBwdArgs& a, hipStream_t stream) {
+  const dim3 grid(a.blocks0 + a.B * a.chunks[1]), block(256);
+  if (a.C <= 1024)
+    hipLaunchKernelGGL(rows_bwd_kernel<4>, grid, block, 0, stream, a);
+  else if (a.C <= 2048)
+    hipLaunchKernelGGL(rows_bwd_kernel<8>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(rows_bwd_kernel<16>, grid, block, 0, stream, a);
+}
+
+void launch_mod_reduce(const ReduceArgs& a, hipStream_t stream) {
+  const int64_t n = (int64_t)a.len[0] + a.len[1];
+  hipLaunchKernelGGL(mod_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+}
+
+void launch_w_reduce(const ReduceArgs& a, hipStream_t stream) {
+  const int64_t n4 = ((int64_t)a.len[0] + a.len[1]) / 4;
+  const int64_t nc = (int64_t)(a.cout[0] ? a.clen[0] : 0) + (a.cout[1] ? a.clen[1] : 0);
+  const int64_t threads = n4 > nc ? n4 : nc;
+  hipLaunchKernelGGL(w_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+}
+
+}  // namespace jattn

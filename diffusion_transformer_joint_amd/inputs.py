@@ -1,7 +1,7 @@
-"""Seeded synthetic inputs for joint image+text attention.
+"""Seeded synthetic inputs for joint image+text attention and the adaLN-modulated QKV projection.
 
 This module only draws random tensors with the shapes of the workloads below; it holds none of the
-attention arithmetic, so both the fp64 oracle (test-side) and the HIP path can be fed from it.
+method's arithmetic, so both the fp64 oracles (test-side) and the HIP path can be fed from it.
 
 Workload shapes (the pages give no dataset we can use; these tensors stand in for the activations
 the models on the pages produce):
@@ -244,3 +244,59 @@ def varlen_flops(lengths, H: int, D: int) -> dict:
     pairs = sum(int(n) * int(n) for n in lengths)
     fwd = 4.0 * H * D * pairs
     return dict(fwd=fwd, bwd=2.5 * fwd, total=3.5 * fwd)
+
+
+# ------------------------------------------------------------------------------------------------
+# adaLN-modulated QKV projection (one call covers the image and the text stream of a layer)
+#
+# * ``mmdit512`` - B16, 1024 image + 77 text tokens, C = 768 (12 heads x 64): the 512 px model.
+# * ``mmdit768`` - B4, 2304 image + 77 text tokens, C = 3072 (24 heads x 128): the 768 px model.
+#
+# Recipe (one CPU generator seeded with ``seed``; for the image stream, then the text stream):
+#   x = randn(B, n_s, C).bfloat16();  mod = 0.2 * randn(B, 2, C) (fp32; row 0 shift, row 1 scale);
+#   w = ((2 rand(3C, C) - 1) / sqrt(C)).bfloat16()  and  bias = (2 rand(3C) - 1) / sqrt(C)  (torch's
+#   default Linear initialisation); dq, dk, dv = randn(B, n_s, C).bfloat16() each.
+# The modulation is zero at initialisation in the models on the pages and grows in training; 0.2
+# makes both of its terms matter in the tests.
+
+@dataclass(frozen=True)
+class AdalnWorkload:
+    name: str
+    B: int
+    n_img: int
+    n_txt: int
+    C: int
+
+
+ADALN_WORKLOADS = {
+    "mmdit512": AdalnWorkload("mmdit512", B=16, n_img=1024, n_txt=77, C=768),
+    "mmdit768": AdalnWorkload("mmdit768", B=4, n_img=2304, n_txt=77, C=3072),
+}
+
+
+def make_adaln_inputs(B: int, n_img: int, n_txt: int, C: int, seed: int = 0, mod_std: float = 0.2) -> dict:
+    g = torch.Generator().manual_seed(seed)
+    out = {k: [] for k in ("x", "mod", "w", "bias", "dq", "dk", "dv")}
+    for n in (n_img, n_txt):
+        out["x"].append(torch.randn(B, n, C, generator=g).bfloat16())
+        out["mod"].append(mod_std * torch.randn(B, 2, C, generator=g))
+        out["w"].append(((2 * torch.rand(3 * C, C, generator=g) - 1) / math.sqrt(C)).bfloat16())
+        out["bias"].append((2 * torch.rand(3 * C, generator=g) - 1) / math.sqrt(C))
+        for key in ("dq", "dk", "dv"):
+            out[key].append(torch.randn(B, n, C, generator=g).bfloat16())
+    res = {k: tuple(v) for k, v in out.items()}
+    res.update(B=B, n_img=n_img, n_txt=n_txt, C=C, eps=EPS)
+    return res
+
+
+def make_workload_adaln_inputs(name: str, seed: int = 0) -> dict:
+    w = ADALN_WORKLOADS[name]
+    return make_adaln_inputs(w.B, w.n_img, w.n_txt, w.C, seed=seed)
+
+
+def adaln_flops(B: int, n_img: int, n_txt: int, C: int) -> dict:
+    """Algorithmic FLOPs of the projection GEMMs: forward 2 T C 3C (T = all tokens of both streams);
+    backward twice that (dh = dY W and dW = dY^T h). The elementwise LayerNorm work is not counted."""
+    T = B * (n_img + n_txt)
+    fwd = 2.0 * T * C * 3 * C
+    return {"fwd": fwd, "bwd": 2 * fwd, "total": 3 * fwd}
