@@ -428,7 +428,7 @@ def bench_adaln(args, torch):
     torch.cuda.synchronize()
 
     K = args.steps
-    targs = {"qkv_gemm_kernel": "256, 256, 2", "dh_gemm_kernel": "256, 256, 2", "dw_gemm_kernel": "128, 128, 4"}
+    targs = {"qkv_gemm_kernel": "256, 128, 3", "dh_gemm_kernel": "256, 256, 2", "dw_gemm_kernel": "256, 256, 2"}
     label = lambda n: f"{n}<{targs[n]}>" if n in targs else n
     stages = [label(n) + " (fwd)" if n == "modulate_kernel" else label(n) for n in _lib.ADALN_FWD_STAGES]
     stages += [label(n) for n in _lib.ADALN_BWD_STAGES]

@@ -56,17 +56,26 @@ FwdLayout fwd_layout(const Sizes& z) {
   return l;
 }
 
-// Splits of the weight-gradient GEMM over the tokens: about 4096 tokens each, at most 8, each a
-// whole number of contraction steps.
-void dw_splits(int64_t T, int* splits, int* kchunk) {
-  int sp = (int)(T / 4096);
-  sp = sp < 1 ? 1 : sp > 8 ? 8 : sp;
-  int64_t chunk = (T + sp - 1) / sp;
-  chunk = (chunk + kGemmK - 1) / kGemmK * kGemmK;
-  if (chunk < kGemmK) chunk = kGemmK;
-  *kchunk = (int)chunk;
-  *splits = (int)((T + chunk - 1) / chunk);
-  if (*splits < 1) *splits = 1;
+// Splits of the weight-gradient GEMM over the tokens. Its output has only (C / MA) (3C / MB) tiles,
+// too few to fill 256 CUs when C is small, so the tokens are split: each stream gets
+// floor(steps_s / target) splits (at least one), where target is the contraction steps per
+// workgroup that spread the whole launch's work over 256 workgroups. With one split the GEMM writes
+// the weight and bias gradients directly; with more, fp32 partials that a reduction sums in order.
+void dw_splits(const int64_t T[2], int C, int splits[2], int kchunk[2]) {
+  const int64_t tiles = (int64_t)((C + jattn::kDwMA - 1) / jattn::kDwMA) * ((3 * C + jattn::kDwMB - 1) / jattn::kDwMB);
+  int64_t steps[2], total = 0;
+  for (int s = 0; s < 2; ++s) {
+    steps[s] = (T[s] + kGemmK - 1) / kGemmK;
+    total += steps[s] * tiles;
+  }
+  const int64_t target = total > 0 ? (total + 255) / 256 : 1;
+  for (int s = 0; s < 2; ++s) {
+    int64_t sp = steps[s] / target;
+    sp = sp < 1 ? 1 : sp > 64 ? 64 : sp;
+    const int64_t per = steps[s] > 0 ? (steps[s] + sp - 1) / sp : 1;  // steps per split
+    kchunk[s] = (int)(per * kGemmK);
+    splits[s] = steps[s] > 0 ? (int)((steps[s] + per - 1) / per) : 1;
+  }
 }
 
 struct BwdLayout {
@@ -78,9 +87,9 @@ BwdLayout bwd_layout(const Sizes& z) {
   BwdLayout l;
   const size_t C = z.C;
   size_t off = 0;
+  dw_splits(z.T, z.C, l.splits, l.kchunk);
   for (int s = 0; s < 2; ++s) {
     l.chunks[s] = (z.n[s] + kBwdRowChunk - 1) / kBwdRowChunk;
-    dw_splits(z.T[s], &l.splits[s], &l.kchunk[s]);
     const bool on = z.T[s] > 0;
     l.wt[s] = off;
     off += on ? round_up(3 * C * C * 2, 256) : 0;
@@ -88,10 +97,11 @@ BwdLayout bwd_layout(const Sizes& z) {
     off += round_up((size_t)z.T[s] * C * 4, 256);
     l.modpart[s] = off;
     off += round_up((size_t)z.B * l.chunks[s] * 2 * C * 4, 256);
+    const bool parts = on && l.splits[s] > 1;  // (one split writes the gradients directly)
     l.wpart[s] = off;
-    off += on ? round_up((size_t)l.splits[s] * 3 * C * C * 4, 256) : 0;
+    off += parts ? round_up((size_t)l.splits[s] * 3 * C * C * 4, 256) : 0;
     l.cpart[s] = off;
-    off += on ? round_up((size_t)l.splits[s] * 3 * C * 4, 256) : 0;
+    off += parts ? round_up((size_t)l.splits[s] * 3 * C * 4, 256) : 0;
   }
   l.total = off;
   return l;
@@ -329,11 +339,12 @@ jattn_status jattn_adaln_qkv_bwd(const void* const x[2], const float* const mod[
     r.K = (int)z.T[s];
     r.splits = bl.splits[s];
     r.kchunk = bl.kchunk[s];
-    r.out[0] = ws + bl.wpart[s];
+    const bool direct = bl.splits[s] == 1;  // one split: straight into dw and dbias
+    r.out[0] = direct ? static_cast<void*>(on ? dw[s] : nullptr) : static_cast<void*>(ws + bl.wpart[s]);
     r.out[1] = r.out[2] = nullptr;
     r.out_seg = C;
     r.bias = nullptr;
-    r.colsum = on && dbias[s] ? reinterpret_cast<float*>(ws + bl.cpart[s]) : nullptr;
+    r.colsum = on && dbias[s] ? (direct ? dbias[s] : reinterpret_cast<float*>(ws + bl.cpart[s])) : nullptr;
     if (!on) r.M = 0;
     // LayerNorm backward
     ra.x[s] = static_cast<const uint16_t*>(on ? x[s] : nullptr);
@@ -354,11 +365,14 @@ jattn_status jattn_adaln_qkv_bwd(const void* const x[2], const float* const mod[
     rm.inner[s] = 2 * C;
     rm.clen[s] = 0;
     rw.part[s] = reinterpret_cast<const float*>(ws + bl.wpart[s]);
+    // reduction of the split partials; a stream with one split has nothing to reduce, an empty
+    // stream gets zeros (count 0)
+    const bool reduce = !on || !direct;
     rw.out[s] = dw[s];
     rw.cpart[s] = on ? r.colsum : rw.part[s];
-    rw.cout[s] = on ? (r.colsum ? dbias[s] : nullptr) : dbias[s];
+    rw.cout[s] = reduce ? (on ? (r.colsum ? dbias[s] : nullptr) : dbias[s]) : nullptr;
     rw.count[s] = on ? bl.splits[s] : 0;
-    rw.len[s] = dw[s] ? 3 * C * C : 0;
+    rw.len[s] = reduce && dw[s] ? 3 * C * C : 0;
     rw.inner[s] = 0;
     rw.clen[s] = 3 * C;
   }

@@ -101,8 +101,8 @@ void launch_mod_reduce(const ReduceArgs& a, hipStream_t stream);
 void launch_w_reduce(const ReduceArgs& a, hipStream_t stream);
 
 // Output-tile sizes of the three GEMMs (MFMA-A rows x MFMA-B rows per workgroup).
-constexpr int kQkvMA = 256, kQkvMB = 256;
+constexpr int kQkvMA = 256, kQkvMB = 128;
 constexpr int kDhMA = 256, kDhMB = 256;
-constexpr int kDwMA = 128, kDwMB = 128;
+constexpr int kDwMA = 256, kDwMB = 256;
 
 }  // namespace jattn

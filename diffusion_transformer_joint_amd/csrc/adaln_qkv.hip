@@ -15,9 +15,12 @@
 // finish the modulation, weight and bias gradients, so every result is deterministic.
 //
 // GEMM structure: 256 threads, the output tile split 2 x 2 over the 4 waves; both operands stream
-// through LDS in 64-column contraction steps with direct-to-LDS buffer loads (no VGPR staging) into
-// 64 x 64 swizzled sub-tiles; v_mfma_f32_32x32x16_bf16 with fp32 accumulators. Operands stored with
-// the contraction index along memory rows (the weight gradient's) are read with ds_read_b64_tr_b16.
+// through an LDS ring in 64-wide contraction steps with direct-to-LDS buffer loads (no VGPR
+// staging) into 64 x 64 swizzled sub-tiles; v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
+// Operands stored with the contraction index along memory rows (the weight gradient's) are read
+// with ds_read_b64_tr_b16. The buffer descriptors of a tile's sub-tiles are set up once per tile and
+// advanced per step with a pointer add: at one wave per SIMD every scalar instruction of the step
+// sits in the MFMA stream (recomputing them per step cost a third of the step).
 #include "adaln_launch.h"
 #include "jattn_device.h"
 
@@ -27,20 +30,95 @@ using GL = Lay<64, kSwizzled>;     // one 64 x 64 bf16 sub-tile: 128-byte rows, 
 using GT = DirectTile<64, GL, 4>;  // its direct-to-LDS loads, shared by the 4 waves of a workgroup
 constexpr int kSub = GT::ALLOC;    // elements per sub-tile
 
+// The sub-tiles of one operand in one output tile, as wave-uniform scalar state: S sub-tiles of 64
+// operand rows each (rows mode: memory rows r0 + 64 s, contraction along the memory columns, through
+// the column segments of the MatRef; transposed mode: memory columns c0 + 64 s, contraction along the
+// memory rows). base[s] addresses the current step's sub-tile, range[s] the bytes from there that
+// hold valid rows (later rows, and sub-tiles past the matrix width, read as zeros).
+template <int S, bool TR>
+struct OpStream {
+  const uint16_t* base[S];
+  uint32_t range[S];
+  // rows mode: the segment and column of the current step
+  const uint16_t *p0, *p1, *p2;
+
+  // Segment k's pointer as arithmetic rather than a select: the compiler turns a select between two
+  // members into a load at a computed offset, which keeps the whole object in scratch memory.
+  __device__ __forceinline__ const uint16_t* seg_ptr(int k) const {
+    const uintptr_t u = (uintptr_t)p0 * (uintptr_t)(k == 0) + (uintptr_t)p1 * (uintptr_t)(k == 1) +
+                        (uintptr_t)p2 * (uintptr_t)(k == 2);
+    return reinterpret_cast<const uint16_t*>(u);
+  }
+  size_t row_off[S];
+  int seg, col, kseg, rs, rows;
+
+  __device__ __forceinline__ void init(const MatRef& M, int r0, int k0) {
+    rs = M.rs;
+    rows = M.rows;
+    if constexpr (!TR) {
+      p0 = M.p[0];
+      p1 = M.p[1];
+      p2 = M.p[2];
+      seg = M.seg;
+      kseg = k0 / M.seg;  // (once per tile)
+      col = k0 - kseg * M.seg;
+      const uint16_t* sp = seg_ptr(kseg);
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int row0 = r0 + 64 * s, valid = M.rows - row0;
+        row_off[s] = (size_t)row0 * M.rs;
+        range[s] = __builtin_amdgcn_readfirstlane(valid > 0 ? (uint32_t)((valid - 1) * M.rs + 64) * 2u : 0u);
+        base[s] = sp + row_off[s] + col;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int c0 = r0 + 64 * s;
+        const int sg = c0 < M.width ? c0 / M.seg : 0;
+        const uint16_t* sp = sg == 0 ? M.p[0] : sg == 1 ? M.p[1] : M.p[2];
+        base[s] = sp + (c0 - sg * M.seg) + (size_t)k0 * M.rs;
+        const int valid = M.rows - k0;
+        range[s] = __builtin_amdgcn_readfirstlane(c0 < M.width && valid > 0 ? (uint32_t)((valid - 1) * M.rs + 64) * 2u
+                                                                              : 0u);
+      }
+    }
+  }
+
+  // Move to the next contraction step.
+  __device__ __forceinline__ void advance() {
+    if constexpr (!TR) {
+      col += kGemmK;
+      if (col >= seg) {
+        col = 0;
+        ++kseg;
+      }
+      const uint16_t* sp = seg_ptr(kseg);
+#pragma unroll
+      for (int s = 0; s < S; ++s) base[s] = sp + row_off[s] + col;
+    } else {
+      const uint32_t step = (uint32_t)kGemmK * (uint32_t)rs * 2u;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        base[s] += (size_t)kGemmK * rs;
+        range[s] = range[s] > step ? range[s] - step : 0u;
+      }
+    }
+  }
+
+  // (The base is wave-uniform by construction; saying so keeps the descriptor in scalar registers
+  // instead of a loop over its per-lane values, which the compiler emits when it cannot prove it.)
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int s) const {
+    const uint64_t u = reinterpret_cast<uint64_t>(base[s]);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return make_rsrc(reinterpret_cast<const void*>(lo | (hi << 32)), range[s]);
+  }
+};
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
   return x;
-}
-
-// Buffer resource of the 64 x 64 sub-tile of M at memory rows [row0, row0 + 64) and columns
-// [col0, col0 + 64) (col0 a multiple of 64, segments a multiple of 64 wide): rows at or past M.rows
-// read as zeros, and so does a sub-tile at or past M.width. All arguments are wave-uniform.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t sub_rsrc(const MatRef& M, int row0, int col0) {
-  if (col0 >= M.width) return make_rsrc(M.p[0], 0u);
-  const int s = col0 / M.seg;
-  const uint16_t* base = (s == 0 ? M.p[0] : s == 1 ? M.p[1] : M.p[2]) + (col0 - s * M.seg);
-  return tile_rsrc<64>(base, M.rs, row0, M.rows);
 }
 
 // Main loop of one output tile: acc[i][j] += sum over k in [kbeg, kend) of A-block i x B-block j,
@@ -61,7 +139,7 @@ struct GemmCore {
   GT ta, tb;
   int wa, wb, wave, lane;
 
-  __device__ GemmCore(const GemmProblem& p) {
+  __device__ __forceinline__ GemmCore(const GemmProblem& p) {
     wave = wave_id();
     lane = threadIdx.x & 63;
     wa = wave & 1;
@@ -70,17 +148,16 @@ struct GemmCore {
     tb.init(p.b.rs, wave, lane);
   }
 
-  __device__ void issue(const GemmProblem& p, int m0, int n0, int k0, __bf16* __restrict__ lds) const {
+  // Issue the loads of the step the streams point at.
+  __device__ __forceinline__ void issue(const OpStream<SA, TR>& sa, const OpStream<SB, TR>& sb, __bf16* __restrict__ lds) const {
 #pragma unroll
-    for (int s = 0; s < SA; ++s)
-      ta.issue(TR ? sub_rsrc(p.a, k0, m0 + 64 * s) : sub_rsrc(p.a, m0 + 64 * s, k0), lds + s * kSub, wave);
+    for (int s = 0; s < SA; ++s) ta.issue(sa.rsrc(s), lds + s * kSub, wave);
 #pragma unroll
-    for (int s = 0; s < SB; ++s)
-      tb.issue(TR ? sub_rsrc(p.b, k0, n0 + 64 * s) : sub_rsrc(p.b, n0 + 64 * s, k0), lds + (SA + s) * kSub, wave);
+    for (int s = 0; s < SB; ++s) tb.issue(sb.rsrc(s), lds + (SA + s) * kSub, wave);
   }
 
   // Operand fragment of the 32 rows starting at tile row r (a multiple of 32), k-step ks.
-  __device__ bf16x8 frag(const __bf16* __restrict__ op, int r, int ks) const {
+  __device__ __forceinline__ bf16x8 frag(const __bf16* __restrict__ op, int r, int ks) const {
     const __bf16* sub = op + (r >> 6) * kSub;
     if constexpr (TR)
       return lds_tr_frag<GL>(sub, ks * 16, r & 63, lane);
@@ -88,7 +165,7 @@ struct GemmCore {
       return lds_row_frag<GL>(sub, (r & 63) + (lane & 31), ks * 16 + 8 * (lane >> 5));
   }
 
-  __device__ void load(const __bf16* __restrict__ st, int ks, bf16x8 (&fa)[IA], bf16x8 (&fb)[IB]) const {
+  __device__ __forceinline__ void load(const __bf16* __restrict__ st, int ks, bf16x8 (&fa)[IA], bf16x8 (&fb)[IB]) const {
 #pragma unroll
     for (int i = 0; i < IA; ++i) fa[i] = frag(st, wa * (MA / 2) + 32 * i, ks);
 #pragma unroll
@@ -100,7 +177,10 @@ struct GemmCore {
   // reads: with one wave per SIMD nothing else hides the LDS latency. The scheduling fences keep that
   // order; left alone, the compiler keeps a few fragment registers and waits for each read right
   // before its MFMAs.
-  __device__ void step(const __bf16* __restrict__ st, f32x16 (&acc)[IA][IB]) const {
+  // `before_last` runs after the last k-step's fragments are read and before its MFMAs: the ring
+  // barrier goes there, so those MFMAs overlap the next stage's first fragment reads.
+  template <class F>
+  __device__ __forceinline__ void step(const __bf16* __restrict__ st, f32x16 (&acc)[IA][IB], F before_last) const {
     constexpr int KS = kGemmK / 16;
     bf16x8 fa[2][IA], fb[2][IB];
     load(st, 0, fa[0], fb[0]);
@@ -108,6 +188,7 @@ struct GemmCore {
     for (int ks = 0; ks < KS; ++ks) {
       const int c = ks & 1;
       if (ks + 1 < KS) load(st, ks + 1, fa[c ^ 1], fb[c ^ 1]);
+      else before_last();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < IA; ++i)
@@ -132,17 +213,28 @@ __device__ __forceinline__ void gemm_tile(const GemmCore<MA, MB, NB, TR>& g, con
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   const int nk = max(0, (kend - kbeg + kGemmK - 1) / kGemmK);
+  OpStream<GC::SA, TR> sa;
+  OpStream<GC::SB, TR> sb;
+  sa.init(p.a, m0, kbeg);
+  sb.init(p.b, n0, kbeg);
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t)
-    if (t < nk) g.issue(p, m0, n0, kbeg + t * kGemmK, lds + t * GC::STAGE);
+    if (t < nk) {
+      g.issue(sa, sb, lds + t * GC::STAGE);
+      sa.advance();
+      sb.advance();
+    }
   ring_barrier<GC::PER, NB - 2>(min(NB - 2, nk - 1));
   for (int t = 0; t < nk; ++t) {
     const int ahead = t + NB - 1;
-    if (ahead < nk) g.issue(p, m0, n0, kbeg + ahead * kGemmK, lds + (ahead % NB) * GC::STAGE);
+    if (ahead < nk) {
+      g.issue(sa, sb, lds + (ahead % NB) * GC::STAGE);
+      sa.advance();
+      sb.advance();
+    }
     const __bf16* st = lds + (t % NB) * GC::STAGE;
     visit(st, t);
-    g.step(st, acc);
-    ring_barrier<GC::PER, NB - 2>(max(0, min(NB - 2, nk - t - 2)));
+    g.step(st, acc, [&]() { ring_barrier<GC::PER, NB - 2>(max(0, min(NB - 2, nk - t - 2))); });
   }
 }
 
@@ -182,32 +274,44 @@ __device__ __forceinline__ GemmProblem pick(const GemmArgs& a, bool s) {
   return p;
 }
 
-// Output tile of workgroup blockIdx.x: the tiles of both problems in one list, dealt to the XCDs in
-// contiguous ranges (workgroup w runs on XCD w % 8), with the A-tile index fastest so that the tiles
-// sharing a block of B rows (token rows in the forward) run on one XCD and reuse them from its L2.
+// Output tile of workgroup blockIdx.x. Workgroup w runs on XCD w % 8 as that XCD's (w / 8)-th. Each
+// problem's tiles are dealt to the XCDs in contiguous ranges, problem by problem, so every XCD gets
+// the same share of each stream (with one list for both, the XCDs holding the short text-stream
+// tiles idled while the others ran the image stream's). Within a range, tiles go in groups of
+// kGroupM A-tiles: consecutive tiles walk the group's A-tiles for one B-tile, then the next B-tile,
+// so the ~32 workgroups an XCD runs at once share 4 blocks of A rows and ~8 of B rows in its L2
+// (A-tile fastest over all of A re-streamed the forward's weight once per block of tokens).
+constexpr int kGroupM = 4;
+
 struct TileId {
   int s, tm, tn, sp;
   bool ok;
   __device__ explicit TileId(const GemmArgs& a) {
-    const int per = (a.ntiles + 7) >> 3;
-    const int j = (int)(blockIdx.x >> 3);
-    int t = (int)(blockIdx.x & 7) * per + j;
-    ok = j < per && t < a.ntiles;
+    const int x = (int)(blockIdx.x & 7), j = (int)(blockIdx.x >> 3);
+    const int nt0 = a.pr[0].ntiles, nt1 = a.pr[1].ntiles;
+    const int per0 = (nt0 + 7) >> 3, per1 = (nt1 + 7) >> 3;
+    s = j < per0 ? 0 : 1;
+    int t = s ? x * per1 + (j - per0) : x * per0 + j;
+    ok = s ? (j - per0 < per1 && t < nt1) : t < nt0;
     if (!ok) {
       s = tm = tn = sp = 0;
       return;
     }
-    s = t >= a.pr[0].ntiles ? 1 : 0;
     const int tiles_m = s ? a.pr[1].tiles_m : a.pr[0].tiles_m, tiles_n = s ? a.pr[1].tiles_n : a.pr[0].tiles_n;
-    t -= s ? a.pr[0].ntiles : 0;
-    tm = t % tiles_m;
-    t /= tiles_m;
-    tn = t % tiles_n;
-    sp = t / tiles_n;
+    const int per_split = tiles_m * tiles_n;
+    sp = t / per_split;
+    t -= sp * per_split;
+    const int group = t / (kGroupM * tiles_n), first = group * kGroupM;
+    const int gm = min(tiles_m - first, kGroupM);
+    const int r = t - group * kGroupM * tiles_n;
+    tm = first + r % gm;
+    tn = r / gm;
   }
 };
 
-__host__ __device__ inline int gemm_grid(int ntiles) { return 8 * ((ntiles + 7) / 8); }
+__host__ __device__ inline int gemm_grid(const GemmArgs& a) {
+  return 8 * ((a.pr[0].ntiles + 7) / 8 + (a.pr[1].ntiles + 7) / 8);
+}
 
 struct NoVisit {
   __device__ void operator()(const __bf16*, int) {}
@@ -226,6 +330,19 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModulateArgs a) {
   const int C = a.C, nch = C >> 3;
   const int b = r / (s ? a.n[1] : a.n[0]);
   const uint16_t* x = (s ? a.x[1] : a.x[0]) + (size_t)r * C;
+  const float* m = (s ? a.mod[1] : a.mod[0]) + (size_t)b * 2 * C;
+  // the row and its sample's shift and scale, all loads issued before the reductions
+  f32x4 shv4[U][2], scv4[U][2];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c8 = lane + 64 * u;
+    if (c8 < nch) {
+      shv4[u][0] = *reinterpret_cast<const f32x4*>(m + c8 * 8);
+      shv4[u][1] = *reinterpret_cast<const f32x4*>(m + c8 * 8 + 4);
+      scv4[u][0] = *reinterpret_cast<const f32x4*>(m + C + c8 * 8);
+      scv4[u][1] = *reinterpret_cast<const f32x4*>(m + C + c8 * 8 + 4);
+    }
+  }
   u32x4 v[U];
   float sum = 0.f;
 #pragma unroll
@@ -249,15 +366,12 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModulateArgs a) {
     }
   }
   const float rstd = 1.f / sqrtf(wave_sum(ss) / (float)C + a.eps);
-  const float* m = (s ? a.mod[1] : a.mod[0]) + (size_t)b * 2 * C;
   uint16_t* h = (s ? a.h[1] : a.h[0]) + (size_t)r * C;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int c8 = lane + 64 * u;
     if (c8 < nch) {
-      const f32x4* sh = reinterpret_cast<const f32x4*>(m + c8 * 8);
-      const f32x4* sc = reinterpret_cast<const f32x4*>(m + C + c8 * 8);
-      const f32x4 sh0 = sh[0], sh1 = sh[1], sc0 = sc[0], sc1 = sc[1];
+      const f32x4 sh0 = shv4[u][0], sh1 = shv4[u][1], sc0 = scv4[u][0], sc1 = scv4[u][1];
       const float shv[8] = {sh0[0], sh0[1], sh0[2], sh0[3], sh1[0], sh1[1], sh1[2], sh1[3]};
       const float scv[8] = {sc0[0], sc0[1], sc0[2], sc0[3], sc1[0], sc1[1], sc1[2], sc1[3]};
       float f[8], o[8];
@@ -384,12 +498,12 @@ struct ColSumVisit {
   float acc[8];  // this thread's 8 column sums
   int sb_off;    // element offset of the B operand inside a stage
   bool on;
-  __device__ void operator()(const __bf16* st, int) {
+  __device__ __forceinline__ void operator()(const __bf16* st, int) {
     if (!on) return;
     const int c8 = (int)threadIdx.x % CH, rg = (int)threadIdx.x / CH;
     const __bf16* sub = st + sb_off + (c8 * 8 / 64) * kSub;
 #pragma unroll
-    for (int i = 0; i < 64 / RG; ++i) {
+    for (int i = 0; i < kGemmK / RG; ++i) {
       const bf16x8 f = lds_row_frag<GL>(sub, rg + RG * i, (c8 * 8) & 63);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += (float)f[e];
@@ -478,17 +592,42 @@ __global__ __launch_bounds__(256) void rows_bwd_kernel(RowsBwdArgs a) {
       acc0[u][e] = acc1[u][e] = 0.f;
     }
   }
-  for (int r = r_lo + wave; r < r_hi; r += 4) {
+  // each wave keeps the loads of RPW rows (r, r + 4, ...) in flight before computing any of them
+  constexpr int RPW = U <= 4 ? 4 : U <= 8 ? 2 : 1;
+  for (int r0 = r_lo + wave; r0 < r_hi; r0 += 4 * RPW) {
+    f32x4 dv[RPW][U];
+    u32x2 xv[RPW][U];
+    f32x2 ms[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const int r = r0 + 4 * q;
+      if (r < r_hi) {
+        const size_t row = (size_t)b * n + r;
+        ms[q] = *reinterpret_cast<const f32x2*>(st + 2 * row);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = 4 * lane + 256 * u;
+          if (c < C) {
+            dv[q][u] = *reinterpret_cast<const f32x4*>(dh + row * C + c);
+            xv[q][u] = *reinterpret_cast<const u32x2*>(x + row * C + c);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+    const int r = r0 + 4 * q;
+    if (r >= r_hi) break;
     const size_t row = (size_t)b * n + r;
-    const float mean = st[2 * row], rstd = st[2 * row + 1];
+    const float mean = ms[q][0], rstd = ms[q][1];
     float g[U][4], xh[U][4], sg = 0.f, sgx = 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = 4 * lane + 256 * u;
       if (c < C) {
-        const f32x4 d = *reinterpret_cast<const f32x4*>(dh + row * C + c);
+        const f32x4 d = dv[q][u];
         float xf[4];
-        unpack4(*reinterpret_cast<const u32x2*>(x + row * C + c), xf);
+        unpack4(xv[q][u], xf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           xh[u][e] = (xf[e] - mean) * rstd;
@@ -513,6 +652,7 @@ __global__ __launch_bounds__(256) void rows_bwd_kernel(RowsBwdArgs a) {
         for (int e = 0; e < 4; ++e) o[e] = rstd * (g[u][e] - mg - xh[u][e] * mgx);
         *reinterpret_cast<u32x2*>(dx + row * C + c) = (u32x2){pack2(o[0], o[1]), pack2(o[2], o[3])};
       }
+    }
     }
   }
   // waves add their sums into LDS one after the other (fixed order)
@@ -545,8 +685,17 @@ __global__ __launch_bounds__(256) void mod_reduce_kernel(ReduceArgs a) {
   const int inner = s ? a.inner[1] : a.inner[0], count = s ? a.count[1] : a.count[0];
   const int64_t outer = i / inner, in = i - outer * inner;
   const float* p = (s ? a.part[1] : a.part[0]) + outer * count * inner + in;
+  // eight independent loads in flight per round, summed in chunk order
   float t = 0.f;
-  for (int c = 0; c < count; ++c) t += p[(int64_t)c * inner];
+  int c = 0;
+  for (; c + 8 <= count; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(c + u) * inner];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t += v[u];
+  }
+  for (; c < count; ++c) t += p[(int64_t)c * inner];
   (s ? a.out[1] : a.out[0])[i] = t;
 }
 
@@ -579,10 +728,13 @@ __global__ __launch_bounds__(256) void w_reduce_kernel(ReduceArgs a) {
 // ---------------------------------------------------------------------------------------------
 // Launchers
 
-constexpr int kQkvNB = 2, kDhNB = 2, kDwNB = 4;
+constexpr int kQkvNB = 3, kDhNB = 2, kDwNB = 2;
 
+// (Every launcher returns without a launch when there is no work: a grid of 0 workgroups is an
+// invalid launch configuration.)
 void launch_modulate(const ModulateArgs& a, hipStream_t stream) {
   const int rows = a.T[0] + a.T[1];
+  if (rows == 0) return;
   const dim3 grid((rows + 3) / 4), block(256);
   if (a.C <= 1024)
     hipLaunchKernelGGL(modulate_kernel<2>, grid, block, 0, stream, a);
@@ -593,27 +745,32 @@ void launch_modulate(const ModulateArgs& a, hipStream_t stream) {
 }
 
 void launch_qkv_gemm(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((qkv_gemm_kernel<kQkvMA, kQkvMB, kQkvNB>), dim3(gemm_grid(a.ntiles)), dim3(kGemmThreads), 0,
+  if (a.ntiles == 0) return;
+  hipLaunchKernelGGL((qkv_gemm_kernel<kQkvMA, kQkvMB, kQkvNB>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0,
                      stream, a);
 }
 
 void launch_dh_gemm(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((dh_gemm_kernel<kDhMA, kDhMB, kDhNB>), dim3(gemm_grid(a.ntiles)), dim3(kGemmThreads), 0, stream,
+  if (a.ntiles == 0) return;
+  hipLaunchKernelGGL((dh_gemm_kernel<kDhMA, kDhMB, kDhNB>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0, stream,
                      a);
 }
 
 void launch_dw_gemm(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((dw_gemm_kernel<kDwMA, kDwMB, kDwNB>), dim3(gemm_grid(a.ntiles)), dim3(kGemmThreads), 0, stream,
+  if (a.ntiles == 0) return;
+  hipLaunchKernelGGL((dw_gemm_kernel<kDwMA, kDwMB, kDwNB>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0, stream,
                      a);
 }
 
 void launch_transpose_w(const TransposeArgs& a, hipStream_t stream) {
   const int per = 3 * (a.C / 64) * (a.C / 64);
+  if (a.nstreams == 0) return;
   hipLaunchKernelGGL(transpose_w_kernel, dim3(per * a.nstreams), dim3(256), 0, stream, a);
 }
 
 void launch_rows_bwd(const RowsBwdArgs& a, hipStream_t stream) {
   const dim3 grid(a.blocks0 + a.B * a.chunks[1]), block(256);
+  if (grid.x == 0) return;
   if (a.C <= 1024)
     hipLaunchKernelGGL(rows_bwd_kernel<4>, grid, block, 0, stream, a);
   else if (a.C <= 2048)
@@ -624,6 +781,7 @@ void launch_rows_bwd(const RowsBwdArgs& a, hipStream_t stream) {
 
 void launch_mod_reduce(const ReduceArgs& a, hipStream_t stream) {
   const int64_t n = (int64_t)a.len[0] + a.len[1];
+  if (n == 0) return;
   hipLaunchKernelGGL(mod_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
 }
 
@@ -631,6 +789,7 @@ void launch_w_reduce(const ReduceArgs& a, hipStream_t stream) {
   const int64_t n4 = ((int64_t)a.len[0] + a.len[1]) / 4;
   const int64_t nc = (int64_t)(a.cout[0] ? a.clen[0] : 0) + (a.cout[1] ? a.clen[1] : 0);
   const int64_t threads = n4 > nc ? n4 : nc;
+  if (threads == 0) return;
   hipLaunchKernelGGL(w_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
 }
 
