@@ -25,6 +25,11 @@ key mask (`padded`).
 both streams of a layer (jattn_adaln_qkv_fwd + jattn_adaln_qkv_bwd; FLOPs of its three GEMMs,
 2 T C 3C each for T tokens of width C), and beside it the same step written as torch's LayerNorm,
 modulation and Linear with autograd (`torch_unfused`).
+
+--variant mlp (with --workload mmdit512 or mmdit768) times the MLP block after the attention (fc,
+adaLN, SwiGLU, one residual; jattn_mlp_fwd + jattn_mlp_bwd over both streams; FLOPs of its GEMMs,
+2 T (C^2 + 3 C F) forward and twice that backward), and beside it the same step in torch ops
+(`torch_unfused`).
 """
 import argparse
 import ctypes
@@ -50,7 +55,7 @@ def parse():
     ap.add_argument("--workload", default="mmdit512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--variant", choices=("joint", "streams", "varlen", "window", "adaln"), default="joint")
+    ap.add_argument("--variant", choices=("joint", "streams", "varlen", "window", "adaln", "mlp"), default="joint")
     ap.add_argument("--window", type=int, nargs=2, default=(256, 256), metavar=("LEFT", "RIGHT"))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 512 MiB device-to-device three times: under rocprofv3 --pmc its "
@@ -106,6 +111,8 @@ def main():
 
     if args.variant == "adaln":
         return bench_adaln(args, torch)
+    if args.variant == "mlp":
+        return bench_mlp(args, torch)
 
     from diffusion_transformer_joint_amd import _lib
     from diffusion_transformer_joint_amd.inputs import (VARLEN_WORKLOADS, WORKLOADS, flops, make_inputs,
@@ -428,7 +435,7 @@ def bench_adaln(args, torch):
     torch.cuda.synchronize()
 
     K = args.steps
-    targs = {"qkv_gemm_kernel": "256, 128, 3", "dh_gemm_kernel": "256, 256, 2", "dw_gemm_kernel": "256, 256, 2"}
+    targs = {"qkv_gemm_kernel": "256, 128, 3", "dh_gemm_kernel": "256, 256, 2, false", "dw_gemm_kernel": "256, 256, 2"}
     label = lambda n: f"{n}<{targs[n]}>" if n in targs else n
     stages = [label(n) + " (fwd)" if n == "modulate_kernel" else label(n) for n in _lib.ADALN_FWD_STAGES]
     stages += [label(n) for n in _lib.ADALN_BWD_STAGES]
@@ -494,6 +501,201 @@ def bench_adaln(args, torch):
                                   "autograd backward with the same upstream gradients, both streams, bf16"},
     }
     print(json.dumps(res), flush=True)
+
+
+MLP_METRIC = "MLP block (fc, adaLN, SwiGLU, residual) fwd+bwd TFLOP/s (both streams) bf16; % of bf16 MFMA peak"
+
+
+def bench_mlp(args, torch):
+    """The MLP block of one layer, forward + backward over both streams."""
+    from diffusion_transformer_joint_amd import _lib
+    from diffusion_transformer_joint_amd.inputs import MLP_WORKLOADS, make_workload_mlp_inputs, mlp_flops
+
+    if args.workload not in MLP_WORKLOADS:
+        args.workload = "mmdit512"
+    w = MLP_WORKLOADS[args.workload]
+    B, C, Fh = w.B, w.C, w.F
+    inp = make_workload_mlp_inputs(args.workload, seed=0)
+    dev = torch.device("cuda:0")
+    keys = ("o", "x", "mod", "wfc", "bfc", "w12", "b12", "w2", "b2", "dout")
+    d = {k: tuple(t.to(dev).contiguous() for t in inp[k]) for k in keys}
+    lib = _lib.load()
+    dims = (B, w.n_img, w.n_txt, C, Fh)
+    fws_bytes, ws_bytes = int(lib.jattn_mlp_fwd_workspace_bytes(*dims)), int(lib.jattn_mlp_bwd_workspace_bytes(*dims))
+    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ns = (w.n_img, w.n_txt)
+    out, do = ([torch.empty(B, n, C, dtype=torch.bfloat16, device=dev) for n in ns] for _ in range(2))
+    f32 = lambda *shape: [torch.empty(*shape, dtype=torch.float32, device=dev) for _ in ns]
+    g = dict(dmod=f32(B, 2, C), dwfc=f32(C, C), dbfc=f32(C), dw12=f32(2 * Fh, C), db12=f32(2 * Fh), dw2=f32(C, Fh),
+             db2=f32(C))
+    pp = lambda t: _lib.PtrPair(t[0].data_ptr(), t[1].data_ptr())
+    keep = {k: pp(d[k]) for k in keys}
+    keep.update(out=pp(out), do=pp(do), **{k: pp(v) for k, v in g.items()})
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    nfs, nbs = len(_lib.MLP_FWD_STAGES), len(_lib.MLP_BWD_STAGES)
+    a = lambda *names: [keep[n].arg for n in names]
+
+    def fwd(events=None, n=nfs):
+        _lib.check("jattn_mlp_fwd", lib.jattn_mlp_fwd(*a("o", "x", "mod", "wfc", "bfc", "w12", "b12", "w2", "b2"), *dims,
+                                                      ctypes.c_float(inp["eps"]), keep["out"].arg, fws.data_ptr(),
+                                                      fws_bytes, events, 0 if events is None else n, sp))
+
+    def bwd(events=None, n=nbs):
+        _lib.check("jattn_mlp_bwd", lib.jattn_mlp_bwd(*a("o", "mod", "wfc", "w12", "w2", "dout"), *dims,
+                                                      *a("do", "dmod", "dwfc", "dbfc", "dw12", "db12", "dw2", "db2"),
+                                                      fws.data_ptr(), fws_bytes, ws.data_ptr(), ws_bytes, events,
+                                                      0 if events is None else n, sp))
+
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def handle(evs):
+        arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+        return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    K = args.steps
+    # stage labels: kernel instantiations (the forward's fc and down projection and the backward's do
+    # GEMM are the bf16-output GEMM; du the fp32-output one; d(hid) that one with the SwiGLU epilogue)
+    lab = {"fc_gemm": "qkv_gemm_kernel<256, 128, 3> (fc)", "modulate_kernel": "modulate_kernel",
+           "swiglu_gemm_kernel": "swiglu_gemm_kernel<256, 128, 3>", "down_gemm": "qkv_gemm_kernel<256, 128, 3> (down)",
+           "transpose_w_kernel": "transpose_w_kernel", "dhid_gemm": "dh_gemm_kernel<256, 256, 2, true> (d hid)",
+           "dw2_gemm": "dw_gemm_kernel<256, 256, 2> (dW2)", "du_gemm": "dh_gemm_kernel<256, 256, 2, false> (du)",
+           "dw12_gemm": "dw_gemm_kernel<256, 256, 2> (dW12)", "rows_bwd_kernel": "rows_bwd_kernel",
+           "do_gemm": "qkv_gemm_kernel<256, 128, 3> (do)", "dwfc_gemm": "dw_gemm_kernel<256, 256, 2> (dWfc)",
+           "reductions": "reductions"}
+    stages = [lab[n] for n in _lib.MLP_FWD_STAGES] + [lab[n] for n in _lib.MLP_BWD_STAGES]
+    # timed region: the backward's first three stage events give the live duration of the d(hid) and dW2 GEMMs
+    ev = [[new_event() for _ in range(3)] for _ in range(K)]
+    bh = [handle(ev[i]) for i in range(K)]
+    start, end = new_event(), new_event()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        fwd()
+        bwd(bh[i][1], 3)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    live_ms = {lab["dhid_gemm"]: sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K,
+               lab["dw2_gemm"]: sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K}
+    KB = min(K, 50)
+    ev0 = [new_event() for _ in range(KB)]
+    evb = [[new_event() for _ in stages] for _ in range(KB)]
+    fh = [handle(evb[i][:nfs]) for i in range(KB)]
+    bhh = [handle(evb[i][nfs:]) for i in range(KB)]
+    torch.cuda.synchronize()
+    for i in range(KB):
+        ev0[i].record(stream)
+        fwd(fh[i][1])
+        bwd(bhh[i][1])
+    torch.cuda.synchronize()
+    kern_ms = {}
+    for j, name in enumerate(stages):
+        kern_ms[name] = sum((ev0[i] if j == 0 else evb[i][j - 1]).elapsed_time(evb[i][j]) for i in range(KB)) / KB
+    ms_fwd = sum(ev0[i].elapsed_time(evb[i][nfs - 1]) for i in range(KB)) / KB
+
+    fl = mlp_flops(B, w.n_img, w.n_txt, C, Fh)
+    T = B * (w.n_img + w.n_txt)
+    tflops = fl["total"] / (ms_step * 1e-3) / 1e12
+    # GEMM FLOPs per launch (2 T x output x contraction); the dominant one is the largest by time
+    per_launch = {lab["fc_gemm"]: 2.0 * T * C * C, lab["swiglu_gemm_kernel"]: 2.0 * T * 2 * Fh * C,
+                  lab["down_gemm"]: 2.0 * T * C * Fh, lab["dhid_gemm"]: 2.0 * T * Fh * C,
+                  lab["dw2_gemm"]: 2.0 * T * C * Fh, lab["du_gemm"]: 2.0 * T * C * 2 * Fh,
+                  lab["dw12_gemm"]: 2.0 * T * 2 * Fh * C, lab["do_gemm"]: 2.0 * T * C * C, lab["dwfc_gemm"]: 2.0 * T * C * C}
+    dom = max(per_launch, key=lambda n: kern_ms[n])
+    dom_ms = live_ms.get(dom, kern_ms[dom])
+    achieved = per_launch[dom] / (dom_ms * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(args.workload, dom, "mlp"), "flop_per_launch": per_launch[dom],
+                "avg_launch_ms": round(dom_ms, 5),
+                "avg_launch_ms_source": "timed region" if dom in live_ms else "breakdown pass"}
+
+    unfused = time_mlp_unfused(torch, d, inp, stream, K, args.warmup)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_mlp(inp, args.cpu_seconds)
+    res = {
+        "metric": MLP_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "variant": "mlp", "B": B, "n_img": w.n_img, "n_txt": w.n_txt, "C": C,
+                   "F": Fh, "global_batch": B, "parallelism": "single-gpu"},
+        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_step - ms_fwd, 5),
+        "gflop_per_step": round(fl["total"] / 1e9, 3),
+        "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
+        "kernel_ms_timed_region": {k: round(v, 5) for k, v in live_ms.items()},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "torch_unfused": {"ms_per_step": round(unfused, 5), "speedup": round(unfused / ms_step, 4),
+                          "what": "torch: linear, layer_norm, * (1 + scale) + shift, linear, silu * gate, linear, "
+                                  "+ residual, and autograd backward, both streams, bf16"},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def time_mlp_unfused(torch, d, inp, stream, K, warmup):
+    """The same block step in plain torch ops (separate kernels, hipBLASLt GEMMs), forward + autograd
+    backward."""
+    import torch.nn.functional as F
+    C = inp["C"]
+    leaf = {k: tuple(t.clone().requires_grad_(True) for t in d[k]) for k in ("o", "x", "mod")}
+    par = {k: [t.detach().clone().to(torch.bfloat16).requires_grad_(True) for t in d[k]]
+           for k in ("wfc", "bfc", "w12", "b12", "w2", "b2")}
+
+    def step():
+        outs, grads = [], []
+        for s in range(2):
+            m = leaf["mod"][s].to(torch.bfloat16)
+            z = F.linear(leaf["o"][s], par["wfc"][s], par["bfc"][s])
+            u = F.layer_norm(z, (C,), eps=inp["eps"]) * (1 + m[:, 1:2]) + m[:, 0:1]
+            a, g = F.linear(u, par["w12"][s], par["b12"][s]).chunk(2, dim=-1)
+            outs.append(leaf["x"][s] + F.linear(F.silu(a) * g, par["w2"][s], par["b2"][s]))
+            grads.append(d["dout"][s])
+        torch.autograd.backward(outs, grads)
+
+    return time_steps(torch, stream, step, K, warmup)
+
+
+def cpu_baseline_mlp(inp, seconds):
+    """The fp64 oracle (mlp_fwd_bwd) on whole samples of the image stream, as many as fit the time budget
+    (at least one), in TFLOP/s of the GEMM FLOPs it covered."""
+    from oracle import mlp_fwd_bwd
+    f64 = lambda t: t.double().numpy()
+    B, C, Fh, n = inp["B"], inp["C"], inp["F"], inp["n_img"]
+    t0 = time.perf_counter()
+    done = 0
+    while done < B and (done == 0 or time.perf_counter() - t0 < seconds):
+        sl = slice(done, done + 1)
+        t = lambda k: f64(inp[k][0][sl])
+        wt = lambda k: f64(inp[k][0])
+        mlp_fwd_bwd(t("o"), t("x"), t("mod"), wt("wfc"), wt("bfc"), wt("w12"), wt("b12"), wt("w2"), wt("b2"), inp["eps"],
+                    t("dout"))
+        done += 1
+    sec = time.perf_counter() - t0
+    flop = 3 * 2.0 * done * n * (C * C + 3 * C * Fh)
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = 1
+    return {"value": round(flop / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle (mlp_fwd_bwd) fwd+bwd on the first {done} of {B} samples of the image "
+                      f"stream ({n} tokens each) of the same seed-0 inputs, {sec:.1f} s wall; BLAS threads = cores",
+            "seconds": round(sec, 2), "samples": done}
 
 
 def time_adaln_unfused(torch, d, inp, stream, K, warmup):

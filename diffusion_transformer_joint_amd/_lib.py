@@ -1,4 +1,4 @@
-"""ctypes loader for libjattn.so (the C ABI declared in include/jattn.h and include/jattn_adaln.h).
+"""ctypes loader for libjattn.so (the C ABI declared in include/jattn.h, jattn_adaln.h and jattn_mlp.h).
 
 The library is built in-tree by ``diffusion_transformer_joint_amd.build``. Loading fails loudly if it
 is missing: there is no fallback implementation.
@@ -19,12 +19,16 @@ EXPORTED = ("jattn_fwd", "jattn_fwd_ex", "jattn_fwd_workspace_bytes", "jattn_bwd
             "jattn_fwd_streams", "jattn_bwd_streams", "jattn_varlen_fwd_workspace_bytes",
             "jattn_varlen_bwd_workspace_bytes", "jattn_fwd_varlen", "jattn_bwd_varlen", "jattn_fwd_window",
             "jattn_bwd_window", "jattn_adaln_qkv_fwd_workspace_bytes", "jattn_adaln_qkv_bwd_workspace_bytes",
-            "jattn_adaln_qkv_fwd", "jattn_adaln_qkv_bwd", "jattn_status_string", "jattn_abi_version")
-ABI_VERSION = 7
+            "jattn_adaln_qkv_fwd", "jattn_adaln_qkv_bwd", "jattn_mlp_fwd_workspace_bytes", "jattn_mlp_bwd_workspace_bytes",
+            "jattn_mlp_fwd", "jattn_mlp_bwd", "jattn_status_string", "jattn_abi_version")
+ABI_VERSION = 8
 FWD_STAGES = ("prenorm_kernel", "fwd_kernel")
 BWD_STAGES = ("prenorm_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "dg_reduce_kernel")
 ADALN_FWD_STAGES = ("modulate_kernel", "qkv_gemm_kernel")
 ADALN_BWD_STAGES = ("transpose_w_kernel", "dh_gemm_kernel", "rows_bwd_kernel", "dw_gemm_kernel", "reductions")
+MLP_FWD_STAGES = ("fc_gemm", "modulate_kernel", "swiglu_gemm_kernel", "down_gemm")
+MLP_BWD_STAGES = ("transpose_w_kernel", "dhid_gemm", "dw2_gemm", "du_gemm", "dw12_gemm", "rows_bwd_kernel", "do_gemm",
+                  "dwfc_gemm", "reductions")
 
 _lock = threading.Lock()
 _lib = None
@@ -92,6 +96,15 @@ def load() -> ctypes.CDLL:
         lib.jattn_adaln_qkv_bwd.restype = I
         lib.jattn_adaln_qkv_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, P, P, P, ctypes.c_size_t, P,
                                             ctypes.c_size_t, P, I, P]
+        lib.jattn_mlp_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.jattn_mlp_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
+        lib.jattn_mlp_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.jattn_mlp_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+        lib.jattn_mlp_fwd.restype = I
+        lib.jattn_mlp_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, P, ctypes.c_size_t, P, I, P]
+        lib.jattn_mlp_bwd.restype = I
+        lib.jattn_mlp_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
+                                      ctypes.c_size_t, P, I, P]
         lib.jattn_status_string.restype = ctypes.c_char_p
         lib.jattn_status_string.argtypes = [I]
         lib.jattn_abi_version.restype = I

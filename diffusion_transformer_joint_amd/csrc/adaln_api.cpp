@@ -7,14 +7,13 @@
 #include <cstdint>
 
 #include "adaln_launch.h"
+#include "api_common.h"
 
 namespace {
 
 using jattn::kBwdRowChunk;
 using jattn::kGemmK;
-
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+using namespace jattn_api;
 
 struct Sizes {
   int B, n[2], C;
@@ -56,28 +55,6 @@ FwdLayout fwd_layout(const Sizes& z) {
   return l;
 }
 
-// Splits of the weight-gradient GEMM over the tokens. Its output has only (C / MA) (3C / MB) tiles,
-// too few to fill 256 CUs when C is small, so the tokens are split: each stream gets
-// floor(steps_s / target) splits (at least one), where target is the contraction steps per
-// workgroup that spread the whole launch's work over 256 workgroups. With one split the GEMM writes
-// the weight and bias gradients directly; with more, fp32 partials that a reduction sums in order.
-void dw_splits(const int64_t T[2], int C, int splits[2], int kchunk[2]) {
-  const int64_t tiles = (int64_t)((C + jattn::kDwMA - 1) / jattn::kDwMA) * ((3 * C + jattn::kDwMB - 1) / jattn::kDwMB);
-  int64_t steps[2], total = 0;
-  for (int s = 0; s < 2; ++s) {
-    steps[s] = (T[s] + kGemmK - 1) / kGemmK;
-    total += steps[s] * tiles;
-  }
-  const int64_t target = total > 0 ? (total + 255) / 256 : 1;
-  for (int s = 0; s < 2; ++s) {
-    int64_t sp = steps[s] / target;
-    sp = sp < 1 ? 1 : sp > 64 ? 64 : sp;
-    const int64_t per = steps[s] > 0 ? (steps[s] + sp - 1) / sp : 1;  // steps per split
-    kchunk[s] = (int)(per * kGemmK);
-    splits[s] = steps[s] > 0 ? (int)((steps[s] + per - 1) / per) : 1;
-  }
-}
-
 struct BwdLayout {
   size_t wt[2], dh[2], modpart[2], wpart[2], cpart[2], total;
   int chunks[2], splits[2], kchunk[2];
@@ -87,7 +64,7 @@ BwdLayout bwd_layout(const Sizes& z) {
   BwdLayout l;
   const size_t C = z.C;
   size_t off = 0;
-  dw_splits(z.T, z.C, l.splits, l.kchunk);
+  dw_splits(z.T, z.C, 3 * z.C, l.splits, l.kchunk);
   for (int s = 0; s < 2; ++s) {
     l.chunks[s] = (z.n[s] + kBwdRowChunk - 1) / kBwdRowChunk;
     const bool on = z.T[s] > 0;
@@ -105,68 +82,6 @@ BwdLayout bwd_layout(const Sizes& z) {
   }
   l.total = off;
   return l;
-}
-
-struct Range {
-  const void* p;
-  size_t bytes;
-};
-
-bool overlap(const Range& a, const Range& b) {
-  if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
-  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
-  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
-}
-
-bool disjoint(const Range* outs, int nout, const Range* ins, int nin) {
-  for (int i = 0; i < nout; ++i) {
-    for (int j = 0; j < nin; ++j)
-      if (overlap(outs[i], ins[j])) return false;
-    for (int j = i + 1; j < nout; ++j)
-      if (overlap(outs[i], outs[j])) return false;
-  }
-  return true;
-}
-
-bool ptr_ok(const void* p) { return p != nullptr && aligned(p, 16); }
-
-jattn_status check_events(const hipEvent_t* ev, int n, int max) {
-  if (n < 0 || n > max || (n > 0 && ev == nullptr)) return JATTN_ERROR_INVALID_VALUE;
-  return JATTN_SUCCESS;
-}
-
-// After enqueueing stage i: check the launch and record its event.
-bool stage_done(int i, const hipEvent_t* ev, int n, hipStream_t stream) {
-  if (hipGetLastError() != hipSuccess) return false;
-  if (i < n && hipEventRecord(ev[i], stream) != hipSuccess) return false;
-  return true;
-}
-
-jattn::MatRef mat(const void* p0, const void* p1, const void* p2, int seg, int rs, int64_t rows, int width) {
-  jattn::MatRef m;
-  m.p[0] = static_cast<const uint16_t*>(p0);
-  m.p[1] = static_cast<const uint16_t*>(p1 ? p1 : p0);
-  m.p[2] = static_cast<const uint16_t*>(p2 ? p2 : p0);
-  m.seg = seg;
-  m.rs = rs;
-  m.rows = (int)rows;
-  m.width = width;
-  return m;
-}
-
-void finish(jattn::GemmArgs& g, int ma, int mb) {
-  for (int s = 0; s < 2; ++s) {
-    jattn::GemmProblem& p = g.pr[s];
-    if (p.N == 0 || p.M == 0) {
-      p.tiles_m = p.tiles_n = p.splits = 1;
-      p.ntiles = 0;
-      continue;
-    }
-    p.tiles_m = (p.M + ma - 1) / ma;
-    p.tiles_n = (p.N + mb - 1) / mb;
-    p.ntiles = p.tiles_m * p.tiles_n * p.splits;
-  }
-  g.ntiles = g.pr[0].ntiles + g.pr[1].ntiles;
 }
 
 }  // namespace
@@ -218,8 +133,8 @@ jattn_status jattn_adaln_qkv_fwd(const void* const x[2], const float* const mod[
   if (!disjoint(outs, no, ins, ni)) return JATTN_ERROR_INVALID_VALUE;
 
   char* ws = static_cast<char*>(workspace);
-  jattn::ModulateArgs ma;
-  jattn::GemmArgs g;
+  jattn::ModulateArgs ma{};
+  jattn::GemmArgs g{};
   for (int s = 0; s < 2; ++s) {
     const bool on = z.T[s] > 0;
     ma.x[s] = static_cast<const uint16_t*>(on ? x[s] : nullptr);
@@ -301,19 +216,22 @@ jattn_status jattn_adaln_qkv_bwd(const void* const x[2], const float* const mod[
 
   const char* fws = static_cast<const char*>(fwd_workspace);
   char* ws = static_cast<char*>(workspace);
-  jattn::TransposeArgs ta;
-  jattn::GemmArgs gdh, gdw;
-  jattn::RowsBwdArgs ra;
-  jattn::ReduceArgs rm, rw;
-  // (an empty image stream moves the text stream into slot 0 of the transpose)
-  int slot = 0;
+  jattn::TransposeArgs ta{};
+  jattn::GemmArgs gdh{}, gdw{};
+  jattn::RowsBwdArgs ra{};
+  jattn::ReduceArgs rm{}, rw{};
+  ta.n = 0;
+  ta.start[0] = 0;
   for (int s = 0; s < 2; ++s) {
     const bool on = z.T[s] > 0;
     const uint16_t* wt = reinterpret_cast<const uint16_t*>(ws + bl.wt[s]);
-    if (on) {
-      ta.w[slot] = static_cast<const uint16_t*>(w[s]);
-      ta.wt[slot] = reinterpret_cast<uint16_t*>(ws + bl.wt[s]);
-      ++slot;
+    if (on) {  // W [3C, C] -> W^T
+      ta.src[ta.n] = static_cast<const uint16_t*>(w[s]);
+      ta.dst[ta.n] = reinterpret_cast<uint16_t*>(ws + bl.wt[s]);
+      ta.rows[ta.n] = 3 * C;
+      ta.cols[ta.n] = C;
+      ta.start[ta.n + 1] = ta.start[ta.n] + 3 * (C / 64) * (C / 64);
+      ++ta.n;
     }
     const void* h = fws + fl.h[s];
     // dh = dY W: MFMA-A = W^T [C, 3C], MFMA-B = dY [T, 3C] over the three tensors
@@ -376,8 +294,6 @@ jattn_status jattn_adaln_qkv_bwd(const void* const x[2], const float* const mod[
     rw.inner[s] = 0;
     rw.clen[s] = 3 * C;
   }
-  ta.C = C;
-  ta.nstreams = slot;
   ra.B = B;
   ra.C = C;
   ra.blocks0 = B * ra.chunks[0];

@@ -1,5 +1,5 @@
-// Internal interface between the C ABI (adaln_api.cpp) and the kernels of the adaLN-modulated QKV
-// projection (adaln_qkv.hip).
+// Internal interface between the C ABIs (adaln_api.cpp, mlp_api.cpp) and the kernels of the
+// adaLN-modulated QKV projection and of the MLP block after the attention (adaln_qkv.hip).
 //
 // Per token stream s (image = 0, text = 1) with T_s = B * n_s token rows and C channels:
 //   x_s    bf16 [T_s, C]         input rows (sample b = row / n_s)
@@ -37,8 +37,12 @@ struct GemmProblem {
   int ntiles;                            // tiles_m * tiles_n * splits
   void* out[3];                          // epilogue targets (see the kernels)
   int out_seg;                           // columns per output tensor
-  const float* bias;                     // qkv epilogue only (or null)
+  const float* bias;                     // bf16-output and SwiGLU epilogues (or null)
   float* colsum;                         // weight-gradient kernel: [splits, N] sums of B over k (or null)
+  const uint16_t* aux;                   // bf16-output kernel: residual added to the output (or null);
+                                         // fp32-output kernel: the forward's [a | g] for the SwiGLU backward
+  int pair_off;                          // SwiGLU forward: A tile = rows [j0, j0 + MA/2) and the same rows
+                                         // + pair_off (W1 and W3 of W12); 0 elsewhere
 };
 
 struct GemmArgs {
@@ -85,15 +89,21 @@ struct ReduceArgs {
   int clen[2];
 };
 
+// Up to 6 bf16 matrices src_i [rows_i, cols_i] -> dst_i [cols_i, rows_i] (sizes multiples of 64), one
+// 64 x 64 tile per workgroup; start_i = first workgroup of matrix i, start_n = total.
 struct TransposeArgs {
-  const uint16_t* w[2];   // [3C, C]
-  uint16_t* wt[2];        // [C, 3C]
-  int C, nstreams;
+  const uint16_t* src[6];
+  uint16_t* dst[6];
+  int rows[6], cols[6];
+  int start[7];
+  int n;
 };
 
 void launch_modulate(const ModulateArgs& a, hipStream_t stream);
 void launch_qkv_gemm(const GemmArgs& a, hipStream_t stream);
+void launch_swiglu_gemm(const GemmArgs& a, hipStream_t stream);
 void launch_dh_gemm(const GemmArgs& a, hipStream_t stream);
+void launch_dhid_gemm(const GemmArgs& a, hipStream_t stream);  // dh GEMM with the SwiGLU-backward epilogue
 void launch_dw_gemm(const GemmArgs& a, hipStream_t stream);
 void launch_transpose_w(const TransposeArgs& a, hipStream_t stream);
 void launch_rows_bwd(const RowsBwdArgs& a, hipStream_t stream);
@@ -102,6 +112,7 @@ void launch_w_reduce(const ReduceArgs& a, hipStream_t stream);
 
 // Output-tile sizes of the three GEMMs (MFMA-A rows x MFMA-B rows per workgroup).
 constexpr int kQkvMA = 256, kQkvMB = 128;
+constexpr int kSwigluMA = 256, kSwigluMB = 128;  // 128 columns j of W1 and the same 128 of W3 per tile
 constexpr int kDhMA = 256, kDhMB = 256;
 constexpr int kDwMA = 256, kDwMB = 256;
 

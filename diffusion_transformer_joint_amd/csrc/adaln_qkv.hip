@@ -52,7 +52,8 @@ struct OpStream {
   size_t row_off[S];
   int seg, col, kseg, rs, rows;
 
-  __device__ __forceinline__ void init(const MatRef& M, int r0, int k0) {
+  // pair: rows mode only; sub-tiles s >= S/2 start pair rows further (r0 then counts A rows per half)
+  __device__ __forceinline__ void init(const MatRef& M, int r0, int k0, int pair = 0) {
     rs = M.rs;
     rows = M.rows;
     if constexpr (!TR) {
@@ -65,7 +66,8 @@ struct OpStream {
       const uint16_t* sp = seg_ptr(kseg);
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const int row0 = r0 + 64 * s, valid = M.rows - row0;
+        const int row0 = pair ? (s < S / 2 ? r0 + 64 * s : pair + r0 + 64 * (s - S / 2)) : r0 + 64 * s;
+        const int valid = M.rows - row0;
         row_off[s] = (size_t)row0 * M.rs;
         range[s] = __builtin_amdgcn_readfirstlane(valid > 0 ? (uint32_t)((valid - 1) * M.rs + 64) * 2u : 0u);
         base[s] = sp + row_off[s] + col;
@@ -114,6 +116,51 @@ struct OpStream {
     return make_rsrc(reinterpret_cast<const void*>(lo | (hi << 32)), range[s]);
   }
 };
+
+// Row-staged epilogue I/O. An MFMA result tile leaves each lane with one token row and runs of 4
+// columns; stored straight from there, every instruction writes 8 bytes into 32 different rows, and a
+// workgroup's lines stay partly written until its last iteration. With many tiles in flight per XCD
+// those lines were evicted half-written (3.7x the HBM writes of the SwiGLU outputs). So a wave
+// stages its 32 rows x 128 columns (bf16) in LDS, pitch kStgPitch elements, and moves whole rows with
+// 16-byte accesses: lane l takes row 4 it + l / 16, columns 8 (l % 16) .. + 7, 8 instructions per
+// 32 x 128 block.
+constexpr int kStgPitch = 136;                 // 128 columns + 8: 4-bank shift per row
+constexpr int kStgElems = 32 * kStgPitch;      // one 32 x 128 block
+
+// Store block `stg` (32 rows x 128 columns) to out + row * rs + col0, rows < nrows, columns < ncols
+// (ncols - col0 a multiple of 8 or >= 128).
+__device__ __forceinline__ void stg_store_rows(const __bf16* stg, uint16_t* __restrict__ out, size_t rs, int row0,
+                                               int nrows, int col0, int ncols, int lane) {
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = 4 * it + (lane >> 4), c = 8 * (lane & 15);
+    if (row0 + r < nrows && col0 + c < ncols)
+      *reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * rs + col0 + c) =
+          *reinterpret_cast<const u32x4*>(stg + r * kStgPitch + c);
+  }
+}
+
+// Load a block the same way (rows >= nrows or columns >= ncols read as zeros).
+__device__ __forceinline__ void stg_load_rows(__bf16* stg, const uint16_t* __restrict__ in, size_t rs, int row0,
+                                              int nrows, int col0, int ncols, int lane) {
+  u32x4 v[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = 4 * it + (lane >> 4), c = 8 * (lane & 15);
+    v[it] = row0 + r < nrows && col0 + c < ncols ? *reinterpret_cast<const u32x4*>(in + (size_t)(row0 + r) * rs + col0 + c)
+                                                   : (u32x4){0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int it = 0; it < 8; ++it)
+    *reinterpret_cast<u32x4*>(stg + (4 * it + (lane >> 4)) * kStgPitch + 8 * (lane & 15)) = v[it];
+}
+
+// sigmoid(x) = 1 / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each): an IEEE
+// division is a dependent chain of several instructions, and the SwiGLU epilogues take hundreds of
+// them per wave.
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -215,7 +262,7 @@ __device__ __forceinline__ void gemm_tile(const GemmCore<MA, MB, NB, TR>& g, con
   const int nk = max(0, (kend - kbeg + kGemmK - 1) / kGemmK);
   OpStream<GC::SA, TR> sa;
   OpStream<GC::SB, TR> sb;
-  sa.init(p.a, m0, kbeg);
+  sa.init(p.a, m0, kbeg, TR ? 0 : p.pair_off);
   sb.init(p.b, n0, kbeg);
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t)
@@ -271,6 +318,8 @@ __device__ __forceinline__ GemmProblem pick(const GemmArgs& a, bool s) {
   p.out_seg = s ? y.out_seg : x.out_seg;
   p.bias = s ? y.bias : x.bias;
   p.colsum = s ? y.colsum : x.colsum;
+  p.aux = s ? y.aux : x.aux;
+  p.pair_off = s ? y.pair_off : x.pair_off;
   return p;
 }
 
@@ -429,36 +478,120 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
         const int tok = n0 + g.wb * (MB / 2) + 32 * j + (g.lane & 31);
         if (tok < p.N) {
           const f32x16& v = acc[i][j];
-          *reinterpret_cast<u32x2*>(out + (size_t)tok * p.out_seg + c) =
-              (u32x2){pack2(v[4 * q] + b[0], v[4 * q + 1] + b[1]), pack2(v[4 * q + 2] + b[2], v[4 * q + 3] + b[3])};
+          const size_t o = (size_t)tok * p.out_seg + c;
+          float r[4] = {0.f, 0.f, 0.f, 0.f};
+          if (p.aux) unpack4(*reinterpret_cast<const u32x2*>(p.aux + o), r);  // the residual (same layout)
+          *reinterpret_cast<u32x2*>(out + o) = (u32x2){pack2(v[4 * q] + b[0] + r[0], v[4 * q + 1] + b[1] + r[1]),
+                                                       pack2(v[4 * q + 2] + b[2] + r[2], v[4 * q + 3] + b[3] + r[3])};
         }
       }
     }
   }
 }
 
+// SwiGLU forward of the MLP: [a | g] = u W12^T + b12 and hid = silu(a) * g. The A tile holds 128 rows
+// j0.. of W1 (waves wa = 0) and the same 128 rows of W3 (waves wa = 1, pair_off = F rows further),
+// so a and g of one (token, j) sit in the same lane and register of the two waves of a pair; the
+// wa = 1 waves hand their accumulators over through LDS. Writes [a | g] (bf16 [T, 2F], kept for the
+// backward) and hid (bf16 [T, F]).
+template <int MA, int MB, int NB>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void swiglu_gemm_kernel(
+    GemmArgs a) {
+  using GC = GemmCore<MA, MB, NB, false>;
+  constexpr int H = MA / 2;  // columns j per tile
+  static_assert(GC::IA * GC::IB * 16 * 64 * 2 * 4 <= GC::BYTES, "LDS hand-over fits the ring");
+  __shared__ __attribute__((aligned(16))) __bf16 smem[GC::BYTES / 2];
+  __shared__ __attribute__((aligned(16))) float bias_lds[MA];  // [b1 of the tile | b3 of the tile]
+  const TileId id(a);
+  if (!id.ok) return;
+  const GemmProblem p = pick(a, id.s != 0);
+  const GC g(p);
+  const int Fh = p.pair_off, j0 = id.tm * H, n0 = id.tn * MB;
+  if (p.bias) {  // wave w: 64 bias values, b1 for w < 2, b3 for w >= 2 (issued before the ring's loads)
+    const int jw = j0 + 64 * (g.wave & 1), nb = max(0, min(64, Fh - jw));
+    lds_load_dwords(make_rsrc(p.bias + (g.wave < 2 ? 0 : Fh) + jw, (uint32_t)__builtin_amdgcn_readfirstlane(nb * 4)),
+                    bias_lds + 64 * g.wave, (uint32_t)g.lane * 4u);
+  }
+  f32x16 acc[GC::IA][GC::IB];
+  NoVisit none;
+  gemm_tile(g, p, j0, n0, 0, p.K, smem, acc, none);
+  // Hand-over: each wave of a pair (same wb) finishes token block jb = wa of the pair's IB = 2 blocks;
+  // it gives its accumulators of the other block to its partner through LDS.
+  static_assert(GC::IB == 2, "one token block per wave of a pair");
+  static_assert(4 * 3 * kStgElems * 2 <= GC::BYTES, "three staged 32 x 128 blocks per wave");
+  float* xch = reinterpret_cast<float*>(smem);  // (the ring's last barrier has passed)
+  const int give = 1 - g.wa;
+#pragma unroll
+  for (int i = 0; i < GC::IA; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      xch[(((g.wb * 2 + g.wa) * GC::IA + i) * 16 + e) * 64 + g.lane] = give == 0 ? acc[i][0][e] : acc[i][1][e];
+  __syncthreads();
+  const int jb = g.wa, partner = 1 - g.wa;  // this wave's token block; the partner's slot in LDS
+  float other[GC::IA][16];
+#pragma unroll
+  for (int i = 0; i < GC::IA; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) other[i][e] = xch[(((g.wb * 2 + partner) * GC::IA + i) * 16 + e) * 64 + g.lane];
+  __syncthreads();  // (every hand-over read is done: the LDS now holds the staged output blocks)
+  __bf16* s_a = smem + g.wave * 3 * kStgElems;
+  __bf16* s_g = s_a + kStgElems;
+  __bf16* s_h = s_g + kStgElems;
+#pragma unroll
+  for (int i = 0; i < GC::IA; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int jl = 32 * i + 8 * q + 4 * (g.lane >> 5), tl = g.lane & 31;
+      const f32x4 b1 = p.bias ? *reinterpret_cast<const f32x4*>(bias_lds + jl) : (f32x4){0.f, 0.f, 0.f, 0.f};
+      const f32x4 b3 = p.bias ? *reinterpret_cast<const f32x4*>(bias_lds + H + jl) : (f32x4){0.f, 0.f, 0.f, 0.f};
+      float av[4], gv[4], hv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // a (W1 rows) is held by the wa = 0 wave, g (W3 rows) by the wa = 1 wave
+        const float mine = jb == 0 ? acc[i][0][4 * q + e] : acc[i][1][4 * q + e];
+        const float oth = other[i][4 * q + e];
+        av[e] = (g.wa == 0 ? mine : oth) + b1[e];
+        gv[e] = (g.wa == 0 ? oth : mine) + b3[e];
+        hv[e] = av[e] * sigmoid_fast(av[e]) * gv[e];
+      }
+      const int o = tl * kStgPitch + jl;
+      *reinterpret_cast<u32x2*>(s_a + o) = (u32x2){pack2(av[0], av[1]), pack2(av[2], av[3])};
+      *reinterpret_cast<u32x2*>(s_g + o) = (u32x2){pack2(gv[0], gv[1]), pack2(gv[2], gv[3])};
+      *reinterpret_cast<u32x2*>(s_h + o) = (u32x2){pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staged blocks are complete
+  const int t0 = n0 + g.wb * (MB / 2) + 32 * jb;
+  uint16_t* ag = static_cast<uint16_t*>(p.out[0]);
+  uint16_t* hid = static_cast<uint16_t*>(p.out[1]);
+  stg_store_rows(s_a, ag, 2 * (size_t)Fh, t0, p.N, j0, Fh, g.lane);
+  stg_store_rows(s_g, ag + Fh, 2 * (size_t)Fh, t0, p.N, j0, Fh, g.lane);
+  stg_store_rows(s_h, hid, (size_t)Fh, t0, p.N, j0, Fh, g.lane);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Backward.
 
-// W [3C, C] -> W^T [C, 3C] through a padded LDS tile, 64 x 64 elements per workgroup.
+// src_i [R, Cc] -> dst_i [Cc, R] through a padded LDS tile, 64 x 64 elements per workgroup.
 __global__ __launch_bounds__(256) void transpose_w_kernel(TransposeArgs a) {
   __shared__ uint16_t t[64][66];
-  const int C = a.C, tiles_c = C / 64;
-  const int per = 3 * tiles_c * tiles_c;
-  const int s = (int)blockIdx.x >= per ? 1 : 0;
-  const int id = (int)blockIdx.x - s * per;
-  const int r0 = (id / tiles_c) * 64, c0 = (id % tiles_c) * 64;  // rows of W (0..3C), columns (0..C)
-  const uint16_t* w = s ? a.w[1] : a.w[0];
-  uint16_t* wt = s ? a.wt[1] : a.wt[0];
+  const int b = (int)blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < 6; ++k) i += (k < a.n && b >= a.start[k]) ? 1 : 0;
+  const int R = a.rows[i], Cc = a.cols[i], tiles_c = Cc / 64, id = b - a.start[i];
+  const int r0 = (id / tiles_c) * 64, c0 = (id % tiles_c) * 64;
+  const uint16_t* src = a.src[i];
+  uint16_t* dst = a.dst[i];
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) t[r][tx] = w[(size_t)(r0 + r) * C + c0 + tx];
+  for (int r = ty; r < 64; r += 4) t[r][tx] = src[(size_t)(r0 + r) * Cc + c0 + tx];
   __syncthreads();
-  for (int c = ty; c < 64; c += 4) wt[(size_t)(c0 + c) * 3 * C + r0 + tx] = t[tx][c];
+  for (int c = ty; c < 64; c += 4) dst[(size_t)(c0 + c) * R + r0 + tx] = t[tx][c];
 }
 
 // dh = dY W as MFMA-A = W^T rows (channels), MFMA-B = dY rows (tokens; k runs over the three tensors
 // dq, dk, dv): fp32 stores of 4 consecutive channels per lane.
-template <int MA, int MB, int NB>
+// SWIGLU: the MLP's d(hid) GEMM, whose epilogue applies the SwiGLU backward (p.aux = the forward's [a | g]).
+template <int MA, int MB, int NB, bool SWIGLU>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dh_gemm_kernel(
     GemmArgs a) {
   using GC = GemmCore<MA, MB, NB, false>;
@@ -471,23 +604,66 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
   f32x16 acc[GC::IA][GC::IB];
   NoVisit none;
   gemm_tile(g, p, m0, n0, 0, p.K, smem, acc, none);
-  float* dh = static_cast<float*>(p.out[0]);
+  if constexpr (SWIGLU) {  // acc = d(hid)[tok][j]; with the forward's a and g, write [da | dg]
+    // Per block of 32 tokens: the a and g rows go through this wave's LDS blocks (coalesced loads),
+    // da and dg replace them in place, and whole rows go back out (see the row-staged epilogue I/O).
+    static_assert(MA / 2 == 128 && 4 * 2 * kStgElems * 2 <= GC::BYTES, "two staged 32 x 128 blocks per wave");
+    const int Fh = p.M;
+    uint16_t* __restrict__ dag = static_cast<uint16_t*>(p.out[0]);
+    __bf16* sa = smem + g.wave * 2 * kStgElems;  // (the ring's last barrier has passed)
+    __bf16* sg = sa + kStgElems;
+    const int jw = m0 + g.wa * (MA / 2);  // this wave's first column j
 #pragma unroll
-  for (int i = 0; i < GC::IA; ++i)
+    for (int jb = 0; jb < GC::IB; ++jb) {
+      const int t0 = n0 + g.wb * (MB / 2) + 32 * jb;
+      stg_load_rows(sa, p.aux, 2 * (size_t)Fh, t0, p.N, jw, Fh, g.lane);
+      stg_load_rows(sg, p.aux + Fh, 2 * (size_t)Fh, t0, p.N, jw, Fh, g.lane);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are visible to its lanes
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = m0 + g.wa * (MA / 2) + 32 * i + 8 * q + 4 * (g.lane >> 5);
-      if (c >= p.M) continue;
+      for (int i = 0; i < GC::IA; ++i)
 #pragma unroll
-      for (int j = 0; j < GC::IB; ++j) {
-        const int tok = n0 + g.wb * (MB / 2) + 32 * j + (g.lane & 31);
-        if (tok < p.N) {
-          const f32x16& v = acc[i][j];
-          *reinterpret_cast<f32x4*>(dh + (size_t)tok * p.out_seg + c) =
-              (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        for (int q = 0; q < 4; ++q) {
+          const int jl = 32 * i + 8 * q + 4 * (g.lane >> 5), tl = g.lane & 31;
+          u32x2* pa = reinterpret_cast<u32x2*>(sa + tl * kStgPitch + jl);
+          u32x2* pg = reinterpret_cast<u32x2*>(sg + tl * kStgPitch + jl);
+          float av[4], gv[4], da[4], dg[4];
+          unpack4(*pa, av);
+          unpack4(*pg, gv);
+          const f32x16& v = acc[i][jb];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sgm = sigmoid_fast(av[e]);
+            da[e] = v[4 * q + e] * gv[e] * sgm * (1.f + av[e] * (1.f - sgm));
+            dg[e] = v[4 * q + e] * av[e] * sgm;
+          }
+          *pa = (u32x2){pack2(da[0], da[1]), pack2(da[2], da[3])};
+          *pg = (u32x2){pack2(dg[0], dg[1]), pack2(dg[2], dg[3])};
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      stg_store_rows(sa, dag, 2 * (size_t)Fh, t0, p.N, jw, Fh, g.lane);
+      stg_store_rows(sg, dag + Fh, 2 * (size_t)Fh, t0, p.N, jw, Fh, g.lane);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // (the next block's loads overwrite these LDS blocks)
+    }
+    return;
+  } else {
+    float* dh = static_cast<float*>(p.out[0]);
+#pragma unroll
+    for (int i = 0; i < GC::IA; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = m0 + g.wa * (MA / 2) + 32 * i + 8 * q + 4 * (g.lane >> 5);
+        if (c >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < GC::IB; ++j) {
+          const int tok = n0 + g.wb * (MB / 2) + 32 * j + (g.lane & 31);
+          if (tok < p.N) {
+            const f32x16& v = acc[i][j];
+            *reinterpret_cast<f32x4*>(dh + (size_t)tok * p.out_seg + c) =
+                (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+          }
         }
       }
-    }
+  }
 }
 
 // Column sums of the B tiles (dY over the tokens, for the bias gradient), in the workgroups of
@@ -752,7 +928,13 @@ void launch_qkv_gemm(const GemmArgs& a, hipStream_t stream) {
 
 void launch_dh_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.ntiles == 0) return;
-  hipLaunchKernelGGL((dh_gemm_kernel<kDhMA, kDhMB, kDhNB>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0, stream,
+  hipLaunchKernelGGL((dh_gemm_kernel<kDhMA, kDhMB, kDhNB, false>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0, stream,
+                     a);
+}
+
+void launch_dhid_gemm(const GemmArgs& a, hipStream_t stream) {
+  if (a.ntiles == 0) return;
+  hipLaunchKernelGGL((dh_gemm_kernel<kDhMA, kDhMB, kDhNB, true>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0, stream,
                      a);
 }
 
@@ -763,9 +945,14 @@ void launch_dw_gemm(const GemmArgs& a, hipStream_t stream) {
 }
 
 void launch_transpose_w(const TransposeArgs& a, hipStream_t stream) {
-  const int per = 3 * (a.C / 64) * (a.C / 64);
-  if (a.nstreams == 0) return;
-  hipLaunchKernelGGL(transpose_w_kernel, dim3(per * a.nstreams), dim3(256), 0, stream, a);
+  if (a.n == 0 || a.start[a.n] == 0) return;
+  hipLaunchKernelGGL(transpose_w_kernel, dim3(a.start[a.n]), dim3(256), 0, stream, a);
+}
+
+void launch_swiglu_gemm(const GemmArgs& a, hipStream_t stream) {
+  if (a.ntiles == 0) return;
+  hipLaunchKernelGGL((swiglu_gemm_kernel<kSwigluMA, kSwigluMB, kQkvNB>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0,
+                     stream, a);
 }
 
 void launch_rows_bwd(const RowsBwdArgs& a, hipStream_t stream) {

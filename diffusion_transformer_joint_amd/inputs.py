@@ -300,3 +300,66 @@ def adaln_flops(B: int, n_img: int, n_txt: int, C: int) -> dict:
     T = B * (n_img + n_txt)
     fwd = 2.0 * T * C * 3 * C
     return {"fwd": fwd, "bwd": 2 * fwd, "total": 3 * fwd}
+
+
+# ------------------------------------------------------------------------------------------------
+# MLP block after the attention (fc, adaLN, SwiGLU, one residual; both streams per call)
+#
+# * ``mmdit512`` - B16, 1024 image + 77 text tokens, C = 768, hidden F = 2048 (8C/3: the SwiGLU width
+#                  with the parameters of a 4C GELU MLP; the pages give no width).
+# * ``mmdit768`` - B4, 2304 image + 77 text tokens, C = 3072, F = 8192.
+#
+# Recipe (one CPU generator seeded with ``seed``; image stream, then text stream): o, x =
+# randn(B, n_s, C).bfloat16() each; mod = 0.2 * randn(B, 2, C); wfc = U(+-1/sqrt C) [C, C] bf16,
+# bfc = U(+-1/sqrt C) [C]; w12 = U(+-1/sqrt C) [2F, C] bf16, b12 = U(+-1/sqrt C) [2F]; w2 = U(+-1/sqrt F)
+# [C, F] bf16, b2 = U(+-1/sqrt F) [C] (torch's default Linear initialisation); dout =
+# randn(B, n_s, C).bfloat16().
+
+@dataclass(frozen=True)
+class MlpWorkload:
+    name: str
+    B: int
+    n_img: int
+    n_txt: int
+    C: int
+    F: int
+
+
+MLP_WORKLOADS = {
+    "mmdit512": MlpWorkload("mmdit512", B=16, n_img=1024, n_txt=77, C=768, F=2048),
+    "mmdit768": MlpWorkload("mmdit768", B=4, n_img=2304, n_txt=77, C=3072, F=8192),
+}
+
+
+def make_mlp_inputs(B: int, n_img: int, n_txt: int, C: int, F: int, seed: int = 0, mod_std: float = 0.2) -> dict:
+    g = torch.Generator().manual_seed(seed)
+    u = lambda shape, fan: (2 * torch.rand(*shape, generator=g) - 1) / math.sqrt(fan)
+    keys = ("o", "x", "mod", "wfc", "bfc", "w12", "b12", "w2", "b2", "dout")
+    out = {k: [] for k in keys}
+    for n in (n_img, n_txt):
+        out["o"].append(torch.randn(B, n, C, generator=g).bfloat16())
+        out["x"].append(torch.randn(B, n, C, generator=g).bfloat16())
+        out["mod"].append(mod_std * torch.randn(B, 2, C, generator=g))
+        out["wfc"].append(u((C, C), C).bfloat16())
+        out["bfc"].append(u((C,), C))
+        out["w12"].append(u((2 * F, C), C).bfloat16())
+        out["b12"].append(u((2 * F,), C))
+        out["w2"].append(u((C, F), F).bfloat16())
+        out["b2"].append(u((C,), F))
+        out["dout"].append(torch.randn(B, n, C, generator=g).bfloat16())
+    res = {k: tuple(v) for k, v in out.items()}
+    res.update(B=B, n_img=n_img, n_txt=n_txt, C=C, F=F, eps=EPS)
+    return res
+
+
+def make_workload_mlp_inputs(name: str, seed: int = 0) -> dict:
+    w = MLP_WORKLOADS[name]
+    return make_mlp_inputs(w.B, w.n_img, w.n_txt, w.C, w.F, seed=seed)
+
+
+def mlp_flops(B: int, n_img: int, n_txt: int, C: int, F: int) -> dict:
+    """Algorithmic FLOPs of the block's GEMMs: forward 2 T (C^2 + 2 C F + F C) for T tokens of both
+    streams (fc, gate/up, down); backward twice that (input and weight gradients of each)."""
+    T = B * (n_img + n_txt)
+    fwd = 2.0 * T * (C * C + 3 * C * F)
+    return {"fwd": fwd, "bwd": 2 * fwd, "total": 3 * fwd}

@@ -1,5 +1,5 @@
 """C ABI checks that need no GPU: the library loads, exports every entry point declared in
-include/jattn.h and include/jattn_adaln.h, and rejects invalid arguments on the host before any HIP call.
+include/jattn.h, include/jattn_adaln.h and include/jattn_mlp.h, and rejects invalid arguments on the host before any HIP call.
 
 Every call here is constructed to fail validation: the fake device addresses are never
 dereferenced, because a call that passed validation would enqueue kernels."""
@@ -31,7 +31,7 @@ def lib():
 
 
 def test_exports_every_declared_symbol(lib):
-    header = "".join(open(os.path.join(ROOT, "include", h)).read() for h in ("jattn.h", "jattn_adaln.h"))
+    header = "".join(open(os.path.join(ROOT, "include", h)).read() for h in ("jattn.h", "jattn_adaln.h", "jattn_mlp.h"))
     declared = set(re.findall(r"\b(jattn_[a-z_]+)\s*\(", header))
     assert declared == set(_lib.EXPORTED)
     for name in declared:
