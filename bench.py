@@ -66,16 +66,23 @@ def parse():
 COPY_BYTES = 512 << 20
 
 
-def kernel_sources_digest():
-    """sha256 over the HIP/C++ sources of the library: ties stored counter readings to a kernel version."""
+# Device sources (kernels, their launchers and device headers) behind each entry-point family.
+KERNEL_SOURCES = {
+    "attention": ("jattn_device.h", "jattn_launch.h", "jattn_prenorm.hip", "jattn_fwd.hip", "jattn_bwd.hip"),
+    "projection": ("jattn_device.h", "adaln_launch.h", "adaln_qkv.hip"),
+}
+
+
+def kernel_sources_digest(variant="joint"):
+    """sha256 over the device sources of the kernels a variant runs: ties stored counter readings to a
+    kernel version (a change to those sources voids them; host-side API files do not)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "diffusion_transformer_joint_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode())
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+    for name in KERNEL_SOURCES["projection" if variant in ("adaln", "mlp") else "attention"]:
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -92,7 +99,7 @@ def stored_traffic(workload, kernel, variant="joint", window=None):
     if start < 0:
         return None
     rec = json.loads(text[start + 7:text.index("```", start + 7)])
-    if rec.get("source_sha256") != kernel_sources_digest():
+    if rec.get("source_sha256") != kernel_sources_digest(variant):
         return None
     if window is not None and rec.get("window") != list(window):
         return None
@@ -368,6 +375,58 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def breakdown_pass(fwd, bwd, stages, nfs, KB, stream, new_event, handle):
+    """Per-stage average durations over KB steps with every stage event recorded (outside the timed
+    region), and the forward's share of the step."""
+    import torch
+    ev0 = [new_event() for _ in range(KB)]
+    evb = [[new_event() for _ in stages] for _ in range(KB)]
+    fh = [handle(evb[i][:nfs]) for i in range(KB)]
+    bhh = [handle(evb[i][nfs:]) for i in range(KB)]
+    torch.cuda.synchronize()
+    for i in range(KB):
+        ev0[i].record(stream)
+        fwd(fh[i][1])
+        bwd(bhh[i][1])
+    torch.cuda.synchronize()
+    kern_ms = {}
+    for j, name in enumerate(stages):
+        kern_ms[name] = sum((ev0[i] if j == 0 else evb[i][j - 1]).elapsed_time(evb[i][j]) for i in range(KB)) / KB
+    ms_fwd = sum(ev0[i].elapsed_time(evb[i][nfs - 1]) for i in range(KB)) / KB
+    return kern_ms, ms_fwd
+
+
+def timed_region(fwd, bwd, j, nfs, K, stream, new_event, handle):
+    """K whole steps between two events. The library's own stage events bracket stage j (of the
+    forward's nfs stages followed by the backward's) in every step, so that stage's average launch
+    duration is measured live, on the stream the kernels run on."""
+    import torch
+    jb = j - nfs
+    n = (j if jb < 0 else jb) + 1  # stage events handed to the pass that runs stage j
+    ev = [[new_event() for _ in range(n)] for _ in range(K)]
+    pre = [new_event() for _ in range(K)] if n == 1 else None  # stage j is that pass's first
+    hs = [handle(ev[i]) for i in range(K)]
+    start, end = new_event(), new_event()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        if jb < 0:
+            if pre is not None:
+                pre[i].record(stream)
+            fwd(hs[i][1], n)
+            bwd()
+        else:
+            fwd()
+            if pre is not None:
+                pre[i].record(stream)
+            bwd(hs[i][1], n)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    dom_ms = sum((pre[i] if pre is not None else ev[i][-2]).elapsed_time(ev[i][-1]) for i in range(K)) / K
+    return ms_step, dom_ms
+
+
 ADALN_METRIC = "adaLN+QKV projection fwd+bwd TFLOP/s (both streams) bf16; % of bf16 MFMA peak"
 
 
@@ -439,48 +498,18 @@ def bench_adaln(args, torch):
     label = lambda n: f"{n}<{targs[n]}>" if n in targs else n
     stages = [label(n) + " (fwd)" if n == "modulate_kernel" else label(n) for n in _lib.ADALN_FWD_STAGES]
     stages += [label(n) for n in _lib.ADALN_BWD_STAGES]
-    # timed region: the backward's first four stage events give the live durations of its GEMMs
-    ev = [[new_event() for _ in range(4)] for _ in range(K)]
-    bh = [handle(ev[i]) for i in range(K)]
-    start, end = new_event(), new_event()
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K):
-        fwd()
-        bwd(bh[i][1], 4)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / K
-    live_ms = {label("dh_gemm_kernel"): sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K,
-               label("dw_gemm_kernel"): sum(ev[i][2].elapsed_time(ev[i][3]) for i in range(K)) / K}
-
-    KB = min(K, 50)
-    ev0 = [new_event() for _ in range(KB)]
-    evb = [[new_event() for _ in stages] for _ in range(KB)]
-    fh = [handle(evb[i][:nfs]) for i in range(KB)]
-    bhh = [handle(evb[i][nfs:]) for i in range(KB)]
-    torch.cuda.synchronize()
-    for i in range(KB):
-        ev0[i].record(stream)
-        fwd(fh[i][1])
-        bwd(bhh[i][1])
-    torch.cuda.synchronize()
-    kern_ms = {}
-    for j, name in enumerate(stages):
-        kern_ms[name] = sum((ev0[i] if j == 0 else evb[i][j - 1]).elapsed_time(evb[i][j]) for i in range(KB)) / KB
-    ms_fwd = sum(ev0[i].elapsed_time(evb[i][nfs - 1]) for i in range(KB)) / KB
+    kern_ms, ms_fwd = breakdown_pass(fwd, bwd, stages, nfs, min(K, 50), stream, new_event, handle)
+    gemms = [label(n) for n in ("qkv_gemm_kernel", "dh_gemm_kernel", "dw_gemm_kernel")]
+    dom = max(gemms, key=lambda n: kern_ms[n])
+    ms_step, dom_ms = timed_region(fwd, bwd, stages.index(dom), nfs, K, stream, new_event, handle)
 
     fl = adaln_flops(B, w.n_img, w.n_txt, C)
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
-    gemms = [label(n) for n in ("qkv_gemm_kernel", "dh_gemm_kernel", "dw_gemm_kernel")]
-    dom = max(gemms, key=lambda n: kern_ms[n])
-    dom_ms = live_ms.get(dom, kern_ms[dom])
     achieved = fl["fwd"] / (dom_ms * 1e-3) / 1e12  # each GEMM is 2 T C 3C FLOPs per launch
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": stored_traffic(args.workload, dom, "adaln"), "flop_per_launch": fl["fwd"],
-                "avg_launch_ms": round(dom_ms, 5),
-                "avg_launch_ms_source": "timed region" if dom in live_ms else "breakdown pass"}
+                "avg_launch_ms": round(dom_ms, 5), "avg_launch_ms_source": "timed region"}
 
     unfused = time_adaln_unfused(torch, d, inp, stream, K, args.warmup)
     cpu = None if args.no_cpu_baseline else cpu_baseline_adaln(inp, args.cpu_seconds)
@@ -494,7 +523,6 @@ def bench_adaln(args, torch):
         "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_step - ms_fwd, 5),
         "gflop_per_step": round(fl["total"] / 1e9, 3),
         "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
-        "kernel_ms_timed_region": {k: round(v, 5) for k, v in live_ms.items()},
         "roofline": roofline, "cpu_baseline": cpu,
         "torch_unfused": {"ms_per_step": round(unfused, 5), "speedup": round(unfused / ms_step, 4),
                           "what": "torch: layer_norm, * (1 + scale) + shift, linear, split into q, k, v, and "
@@ -579,52 +607,23 @@ def bench_mlp(args, torch):
            "do_gemm": "qkv_gemm_kernel<256, 128, 3> (do)", "dwfc_gemm": "dw_gemm_kernel<256, 256, 2> (dWfc)",
            "reductions": "reductions"}
     stages = [lab[n] for n in _lib.MLP_FWD_STAGES] + [lab[n] for n in _lib.MLP_BWD_STAGES]
-    # timed region: the backward's first three stage events give the live duration of the d(hid) and dW2 GEMMs
-    ev = [[new_event() for _ in range(3)] for _ in range(K)]
-    bh = [handle(ev[i]) for i in range(K)]
-    start, end = new_event(), new_event()
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K):
-        fwd()
-        bwd(bh[i][1], 3)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / K
-    live_ms = {lab["dhid_gemm"]: sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K,
-               lab["dw2_gemm"]: sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K}
-    KB = min(K, 50)
-    ev0 = [new_event() for _ in range(KB)]
-    evb = [[new_event() for _ in stages] for _ in range(KB)]
-    fh = [handle(evb[i][:nfs]) for i in range(KB)]
-    bhh = [handle(evb[i][nfs:]) for i in range(KB)]
-    torch.cuda.synchronize()
-    for i in range(KB):
-        ev0[i].record(stream)
-        fwd(fh[i][1])
-        bwd(bhh[i][1])
-    torch.cuda.synchronize()
-    kern_ms = {}
-    for j, name in enumerate(stages):
-        kern_ms[name] = sum((ev0[i] if j == 0 else evb[i][j - 1]).elapsed_time(evb[i][j]) for i in range(KB)) / KB
-    ms_fwd = sum(ev0[i].elapsed_time(evb[i][nfs - 1]) for i in range(KB)) / KB
-
-    fl = mlp_flops(B, w.n_img, w.n_txt, C, Fh)
+    kern_ms, ms_fwd = breakdown_pass(fwd, bwd, stages, nfs, min(K, 50), stream, new_event, handle)
     T = B * (w.n_img + w.n_txt)
-    tflops = fl["total"] / (ms_step * 1e-3) / 1e12
     # GEMM FLOPs per launch (2 T x output x contraction); the dominant one is the largest by time
     per_launch = {lab["fc_gemm"]: 2.0 * T * C * C, lab["swiglu_gemm_kernel"]: 2.0 * T * 2 * Fh * C,
                   lab["down_gemm"]: 2.0 * T * C * Fh, lab["dhid_gemm"]: 2.0 * T * Fh * C,
                   lab["dw2_gemm"]: 2.0 * T * C * Fh, lab["du_gemm"]: 2.0 * T * C * 2 * Fh,
                   lab["dw12_gemm"]: 2.0 * T * 2 * Fh * C, lab["do_gemm"]: 2.0 * T * C * C, lab["dwfc_gemm"]: 2.0 * T * C * C}
     dom = max(per_launch, key=lambda n: kern_ms[n])
-    dom_ms = live_ms.get(dom, kern_ms[dom])
+    ms_step, dom_ms = timed_region(fwd, bwd, stages.index(dom), nfs, K, stream, new_event, handle)
+
+    fl = mlp_flops(B, w.n_img, w.n_txt, C, Fh)
+    tflops = fl["total"] / (ms_step * 1e-3) / 1e12
     achieved = per_launch[dom] / (dom_ms * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": stored_traffic(args.workload, dom, "mlp"), "flop_per_launch": per_launch[dom],
-                "avg_launch_ms": round(dom_ms, 5),
-                "avg_launch_ms_source": "timed region" if dom in live_ms else "breakdown pass"}
+                "avg_launch_ms": round(dom_ms, 5), "avg_launch_ms_source": "timed region"}
 
     unfused = time_mlp_unfused(torch, d, inp, stream, K, args.warmup)
     cpu = None if args.no_cpu_baseline else cpu_baseline_mlp(inp, args.cpu_seconds)
@@ -638,7 +637,6 @@ def bench_mlp(args, torch):
         "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_step - ms_fwd, 5),
         "gflop_per_step": round(fl["total"] / 1e9, 3),
         "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
-        "kernel_ms_timed_region": {k: round(v, 5) for k, v in live_ms.items()},
         "roofline": roofline, "cpu_baseline": cpu,
         "torch_unfused": {"ms_per_step": round(unfused, 5), "speedup": round(unfused / ms_step, 4),
                           "what": "torch: linear, layer_norm, * (1 + scale) + shift, linear, silu * gate, linear, "
