@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libjattn.so")
 
 SOURCES = ["jattn_prenorm.hip", "jattn_fwd.hip", "jattn_bwd.hip", "jattn_api.cpp", "adaln_qkv.hip", "adaln_api.cpp",
-           "mlp_api.cpp"]
+           "mlp_api.cpp", "jattn_diag.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the code objects (the backend would otherwise form

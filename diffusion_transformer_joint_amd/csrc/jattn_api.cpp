@@ -13,7 +13,7 @@ namespace {
 
 using jattn::kBwdRowsPerBlock;
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 
 bool supported_head_dim(int D) { return D == 32 || D == 64 || D == 72 || D == 128; }
 

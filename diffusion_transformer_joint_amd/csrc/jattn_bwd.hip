@@ -213,7 +213,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int c = h * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        s[h][i] = (c >= clo) & (c < chi) ? s[h][i] : -INFINITY;
+        s[h][i] = ((c >= clo) & (c < chi)) ? s[h][i] : -INFINITY;
       }
     } else if constexpr (MASKED) {
 #pragma unroll
@@ -468,7 +468,7 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const _
       if constexpr (KMASK) p[i] = kvalid ? p[i] : 0.f;
       if constexpr (WM) {  // queries q0 + c with c in [key - wr - q0, key + wl - q0] see this key
         const int c = h * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        p[i] = (c >= key - wr - q0) & (c <= key + wl - q0) ? p[i] : 0.f;
+        p[i] = ((c >= key - wr - q0) & (c <= key + wl - q0)) ? p[i] : 0.f;
       }
       ds[i] = p[i] * dp[h][i];
     }

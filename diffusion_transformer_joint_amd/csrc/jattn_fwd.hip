@@ -121,7 +121,7 @@ __device__ __forceinline__ void fwd_tile(const __bf16* __restrict__ kt, const __
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int c = h * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          s[qt][i] = (c >= clo) & (c < chi) ? s[qt][i] : -INFINITY;
+          s[qt][i] = ((c >= clo) & (c < chi)) ? s[qt][i] : -INFINITY;
         }
       } else if constexpr (MASKED) {
 #pragma unroll

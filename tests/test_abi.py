@@ -1,5 +1,5 @@
 """C ABI checks that need no GPU: the library loads, exports every entry point declared in
-include/jattn.h, include/jattn_adaln.h and include/jattn_mlp.h, and rejects invalid arguments on the host before any HIP call.
+include/jattn.h, include/jattn_adaln.h, include/jattn_mlp.h and include/jattn_diag.h, and rejects invalid arguments on the host before any HIP call.
 
 Every call here is constructed to fail validation: the fake device addresses are never
 dereferenced, because a call that passed validation would enqueue kernels."""
@@ -31,7 +31,7 @@ def lib():
 
 
 def test_exports_every_declared_symbol(lib):
-    header = "".join(open(os.path.join(ROOT, "include", h)).read() for h in ("jattn.h", "jattn_adaln.h", "jattn_mlp.h"))
+    header = "".join(open(os.path.join(ROOT, "include", h)).read() for h in ("jattn.h", "jattn_adaln.h", "jattn_mlp.h", "jattn_diag.h"))
     declared = set(re.findall(r"\b(jattn_[a-z_]+)\s*\(", header))
     assert declared == set(_lib.EXPORTED)
     for name in declared:
@@ -355,3 +355,16 @@ def test_window_entry_points_reject(lib):
                                     fake(10), a["ws"], a["ws_bytes"], None, None, 0, None)
     assert bwdw(dq=fake(6)) == _lib.INVALID_VALUE
     assert bwdw(ws_bytes=need - 1) == _lib.WORKSPACE
+
+
+@pytest.mark.parametrize("which,blocks,iters,out", [
+    (2, 8, 4, fake(0)),            # unknown probe
+    (-1, 8, 4, fake(0)),
+    (0, 0, 4, fake(0)),            # no workgroups
+    (1, 8, 0, fake(0)),            # no iterations
+    (0, 1 << 23, 4, fake(0)),      # blocks * 256 reaches 2^31
+    (0, 8, 4, None),               # no output
+    (1, 8, 4, fake(0) + 2),        # misaligned output
+])
+def test_probe_rejects_invalid_arguments(lib, which, blocks, iters, out):
+    assert lib.jattn_probe_saturate(which, blocks, iters, ctypes.c_float(1.0), out, None) == _lib.INVALID_VALUE
