@@ -177,3 +177,35 @@ def test_adaln_deterministic_and_autograd():
     for s in range(2):
         assert torch.equal(leaf["x"][s].grad, dx[s]) and torch.equal(leaf["mod"][s].grad, dmod[s])
         assert torch.equal(leaf["w"][s].grad, dw[s].to(torch.bfloat16)) and torch.equal(leaf["bias"][s].grad, db[s])
+
+
+def test_adaln_events_and_reused_workspaces():
+    """Stage events on every kernel leave the outputs bitwise unchanged, and a smaller problem run in
+    the workspaces of a larger one matches the oracle."""
+    from diffusion_transformer_joint_amd import _lib
+    say("case: adaln events, B2 n_img 90 n_txt 21 C192; then B1 n_img 33 n_txt 5 in the same workspaces")
+    dev = torch.device("cuda:0")
+    inp = make_adaln_inputs(2, 90, 21, 192, seed=8)
+    d = {k: tuple(t.to(dev).contiguous() for t in inp[k]) for k in ("x", "mod", "w", "bias", "dq", "dk", "dv")}
+    q, k, v, ws = adaln.adaln_qkv_forward(d["x"], d["mod"], d["w"], d["bias"], inp["eps"])
+    g = adaln.adaln_qkv_backward(d["x"], d["mod"], d["w"], d["dq"], d["dk"], d["dv"], ws)
+    g = tuple(tuple(t.clone() for t in pair) for pair in g)
+    ev_f = [torch.cuda.Event(enable_timing=True) for _ in _lib.ADALN_FWD_STAGES]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in _lib.ADALN_BWD_STAGES]
+    q2, k2, v2, ws2 = adaln.adaln_qkv_forward(d["x"], d["mod"], d["w"], d["bias"], inp["eps"], events=ev_f)
+    g2 = adaln.adaln_qkv_backward(d["x"], d["mod"], d["w"], d["dq"], d["dk"], d["dv"], ws2, events=ev_b)
+    torch.cuda.synchronize()
+    for s in range(2):
+        for a, b in ((q, q2), (k, k2), (v, v2)) + tuple(zip(g, g2)):
+            assert torch.equal(a[s], b[s])
+    small = make_adaln_inputs(1, 33, 5, 192, seed=9)
+    ds = {k: tuple(t.to(dev).contiguous() for t in small[k]) for k in ("x", "mod", "w", "bias", "dq", "dk", "dv")}
+    bws = torch.empty(adaln.bwd_workspace_bytes(2, 90, 21, 192), dtype=torch.uint8, device=dev)
+    qs, ks, vs, _ = adaln.adaln_qkv_forward(ds["x"], ds["mod"], ds["w"], ds["bias"], small["eps"], workspace=ws)
+    dx, dmod, dw, db = adaln.adaln_qkv_backward(ds["x"], ds["mod"], ds["w"], ds["dq"], ds["dk"], ds["dv"], ws,
+                                                workspace=bws)
+    torch.cuda.synchronize()
+    for s in range(2):
+        got = dict(q=f64(qs[s]), k=f64(ks[s]), v=f64(vs[s]), dx=f64(dx[s]), dmod=f64(dmod[s]), dw=f64(dw[s]),
+                   dbias=f64(db[s]))
+        check(got, run_oracle(small, s), f"reused workspaces, stream {s}")

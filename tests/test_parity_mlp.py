@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from diffusion_transformer_joint_amd import mlp
+from diffusion_transformer_joint_amd import _lib, mlp
 from diffusion_transformer_joint_amd.inputs import MLP_WORKLOADS, make_mlp_inputs, make_workload_mlp_inputs
 from oracle import mlp_fwd_bwd
 
@@ -163,3 +163,57 @@ def test_mlp_deterministic_and_autograd():
             assert torch.equal(leaf[k][s].grad, g1[gk][s].to(torch.bfloat16)), k
         for k, gk in (("bfc", "dbfc"), ("b12", "db12"), ("b2", "db2")):
             assert torch.equal(leaf[k][s].grad, g1[gk][s]), k
+
+
+def test_mlp_options_do_not_change_results():
+    """No bias gradients (NULL pointers), stage events on every kernel, and caller workspaces reused
+    from a larger call leave every written output bitwise equal to the plain call."""
+    say("case: mlp options, B2 n_img 96 n_txt 33 C128 F192 (then B1 n_img 40 n_txt 9 into the same workspaces)")
+    dev = torch.device("cuda:0")
+    inp = make_mlp_inputs(2, 96, 33, 128, 192, seed=5)
+    d = {k: tuple(t.to(dev).contiguous() for t in inp[k]) for k in KEYS}
+    fa = lambda **kw: mlp.mlp_forward(d["o"], d["x"], d["mod"], d["wfc"], d["w12"], d["w2"], d["bfc"], d["b12"],
+                                      d["b2"], inp["eps"], **kw)
+    ba = lambda ws, **kw: mlp.mlp_backward(d["o"], d["mod"], d["wfc"], d["w12"], d["w2"], d["dout"], ws, **kw)
+    out, ws = fa()
+    ref = ba(ws)
+    ref = {k: tuple(t.clone() for t in v) for k, v in ref.items()}
+    ev_f = [torch.cuda.Event(enable_timing=True) for _ in range(len(_lib.MLP_FWD_STAGES))]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(len(_lib.MLP_BWD_STAGES))]
+    out_e, ws_e = fa(events=ev_f)
+    g_e = ba(ws_e, events=ev_b)
+    g_n = ba(ws, need_dbias=False)
+    torch.cuda.synchronize()
+    for s in range(2):
+        assert torch.equal(out_e[s], out[s])
+        for k in ref:
+            assert torch.equal(g_e[k][s], ref[k][s]), k
+            if k not in ("dbfc", "db12", "db2"):
+                assert torch.equal(g_n[k][s], ref[k][s]), k
+    assert not any(k in g_n for k in ("dbfc", "db12", "db2"))
+    # a smaller problem into the first call's (larger) workspaces, against the oracle
+    small = make_mlp_inputs(1, 40, 9, 128, 192, seed=6)
+    ds = {k: tuple(t.to(dev).contiguous() for t in small[k]) for k in KEYS}
+    fws_big = ws
+    bws_big = torch.empty(mlp.bwd_workspace_bytes(2, 96, 33, 128, 192), dtype=torch.uint8, device=dev)
+    out_s, _ = mlp.mlp_forward(ds["o"], ds["x"], ds["mod"], ds["wfc"], ds["w12"], ds["w2"], ds["bfc"], ds["b12"],
+                               ds["b2"], small["eps"], workspace=fws_big)
+    g_s = mlp.mlp_backward(ds["o"], ds["mod"], ds["wfc"], ds["w12"], ds["w2"], ds["dout"], fws_big, workspace=bws_big)
+    zero = tuple(torch.zeros_like(t) for t in ds["x"])
+    y_s, _ = mlp.mlp_forward(ds["o"], zero, ds["mod"], ds["wfc"], ds["w12"], ds["w2"], ds["bfc"], ds["b12"], ds["b2"],
+                             small["eps"])
+    torch.cuda.synchronize()
+    for s in range(2):
+        got = {k: f64(v[s]) for k, v in g_s.items()}
+        got["out"], got["y"] = f64(out_s[s]), f64(y_s[s])
+        check(got, run_oracle(small, s), small, s, f"reused workspaces, stream {s}")
+
+
+def test_mlp_wide_layer_partial_tiles():
+    """C = 1152 (18 heads of 64) and F = 3136 (not a multiple of 128: the last W1/W3 column tile is half
+    full), 2 samples of 250 + 29 tokens, against the full oracle."""
+    say("case: mlp B2 n_img 250 n_txt 29 C1152 F3136, seed 7")
+    inp = make_mlp_inputs(2, 250, 29, 1152, 3136, seed=7)
+    got = run_gpu(inp)
+    for s in range(2):
+        check(got[s], run_oracle(inp, s), inp, s, f"wide layer stream {s}")
