@@ -309,7 +309,7 @@ jattn_status jattn_adaln_qkv_bwd(const void* const x[2], const float* const mod[
   jattn::launch_dw_gemm(gdw, stream);
   if (!stage_done(3, stage_events, n_stage_events, stream)) return JATTN_ERROR_HIP;
   jattn::launch_mod_reduce(rm, stream);
-  if (hipGetLastError() != hipSuccess) return JATTN_ERROR_HIP;
+  if (!launched()) return JATTN_ERROR_HIP;
   jattn::launch_w_reduce(rw, stream);
   if (!stage_done(4, stage_events, n_stage_events, stream)) return JATTN_ERROR_HIP;
   return JATTN_SUCCESS;

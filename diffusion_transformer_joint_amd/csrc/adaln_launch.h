@@ -18,7 +18,7 @@ namespace jattn {
 
 constexpr int kGemmThreads = 256;  // 4 waves, 2 x 2 over the output tile
 constexpr int kGemmK = 64;         // contraction columns staged per step
-constexpr int kBwdRowChunk = 16;   // token rows of one sample per workgroup of the row backward
+constexpr int kBwdRowChunk = 64;   // token rows of one sample per workgroup of the row backward
 
 // A bf16 matrix M[rows][width] in memory whose columns are split into segments of `seg` columns,
 // segment i stored at p[i] (row stride rs elements). Rows at or past `rows` read as zeros.

@@ -768,67 +768,91 @@ __global__ __launch_bounds__(256) void rows_bwd_kernel(RowsBwdArgs a) {
       acc0[u][e] = acc1[u][e] = 0.f;
     }
   }
-  // each wave keeps the loads of RPW rows (r, r + 4, ...) in flight before computing any of them
-  constexpr int RPW = U <= 4 ? 4 : U <= 8 ? 2 : 1;
-  for (int r0 = r_lo + wave; r0 < r_hi; r0 += 4 * RPW) {
+  // A wave takes rounds of RPW rows (r, r + 4, ...). For C <= 1024 the loads of the next round are
+  // issued before the current round is computed (two row buffers), so each wave keeps up to 2 RPW
+  // rows in flight through its whole chunk instead of waiting for every round's loads.
+  constexpr int RPW = U <= 4 ? 2 : 1;
+  struct Rows {
     f32x4 dv[RPW][U];
     u32x2 xv[RPW][U];
     f32x2 ms[RPW];
+  };
+  auto load = [&](Rows& rb, int r0) {
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
       const int r = r0 + 4 * q;
       if (r < r_hi) {
         const size_t row = (size_t)b * n + r;
-        ms[q] = *reinterpret_cast<const f32x2*>(st + 2 * row);
+        rb.ms[q] = *reinterpret_cast<const f32x2*>(st + 2 * row);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = 4 * lane + 256 * u;
           if (c < C) {
-            dv[q][u] = *reinterpret_cast<const f32x4*>(dh + row * C + c);
-            xv[q][u] = *reinterpret_cast<const u32x2*>(x + row * C + c);
+            rb.dv[q][u] = *reinterpret_cast<const f32x4*>(dh + row * C + c);
+            rb.xv[q][u] = *reinterpret_cast<const u32x2*>(x + row * C + c);
           }
         }
       }
     }
+  };
+  // (g and xhat are recomputed for the output rather than kept: registers hold two row buffers, and
+  // the kernel is bound by memory, not arithmetic)
+  auto compute = [&](const Rows& rb, int r0) {
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
-    const int r = r0 + 4 * q;
-    if (r >= r_hi) break;
-    const size_t row = (size_t)b * n + r;
-    const float mean = ms[q][0], rstd = ms[q][1];
-    float g[U][4], xh[U][4], sg = 0.f, sgx = 0.f;
+      const int r = r0 + 4 * q;
+      if (r >= r_hi) break;
+      const size_t row = (size_t)b * n + r;
+      const float mean = rb.ms[q][0], rstd = rb.ms[q][1];
+      float sg = 0.f, sgx = 0.f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = 4 * lane + 256 * u;
-      if (c < C) {
-        const f32x4 d = dv[q][u];
-        float xf[4];
-        unpack4(xv[q][u], xf);
+      for (int u = 0; u < U; ++u) {
+        const int c = 4 * lane + 256 * u;
+        if (c < C) {
+          const f32x4 d = rb.dv[q][u];
+          float xf[4];
+          unpack4(rb.xv[q][u], xf);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xh[u][e] = (xf[e] - mean) * rstd;
-          g[u][e] = d[e] * s1[u][e];
-          sg += g[u][e];
-          sgx += g[u][e] * xh[u][e];
-          acc0[u][e] += d[e];
-          acc1[u][e] += d[e] * xh[u][e];
+          for (int e = 0; e < 4; ++e) {
+            const float xh = (xf[e] - mean) * rstd, g = d[e] * s1[u][e];
+            sg += g;
+            sgx += g * xh;
+            acc0[u][e] += d[e];
+            acc1[u][e] += d[e] * xh;
+          }
         }
-      } else {
+      }
+      const float mg = wave_sum(sg) / (float)C, mgx = wave_sum(sgx) / (float)C;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) g[u][e] = xh[u][e] = 0.f;
+      for (int u = 0; u < U; ++u) {
+        const int c = 4 * lane + 256 * u;
+        if (c < C) {
+          const f32x4 d = rb.dv[q][u];
+          float xf[4], o[4];
+          unpack4(rb.xv[q][u], xf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = rstd * (d[e] * s1[u][e] - mg - (xf[e] - mean) * rstd * mgx);
+          *reinterpret_cast<u32x2*>(dx + row * C + c) = (u32x2){pack2(o[0], o[1]), pack2(o[2], o[3])};
+        }
       }
     }
-    const float mg = wave_sum(sg) / (float)C, mgx = wave_sum(sgx) / (float)C;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = 4 * lane + 256 * u;
-      if (c < C) {
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = rstd * (g[u][e] - mg - xh[u][e] * mgx);
-        *reinterpret_cast<u32x2*>(dx + row * C + c) = (u32x2){pack2(o[0], o[1]), pack2(o[2], o[3])};
-      }
+  };
+  constexpr int STEP = 4 * RPW;  // rows between a wave's consecutive rounds
+  Rows ra;
+  int r0 = r_lo + wave;
+  if constexpr (U <= 4) {
+    Rows rb;
+    if (r0 < r_hi) load(ra, r0);
+    for (; r0 < r_hi; r0 += 2 * STEP) {
+      if (r0 + STEP < r_hi) load(rb, r0 + STEP);
+      compute(ra, r0);
+      if (r0 + 2 * STEP < r_hi) load(ra, r0 + 2 * STEP);
+      if (r0 + STEP < r_hi) compute(rb, r0 + STEP);
     }
+  } else {  // (wider rows: the accumulators leave room for one row buffer only)
+    for (; r0 < r_hi; r0 += STEP) {
+      load(ra, r0);
+      compute(ra, r0);
     }
   }
   // waves add their sums into LDS one after the other (fixed order)

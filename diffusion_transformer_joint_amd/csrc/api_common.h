@@ -42,6 +42,10 @@ inline jattn_status check_events(const hipEvent_t* ev, int n, int max) {
   return JATTN_SUCCESS;
 }
 
+// After a launch that is not the last of its stage: was it enqueued? (Checked per launch, so that a
+// failed launch cannot be hidden by a later one.)
+inline bool launched() { return hipGetLastError() == hipSuccess; }
+
 // After enqueueing stage i: check the launch and record its event.
 inline bool stage_done(int i, const hipEvent_t* ev, int n, hipStream_t stream) {
   if (hipGetLastError() != hipSuccess) return false;

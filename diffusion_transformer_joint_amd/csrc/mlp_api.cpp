@@ -390,8 +390,11 @@ jattn_status jattn_mlp_bwd(const void* const o[2], const float* const mod[2], co
   jattn::launch_dw_gemm(gwfc, stream);
   if (!stage_done(7, stage_events, n_stage_events, stream)) return JATTN_ERROR_HIP;
   jattn::launch_mod_reduce(rm, stream);
+  if (!launched()) return JATTN_ERROR_HIP;
   jattn::launch_w_reduce(r2, stream);
+  if (!launched()) return JATTN_ERROR_HIP;
   jattn::launch_w_reduce(r12, stream);
+  if (!launched()) return JATTN_ERROR_HIP;
   jattn::launch_w_reduce(rfc, stream);
   if (!stage_done(8, stage_events, n_stage_events, stream)) return JATTN_ERROR_HIP;
   return JATTN_SUCCESS;
