@@ -367,74 +367,100 @@ struct NoVisit {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Forward: adaLN modulation, one wave per token row.
+// Forward: adaLN modulation. A wave takes MR consecutive token rows (4 for C <= 1024, 2 up to 2048,
+// 1 above, where the registers of more rows would halve the waves per SIMD): the loads of all of them are
+// issued first, and a sample's shift and scale are loaded again only where the sample changes (one
+// row per wave made the launch tens of thousands of short load-reduce-store chains).
+
+template <int U>
+constexpr int mod_rows_per_wave() { return U <= 2 ? 4 : U <= 4 ? 2 : 1; }
 
 template <int U>  // 16-byte chunks per lane (C <= 512 U)
 __global__ __launch_bounds__(256) void modulate_kernel(ModulateArgs a) {
+  constexpr int MR = mod_rows_per_wave<U>();
   const int lane = threadIdx.x & 63;
-  const int row = (int)blockIdx.x * 4 + wave_id();
-  if (row >= a.T[0] + a.T[1]) return;
-  const int s = row >= a.T[0] ? 1 : 0;
-  const int r = row - (s ? a.T[0] : 0);
+  const int total = a.T[0] + a.T[1];
+  const int row0 = ((int)blockIdx.x * 4 + wave_id()) * MR;
+  if (row0 >= total) return;
   const int C = a.C, nch = C >> 3;
-  const int b = r / (s ? a.n[1] : a.n[0]);
-  const uint16_t* x = (s ? a.x[1] : a.x[0]) + (size_t)r * C;
-  const float* m = (s ? a.mod[1] : a.mod[0]) + (size_t)b * 2 * C;
-  // the row and its sample's shift and scale, all loads issued before the reductions
+  u32x4 v[MR][U];
+#pragma unroll
+  for (int k = 0; k < MR; ++k) {
+    const int row = row0 + k;
+    const int s = row >= a.T[0] ? 1 : 0;
+    const int r = row - (s ? a.T[0] : 0);
+    const uint16_t* x = (s ? a.x[1] : a.x[0]) + (size_t)r * C;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c8 = lane + 64 * u;
+      v[k][u] = row < total && c8 < nch ? *reinterpret_cast<const u32x4*>(x + c8 * 8) : (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
   f32x4 shv4[U][2], scv4[U][2];
+  int cur_s = -1, cur_b = -1;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c8 = lane + 64 * u;
-    if (c8 < nch) {
-      shv4[u][0] = *reinterpret_cast<const f32x4*>(m + c8 * 8);
-      shv4[u][1] = *reinterpret_cast<const f32x4*>(m + c8 * 8 + 4);
-      scv4[u][0] = *reinterpret_cast<const f32x4*>(m + C + c8 * 8);
-      scv4[u][1] = *reinterpret_cast<const f32x4*>(m + C + c8 * 8 + 4);
+  for (int k = 0; k < MR; ++k) {
+    const int row = row0 + k;
+    if (row >= total) break;
+    const int s = row >= a.T[0] ? 1 : 0;
+    const int r = row - (s ? a.T[0] : 0);
+    const int b = r / (s ? a.n[1] : a.n[0]);
+    if (s != cur_s || b != cur_b) {  // (wave-uniform)
+      const float* m = (s ? a.mod[1] : a.mod[0]) + (size_t)b * 2 * C;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c8 = lane + 64 * u;
+        if (c8 < nch) {
+          shv4[u][0] = *reinterpret_cast<const f32x4*>(m + c8 * 8);
+          shv4[u][1] = *reinterpret_cast<const f32x4*>(m + c8 * 8 + 4);
+          scv4[u][0] = *reinterpret_cast<const f32x4*>(m + C + c8 * 8);
+          scv4[u][1] = *reinterpret_cast<const f32x4*>(m + C + c8 * 8 + 4);
+        }
+      }
+      cur_s = s;
+      cur_b = b;
     }
-  }
-  u32x4 v[U];
-  float sum = 0.f;
+    float sum = 0.f;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c8 = lane + 64 * u;
-    v[u] = c8 < nch ? *reinterpret_cast<const u32x4*>(x + c8 * 8) : (u32x4){0u, 0u, 0u, 0u};
-    float f[8];
-    unpack8(v[u], f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sum += f[e];
-  }
-  const float mean = wave_sum(sum) / (float)C;
-  float ss = 0.f;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (lane + 64 * u < nch) {
+    for (int u = 0; u < U; ++u) {
       float f[8];
-      unpack8(v[u], f);
+      unpack8(v[k][u], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += (f[e] - mean) * (f[e] - mean);
+      for (int e = 0; e < 8; ++e) sum += f[e];
     }
-  }
-  const float rstd = 1.f / sqrtf(wave_sum(ss) / (float)C + a.eps);
-  uint16_t* h = (s ? a.h[1] : a.h[0]) + (size_t)r * C;
+    const float mean = wave_sum(sum) / (float)C;
+    float ss = 0.f;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c8 = lane + 64 * u;
-    if (c8 < nch) {
-      const f32x4 sh0 = shv4[u][0], sh1 = shv4[u][1], sc0 = scv4[u][0], sc1 = scv4[u][1];
-      const float shv[8] = {sh0[0], sh0[1], sh0[2], sh0[3], sh1[0], sh1[1], sh1[2], sh1[3]};
-      const float scv[8] = {sc0[0], sc0[1], sc0[2], sc0[3], sc1[0], sc1[1], sc1[2], sc1[3]};
-      float f[8], o[8];
-      unpack8(v[u], f);
+    for (int u = 0; u < U; ++u) {
+      if (lane + 64 * u < nch) {
+        float f[8];
+        unpack8(v[k][u], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (f[e] - mean) * rstd * (1.f + scv[e]) + shv[e];
-      *reinterpret_cast<u32x4*>(h + c8 * 8) =
-          (u32x4){pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
+        for (int e = 0; e < 8; ++e) ss += (f[e] - mean) * (f[e] - mean);
+      }
     }
-  }
-  if (lane == 0) {
-    float* st = (s ? a.stats[1] : a.stats[0]) + 2 * (size_t)r;
-    st[0] = mean;
-    st[1] = rstd;
+    const float rstd = 1.f / sqrtf(wave_sum(ss) / (float)C + a.eps);
+    uint16_t* h = (s ? a.h[1] : a.h[0]) + (size_t)r * C;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c8 = lane + 64 * u;
+      if (c8 < nch) {
+        const f32x4 sh0 = shv4[u][0], sh1 = shv4[u][1], sc0 = scv4[u][0], sc1 = scv4[u][1];
+        const float shv[8] = {sh0[0], sh0[1], sh0[2], sh0[3], sh1[0], sh1[1], sh1[2], sh1[3]};
+        const float scv[8] = {sc0[0], sc0[1], sc0[2], sc0[3], sc1[0], sc1[1], sc1[2], sc1[3]};
+        float f[8], o[8];
+        unpack8(v[k][u], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (f[e] - mean) * rstd * (1.f + scv[e]) + shv[e];
+        *reinterpret_cast<u32x4*>(h + c8 * 8) =
+            (u32x4){pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
+      }
+    }
+    if (lane == 0) {
+      float* st = (s ? a.stats[1] : a.stats[0]) + 2 * (size_t)r;
+      st[0] = mean;
+      st[1] = rstd;
+    }
   }
 }
 
@@ -935,13 +961,14 @@ constexpr int kQkvNB = 3, kDhNB = 2, kDwNB = 2;
 void launch_modulate(const ModulateArgs& a, hipStream_t stream) {
   const int rows = a.T[0] + a.T[1];
   if (rows == 0) return;
-  const dim3 grid((rows + 3) / 4), block(256);
+  const dim3 block(256);
+  auto grid = [&](int per_wave) { return dim3((rows + 4 * per_wave - 1) / (4 * per_wave)); };
   if (a.C <= 1024)
-    hipLaunchKernelGGL(modulate_kernel<2>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(modulate_kernel<2>, grid(mod_rows_per_wave<2>()), block, 0, stream, a);
   else if (a.C <= 2048)
-    hipLaunchKernelGGL(modulate_kernel<4>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(modulate_kernel<4>, grid(mod_rows_per_wave<4>()), block, 0, stream, a);
   else
-    hipLaunchKernelGGL(modulate_kernel<8>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(modulate_kernel<8>, grid(mod_rows_per_wave<8>()), block, 0, stream, a);
 }
 
 void launch_qkv_gemm(const GemmArgs& a, hipStream_t stream) {
