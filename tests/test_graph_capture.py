@@ -1,0 +1,92 @@
+"""HIP graph capture: the library allocates nothing, never synchronises and clears memory with its
+own kernels (no memset nodes), so a forward + backward step of each entry-point family can be
+captured into a graph and replayed. Each graph is replayed several times, with eager work of the
+same entry points and synchronisations between the replays, and every replay must reproduce the
+eager results bit for bit (all kernels are deterministic)."""
+import pytest
+import torch
+
+from diffusion_transformer_joint_amd import adaln, mlp, ops
+from diffusion_transformer_joint_amd.inputs import make_adaln_inputs, make_mlp_inputs, make_shape_inputs
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 4
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def capture(step):
+    """Run `step` once eagerly on a side stream (as torch requires before capture), then capture it."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        res = step()
+    return g, res
+
+
+def flatten(x):
+    if isinstance(x, torch.Tensor):
+        return [x]
+    if isinstance(x, dict):
+        return [t for k in sorted(x) for t in flatten(x[k])]
+    return [t for item in x for t in flatten(item)]
+
+
+def replay_and_compare(tag, step, g, captured):
+    ref = [t.clone() for t in flatten(step())]  # eager results
+    torch.cuda.synchronize()
+    out = flatten(captured)
+    for r in range(REPLAYS):
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(out, ref)):
+            assert torch.equal(a, b), (tag, r, i)
+        junk = flatten(step())  # eager work of the same entry points between replays
+        torch.cuda.synchronize()
+        del junk
+    say(f"{tag}: {REPLAYS} replays bitwise equal to eager ({len(out)} tensors)")
+
+
+def test_graph_joint_attention():
+    say("case: graph capture, joint attention B2 L300 H2 D64 valid_len [300, 171], seed 21")
+    dev = torch.device("cuda:0")
+    inp = make_shape_inputs(2, 300, 2, 64, seed=21, valid_len=[300, 171])
+    q, k, v, dout, gains = (inp[n].to(dev) for n in ("q", "k", "v", "dout", "gains"))
+    vl = inp["valid_len"].to(dev)
+
+    def step():
+        out, lse, fws = ops.forward(q, k, v, gains, vl, inp["scale"], inp["eps"], return_workspace=True)
+        return (out, lse) + tuple(ops.backward(q, k, v, gains, out, lse, dout, vl, inp["scale"], inp["eps"],
+                                               fwd_workspace=fws))
+
+    g, captured = capture(step)
+    replay_and_compare("joint attention", step, g, captured)
+
+
+def test_graph_adaln_and_mlp():
+    say("case: graph capture, adaLN projection B2 n_img 96 n_txt 21 C192 and MLP block C192 F256, seed 22")
+    dev = torch.device("cuda:0")
+    ai = make_adaln_inputs(2, 96, 21, 192, seed=22)
+    a = {k: tuple(t.to(dev) for t in ai[k]) for k in ("x", "mod", "w", "bias", "dq", "dk", "dv")}
+    mi = make_mlp_inputs(2, 96, 21, 192, 256, seed=23)
+    keys = ("o", "x", "mod", "wfc", "bfc", "w12", "b12", "w2", "b2", "dout")
+    m = {k: tuple(t.to(dev) for t in mi[k]) for k in keys}
+
+    def step():
+        q, k, v, ws = adaln.adaln_qkv_forward(a["x"], a["mod"], a["w"], a["bias"], ai["eps"])
+        ga = adaln.adaln_qkv_backward(a["x"], a["mod"], a["w"], a["dq"], a["dk"], a["dv"], ws)
+        out, mws = mlp.mlp_forward(m["o"], m["x"], m["mod"], m["wfc"], m["w12"], m["w2"], m["bfc"], m["b12"], m["b2"],
+                                   mi["eps"])
+        gm = mlp.mlp_backward(m["o"], m["mod"], m["wfc"], m["w12"], m["w2"], m["dout"], mws)
+        return (q, k, v, ga, out, gm)
+
+    g, captured = capture(step)
+    replay_and_compare("adaLN projection + MLP block", step, g, captured)
