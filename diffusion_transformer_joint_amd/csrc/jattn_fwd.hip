@@ -205,7 +205,27 @@ __device__ __forceinline__ void fwd_loop(FwdRing<D, S>& ring, const bf16x8 (&qf)
   };
   if constexpr (!W) {
     for (int t = 0; t < nfull; ++t) step(std::false_type{}, t);
-    if (nfull < ntiles) step(std::true_type{}, nfull);
+    if (nfull < ntiles) {
+      if constexpr (BOUNDED) {
+        // The last tile runs unmasked. Its rows past n arrived as zeros (K and V), so each such key's
+        // score is exactly the accumulator seed -shift and its rounded probability p0 = bf16(2^-shift)
+        // is the same for every one of them, while its V row adds nothing to O: the row sums only
+        // need the masked keys' p0 taken out again. This lane holds the keys 8 k + 4 g + b (k < 8,
+        // b < 4) of the tile; those at or past m0 = n - key0 are masked.
+        step(std::false_type{}, nfull);
+        const int m0 = n - nfull * kTile, g4 = 4 * (lane >> 5);
+        int nm = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) nm += min(4, max(0, 8 * k + g4 + 4 - m0));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float p0 = bf_lo(pack2(fast_exp2(-shift[qt]), 0.f));
+          st.lsum[qt] -= (float)nm * p0;
+        }
+      } else {
+        step(std::true_type{}, nfull);
+      }
+    }
   } else {
     auto wstep = [&](auto masked, int t) {
       if (t + NB - 1 < tr.hi) ring.issue(t + NB - 1, cur == 0 ? NB - 1 : cur - 1);
