@@ -7,10 +7,14 @@ take minutes); only the sampled rows or (batch, head) pairs are copied back for 
 computes them exactly because pairs (attention) and token rows (per-row outputs of the projections)
 are independent. Sums over all tokens are checked through exact column sums and the Euler identity
 of the linear parameters, as in the full-workload tests. Tolerances are those of each family."""
+import os
+import sys
+
 import numpy as np
 import pytest
 import torch
 
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))  # (the sibling parity files)
 import test_parity as tj
 import test_parity_adaln as ta
 import test_parity_mlp as tm
@@ -19,6 +23,14 @@ from diffusion_transformer_joint_amd.inputs import default_scale
 from oracle import adaln_qkv_fwd_bwd, attention_fwd_bwd, mlp_fwd_bwd
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def release_memory():
+    """These tests hold tens of GB; hand the cached blocks back so later tests start from a clean pool."""
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def say(msg):

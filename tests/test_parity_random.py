@@ -7,9 +7,13 @@ runs. Tolerances and comparisons are those of the family's own parity file (impo
 a drawn key mask or window can leave a row with a single key, that row's LSE is one score with no
 averaging of its rounding, and the LSE bound is the single-score bound the window parity file derives.
 """
+import os
+import sys
+
 import numpy as np
 import pytest
 
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))  # (the sibling parity files)
 import test_parity as tj
 import test_parity_adaln as ta
 import test_parity_mlp as tm
