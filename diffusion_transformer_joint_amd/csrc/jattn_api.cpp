@@ -15,7 +15,7 @@ using jattn::kBwdRowsPerBlock;
 
 constexpr int kAbiVersion = 9;
 
-bool supported_head_dim(int D) { return D == 32 || D == 64 || D == 72 || D == 128; }
+bool supported_head_dim(int D) { return D % 8 == 0 && D >= 32 && D <= 128; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 

@@ -47,14 +47,17 @@ namespace jattn {
 
 static_assert(kBwdRowsPerBlock == kBwdWaves * kWaveRows && kBwdWaves >= 2, "backward workgroup shape");
 
-// Waves per SIMD the register allocation targets: two up to D = 72, one at D = 128 (whose
+// Waves per SIMD the register allocation targets: two up to D = 72, one above (from D = 80 the
 // accumulators and operand fragments need the whole register file).
 template <int D>
 constexpr int bwd_waves_per_eu() { return D <= 72 ? 2 : 1; }
-// LDS ring depth: four tile buffers (loads issued three tiles ahead; measured slightly faster than
-// three), two at D = 72 whose padded tiles would otherwise not leave room for two workgroups per CU.
+// Two waves per SIMD with tiles padded past 64 columns (D = 72): the tightest case for LDS and registers.
 template <int D>
-constexpr int bwd_nbuf() { return D == 72 || kBwdWaves < 4 ? 2 : 4; }
+constexpr bool bwd_tight() { return Dims<D>::DM > 64 && bwd_waves_per_eu<D>() == 2; }
+// LDS ring depth: four tile buffers (loads issued three tiles ahead; measured slightly faster than
+// three), two in the tight case, whose padded tiles would otherwise not leave room for two workgroups per CU.
+template <int D>
+constexpr int bwd_nbuf() { return bwd_tight<D>() || kBwdWaves < 4 ? 2 : 4; }
 
 
 // LDS plan of the two main kernels. The swizzled layout (D = 64, 128) serves both row-fragment and
@@ -96,7 +99,7 @@ struct RowC {
   u32x2 w[Dims<D>::MT][4];
 };
 template <int D>
-constexpr bool keep_row_c() { return D != 72; }  // D = 72 has no registers to spare at two waves/SIMD
+constexpr bool keep_row_c() { return !bwd_tight<D>(); }  // (no registers to spare in the tight case)
 
 template <int D>
 __device__ __forceinline__ void load_row_c(RowC<D>& x, const uint16_t* __restrict__ row, bool valid, int g) {
@@ -812,10 +815,10 @@ template <bool S, bool V, bool W>
 static hipError_t launch_bwd_s(int D, const BwdArgs& a, bool prenorm, const hipEvent_t* events, int n_events,
                                hipStream_t stream) {
   switch (D) {
-    case 32: return launch_bwd_d<32, S, V, W>(a, prenorm, events, n_events, stream);
-    case 64: return launch_bwd_d<64, S, V, W>(a, prenorm, events, n_events, stream);
-    case 72: return launch_bwd_d<72, S, V, W>(a, prenorm, events, n_events, stream);
-    case 128: return launch_bwd_d<128, S, V, W>(a, prenorm, events, n_events, stream);
+#define JATTN_CASE(DD) \
+  case DD: return launch_bwd_d<DD, S, V, W>(a, prenorm, events, n_events, stream);
+    JATTN_FOR_EACH_HEAD_DIM(JATTN_CASE)
+#undef JATTN_CASE
     default: return hipErrorInvalidValue;
   }
 }

@@ -47,7 +47,7 @@ struct Dims {
   static constexpr int KS = DK / 16;                  // MFMA k-steps over d
   static constexpr int DM = (D + 31) / 32 * 32;       // output width (32-row MFMA tiles over d)
   static constexpr int MT = DM / 32;                  // MFMA tiles over d
-  static constexpr int TPR = NCH >= 8 ? 8 : NCH;      // staging threads per row
+  static constexpr int TPR = NCH >= 8 ? 8 : 4;        // staging threads per row (a power of two)
   static constexpr int CPT = (NCH + TPR - 1) / TPR;   // staging chunks per thread
   static constexpr int RPP = kThreads / TPR;          // rows staged per pass
   static constexpr int PASSES = kTile / RPP;          // passes per tile

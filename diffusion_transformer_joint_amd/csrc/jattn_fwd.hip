@@ -54,7 +54,8 @@ struct Fwd {
   // value rows: read transposed only (swizzled for D = 64, 128, else a pitch for transposed reads)
   using LV = Lay<D, (D == 64 || D == 128) ? kSwizzled : kTrRead>;
   // ring depth: three buffers (loads two tiles ahead) where two workgroups per CU still fit in LDS
-  static constexpr int NB = (D == 72 || D == 128) ? 2 : 3;
+  // (up to 64 padded columns), else two
+  static constexpr int NB = Dims<D>::DM > 64 ? 2 : 3;
   static constexpr int STAGE = NB * (LK::ELEMS + LV::ELEMS) * 2;  // bytes
   static constexpr int BYTES = STAGE + 16;
   static_assert(QT == 1 || QT == 2, "query tiles per wave");
@@ -424,10 +425,10 @@ template <bool S, bool V, bool W>
 static hipError_t launch_fwd_s(int D, const FwdArgs& a, const hipEvent_t* events, int n_events,
                                hipStream_t stream) {
   switch (D) {
-    case 32: return launch_fwd_d<32, S, V, W>(a, events, n_events, stream);
-    case 64: return launch_fwd_d<64, S, V, W>(a, events, n_events, stream);
-    case 72: return launch_fwd_d<72, S, V, W>(a, events, n_events, stream);
-    case 128: return launch_fwd_d<128, S, V, W>(a, events, n_events, stream);
+#define JATTN_CASE(DD) \
+  case DD: return launch_fwd_d<DD, S, V, W>(a, events, n_events, stream);
+    JATTN_FOR_EACH_HEAD_DIM(JATTN_CASE)
+#undef JATTN_CASE
     default: return hipErrorInvalidValue;
   }
 }

@@ -97,6 +97,10 @@ struct BwdArgs {
 // Rows per workgroup, shared by the host-side grid and workspace sizing and the kernels.
 // Forward: 4 waves of 64 queries (two independent 32-query tiles per wave) for D <= 64, where the
 // register budget allows it; 4 waves of 32 queries otherwise.
+// The compiled head dims: every multiple of 8 from 32 to 128. X(D) is expanded once per head dim
+// (used for the switch statements that pick a kernel instantiation).
+#define JATTN_FOR_EACH_HEAD_DIM(X) X(32) X(40) X(48) X(56) X(64) X(72) X(80) X(88) X(96) X(104) X(112) X(120) X(128)
+
 constexpr int fwd_rows_per_block(int D) { return D <= 64 ? 256 : 128; }
 // Backward: both kernels use workgroups of kBwdWaves waves of 32 rows.
 constexpr int kBwdWaves = 4;

@@ -99,10 +99,10 @@ static hipError_t launch_prenorm_d(const PrenormArgs& a, hipStream_t stream) {
 template <bool S, bool V>
 static hipError_t launch_prenorm_s(int D, const PrenormArgs& a, hipStream_t stream) {
   switch (D) {
-    case 32: return launch_prenorm_d<32, S, V>(a, stream);
-    case 64: return launch_prenorm_d<64, S, V>(a, stream);
-    case 72: return launch_prenorm_d<72, S, V>(a, stream);
-    case 128: return launch_prenorm_d<128, S, V>(a, stream);
+#define JATTN_CASE(DD) \
+  case DD: return launch_prenorm_d<DD, S, V>(a, stream);
+    JATTN_FOR_EACH_HEAD_DIM(JATTN_CASE)
+#undef JATTN_CASE
     default: return hipErrorInvalidValue;
   }
 }

@@ -29,7 +29,8 @@
  *    allocates, frees, synchronises or prints, and keeps no mutable global state.
  *  - Arguments are validated on the host before any HIP call. Device-side data (valid_len values,
  *    tensor contents) is not validated: valid_len values are clamped to [0, L]; NaN inputs propagate.
- *  - Supported head dims: D in {32, 64, 72, 128}. Sizes must satisfy L*H*D < 2^31 and B*H*L < 2^31.
+ *  - Supported head dims: every multiple of 8 from 32 to 128. Sizes must satisfy L*H*D < 2^31 and
+ *    B*H*L < 2^31.
  */
 #ifndef JATTN_H
 #define JATTN_H

@@ -66,7 +66,7 @@ def fwd(lib, **kw):
     (dict(B=0), _lib.INVALID_VALUE),
     (dict(L=0), _lib.INVALID_VALUE),
     (dict(H=-1), _lib.INVALID_VALUE),
-    (dict(D=48), _lib.NOT_SUPPORTED),
+    (dict(D=44), _lib.NOT_SUPPORTED),
     (dict(D=256), _lib.NOT_SUPPORTED),
     (dict(B=1, L=1 << 20, H=64, D=128), _lib.NOT_SUPPORTED),
     (dict(scale=math.inf), _lib.INVALID_VALUE),
@@ -144,14 +144,14 @@ def test_bwd_rejects_small_workspace(lib):
 
 def test_fwd_workspace_bytes(lib):
     assert lib.jattn_fwd_workspace_bytes(0, 10, 1, 64) == 0
-    assert lib.jattn_fwd_workspace_bytes(1, 10, 1, 40) == 0
+    assert lib.jattn_fwd_workspace_bytes(1, 10, 1, 44) == 0
     w = lib.jattn_fwd_workspace_bytes(16, 1101, 12, 64)
     assert w >= 16 * 1101 * 12 * 64 * 2 and w % 256 == 0
 
 
 def test_workspace_bytes(lib):
     assert lib.jattn_bwd_workspace_bytes(0, 10, 1, 64) == 0
-    assert lib.jattn_bwd_workspace_bytes(1, 10, 1, 40) == 0
+    assert lib.jattn_bwd_workspace_bytes(1, 10, 1, 44) == 0
     w = lib.jattn_bwd_workspace_bytes(16, 1101, 12, 64)
     # normalised K and Q rows (bf16), two statistics per padded query row (9 blocks of 128 rows per
     # pair) and one set of per-workgroup gain-gradient partials
@@ -210,7 +210,7 @@ def fwd_streams(lib, **kw):
     (dict(k=(fake(2) + 8, 3)), _lib.INVALID_VALUE),           # misaligned image part
     (dict(n_img=-1), _lib.INVALID_VALUE),
     (dict(n_img=0, n_txt=0), _lib.INVALID_VALUE),
-    (dict(D=48), _lib.NOT_SUPPORTED),
+    (dict(D=44), _lib.NOT_SUPPORTED),
     (dict(gains=None), _lib.INVALID_VALUE),
     (dict(eps=math.nan), _lib.INVALID_VALUE),
     (dict(out=(1, 8)), _lib.INVALID_VALUE),                   # image output aliases the text query part
@@ -288,7 +288,7 @@ def fwd_varlen(lib, **kw):
     (dict(total=0), _lib.INVALID_VALUE),
     (dict(maxlen=0), _lib.INVALID_VALUE),
     (dict(B=0), _lib.INVALID_VALUE),
-    (dict(D=40), _lib.NOT_SUPPORTED),
+    (dict(D=36), _lib.NOT_SUPPORTED),
     (dict(B=70000), _lib.NOT_SUPPORTED),
     (dict(cu=fake(4) + 2), _lib.INVALID_VALUE),           # misaligned offsets
     (dict(out=fake(0)), _lib.INVALID_VALUE),              # out aliases q
@@ -323,7 +323,7 @@ def test_bwd_varlen_rejects(lib):
 
 def test_varlen_workspace_bytes(lib):
     assert lib.jattn_varlen_fwd_workspace_bytes(2, 10, 0, 1, 64) == 0
-    assert lib.jattn_varlen_fwd_workspace_bytes(2, 10, 15, 1, 40) == 0
+    assert lib.jattn_varlen_fwd_workspace_bytes(2, 10, 15, 1, 44) == 0
     f = lib.jattn_varlen_fwd_workspace_bytes(16, 2370, 22682, 12, 64)
     assert f >= 22682 * 12 * 64 * 2 and f % 256 == 0
     w = lib.jattn_varlen_bwd_workspace_bytes(16, 2370, 22682, 12, 64)
@@ -343,7 +343,7 @@ def test_window_entry_points_reject(lib):
                                     a["ws_bytes"], None, 0, None)
     assert fwdw(q=None) == _lib.INVALID_VALUE
     assert fwdw(out=fake(1)) == _lib.INVALID_VALUE
-    assert fwdw(D=48) == _lib.NOT_SUPPORTED
+    assert fwdw(D=44) == _lib.NOT_SUPPORTED
     assert fwdw(ws_bytes=16) == _lib.WORKSPACE
     assert fwdw(left=-5, right=10**9, ws_bytes=16) == _lib.WORKSPACE   # any bounds are accepted
     need = lib.jattn_bwd_workspace_bytes(2, 100, 3, 64)
