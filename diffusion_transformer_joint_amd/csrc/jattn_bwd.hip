@@ -729,7 +729,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
 // ------------------------------------------------------------------------------------------------
 // Gain gradients from the per-workgroup partial sums (stored column-major, part[set][d][item]), each
 // summed in a fixed order: block x sums row x of the partials; thread t sums items t, t + 256, ...
-// (coalesced), then the wave sums are combined by a fixed butterfly and in wave order.
+// (coalesced) in batches of eight whose loads are all issued before the first add (the kernel is
+// latency-bound: a few thousand items take one or two round trips to memory), then the wave sums
+// are combined by a fixed butterfly and in wave order.
 // Joint form (x = d < D): dgains[0][d] = g_k[d] * T[d] and dgains[1][d] = g_q[d] * T[d] with T the
 // total of set 0. Two-stream form (x = set * D + d < 4 D): dgains[x] = the total of row x, i.e.
 // dgains[s][0] (Q gain of stream s) from set 2 s and dgains[s][1] from set 2 s + 1.
@@ -742,17 +744,18 @@ __global__ __launch_bounds__(kReduceThreads) void dg_reduce_kernel(const float* 
   __shared__ float wsum[kReduceThreads / 64];
   const int x = blockIdx.x, t = threadIdx.x;
   const float* p = part + (size_t)x * items;
+  constexpr int kBatch = 8;
   float s = 0.f;
-  int i = t;
-  for (; i + 3 * kReduceThreads < items; i += 4 * kReduceThreads) {
-    const float v0 = p[i], v1 = p[i + kReduceThreads], v2 = p[i + 2 * kReduceThreads],
-                v3 = p[i + 3 * kReduceThreads];
-    s += v0;
-    s += v1;
-    s += v2;
-    s += v3;
+  for (int i0 = t; i0 < items; i0 += kBatch * kReduceThreads) {
+    float v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + j * kReduceThreads;
+      v[j] = i < items ? p[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) s += v[j];
   }
-  for (; i < items; i += kReduceThreads) s += p[i];
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
   if ((t & 63) == 0) wsum[t >> 6] = s;
