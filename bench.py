@@ -5,7 +5,9 @@
                     [--variant joint|streams|varlen|window|adaln|mlp]
 
 A step is one forward (jattn_fwd) plus one backward (jattn_bwd) over the whole batch of the workload,
-inputs resident in HBM. Prints one JSON line. The throughput is algorithmic TFLOP/s:
+inputs resident in HBM. Prints one JSON line. Before the --warmup steps a pre-roll runs steps in
+windows of 10 until the last three windows agree within 2 % (reported as `preroll`), so the timed
+region starts at steady clocks however few warm-up steps are asked for. The throughput is algorithmic TFLOP/s:
 4*B*H*L*L*D for the forward (valid keys only for ragged workloads) and 2.5x that for the backward.
 
 Joint-variant lines also carry `hbm` (the step's algorithmic HBM bytes, 8BLHD + 4BHL forward and
@@ -256,6 +258,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    pre = preroll(torch, stream, lambda: (fwd(), bwd()), new_event)
     for _ in range(args.warmup):
         fwd()
         bwd()
@@ -309,8 +312,10 @@ def main():
     kern_ms = {}
     for j, name in enumerate(stages):
         kern_ms[name] = sum((ev0[i] if j == 0 else evb[i][j - 1]).elapsed_time(evb[i][j]) for i in range(KB)) / KB
+    # forward and backward shares from the same (breakdown) pass: the span from the step's start to the
+    # forward's last stage event, and from there to the backward's last one
     ms_fwd = sum(ev0[i].elapsed_time(evb[i][nf - 1]) for i in range(KB)) / KB
-    ms_bwd = ms_step - ms_fwd
+    ms_bwd = sum(evb[i][nf - 1].elapsed_time(evb[i][-1]) for i in range(KB)) / KB
     # per-step spread from the same pass (events at the step's start, between fwd and bwd, at its end)
     spread = lambda xs: {"median": round(sorted(xs)[len(xs) // 2], 5), "min": round(min(xs), 5)}
     per_step = {"fwd": spread([ev0[i].elapsed_time(evb[i][nf - 1]) for i in range(KB)]),
@@ -383,12 +388,14 @@ def main():
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(ms_fwd, 5),
         "bwd_ms": round(ms_bwd, 5),
+        "fwd_bwd_source": "breakdown pass (every stage event recorded; both from the same pass)",
         "fwd_tflops": round(fwd_tflops, 2),
         "bwd_tflops": round(bwd_tflops, 2),
         "gflop_per_step": round(fl["total"] / 1e9, 3),
         "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
         "kernel_ms_timed_region": {k: round(v, 5) for k, v in live_ms.items()},
         "per_step": per_step,
+        "preroll": pre,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -418,6 +425,28 @@ def main():
         res["padded"] = padded
         res["padded"]["speedup"] = round(padded["ms_per_step"] / ms_step, 4)
     print(json.dumps(res), flush=True)
+
+
+def preroll(torch, stream, step, new_event, window=10, tol=0.02, min_windows=5, max_windows=100):
+    """Run `step` in windows of `window` steps until the last three windows' times agree within `tol`
+    (relative), so that the timed region starts at steady clocks whatever --warmup says. Returns the
+    record reported as `preroll` in the JSON line."""
+    times = []
+    for _ in range(max_windows):
+        a, b = new_event(), new_event()
+        a.record(stream)
+        for _ in range(window):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+        last = times[-3:]
+        if len(times) >= min_windows and max(last) - min(last) <= tol * min(last):
+            break
+    last = times[-3:]
+    return {"preroll_steps": window * len(times), "preroll_ms": round(sum(times), 3),
+            "last_windows_ms_per_step": [round(t / window, 5) for t in last],
+            "converged": len(last) == 3 and max(last) - min(last) <= tol * min(last)}
 
 
 def run_busy_probes(torch):
@@ -473,7 +502,8 @@ def breakdown_pass(fwd, bwd, stages, nfs, KB, stream, new_event, handle):
     for j, name in enumerate(stages):
         kern_ms[name] = sum((ev0[i] if j == 0 else evb[i][j - 1]).elapsed_time(evb[i][j]) for i in range(KB)) / KB
     ms_fwd = sum(ev0[i].elapsed_time(evb[i][nfs - 1]) for i in range(KB)) / KB
-    return kern_ms, ms_fwd
+    ms_bwd = sum(evb[i][nfs - 1].elapsed_time(evb[i][-1]) for i in range(KB)) / KB
+    return kern_ms, ms_fwd, ms_bwd
 
 
 def timed_region(fwd, bwd, j, nfs, K, stream, new_event, handle):
@@ -568,6 +598,7 @@ def bench_adaln(args, torch):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    pre = preroll(torch, stream, lambda: (fwd(), bwd()), new_event)
     for _ in range(args.warmup):
         fwd()
         bwd()
@@ -578,7 +609,7 @@ def bench_adaln(args, torch):
     label = lambda n: f"{n}<{targs[n]}>" if n in targs else n
     stages = [label(n) + " (fwd)" if n == "modulate_kernel" else label(n) for n in _lib.ADALN_FWD_STAGES]
     stages += [label(n) for n in _lib.ADALN_BWD_STAGES]
-    kern_ms, ms_fwd = breakdown_pass(fwd, bwd, stages, nfs, min(K, 50), stream, new_event, handle)
+    kern_ms, ms_fwd, ms_bwd = breakdown_pass(fwd, bwd, stages, nfs, min(K, 50), stream, new_event, handle)
     gemms = [label(n) for n in ("qkv_gemm_kernel", "dh_gemm_kernel", "dw_gemm_kernel")]
     dom = max(gemms, key=lambda n: kern_ms[n])
     ms_step, dom_ms = timed_region(fwd, bwd, stages.index(dom), nfs, K, stream, new_event, handle)
@@ -600,7 +631,8 @@ def bench_adaln(args, torch):
         "config": {"workload": args.workload, "variant": "adaln", "B": B, "n_img": w.n_img, "n_txt": w.n_txt,
                    "C": C, "global_batch": B, "parallelism": "single-gpu"},
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_step - ms_fwd, 5),
+        "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_bwd, 5), "preroll": pre,
+        "fwd_bwd_source": "breakdown pass (both from the same pass)",
         "gflop_per_step": round(fl["total"] / 1e9, 3),
         "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
         "roofline": roofline, "cpu_baseline": cpu,
@@ -672,6 +704,7 @@ def bench_mlp(args, torch):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    pre = preroll(torch, stream, lambda: (fwd(), bwd()), new_event)
     for _ in range(args.warmup):
         fwd()
         bwd()
@@ -687,7 +720,7 @@ def bench_mlp(args, torch):
            "do_gemm": "qkv_gemm_kernel<256, 128, 3> (do)", "dwfc_gemm": "dw_gemm_kernel<256, 256, 2> (dWfc)",
            "reductions": "reductions"}
     stages = [lab[n] for n in _lib.MLP_FWD_STAGES] + [lab[n] for n in _lib.MLP_BWD_STAGES]
-    kern_ms, ms_fwd = breakdown_pass(fwd, bwd, stages, nfs, min(K, 50), stream, new_event, handle)
+    kern_ms, ms_fwd, ms_bwd = breakdown_pass(fwd, bwd, stages, nfs, min(K, 50), stream, new_event, handle)
     T = B * (w.n_img + w.n_txt)
     # GEMM FLOPs per launch (2 T x output x contraction); the dominant one is the largest by time
     per_launch = {lab["fc_gemm"]: 2.0 * T * C * C, lab["swiglu_gemm_kernel"]: 2.0 * T * 2 * Fh * C,
@@ -714,7 +747,8 @@ def bench_mlp(args, torch):
         "config": {"workload": args.workload, "variant": "mlp", "B": B, "n_img": w.n_img, "n_txt": w.n_txt, "C": C,
                    "F": Fh, "global_batch": B, "parallelism": "single-gpu"},
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_step - ms_fwd, 5),
+        "fwd_ms": round(ms_fwd, 5), "bwd_ms": round(ms_bwd, 5), "preroll": pre,
+        "fwd_bwd_source": "breakdown pass (both from the same pass)",
         "gflop_per_step": round(fl["total"] / 1e9, 3),
         "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
         "roofline": roofline, "cpu_baseline": cpu,
