@@ -15,7 +15,7 @@ STATUS = {0: "JATTN_SUCCESS", 1: "JATTN_ERROR_INVALID_VALUE", 2: "JATTN_ERROR_NO
           3: "JATTN_ERROR_WORKSPACE", 4: "JATTN_ERROR_HIP"}
 SUCCESS, INVALID_VALUE, NOT_SUPPORTED, WORKSPACE, HIP = range(5)
 
-EXPORTED = ("jattn_fwd", "jattn_fwd_ex", "jattn_fwd_workspace_bytes", "jattn_bwd", "jattn_bwd_ex", "jattn_bwd_workspace_bytes",
+EXPORTED = ("jattn_fwd", "jattn_fwd_noalloc", "jattn_fwd_noalloc_max_scratch_bytes", "jattn_fwd_ex", "jattn_fwd_workspace_bytes", "jattn_bwd", "jattn_bwd_ex", "jattn_bwd_workspace_bytes",
             "jattn_fwd_streams", "jattn_bwd_streams", "jattn_varlen_fwd_workspace_bytes",
             "jattn_varlen_bwd_workspace_bytes", "jattn_fwd_varlen", "jattn_bwd_varlen", "jattn_fwd_window",
             "jattn_bwd_window", "jattn_adaln_qkv_fwd_workspace_bytes", "jattn_adaln_qkv_bwd_workspace_bytes",
@@ -56,6 +56,10 @@ def load() -> ctypes.CDLL:
         lib = ctypes.CDLL(LIB_PATH)
         lib.jattn_fwd.restype = I
         lib.jattn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, F, P, P, P, ctypes.c_size_t, P]
+        lib.jattn_fwd_noalloc.restype = I
+        lib.jattn_fwd_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, F, F, P, P, P]
+        lib.jattn_fwd_noalloc_max_scratch_bytes.restype = ctypes.c_size_t
+        lib.jattn_fwd_noalloc_max_scratch_bytes.argtypes = []
         lib.jattn_fwd_ex.restype = I
         lib.jattn_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, F, P, P, P, ctypes.c_size_t, P, I, P]
         lib.jattn_fwd_workspace_bytes.restype = ctypes.c_size_t

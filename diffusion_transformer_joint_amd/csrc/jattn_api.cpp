@@ -6,6 +6,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "jattn_launch.h"
 
@@ -292,6 +293,67 @@ jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float*
                        hipStream_t stream) {
   return jattn_fwd_ex(q, k, v, gains, valid_len, B, L, H, D, softmax_scale, eps, out, lse, workspace,
                       workspace_bytes, nullptr, 0, stream);
+}
+
+}  // extern "C"
+
+// Device-resident scratch of jattn_fwd_noalloc: the normalised key rows of the last call on each GPU.
+// Each device holds its own copy for the life of the process; host code reaches it only through the
+// per-device address that hipGetSymbolAddress returns (the array's name is a host-side stand-in).
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint16_t scratch[kNoallocScratchBytes / sizeof(uint16_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The address of this device's scratch array, looked up once per device with that device current.
+hipError_t scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return *ptr ? hipSuccess : hipErrorInvalidSymbol;
+}
+}  // namespace
+
+extern "C" {
+
+size_t jattn_fwd_noalloc_max_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+jattn_status jattn_fwd_noalloc(const void* q, const void* k, const void* v, const float* gains,
+                               const int32_t* valid_len, int B, int L, int H, int D, float softmax_scale,
+                               float eps, void* out, float* lse, hipStream_t stream) {
+  // every check before the first HIP call, as for jattn_fwd
+  if (!q || !k || !v || !gains || !out || !lse) return JATTN_ERROR_INVALID_VALUE;
+  const jattn_status st = check_sizes(B, L, H, D);
+  if (st != JATTN_SUCCESS) return st;
+  if (!std::isfinite(softmax_scale) || !std::isfinite(eps) || eps < 0.f) return JATTN_ERROR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(gains, 4) ||
+      !aligned(lse, 4) || !aligned(valid_len, 4))
+    return JATTN_ERROR_INVALID_VALUE;
+  if (jattn_fwd_workspace_bytes(B, L, H, D) > kNoallocScratchBytes) return JATTN_ERROR_WORKSPACE;
+  const size_t tb = (size_t)B * L * H * D * 2, lb = (size_t)B * H * L * 4;
+  const Range ins[] = {{q, tb}, {k, tb}, {v, tb}, {gains, (size_t)2 * D * 4}, {valid_len, (size_t)B * 4}};
+  const Range outs[] = {{out, tb}, {lse, lb}};
+  if (!outputs_disjoint(outs, 2, ins, 5)) return JATTN_ERROR_INVALID_VALUE;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return JATTN_ERROR_HIP;
+  const void* const qp[2] = {q, nullptr};
+  const void* const kp[2] = {k, nullptr};
+  const void* const vp[2] = {v, nullptr};
+  void* const op[2] = {out, nullptr};
+  return run_fwd(jattn::kJoint, qp, kp, vp, gains, valid_len, nullptr, B * L, B, L, L, H, D, softmax_scale, eps, op,
+                 lse, ws, nullptr, 0, stream);
 }
 
 jattn_status jattn_bwd(const void* q, const void* k, const void* v, const float* gains,

@@ -26,7 +26,8 @@
  *  - Inputs are read only. Outputs are fully overwritten (including zeros for dk and dv at padded
  *    keys); dgains is overwritten, not accumulated.
  *  - Work is enqueued asynchronously on `stream` (NULL = the null stream). The library never
- *    allocates, frees, synchronises or prints, and keeps no mutable global state.
+ *    allocates, frees, synchronises or prints. Its only mutable global state is the device-resident
+ *    scratch array of jattn_fwd_noalloc (one per GPU, with its address looked up once per device).
  *  - Arguments are validated on the host before any HIP call. Device-side data (valid_len values,
  *    tensor contents) is not validated: valid_len values are clamped to [0, L]; NaN inputs propagate.
  *  - Supported head dims: every multiple of 8 from 32 to 128. Sizes must satisfy L*H*D < 2^31 and
@@ -52,6 +53,15 @@ typedef enum {
     JATTN_ERROR_HIP = 4            /* a kernel launch failed (hipGetLastError)                 */
 } jattn_status;
 
+/* Relation to the boundary first specified for this library (jattn_fwd(q, k, v, gains, valid_len, B, L, H,
+ * D, softmax_scale, eps, out, lse, stream) and jattn_bwd(..., workspace, workspace_bytes, stream)): the
+ * forward takes a caller workspace, because its keys are RMS-normalised once into device memory
+ * before the attention kernel streams them and the library never allocates; the backward takes the
+ * forward's workspace as an optional extra argument, to reuse those normalised keys instead of
+ * computing them again (NULL: the backward normalises them itself, as the first specification has
+ * it). A caller written to that first forward prototype, and any caller that cannot provide device
+ * memory, uses jattn_fwd_noalloc below, which has exactly that parameter list. */
+
 /* Bytes of device workspace jattn_fwd needs for these sizes: the RMS-normalised K rows
  * (B*L*H*D bf16, rounded up to 256 bytes). Returns 0 for invalid or unsupported sizes. */
 size_t jattn_fwd_workspace_bytes(int B, int L, int H, int D);
@@ -70,6 +80,23 @@ jattn_status jattn_fwd(const void* q, const void* k, const void* v, const float*
                        const int32_t* valid_len, int B, int L, int H, int D,
                        float softmax_scale, float eps, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* jattn_fwd for callers that cannot allocate or pass device memory (code under HIP graph capture,
+ * serving loops, harnesses that forbid allocation): the same arguments and results as jattn_fwd
+ * without the workspace. The normalised K rows go to a fixed device-resident scratch array of
+ * jattn_fwd_noalloc_max_scratch_bytes() bytes (64 MiB) that the library holds on every GPU it runs
+ * on until the process ends; the call allocates nothing. B*L*H*D*2 bytes (rounded up to 256) must
+ * fit in it, else JATTN_ERROR_WORKSPACE (checked on the host before any HIP call). All calls on one
+ * GPU share that GPU's array: two calls whose executions overlap on the same GPU (other streams,
+ * other threads) race and give undefined results; calls ordered on one stream are fine. The
+ * backward of such a call is jattn_bwd with fwd_workspace = NULL. Errors as jattn_fwd; a failure to
+ * find the scratch array -> JATTN_ERROR_HIP. */
+jattn_status jattn_fwd_noalloc(const void* q, const void* k, const void* v, const float* gains,
+                               const int32_t* valid_len, int B, int L, int H, int D,
+                               float softmax_scale, float eps, void* out, float* lse, hipStream_t stream);
+
+/* Size in bytes of the scratch array of jattn_fwd_noalloc. */
+size_t jattn_fwd_noalloc_max_scratch_bytes(void);
 
 /* Number of kernels jattn_fwd enqueues, in order: 0 = K-row RMS normalisation (into the
  * workspace), 1 = the attention forward. */

@@ -368,3 +368,39 @@ def test_window_entry_points_reject(lib):
 ])
 def test_probe_rejects_invalid_arguments(lib, which, blocks, iters, out):
     assert lib.jattn_probe_saturate(which, blocks, iters, ctypes.c_float(1.0), out, None) == _lib.INVALID_VALUE
+
+
+def fwd_noalloc(lib, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gains=fake(3), valid_len=None, B=2, L=100, H=3, D=64,
+             scale=0.125, eps=1e-6, out=fake(4), lse=fake(5), stream=None)
+    a.update(kw)
+    return lib.jattn_fwd_noalloc(a["q"], a["k"], a["v"], a["gains"], a["valid_len"], a["B"], a["L"], a["H"], a["D"],
+                                 ctypes.c_float(a["scale"]), ctypes.c_float(a["eps"]), a["out"], a["lse"], a["stream"])
+
+
+def test_noalloc_scratch_size(lib):
+    assert lib.jattn_fwd_noalloc_max_scratch_bytes() == 64 << 20
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), _lib.INVALID_VALUE),
+    (dict(lse=None), _lib.INVALID_VALUE),
+    (dict(D=44), _lib.NOT_SUPPORTED),
+    (dict(eps=-1.0), _lib.INVALID_VALUE),
+    (dict(out=fake(1)), _lib.INVALID_VALUE),        # out aliases k
+    (dict(q=fake(0) + 8), _lib.INVALID_VALUE),      # misaligned
+    # normalised keys (B L H D bf16) one 256-byte chunk past the 64 MiB scratch array; tensors that
+    # big at fake addresses 2^32 apart, so only the scratch limit can refuse the call
+    (dict(B=1, L=(64 << 20) // (16 * 64 * 2) + 1, H=16, D=64, q=1 << 32, k=2 << 32, v=3 << 32, gains=4 << 32,
+          out=5 << 32, lse=6 << 32), _lib.WORKSPACE),
+])
+def test_noalloc_validation(lib, kw, expect):
+    assert fwd_noalloc(lib, **kw) == expect
+
+
+def test_noalloc_largest_accepted_size_is_the_scratch(lib):
+    # exactly 64 MiB of normalised keys passes the size check: the call is then refused by the next
+    # check (out aliasing q), still before any HIP call
+    L = (64 << 20) // (16 * 64 * 2)
+    assert fwd_noalloc(lib, B=1, L=L, H=16, D=64, q=1 << 32, k=2 << 32, v=3 << 32, gains=4 << 32, out=1 << 32,
+                       lse=6 << 32) == _lib.INVALID_VALUE
