@@ -72,6 +72,10 @@ def parse():
     ap.add_argument("--calibrate-busy", action="store_true",
                     help="first run the library's saturating MFMA and FMA probe kernels (about 1 ms each): "
                          "under rocprofv3 --pmc their busy-counter readings are the full-scale values")
+    ap.add_argument("--probe-dq-accumulation", action="store_true",
+                    help="instead of the step: time the memory traffic a key-parallel backward would need to "
+                         "accumulate dQ across key blocks (fp32 atomics, or partial sums and their reduction; "
+                         "include/jattn_diag.h) at the workload's shape, beside the dq kernel it would replace")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 512 MiB device-to-device three times: under rocprofv3 --pmc its "
                          "FETCH_SIZE / WRITE_SIZE give the counters' scale for a known byte count")
@@ -133,6 +137,8 @@ def main():
 
     if args.calibrate_busy:
         run_busy_probes(torch)
+    if args.probe_dq_accumulation:
+        return probe_dq_accumulation(args, torch)
     if args.variant == "adaln":
         return bench_adaln(args, torch)
     if args.variant == "mlp":
@@ -447,6 +453,58 @@ def preroll(torch, stream, step, new_event, window=10, tol=0.02, min_windows=5, 
     return {"preroll_steps": window * len(times), "preroll_ms": round(sum(times), 3),
             "last_windows_ms_per_step": [round(t / window, 5) for t in last],
             "converged": len(last) == 3 and max(last) - min(last) <= tol * min(last)}
+
+
+def probe_dq_accumulation(args, torch):
+    """Times the dQ accumulation a fused key-parallel backward would need (no attention arithmetic), for
+    key blocks of 128, 256 and 384 keys; the dq kernel that recomputes dQ instead is timed by the
+    ordinary run of the same workload. Prints one JSON line."""
+    from diffusion_transformer_joint_amd import _lib
+    from diffusion_transformer_joint_amd.inputs import WORKLOADS
+    w = WORKLOADS[args.workload]
+    pairs, L, D = w.B * w.H, w.L, w.D
+    lib = _lib.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    n = pairs * L * D
+    res = {"what": "dQ accumulation across key blocks of a key-parallel backward, memory traffic only",
+           "workload": args.workload, "pairs": pairs, "L": L, "D": D, "modes": []}
+    for nkb_rows in (128, 256, 384):
+        nkb = (L + nkb_rows - 1) // nkb_rows
+        buf = torch.zeros((nkb + 1) * n, dtype=torch.float32, device=dev)
+
+        def run(mode):
+            _lib.check("jattn_probe_dq_accumulation",
+                       lib.jattn_probe_dq_accumulation(mode, pairs, L, D, nkb, buf.data_ptr(), buf.numel() * 4, sp))
+
+        for mode, name in ((0, "atomic"), (1, "partial_store"), (2, "partial_reduce")):
+            times = []
+            for rep in range(6):
+                if mode == 0:
+                    buf[:n].zero_()
+                a, b = new_event(), new_event()
+                a.record(stream)
+                run(mode)
+                b.record(stream)
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b))
+            ent = {"mode": name, "key_block_rows": nkb_rows, "key_blocks": nkb, "ms": round(min(times), 5)}
+            if mode == 0:
+                ok = bool(torch.all(buf[:n] == float(nkb)).item())
+                ent.update({"g_atomics_per_s": round(nkb * n / (min(times) * 1e-3) / 1e9, 1), "sums_exact": ok})
+            else:
+                moved = (nkb * n if mode == 1 else (nkb + 1) * n) * 4
+                ent["gbs"] = round(moved / (min(times) * 1e-3) / 1e9, 1)
+            res["modes"].append(ent)
+        del buf
+    print(json.dumps(res), flush=True)
 
 
 def run_busy_probes(torch):

@@ -30,6 +30,26 @@ extern "C" {
  * null or misaligned out; HIP if the launch fails. */
 jattn_status jattn_probe_saturate(int which, int blocks, int iters, float seed, float* out, hipStream_t stream);
 
+/* The memory traffic a key-parallel backward would need to accumulate dQ across key blocks, without
+ * any of the attention arithmetic: `pairs` (batch, head) pairs of L query rows and D columns (D a
+ * multiple of 4, at most 128), `nkb` key blocks per pair, each block contributing one fp32 value per
+ * (query row, column), in 64-row query tiles.
+ *   JATTN_PROBE_DQ_ATOMIC   pairs * nkb workgroups add their values into acc[pairs][L][D] with
+ *                           hardware fp32 atomic adds (acc must start at zero for a meaningful sum);
+ *   JATTN_PROBE_DQ_PARTIAL  the same workgroups store their values to acc[nkb][pairs][L][D];
+ *   JATTN_PROBE_DQ_REDUCE   sums acc[nkb][pairs][L][D] over the key blocks into
+ *                           acc[nkb * pairs * L * D ...] (the pass that finishes the partial scheme).
+ * Every value added or stored is 1.0, so after ATOMIC each element of acc equals nkb.
+ *   acc, acc_bytes  device fp32 buffer and its size: at least pairs*L*D*4 bytes (ATOMIC),
+ *                   nkb*pairs*L*D*4 (PARTIAL), (nkb + 1)*pairs*L*D*4 (REDUCE); 16-byte aligned.
+ * Errors: INVALID_VALUE for an unknown mode, sizes < 1, D not a multiple of 4 or > 128, nkb > 64,
+ * element counts >= 2^31, or a null, misaligned or too small acc; HIP if the launch fails. */
+#define JATTN_PROBE_DQ_ATOMIC 0
+#define JATTN_PROBE_DQ_PARTIAL 1
+#define JATTN_PROBE_DQ_REDUCE 2
+jattn_status jattn_probe_dq_accumulation(int mode, int pairs, int L, int D, int nkb, float* acc, size_t acc_bytes,
+                                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

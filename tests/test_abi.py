@@ -404,3 +404,25 @@ def test_noalloc_largest_accepted_size_is_the_scratch(lib):
     L = (64 << 20) // (16 * 64 * 2)
     assert fwd_noalloc(lib, B=1, L=L, H=16, D=64, q=1 << 32, k=2 << 32, v=3 << 32, gains=4 << 32, out=1 << 32,
                        lse=6 << 32) == _lib.INVALID_VALUE
+
+
+@pytest.mark.parametrize("args", [
+    (3, 192, 1101, 64, 9),      # unknown mode
+    (0, 0, 1101, 64, 9),        # no pairs
+    (0, 192, 1101, 66, 9),      # D not a multiple of 4
+    (0, 192, 1101, 132, 9),     # D past 128
+    (0, 192, 1101, 64, 65),     # too many key blocks
+    (1, 4096, 4096, 128, 9),    # element count past 2^31
+])
+def test_probe_dq_accumulation_validation(lib, args):
+    mode, pairs, L, D, nkb = args
+    assert lib.jattn_probe_dq_accumulation(mode, pairs, L, D, nkb, fake(0), 1 << 40, None) == _lib.INVALID_VALUE
+
+
+def test_probe_dq_accumulation_buffer_size(lib):
+    pairs, L, D, nkb = 2, 100, 64, 3
+    n = pairs * L * D * 4
+    for mode, need in ((0, n), (1, nkb * n), (2, (nkb + 1) * n)):
+        assert lib.jattn_probe_dq_accumulation(mode, pairs, L, D, nkb, fake(0), need - 4, None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_dq_accumulation(0, pairs, L, D, nkb, None, n, None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_dq_accumulation(0, pairs, L, D, nkb, fake(0) + 4, n, None) == _lib.INVALID_VALUE
