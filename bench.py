@@ -87,7 +87,8 @@ COPY_BYTES = 512 << 20
 
 # Device sources (kernels, their launchers and device headers) behind each entry-point family.
 KERNEL_SOURCES = {
-    "attention": ("jattn_device.h", "jattn_launch.h", "jattn_prenorm.hip", "jattn_fwd.hip", "jattn_bwd.hip"),
+    "attention": ("jattn_device.h", "jattn_launch.h", "jattn_prenorm.hip", "jattn_fwd.hip", "jattn_bwd.hip",
+                  "jattn_bwd_kernels.h", "jattn_bwd_wide.hip"),
     "projection": ("jattn_device.h", "adaln_launch.h", "adaln_qkv.hip"),
 }
 

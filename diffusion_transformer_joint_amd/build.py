@@ -17,8 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libjattn.so")
 
-SOURCES = ["jattn_prenorm.hip", "jattn_fwd.hip", "jattn_bwd.hip", "jattn_api.cpp", "adaln_qkv.hip", "adaln_api.cpp",
-           "mlp_api.cpp", "jattn_diag.hip"]
+SOURCES = ["jattn_prenorm.hip", "jattn_fwd.hip", "jattn_bwd.hip", "jattn_bwd_wide.hip", "jattn_api.cpp",
+           "adaln_qkv.hip", "adaln_api.cpp", "mlp_api.cpp", "jattn_diag.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the code objects (the backend would otherwise form
@@ -26,9 +26,10 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # The attention kernels keep their MFMA accumulators in VGPRs: the score tiles feed VALU work right
 # away, and the AGPR form costs two copies per element plus a hazard wait. The projection GEMMs hold
-# 256 accumulators per lane and need the AGPRs.
+# 256 accumulators per lane and need the AGPRs, and so do the backward kernels of head dims above 72
+# (one wave per SIMD, 128 dK/dV accumulator floats per lane at D = 128).
 VGPR_ACC = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-AGPR_ACC_SOURCES = {"adaln_qkv.hip"}
+AGPR_ACC_SOURCES = {"adaln_qkv.hip", "jattn_bwd_wide.hip"}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
                 f"-I{INCLUDE}", f"-I{CSRC}"]
 

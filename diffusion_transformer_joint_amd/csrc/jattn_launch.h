@@ -99,7 +99,12 @@ struct BwdArgs {
 // register budget allows it; 4 waves of 32 queries otherwise.
 // The compiled head dims: every multiple of 8 from 32 to 128. X(D) is expanded once per head dim
 // (used for the switch statements that pick a kernel instantiation).
-#define JATTN_FOR_EACH_HEAD_DIM(X) X(32) X(40) X(48) X(56) X(64) X(72) X(80) X(88) X(96) X(104) X(112) X(120) X(128)
+#define JATTN_FOR_EACH_HEAD_DIM(X) JATTN_FOR_EACH_NARROW_HEAD_DIM(X) JATTN_FOR_EACH_WIDE_HEAD_DIM(X)
+// The backward splits them at kNarrowMaxD: two waves per SIMD up to it (jattn_bwd.hip), one above
+// (jattn_bwd_wide.hip, compiled with MFMA accumulators in AGPRs).
+#define JATTN_FOR_EACH_NARROW_HEAD_DIM(X) X(32) X(40) X(48) X(56) X(64) X(72)
+#define JATTN_FOR_EACH_WIDE_HEAD_DIM(X) X(80) X(88) X(96) X(104) X(112) X(120) X(128)
+constexpr int kNarrowMaxD = 72;
 
 constexpr int fwd_rows_per_block(int D) { return D <= 64 ? 256 : 128; }
 // Backward: both kernels use workgroups of kBwdWaves waves of 32 rows.
@@ -128,5 +133,8 @@ hipError_t launch_fwd(int D, Variant var, const FwdArgs& a, const hipEvent_t* ev
 // it); if n_events > 0, records events[i] after stage i (i < n_events).
 hipError_t launch_bwd(int D, Variant var, const BwdArgs& a, bool prenorm, const hipEvent_t* events,
                       int n_events, hipStream_t stream);
+// launch_bwd for D > kNarrowMaxD (defined in jattn_bwd_wide.hip).
+hipError_t launch_bwd_wide(int D, Variant var, const BwdArgs& a, bool prenorm, const hipEvent_t* events,
+                           int n_events, hipStream_t stream);
 
 }  // namespace jattn
