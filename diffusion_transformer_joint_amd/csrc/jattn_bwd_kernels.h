@@ -181,12 +181,13 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
     s[h] = cs;
     dp[h] = cp;
     if constexpr (MASKED && W) {
-      // keys key0 + c with c = h*32 + (i>>2)*8 + 4g + (i&3) are allowed for c in [clo, chi)
-      const int clo = qrow - wl - key0, chi = min(n, qrow + wr + 1) - key0;
+      // keys key0 + c with c = h*32 + (i>>2)*8 + 4g + (i&3) are allowed for c in [clo, clo + span),
+      // tested as one unsigned compare per element
+      const int clo = qrow - wl - key0, span = max(min(n, qrow + wr + 1) - key0 - clo, 0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int c = h * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        s[h][i] = ((c >= clo) & (c < chi)) ? s[h][i] : -INFINITY;
+        s[h][i] = (uint32_t)(c - clo) < (uint32_t)span ? s[h][i] : -INFINITY;
       }
     } else if constexpr (MASKED) {
 #pragma unroll
@@ -439,9 +440,11 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const _
     for (int i = 0; i < 16; ++i) {
       p[i] = fast_exp2(s[h][i]);
       if constexpr (KMASK) p[i] = kvalid ? p[i] : 0.f;
-      if constexpr (WM) {  // queries q0 + c with c in [key - wr - q0, key + wl - q0] see this key
+      if constexpr (WM) {
+        // queries q0 + c with c in [key - wr - q0, key + wl - q0] see this key, i.e. 0 <= c + wr + q0 - key
+        // <= wl + wr, tested as one unsigned compare per element against a lane offset
         const int c = h * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        p[i] = ((c >= key - wr - q0) & (c <= key + wl - q0)) ? p[i] : 0.f;
+        p[i] = (uint32_t)(c + wr + q0 - key) <= (uint32_t)(wl + wr) ? p[i] : 0.f;
       }
       ds[i] = p[i] * dp[h][i];
     }
@@ -561,9 +564,11 @@ __device__ __forceinline__ void dkdv_tile_staged(const __bf16* __restrict__ qt, 
     for (int i = 0; i < 16; ++i) {
       p[i] = fast_exp2(s[h][i]);
       if constexpr (KMASK) p[i] = kvalid ? p[i] : 0.f;
-      if constexpr (WM) {  // queries q0 + c with c in [key - wr - q0, key + wl - q0] see this key
+      if constexpr (WM) {
+        // queries q0 + c with c in [key - wr - q0, key + wl - q0] see this key, i.e. 0 <= c + wr + q0 - key
+        // <= wl + wr, tested as one unsigned compare per element against a lane offset
         const int c = h * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        p[i] = ((c >= key - wr - q0) & (c <= key + wl - q0)) ? p[i] : 0.f;
+        p[i] = (uint32_t)(c + wr + q0 - key) <= (uint32_t)(wl + wr) ? p[i] : 0.f;
       }
       ds[i] = p[i] * dp[h][i];
     }
@@ -719,7 +724,12 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, const Ro
 template <int D, bool S, bool V, bool W>
 __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, int blk, int item) {
   using Dm = Dims<D>;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
+  // (windowed form: the thread index is made opaque per item, so that the per-lane values derived from
+  // it are formed in each item instead of being hoisted out of the item loop and kept, or spilled,
+  // through it)
+  int tid_ = threadIdx.x;
+  if constexpr (W) asm volatile("" : "+v"(tid_));
+  const int tid = tid_, lane = tid & 63, wave = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int H = a.H;
   const int b = bh / H, h = bh - b * H;
   const SeqGeom<V> seq(a.cu_seqlens, b, a.L, a.total, a.L);

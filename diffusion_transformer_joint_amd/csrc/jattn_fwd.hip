@@ -355,6 +355,10 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
     for (int qt = 0; qt < QT; ++qt) st.mrow[qt] = -INFINITY;
     fwd_loop<D, S, V, W, false>(ring, qf, shift, st, active, lane, tr, qrow, a.wl, a.wr);
   }
+  // (the output addresses are formed after the loop rather than kept from the prologue: at D = 64 the
+  // windowed loop has no registers to spare for them)
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) asm volatile("" : "+v"(qrow[qt]));
 
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
