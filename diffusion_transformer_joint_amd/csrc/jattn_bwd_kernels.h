@@ -149,14 +149,51 @@ __device__ __forceinline__ void rmsnorm_backward_row(f32x16 (&dxn)[Dims<D>::MT],
     }
 }
 
+// Scheduling pattern for code emitted just before it: N groups of one MFMA followed by V VALU
+// instructions, so that a stage's MFMAs issue under another stage's independent VALU work (one wave per
+// SIMD has no second wave to fill the MFMA pipe while it runs its softmax).
+template <int N, int V>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // then V VALU instructions
+  }
+}
+
+// Per-lane LDS byte offsets of a swizzled or padded tile's row fragments (row l32, k-step ks) and
+// transposed fragments (column block mt, rows r and r + 8), computed once: rows 32 and 16 further on
+// share the swizzle, so both halves and both 16-row steps are immediate offsets.
+template <int D>
+struct LaneOffs {
+  uint32_t row[Dims<D>::KS];
+  uint32_t tr[Dims<D>::MT][2];
+  template <class LY>
+  __device__ void init(int lane) {
+    const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < Dims<D>::KS; ++ks) row[ks] = 2u * (uint32_t)LY::off(l32, ks * 16 + g * 8);
+    const int r = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int c = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+#pragma unroll
+    for (int mt = 0; mt < Dims<D>::MT; ++mt) {
+      tr[mt][0] = 2u * (uint32_t)LY::off(r, mt * 32 + c);
+      tr[mt][1] = 2u * (uint32_t)LY::off(r + 8, mt * 32 + c);
+    }
+  }
+};
+
 // ------------------------------------------------------------------------------------------------
 // dq kernel: query-parallel
 
 // One 64-key tile: for both 32-key halves S'^T = Kr Q'^T and dP^T - Delta = V dO^T (lane = query),
 // dS^T = P * (dP - Delta) with P = exp2(S' - lse2), then dQn^T += Kr^T dS^T. MASKED: keys at or
 // past n are seeded with -inf (P = 0).
-// The halves run one after the other (issuing the second half's row reads under the first half's
-// products measured no faster).
+// At two waves per SIMD the halves run one after the other (issuing the second half's row reads under
+// the first half's products measured no faster). At one wave per SIMD (D > 72) the tile runs in
+// stages, each LDS read a stage ahead of its use and the MFMAs of one stage under the VALU work of
+// another: rows(0) | scores(0) | transposed Kr of half 0, rows(1) | softmax(0) with scores(1) |
+// softmax(1) with dQ(0) | transposed Kr of half 1 | dQ(1). (B4 L2381 H24 D128: 611 -> 600 us.)
 // W (local window): masked tiles also seed -inf outside the lane's query window qrow - wl .. qrow + wr.
 template <int D, bool MASKED, bool W = false>
 __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __bf16* __restrict__ vt,
@@ -214,14 +251,58 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
       acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32 + 16, mt * 32, lane), f[h][1], acc[mt]);
     }
   };
-  rows(0);
-  scores(0);
-  softmax(0);
-  accumulate(0);
-  rows(1);
-  scores(1);
-  softmax(1);
-  accumulate(1);
+  if constexpr (bwd_waves_per_eu<D>() == 1) {
+    LaneOffs<D> lo;
+    lo.template init<LK>(lane);
+    bf16x8 tk[MT][2];
+    const char* kb = reinterpret_cast<const char*>(kt);
+    auto trload = [&](int h) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int r0 = h * 32 + r * 16;
+          const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JATTN_LDS i16x4*)(kb + lo.tr[mt][0] + r0 * LK::PITCH * 2));
+          const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JATTN_LDS i16x4*)(kb + lo.tr[mt][1] + r0 * LK::PITCH * 2));
+          tk[mt][r] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, x), __builtin_bit_cast(bf16x4, y), 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    auto accumulate2 = [&](int h) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt] = mfma(tk[mt][0], f[h][0], acc[mt]);
+        acc[mt] = mfma(tk[mt][1], f[h][1], acc[mt]);
+      }
+    };
+    rows(0);
+    __builtin_amdgcn_sched_barrier(0);
+    scores(0);
+    __builtin_amdgcn_sched_barrier(0);
+    trload(0);
+    rows(1);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(0);
+    scores(1);
+    interleave_mfma_valu<2 * KS, 3>();
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(1);
+    accumulate2(0);
+    interleave_mfma_valu<2 * MT, 3>();
+    __builtin_amdgcn_sched_barrier(0);
+    trload(1);
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate2(1);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    rows(0);
+    scores(0);
+    softmax(0);
+    accumulate(0);
+    rows(1);
+    scores(1);
+    softmax(1);
+    accumulate(1);
+  }
 }
 
 // One work item of the dq kernel: query rows [128 blk, 128 blk + 128) of (sequence, head) pair bh.
@@ -473,33 +554,16 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* __restrict__ qt, const _
 }
 
 // The dk/dv tile for the instantiations that run one wave per SIMD (D > 72): the same arithmetic as
-// dkdv_tile with an explicit issue order, every LDS read a stage ahead of its use:
-//   statistics and rows of half 0 | scores(0) | transposed fragments of half 0, rows of half 1 |
-//   probabilities(0), statistics of half 1 | accumulate(0) | scores(1) | transposed fragments of half 1 |
-//   probabilities(1) | accumulate(1)
+// dkdv_tile with an explicit issue order, every LDS read a stage ahead of its use and the MFMAs of one
+// stage under the VALU work of another:
+//   statistics and rows of half 0 | scores(0) | transposed fragments of half 0, rows and statistics of
+//   half 1 | probabilities(0) with scores(1) | probabilities(1) with accumulate(0) | transposed
+//   fragments of half 1 | accumulate(1)
 // With no second wave on the SIMD to run while one waits, the default schedule (each MFMA waits for
-// the LDS read issued just before it) leaves the read latency exposed. (With two waves per SIMD the
-// explicit order measured no faster and needs more registers, so those instantiations keep dkdv_tile.)
-// LDS addresses are lane offsets computed once per item (LaneOffs): rows 32 and 16 further on share
-// the swizzle, so both halves and both 16-row steps are immediate offsets.
-template <int D>
-struct LaneOffs {
-  uint32_t row[Dims<D>::KS];
-  uint32_t tr[Dims<D>::MT][2];
-  template <class LY>
-  __device__ void init(int lane) {
-    const int g = lane >> 5, l32 = lane & 31;
-#pragma unroll
-    for (int ks = 0; ks < Dims<D>::KS; ++ks) row[ks] = 2u * (uint32_t)LY::off(l32, ks * 16 + g * 8);
-    const int r = 4 * (lane >> 5) + ((lane & 15) >> 2);
-    const int c = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-#pragma unroll
-    for (int mt = 0; mt < Dims<D>::MT; ++mt) {
-      tr[mt][0] = 2u * (uint32_t)LY::off(r, mt * 32 + c);
-      tr[mt][1] = 2u * (uint32_t)LY::off(r + 8, mt * 32 + c);
-    }
-  }
-};
+// the LDS read issued just before it, and the MFMA pipe idles through the softmax) leaves both
+// exposed: at B4 L2381 H24 D128 the plain staged order took dk/dv 824 -> 749 us, the interleave
+// 721 -> 688 us. (With two waves per SIMD the explicit order measured no faster and needs more
+// registers, so those instantiations keep dkdv_tile.) LDS addresses come from LaneOffs.
 
 template <int D, bool KMASK, bool WM = false>
 __device__ __forceinline__ void dkdv_tile_staged(const __bf16* __restrict__ qt, const __bf16* __restrict__ ot,
@@ -513,7 +577,7 @@ __device__ __forceinline__ void dkdv_tile_staged(const __bf16* __restrict__ qt, 
   static_assert(std::is_same<LQ, typename DkdvCfg<D>::LO>::value, "Qs and dO tiles share one layout");
   constexpr int KS = Dm::KS, MT = Dm::MT;
   const int g = lane >> 5;
-  bf16x8 qr[2][KS], orr[2][KS], pf[2], df[2], tq[MT][2], to[MT][2];
+  bf16x8 qr[2][KS], orr[2][KS], pf[2][2], df[2][2], tq[MT][2], to[MT][2];
   f32x16 s[2], dp[2];
   const char* qb = reinterpret_cast<const char*>(qt);
   const char* ob = reinterpret_cast<const char*>(ot);
@@ -572,18 +636,18 @@ __device__ __forceinline__ void dkdv_tile_staged(const __bf16* __restrict__ qt, 
       }
       ds[i] = p[i] * dp[h][i];
     }
-    pf[0] = to_bf16x8(p);
-    pf[1] = to_bf16x8(p + 8);
-    df[0] = to_bf16x8(ds);
-    df[1] = to_bf16x8(ds + 8);
+    pf[h][0] = to_bf16x8(p);
+    pf[h][1] = to_bf16x8(p + 8);
+    df[h][0] = to_bf16x8(ds);
+    df[h][1] = to_bf16x8(ds + 8);
   };
-  auto accumulate = [&]() {
+  auto accumulate = [&](int h) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      dva[mt] = mfma(to[mt][0], pf[0], dva[mt]);
-      dva[mt] = mfma(to[mt][1], pf[1], dva[mt]);
-      dka[mt] = mfma(tq[mt][0], df[0], dka[mt]);
-      dka[mt] = mfma(tq[mt][1], df[1], dka[mt]);
+      dva[mt] = mfma(to[mt][0], pf[h][0], dva[mt]);
+      dva[mt] = mfma(to[mt][1], pf[h][1], dva[mt]);
+      dka[mt] = mfma(tq[mt][0], df[h][0], dka[mt]);
+      dka[mt] = mfma(tq[mt][1], df[h][1], dka[mt]);
     }
   };
   // (sched_barrier(0) keeps each stage's instructions in place: left alone, the scheduler sinks the
@@ -595,19 +659,19 @@ __device__ __forceinline__ void dkdv_tile_staged(const __bf16* __restrict__ qt, 
   __builtin_amdgcn_sched_barrier(0);
   trload(0);
   rows(1);
-  __builtin_amdgcn_sched_barrier(0);
-  probs(0);
   seeds(1);
   __builtin_amdgcn_sched_barrier(0);
-  accumulate();
-  __builtin_amdgcn_sched_barrier(0);
+  probs(0);
   scores(1);
+  interleave_mfma_valu<2 * KS, 3>();
+  __builtin_amdgcn_sched_barrier(0);
+  probs(1);
+  accumulate(0);
+  interleave_mfma_valu<4 * MT, 3>();
   __builtin_amdgcn_sched_barrier(0);
   trload(1);
   __builtin_amdgcn_sched_barrier(0);
-  probs(1);
-  __builtin_amdgcn_sched_barrier(0);
-  accumulate();
+  accumulate(1);
   __builtin_amdgcn_sched_barrier(0);
 }
 
