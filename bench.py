@@ -76,6 +76,9 @@ def parse():
                     help="instead of the step: time the memory traffic a key-parallel backward would need to "
                          "accumulate dQ across key blocks (fp32 atomics, or partial sums and their reduction; "
                          "include/jattn_diag.h) at the workload's shape, beside the dq kernel it would replace")
+    ap.add_argument("--probe-tile", action="store_true",
+                    help="time the dk/dv tile's dependency structure (jattn_probe_tile) with its operands in "
+                         "registers or LDS, and the LDS read rates (jattn_probe_lds_read); prints one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 512 MiB device-to-device three times: under rocprofv3 --pmc its "
                          "FETCH_SIZE / WRITE_SIZE give the counters' scale for a known byte count")
@@ -140,6 +143,8 @@ def main():
         run_busy_probes(torch)
     if args.probe_dq_accumulation:
         return probe_dq_accumulation(args, torch)
+    if args.probe_tile:
+        return probe_tile(torch)
     if args.variant == "adaln":
         return bench_adaln(args, torch)
     if args.variant == "mlp":
@@ -505,6 +510,44 @@ def probe_dq_accumulation(args, torch):
                 ent["gbs"] = round(moved / (min(times) * 1e-3) / 1e9, 1)
             res["modes"].append(ent)
         del buf
+    print(json.dumps(res), flush=True)
+
+
+def probe_tile(torch):
+    """The probes of jattn_diag.h that time the dk/dv tile's dependency structure (which operands come from
+    LDS) and the LDS read rates, at one and two waves per SIMD, on the shader clock. Prints one JSON line."""
+    from diffusion_transformer_joint_amd import _lib
+    lib = _lib.load()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sp = torch.cuda.current_stream().cuda_stream
+    modes = ("registers", "lds", "lds_barrier", "rows_stats", "transposed", "stats", "rows", "pipelined")
+    res = {"what": "dk/dv tile dependency structure at D = 64 (32 MFMAs of 32x32x16 per wave and tile) and LDS "
+                   "read rates; shader-clock cycles from s_memtime", "compute_units": cus, "tile": [], "lds_read": []}
+    iters = 2000
+    for wps in (1, 2):
+        blocks = cus * wps
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+        cyc = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda:0")
+        for mode, name in enumerate(modes):
+            for _ in range(2):  # (the first launch warms the clocks)
+                _lib.check("jattn_probe_tile", lib.jattn_probe_tile(mode, blocks, iters, ctypes.c_float(1e-3),
+                                                                    out.data_ptr(), cyc.data_ptr(), sp))
+            torch.cuda.synchronize()
+            c = cyc.double() / iters
+            res["tile"].append({"mode": name, "waves_per_simd": wps, "cycles_per_tile_mean": round(c.mean().item(), 1),
+                                "min": round(c.min().item(), 1), "max": round(c.max().item(), 1),
+                                "mfma_busy": round(1024.0 * wps / c.mean().item(), 3)})
+    for wgs in (1, 2):
+        blocks = cus * wgs
+        cyc = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda:0")
+        for mode, (name, width) in enumerate((("b128", 16), ("b128_broadcast", 16), ("b64_transposed", 8))):
+            for _ in range(2):
+                _lib.check("jattn_probe_lds_read", lib.jattn_probe_lds_read(mode, blocks, 4000, cyc.data_ptr(), sp))
+            torch.cuda.synchronize()
+            c = cyc.double().mean().item()
+            res["lds_read"].append({"read": name, "waves_per_cu": 4 * wgs,
+                                    "bytes_per_cu_per_cycle": round(8 * 4000 * 64 * width * 4 * wgs / c, 1),
+                                    "cycles_per_wave_instruction": round(c / (8 * 4000), 2)})
     print(json.dumps(res), flush=True)
 
 

@@ -1,5 +1,6 @@
-// Saturating probe kernels for reading the full-scale values of the SQ busy counters (measurement
-// support; see jattn_diag.h). Register data only; each thread writes one float.
+// Measurement support (see jattn_diag.h): saturating probe kernels for reading the full-scale values
+// of the SQ busy counters, the dQ-accumulation traffic probe, and probes of the dk/dv tile's
+// dependency structure and of LDS read rates.
 #include "jattn_diag.h"
 #include "jattn_device.h"
 
@@ -80,6 +81,205 @@ __global__ __launch_bounds__(kProbeThreads) void probe_dq_reduce_kernel(size_t n
   }
 }
 
+
+// ------------------------------------------------------------------------------------------------
+// The dk/dv tile's dependency structure at D = 64, without global loads: per 32-query half 8 score
+// MFMAs (S and dP, 4 k-steps each, seeded with the row statistics), then 16 exp2, 16 multiplies and
+// 16 bf16 conversions, then 8 gradient MFMAs fed by transposed fragments; one 64-query tile per
+// iteration. Each operand comes from registers or from an LDS tile laid out like the kernel's (128-byte
+// rows, 16-byte chunks XOR-swizzled by row), as the mode selects. The tiles hold small values, so the
+// arithmetic stays finite; its results only feed the per-thread output.
+constexpr int kTileBytes = 64 * 64 * 2;  // one 64 x 64 bf16 tile
+constexpr int kTileStage = 2 * kTileBytes + 512;  // Qs and dO tiles, then -lse2 and -Delta of 64 rows
+
+template <int MODE>
+__global__ __launch_bounds__(kProbeThreads) void probe_tile_kernel(int iters, float seed, float* __restrict__ out,
+                                                                   uint64_t* __restrict__ cycles) {
+  constexpr bool ROWS = MODE == JATTN_PROBE_TILE_LDS || MODE == JATTN_PROBE_TILE_LDS_BARRIER ||
+                        MODE == JATTN_PROBE_TILE_ROWS_STATS || MODE == JATTN_PROBE_TILE_ROWS ||
+                        MODE == JATTN_PROBE_TILE_PIPELINED;
+  constexpr bool STATS = MODE == JATTN_PROBE_TILE_LDS || MODE == JATTN_PROBE_TILE_LDS_BARRIER ||
+                         MODE == JATTN_PROBE_TILE_ROWS_STATS || MODE == JATTN_PROBE_TILE_STATS ||
+                         MODE == JATTN_PROBE_TILE_PIPELINED;
+  constexpr bool TRANS = MODE == JATTN_PROBE_TILE_LDS || MODE == JATTN_PROBE_TILE_LDS_BARRIER ||
+                         MODE == JATTN_PROBE_TILE_TRANSPOSED || MODE == JATTN_PROBE_TILE_PIPELINED;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kTileStage];
+  const int tid = (int)threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  for (int i = tid; i < 2 * kTileStage / 4; i += kProbeThreads)
+    reinterpret_cast<float*>(smem)[i] = seed * (float)(i & 127) * 1e-3f;
+  __syncthreads();
+  bf16x8 kf[4], vf[4], treg[2][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kf[j][e] = (__bf16)(seed * (float)(lane + e + j));
+      vf[j][e] = (__bf16)(seed * (float)(e - j));
+    }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      treg[m][0][e] = (__bf16)(seed * (float)(e + m));
+      treg[m][1][e] = (__bf16)(seed * (float)(e - m));
+    }
+  f32x16 sreg, dreg, acc[4];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sreg[i] = -seed * (float)i;
+    dreg[i] = 0.5f * seed * (float)i;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
+  auto stage = [&](int u) { return smem + ((u >> 1) & 1) * kTileStage; };  // unit u = half u % 2 of tile u / 2
+  auto row_off = [&](int h, int ks) {  // byte offset of this lane's row fragment (row h*32 + l32, k-step ks)
+    const int row = h * 32 + l32;
+    return row * 128 + (((ks * 2 + g) ^ (row & 7)) << 4);
+  };
+  auto tr_frag = [&](const char* tile, int row0, int mt) {  // transposed fragment: rows row0 .. row0 + 15
+    const int r = row0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int c = mt * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+    const int o0 = r * 128 + ((((c >> 3) ^ (r & 7)) << 4) | ((c & 7) * 2));
+    const int o1 = (r + 8) * 128 + ((((c >> 3) ^ ((r + 8) & 7)) << 4) | ((c & 7) * 2));
+    const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JATTN_LDS i16x4*)(tile + o0));
+    const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JATTN_LDS i16x4*)(tile + o1));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4, x), __builtin_bit_cast(bf16x4, y), 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  f32x16 s[2], dp[2];
+  bf16x8 qr[2][4], orr[2][4];
+  // statistics (seeds) and row fragments of unit u into set b
+  auto read_unit = [&](int u, int b) {
+    const char* base = stage(u);
+    const int h = u & 1;
+    if constexpr (STATS) {
+      const float* st = reinterpret_cast<const float*>(base + 2 * kTileBytes);
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + h * 32 + j4 * 8 + g * 4);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + 64 + h * 32 + j4 * 8 + g * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[b][j4 * 4 + e] = l4[e];
+          dp[b][j4 * 4 + e] = d4[e];
+        }
+      }
+    } else {
+      asm volatile("" : "+v"(sreg));  // (a fresh seed each unit, as the kernel's statistics are)
+      s[b] = sreg;
+      dp[b] = dreg;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if constexpr (ROWS) {
+        qr[b][ks] = *reinterpret_cast<const bf16x8*>(base + row_off(h, ks));
+        orr[b][ks] = *reinterpret_cast<const bf16x8*>(base + kTileBytes + row_off(h, ks));
+      } else {
+        qr[b][ks] = kf[(ks + h + 1) & 3];
+        orr[b][ks] = vf[(ks + h + 2) & 3];
+      }
+    }
+  };
+  auto unit = [&](int u, int b) {  // the products and softmax of unit u from set b
+    const char* base = stage(u);
+    const int h = u & 1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      s[b] = mfma(qr[b][ks], kf[ks], s[b]);
+      dp[b] = mfma(orr[b][ks], vf[ks], dp[b]);
+    }
+    bf16x8 tq[2][2], to[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if constexpr (TRANS) {
+          to[mt][r] = tr_frag(base + kTileBytes, h * 32 + r * 16, mt);
+          tq[mt][r] = tr_frag(base, h * 32 + r * 16, mt);
+        } else {
+          to[mt][r] = treg[mt][r];
+          tq[mt][r] = treg[mt][r ^ 1];
+        }
+      }
+    if constexpr (MODE == JATTN_PROBE_TILE_PIPELINED) {
+      read_unit(u + 1, b ^ 1);  // the next unit's reads go out under this unit's softmax and products
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = fast_exp2(s[b][i]);
+      ds[i] = p[i] * dp[b][i];
+    }
+    const bf16x8 pf[2] = {to_bf16x8(p), to_bf16x8(p + 8)}, df[2] = {to_bf16x8(ds), to_bf16x8(ds + 8)};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      acc[mt] = mfma(to[mt][0], pf[0], acc[mt]);
+      acc[mt] = mfma(to[mt][1], pf[1], acc[mt]);
+      acc[2 + mt] = mfma(tq[mt][0], df[0], acc[2 + mt]);
+      acc[2 + mt] = mfma(tq[mt][1], df[1], acc[2 + mt]);
+    }
+  };
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  if constexpr (MODE == JATTN_PROBE_TILE_PIPELINED) {
+    read_unit(0, 0);
+    for (int it = 0; it < iters; ++it) {
+      unit(2 * it, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      unit(2 * it + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        read_unit(2 * it + h, 0);
+        unit(2 * it + h, 0);
+      }
+      if constexpr (MODE == JATTN_PROBE_TILE_LDS_BARRIER) __syncthreads();
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += acc[j][i];
+  out[(size_t)blockIdx.x * kProbeThreads + tid] = sum;
+  if (lane == 0) cycles[(size_t)blockIdx.x * (kProbeThreads / 64) + (tid >> 6)] = t1 - t0;
+}
+
+// LDS read rate: every wave issues 8 independent reads per iteration and consumes them together.
+template <int MODE>
+__global__ __launch_bounds__(kProbeThreads) void probe_lds_read_kernel(int iters, uint64_t* __restrict__ cycles) {
+  __shared__ __attribute__((aligned(16))) float smem[16384];  // 64 KiB
+  const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < 16384; i += kProbeThreads) smem[i] = (float)(i & 255);
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    const int base = ((it * 7 + w) & 7) * 2048;  // an 8 KiB window (floats)
+    if constexpr (MODE == JATTN_PROBE_LDS_B128 || MODE == JATTN_PROBE_LDS_B128_BROADCAST) {
+      f32x4 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        v[r] = MODE == JATTN_PROBE_LDS_B128 ? *reinterpret_cast<const f32x4*>(smem + base + r * 256 + lane * 4)
+                                            : *reinterpret_cast<const f32x4*>(smem + base + r * 8 + (lane >> 5) * 4);
+      asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+    } else {
+      i16x4 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (JATTN_LDS i16x4*)(reinterpret_cast<char*>(smem) + (base + r * 128) * 4 + lane * 8));
+      asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  if (lane == 0) cycles[(size_t)blockIdx.x * (kProbeThreads / 64) + w] = t1 - t0;
+}
+
 }  // namespace jattn
 
 extern "C" jattn_status jattn_probe_dq_accumulation(int mode, int pairs, int L, int D, int nkb, float* acc,
@@ -113,5 +313,45 @@ extern "C" jattn_status jattn_probe_saturate(int which, int blocks, int iters, f
   else
     hipLaunchKernelGGL(jattn::probe_fma_kernel, dim3(blocks), dim3(jattn::kProbeThreads), 0, stream, iters, seed,
                        out);
+  return hipGetLastError() == hipSuccess ? JATTN_SUCCESS : JATTN_ERROR_HIP;
+}
+
+extern "C" jattn_status jattn_probe_tile(int mode, int blocks, int iters, float seed, float* out, uint64_t* cycles,
+                                         hipStream_t stream) {
+  if (mode < JATTN_PROBE_TILE_REGS || mode > JATTN_PROBE_TILE_PIPELINED || blocks < 1 || iters < 1 ||
+      (int64_t)blocks * jattn::kProbeThreads >= ((int64_t)1 << 31) || out == nullptr || cycles == nullptr ||
+      (reinterpret_cast<uintptr_t>(out) & 3u) != 0 || (reinterpret_cast<uintptr_t>(cycles) & 7u) != 0)
+    return JATTN_ERROR_INVALID_VALUE;
+  switch (mode) {
+#define JATTN_TILE_CASE(M) \
+  case M: hipLaunchKernelGGL(jattn::probe_tile_kernel<M>, dim3(blocks), dim3(jattn::kProbeThreads), 0, stream, iters, \
+                             seed, out, cycles); break;
+    JATTN_TILE_CASE(JATTN_PROBE_TILE_REGS)
+    JATTN_TILE_CASE(JATTN_PROBE_TILE_LDS)
+    JATTN_TILE_CASE(JATTN_PROBE_TILE_LDS_BARRIER)
+    JATTN_TILE_CASE(JATTN_PROBE_TILE_ROWS_STATS)
+    JATTN_TILE_CASE(JATTN_PROBE_TILE_TRANSPOSED)
+    JATTN_TILE_CASE(JATTN_PROBE_TILE_STATS)
+    JATTN_TILE_CASE(JATTN_PROBE_TILE_ROWS)
+    JATTN_TILE_CASE(JATTN_PROBE_TILE_PIPELINED)
+#undef JATTN_TILE_CASE
+  }
+  return hipGetLastError() == hipSuccess ? JATTN_SUCCESS : JATTN_ERROR_HIP;
+}
+
+extern "C" jattn_status jattn_probe_lds_read(int mode, int blocks, int iters, uint64_t* cycles, hipStream_t stream) {
+  if (mode < JATTN_PROBE_LDS_B128 || mode > JATTN_PROBE_LDS_B64_TRANSPOSED || blocks < 1 || iters < 1 ||
+      (int64_t)blocks * jattn::kProbeThreads >= ((int64_t)1 << 31) || cycles == nullptr ||
+      (reinterpret_cast<uintptr_t>(cycles) & 7u) != 0)
+    return JATTN_ERROR_INVALID_VALUE;
+  if (mode == JATTN_PROBE_LDS_B128)
+    hipLaunchKernelGGL(jattn::probe_lds_read_kernel<JATTN_PROBE_LDS_B128>, dim3(blocks), dim3(jattn::kProbeThreads), 0,
+                       stream, iters, cycles);
+  else if (mode == JATTN_PROBE_LDS_B128_BROADCAST)
+    hipLaunchKernelGGL(jattn::probe_lds_read_kernel<JATTN_PROBE_LDS_B128_BROADCAST>, dim3(blocks),
+                       dim3(jattn::kProbeThreads), 0, stream, iters, cycles);
+  else
+    hipLaunchKernelGGL(jattn::probe_lds_read_kernel<JATTN_PROBE_LDS_B64_TRANSPOSED>, dim3(blocks),
+                       dim3(jattn::kProbeThreads), 0, stream, iters, cycles);
   return hipGetLastError() == hipSuccess ? JATTN_SUCCESS : JATTN_ERROR_HIP;
 }

@@ -2,6 +2,9 @@
  * jattn_diag.h -- C ABI of libjattn.so, part 4: measurement support. Not part of the attention or
  * projection math.
  *
+ * Busy-counter calibration, a dQ-accumulation traffic probe, and probes of the dk/dv tile's
+ * dependency structure and of LDS read rates (the tile probes time themselves with the shader clock).
+ *
  * Hardware busy counters (the SQ block's MFMA-busy and VALU-issue cycles) have no documented
  * full-scale value per GPU, clock and counter-aggregation mode. The probe kernels here keep one pipe
  * of every SIMD saturated for a known number of instructions, so a counter run that includes them
@@ -49,6 +52,52 @@ jattn_status jattn_probe_saturate(int which, int blocks, int iters, float seed, 
 #define JATTN_PROBE_DQ_REDUCE 2
 jattn_status jattn_probe_dq_accumulation(int mode, int pairs, int L, int D, int nkb, float* acc, size_t acc_bytes,
                                          hipStream_t stream);
+
+/* The dk/dv tile's dependency structure at D = 64, without global loads: per 32-query half, 8 score
+ * MFMAs (two chains of 4 k-steps, seeded with the rows' statistics), 16 exp2, 16 multiplies and 16
+ * bf16 conversions, then 8 gradient MFMAs fed by transposed fragments; one 64-query tile (two halves)
+ * per iteration, `iters` iterations per wave. `mode` selects which operands are read from LDS tiles
+ * laid out like the kernel's (the rest come from registers):
+ *   JATTN_PROBE_TILE_REGS          none;
+ *   JATTN_PROBE_TILE_LDS           row fragments, statistics and transposed fragments, as in the kernel;
+ *   JATTN_PROBE_TILE_LDS_BARRIER   the same with a workgroup barrier per tile;
+ *   JATTN_PROBE_TILE_ROWS_STATS    row fragments and statistics;
+ *   JATTN_PROBE_TILE_TRANSPOSED    transposed fragments;
+ *   JATTN_PROBE_TILE_STATS         statistics;
+ *   JATTN_PROBE_TILE_ROWS          row fragments;
+ *   JATTN_PROBE_TILE_PIPELINED     as LDS, with the next half's statistics and rows read under the current
+ *                                  half's softmax and gradient products.
+ * `blocks` workgroups of 256 threads (4 waves) run it; blocks = (compute units) x (waves per SIMD).
+ *   out     device fp32 [blocks * 256]: one value per thread (keeps the work live), overwritten;
+ *   cycles  device uint64 [blocks * 4]: each wave's shader-clock cycles (s_memtime) over its loop.
+ * Each iteration holds 32 MFMAs of 32x32x16 per wave: the MFMA pipe's busy fraction is
+ * 1024 * iters * (waves per SIMD) / cycles.
+ * Errors: INVALID_VALUE for an unknown mode, blocks < 1, iters < 1, blocks * 256 >= 2^31, or a null or
+ * misaligned out or cycles; HIP if the launch fails. */
+#define JATTN_PROBE_TILE_REGS 0
+#define JATTN_PROBE_TILE_LDS 1
+#define JATTN_PROBE_TILE_LDS_BARRIER 2
+#define JATTN_PROBE_TILE_ROWS_STATS 3
+#define JATTN_PROBE_TILE_TRANSPOSED 4
+#define JATTN_PROBE_TILE_STATS 5
+#define JATTN_PROBE_TILE_ROWS 6
+#define JATTN_PROBE_TILE_PIPELINED 7
+jattn_status jattn_probe_tile(int mode, int blocks, int iters, float seed, float* out, uint64_t* cycles,
+                              hipStream_t stream);
+
+/* LDS read rate: `blocks` workgroups of 256 threads each issue, per wave and iteration, 8 independent
+ * reads of one kind and consume them together (`iters` iterations):
+ *   JATTN_PROBE_LDS_B128            ds_read_b128, lane l at byte 16 l of a 1 KiB row (no bank conflicts);
+ *   JATTN_PROBE_LDS_B128_BROADCAST  ds_read_b128, all lanes of a half-wave at one address;
+ *   JATTN_PROBE_LDS_B64_TRANSPOSED  ds_read_b64_tr_b16, lane l at byte 8 l of a 512-byte row.
+ *   cycles  device uint64 [blocks * 4]: each wave's shader-clock cycles over its loop.
+ * Bytes returned per compute unit and cycle = 8 * iters * 64 * (16, 16 or 8) * (waves per CU) / cycles.
+ * Errors: INVALID_VALUE for an unknown mode, blocks < 1, iters < 1, blocks * 256 >= 2^31, or a null or
+ * misaligned cycles; HIP if the launch fails. */
+#define JATTN_PROBE_LDS_B128 0
+#define JATTN_PROBE_LDS_B128_BROADCAST 1
+#define JATTN_PROBE_LDS_B64_TRANSPOSED 2
+jattn_status jattn_probe_lds_read(int mode, int blocks, int iters, uint64_t* cycles, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -426,3 +426,30 @@ def test_probe_dq_accumulation_buffer_size(lib):
         assert lib.jattn_probe_dq_accumulation(mode, pairs, L, D, nkb, fake(0), need - 4, None) == _lib.INVALID_VALUE
     assert lib.jattn_probe_dq_accumulation(0, pairs, L, D, nkb, None, n, None) == _lib.INVALID_VALUE
     assert lib.jattn_probe_dq_accumulation(0, pairs, L, D, nkb, fake(0) + 4, n, None) == _lib.INVALID_VALUE
+
+
+@pytest.mark.parametrize("args", [
+    (8, 4, 10),    # unknown mode
+    (-1, 4, 10),
+    (0, 0, 10),    # no workgroups
+    (0, 4, 0),     # no iterations
+    (0, 1 << 23, 10),  # blocks * 256 >= 2^31
+])
+def test_probe_tile_validation(lib, args):
+    mode, blocks, iters = args
+    assert lib.jattn_probe_tile(mode, blocks, iters, ctypes.c_float(1.0), fake(0), fake(1), None) == _lib.INVALID_VALUE
+
+
+def test_probe_tile_pointers(lib):
+    assert lib.jattn_probe_tile(0, 4, 10, ctypes.c_float(1.0), None, fake(1), None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_tile(0, 4, 10, ctypes.c_float(1.0), fake(0), None, None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_tile(0, 4, 10, ctypes.c_float(1.0), fake(0) + 2, fake(1), None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_tile(0, 4, 10, ctypes.c_float(1.0), fake(0), fake(1) + 4, None) == _lib.INVALID_VALUE
+
+
+@pytest.mark.parametrize("args", [(3, 4, 10), (-1, 4, 10), (0, 0, 10), (0, 4, 0), (0, 1 << 23, 10)])
+def test_probe_lds_read_validation(lib, args):
+    mode, blocks, iters = args
+    assert lib.jattn_probe_lds_read(mode, blocks, iters, fake(1), None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_lds_read(0, 4, 10, None, None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_lds_read(0, 4, 10, fake(1) + 4, None) == _lib.INVALID_VALUE
