@@ -519,21 +519,6 @@ __device__ __forceinline__ void zero_pad_columns(__bf16* lds, int ntiles, int ti
 // i.e. d = 16*ks + 8*(l/32) + [0..7] for each k-step ks.
 
 template <int D>
-__device__ __forceinline__ void load_row_chunks(float (&x)[Dims<D>::KS][8],
-                                                const uint16_t* __restrict__ row, bool valid, int g) {
-  using Dm = Dims<D>;
-#pragma unroll
-  for (int ks = 0; ks < Dm::KS; ++ks) {
-    const int c = 2 * ks + g;
-    if (valid && c < Dm::NCH)
-      unpack8(*reinterpret_cast<const u32x4*>(row + c * 8), x[ks]);
-    else
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[ks][e] = 0.f;
-  }
-}
-
-template <int D>
 __device__ __forceinline__ void load_row_frags_raw(bf16x8 (&f)[Dims<D>::KS],
                                                    const uint16_t* __restrict__ row, bool valid, int g) {
   using Dm = Dims<D>;
@@ -546,11 +531,13 @@ __device__ __forceinline__ void load_row_frags_raw(bf16x8 (&f)[Dims<D>::KS],
   }
 }
 
-// RMS-normalise a wave row held as in load_row_chunks (the other half of the row sits in lane l^32)
-// and round x * r * mul * ga[d] * gb[d] to bf16 fragments (gb may be null). Returns r (0 for
-// invalid rows).
+// RMS-normalise a wave row held as in load_row_frags_raw (the other half of the row sits in lane
+// l^32) and round x * r * mul * ga[d] * gb[d] to bf16 fragments (gb may be null). Returns r (0 for
+// invalid rows). The row stays in its bf16 form and is widened where it is used: widened copies
+// made at the load would either be made inside the per-lane load branch, which then waits there for
+// its load (one memory round trip per chunk), or hold a second copy of the row in registers.
 template <int D>
-__device__ __forceinline__ float rmsnorm_row_frags(bf16x8 (&f)[Dims<D>::KS], const float (&x)[Dims<D>::KS][8],
+__device__ __forceinline__ float rmsnorm_row_frags(bf16x8 (&f)[Dims<D>::KS], const bf16x8 (&x)[Dims<D>::KS],
                                                    const float* __restrict__ ga, const float* __restrict__ gb,
                                                    float mul, float eps, bool valid, int g) {
   using Dm = Dims<D>;
@@ -558,7 +545,10 @@ __device__ __forceinline__ float rmsnorm_row_frags(bf16x8 (&f)[Dims<D>::KS], con
 #pragma unroll
   for (int ks = 0; ks < Dm::KS; ++ks)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss += x[ks][e] * x[ks][e];
+    for (int e = 0; e < 8; ++e) {
+      const float v = (float)x[ks][e];
+      ss += v * v;
+    }
   ss += __shfl_xor(ss, 32);
   const float r = valid ? rsqrtf(ss * (1.0f / D) + eps) : 0.f;
 #pragma unroll
@@ -568,7 +558,7 @@ __device__ __forceinline__ float rmsnorm_row_frags(bf16x8 (&f)[Dims<D>::KS], con
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = c * 8 + e;
-      y[e] = c < Dm::NCH ? x[ks][e] * r * mul * ga[d] * (gb ? gb[d] : 1.f) : 0.f;
+      y[e] = c < Dm::NCH ? (float)x[ks][e] * r * mul * ga[d] * (gb ? gb[d] : 1.f) : 0.f;
     }
     f[ks] = to_bf16x8(y);
   }

@@ -295,8 +295,8 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
   for (int qt = 0; qt < QT; ++qt) {
     qrow[qt] = blk * Fwd<D>::ROWS + wave * 32 * QT + qt * 32 + l32;
     const bool qvalid = qrow[qt] < L;
-    float x[Dm::KS][8];
-    load_row_chunks<D>(x, map.row(a.q, a.q1, qrow[qt]), qvalid, g);
+    bf16x8 x[Dm::KS];
+    load_row_frags_raw<D>(x, map.row(a.q, a.q1, qrow[qt]), qvalid, g);
     float qq = 0.f;
     if constexpr (!S) {
       rmsnorm_row_frags<D>(qf[qt], x, a.gains, a.gains + D, a.c, a.eps, qvalid, g);
