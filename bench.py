@@ -78,7 +78,9 @@ def parse():
                          "include/jattn_diag.h) at the workload's shape, beside the dq kernel it would replace")
     ap.add_argument("--probe-tile", action="store_true",
                     help="time the dk/dv tile's dependency structure (jattn_probe_tile) with its operands in "
-                         "registers or LDS, and the LDS read rates (jattn_probe_lds_read); prints one JSON line")
+                         "registers or LDS, the LDS read rates (jattn_probe_lds_read), the MFMA / FMA / exp2 "
+                         "issue rates (jattn_probe_issue) and the forward tile's wave schedules "
+                         "(jattn_probe_pingpong); prints one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 512 MiB device-to-device three times: under rocprofv3 --pmc its "
                          "FETCH_SIZE / WRITE_SIZE give the counters' scale for a known byte count")
@@ -515,7 +517,7 @@ def probe_dq_accumulation(args, torch):
 
 def probe_tile(torch):
     """The probes of jattn_diag.h that time the dk/dv tile's dependency structure (which operands come from
-    LDS) and the LDS read rates, at one and two waves per SIMD, on the shader clock. Prints one JSON line."""
+    LDS), the LDS read rates and the MFMA / VALU issue rates, on the shader clock. Prints one JSON line."""
     from diffusion_transformer_joint_amd import _lib
     lib = _lib.load()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -548,6 +550,41 @@ def probe_tile(torch):
             res["lds_read"].append({"read": name, "waves_per_cu": 4 * wgs,
                                     "bytes_per_cu_per_cycle": round(8 * 4000 * 64 * width * 4 * wgs / c, 1),
                                     "cycles_per_wave_instruction": round(c / (8 * 4000), 2)})
+    # Issue rates (jattn_probe_issue): one workgroup of 8 waves per compute unit, two waves per SIMD.
+    # Per SIMD, the slower of its two waves over the 8 * iters steps is the SIMD's cycles per step of both.
+    res["issue"] = []
+    iters = 4000
+    out = torch.empty(cus * 512, dtype=torch.float32, device="cuda:0")
+    cyc = torch.zeros(cus * 8, dtype=torch.int64, device="cuda:0")
+    steps = (("mfma", "1 MFMA in each wave"), ("fma", "16 FMAs in each wave"), ("exp", "8 exp2 in each wave"),
+             ("mixed_fma", "1 MFMA + 16 FMAs in each wave"), ("mixed_exp", "1 MFMA + 8 exp2 in each wave"),
+             ("split_fma", "1 MFMA in one wave, 16 FMAs in the other"),
+             ("split_exp", "1 MFMA in one wave, 8 exp2 in the other"))
+    for mode, (name, step) in enumerate(steps):
+        for _ in range(2):
+            _lib.check("jattn_probe_issue", lib.jattn_probe_issue(mode, cus, iters, ctypes.c_float(1e-3),
+                                                                  out.data_ptr(), cyc.data_ptr(), sp))
+        torch.cuda.synchronize()
+        c = cyc.view(cus, 2, 4).double() / (8 * iters)  # [cu, wave pair slot, simd]
+        simd = torch.maximum(c[:, 0, :], c[:, 1, :])
+        res["issue"].append({"mode": name, "step_per_wave": step, "simd_cycles_per_step": round(simd.mean().item(), 1),
+                             "waves_0_3_cycles_per_step": round(c[:, 0, :].mean().item(), 1),
+                             "waves_4_7_cycles_per_step": round(c[:, 1, :].mean().item(), 1)})
+    # The forward tile's schedules (jattn_probe_pingpong): 16 MFMAs per wave and step, two waves per SIMD.
+    res["pingpong"] = []
+    iters = 2000
+    for mode, name in enumerate(("free", "barrier_per_step", "phased")):
+        for lds in (0, 1):
+            for _ in range(2):
+                _lib.check("jattn_probe_pingpong", lib.jattn_probe_pingpong(mode, lds, cus, iters, ctypes.c_float(1e-3),
+                                                                            out.data_ptr(), cyc.data_ptr(), sp))
+            torch.cuda.synchronize()
+            c = cyc.double() / iters
+            res["pingpong"].append({"schedule": name, "operands": "lds" if lds else "registers",
+                                    "cycles_per_step_mean": round(c.mean().item(), 1),
+                                    "cycles_per_step_max": round(c.max().item(), 1),
+                                    "mfma_busy_mean": round(1024.0 / c.mean().item(), 3),
+                                    "mfma_busy_slowest_wave": round(1024.0 / c.max().item(), 3)})
     print(json.dumps(res), flush=True)
 
 

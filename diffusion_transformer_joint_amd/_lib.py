@@ -21,7 +21,8 @@ EXPORTED = ("jattn_fwd", "jattn_fwd_noalloc", "jattn_fwd_noalloc_max_scratch_byt
             "jattn_bwd_window", "jattn_adaln_qkv_fwd_workspace_bytes", "jattn_adaln_qkv_bwd_workspace_bytes",
             "jattn_adaln_qkv_fwd", "jattn_adaln_qkv_bwd", "jattn_mlp_fwd_workspace_bytes", "jattn_mlp_bwd_workspace_bytes",
             "jattn_mlp_fwd", "jattn_mlp_bwd", "jattn_probe_saturate", "jattn_probe_dq_accumulation", "jattn_probe_tile",
-            "jattn_probe_lds_read", "jattn_status_string", "jattn_abi_version")
+            "jattn_probe_lds_read", "jattn_probe_issue", "jattn_probe_pingpong",
+            "jattn_status_string", "jattn_abi_version")
 ABI_VERSION = 9
 FWD_STAGES = ("prenorm_kernel", "fwd_kernel")
 BWD_STAGES = ("prenorm_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "dg_reduce_kernel")
@@ -115,6 +116,10 @@ def load() -> ctypes.CDLL:
         lib.jattn_probe_tile.argtypes = [I, I, I, ctypes.c_float, P, P, P]
         lib.jattn_probe_lds_read.restype = I
         lib.jattn_probe_lds_read.argtypes = [I, I, I, P, P]
+        lib.jattn_probe_issue.restype = I
+        lib.jattn_probe_issue.argtypes = [I, I, I, ctypes.c_float, P, P, P]
+        lib.jattn_probe_pingpong.restype = I
+        lib.jattn_probe_pingpong.argtypes = [I, I, I, I, ctypes.c_float, P, P, P]
         lib.jattn_mlp_bwd.restype = I
         lib.jattn_mlp_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
                                       ctypes.c_size_t, P, I, P]

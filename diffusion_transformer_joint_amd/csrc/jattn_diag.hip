@@ -1,6 +1,6 @@
 // Measurement support (see jattn_diag.h): saturating probe kernels for reading the full-scale values
 // of the SQ busy counters, the dQ-accumulation traffic probe, and probes of the dk/dv tile's
-// dependency structure and of LDS read rates.
+// dependency structure, of LDS read rates and of the MFMA / VALU issue rates.
 #include "jattn_diag.h"
 #include "jattn_device.h"
 
@@ -280,6 +280,188 @@ __global__ __launch_bounds__(kProbeThreads) void probe_lds_read_kernel(int iters
   if (lane == 0) cycles[(size_t)blockIdx.x * (kProbeThreads / 64) + w] = t1 - t0;
 }
 
+
+// Issue rates of the matrix pipe, fp32 FMAs and exp2 (v_exp_f32), alone and together: workgroups of
+// 8 waves, two per SIMD (waves w and w + 4 share SIMD w % 4), each looping `iters` times over 8 steps.
+// A step is one MFMA (four independent accumulators in turn), 16 FMAs (eight independent chains) or
+// 8 exp2 (eight independent chains), or one MFMA plus the FMAs or exps in the same wave (MIXED), or
+// the MFMA in waves 0-3 and the FMAs or exps in waves 4-7 (SPLIT).
+constexpr int kIssueThreads = 512;
+
+template <int MODE>
+__global__ __launch_bounds__(kIssueThreads) void probe_issue_kernel(int iters, float seed, float* __restrict__ out,
+                                                                    uint64_t* __restrict__ cycles) {
+  const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool first = w < 4;  // (wave-uniform)
+  constexpr bool ANY_MFMA = MODE != JATTN_PROBE_ISSUE_FMA && MODE != JATTN_PROBE_ISSUE_EXP;
+  constexpr bool ANY_FMA = MODE == JATTN_PROBE_ISSUE_FMA || MODE == JATTN_PROBE_ISSUE_MIXED_FMA ||
+                           MODE == JATTN_PROBE_ISSUE_SPLIT_FMA;
+  constexpr bool ANY_EXP = MODE == JATTN_PROBE_ISSUE_EXP || MODE == JATTN_PROBE_ISSUE_MIXED_EXP ||
+                           MODE == JATTN_PROBE_ISSUE_SPLIT_EXP;
+  constexpr bool SPLIT = MODE == JATTN_PROBE_ISSUE_SPLIT_FMA || MODE == JATTN_PROBE_ISSUE_SPLIT_EXP;
+  const bool do_mfma = ANY_MFMA && (!SPLIT || first);
+  const bool do_valu = (ANY_FMA || ANY_EXP) && (!SPLIT || !first);
+  f32x16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
+  bf16x8 a, b;
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(seed * (float)(tid + i));
+    b[i] = (__bf16)(seed * (float)i);
+    x[i] = seed * (float)(tid + i) * 1e-3f;
+  }
+  auto valu = [&]() {
+    if constexpr (ANY_FMA) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = x[i] * 0.999f + 1e-3f;
+    } else if constexpr (ANY_EXP) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = fast_exp2(-x[i]);  // stays in [0.5, 1]
+    }
+  };
+  // (one straight-line loop per wave kind: no branch inside the steps)
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  if (do_mfma && do_valu) {
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        acc[r & 3] = mfma(a, b, acc[r & 3]);
+        valu();
+      }
+  } else if (do_mfma) {
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r & 3] = mfma(a, b, acc[r & 3]);
+  } else {
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) valu();
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += x[i];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += acc[j][i];
+  out[(size_t)blockIdx.x * kIssueThreads + tid] = sum;
+  if (lane == 0) cycles[(size_t)blockIdx.x * (kIssueThreads / 64) + w] = t1 - t0;
+}
+
+
+// The forward tile's structure at D = 64 without global loads: per wave and step two 32-query tiles,
+// each with 4 score MFMAs (seeded accumulator), 16 exp2, 8 bf16 packs and 8 dot2 row-sum steps, and
+// 4 PV MFMAs on the packed probabilities. Workgroups of 8 waves (two per SIMD). K fragments
+// (ds_read_b128) and V fragments (ds_read_b64_tr_b16) come from a 64 x 64 LDS tile pair or registers.
+template <int MODE, bool LDS>
+__global__ __launch_bounds__(kIssueThreads) void probe_pingpong_kernel(int iters, float seed, float* __restrict__ out,
+                                                                       uint64_t* __restrict__ cycles) {
+  __shared__ __attribute__((aligned(16))) __bf16 tile[2][64 * 64];  // K rows, V rows
+  const int tid = (int)threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  for (int i = tid; i < 2 * 64 * 64; i += kIssueThreads) (&tile[0][0])[i] = (__bf16)(seed * (float)(i & 63));
+  __syncthreads();
+  bf16x8 qf[2][4], kr[4], vr[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qf[0][ks][e] = (__bf16)(seed * (float)(tid + ks + e));
+      qf[1][ks][e] = (__bf16)(seed * (float)(tid - ks + e));
+      kr[ks][e] = (__bf16)(seed * (float)(lane + ks * e));
+      vr[ks][e] = (__bf16)(seed * (float)(lane - ks * e));
+    }
+  f32x16 o[2][2], sc[2];
+  bf16x8 pf[2][2];
+  float lsum[2] = {0.f, 0.f};
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[qt][0][i] = o[qt][1][i] = sc[qt][i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[qt][0][e] = pf[qt][1][e] = (__bf16)0.f;
+  }
+  // (the fragments' tile offsets change every step, so the reads stay inside the loop: K rows koff ..
+  // koff + 31 of 64, V columns up to voff + 47 of 64)
+  int koff = 0, voff = 0;
+  auto scores = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      f32x16 c;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = -4.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        c = mfma(LDS ? *reinterpret_cast<const bf16x8*>(&tile[0][(l32 + koff) * 64 + ks * 16 + g * 8]) : kr[ks],
+                 qf[qt][ks], c);
+      sc[qt] = c;
+    }
+  };
+  auto pv = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 vf = vr[mt * 2 + h];
+          if constexpr (LDS) {
+            // lane j of each 16-lane group addresses row (j / 4) of its group's 4 rows, column 4 (j % 4)
+            const int row = h * 16 + (lane >> 4) * 4 + ((lane & 15) >> 2), col = mt * 32 + 4 * (lane & 3) + voff;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (JATTN_LDS i16x4*)(reinterpret_cast<char*>(&tile[1][0]) + (row * 64 + col) * 2));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (JATTN_LDS i16x4*)(reinterpret_cast<char*>(&tile[1][0]) + ((row + 8) * 64 + col) * 2));
+            vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+          o[qt][mt] = mfma(vf, pf[qt][h], o[qt][mt]);
+        }
+  };
+  auto softmax = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = fast_exp2(sc[qt][i]);
+      pack_probs(p, pf[qt][0], pf[qt][1], lsum[qt]);
+    }
+  };
+  const bool second = w >= 4;  // (wave-uniform)
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  if (MODE == JATTN_PROBE_PINGPONG_PHASED && second) __syncthreads();  // waves 4-7 start one phase later
+  for (int it = 0; it < iters; ++it) {
+    koff = (it & 1) * 32;
+    voff = (it & 1) * 16;
+    if constexpr (MODE == JATTN_PROBE_PINGPONG_PHASED) {
+      scores();  // MFMA phase: S(t) and PV(t - 1)
+      pv();
+      __syncthreads();
+      softmax();  // softmax phase, while the other wave of the SIMD runs its MFMA phase
+      __syncthreads();
+    } else {
+      scores();
+      softmax();
+      pv();
+      if constexpr (MODE == JATTN_PROBE_PINGPONG_BARRIER) __syncthreads();
+    }
+  }
+  if (MODE == JATTN_PROBE_PINGPONG_PHASED && !second) __syncthreads();
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  float sum = lsum[0] + lsum[1];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += o[qt][0][i] + o[qt][1][i];
+  out[(size_t)blockIdx.x * kIssueThreads + tid] = sum;
+  if (lane == 0) cycles[(size_t)blockIdx.x * (kIssueThreads / 64) + w] = t1 - t0;
+}
+
 }  // namespace jattn
 
 extern "C" jattn_status jattn_probe_dq_accumulation(int mode, int pairs, int L, int D, int nkb, float* acc,
@@ -353,5 +535,51 @@ extern "C" jattn_status jattn_probe_lds_read(int mode, int blocks, int iters, ui
   else
     hipLaunchKernelGGL(jattn::probe_lds_read_kernel<JATTN_PROBE_LDS_B64_TRANSPOSED>, dim3(blocks),
                        dim3(jattn::kProbeThreads), 0, stream, iters, cycles);
+  return hipGetLastError() == hipSuccess ? JATTN_SUCCESS : JATTN_ERROR_HIP;
+}
+
+extern "C" jattn_status jattn_probe_issue(int mode, int blocks, int iters, float seed, float* out, uint64_t* cycles,
+                                          hipStream_t stream) {
+  if (mode < JATTN_PROBE_ISSUE_MFMA || mode > JATTN_PROBE_ISSUE_SPLIT_EXP || blocks < 1 || iters < 1 ||
+      (int64_t)blocks * jattn::kIssueThreads >= ((int64_t)1 << 31) || out == nullptr || cycles == nullptr ||
+      (reinterpret_cast<uintptr_t>(out) & 3u) != 0 || (reinterpret_cast<uintptr_t>(cycles) & 7u) != 0)
+    return JATTN_ERROR_INVALID_VALUE;
+  const dim3 grid(blocks), block(jattn::kIssueThreads);
+  switch (mode) {
+#define JATTN_ISSUE_CASE(M) \
+  case M: hipLaunchKernelGGL(jattn::probe_issue_kernel<M>, grid, block, 0, stream, iters, seed, out, cycles); break;
+    JATTN_ISSUE_CASE(JATTN_PROBE_ISSUE_MFMA)
+    JATTN_ISSUE_CASE(JATTN_PROBE_ISSUE_FMA)
+    JATTN_ISSUE_CASE(JATTN_PROBE_ISSUE_EXP)
+    JATTN_ISSUE_CASE(JATTN_PROBE_ISSUE_MIXED_FMA)
+    JATTN_ISSUE_CASE(JATTN_PROBE_ISSUE_MIXED_EXP)
+    JATTN_ISSUE_CASE(JATTN_PROBE_ISSUE_SPLIT_FMA)
+    JATTN_ISSUE_CASE(JATTN_PROBE_ISSUE_SPLIT_EXP)
+#undef JATTN_ISSUE_CASE
+  }
+  return hipGetLastError() == hipSuccess ? JATTN_SUCCESS : JATTN_ERROR_HIP;
+}
+
+extern "C" jattn_status jattn_probe_pingpong(int mode, int lds, int blocks, int iters, float seed, float* out,
+                                             uint64_t* cycles, hipStream_t stream) {
+  if (mode < JATTN_PROBE_PINGPONG_FREE || mode > JATTN_PROBE_PINGPONG_PHASED || (lds != 0 && lds != 1) ||
+      blocks < 1 || iters < 1 || (int64_t)blocks * jattn::kIssueThreads >= ((int64_t)1 << 31) || out == nullptr ||
+      cycles == nullptr || (reinterpret_cast<uintptr_t>(out) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(cycles) & 7u) != 0)
+    return JATTN_ERROR_INVALID_VALUE;
+  const dim3 grid(blocks), block(jattn::kIssueThreads);
+  switch (mode * 2 + lds) {
+#define JATTN_PP_CASE(M, LD)                                                                                 \
+  case M * 2 + LD:                                                                                           \
+    hipLaunchKernelGGL((jattn::probe_pingpong_kernel<M, LD>), grid, block, 0, stream, iters, seed, out, cycles); \
+    break;
+    JATTN_PP_CASE(JATTN_PROBE_PINGPONG_FREE, 0)
+    JATTN_PP_CASE(JATTN_PROBE_PINGPONG_FREE, 1)
+    JATTN_PP_CASE(JATTN_PROBE_PINGPONG_BARRIER, 0)
+    JATTN_PP_CASE(JATTN_PROBE_PINGPONG_BARRIER, 1)
+    JATTN_PP_CASE(JATTN_PROBE_PINGPONG_PHASED, 0)
+    JATTN_PP_CASE(JATTN_PROBE_PINGPONG_PHASED, 1)
+#undef JATTN_PP_CASE
+  }
   return hipGetLastError() == hipSuccess ? JATTN_SUCCESS : JATTN_ERROR_HIP;
 }

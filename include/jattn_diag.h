@@ -3,7 +3,8 @@
  * projection math.
  *
  * Busy-counter calibration, a dQ-accumulation traffic probe, and probes of the dk/dv tile's
- * dependency structure and of LDS read rates (the tile probes time themselves with the shader clock).
+ * dependency structure, of LDS read rates and of the MFMA / VALU issue rates (the tile probes time
+ * themselves with the shader clock).
  *
  * Hardware busy counters (the SQ block's MFMA-busy and VALU-issue cycles) have no documented
  * full-scale value per GPU, clock and counter-aggregation mode. The probe kernels here keep one pipe
@@ -98,6 +99,52 @@ jattn_status jattn_probe_tile(int mode, int blocks, int iters, float seed, float
 #define JATTN_PROBE_LDS_B128_BROADCAST 1
 #define JATTN_PROBE_LDS_B64_TRANSPOSED 2
 jattn_status jattn_probe_lds_read(int mode, int blocks, int iters, uint64_t* cycles, hipStream_t stream);
+
+/* Issue rates of the matrix pipe, fp32 FMAs and exp2 (v_exp_f32), alone and together. `blocks`
+ * workgroups of 512 threads (8 waves, two per SIMD: waves w and w + 4 share SIMD w % 4 as the waves of a
+ * workgroup are placed in order) loop `iters` times over 8 steps each. Per wave and step:
+ *   JATTN_PROBE_ISSUE_MFMA       one v_mfma_f32_32x32x16_bf16 (four independent accumulators in turn);
+ *   JATTN_PROBE_ISSUE_FMA        16 fp32 FMAs (eight independent chains);
+ *   JATTN_PROBE_ISSUE_EXP        8 exp2 (eight independent chains);
+ *   JATTN_PROBE_ISSUE_MIXED_FMA  the MFMA and the 16 FMAs in every wave;
+ *   JATTN_PROBE_ISSUE_MIXED_EXP  the MFMA and the 8 exp2 in every wave;
+ *   JATTN_PROBE_ISSUE_SPLIT_FMA  the MFMA in waves 0-3, the 16 FMAs in waves 4-7 (one of each per SIMD);
+ *   JATTN_PROBE_ISSUE_SPLIT_EXP  the MFMA in waves 0-3, the 8 exp2 in waves 4-7.
+ *   out     device fp32 [blocks * 512]: one value per thread (keeps the work live), overwritten;
+ *   cycles  device uint64 [blocks * 8]: each wave's shader-clock cycles (s_memtime) over its loop.
+ * With one workgroup per compute unit, the larger of the cycles of waves w and w + 4 over 8 * iters is
+ * the SIMD's cycles per step of both its waves.
+ * Errors: INVALID_VALUE for an unknown mode, blocks < 1, iters < 1, blocks * 512 >= 2^31, or a null or
+ * misaligned out or cycles; HIP if the launch fails. */
+#define JATTN_PROBE_ISSUE_MFMA 0
+#define JATTN_PROBE_ISSUE_FMA 1
+#define JATTN_PROBE_ISSUE_EXP 2
+#define JATTN_PROBE_ISSUE_MIXED_FMA 3
+#define JATTN_PROBE_ISSUE_MIXED_EXP 4
+#define JATTN_PROBE_ISSUE_SPLIT_FMA 5
+#define JATTN_PROBE_ISSUE_SPLIT_EXP 6
+jattn_status jattn_probe_issue(int mode, int blocks, int iters, float seed, float* out, uint64_t* cycles,
+                               hipStream_t stream);
+
+/* The forward tile's structure at D = 64 without global loads, to compare schedules of the two waves
+ * that share a SIMD. `blocks` workgroups of 512 threads (8 waves, two per SIMD) loop `iters` times over
+ * one step: per wave two 32-query tiles, each with 4 score MFMAs, 16 exp2, 8 bf16 packs and 8 row-sum
+ * steps, then 4 PV MFMAs (16 MFMAs of 32x32x16 per wave and step). K and V fragments come from a
+ * 64 x 64 LDS tile pair (lds = 1: ds_read_b128 and ds_read_b64_tr_b16) or from registers (lds = 0).
+ *   JATTN_PROBE_PINGPONG_FREE     every wave runs scores -> softmax -> PV, no barrier;
+ *   JATTN_PROBE_PINGPONG_BARRIER  the same with a workgroup barrier per step;
+ *   JATTN_PROBE_PINGPONG_PHASED   two phases per step between barriers, waves 4-7 one phase behind
+ *                                 waves 0-3: the MFMAs (S(t), PV(t - 1)) of one wave of each SIMD run
+ *                                 while the other wave runs its softmax.
+ *   out     device fp32 [blocks * 512], overwritten; cycles device uint64 [blocks * 8]: each wave's
+ *   shader-clock cycles over its loop. MFMA pipe busy = 1024 * iters / cycles (two waves per SIMD).
+ * Errors: INVALID_VALUE for an unknown mode, lds not 0 or 1, blocks < 1, iters < 1,
+ * blocks * 512 >= 2^31, or a null or misaligned out or cycles; HIP if the launch fails. */
+#define JATTN_PROBE_PINGPONG_FREE 0
+#define JATTN_PROBE_PINGPONG_BARRIER 1
+#define JATTN_PROBE_PINGPONG_PHASED 2
+jattn_status jattn_probe_pingpong(int mode, int lds, int blocks, int iters, float seed, float* out, uint64_t* cycles,
+                                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -453,3 +453,32 @@ def test_probe_lds_read_validation(lib, args):
     assert lib.jattn_probe_lds_read(mode, blocks, iters, fake(1), None) == _lib.INVALID_VALUE
     assert lib.jattn_probe_lds_read(0, 4, 10, None, None) == _lib.INVALID_VALUE
     assert lib.jattn_probe_lds_read(0, 4, 10, fake(1) + 4, None) == _lib.INVALID_VALUE
+
+
+@pytest.mark.parametrize("args", [(7, 4, 10), (-1, 4, 10), (0, 0, 10), (0, 4, 0), (0, 1 << 22, 10)])
+def test_probe_issue_validation(lib, args):
+    mode, blocks, iters = args
+    assert lib.jattn_probe_issue(mode, blocks, iters, ctypes.c_float(1.0), fake(0), fake(1), None) == _lib.INVALID_VALUE
+
+
+def test_probe_issue_pointers(lib):
+    assert lib.jattn_probe_issue(0, 4, 10, ctypes.c_float(1.0), None, fake(1), None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_issue(0, 4, 10, ctypes.c_float(1.0), fake(0), None, None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_issue(0, 4, 10, ctypes.c_float(1.0), fake(0) + 2, fake(1), None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_issue(0, 4, 10, ctypes.c_float(1.0), fake(0), fake(1) + 4, None) == _lib.INVALID_VALUE
+
+
+@pytest.mark.parametrize("args", [(3, 0, 4, 10), (-1, 0, 4, 10), (0, 2, 4, 10), (0, -1, 4, 10), (0, 0, 0, 10),
+                                  (0, 1, 4, 0), (2, 1, 1 << 22, 10)])
+def test_probe_pingpong_validation(lib, args):
+    mode, lds, blocks, iters = args
+    assert lib.jattn_probe_pingpong(mode, lds, blocks, iters, ctypes.c_float(1.0), fake(0), fake(1),
+                                    None) == _lib.INVALID_VALUE
+
+
+def test_probe_pingpong_pointers(lib):
+    f = ctypes.c_float(1.0)
+    assert lib.jattn_probe_pingpong(0, 0, 4, 10, f, None, fake(1), None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_pingpong(0, 0, 4, 10, f, fake(0), None, None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_pingpong(0, 0, 4, 10, f, fake(0) + 2, fake(1), None) == _lib.INVALID_VALUE
+    assert lib.jattn_probe_pingpong(0, 0, 4, 10, f, fake(0), fake(1) + 4, None) == _lib.INVALID_VALUE
