@@ -745,10 +745,14 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, const Ro
   const int ntiles = (L + kTile - 1) / kTile;
   LaneOffs<D> lo;
   if constexpr (bwd_waves_per_eu<D>() == 1) lo.template init<LQ>(lane);
+  // Two waves per SIMD with a 4-buffer ring: two query tiles per barrier (each step computes tiles t and
+  // t + 1 and loads t + 2 and t + 3 into the buffers the previous step used; 2 % faster at D = 64 than a
+  // barrier per tile. The dq kernel measured slower that way and keeps one tile per barrier.)
+  constexpr bool PAIRS = NB == 4 && !W && bwd_waves_per_eu<D>() == 2;
   if constexpr (W) {
     for (int i = 0; i < NB - 1 && tr.lo + i < tr.hi; ++i) issue(tr.lo + i, i);
   } else {
-    for (int t = 0; t < NB - 1 && t < ntiles; ++t) issue(t, t);
+    for (int t = 0; t < (PAIRS ? 2 : NB - 1) && t < ntiles; ++t) issue(t, t);
   }
   wait_vmem();
   __syncthreads();
@@ -771,6 +775,24 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, const Ro
     for (; t < tr.flo; ++t) wstep(std::true_type{}, t);
     for (; t < tr.fhi; ++t) wstep(std::false_type{}, t);
     for (; t < tr.hi; ++t) wstep(std::true_type{}, t);
+    return;
+  }
+  if constexpr (PAIRS) {
+    for (int t = 0; t < ntiles; t += 2) {
+      if (t + 2 < ntiles) issue(t + 2, (t + 2) & 3);
+      if (t + 3 < ntiles) issue(t + 3, (t + 3) & 3);
+      if (active) {
+        const int b0 = t & 3;
+        dkdv_tile_any<D, KMASK>(sq + b0 * LQ::ELEMS, so + b0 * LO::ELEMS, sl + b0 * kTile, sd + b0 * kTile, kf,
+                                vf, dva, dka, kvalid, lane, lo);
+        if (t + 1 < ntiles) {
+          const int b1 = b0 + 1;
+          dkdv_tile_any<D, KMASK>(sq + b1 * LQ::ELEMS, so + b1 * LO::ELEMS, sl + b1 * kTile, sd + b1 * kTile, kf,
+                                  vf, dva, dka, kvalid, lane, lo);
+        }
+      }
+      stream_barrier<0>();  // (also ends the item: the ring is free for the next one)
+    }
     return;
   }
   for (int t = 0; t < ntiles; ++t) {

@@ -53,9 +53,10 @@ struct Fwd {
   using LK = Lay<D, kSwizzled>;  // key rows: row fragments (padded rows where D has no swizzle)
   // value rows: read transposed only (swizzled for D = 64, 128, else a pitch for transposed reads)
   using LV = Lay<D, (D == 64 || D == 128) ? kSwizzled : kTrRead>;
-  // ring depth: three buffers (loads two tiles ahead) where two workgroups per CU still fit in LDS
-  // (up to 64 padded columns), else two
-  static constexpr int NB = Dims<D>::DM > 64 ? 2 : 3;
+  // ring depth: up to 64 padded columns, four buffers (stepped two tiles per barrier, below) where two
+  // workgroups per CU still fit in the 160 KB of LDS, else three; two for wider rows
+  static constexpr int BUF = (LK::ELEMS + LV::ELEMS) * 2;  // bytes per ring buffer
+  static constexpr int NB = Dims<D>::DM > 64 ? 2 : (4 * BUF + 16 <= 80 * 1024 ? 4 : 3);
   static constexpr int STAGE = NB * (LK::ELEMS + LV::ELEMS) * 2;  // bytes
   static constexpr int BYTES = STAGE + 16;
   static_assert(QT == 1 || QT == 2, "query tiles per wave");
@@ -204,7 +205,48 @@ __device__ __forceinline__ void fwd_loop(FwdRing<D, S>& ring, const bf16x8 (&qf)
     ring_barrier<FwdRing<D, S>::PER, NB - 2>(ntiles - 2 - t);
     cur = cur + 1 == NB ? 0 : cur + 1;
   };
-  if constexpr (!W) {
+  if constexpr (!W && NB == 4) {
+    // Two tiles per barrier: each step computes tiles t and t + 1 and loads t + 2 and t + 3 into the
+    // buffers the previous step used (a workgroup barrier per tile cost ~4 % of the forward at D = 64).
+    // The scheduling barrier keeps the two tiles' instructions apart (interleaved, they spill).
+    auto tile = [&](auto masked, int t) {
+      const int b = t & 3;
+      fwd_tile<D, BOUNDED, decltype(masked)::value>(ring.sk + b * LK::ELEMS, ring.sv + b * LV::ELEMS, qf, cinit, st,
+                                                    t * kTile, n, lane);
+    };
+    int t = 0;
+    for (; t + 1 < nfull; t += 2) {
+      if (t + 2 < ntiles) ring.issue(t + 2, (t + 2) & 3);
+      if (t + 3 < ntiles) ring.issue(t + 3, (t + 3) & 3);
+      if (active) {
+        tile(std::false_type{}, t);
+        __builtin_amdgcn_sched_barrier(0);
+        tile(std::false_type{}, t + 1);
+      }
+      stream_barrier<0>();
+    }
+    // The last one or two tiles are in their buffers already; a barrier after them frees the ring for
+    // the next item. The partial last tile is handled as in the one-tile form below.
+    const int t_rest = t;
+    if (t < nfull && active) tile(std::false_type{}, t);
+    if (nfull < ntiles) {
+      if constexpr (BOUNDED) {
+        if (active) tile(std::false_type{}, nfull);
+        const int m0 = n - nfull * kTile, g4 = 4 * (lane >> 5);
+        int nm = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) nm += min(4, max(0, 8 * k + g4 + 4 - m0));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float p0 = bf_lo(pack2(fast_exp2(-shift[qt]), 0.f));
+          st.lsum[qt] -= (float)nm * p0;
+        }
+      } else {
+        if (active) tile(std::true_type{}, nfull);
+      }
+    }
+    if (t_rest < ntiles) __syncthreads();
+  } else if constexpr (!W) {
     for (int t = 0; t < nfull; ++t) step(std::false_type{}, t);
     if (nfull < ntiles) {
       if constexpr (BOUNDED) {
@@ -281,7 +323,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
   if constexpr (W) {
     for (int i = 0; i < Fwd<D>::NB - 1 && tr.lo + i < tr.hi; ++i) ring.issue(tr.lo + i, i);
   } else {
-    for (int t = 0; t < Fwd<D>::NB - 1 && t < ring.ntiles; ++t) ring.issue(t, t);
+    for (int t = 0; t < (Fwd<D>::NB == 4 ? 2 : Fwd<D>::NB - 1) && t < ring.ntiles; ++t) ring.issue(t, t);
   }
 
   // This wave's query rows, normalised with both gains (two-stream: its own stream's Q gain) and
