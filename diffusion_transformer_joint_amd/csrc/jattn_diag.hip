@@ -105,8 +105,13 @@ __global__ __launch_bounds__(kProbeThreads) void probe_tile_kernel(int iters, fl
                          MODE == JATTN_PROBE_TILE_TRANSPOSED || MODE == JATTN_PROBE_TILE_PIPELINED;
   __shared__ __attribute__((aligned(16))) char smem[2 * kTileStage];
   const int tid = (int)threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  for (int i = tid; i < 2 * kTileStage / 4; i += kProbeThreads)
-    reinterpret_cast<float*>(smem)[i] = seed * (float)(i & 127) * 1e-3f;
+  // (the tiles as small bf16 values, the statistics as small fp32 values: the fragments are read as bf16,
+  // so fp32 patterns there would put arbitrary bit patterns, NaN among them, into the arithmetic)
+  for (int i = tid; i < kTileStage; i += kProbeThreads) {  // 16-bit elements of both stages
+    if ((i * 2) % kTileStage < 2 * kTileBytes) reinterpret_cast<__bf16*>(smem)[i] = (__bf16)(seed * (float)(i & 127));
+  }
+  for (int i = tid; i < 2 * 128; i += kProbeThreads)
+    reinterpret_cast<float*>(smem + (i >> 7) * kTileStage + 2 * kTileBytes)[i & 127] = -seed * (float)(i & 63);
   __syncthreads();
   bf16x8 kf[4], vf[4], treg[2][2];
 #pragma unroll
