@@ -13,17 +13,21 @@ namespace jattn {
 
 static_assert(kBwdRowsPerBlock == kBwdWaves * kWaveRows && kBwdWaves >= 2, "backward workgroup shape");
 
-// Waves per SIMD the register allocation targets: two up to D = 72, one above (from D = 80 the
-// accumulators and operand fragments need the whole register file).
+// Waves per SIMD the register allocation targets. dq kernel: two at every head dim (above D = 64 its
+// tile reads the key and value row fragments one k-step at a time, so that they fit beside the dQ
+// accumulators). dk/dv kernel: two up to D = 72, one above (from D = 80 its dK and dV accumulators
+// and key/value fragments need the whole register file).
 template <int D>
-constexpr int bwd_waves_per_eu() { return D <= kNarrowMaxD ? 2 : 1; }
-// Two waves per SIMD with tiles padded past 64 columns (D = 72): the tightest case for LDS and registers.
+constexpr int dq_waves_per_eu() { return 2; }
 template <int D>
-constexpr bool bwd_tight() { return Dims<D>::DM > 64 && bwd_waves_per_eu<D>() == 2; }
+constexpr int dkdv_waves_per_eu() { return D <= kNarrowMaxD ? 2 : 1; }
+// Two waves per SIMD with tiles padded past 64 columns: the tightest case for LDS and registers.
+template <int D, int WPE>
+constexpr bool bwd_tight() { return Dims<D>::DM > 64 && WPE == 2; }
 // LDS ring depth: four tile buffers (loads issued three tiles ahead; measured slightly faster than
 // three), two in the tight case, whose padded tiles would otherwise not leave room for two workgroups per CU.
-template <int D>
-constexpr int bwd_nbuf() { return bwd_tight<D>() || kBwdWaves < 4 ? 2 : 4; }
+template <int D, int WPE>
+constexpr int bwd_nbuf() { return bwd_tight<D, WPE>() || kBwdWaves < 4 ? 2 : 4; }
 
 
 // LDS plan of the two main kernels. The swizzled layout (D = 64, 128) serves both row-fragment and
@@ -32,7 +36,7 @@ template <int D>
 struct DqCfg {
   using LK = Lay<D, kSwizzled>;  // normalised key rows: S (row fragments) and dQ (transposed)
   using LV = Lay<D, kSwizzled>;  // value rows: dP (row fragments)
-  static constexpr int NB = bwd_nbuf<D>();
+  static constexpr int NB = bwd_nbuf<D, dq_waves_per_eu<D>()>();
   static constexpr int STAGE = NB * (LK::ELEMS + LV::ELEMS) * 2;
   // LDS bytes of the kernel (two-stream: the epilogue's per-stream column sums reuse the ring)
   template <bool S>
@@ -46,7 +50,7 @@ template <int D>
 struct DkdvCfg {
   using LQ = Lay<D, kSwizzled>;  // pre-scaled normalised query rows: S and dK
   using LO = Lay<D, kSwizzled>;  // dout rows: dP and dV
-  static constexpr int NB = bwd_nbuf<D>();
+  static constexpr int NB = bwd_nbuf<D, dkdv_waves_per_eu<D>()>();
   static constexpr int STAGE = NB * (LQ::ELEMS + LO::ELEMS) * 2;
   static constexpr int STATS = NB * 2 * kTile * 4;  // -lse2 and -delta per streamed row
   template <bool S>
@@ -64,11 +68,11 @@ template <int D>
 struct RowC {
   u32x2 w[Dims<D>::MT][4];
 };
-template <int D>
+template <int D, int WPE>
 constexpr bool keep_row_c() {
   // (no registers to spare in the tight case; at one wave per SIMD the loops use them better than the
   // row: without it, dq 7 % and dk/dv 4 % faster at D = 128)
-  return bwd_waves_per_eu<D>() == 2 && !bwd_tight<D>();
+  return WPE == 2 && !bwd_tight<D, WPE>();
 }
 
 template <int D>
@@ -251,7 +255,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
       acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32 + 16, mt * 32, lane), f[h][1], acc[mt]);
     }
   };
-  if constexpr (bwd_waves_per_eu<D>() == 1) {
+  if constexpr (dq_waves_per_eu<D>() == 1) {
     LaneOffs<D> lo;
     lo.template init<LK>(lane);
     bf16x8 tk[MT][2];
@@ -293,6 +297,51 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
     __builtin_amdgcn_sched_barrier(0);
     accumulate2(1);
     __builtin_amdgcn_sched_barrier(0);
+  } else if constexpr (KS > 4) {
+    // Two waves per SIMD at wide head dims: each key and value row fragment is read from LDS just
+    // before its MFMAs instead of a whole half at once, and the MFMA seeds are formed in each tile from
+    // the row statistics rather than kept through the loop, so that the tile fits beside the dQ
+    // accumulators in 256 registers.
+    // (the lane index is made opaque too: the per-lane LDS offsets derived from it are then formed in
+    // each tile instead of being hoisted out of the loop and spilled)
+    float nl = cs[0], nd = cp[0];
+    int ln = lane;
+    asm volatile("" : "+v"(nl), "+v"(nd), "+v"(ln));
+    const int gg = ln >> 5, r32 = ln & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[h][i] = nl;
+        dp[h][i] = nd;
+      }
+      if constexpr (MASKED && W) {
+        const int clo = qrow - wl - key0, span = max(min(n, qrow + wr + 1) - key0 - clo, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = h * 32 + (i >> 2) * 8 + gg * 4 + (i & 3);
+          s[h][i] = (uint32_t)(c - clo) < (uint32_t)span ? s[h][i] : -INFINITY;
+        }
+      } else if constexpr (MASKED) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key0 + h * 32 + (i >> 2) * 8 + gg * 4 + (i & 3) >= n) s[h][i] = -INFINITY;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 k1 = lds_row_frag<LK>(kt, h * 32 + r32, ks * 16 + gg * 8);
+        const bf16x8 v1 = lds_row_frag<LV>(vt, h * 32 + r32, ks * 16 + gg * 8);
+        s[h] = mfma(k1, qf[ks], s[h]);
+        dp[h] = mfma(v1, dof[ks], dp[h]);
+      }
+      softmax(h);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32, mt * 32, ln), f[h][0], acc[mt]);
+        acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32 + 16, mt * 32, ln), f[h][1], acc[mt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   } else {
     rows(0);
     scores(0);
@@ -360,7 +409,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
   // One wave per SIMD: every row load is issued before any is used, one memory round trip for the
   // set-up (dq 2 % faster at D = 128). At two waves the other wave covers the waits, and the rows
   // held longer made dq 2 % slower at D = 64.
-  constexpr bool kLoadFirst = bwd_waves_per_eu<D>() == 1;
+  constexpr bool kLoadFirst = dq_waves_per_eu<D>() == 1;
   bf16x8 qf[Dm::KS], dof[Dm::KS], x[Dm::KS], o[Dm::KS];
   RowC<D> xq;
   float lse = 0.f;
@@ -372,7 +421,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
   }
   const float rq = rmsnorm_row_frags<D>(qf, x, gq, S ? nullptr : a.gains + D, a.c, a.eps, qvalid, g);
   if constexpr (!kLoadFirst) load_row_frags_raw<D>(dof, map.row(a.dout, a.dout1, qrow), qvalid, g);
-  if constexpr (keep_row_c<D>()) load_row_c<D>(xq, qptr, qvalid, g);
+  if constexpr (keep_row_c<D, dq_waves_per_eu<D>()>()) load_row_c<D>(xq, qptr, qvalid, g);
   if constexpr (!kLoadFirst) load_row_frags_raw<D>(o, map.row(a.out, a.out1, qrow), qvalid, g);
   float delta = 0.f;
 #pragma unroll
@@ -440,7 +489,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
   // dQn = scale * (dS Kr) times g_k in the joint form (its streamed key rows carry no gain)
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) acc[mt] *= a.scale;
-  if constexpr (!keep_row_c<D>()) load_row_c<D>(xq, qptr, qvalid, g);
+  if constexpr (!keep_row_c<D, dq_waves_per_eu<D>()>()) load_row_c<D>(xq, qptr, qvalid, g);
   uint16_t* qsrow = a.qs + (row0 + qrow) * D;
   if constexpr (!S) {
     rmsnorm_backward_row<D, false>(acc, xq, a.gains, a.gains + D, rq, qvalid, qvalid, map.row(a.dq, a.dq1, qrow),
@@ -458,7 +507,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
 }
 
 template <int D, bool S, bool V, bool W>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(dq_waves_per_eu<D>())))
 void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DqCfg<D>::template bytes<S>()];
   // (an item ends with its tile loop's barrier and, in the joint form, its epilogue does not touch
@@ -688,7 +737,7 @@ __device__ __forceinline__ void dkdv_tile_any(const __bf16* __restrict__ qt, con
                                               f32x16 (&dva)[Dims<D>::MT], f32x16 (&dka)[Dims<D>::MT], bool kvalid,
                                               int lane, const LaneOffs<D>& lo, int q0 = 0, int key = 0, int wl = 0,
                                               int wr = 0) {
-  if constexpr (bwd_waves_per_eu<D>() == 1)
+  if constexpr (dkdv_waves_per_eu<D>() == 1)
     dkdv_tile_staged<D, KMASK, WM>(qt, ot, sl, sd, kf, vf, dva, dka, kvalid, lane, lo, q0, key, wl, wr);
   else
     dkdv_tile<D, KMASK, WM>(qt, ot, sl, sd, kf, vf, dva, dka, kvalid, lane, q0, key, wl, wr);
@@ -744,11 +793,11 @@ __device__ __forceinline__ void dkdv_loop(const BwdArgs& a, char* smem, const Ro
   };
   const int ntiles = (L + kTile - 1) / kTile;
   LaneOffs<D> lo;
-  if constexpr (bwd_waves_per_eu<D>() == 1) lo.template init<LQ>(lane);
+  if constexpr (dkdv_waves_per_eu<D>() == 1) lo.template init<LQ>(lane);
   // Two waves per SIMD with a 4-buffer ring: two query tiles per barrier (each step computes tiles t and
   // t + 1 and loads t + 2 and t + 3 into the buffers the previous step used; 2 % faster at D = 64 than a
   // barrier per tile. The dq kernel measured slower that way and keeps one tile per barrier.)
-  constexpr bool PAIRS = NB == 4 && !W && bwd_waves_per_eu<D>() == 2;
+  constexpr bool PAIRS = NB == 4 && !W && dkdv_waves_per_eu<D>() == 2;
   if constexpr (W) {
     for (int i = 0; i < NB - 1 && tr.lo + i < tr.hi; ++i) issue(tr.lo + i, i);
   } else {
@@ -867,7 +916,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
       rmsnorm_row_frags<D>(kf, x, S ? gk : a.gains, S ? nullptr : a.gains + D, 1.f, a.eps, kvalid, g);
   load_row_frags_raw<D>(vf, S ? map.row(a.v, a.v1, key) : a.v + roff, kvalid, g);
   RowC<D> xk;
-  if constexpr (keep_row_c<D>()) load_row_c<D>(xk, S ? map.row(a.k, a.k1, key) : a.k + roff, kvalid, g);
+  if constexpr (keep_row_c<D, dkdv_waves_per_eu<D>()>()) load_row_c<D>(xk, S ? map.row(a.k, a.k1, key) : a.k + roff, kvalid, g);
 
   f32x16 dva[Dm::MT], dka[Dm::MT];
 #pragma unroll
@@ -910,7 +959,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
 #pragma unroll
   for (int mt = 0; mt < Dm::MT; ++mt) dka[mt] *= kLn2;
   if (kin) {
-    if constexpr (!keep_row_c<D>()) load_row_c<D>(xk, map.row(a.k, a.k1, key), kvalid, g);
+    if constexpr (!keep_row_c<D, dkdv_waves_per_eu<D>()>()) load_row_c<D>(xk, map.row(a.k, a.k1, key), kvalid, g);
     rmsnorm_backward_row<D, true>(dka, xk, gk, S ? nullptr : a.gains, rk, kvalid, true, S ? map.row(a.dk, a.dk1, key) : a.dk + roff,
                                   nullptr, 0.f, nullptr, g);
   } else {
@@ -930,7 +979,7 @@ __device__ __forceinline__ void dkdv_item(const BwdArgs& a, char* smem, int bh, 
 }
 
 template <int D, bool S, bool V, bool W>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>())))
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(dkdv_waves_per_eu<D>())))
 void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DkdvCfg<D>::template bytes<S>()];
   if constexpr (V) {

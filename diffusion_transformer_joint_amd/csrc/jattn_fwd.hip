@@ -6,13 +6,14 @@
 // this kernel never materialises):
 //   out_i = sum_j softmax_j(scale * <Qn_i, Kn_j>) v_j over valid keys j < n_b,  lse_i = log sum_j exp(.)
 //
-// One workgroup = 4 waves; each wave owns QT independent tiles of 32 queries (QT = 2 for D <= 64)
-// and streams all valid keys of the (batch, head) pair in tiles of 64 through LDS (double
-// buffered, one barrier per tile). Per 32-key half and query tile a wave computes S'^T = Kr Q'^T
+// One workgroup = 4 waves; each wave owns QT = 1 tile of 32 queries (the tile loop is written for
+// up to two) and streams all valid keys of the (batch, head) pair in tiles of 64 through a ring of
+// LDS buffers (one barrier per tile). Per 32-key half and query tile a wave computes S'^T = Kr Q'^T
 // (the result has the query on the lane), turns it into P in registers, and accumulates
 // O^T += V^T P^T with V^T read by ds_read_b64_tr_b16 straight from the row-major V tile. Each K and V
-// fragment read from LDS feeds QT MFMAs, and the QT query tiles give every wave independent MFMA
-// work to overlap with the softmax of the other tile.
+// fragment read from LDS feeds QT MFMAs. (Two tiles per wave at 256 rows per workgroup and two waves
+// per SIMD measured no faster than one tile at three waves per SIMD; the smaller blocks cut the
+// windowed forward's reach by a quarter.)
 //
 // Both gains go to the query side: Q' = bf16(q * r_q * g_q * g_k * scale * log2(e)) lives in
 // registers for the whole loop, and the staged key rows are only normalised, Kr = bf16(k * r_k), so
@@ -34,7 +35,7 @@
 //
 // Streaming: a prenorm kernel first writes Kr = bf16(k * r_k) (per (batch, head), contiguous rows)
 // to the workspace. The forward kernel then streams Kr and V tiles straight from memory into a ring
-// of LDS buffers with buffer loads that carry the LDS bit, issued two tiles ahead. Their range ends
+// of LDS buffers with buffer loads that carry the LDS bit, issued NB - 1 tiles ahead. Their range ends
 // at the last valid key, so later rows and padding columns land as zeros. No registers or VALU work
 // are spent on staging, and the tile body is straight-line code.
 #include <type_traits>
@@ -53,10 +54,11 @@ struct Fwd {
   using LK = Lay<D, kSwizzled>;  // key rows: row fragments (padded rows where D has no swizzle)
   // value rows: read transposed only (swizzled for D = 64, 128, else a pitch for transposed reads)
   using LV = Lay<D, (D == 64 || D == 128) ? kSwizzled : kTrRead>;
-  // ring depth: up to 64 padded columns, four buffers (stepped two tiles per barrier, below) where two
-  // workgroups per CU still fit in the 160 KB of LDS, else three; two for wider rows
+  // ring depth: three buffers for rows of up to 64 columns, two for wider rows; the workgroups per CU
+  // that fwd_waves_per_eu assumes must fit in the 160 KB of LDS
   static constexpr int BUF = (LK::ELEMS + LV::ELEMS) * 2;  // bytes per ring buffer
-  static constexpr int NB = Dims<D>::DM > 64 ? 2 : (4 * BUF + 16 <= 80 * 1024 ? 4 : 3);
+  static constexpr int NB = Dims<D>::DM > 64 ? 2 : 3;
+  static_assert(NB * BUF + 16 <= 160 * 1024 / fwd_waves_per_eu(D), "ring does not fit the workgroups per CU");
   static constexpr int STAGE = NB * (LK::ELEMS + LV::ELEMS) * 2;  // bytes
   static constexpr int BYTES = STAGE + 16;
   static_assert(QT == 1 || QT == 2, "query tiles per wave");
@@ -205,48 +207,7 @@ __device__ __forceinline__ void fwd_loop(FwdRing<D, S>& ring, const bf16x8 (&qf)
     ring_barrier<FwdRing<D, S>::PER, NB - 2>(ntiles - 2 - t);
     cur = cur + 1 == NB ? 0 : cur + 1;
   };
-  if constexpr (!W && NB == 4) {
-    // Two tiles per barrier: each step computes tiles t and t + 1 and loads t + 2 and t + 3 into the
-    // buffers the previous step used (a workgroup barrier per tile cost ~4 % of the forward at D = 64).
-    // The scheduling barrier keeps the two tiles' instructions apart (interleaved, they spill).
-    auto tile = [&](auto masked, int t) {
-      const int b = t & 3;
-      fwd_tile<D, BOUNDED, decltype(masked)::value>(ring.sk + b * LK::ELEMS, ring.sv + b * LV::ELEMS, qf, cinit, st,
-                                                    t * kTile, n, lane);
-    };
-    int t = 0;
-    for (; t + 1 < nfull; t += 2) {
-      if (t + 2 < ntiles) ring.issue(t + 2, (t + 2) & 3);
-      if (t + 3 < ntiles) ring.issue(t + 3, (t + 3) & 3);
-      if (active) {
-        tile(std::false_type{}, t);
-        __builtin_amdgcn_sched_barrier(0);
-        tile(std::false_type{}, t + 1);
-      }
-      stream_barrier<0>();
-    }
-    // The last one or two tiles are in their buffers already; a barrier after them frees the ring for
-    // the next item. The partial last tile is handled as in the one-tile form below.
-    const int t_rest = t;
-    if (t < nfull && active) tile(std::false_type{}, t);
-    if (nfull < ntiles) {
-      if constexpr (BOUNDED) {
-        if (active) tile(std::false_type{}, nfull);
-        const int m0 = n - nfull * kTile, g4 = 4 * (lane >> 5);
-        int nm = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) nm += min(4, max(0, 8 * k + g4 + 4 - m0));
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const float p0 = bf_lo(pack2(fast_exp2(-shift[qt]), 0.f));
-          st.lsum[qt] -= (float)nm * p0;
-        }
-      } else {
-        if (active) tile(std::true_type{}, nfull);
-      }
-    }
-    if (t_rest < ntiles) __syncthreads();
-  } else if constexpr (!W) {
+  if constexpr (!W) {
     for (int t = 0; t < nfull; ++t) step(std::false_type{}, t);
     if (nfull < ntiles) {
       if constexpr (BOUNDED) {
@@ -323,7 +284,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
   if constexpr (W) {
     for (int i = 0; i < Fwd<D>::NB - 1 && tr.lo + i < tr.hi; ++i) ring.issue(tr.lo + i, i);
   } else {
-    for (int t = 0; t < (Fwd<D>::NB == 4 ? 2 : Fwd<D>::NB - 1) && t < ring.ntiles; ++t) ring.issue(t, t);
+    for (int t = 0; t < Fwd<D>::NB - 1 && t < ring.ntiles; ++t) ring.issue(t, t);
   }
 
   // This wave's query rows, normalised with both gains (two-stream: its own stream's Q gain) and
@@ -426,7 +387,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
 }
 
 template <int D, bool S, bool V, bool W>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu(D)))) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Fwd<D>::BYTES];
   // one item per workgroup (a persistent grid measured slower here: the items are few and large),
   // numbered so that the row blocks of one (batch, head) pair share an XCD and its L2

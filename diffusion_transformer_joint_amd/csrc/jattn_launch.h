@@ -95,8 +95,9 @@ struct BwdArgs {
 };
 
 // Rows per workgroup, shared by the host-side grid and workspace sizing and the kernels.
-// Forward: 4 waves of 64 queries (two independent 32-query tiles per wave) for D <= 64, where the
-// register budget allows it; 4 waves of 32 queries otherwise.
+// Forward: 4 waves of 32 queries. (Two 32-query tiles per wave, 256 rows per workgroup at two waves
+// per SIMD, measured 3 % slower at D = 64 than one tile per wave at three: the smaller blocks also
+// split the 1101-row sequences more evenly and shorten the reach of a local window.)
 // The compiled head dims: every multiple of 8 from 32 to 128. X(D) is expanded once per head dim
 // (used for the switch statements that pick a kernel instantiation).
 #define JATTN_FOR_EACH_HEAD_DIM(X) JATTN_FOR_EACH_NARROW_HEAD_DIM(X) JATTN_FOR_EACH_WIDE_HEAD_DIM(X)
@@ -106,7 +107,10 @@ struct BwdArgs {
 #define JATTN_FOR_EACH_WIDE_HEAD_DIM(X) X(80) X(88) X(96) X(104) X(112) X(120) X(128)
 constexpr int kNarrowMaxD = 72;
 
-constexpr int fwd_rows_per_block(int D) { return D <= 64 ? 256 : 128; }
+constexpr int fwd_rows_per_block(int D) { return 128; }
+// Waves per SIMD the forward kernel's register allocation targets: three for D = 32 and 64, whose
+// key/value ring of three buffers leaves room for three workgroups per CU, else two.
+constexpr int fwd_waves_per_eu(int D) { return D == 32 || D == 64 ? 3 : 2; }
 // Backward: both kernels use workgroups of kBwdWaves waves of 32 rows.
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
