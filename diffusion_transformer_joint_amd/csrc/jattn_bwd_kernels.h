@@ -193,11 +193,11 @@ struct LaneOffs {
 // One 64-key tile: for both 32-key halves S'^T = Kr Q'^T and dP^T - Delta = V dO^T (lane = query),
 // dS^T = P * (dP - Delta) with P = exp2(S' - lse2), then dQn^T += Kr^T dS^T. MASKED: keys at or
 // past n are seeded with -inf (P = 0).
-// At two waves per SIMD the halves run one after the other (issuing the second half's row reads under
-// the first half's products measured no faster). At one wave per SIMD (D > 72) the tile runs in
-// stages, each LDS read a stage ahead of its use and the MFMAs of one stage under the VALU work of
-// another: rows(0) | scores(0) | transposed Kr of half 0, rows(1) | softmax(0) with scores(1) |
-// softmax(1) with dQ(0) | transposed Kr of half 1 | dQ(1). (B4 L2381 H24 D128: 611 -> 600 us.)
+// The halves run one after the other (issuing the second half's row reads under the first half's
+// products measured no faster). Above D = 64 the row fragments are read one k-step at a time (below).
+// (The staged order of the one-wave-per-SIMD dk/dv tile, with the MFMAs of one stage under another's
+// softmax, ran the dq kernel at one wave per SIMD in 577.5 us at B4 L2381 H24 D128; the streamed tile
+// at two waves per SIMD takes 524.0 us.)
 // W (local window): masked tiles also seed -inf outside the lane's query window qrow - wl .. qrow + wr.
 template <int D, bool MASKED, bool W = false>
 __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __bf16* __restrict__ vt,
@@ -255,49 +255,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* __restrict__ kt, const __b
       acc[mt] = mfma(lds_tr_frag<LK>(kt, h * 32 + 16, mt * 32, lane), f[h][1], acc[mt]);
     }
   };
-  if constexpr (dq_waves_per_eu<D>() == 1) {
-    LaneOffs<D> lo;
-    lo.template init<LK>(lane);
-    bf16x8 tk[MT][2];
-    const char* kb = reinterpret_cast<const char*>(kt);
-    auto trload = [&](int h) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int r0 = h * 32 + r * 16;
-          const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JATTN_LDS i16x4*)(kb + lo.tr[mt][0] + r0 * LK::PITCH * 2));
-          const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JATTN_LDS i16x4*)(kb + lo.tr[mt][1] + r0 * LK::PITCH * 2));
-          tk[mt][r] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, x), __builtin_bit_cast(bf16x4, y), 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-    };
-    auto accumulate2 = [&](int h) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[mt] = mfma(tk[mt][0], f[h][0], acc[mt]);
-        acc[mt] = mfma(tk[mt][1], f[h][1], acc[mt]);
-      }
-    };
-    rows(0);
-    __builtin_amdgcn_sched_barrier(0);
-    scores(0);
-    __builtin_amdgcn_sched_barrier(0);
-    trload(0);
-    rows(1);
-    __builtin_amdgcn_sched_barrier(0);
-    softmax(0);
-    scores(1);
-    interleave_mfma_valu<2 * KS, 3>();
-    __builtin_amdgcn_sched_barrier(0);
-    softmax(1);
-    accumulate2(0);
-    interleave_mfma_valu<2 * MT, 3>();
-    __builtin_amdgcn_sched_barrier(0);
-    trload(1);
-    __builtin_amdgcn_sched_barrier(0);
-    accumulate2(1);
-    __builtin_amdgcn_sched_barrier(0);
-  } else if constexpr (KS > 4) {
+  if constexpr (KS > 4) {
     // Two waves per SIMD at wide head dims: each key and value row fragment is read from LDS just
     // before its MFMAs instead of a whole half at once, and the MFMA seeds are formed in each tile from
     // the row statistics rather than kept through the loop, so that the tile fits beside the dQ
@@ -406,31 +364,24 @@ __device__ __forceinline__ void dq_item(const BwdArgs& a, char* smem, int bh, in
   // the row's Q gain (two-stream: its own stream's; the joint form folds both gains in)
   const float* gq = a.gains + (S ? map.block(qrow) * 2 * D : 0);
   const uint16_t* qptr = map.row(a.q, a.q1, qrow);
-  // One wave per SIMD: every row load is issued before any is used, one memory round trip for the
-  // set-up (dq 2 % faster at D = 128). At two waves the other wave covers the waits, and the rows
-  // held longer made dq 2 % slower at D = 64.
-  constexpr bool kLoadFirst = dq_waves_per_eu<D>() == 1;
+  // (The dO, O and LSE loads are issued after the Q normalisation: at two waves per SIMD the other wave
+  // covers the waits, and issuing every row load first held the rows longer and made dq 2 % slower at
+  // D = 64.)
   bf16x8 qf[Dm::KS], dof[Dm::KS], x[Dm::KS], o[Dm::KS];
   RowC<D> xq;
   float lse = 0.f;
   load_row_frags_raw<D>(x, qptr, qvalid, g);
-  if constexpr (kLoadFirst) {
-    load_row_frags_raw<D>(dof, map.row(a.dout, a.dout1, qrow), qvalid, g);
-    load_row_frags_raw<D>(o, map.row(a.out, a.out1, qrow), qvalid, g);
-    if (qvalid) lse = a.lse[row0 + qrow];
-  }
   const float rq = rmsnorm_row_frags<D>(qf, x, gq, S ? nullptr : a.gains + D, a.c, a.eps, qvalid, g);
-  if constexpr (!kLoadFirst) load_row_frags_raw<D>(dof, map.row(a.dout, a.dout1, qrow), qvalid, g);
+  load_row_frags_raw<D>(dof, map.row(a.dout, a.dout1, qrow), qvalid, g);
   if constexpr (keep_row_c<D, dq_waves_per_eu<D>()>()) load_row_c<D>(xq, qptr, qvalid, g);
-  if constexpr (!kLoadFirst) load_row_frags_raw<D>(o, map.row(a.out, a.out1, qrow), qvalid, g);
+  load_row_frags_raw<D>(o, map.row(a.out, a.out1, qrow), qvalid, g);
   float delta = 0.f;
 #pragma unroll
   for (int ks = 0; ks < Dm::KS; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) delta += (float)dof[ks][e] * (float)o[ks][e];
   delta += __shfl_xor(delta, 32);
-  if constexpr (!kLoadFirst)
-    if (qvalid) lse = a.lse[row0 + qrow];
+  if (qvalid) lse = a.lse[row0 + qrow];
   const float lse2 = lse * kLog2e;
   f32x16 cs, cp;
 #pragma unroll
