@@ -744,7 +744,8 @@ def bench_adaln(args, torch):
     torch.cuda.synchronize()
 
     K = args.steps
-    targs = {"qkv_gemm_kernel": "256, 128, 3", "dh_gemm_kernel": "256, 256, 2, false", "dw_gemm_kernel": "256, 256, 2"}
+    targs = {"qkv_gemm_kernel": "256, 256, 2, 8", "dh_gemm_kernel": "256, 256, 2, false, 8",
+             "dw_gemm_kernel": "256, 256, 2, 8"}
     label = lambda n: f"{n}<{targs[n]}>" if n in targs else n
     stages = [label(n) + " (fwd)" if n == "modulate_kernel" else label(n) for n in _lib.ADALN_FWD_STAGES]
     stages += [label(n) for n in _lib.ADALN_BWD_STAGES]
@@ -851,12 +852,13 @@ def bench_mlp(args, torch):
     K = args.steps
     # stage labels: kernel instantiations (the forward's fc and down projection and the backward's do
     # GEMM are the bf16-output GEMM; du the fp32-output one; d(hid) that one with the SwiGLU epilogue)
-    lab = {"fc_gemm": "qkv_gemm_kernel<256, 128, 3> (fc)", "modulate_kernel": "modulate_kernel",
-           "swiglu_gemm_kernel": "swiglu_gemm_kernel<256, 128, 3>", "down_gemm": "qkv_gemm_kernel<256, 128, 3> (down)",
-           "transpose_w_kernel": "transpose_w_kernel", "dhid_gemm": "dh_gemm_kernel<256, 256, 2, true> (d hid)",
-           "dw2_gemm": "dw_gemm_kernel<256, 256, 2> (dW2)", "du_gemm": "dh_gemm_kernel<256, 256, 2, false> (du)",
-           "dw12_gemm": "dw_gemm_kernel<256, 256, 2> (dW12)", "rows_bwd_kernel": "rows_bwd_kernel",
-           "do_gemm": "qkv_gemm_kernel<256, 128, 3> (do)", "dwfc_gemm": "dw_gemm_kernel<256, 256, 2> (dWfc)",
+    lab = {"fc_gemm": "qkv_gemm_kernel<256, 256, 2, 8> (fc)", "modulate_kernel": "modulate_kernel",
+           "swiglu_gemm_kernel": "swiglu_gemm_kernel<256, 256, 2, 8>",
+           "down_gemm": "qkv_gemm_kernel<256, 256, 2, 8> (down)", "transpose_w_kernel": "transpose_w_kernel",
+           "dhid_gemm": "dh_gemm_kernel<256, 256, 2, true, 8> (d hid)",
+           "dw2_gemm": "dw_gemm_kernel<256, 256, 2, 8> (dW2)", "du_gemm": "dh_gemm_kernel<256, 256, 2, false, 8> (du)",
+           "dw12_gemm": "dw_gemm_kernel<256, 256, 2, 8> (dW12)", "rows_bwd_kernel": "rows_bwd_kernel",
+           "do_gemm": "qkv_gemm_kernel<256, 256, 2, 8> (do)", "dwfc_gemm": "dw_gemm_kernel<256, 256, 2, 8> (dWfc)",
            "reductions": "reductions"}
     stages = [lab[n] for n in _lib.MLP_FWD_STAGES] + [lab[n] for n in _lib.MLP_BWD_STAGES]
     kern_ms, ms_fwd, ms_bwd = breakdown_pass(fwd, bwd, stages, nfs, min(K, 50), stream, new_event, handle)

@@ -16,7 +16,7 @@
 
 namespace jattn {
 
-constexpr int kGemmThreads = 256;  // 4 waves, 2 x 2 over the output tile
+constexpr int kGemmWaves = 8;      // waves per GEMM workgroup, 2 x 4 over the output tile
 constexpr int kGemmK = 64;         // contraction columns staged per step
 constexpr int kBwdRowChunk = 64;   // token rows of one sample per workgroup of the row backward
 
@@ -111,8 +111,8 @@ void launch_mod_reduce(const ReduceArgs& a, hipStream_t stream);
 void launch_w_reduce(const ReduceArgs& a, hipStream_t stream);
 
 // Output-tile sizes of the three GEMMs (MFMA-A rows x MFMA-B rows per workgroup).
-constexpr int kQkvMA = 256, kQkvMB = 128;
-constexpr int kSwigluMA = 256, kSwigluMB = 128;  // 128 columns j of W1 and the same 128 of W3 per tile
+constexpr int kQkvMA = 256, kQkvMB = 256;
+constexpr int kSwigluMA = 256, kSwigluMB = 256;  // 128 columns j of W1 and the same 128 of W3 per tile
 constexpr int kDhMA = 256, kDhMB = 256;
 constexpr int kDwMA = 256, kDwMB = 256;
 

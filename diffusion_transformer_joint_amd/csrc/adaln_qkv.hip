@@ -14,21 +14,27 @@
 // per chunk of rows, and dW = dY^T h is a split-K GEMM over the tokens; fixed-order reductions
 // finish the modulation, weight and bias gradients, so every result is deterministic.
 //
-// GEMM structure: 256 threads, the output tile split 2 x 2 over the 4 waves; both operands stream
+// GEMM structure: W waves split the output tile 2 x W/2 (A rows x B rows); both operands stream
 // through an LDS ring in 64-wide contraction steps with direct-to-LDS buffer loads (no VGPR
 // staging) into 64 x 64 swizzled sub-tiles; v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
 // Operands stored with the contraction index along memory rows (the weight gradient's) are read
 // with ds_read_b64_tr_b16. The buffer descriptors of a tile's sub-tiles are set up once per tile and
-// advanced per step with a pointer add: at one wave per SIMD every scalar instruction of the step
-// sits in the MFMA stream (recomputing them per step cost a third of the step).
+// advanced per step with a pointer add: every scalar instruction of the step sits in the MFMA stream
+// (recomputing them per step cost a third of the step at one wave per SIMD).
+// Every GEMM runs 256 x 256 output tiles on 8 waves, two per SIMD, each wave 128 x 64 of the tile:
+// a SIMD's second wave issues its MFMAs while the first waits on its LDS fragment reads, and the
+// larger tile reads each operand fewer times. Measured at C = 3072 against one wave per SIMD on the
+// same tile (and, for the projection and SwiGLU forward, 256 x 128 tiles): projection 681 -> 543 us,
+// dh 610 -> 513, dW 699 -> 590, SwiGLU forward 1172 -> 933, SwiGLU d(hid) 624 -> 529, on one box.
+// (8 waves on 256 x 128 tiles, one 32-row block of tokens per wave, made the SwiGLU forward slower:
+// 1339 us.)
 #include "adaln_launch.h"
 #include "jattn_device.h"
 
 namespace jattn {
 
 using GL = Lay<64, kSwizzled>;     // one 64 x 64 bf16 sub-tile: 128-byte rows, swizzled 16-byte chunks
-using GT = DirectTile<64, GL, 4>;  // its direct-to-LDS loads, shared by the 4 waves of a workgroup
-constexpr int kSub = GT::ALLOC;    // elements per sub-tile
+constexpr int kSub = DirectTile<64, GL, kGemmWaves>::ALLOC;  // elements per sub-tile in the LDS ring
 
 // The sub-tiles of one operand in one output tile, as wave-uniform scalar state: S sub-tiles of 64
 // operand rows each (rows mode: memory rows r0 + 64 s, contraction along the memory columns, through
@@ -121,19 +127,20 @@ struct OpStream {
 // columns; stored straight from there, every instruction writes 8 bytes into 32 different rows, and a
 // workgroup's lines stay partly written until its last iteration. With many tiles in flight per XCD
 // those lines were evicted half-written (3.7x the HBM writes of the SwiGLU outputs). So a wave
-// stages its 32 rows x 128 columns (bf16) in LDS, pitch kStgPitch elements, and moves whole rows with
-// 16-byte accesses: lane l takes row 4 it + l / 16, columns 8 (l % 16) .. + 7, 8 instructions per
-// 32 x 128 block.
-constexpr int kStgPitch = 136;                 // 128 columns + 8: 4-bank shift per row
-constexpr int kStgElems = 32 * kStgPitch;      // one 32 x 128 block
+// stages 32 rows x 64 columns (bf16) in LDS, pitch kStgPitch elements, and moves whole 128-byte row
+// pieces with 16-byte accesses: lane l takes row 8 it + l / 8, columns 8 (l % 8) .. + 7, 4
+// instructions per block. (A wave's 128 columns go through in two such halves: with 8 waves, blocks
+// of 32 x 128 would not fit beside each other in the ring.)
+constexpr int kStgPitch = 72;              // 64 columns + 8: rows stay 16-byte aligned, 4-bank shift per row
+constexpr int kStgElems = 32 * kStgPitch;  // one 32 x 64 block
 
-// Store block `stg` (32 rows x 128 columns) to out + row * rs + col0, rows < nrows, columns < ncols
-// (ncols - col0 a multiple of 8 or >= 128).
+// Store block `stg` (32 rows x 64 columns) to out + row * rs + col0, rows < nrows, columns < ncols
+// (ncols - col0 a multiple of 8 or >= 64).
 __device__ __forceinline__ void stg_store_rows(const __bf16* stg, uint16_t* __restrict__ out, size_t rs, int row0,
                                                int nrows, int col0, int ncols, int lane) {
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int r = 4 * it + (lane >> 4), c = 8 * (lane & 15);
+  for (int it = 0; it < 4; ++it) {
+    const int r = 8 * it + (lane >> 3), c = 8 * (lane & 7);
     if (row0 + r < nrows && col0 + c < ncols)
       *reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * rs + col0 + c) =
           *reinterpret_cast<const u32x4*>(stg + r * kStgPitch + c);
@@ -143,16 +150,16 @@ __device__ __forceinline__ void stg_store_rows(const __bf16* stg, uint16_t* __re
 // Load a block the same way (rows >= nrows or columns >= ncols read as zeros).
 __device__ __forceinline__ void stg_load_rows(__bf16* stg, const uint16_t* __restrict__ in, size_t rs, int row0,
                                               int nrows, int col0, int ncols, int lane) {
-  u32x4 v[8];
+  u32x4 v[4];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int r = 4 * it + (lane >> 4), c = 8 * (lane & 15);
+  for (int it = 0; it < 4; ++it) {
+    const int r = 8 * it + (lane >> 3), c = 8 * (lane & 7);
     v[it] = row0 + r < nrows && col0 + c < ncols ? *reinterpret_cast<const u32x4*>(in + (size_t)(row0 + r) * rs + col0 + c)
                                                    : (u32x4){0u, 0u, 0u, 0u};
   }
 #pragma unroll
-  for (int it = 0; it < 8; ++it)
-    *reinterpret_cast<u32x4*>(stg + (4 * it + (lane >> 4)) * kStgPitch + 8 * (lane & 15)) = v[it];
+  for (int it = 0; it < 4; ++it)
+    *reinterpret_cast<u32x4*>(stg + (8 * it + (lane >> 3)) * kStgPitch + 8 * (lane & 7)) = v[it];
 }
 
 // sigmoid(x) = 1 / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each): an IEEE
@@ -169,21 +176,24 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Main loop of one output tile: acc[i][j] += sum over k in [kbeg, kend) of A-block i x B-block j,
-// where the wave owns A rows wa * MA/2 + 32 i + [0, 32) and B rows wb * MB/2 + 32 j + [0, 32).
+// where the wave owns A rows wa * MA/2 + 32 i + [0, 32) and B rows wb * MB/WB + 32 j + [0, 32)
+// (W waves: 2 along A, WB = W/2 along B).
 // TR: operands stored with k along memory rows. NB: LDS stages in the ring.
 // (Member functions of a class template rather than function templates: the host-side pass of the
 // compiler rejects function templates that reach the LDS-DMA builtin from several kernels.)
-template <int MA, int MB, int NB, bool TR>
+template <int MA, int MB, int NB, bool TR, int W>
 struct GemmCore {
+  using GTW = DirectTile<64, GL, W>;
+  static constexpr int WB = W / 2;                      // waves along the B operand
   static constexpr int SA = MA / 64, SB = MB / 64;     // sub-tiles per operand and stage
   static constexpr int STAGE = (SA + SB) * kSub;        // elements per stage
-  static constexpr int IA = MA / 64, IB = MB / 64;      // 32-row MFMA blocks per wave and operand
-  static constexpr int PER = (SA + SB) * GT::PER_WAVE;  // loads each wave issues per stage
+  static constexpr int IA = MA / 64, IB = MB / (32 * WB);  // 32-row MFMA blocks per wave and operand
+  static constexpr int PER = (SA + SB) * GTW::PER_WAVE;  // loads each wave issues per stage
   static constexpr int BYTES = NB * STAGE * 2;
-  static_assert(GT::PER_WAVE == GT::MIN_PER_WAVE, "every wave issues the same number of loads");
+  static_assert(GTW::PER_WAVE == GTW::MIN_PER_WAVE, "every wave issues the same number of loads");
   static_assert(NB >= 2 && NB <= 5 && PER * (NB - 2) < 64, "ring depth");
 
-  GT ta, tb;
+  GTW ta, tb;
   int wa, wb, wave, lane;
 
   __device__ __forceinline__ GemmCore(const GemmProblem& p) {
@@ -216,7 +226,7 @@ struct GemmCore {
 #pragma unroll
     for (int i = 0; i < IA; ++i) fa[i] = frag(st, wa * (MA / 2) + 32 * i, ks);
 #pragma unroll
-    for (int j = 0; j < IB; ++j) fb[j] = frag(st + SA * kSub, wb * (MB / 2) + 32 * j, ks);
+    for (int j = 0; j < IB; ++j) fb[j] = frag(st + SA * kSub, wb * (MB / WB) + 32 * j, ks);
   }
 
   // One contraction step (4 k-steps of 16). The fragments of k-step ks + 1 are read before the
@@ -248,11 +258,11 @@ struct GemmCore {
 
 // Ring over the contraction steps [kbeg, kend) of one tile; `visit(stage, t)` runs after step t's
 // tile has landed and before its MFMAs (the weight-gradient kernel sums its B tiles there).
-template <int MA, int MB, int NB, bool TR, class Visit>
-__device__ __forceinline__ void gemm_tile(const GemmCore<MA, MB, NB, TR>& g, const GemmProblem& p, int m0, int n0,
+template <int MA, int MB, int NB, bool TR, int W, class Visit>
+__device__ __forceinline__ void gemm_tile(const GemmCore<MA, MB, NB, TR, W>& g, const GemmProblem& p, int m0, int n0,
                                           int kbeg, int kend, __bf16* __restrict__ lds,
-                                          f32x16 (&acc)[MA / 64][MB / 64], Visit& visit) {
-  using GC = GemmCore<MA, MB, NB, TR>;
+                                          f32x16 (&acc)[MA / 64][MB / (16 * W)], Visit& visit) {
+  using GC = GemmCore<MA, MB, NB, TR, W>;
 #pragma unroll
   for (int i = 0; i < GC::IA; ++i)
 #pragma unroll
@@ -465,11 +475,12 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModulateArgs a) {
 }
 
 // Forward GEMM: MFMA-A = W rows (output columns), MFMA-B = h rows (tokens), so each lane ends with
-// one token and runs of 4 consecutive output columns: 8-byte bf16 stores into q, k or v.
-template <int MA, int MB, int NB>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qkv_gemm_kernel(
+// one token and runs of 4 consecutive output columns, which go out through the row-staged blocks
+// into q, k or v (bf16).
+template <int MA, int MB, int NB, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4))) void qkv_gemm_kernel(
     GemmArgs a) {
-  using GC = GemmCore<MA, MB, NB, false>;
+  using GC = GemmCore<MA, MB, NB, false, W>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[GC::BYTES / 2];
   __shared__ __attribute__((aligned(16))) float bias_lds[MA];
   const TileId id(a);
@@ -489,28 +500,42 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
   f32x16 acc[GC::IA][GC::IB];
   NoVisit none;
   gemm_tile(g, p, m0, n0, 0, p.K, smem, acc, none);
+  // Row-staged epilogue, one 32-token x 64-column block at a time: the residual rows (if any) come
+  // in through the block, the sums replace them, and whole rows go out. A block never straddles q, k
+  // and v (the segment width is a multiple of 64).
+  static_assert(GC::IA == 4 && W * kStgElems * 2 <= GC::BYTES, "128 columns and one staged block per wave");
+  __bf16* stg = smem + g.wave * kStgElems;  // (the ring's last barrier has passed)
+  const int tl = g.lane & 31;
 #pragma unroll
-  for (int i = 0; i < GC::IA; ++i) {
+  for (int j = 0; j < GC::IB; ++j) {
+    const int t0 = n0 + g.wb * (MB / GC::WB) + 32 * j;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = m0 + g.wa * (MA / 2) + 32 * i + 8 * q + 4 * (g.lane >> 5);
-      if (n >= p.M) continue;
-      const int t = n >= 2 * p.out_seg ? 2 : n >= p.out_seg ? 1 : 0, c = n - t * p.out_seg;
+    for (int h = 0; h < 2; ++h) {
+      const int nb = m0 + g.wa * (MA / 2) + 64 * h;  // the block's first output column (wave-uniform)
+      if (t0 >= p.N || nb >= p.M) continue;
+      const int t = nb >= 2 * p.out_seg ? 2 : nb >= p.out_seg ? 1 : 0, c0 = nb - t * p.out_seg;
       uint16_t* out = static_cast<uint16_t*>(t == 0 ? p.out[0] : t == 1 ? p.out[1] : p.out[2]);
-      const int nl = g.wa * (MA / 2) + 32 * i + 8 * q + 4 * (g.lane >> 5);
-      const f32x4 b = p.bias ? *reinterpret_cast<const f32x4*>(bias_lds + nl) : (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < GC::IB; ++j) {
-        const int tok = n0 + g.wb * (MB / 2) + 32 * j + (g.lane & 31);
-        if (tok < p.N) {
-          const f32x16& v = acc[i][j];
-          const size_t o = (size_t)tok * p.out_seg + c;
-          float r[4] = {0.f, 0.f, 0.f, 0.f};
-          if (p.aux) unpack4(*reinterpret_cast<const u32x2*>(p.aux + o), r);  // the residual (same layout)
-          *reinterpret_cast<u32x2*>(out + o) = (u32x2){pack2(v[4 * q] + b[0] + r[0], v[4 * q + 1] + b[1] + r[1]),
-                                                       pack2(v[4 * q + 2] + b[2] + r[2], v[4 * q + 3] + b[3] + r[3])};
-        }
+      if (p.aux) {  // the residual (same layout as the output)
+        stg_load_rows(stg, p.aux, p.out_seg, t0, p.N, c0, p.out_seg, g.lane);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are visible to its lanes
       }
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int jl = 32 * ii + 8 * q + 4 * (g.lane >> 5);  // column within the block
+          const f32x4 b = p.bias ? *reinterpret_cast<const f32x4*>(bias_lds + g.wa * (MA / 2) + 64 * h + jl)
+                                 : (f32x4){0.f, 0.f, 0.f, 0.f};
+          u32x2* ps = reinterpret_cast<u32x2*>(stg + tl * kStgPitch + jl);
+          float r[4] = {0.f, 0.f, 0.f, 0.f};
+          if (p.aux) unpack4(*ps, r);
+          const f32x16& v = acc[2 * h + ii][j];
+          *ps = (u32x2){pack2(v[4 * q] + b[0] + r[0], v[4 * q + 1] + b[1] + r[1]),
+                        pack2(v[4 * q + 2] + b[2] + r[2], v[4 * q + 3] + b[3] + r[3])};
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      stg_store_rows(stg, out, p.out_seg, t0, p.N, c0, p.out_seg, g.lane);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // (the next block overwrites this one)
     }
   }
 }
@@ -520,12 +545,12 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
 // so a and g of one (token, j) sit in the same lane and register of the two waves of a pair; the
 // wa = 1 waves hand their accumulators over through LDS. Writes [a | g] (bf16 [T, 2F], kept for the
 // backward) and hid (bf16 [T, F]).
-template <int MA, int MB, int NB>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void swiglu_gemm_kernel(
+template <int MA, int MB, int NB, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4))) void swiglu_gemm_kernel(
     GemmArgs a) {
-  using GC = GemmCore<MA, MB, NB, false>;
+  using GC = GemmCore<MA, MB, NB, false, W>;
   constexpr int H = MA / 2;  // columns j per tile
-  static_assert(GC::IA * GC::IB * 16 * 64 * 2 * 4 <= GC::BYTES, "LDS hand-over fits the ring");
+  static_assert(GC::IA * 16 * 64 * W * 4 <= GC::BYTES, "LDS hand-over fits the ring");
   __shared__ __attribute__((aligned(16))) __bf16 smem[GC::BYTES / 2];
   __shared__ __attribute__((aligned(16))) float bias_lds[MA];  // [b1 of the tile | b3 of the tile]
   const TileId id(a);
@@ -533,7 +558,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
   const GemmProblem p = pick(a, id.s != 0);
   const GC g(p);
   const int Fh = p.pair_off, j0 = id.tm * H, n0 = id.tn * MB;
-  if (p.bias) {  // wave w: 64 bias values, b1 for w < 2, b3 for w >= 2 (issued before the ring's loads)
+  if (p.bias && g.wave < 4) {  // wave w < 4: 64 bias values, b1 for w < 2, b3 for w >= 2 (before the ring's loads)
     const int jw = j0 + 64 * (g.wave & 1), nb = max(0, min(64, Fh - jw));
     lds_load_dwords(make_rsrc(p.bias + (g.wave < 2 ? 0 : Fh) + jw, (uint32_t)__builtin_amdgcn_readfirstlane(nb * 4)),
                     bias_lds + 64 * g.wave, (uint32_t)g.lane * 4u);
@@ -543,8 +568,8 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
   gemm_tile(g, p, j0, n0, 0, p.K, smem, acc, none);
   // Hand-over: each wave of a pair (same wb) finishes token block jb = wa of the pair's IB = 2 blocks;
   // it gives its accumulators of the other block to its partner through LDS.
-  static_assert(GC::IB == 2, "one token block per wave of a pair");
-  static_assert(4 * 3 * kStgElems * 2 <= GC::BYTES, "three staged 32 x 128 blocks per wave");
+  static_assert(GC::IB == 2 && GC::IA == 4, "two token blocks and 128 columns per wave");
+  static_assert(MA == 256 && W == 8, "tile of 128 columns j; 8 waves (the hand-over slots)");
   float* xch = reinterpret_cast<float*>(smem);  // (the ring's last barrier has passed)
   const int give = 1 - g.wa;
 #pragma unroll
@@ -560,38 +585,47 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
 #pragma unroll
     for (int e = 0; e < 16; ++e) other[i][e] = xch[(((g.wb * 2 + partner) * GC::IA + i) * 16 + e) * 64 + g.lane];
   __syncthreads();  // (every hand-over read is done: the LDS now holds the staged output blocks)
-  __bf16* s_a = smem + g.wave * 3 * kStgElems;
-  __bf16* s_g = s_a + kStgElems;
-  __bf16* s_h = s_g + kStgElems;
-#pragma unroll
-  for (int i = 0; i < GC::IA; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int jl = 32 * i + 8 * q + 4 * (g.lane >> 5), tl = g.lane & 31;
-      const f32x4 b1 = p.bias ? *reinterpret_cast<const f32x4*>(bias_lds + jl) : (f32x4){0.f, 0.f, 0.f, 0.f};
-      const f32x4 b3 = p.bias ? *reinterpret_cast<const f32x4*>(bias_lds + H + jl) : (f32x4){0.f, 0.f, 0.f, 0.f};
-      float av[4], gv[4], hv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // a (W1 rows) is held by the wa = 0 wave, g (W3 rows) by the wa = 1 wave
-        const float mine = jb == 0 ? acc[i][0][4 * q + e] : acc[i][1][4 * q + e];
-        const float oth = other[i][4 * q + e];
-        av[e] = (g.wa == 0 ? mine : oth) + b1[e];
-        gv[e] = (g.wa == 0 ? oth : mine) + b3[e];
-        hv[e] = av[e] * sigmoid_fast(av[e]) * gv[e];
-      }
-      const int o = tl * kStgPitch + jl;
-      *reinterpret_cast<u32x2*>(s_a + o) = (u32x2){pack2(av[0], av[1]), pack2(av[2], av[3])};
-      *reinterpret_cast<u32x2*>(s_g + o) = (u32x2){pack2(gv[0], gv[1]), pack2(gv[2], gv[3])};
-      *reinterpret_cast<u32x2*>(s_h + o) = (u32x2){pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
-    }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staged blocks are complete
-  const int t0 = n0 + g.wb * (MB / 2) + 32 * jb;
+  // The wave's 32 tokens x 128 columns of a, g and hid leave through staged blocks, 64 columns at a time.
+  constexpr int HALVES = 2, COLS = 64, P = kStgPitch, ELEMS = kStgElems;
+  static_assert(W * 3 * ELEMS * 2 <= GC::BYTES, "three staged blocks per wave");
+  __bf16* s_a = smem + g.wave * 3 * ELEMS;
+  __bf16* s_g = s_a + ELEMS;
+  __bf16* s_h = s_g + ELEMS;
+  const int t0 = n0 + g.wb * (MB / GC::WB) + 32 * jb;
   uint16_t* ag = static_cast<uint16_t*>(p.out[0]);
   uint16_t* hid = static_cast<uint16_t*>(p.out[1]);
-  stg_store_rows(s_a, ag, 2 * (size_t)Fh, t0, p.N, j0, Fh, g.lane);
-  stg_store_rows(s_g, ag + Fh, 2 * (size_t)Fh, t0, p.N, j0, Fh, g.lane);
-  stg_store_rows(s_h, hid, (size_t)Fh, t0, p.N, j0, Fh, g.lane);
+#pragma unroll
+  for (int h = 0; h < HALVES; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < GC::IA / HALVES; ++ii)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = (GC::IA / HALVES) * h + ii;
+        const int jl = 32 * i + 8 * q + 4 * (g.lane >> 5), tl = g.lane & 31;  // jl: column within the tile
+        const f32x4 b1 = p.bias ? *reinterpret_cast<const f32x4*>(bias_lds + jl) : (f32x4){0.f, 0.f, 0.f, 0.f};
+        const f32x4 b3 = p.bias ? *reinterpret_cast<const f32x4*>(bias_lds + H + jl) : (f32x4){0.f, 0.f, 0.f, 0.f};
+        float av[4], gv[4], hv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // a (W1 rows) is held by the wa = 0 wave, g (W3 rows) by the wa = 1 wave
+          const float mine = jb == 0 ? acc[i][0][4 * q + e] : acc[i][1][4 * q + e];
+          const float oth = other[i][4 * q + e];
+          av[e] = (g.wa == 0 ? mine : oth) + b1[e];
+          gv[e] = (g.wa == 0 ? oth : mine) + b3[e];
+          hv[e] = av[e] * sigmoid_fast(av[e]) * gv[e];
+        }
+        const int o = tl * P + jl - COLS * h;
+        *reinterpret_cast<u32x2*>(s_a + o) = (u32x2){pack2(av[0], av[1]), pack2(av[2], av[3])};
+        *reinterpret_cast<u32x2*>(s_g + o) = (u32x2){pack2(gv[0], gv[1]), pack2(gv[2], gv[3])};
+        *reinterpret_cast<u32x2*>(s_h + o) = (u32x2){pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staged blocks are complete
+    const int c0 = j0 + COLS * h;
+    stg_store_rows(s_a, ag, 2 * (size_t)Fh, t0, p.N, c0, Fh, g.lane);
+    stg_store_rows(s_g, ag + Fh, 2 * (size_t)Fh, t0, p.N, c0, Fh, g.lane);
+    stg_store_rows(s_h, hid, (size_t)Fh, t0, p.N, c0, Fh, g.lane);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // (the next half's writes overwrite these LDS blocks)
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -617,10 +651,10 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(TransposeArgs a) {
 // dh = dY W as MFMA-A = W^T rows (channels), MFMA-B = dY rows (tokens; k runs over the three tensors
 // dq, dk, dv): fp32 stores of 4 consecutive channels per lane.
 // SWIGLU: the MLP's d(hid) GEMM, whose epilogue applies the SwiGLU backward (p.aux = the forward's [a | g]).
-template <int MA, int MB, int NB, bool SWIGLU>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dh_gemm_kernel(
+template <int MA, int MB, int NB, bool SWIGLU, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4))) void dh_gemm_kernel(
     GemmArgs a) {
-  using GC = GemmCore<MA, MB, NB, false>;
+  using GC = GemmCore<MA, MB, NB, false, W>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[GC::BYTES / 2];
   const TileId id(a);
   if (!id.ok) return;
@@ -632,26 +666,31 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
   gemm_tile(g, p, m0, n0, 0, p.K, smem, acc, none);
   if constexpr (SWIGLU) {  // acc = d(hid)[tok][j]; with the forward's a and g, write [da | dg]
     // Per block of 32 tokens: the a and g rows go through this wave's LDS blocks (coalesced loads),
-    // da and dg replace them in place, and whole rows go back out (see the row-staged epilogue I/O).
-    static_assert(MA / 2 == 128 && 4 * 2 * kStgElems * 2 <= GC::BYTES, "two staged 32 x 128 blocks per wave");
+    // da and dg replace them in place, and whole rows go back out (see the row-staged epilogue I/O),
+    // 64 columns at a time.
+    constexpr int HALVES = 2, COLS = 64, P = kStgPitch, ELEMS = kStgElems;
+    static_assert(MA / 2 == 128 && W * 2 * ELEMS * 2 <= GC::BYTES, "two staged blocks per wave");
     const int Fh = p.M;
     uint16_t* __restrict__ dag = static_cast<uint16_t*>(p.out[0]);
-    __bf16* sa = smem + g.wave * 2 * kStgElems;  // (the ring's last barrier has passed)
-    __bf16* sg = sa + kStgElems;
-    const int jw = m0 + g.wa * (MA / 2);  // this wave's first column j
+    __bf16* sa = smem + g.wave * 2 * ELEMS;  // (the ring's last barrier has passed)
+    __bf16* sg = sa + ELEMS;
 #pragma unroll
-    for (int jb = 0; jb < GC::IB; ++jb) {
-      const int t0 = n0 + g.wb * (MB / 2) + 32 * jb;
+    for (int jb = 0; jb < GC::IB; ++jb)
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h) {
+      const int t0 = n0 + g.wb * (MB / GC::WB) + 32 * jb;
+      const int jw = m0 + g.wa * (MA / 2) + COLS * h;  // the block's first column j
       stg_load_rows(sa, p.aux, 2 * (size_t)Fh, t0, p.N, jw, Fh, g.lane);
       stg_load_rows(sg, p.aux + Fh, 2 * (size_t)Fh, t0, p.N, jw, Fh, g.lane);
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are visible to its lanes
 #pragma unroll
-      for (int i = 0; i < GC::IA; ++i)
+      for (int ii = 0; ii < GC::IA / HALVES; ++ii)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int jl = 32 * i + 8 * q + 4 * (g.lane >> 5), tl = g.lane & 31;
-          u32x2* pa = reinterpret_cast<u32x2*>(sa + tl * kStgPitch + jl);
-          u32x2* pg = reinterpret_cast<u32x2*>(sg + tl * kStgPitch + jl);
+          const int i = (GC::IA / HALVES) * h + ii;
+          const int jl = 32 * ii + 8 * q + 4 * (g.lane >> 5), tl = g.lane & 31;  // jl: column within the block
+          u32x2* pa = reinterpret_cast<u32x2*>(sa + tl * P + jl);
+          u32x2* pg = reinterpret_cast<u32x2*>(sg + tl * P + jl);
           float av[4], gv[4], da[4], dg[4];
           unpack4(*pa, av);
           unpack4(*pg, gv);
@@ -681,7 +720,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
         if (c >= p.M) continue;
 #pragma unroll
         for (int j = 0; j < GC::IB; ++j) {
-          const int tok = n0 + g.wb * (MB / 2) + 32 * j + (g.lane & 31);
+          const int tok = n0 + g.wb * (MB / GC::WB) + 32 * j + (g.lane & 31);
           if (tok < p.N) {
             const f32x16& v = acc[i][j];
             *reinterpret_cast<f32x4*>(dh + (size_t)tok * p.out_seg + c) =
@@ -694,9 +733,9 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
 
 // Column sums of the B tiles (dY over the tokens, for the bias gradient), in the workgroups of
 // A-tile 0 only: thread t sums 8 consecutive columns over rows t / (MB/8) + (256 / (MB/8)) * i.
-template <int MB>
+template <int MB, int THREADS>
 struct ColSumVisit {
-  static constexpr int CH = MB / 8, RG = kGemmThreads / CH;
+  static constexpr int CH = MB / 8, RG = THREADS / CH;
   float acc[8];  // this thread's 8 column sums
   int sb_off;    // element offset of the B operand inside a stage
   bool on;
@@ -717,11 +756,11 @@ struct ColSumVisit {
 // both read transposed from [64 tokens x 64] sub-tiles. Each split writes its fp32 partial
 // [splits, 3C, C] (lane = output column, 4 consecutive channels per store) and, in the workgroups
 // of A-tile 0, its partial column sums of dY.
-template <int MA, int MB, int NB>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dw_gemm_kernel(
+template <int MA, int MB, int NB, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4))) void dw_gemm_kernel(
     GemmArgs a) {
-  using GC = GemmCore<MA, MB, NB, true>;
-  using CS = ColSumVisit<MB>;
+  using GC = GemmCore<MA, MB, NB, true, W>;
+  using CS = ColSumVisit<MB, 64 * W>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[GC::BYTES / 2];
   const TileId id(a);
   if (!id.ok) return;
@@ -742,7 +781,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
       if (c >= p.M) continue;
 #pragma unroll
       for (int j = 0; j < GC::IB; ++j) {
-        const int n = n0 + g.wb * (MB / 2) + 32 * j + (g.lane & 31);
+        const int n = n0 + g.wb * (MB / GC::WB) + 32 * j + (g.lane & 31);
         if (n < p.N) {
           const f32x16& v = acc[i][j];
           *reinterpret_cast<f32x4*>(part + (size_t)n * p.M + c) = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
@@ -954,7 +993,7 @@ __global__ __launch_bounds__(256) void w_reduce_kernel(ReduceArgs a) {
 // ---------------------------------------------------------------------------------------------
 // Launchers
 
-constexpr int kQkvNB = 3, kDhNB = 2, kDwNB = 2;
+constexpr int kQkvNB = 2, kSwigluNB = 2, kDhNB = 2, kDwNB = 2;
 
 // (Every launcher returns without a launch when there is no work: a grid of 0 workgroups is an
 // invalid launch configuration.)
@@ -973,25 +1012,25 @@ void launch_modulate(const ModulateArgs& a, hipStream_t stream) {
 
 void launch_qkv_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.ntiles == 0) return;
-  hipLaunchKernelGGL((qkv_gemm_kernel<kQkvMA, kQkvMB, kQkvNB>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0,
+  hipLaunchKernelGGL((qkv_gemm_kernel<kQkvMA, kQkvMB, kQkvNB, kGemmWaves>), dim3(gemm_grid(a)), dim3(64 * kGemmWaves), 0,
                      stream, a);
 }
 
 void launch_dh_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.ntiles == 0) return;
-  hipLaunchKernelGGL((dh_gemm_kernel<kDhMA, kDhMB, kDhNB, false>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0, stream,
+  hipLaunchKernelGGL((dh_gemm_kernel<kDhMA, kDhMB, kDhNB, false, kGemmWaves>), dim3(gemm_grid(a)), dim3(64 * kGemmWaves), 0, stream,
                      a);
 }
 
 void launch_dhid_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.ntiles == 0) return;
-  hipLaunchKernelGGL((dh_gemm_kernel<kDhMA, kDhMB, kDhNB, true>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0, stream,
+  hipLaunchKernelGGL((dh_gemm_kernel<kDhMA, kDhMB, kDhNB, true, kGemmWaves>), dim3(gemm_grid(a)), dim3(64 * kGemmWaves), 0, stream,
                      a);
 }
 
 void launch_dw_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.ntiles == 0) return;
-  hipLaunchKernelGGL((dw_gemm_kernel<kDwMA, kDwMB, kDwNB>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0, stream,
+  hipLaunchKernelGGL((dw_gemm_kernel<kDwMA, kDwMB, kDwNB, kGemmWaves>), dim3(gemm_grid(a)), dim3(64 * kGemmWaves), 0, stream,
                      a);
 }
 
@@ -1002,7 +1041,7 @@ void launch_transpose_w(const TransposeArgs& a, hipStream_t stream) {
 
 void launch_swiglu_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.ntiles == 0) return;
-  hipLaunchKernelGGL((swiglu_gemm_kernel<kSwigluMA, kSwigluMB, kQkvNB>), dim3(gemm_grid(a)), dim3(kGemmThreads), 0,
+  hipLaunchKernelGGL((swiglu_gemm_kernel<kSwigluMA, kSwigluMB, kSwigluNB, kGemmWaves>), dim3(gemm_grid(a)), dim3(64 * kGemmWaves), 0,
                      stream, a);
 }
 
