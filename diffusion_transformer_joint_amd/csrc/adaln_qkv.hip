@@ -147,19 +147,29 @@ __device__ __forceinline__ void stg_store_rows(const __bf16* stg, uint16_t* __re
   }
 }
 
-// Load a block the same way (rows >= nrows or columns >= ncols read as zeros).
-__device__ __forceinline__ void stg_load_rows(__bf16* stg, const uint16_t* __restrict__ in, size_t rs, int row0,
-                                              int nrows, int col0, int ncols, int lane) {
-  u32x4 v[4];
+// Load a block the same way (rows >= nrows or columns >= ncols read as zeros), in two parts: the
+// global loads into registers, then their LDS writes, so that a caller can issue the loads early.
+__device__ __forceinline__ void stg_fetch_rows(u32x4 (&v)[4], const uint16_t* __restrict__ in, size_t rs, int row0,
+                                               int nrows, int col0, int ncols, int lane) {
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int r = 8 * it + (lane >> 3), c = 8 * (lane & 7);
     v[it] = row0 + r < nrows && col0 + c < ncols ? *reinterpret_cast<const u32x4*>(in + (size_t)(row0 + r) * rs + col0 + c)
                                                    : (u32x4){0u, 0u, 0u, 0u};
   }
+}
+
+__device__ __forceinline__ void stg_put_rows(__bf16* stg, const u32x4 (&v)[4], int lane) {
 #pragma unroll
   for (int it = 0; it < 4; ++it)
     *reinterpret_cast<u32x4*>(stg + (8 * it + (lane >> 3)) * kStgPitch + 8 * (lane & 7)) = v[it];
+}
+
+__device__ __forceinline__ void stg_load_rows(__bf16* stg, const uint16_t* __restrict__ in, size_t rs, int row0,
+                                              int nrows, int col0, int ncols, int lane) {
+  u32x4 v[4];
+  stg_fetch_rows(v, in, rs, row0, nrows, col0, ncols, lane);
+  stg_put_rows(stg, v, lane);
 }
 
 // sigmoid(x) = 1 / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each): an IEEE
@@ -661,6 +671,16 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W
   const GemmProblem p = pick(a, id.s != 0);
   const GC g(p);
   const int m0 = id.tm * MA, n0 = id.tn * MB;
+  // SWIGLU: the epilogue's blocks k = 0..3 are (32-token block jb, 64-column half h) = (k / 2, k % 2);
+  // the a and g rows of block 0 are loaded before the main loop, and each later block's while the
+  // block before it is processed.
+  auto blk_t0 = [&](int k) { return n0 + g.wb * (MB / GC::WB) + 32 * (k >> 1); };
+  auto blk_j0 = [&](int k) { return m0 + g.wa * (MA / 2) + 64 * (k & 1); };
+  u32x4 ra[4], rg[4];
+  if constexpr (SWIGLU) {
+    stg_fetch_rows(ra, p.aux, 2 * (size_t)p.M, blk_t0(0), p.N, blk_j0(0), p.M, g.lane);
+    stg_fetch_rows(rg, p.aux + p.M, 2 * (size_t)p.M, blk_t0(0), p.N, blk_j0(0), p.M, g.lane);
+  }
   f32x16 acc[GC::IA][GC::IB];
   NoVisit none;
   gemm_tile(g, p, m0, n0, 0, p.K, smem, acc, none);
@@ -668,20 +688,21 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W
     // Per block of 32 tokens: the a and g rows go through this wave's LDS blocks (coalesced loads),
     // da and dg replace them in place, and whole rows go back out (see the row-staged epilogue I/O),
     // 64 columns at a time.
-    constexpr int HALVES = 2, COLS = 64, P = kStgPitch, ELEMS = kStgElems;
-    static_assert(MA / 2 == 128 && W * 2 * ELEMS * 2 <= GC::BYTES, "two staged blocks per wave");
+    constexpr int HALVES = 2, P = kStgPitch, ELEMS = kStgElems;
+    static_assert(MA / 2 == 128 && GC::IB == 2 && W * 2 * ELEMS * 2 <= GC::BYTES, "two staged blocks per wave");
     const int Fh = p.M;
     uint16_t* __restrict__ dag = static_cast<uint16_t*>(p.out[0]);
     __bf16* sa = smem + g.wave * 2 * ELEMS;  // (the ring's last barrier has passed)
     __bf16* sg = sa + ELEMS;
 #pragma unroll
-    for (int jb = 0; jb < GC::IB; ++jb)
-#pragma unroll
-    for (int h = 0; h < HALVES; ++h) {
-      const int t0 = n0 + g.wb * (MB / GC::WB) + 32 * jb;
-      const int jw = m0 + g.wa * (MA / 2) + COLS * h;  // the block's first column j
-      stg_load_rows(sa, p.aux, 2 * (size_t)Fh, t0, p.N, jw, Fh, g.lane);
-      stg_load_rows(sg, p.aux + Fh, 2 * (size_t)Fh, t0, p.N, jw, Fh, g.lane);
+    for (int k = 0; k < 4; ++k) {
+      const int jb = k >> 1, h = k & 1, t0 = blk_t0(k), jw = blk_j0(k);  // jw: the block's first column j
+      stg_put_rows(sa, ra, g.lane);
+      stg_put_rows(sg, rg, g.lane);
+      if (k < 3) {
+        stg_fetch_rows(ra, p.aux, 2 * (size_t)Fh, blk_t0(k + 1), p.N, blk_j0(k + 1), Fh, g.lane);
+        stg_fetch_rows(rg, p.aux + Fh, 2 * (size_t)Fh, blk_t0(k + 1), p.N, blk_j0(k + 1), Fh, g.lane);
+      }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are visible to its lanes
 #pragma unroll
       for (int ii = 0; ii < GC::IA / HALVES; ++ii)
