@@ -197,9 +197,8 @@ def main():
                     lse.data_ptr(), dout.data_ptr(), B, L, total, H, D, scale, eps, dq.data_ptr(), dk.data_ptr(),
                     dv.data_ptr(), dg.data_ptr(), ws.data_ptr(), ws_bytes, fws.data_ptr())
 
-        def fwd(events=None):
-            _lib.check("jattn_fwd_varlen", lib.jattn_fwd_varlen(*fwd_args, events, 0 if events is None else
-                                                                len(_lib.FWD_STAGES), sp))
+        def fwd(events=None, n=len(_lib.FWD_STAGES)):
+            _lib.check("jattn_fwd_varlen", lib.jattn_fwd_varlen(*fwd_args, events, 0 if events is None else n, sp))
 
         def bwd(events=None, n=len(_lib.BWD_STAGES)):
             _lib.check("jattn_bwd_varlen", lib.jattn_bwd_varlen(*bwd_args, events, 0 if events is None else n, sp))
@@ -219,18 +218,17 @@ def main():
             fwd_w = fwd_args[:11] + (wl, wr) + fwd_args[11:-1]
             bwd_w = bwd_args[:14] + (wl, wr) + bwd_args[14:-1]
 
-            def fwd(events=None):
-                _lib.check("jattn_fwd_window", lib.jattn_fwd_window(*fwd_w, events, 0 if events is None else
-                                                                    len(_lib.FWD_STAGES), sp))
+            def fwd(events=None, n=len(_lib.FWD_STAGES)):
+                _lib.check("jattn_fwd_window", lib.jattn_fwd_window(*fwd_w, events, 0 if events is None else n, sp))
 
             def bwd(events=None, n=len(_lib.BWD_STAGES)):
                 _lib.check("jattn_bwd_window", lib.jattn_bwd_window(*bwd_w, events, 0 if events is None else n, sp))
         else:
-            def fwd(events=None):
+            def fwd(events=None, n=len(_lib.FWD_STAGES)):
                 if events is None:
                     _lib.check("jattn_fwd", lib.jattn_fwd(*fwd_args))
                 else:
-                    _lib.check("jattn_fwd_ex", lib.jattn_fwd_ex(*fwd_args[:-1], events, len(_lib.FWD_STAGES), sp))
+                    _lib.check("jattn_fwd_ex", lib.jattn_fwd_ex(*fwd_args[:-1], events, n, sp))
 
             def bwd(events=None, n=len(_lib.BWD_STAGES)):
                 if events is None:
@@ -252,9 +250,8 @@ def main():
                     pp["dout"].arg, B, w.n_img, w.n_txt, H, D, scale, eps, pp["dq"].arg, pp["dk"].arg, pp["dv"].arg,
                     dg.data_ptr(), ws.data_ptr(), ws_bytes, fws.data_ptr())
 
-        def fwd(events=None):
-            _lib.check("jattn_fwd_streams", lib.jattn_fwd_streams(*fwd_args, events, 0 if events is None else
-                                                                  len(_lib.FWD_STAGES), sp))
+        def fwd(events=None, n=len(_lib.FWD_STAGES)):
+            _lib.check("jattn_fwd_streams", lib.jattn_fwd_streams(*fwd_args, events, 0 if events is None else n, sp))
 
         def bwd(events=None, n=len(_lib.BWD_STAGES)):
             _lib.check("jattn_bwd_streams", lib.jattn_bwd_streams(*bwd_args, events, 0 if events is None else n, sp))
@@ -279,7 +276,7 @@ def main():
     torch.cuda.synchronize()
 
     def handle(evs):
-        arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+        arr = (ctypes.c_void_p * len(evs))(*[None if e is None else e.cuda_event for e in evs])
         return arr, ctypes.cast(arr, ctypes.c_void_p)
 
     K = args.steps
@@ -293,25 +290,7 @@ def main():
     nf = len(_lib.FWD_STAGES)
     dq_key, dkdv_key = f"bwd_dq_kernel<{targs}>", f"bwd_dkdv_kernel<{targs}>"
 
-    # Timed region: K steps of forward + backward. Recording an event costs a few microseconds of GPU
-    # time, so only the events after the backward's first three kernels (key normalisation, dq, dk/dv;
-    # recorded by the library on the same stream) are taken here: they give the live launch durations
-    # of the two backward kernels.
-    ev = [[new_event() for _ in range(3)] for _ in range(K)]
-    bh3 = [handle(ev[i]) for i in range(K)]
-    start, end = new_event(), new_event()
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K):
-        fwd()
-        bwd(bh3[i][1], 3)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / K
-    live_ms = {dq_key: sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K,
-               dkdv_key: sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K}
-
-    # Per-kernel breakdown (after the timed region, not part of `value`): every stage event.
+    # Per-kernel breakdown (before the timed region, not part of `value`): every stage event.
     KB = min(K, 50)
     ev0 = [new_event() for _ in range(KB)]
     evb = [[new_event() for _ in stages] for _ in range(KB)]
@@ -337,6 +316,14 @@ def main():
                 "fwd+bwd": spread([ev0[i].elapsed_time(evb[i][-1]) for i in range(KB)]),
                 "steps": KB, "note": "breakdown pass, every stage event recorded"}
 
+    # Timed region: K steps of forward + backward, with the library's stage events around the kernel
+    # that took longest in the breakdown pass only; its live launch duration feeds the roofline. MFMA
+    # FLOPs one launch executes per (query, valid key) pair: forward 4D (S, PV); dq kernel 6D (S, dP
+    # recomputed, dQ); dk/dv kernel 8D (S, dP, dV, dK).
+    per_pair = {f"fwd_kernel<{targs}>": 4 * D, dq_key: 6 * D, dkdv_key: 8 * D}
+    dom = max(per_pair, key=lambda k: kern_ms[k])
+    ms_step, dom_ms = timed_region(fwd, bwd, stages.index(dom), nf, K, stream, new_event, handle)
+
     cold = None
     if args.flush_mall and not (streams or varlen or windowed):
         cold = time_cold_steps(torch, stream, fwd, bwd, new_event, KB)
@@ -359,18 +346,14 @@ def main():
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
     fwd_tflops = fl["fwd"] / (ms_fwd * 1e-3) / 1e12
     bwd_tflops = fl["bwd"] / (ms_bwd * 1e-3) / 1e12
-    # Roofline of the dominant kernel: MFMA FLOPs one launch executes per (query, valid key) pair --
-    # forward 4D (S, PV); dq kernel 6D (S, dP recomputed, dQ); dk/dv kernel 8D (S, dP, dV, dK).
+    # Roofline of the dominant kernel
     pairs = fl["fwd"] / (4.0 * H * D)
-    per_pair = {f"fwd_kernel<{targs}>": 4 * D, dq_key: 6 * D, dkdv_key: 8 * D}
-    dom = max(per_pair, key=lambda k: kern_ms[k])
-    dom_ms = live_ms.get(dom, kern_ms[dom])  # the live timed-region duration where it was recorded
     achieved = per_pair[dom] * H * pairs / (dom_ms * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": stored_traffic(args.workload, dom, args.variant, args.window if windowed else None),
                 "flop_per_launch": per_pair[dom] * H * pairs, "avg_launch_ms": round(dom_ms, 5),
-                "avg_launch_ms_source": "timed region" if dom in live_ms else "breakdown pass"}
+                "avg_launch_ms_source": "timed region"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -407,7 +390,7 @@ def main():
         "bwd_tflops": round(bwd_tflops, 2),
         "gflop_per_step": round(fl["total"] / 1e9, 3),
         "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
-        "kernel_ms_timed_region": {k: round(v, 5) for k, v in live_ms.items()},
+        "kernel_ms_timed_region": {dom: round(dom_ms, 5)},
         "per_step": per_step,
         "preroll": pre,
         "roofline": roofline,
@@ -648,11 +631,13 @@ def breakdown_pass(fwd, bwd, stages, nfs, KB, stream, new_event, handle):
 def timed_region(fwd, bwd, j, nfs, K, stream, new_event, handle):
     """K whole steps between two events. The library's own stage events bracket stage j (of the
     forward's nfs stages followed by the backward's) in every step, so that stage's average launch
-    duration is measured live, on the stream the kernels run on."""
+    duration is measured live, on the stream the kernels run on. Only the two events around stage j
+    are recorded (the entries for the earlier stages are NULL): each recorded event costs the stream
+    a few microseconds."""
     import torch
     jb = j - nfs
     n = (j if jb < 0 else jb) + 1  # stage events handed to the pass that runs stage j
-    ev = [[new_event() for _ in range(n)] for _ in range(K)]
+    ev = [[new_event() if s >= n - 2 else None for s in range(n)] for _ in range(K)]
     pre = [new_event() for _ in range(K)] if n == 1 else None  # stage j is that pass's first
     hs = [handle(ev[i]) for i in range(K)]
     start, end = new_event(), new_event()
@@ -727,7 +712,7 @@ def bench_adaln(args, torch):
         return e
 
     def handle(evs):
-        arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+        arr = (ctypes.c_void_p * len(evs))(*[None if e is None else e.cuda_event for e in evs])
         return arr, ctypes.cast(arr, ctypes.c_void_p)
 
     if args.calibrate_copy:
@@ -834,7 +819,7 @@ def bench_mlp(args, torch):
         return e
 
     def handle(evs):
-        arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+        arr = (ctypes.c_void_p * len(evs))(*[None if e is None else e.cuda_event for e in evs])
         return arr, ctypes.cast(arr, ctypes.c_void_p)
 
     if args.calibrate_copy:

@@ -49,7 +49,7 @@ inline bool launched() { return hipGetLastError() == hipSuccess; }
 // After enqueueing stage i: check the launch and record its event.
 inline bool stage_done(int i, const hipEvent_t* ev, int n, hipStream_t stream) {
   if (hipGetLastError() != hipSuccess) return false;
-  if (i < n && hipEventRecord(ev[i], stream) != hipSuccess) return false;
+  if (i < n && ev[i] && hipEventRecord(ev[i], stream) != hipSuccess) return false;
   return true;
 }
 

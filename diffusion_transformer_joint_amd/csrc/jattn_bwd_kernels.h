@@ -1000,7 +1000,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, bool prenorm, const hipEvent_t*
   int stage = 0;
   auto recorded = [&](hipError_t e) {
     if (e == hipSuccess) e = hipGetLastError();
-    if (e == hipSuccess && n_events > stage) e = hipEventRecord(events[stage], stream);
+    if (e == hipSuccess && n_events > stage && events[stage]) e = hipEventRecord(events[stage], stream);
     ++stage;
     return e;
   };

@@ -419,12 +419,12 @@ static hipError_t launch_fwd_d(const FwdArgs& a, const hipEvent_t* events, int n
   p.total = a.total;
   p.eps = a.eps;
   hipError_t e = launch_prenorm(D, S ? kStreams : (V ? kVarlen : kJoint), p, stream);  // (window: joint)
-  if (e == hipSuccess && n_events > 0) e = hipEventRecord(events[0], stream);
+  if (e == hipSuccess && n_events > 0 && events[0]) e = hipEventRecord(events[0], stream);
   if (e != hipSuccess) return e;
   const int grid = V ? pair_grid(a.B * a.H, a.nblk) : grid_for_items(a.items);
   hipLaunchKernelGGL((fwd_kernel<D, S, V, W>), dim3(grid), dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
-  if (e == hipSuccess && n_events > 1) e = hipEventRecord(events[1], stream);
+  if (e == hipSuccess && n_events > 1 && events[1]) e = hipEventRecord(events[1], stream);
   return e;
 }
 

@@ -130,11 +130,11 @@ hipError_t persistent_grid(const void* kernel, int items, int threads, int* grid
 enum Variant { kJoint = 0, kStreams = 1, kVarlen = 2, kWindow = 3 };
 hipError_t launch_prenorm(int D, Variant var, const PrenormArgs& a, hipStream_t stream);
 // Enqueues the key normalisation (into a.kr) and the forward kernel; if n_events > 0, records
-// events[i] after stage i (i < n_events).
+// events[i] after stage i (i < n_events; a NULL entry records nothing).
 hipError_t launch_fwd(int D, Variant var, const FwdArgs& a, const hipEvent_t* events, int n_events,
                       hipStream_t stream);
 // Enqueues the backward kernels (the key normalisation only if `prenorm`; a.kr then already holds
-// it); if n_events > 0, records events[i] after stage i (i < n_events).
+// it); if n_events > 0, records events[i] after stage i (i < n_events; a NULL entry records nothing).
 hipError_t launch_bwd(int D, Variant var, const BwdArgs& a, bool prenorm, const hipEvent_t* events,
                       int n_events, hipStream_t stream);
 // launch_bwd for D > kNarrowMaxD (defined in jattn_bwd_wide.hip).

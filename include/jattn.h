@@ -142,8 +142,11 @@ jattn_status jattn_bwd(const void* q, const void* k, const void* v, const float*
  * (profilers, benchmarks). Identical results to jattn_bwd. If n_stage_events > 0, stage_events points
  * to n_stage_events (<= JATTN_BWD_STAGES) events created by the caller; event i is recorded on `stream`
  * right after stage i is enqueued, so hipEventElapsedTime between an event recorded before the call
- * and event 0, or between events i-1 and i, gives the duration of stage i. n_stage_events < 0, or
- * > 0 with a NULL array, or > JATTN_BWD_STAGES -> INVALID_VALUE. A failed hipEventRecord -> HIP. */
+ * and event 0, or between events i-1 and i, gives the duration of stage i. A NULL entry records
+ * nothing after its stage (each recorded event is a timestamp on the stream, which costs the stream a
+ * few microseconds, so a caller timing one stage records only the events around it).
+ * n_stage_events < 0, or > 0 with a NULL array, or > JATTN_BWD_STAGES -> INVALID_VALUE. A failed
+ * hipEventRecord -> HIP. */
 jattn_status jattn_bwd_ex(const void* q, const void* k, const void* v, const float* gains,
                           const int32_t* valid_len, const void* out, const float* lse, const void* dout,
                           int B, int L, int H, int D, float softmax_scale, float eps,
