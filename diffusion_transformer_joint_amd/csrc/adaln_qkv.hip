@@ -349,13 +349,15 @@ __device__ __forceinline__ GemmProblem pick(const GemmArgs& a, bool s) {
 // tiles idled while the others ran the image stream's). Within a range, tiles go in groups of
 // kGroupM A-tiles: consecutive tiles walk the group's A-tiles for one B-tile, then the next B-tile,
 // so the ~32 workgroups an XCD runs at once share 4 blocks of A rows and ~8 of B rows in its L2
-// (A-tile fastest over all of A re-streamed the forward's weight once per block of tokens).
-constexpr int kGroupM = 4;
+// (A-tile fastest over all of A re-streamed the forward's weight once per block of tokens). The
+// weight-gradient GEMMs take groups of 16 (C = 3072: dW 604 -> 577 us, dW12 991 -> 924, dW2
+// 601 -> 576 on one box); for the others 16 measured slower (du 878 -> 979 us) and 8 the same as 4.
+constexpr int kGroupM = 4, kGroupMW = 16;  // (kGroupMW: the weight-gradient GEMMs)
 
 struct TileId {
   int s, tm, tn, sp;
   bool ok;
-  __device__ explicit TileId(const GemmArgs& a) {
+  __device__ explicit TileId(const GemmArgs& a, int group_m = kGroupM) {
     const int x = (int)(blockIdx.x & 7), j = (int)(blockIdx.x >> 3);
     const int nt0 = a.pr[0].ntiles, nt1 = a.pr[1].ntiles;
     const int per0 = (nt0 + 7) >> 3, per1 = (nt1 + 7) >> 3;
@@ -370,9 +372,9 @@ struct TileId {
     const int per_split = tiles_m * tiles_n;
     sp = t / per_split;
     t -= sp * per_split;
-    const int group = t / (kGroupM * tiles_n), first = group * kGroupM;
-    const int gm = min(tiles_m - first, kGroupM);
-    const int r = t - group * kGroupM * tiles_n;
+    const int group = t / (group_m * tiles_n), first = group * group_m;
+    const int gm = min(tiles_m - first, group_m);
+    const int r = t - group * group_m * tiles_n;
     tm = first + r % gm;
     tn = r / gm;
   }
@@ -783,7 +785,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W
   using GC = GemmCore<MA, MB, NB, true, W>;
   using CS = ColSumVisit<MB, 64 * W>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[GC::BYTES / 2];
-  const TileId id(a);
+  const TileId id(a, kGroupMW);
   if (!id.ok) return;
   const GemmProblem p = pick(a, id.s != 0);
   const GC g(p);
