@@ -387,7 +387,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, char* smem, int bh, i
 }
 
 template <int D, bool S, bool V, bool W>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu(D)))) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu(D, W)))) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Fwd<D>::BYTES];
   // one item per workgroup (a persistent grid measured slower here: the items are few and large),
   // numbered so that the row blocks of one (batch, head) pair share an XCD and its L2

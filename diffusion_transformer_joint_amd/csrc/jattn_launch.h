@@ -109,8 +109,9 @@ constexpr int kNarrowMaxD = 72;
 
 constexpr int fwd_rows_per_block(int D) { return 128; }
 // Waves per SIMD the forward kernel's register allocation targets: three for D = 32 and 64, whose
-// key/value ring of three buffers leaves room for three workgroups per CU, else two.
-constexpr int fwd_waves_per_eu(int D) { return D == 32 || D == 64 ? 3 : 2; }
+// key/value ring of three buffers leaves room for three workgroups per CU, else two. The windowed
+// (W) instantiations keep two: their mask and tile-range state spills to scratch at three (D = 64).
+constexpr int fwd_waves_per_eu(int D, bool W = false) { return (D == 32 || D == 64) && !W ? 3 : 2; }
 // Backward: both kernels use workgroups of kBwdWaves waves of 32 rows.
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
